@@ -1,0 +1,176 @@
+"""Seeded synthetic inputs for Kimi Delta Attention (KDA) workloads.
+
+This module is shared by the oracle tests, the GPU parity tests and the
+benchmark.  It only draws random numbers and shapes them into the input
+distributions of the workloads; it holds none of the KDA recurrence or chunk
+arithmetic.
+
+Workloads (head dimension 128 follows the Kimi Linear paper summary,
+"Kimi Linear model composition" section, where key and value head dimension is
+128 in every experiment; the 4K / 128K context lengths follow the evaluation
+section; the decode batch stands in for the 1M-token decode measurement,
+whose cost per token does not depend on context length):
+
+  tiny_fp32     B=1  T=256     H=2  d=64   fp32 io, chunk 16, zero initial state
+  prefill       B=4  T=4096    H=16 d=128  bf16 io, chunk 64, S0 ~ 0.02*N(0,1)
+  long_prefill  B=1  T=131072  H=32 d=128  bf16 io, chunk 64, g=-softplus(N(-2,1))
+  decode        256 sequences x 1 token, H=32, d=128, state ~ 0.02*N(0,1)
+  varlen        64 sequences, lengths U[1, 8192], packed with cu_seqlens, H=32
+
+Recipe (one torch CPU generator seeded with the workload's seed; draw order
+[lengths], q, k, v, g_raw, beta_raw, S0):
+  q, k = randn, then divided by their L2 norm over d_k (per token and head)
+  v    = randn
+  g    = -softplus(randn + mu)          (natural-log per-channel gate, mu = 0 or -2)
+  beta = sigmoid(randn)                 (one scalar per token and head)
+  S0   = 0.02 * randn                   ([num_seqs, H, d_k, d_v], fp32)
+q, k, v are then rounded to the io dtype (bf16 round-to-nearest-even); g, beta
+and the state stay fp32.  The same bits feed the oracle and the GPU path.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+import torch
+
+
+@dataclass
+class Workload:
+    name: str
+    B: int
+    T: int
+    H: int
+    dk: int
+    dv: int
+    io: str  # "f32" or "bf16"
+    chunk: int
+    seed: int
+    g_mu: float = 0.0
+    s0_std: Optional[float] = 0.02  # None: zero initial state
+    varlen_seqs: int = 0  # >0: packed variable-length batch with this many sequences
+    varlen_max: int = 0
+    decode: bool = False  # one token per sequence, state updated in place
+
+
+WORKLOADS = {
+    "tiny_fp32": Workload("tiny_fp32", B=1, T=256, H=2, dk=64, dv=64, io="f32", chunk=16, seed=0,
+                          s0_std=None),
+    "prefill": Workload("prefill", B=4, T=4096, H=16, dk=128, dv=128, io="bf16", chunk=64, seed=1),
+    "long_prefill": Workload("long_prefill", B=1, T=131072, H=32, dk=128, dv=128, io="bf16", chunk=64,
+                             seed=2, g_mu=-2.0),
+    "decode": Workload("decode", B=256, T=1, H=32, dk=128, dv=128, io="bf16", chunk=64, seed=3,
+                       decode=True),
+    "varlen": Workload("varlen", B=1, T=0, H=32, dk=128, dv=128, io="bf16", chunk=64, seed=4,
+                       varlen_seqs=64, varlen_max=8192),
+}
+
+
+@dataclass
+class Inputs:
+    """One batch of KDA inputs on the CPU (torch tensors).
+
+    q, k: [B, T, H, dk] (io dtype); v: [B, T, H, dv] (io dtype); g: [B, T, H, dk] fp32;
+    beta: [B, T, H] fp32; s0: [N, H, dk, dv] fp32 or None; cu_seqlens: int32 [N+1] or None
+    (then B == 1 and T is the packed token count).  For decode workloads T == 1 and
+    N == B.
+    """
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    g: torch.Tensor
+    beta: torch.Tensor
+    s0: Optional[torch.Tensor]
+    cu_seqlens: Optional[torch.Tensor]
+    io: str
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def num_seqs(self) -> int:
+        if self.cu_seqlens is not None:
+            return int(self.cu_seqlens.numel()) - 1
+        return int(self.q.shape[0])
+
+    def seq_bounds(self):
+        """(start, length) of every sequence in the flattened [B*T] token axis."""
+        if self.cu_seqlens is not None:
+            cu = self.cu_seqlens.tolist()
+            return [(cu[i], cu[i + 1] - cu[i]) for i in range(len(cu) - 1)]
+        B, T = self.q.shape[0], self.q.shape[1]
+        return [(b * T, T) for b in range(B)]
+
+
+def _io_dtype(io: str) -> torch.dtype:
+    if io == "f32":
+        return torch.float32
+    if io == "bf16":
+        return torch.bfloat16
+    raise ValueError(f"unknown io dtype {io!r}")
+
+
+def _unit_rows(x: torch.Tensor) -> torch.Tensor:
+    return x / torch.linalg.vector_norm(x, dim=-1, keepdim=True)
+
+
+def make_inputs(B: int, T: int, H: int, dk: int, dv: int, io: str, seed: int, *,
+                g_mu: float = 0.0, s0_std: Optional[float] = 0.02,
+                lengths: Optional[list] = None, num_seqs: Optional[int] = None,
+                gen: Optional[torch.Generator] = None) -> Inputs:
+    """Draw one batch following the recipe in the module docstring.
+
+    With ``lengths`` (a list of sequence lengths) the batch is packed: B must be 1 and
+    T is ignored (it becomes sum(lengths)); cu_seqlens is returned.
+    """
+    if gen is None:
+        gen = torch.Generator("cpu").manual_seed(seed)
+    cu = None
+    if lengths is not None:
+        assert B == 1
+        T = int(sum(lengths))
+        cu = torch.zeros(len(lengths) + 1, dtype=torch.int32)
+        cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
+    n = len(lengths) if lengths is not None else (num_seqs if num_seqs is not None else B)
+    dt = _io_dtype(io)
+    q = _unit_rows(torch.randn(B, T, H, dk, generator=gen)).to(dt)
+    k = _unit_rows(torch.randn(B, T, H, dk, generator=gen)).to(dt)
+    v = torch.randn(B, T, H, dv, generator=gen).to(dt)
+    g = -torch.nn.functional.softplus(torch.randn(B, T, H, dk, generator=gen) + g_mu)
+    beta = torch.sigmoid(torch.randn(B, T, H, generator=gen))
+    s0 = None
+    if s0_std is not None:
+        s0 = s0_std * torch.randn(n, H, dk, dv, generator=gen)
+    return Inputs(q=q, k=k, v=v, g=g.contiguous(), beta=beta.contiguous(), s0=s0, cu_seqlens=cu,
+                  io=io, meta=dict(seed=seed, g_mu=g_mu, s0_std=s0_std))
+
+
+def varlen_lengths(num_seqs: int, max_len: int, gen: torch.Generator) -> list:
+    """Sequence lengths uniform in [1, max_len]: the first draw of the workload's generator."""
+    return torch.randint(1, max_len + 1, (num_seqs,), generator=gen).tolist()
+
+
+def workload_inputs(name: str, *, seed: Optional[int] = None) -> Inputs:
+    """Inputs of one named workload (see WORKLOADS)."""
+    w = WORKLOADS[name]
+    s = w.seed if seed is None else seed
+    if w.varlen_seqs:
+        gen = torch.Generator("cpu").manual_seed(s)
+        lengths = varlen_lengths(w.varlen_seqs, w.varlen_max, gen)
+        inp = make_inputs(1, 0, w.H, w.dk, w.dv, w.io, s, g_mu=w.g_mu, s0_std=w.s0_std,
+                          lengths=lengths, gen=gen)
+        inp.meta["lengths"] = lengths
+        return inp
+    if w.decode:
+        # decode: [N, 1, H, d] inputs, state [N, H, dk, dv]
+        return make_inputs(w.B, 1, w.H, w.dk, w.dv, w.io, s, g_mu=w.g_mu, s0_std=w.s0_std)
+    return make_inputs(w.B, w.T, w.H, w.dk, w.dv, w.io, s, g_mu=w.g_mu, s0_std=w.s0_std)
+
+
+def to_numpy_io(x: torch.Tensor) -> np.ndarray:
+    """CPU tensor -> numpy: fp32 stays float32, bf16 becomes its raw uint16 bit pattern."""
+    x = x.contiguous()
+    if x.dtype == torch.bfloat16:
+        return x.view(torch.int16).numpy().view(np.uint16)
+    if x.dtype == torch.float32:
+        return x.numpy()
+    raise TypeError(f"unsupported dtype {x.dtype}")

@@ -1,0 +1,121 @@
+"""Chunkwise KDA in numpy fp64 -- an independent second form of the oracle.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+It follows the Kimi Linear summary page, "Chunkwise parallel algorithm" section:
+the sequence is cut into fixed-length chunks and each chunk's final state is the
+next chunk's initial state; the chunk's rank-1 updates are packed with a WY
+representation built from one UT transform, whose lower-triangular inverse is
+computed row by row by forward substitution and then reused (no second
+inversion); the output merges the inter-chunk recurrent part with the
+intra-chunk parallel part.  The "less compute than general DPLR" section adds
+that both DPLR vectors are tied to the key, so only two C x C chunk matrices
+exist: one from (k, k) and one from (q, k).
+
+Per chunk with positions r = 1..C, in-chunk cumulative log-gate G_r = sum_{i<=r} g_i
+(per channel), and initial state S (d_k x d_v):
+
+    Kt = k * exp(G)        Qt = q * exp(G)        Kh = k * exp(-G)
+    Kb = k * exp(G_C - G)
+    A  = Diag(beta) strictly_lower(Kt Kh^T)                 (C x C, from k and k)
+    T  = (I + A)^{-1} Diag(beta)                            (UT transform)
+    W  = T Kt,   U = T V                                    (WY factors)
+    D  = U - W S                                            (delta-rule corrections)
+    P  = lower_incl_diag(Qt Kh^T)                           (C x C, from q and k)
+    O  = scale (Qt S + P D)
+    S <- Diag(exp(G_C)) S + Kb^T D
+
+Derivation: unrolling the token recurrence inside a chunk gives
+S_r = Diag(e^{G_r}) S + sum_{i<=r} Diag(e^{G_r - G_i}) k_i d_i^T with
+d_r = beta_r (v_r - (Diag(e^{g_r}) S_{r-1})^T k_r); collecting the d_r gives
+(I + A) D = Diag(beta)(V - Kt S).
+
+``anchor="subchunk"`` evaluates exp(G_r - G_i) inside A and P as a product of
+factors taken relative to 16-token sub-chunk boundaries (every factor of an
+off-diagonal block is <= 1), the way a finite-precision kernel has to; in fp64
+both forms agree to rounding.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+
+
+def forward_substitution_inverse(M: np.ndarray) -> np.ndarray:
+    """Inverse of a unit lower-triangular matrix, row by row: row r of X = M^{-1} is
+    e_r - sum_{m<r} M[r, m] X[m, :] (Gaussian-elimination forward substitution)."""
+    n = M.shape[0]
+    X = np.zeros_like(M)
+    for r in range(n):
+        row = np.zeros(n)
+        row[r] = 1.0
+        for m in range(r):
+            row -= M[r, m] * X[m]
+        X[r] = row
+    return X
+
+
+def _gate_products(G: np.ndarray, anchor: str, sub: int) -> np.ndarray:
+    """E[r, i, c] = exp(G[r, c] - G[i, c]) for i <= r (zero above the diagonal)."""
+    C = G.shape[0]
+    E = np.zeros((C, C, G.shape[1]))
+    if anchor == "none":
+        for r in range(C):
+            for i in range(r + 1):
+                E[r, i] = np.exp(G[r]) * np.exp(-G[i])
+        return E
+    if anchor != "subchunk":
+        raise ValueError(anchor)
+    # boundary values b_R = G at the last position before sub-chunk R (b_0 = 0)
+    nsub = (C + sub - 1) // sub
+    b = np.zeros((nsub + 1, G.shape[1]))
+    for R in range(nsub):
+        b[R + 1] = G[min((R + 1) * sub, C) - 1]
+    for r in range(C):
+        R = r // sub
+        for i in range(r + 1):
+            I = i // sub
+            if I == R:  # same sub-chunk: relative to the sub-chunk start
+                E[r, i] = np.exp(G[r] - b[R]) * np.exp(b[R] - G[i])
+            else:  # earlier sub-chunk: three factors, each <= 1
+                E[r, i] = np.exp(G[r] - b[R]) * np.exp(b[R] - b[I + 1]) * np.exp(b[I + 1] - G[i])
+    return E
+
+
+def chunk_step(q, k, v, g, beta, S, scale: float = 1.0, anchor: str = "none", sub: int = 16):
+    """One chunk: q, k, g [C, dk]; v [C, dv]; beta [C]; S [dk, dv] (all fp64).
+    Returns (O [C, dv], S_next [dk, dv])."""
+    C = q.shape[0]
+    G = np.cumsum(g, axis=0)
+    Kt, Qt = k * np.exp(G), q * np.exp(G)
+    Kb = k * np.exp(G[-1] - G)
+    if anchor == "none":
+        Kh = k * np.exp(-G)
+        KK, QK = Kt @ Kh.T, Qt @ Kh.T
+    else:
+        E = _gate_products(G, anchor, sub)
+        KK = np.einsum("rc,ic,ric->ri", k, k, E)
+        QK = np.einsum("rc,ic,ric->ri", q, k, E)
+    A = beta[:, None] * np.tril(KK, -1)
+    X = forward_substitution_inverse(np.eye(C) + A)
+    Tm = X * beta[None, :]  # T = (I + A)^{-1} Diag(beta)
+    W, U = Tm @ Kt, Tm @ v
+    D = U - W @ S
+    P = np.tril(QK)
+    O = scale * (Qt @ S + P @ D)
+    S_next = np.exp(G[-1])[:, None] * S + Kb.T @ D
+    return O, S_next
+
+
+def fwd_one(q, k, v, g, beta, S0: Optional[np.ndarray], chunk: int, scale: float = 1.0, anchor: str = "none",
+            sub: int = 16):
+    """One (sequence, head): q, k, g [T, dk]; v [T, dv]; beta [T].  Returns (O [T, dv], S_T)."""
+    T, dk = q.shape
+    dv = v.shape[1]
+    S = np.zeros((dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    O = np.zeros((T, dv))
+    for c0 in range(0, T, chunk):
+        sl = slice(c0, min(c0 + chunk, T))
+        O[sl], S = chunk_step(q[sl], k[sl], v[sl], g[sl], beta[sl], S, scale, anchor, sub)
+    return O, S
