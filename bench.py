@@ -1,0 +1,166 @@
+#!/usr/bin/env python3
+"""KDA benchmark on one MI355X.
+
+One step = one pass of the hot path over one batch of synthetic input:
+  * kda_chunk_fwd over the prefill workload (B=4, T=4096, H=16, d_k=d_v=128, bf16 q/k/v,
+    fp32 gate/beta/state, chunk 64, initial state given, final state written), and
+  * kda_decode_step over the decode workload (256 sequences x 32 heads, fp32 state
+    128x128 updated in place).
+`value` is prefill tokens/s (B*T tokens per chunk_fwd launch); the decode step is
+reported in GB/s next to it.  Inputs are resident in HBM before the timed region.
+Timing uses HIP events recorded on the stream the kernels are launched on.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--dv-tile T] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s + % bf16 MFMA peak; decode-step GB/s + % HBM peak"
+PEAK_HBM_GBPS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def time_launches(fn, n, stream):
+    """Average duration of one call of fn (ms), from HIP events around n back-to-back calls."""
+    import torch
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(n):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / n
+
+
+def cpu_baseline(inp):
+    import oracle
+    import kda_inputs as ki
+    a = [ki.to_numpy_io(x) for x in (inp.q, inp.k, inp.v)]
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    oracle.fwd(*a, inp.g.numpy(), inp.beta.numpy(), initial_state=inp.s0.numpy(), threads=threads)
+    dt = time.perf_counter() - t0
+    B, T = inp.q.shape[0], inp.q.shape[1]
+    return {"value": B * T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole prefill batch (B={B}, T={T}, H={inp.q.shape[2]}), fp64 token recurrence, "
+                      f"{dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--dv-tile", type=int, default=0)
+    ap.add_argument("--chunk", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the KDA path has no multi-GPU mode (heads and sequences are "
+              "independent; see the sharding note in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_45_amd as kda
+    import kda_inputs as ki
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # ---------------------------------------------------------------- prefill
+    w = ki.WORKLOADS["prefill"]
+    inp = ki.workload_inputs("prefill")
+    d = {k: (None if x is None else x.to(dev)) for k, x in
+         dict(q=inp.q, k=inp.k, v=inp.v, g=inp.g, beta=inp.beta, s0=inp.s0).items()}
+    B, T, H = w.B, w.T, w.H
+    out = torch.empty((B, T, H, w.dv), dtype=torch.bfloat16, device=dev)
+    fin = torch.empty((B, H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    q = kda.query(B, T, H, w.dk, w.dv, "bf16", chunk_size=args.chunk, dv_tile=args.dv_tile, device=True)
+
+    def prefill():
+        kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], chunk_size=args.chunk,
+                      dv_tile=args.dv_tile, out=out, final_state=fin)
+
+    # ----------------------------------------------------------------- decode
+    wd = ki.WORKLOADS["decode"]
+    dinp = ki.workload_inputs("decode")
+    sq = lambda x: x[:, 0].contiguous().to(dev)
+    dq, dk_, dv_, dg, db = (sq(x) for x in (dinp.q, dinp.k, dinp.v, dinp.g, dinp.beta))
+    dstate = dinp.s0.to(dev)
+    dout = torch.empty((wd.B, wd.H, wd.dv), dtype=torch.bfloat16, device=dev)
+
+    def decode():
+        kda.decode_step(dq, dk_, dv_, dg, db, dstate, out=dout)
+
+    for _ in range(args.warmup):
+        prefill()
+        decode()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, each = one prefill launch + one decode launch
+    t_pre = time_launches(prefill, args.steps, stream)
+    t_dec = time_launches(decode, args.steps, stream)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        prefill()
+        decode()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+
+    tokens = B * T
+    pre_tps = tokens / (t_pre * 1e-3)
+    pre_bytes = q["hbm_bytes"]
+    pre_gbps = pre_bytes / (t_pre * 1e-3) / 1e9
+    pre_tflops = q["flops"] / (t_pre * 1e-3) / 1e12
+    dec_bytes = (wd.B * wd.H * (2 * 4 * wd.dk * wd.dv + (2 * wd.dk + 2 * wd.dv) * 2 + 4 * wd.dk + 4))
+    dec_gbps = dec_bytes / (t_dec * 1e-3) / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": round(pre_tps, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"prefill B={B} T={T} H={H} d_k=d_v={w.dk} chunk={q['chunk_size']} bf16 q/k/v, "
+                               f"fp32 gate/beta/state + decode {wd.B} seqs x {wd.H} heads, d=128",
+                   "dv_tile": q["dv_tile"], "device": q["arch"], "compute_units": q["compute_units"]},
+        "roofline": {"bound": "hbm", "achieved": round(pre_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(pre_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "kernel": "kda_chunk_fwd_kernel", "launch_ms": round(t_pre, 4),
+                     "bytes_per_launch": pre_bytes},
+        "prefill": {"ms": round(t_pre, 4), "tokens_per_s": round(pre_tps, 1), "gb_per_s": round(pre_gbps, 1),
+                    "hbm_frac": round(pre_gbps / PEAK_HBM_GBPS, 4), "tflops": round(pre_tflops, 2),
+                    "mfma_frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4), "flops_per_launch": q["flops"]},
+        "decode": {"ms": round(t_dec, 4), "gb_per_s": round(dec_gbps, 1), "hbm_frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
+                   "bytes_per_launch": dec_bytes},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on the prefill batch ...")
+        res["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,236 @@
+"""Kimi Delta Attention (KDA) on AMD Instinct MI355X (gfx950).
+
+Thin Python binding of ``libkda.so`` (C ABI in ``include/kda.h``).  It only checks
+and marshals arguments: every step of the computation runs in the library's HIP
+kernels.  PyTorch provides device memory and the stream; nothing here computes
+KDA itself, and there is no fallback: if the library is missing or the call fails,
+an exception is raised.
+
+Entry points (same names as the C ABI):
+
+* ``chunk_fwd``     -- chunkwise prefill (q, k, v, g, beta, optional initial state,
+                       optional cu_seqlens -> out, final state)
+* ``recurrent_fwd`` -- token-by-token reference mode on the GPU (same arguments)
+* ``decode_step``   -- one token per sequence, state updated in place
+* ``query``         -- launch configuration, algorithmic flops/bytes, device info
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["chunk_fwd", "recurrent_fwd", "decode_step", "query", "KdaError", "LIB_PATH", "library"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
+
+KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP = range(5)
+KDA_F32, KDA_BF16 = 0, 1
+KDA_QUERY_DEVICE = 1
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("head_dim_k", ctypes.c_int32), ("head_dim_v", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int), ("chunk_size", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("dv_tile", ctypes.c_int32)]
+
+
+class QueryResult(ctypes.Structure):
+    _fields_ = [("version", ctypes.c_int32), ("supported", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t),
+                ("chunk_size", ctypes.c_int32), ("dv_tile", ctypes.c_int32), ("threads_per_block", ctypes.c_int32),
+                ("lds_bytes", ctypes.c_int32), ("grid_blocks", ctypes.c_int64), ("flops", ctypes.c_double),
+                ("hbm_bytes", ctypes.c_double), ("device_ok", ctypes.c_int32), ("compute_units", ctypes.c_int32),
+                ("arch", ctypes.c_char * 64), ("peak_bf16_tflops", ctypes.c_double),
+                ("peak_hbm_gbps", ctypes.c_double)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+
+
+def library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libkda.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(path)
+    lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_chunk_fwd.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                  ctypes.c_size_t, _P]
+    lib.kda_recurrent_fwd.restype = ctypes.c_int
+    lib.kda_recurrent_fwd.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.kda_decode_step.restype = ctypes.c_int
+    lib.kda_decode_step.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int,
+                                    ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.kda_query.restype = ctypes.c_int
+    lib.kda_query.argtypes = [ctypes.POINTER(Problem), ctypes.c_uint32, ctypes.POINTER(QueryResult)]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    lib.kda_last_error.restype = ctypes.c_char_p
+    lib.kda_last_error.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != KDA_OK:
+        lib = library()
+        raise KdaError(status, f"{lib.kda_status_string(status).decode()}: {lib.kda_last_error().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(device: torch.device, stream) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _io_code(dtype: torch.dtype) -> int:
+    if dtype == torch.bfloat16:
+        return KDA_BF16
+    if dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"q/k/v must be torch.bfloat16 or torch.float32, got {dtype}")
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape, device) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _problem_from(q, v, cu_seqlens, chunk_size, scale, dv_tile) -> Tuple[Problem, int]:
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, d_k]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if cu_seqlens is not None:
+        if B != 1:
+            raise ValueError("a packed batch (cu_seqlens) needs B == 1")
+        n = cu_seqlens.numel() - 1
+    else:
+        n = B
+    p = Problem(batch=B, seq_len=T, num_heads=H, head_dim_k=dk, head_dim_v=dv,
+                num_seqs=n if cu_seqlens is not None else 0, io_dtype=_io_code(q.dtype), chunk_size=chunk_size,
+                scale=scale, dv_tile=dv_tile)
+    return p, n
+
+
+def _fwd(entry: str, q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_host, chunk_size, scale, dv_tile, out,
+         final_state, output_final_state, stream):
+    dev = q.device
+    p, n = _problem_from(q, v, cu_seqlens, chunk_size, scale, dv_tile)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    _need(q, "q", q.dtype, (B, T, H, dk), dev)
+    _need(k, "k", q.dtype, (B, T, H, dk), dev)
+    _need(v, "v", q.dtype, (B, T, H, dv), dev)
+    _need(g, "g", torch.float32, (B, T, H, dk), dev)
+    _need(beta, "beta", torch.float32, (B, T, H), dev)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (n, H, dk, dv), dev)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, (n + 1,), dev)
+    host_cu = None
+    if cu_seqlens_host is not None:
+        host_cu = torch.as_tensor(cu_seqlens_host, dtype=torch.int32).contiguous().cpu()
+        if host_cu.numel() != n + 1:
+            raise ValueError("cu_seqlens_host has the wrong length")
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    _need(out, "out", q.dtype, (B, T, H, dv), dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((n, H, dk, dv), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _need(final_state, "final_state", torch.float32, (n, H, dk, dv), dev)
+    lib = library()
+    common = [ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
+              None if host_cu is None else ctypes.c_void_p(host_cu.data_ptr()), _ptr(out), _ptr(final_state)]
+    if entry == "chunk":
+        st = lib.kda_chunk_fwd(*common, None, 0, _stream_handle(dev, stream))
+    else:
+        st = lib.kda_recurrent_fwd(*common, _stream_handle(dev, stream))
+    _check(st)
+    return out, final_state
+
+
+def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+              initial_state: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None, *,
+              cu_seqlens_host=None, chunk_size: int = 0, scale: float = 1.0, dv_tile: int = 0,
+              out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+              output_final_state: bool = True, stream=None):
+    """Chunkwise KDA forward.  q, k: [B, T, H, d_k]; v: [B, T, H, d_v] (bf16 or fp32);
+    g: [B, T, H, d_k] fp32 log-gate; beta: [B, T, H] fp32; initial_state: [N, H, d_k, d_v]
+    fp32 or None; cu_seqlens: int32 [N+1] (B == 1) or None.  Returns (out, final_state)."""
+    return _fwd("chunk", q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_host, chunk_size, scale, dv_tile,
+                out, final_state, output_final_state, stream)
+
+
+def recurrent_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+                  initial_state: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None, *,
+                  cu_seqlens_host=None, scale: float = 1.0, out: Optional[torch.Tensor] = None,
+                  final_state: Optional[torch.Tensor] = None, output_final_state: bool = True, stream=None):
+    """Token-by-token KDA on the GPU (reference mode); same arguments as chunk_fwd."""
+    return _fwd("recurrent", q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_host, 0, scale, 0, out,
+                final_state, output_final_state, stream)
+
+
+def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+                state: torch.Tensor, *, scale: float = 1.0, out: Optional[torch.Tensor] = None, stream=None):
+    """One decode token per sequence.  q, k, g: [N, H, d_k]; v: [N, H, d_v]; beta: [N, H];
+    state: [N, H, d_k, d_v] fp32 (updated in place).  Returns out [N, H, d_v]."""
+    dev = q.device
+    if q.dim() != 3:
+        raise ValueError("q must be [N, H, d_k]")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    _need(q, "q", q.dtype, (N, H, dk), dev)
+    _need(k, "k", q.dtype, (N, H, dk), dev)
+    _need(v, "v", q.dtype, (N, H, dv), dev)
+    _need(g, "g", torch.float32, (N, H, dk), dev)
+    _need(beta, "beta", torch.float32, (N, H), dev)
+    _need(state, "state", torch.float32, (N, H, dk, dv), dev)
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
+    _need(out, "out", q.dtype, (N, H, dv), dev)
+    st = library().kda_decode_step(N, H, dk, dv, _io_code(q.dtype), scale, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                   _ptr(beta), _ptr(state), _ptr(out), _stream_handle(dev, stream))
+    _check(st)
+    return out
+
+
+def query(batch: int, seq_len: int, num_heads: int, head_dim_k: int, head_dim_v: int, io: str = "bf16", *,
+          num_seqs: int = 0, chunk_size: int = 0, dv_tile: int = 0, scale: float = 1.0, device: bool = False) -> dict:
+    """Launch configuration and algorithmic work of chunk_fwd for a problem (num_seqs > 0:
+    packed batch with seq_len total tokens)."""
+    p = Problem(batch=batch, seq_len=seq_len, num_heads=num_heads, head_dim_k=head_dim_k, head_dim_v=head_dim_v,
+                num_seqs=num_seqs, io_dtype=KDA_BF16 if io == "bf16" else KDA_F32, chunk_size=chunk_size, scale=scale,
+                dv_tile=dv_tile)
+    r = QueryResult()
+    st = library().kda_query(ctypes.byref(p), KDA_QUERY_DEVICE if device else 0, ctypes.byref(r))
+    if st not in (KDA_OK, KDA_ERR_UNSUPPORTED):
+        _check(st)
+    d = {name: getattr(r, name) for name, _ in QueryResult._fields_}
+    d["arch"] = r.arch.decode()
+    d["status"] = st
+    return d

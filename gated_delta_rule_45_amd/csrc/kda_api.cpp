@@ -1,0 +1,341 @@
+// Host side of libkda.so: argument validation, launch configuration and the C ABI.
+// Every entry point validates on the host before touching HIP, so invalid calls
+// return a status without launching anything (and work on machines without a GPU).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kda_status_t fail(kda_status_t st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+kda_status_t ok() {
+    g_last_error.clear();
+    return KDA_OK;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool supported_head_dim(int d) { return d == 64 || d == 128; }
+
+// Published MI355X peaks used for roofline fractions.
+constexpr double kPeakBf16Tflops = 2500.0;
+constexpr double kPeakHbmGBps = 8000.0;
+constexpr int kAssumedCUs = 256;
+
+struct Resolved {
+    int64_t tokens = 0;     // flattened token count
+    int32_t num_seqs = 0;   // sequences (batch rows or cu_seqlens segments)
+    kda::ChunkConfig cfg{64, 128};
+    int lds = 0;
+};
+
+int default_chunk(const kda_problem_t &p) {
+    if (p.io_dtype == KDA_F32 && p.head_dim_k == 128) return 32;
+    return 64;
+}
+
+// d_v tile: whole rows of the state per workgroup when there are enough (sequence, head)
+// chains to fill the GPU, otherwise narrower tiles so more workgroups run side by side
+// (each tile redoes the key-side work of its chunk).
+int default_dv_tile(int64_t chains, int dv) {
+    int t = dv;
+    while (t > 32 && chains * (dv / t) < kAssumedCUs) t /= 2;
+    return t;
+}
+
+// Shape checks common to the chunked and recurrent forward.
+kda_status_t check_problem(const kda_problem_t *p, Resolved &r, bool chunked) {
+    if (!p) return fail(KDA_ERR_INVALID_ARGUMENT, "problem is NULL");
+    if (p->batch < 0 || p->seq_len < 0 || p->num_heads < 1)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "bad sizes: batch=%d seq_len=%d num_heads=%d", p->batch, p->seq_len,
+                    p->num_heads);
+    if (p->io_dtype != KDA_F32 && p->io_dtype != KDA_BF16)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "io_dtype %d is not KDA_F32 or KDA_BF16", (int)p->io_dtype);
+    if (!supported_head_dim(p->head_dim_k) || !supported_head_dim(p->head_dim_v))
+        return fail(KDA_ERR_UNSUPPORTED, "head dims d_k=%d d_v=%d: supported are 64 and 128", p->head_dim_k,
+                    p->head_dim_v);
+    if (!std::isfinite(p->scale)) return fail(KDA_ERR_INVALID_ARGUMENT, "scale is not finite");
+    if (chunked) {
+        if (p->chunk_size != 0 && p->chunk_size != 16 && p->chunk_size != 32 && p->chunk_size != 64)
+            return fail(KDA_ERR_UNSUPPORTED, "chunk_size %d: supported are 16, 32, 64 (0 = default)", p->chunk_size);
+        if (p->dv_tile != 0 && p->dv_tile != 32 && p->dv_tile != 64 && p->dv_tile != 128)
+            return fail(KDA_ERR_UNSUPPORTED, "dv_tile %d: supported are 32, 64, 128 (0 = default)", p->dv_tile);
+        if (p->dv_tile > p->head_dim_v)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "dv_tile %d exceeds d_v %d", p->dv_tile, p->head_dim_v);
+    }
+    return KDA_OK;
+}
+
+kda_status_t resolve(const kda_problem_t *p, bool varlen, Resolved &r, bool chunked) {
+    kda_status_t st = check_problem(p, r, chunked);
+    if (st != KDA_OK) return st;
+    if (varlen) {
+        if (p->batch != 1) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens needs batch == 1 (got %d)", p->batch);
+        if (p->num_seqs < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs %d < 0", p->num_seqs);
+        r.num_seqs = p->num_seqs;
+        r.tokens = p->seq_len;
+    } else {
+        r.num_seqs = p->batch;
+        r.tokens = (int64_t)p->batch * p->seq_len;
+    }
+    const int64_t blocks_max = (int64_t)r.num_seqs * p->num_heads * 4;
+    if (blocks_max > 0x7fffffffLL) return fail(KDA_ERR_UNSUPPORTED, "too many (sequence, head) pairs");
+    if (r.tokens * p->num_heads * (int64_t)std::max(p->head_dim_k, p->head_dim_v) >= (1LL << 62))
+        return fail(KDA_ERR_UNSUPPORTED, "tensor too large");
+    if (chunked) {
+        r.cfg.chunk = p->chunk_size ? p->chunk_size : default_chunk(*p);
+        r.cfg.dv_tile = p->dv_tile ? p->dv_tile : default_dv_tile((int64_t)r.num_seqs * p->num_heads, p->head_dim_v);
+        r.lds = kda::chunk_variant_lds_bytes(p->io_dtype, p->head_dim_k, r.cfg.dv_tile, r.cfg.chunk);
+        if (r.lds <= 0)
+            return fail(KDA_ERR_UNSUPPORTED, "no compiled variant for io=%s d_k=%d dv_tile=%d chunk=%d (LDS)",
+                        p->io_dtype == KDA_BF16 ? "bf16" : "fp32", p->head_dim_k, r.cfg.dv_tile, r.cfg.chunk);
+    }
+    return KDA_OK;
+}
+
+kda_status_t check_tensors(const kda_problem_t *p, const Resolved &r, const void *q, const void *k, const void *v,
+                           const float *g, const float *beta, const float *s0, const int32_t *cu,
+                           const int32_t *cu_host, const void *out, const float *sf) {
+    if (r.tokens > 0) {
+        const void *req[] = {q, k, v, g, beta, out};
+        const char *names[] = {"q", "k", "v", "g", "beta", "out"};
+        for (int i = 0; i < 6; ++i)
+            if (!req[i]) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
+        const void *al16[] = {q, k, v, g, out};
+        const char *n16[] = {"q", "k", "v", "g", "out"};
+        for (int i = 0; i < 5; ++i)
+            if (!aligned(al16[i], 16)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", n16[i]);
+        if (!aligned(beta, 4)) return fail(KDA_ERR_INVALID_ARGUMENT, "beta is not 4-byte aligned");
+    }
+    if (s0 && !aligned(s0, 16)) return fail(KDA_ERR_INVALID_ARGUMENT, "initial_state is not 16-byte aligned");
+    if (sf && !aligned(sf, 16)) return fail(KDA_ERR_INVALID_ARGUMENT, "final_state is not 16-byte aligned");
+    const bool varlen = cu != nullptr;
+    if (varlen && !aligned(cu, 4)) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens is not 4-byte aligned");
+    if (!varlen && cu_host) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens_host given without cu_seqlens");
+    if (cu_host) {
+        if (cu_host[0] != 0) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens[0] = %d, expected 0", cu_host[0]);
+        for (int32_t i = 0; i < r.num_seqs; ++i)
+            if (cu_host[i + 1] < cu_host[i])
+                return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens decreases at %d (%d -> %d)", i, cu_host[i],
+                            cu_host[i + 1]);
+        if (cu_host[r.num_seqs] != p->seq_len)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens[%d] = %d, expected seq_len %d", r.num_seqs,
+                        cu_host[r.num_seqs], p->seq_len);
+    }
+    // aliasing: only initial_state == final_state is allowed among the written buffers
+    const void *outs[] = {out, sf};
+    const void *ins[] = {q, k, v, g, beta};
+    for (const void *o : outs) {
+        if (!o) continue;
+        for (const void *i : ins)
+            if (o == i) return fail(KDA_ERR_INVALID_ARGUMENT, "an output aliases an input tensor");
+    }
+    if (out && (out == s0 || out == sf)) return fail(KDA_ERR_INVALID_ARGUMENT, "out aliases a state buffer");
+    return KDA_OK;
+}
+
+kda_status_t hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return ok();
+    return fail(KDA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+kda::FwdParams make_params(const kda_problem_t *p, const Resolved &r, const void *q, const void *k, const void *v,
+                           const float *g, const float *beta, const float *s0, const int32_t *cu, void *out,
+                           float *sf) {
+    kda::FwdParams fp;
+    fp.q = q;
+    fp.k = k;
+    fp.v = v;
+    fp.g = g;
+    fp.beta = beta;
+    fp.s0 = s0;
+    fp.cu = cu;
+    fp.order = nullptr;
+    fp.out = out;
+    fp.sf = sf;
+    fp.num_seqs = r.num_seqs;
+    fp.T = p->seq_len;
+    fp.H = p->num_heads;
+    fp.dk = p->head_dim_k;
+    fp.dv = p->head_dim_v;
+    fp.scale = p->scale;
+    return fp;
+}
+
+}  // namespace
+
+namespace kda {
+
+int chunk_variant_lds_bytes(kda_dtype_t io, int dk, int dv_tile, int chunk) {
+    return io == KDA_BF16 ? chunk_variant_lds_bytes_bf16(dk, dv_tile, chunk)
+                          : chunk_variant_lds_bytes_f32(dk, dv_tile, chunk);
+}
+
+hipError_t launch_chunk_fwd(kda_dtype_t io, const FwdParams &p, const ChunkConfig &cfg, hipStream_t stream) {
+    return io == KDA_BF16 ? launch_chunk_fwd_bf16(p, cfg, stream) : launch_chunk_fwd_f32(p, cfg, stream);
+}
+
+}  // namespace kda
+
+extern "C" {
+
+kda_status_t kda_chunk_fwd(const kda_problem_t *problem, const void *q, const void *k, const void *v,
+                           const float *g, const float *beta, const float *initial_state,
+                           const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, void *out,
+                           float *final_state, void *workspace, size_t workspace_bytes, void *stream) {
+    try {
+        Resolved r;
+        kda_status_t st = resolve(problem, cu_seqlens != nullptr, r, true);
+        if (st != KDA_OK) return st;
+        st = check_tensors(problem, r, q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_host, out,
+                           final_state);
+        if (st != KDA_OK) return st;
+        (void)workspace;
+        (void)workspace_bytes;  // no kernel needs scratch memory
+        if (r.num_seqs == 0) return ok();
+        const kda::FwdParams fp =
+            make_params(problem, r, q, k, v, g, beta, initial_state, cu_seqlens, out, final_state);
+        return hip_status(kda::launch_chunk_fwd(problem->io_dtype, fp, r.cfg, static_cast<hipStream_t>(stream)),
+                          "kda_chunk_fwd launch");
+    } catch (...) {
+        return fail(KDA_ERR_HIP, "unexpected exception in kda_chunk_fwd");
+    }
+}
+
+kda_status_t kda_recurrent_fwd(const kda_problem_t *problem, const void *q, const void *k, const void *v,
+                               const float *g, const float *beta, const float *initial_state,
+                               const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, void *out,
+                               float *final_state, void *stream) {
+    try {
+        Resolved r;
+        kda_status_t st = resolve(problem, cu_seqlens != nullptr, r, false);
+        if (st != KDA_OK) return st;
+        st = check_tensors(problem, r, q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_host, out,
+                           final_state);
+        if (st != KDA_OK) return st;
+        if (r.num_seqs == 0) return ok();
+        const kda::FwdParams fp =
+            make_params(problem, r, q, k, v, g, beta, initial_state, cu_seqlens, out, final_state);
+        return hip_status(kda::launch_recurrent_fwd(problem->io_dtype, fp, static_cast<hipStream_t>(stream)),
+                          "kda_recurrent_fwd launch");
+    } catch (...) {
+        return fail(KDA_ERR_HIP, "unexpected exception in kda_recurrent_fwd");
+    }
+}
+
+kda_status_t kda_decode_step(int32_t num_seqs, int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v,
+                             kda_dtype_t io_dtype, float scale, const void *q, const void *k, const void *v,
+                             const float *g, const float *beta, float *state, void *out, void *stream) {
+    try {
+        if (num_seqs < 0 || num_heads < 1)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "bad sizes: num_seqs=%d num_heads=%d", num_seqs, num_heads);
+        if (io_dtype != KDA_F32 && io_dtype != KDA_BF16)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "io_dtype %d is not KDA_F32 or KDA_BF16", (int)io_dtype);
+        if (!supported_head_dim(head_dim_k) || !supported_head_dim(head_dim_v))
+            return fail(KDA_ERR_UNSUPPORTED, "head dims d_k=%d d_v=%d: supported are 64 and 128", head_dim_k,
+                        head_dim_v);
+        if (!std::isfinite(scale)) return fail(KDA_ERR_INVALID_ARGUMENT, "scale is not finite");
+        if ((int64_t)num_seqs * num_heads > 0x7fffffffLL)
+            return fail(KDA_ERR_UNSUPPORTED, "too many (sequence, head) pairs");
+        if (num_seqs == 0) return ok();
+        const void *req[] = {q, k, v, g, beta, state, out};
+        const char *names[] = {"q", "k", "v", "g", "beta", "state", "out"};
+        for (int i = 0; i < 7; ++i)
+            if (!req[i]) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
+        const void *al16[] = {q, k, v, g, state, out};
+        const char *n16[] = {"q", "k", "v", "g", "state", "out"};
+        for (int i = 0; i < 6; ++i)
+            if (!aligned(al16[i], 16)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", n16[i]);
+        if (!aligned(beta, 4)) return fail(KDA_ERR_INVALID_ARGUMENT, "beta is not 4-byte aligned");
+        if (out == state || out == q || out == k || out == v || (const void *)state == (const void *)g ||
+            (const void *)state == q || (const void *)state == k || (const void *)state == v)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "state or out aliases another tensor");
+        return hip_status(kda::launch_decode_step(io_dtype, num_seqs, num_heads, head_dim_k, head_dim_v, scale, q, k,
+                                                  v, g, beta, state, out, static_cast<hipStream_t>(stream)),
+                          "kda_decode_step launch");
+    } catch (...) {
+        return fail(KDA_ERR_HIP, "unexpected exception in kda_decode_step");
+    }
+}
+
+kda_status_t kda_query(const kda_problem_t *problem, uint32_t flags, kda_query_result_t *res) {
+    try {
+        if (!res) return fail(KDA_ERR_INVALID_ARGUMENT, "result is NULL");
+        std::memset(res, 0, sizeof *res);
+        res->version = KDA_VERSION;
+        res->peak_bf16_tflops = kPeakBf16Tflops;
+        res->peak_hbm_gbps = kPeakHbmGBps;
+        Resolved r;
+        const bool varlen = problem && problem->num_seqs > 0;
+        kda_status_t st = resolve(problem, varlen, r, true);
+        if (st == KDA_OK) {
+            const kda_problem_t &p = *problem;
+            res->supported = 1;
+            res->workspace_bytes = 0;
+            res->chunk_size = r.cfg.chunk;
+            res->dv_tile = r.cfg.dv_tile;
+            res->threads_per_block = kda::kChunkThreads;
+            res->lds_bytes = r.lds;
+            res->grid_blocks = (int64_t)r.num_seqs * p.num_heads * (p.head_dim_v / r.cfg.dv_tile);
+            const double C = r.cfg.chunk, dk = p.head_dim_k, dv = p.head_dim_v;
+            const double head_tokens = (double)r.tokens * p.num_heads;
+            // per head-token, as computed chunk by chunk: A and P (C^2 dk each per chunk, triangular),
+            // forward substitution (C^3/3), T applied to the residual and P D (C^2 dv each),
+            // K~ S, Q~ S and K-^T D (2 C dk dv each)
+            res->flops = head_tokens * (2.0 * C * (dk + dv) + C * C / 3.0 + 6.0 * dk * dv);
+            const double s_io = p.io_dtype == KDA_BF16 ? 2.0 : 4.0;
+            res->hbm_bytes = head_tokens * ((2.0 * dk + 2.0 * dv) * s_io + 4.0 * dk + 4.0) +
+                             2.0 * 4.0 * dk * dv * (double)r.num_seqs * p.num_heads;
+        } else if (st != KDA_ERR_UNSUPPORTED) {
+            return st;
+        }
+        if (flags & KDA_QUERY_DEVICE) {
+            int dev = 0;
+            hipDeviceProp_t prop;
+            if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess) {
+                res->device_ok = 1;
+                res->compute_units = prop.multiProcessorCount;
+                std::snprintf(res->arch, sizeof res->arch, "%s", prop.gcnArchName);
+            } else {
+                (void)hipGetLastError();
+            }
+        }
+        if (st == KDA_OK) return ok();
+        return st;
+    } catch (...) {
+        return fail(KDA_ERR_HIP, "unexpected exception in kda_query");
+    }
+}
+
+const char *kda_status_string(kda_status_t s) {
+    switch (s) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_INVALID_ARGUMENT: return "KDA_ERR_INVALID_ARGUMENT";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+        case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP";
+    }
+    return "KDA_ERR_UNKNOWN";
+}
+
+const char *kda_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// Internal (non-ABI) declarations shared by the host dispatch and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kda.h"
+
+namespace kda {
+
+// Everything a forward launch needs; pointers are device pointers.
+struct FwdParams {
+    const void *q, *k, *v;
+    const float *g, *beta;
+    const float *s0;     // [num_seqs, H, DK, DV] or null
+    const int32_t *cu;   // [num_seqs + 1] or null (then sequence n is tokens [n*T, (n+1)*T))
+    const int32_t *order;// optional schedule: order[i] = sequence processed by the i-th group of blocks
+    void *out;
+    float *sf;           // [num_seqs, H, DK, DV] or null
+    int32_t num_seqs, T, H, dk, dv;
+    float scale;
+};
+
+// Chunk-forward configuration chosen by the host.
+struct ChunkConfig {
+    int chunk;
+    int dv_tile;
+};
+
+// Compiled chunk-forward variants (per io dtype) and their LDS footprint; 0 = not built.
+int chunk_variant_lds_bytes(kda_dtype_t io, int dk, int dv_tile, int chunk);
+hipError_t launch_chunk_fwd(kda_dtype_t io, const FwdParams &p, const ChunkConfig &cfg, hipStream_t stream);
+// one entry per io dtype (the two kernel files)
+int chunk_variant_lds_bytes_f32(int dk, int dv_tile, int chunk);
+int chunk_variant_lds_bytes_bf16(int dk, int dv_tile, int chunk);
+hipError_t launch_chunk_fwd_f32(const FwdParams &p, const ChunkConfig &cfg, hipStream_t stream);
+hipError_t launch_chunk_fwd_bf16(const FwdParams &p, const ChunkConfig &cfg, hipStream_t stream);
+
+// Token-serial kernels (recurrent reference mode and the decode step).
+hipError_t launch_recurrent_fwd(kda_dtype_t io, const FwdParams &p, hipStream_t stream);
+hipError_t launch_decode_step(kda_dtype_t io, int32_t N, int32_t H, int32_t dk, int32_t dv, float scale,
+                              const void *q, const void *k, const void *v, const float *g, const float *beta,
+                              float *state, void *out, hipStream_t stream);
+
+constexpr int kChunkThreads = 256;
+constexpr int kSerialThreads = 256;
+
+}  // namespace kda

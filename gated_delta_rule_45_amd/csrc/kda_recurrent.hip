@@ -1,0 +1,235 @@
+// Token-serial KDA kernels for gfx950: the decode step (one token per sequence, state
+// updated in place in HBM) and the recurrent reference mode (a whole sequence, state
+// kept in registers).  Both run the same per-token update (Kimi Linear summary page,
+// "Kimi Delta Attention: fine-grained memory control"):
+//
+//   S' = Diag(e^{g}) S        p = S'^T k        d = beta (v - p)
+//   S  = S' + k d^T           o = scale S^T q = scale (S'^T q + (k.q) d)
+//
+// Every column j of S evolves on its own given (q, k, g, beta, v_j), so the state tile
+// is spread over the workgroup as 4-column groups (16-byte, coalesced row segments)
+// times row groups; the two column reductions (p and S'^T q) cross row groups through
+// LDS.  The decode step is bound by HBM: the 64 KB fp32 state of a (sequence, head) is
+// read once and written once, everything else is a few hundred bytes.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+template <int DK, int DV>
+struct SerialLayout {
+    static constexpr int CG = DV / 4;             // 4-column groups
+    static constexpr int RG = kSerialThreads / CG; // row groups
+    static constexpr int RPT = DK / RG;           // rows per thread: rg, rg+RG, ...
+    static_assert(kSerialThreads % CG == 0 && DK % RG == 0, "layout");
+};
+
+// Per-token inputs staged in LDS (double-buffered across tokens).
+template <int DK, int DV>
+struct TokenSmem {
+    float alpha[DK], k[DK], q[DK], v[DV];
+    float beta, qk;
+    float red_p[SerialLayout<DK, DV>::RG][DV];
+    float red_a[SerialLayout<DK, DV>::RG][DV];
+};
+
+// Stage token inputs: threads < DK load q, k, g; threads < DV load v.  Also reduces k.q.
+template <typename IO, int DK, int DV>
+__device__ __forceinline__ void stage_token(TokenSmem<DK, DV> &ts, float *qk_part, const IO *q, const IO *k,
+                                            const IO *v, const float *g, const float *beta, int tid) {
+    using Tr = IoTraits<IO>;
+    float kq = 0.f;
+    if (tid < DK) {
+        const float kk = Tr::load1(k + tid), qq = Tr::load1(q + tid);
+        ts.alpha[tid] = expf(g[tid]);
+        ts.k[tid] = kk;
+        ts.q[tid] = qq;
+        kq = kk * qq;
+    }
+    if (tid < DV) ts.v[tid] = Tr::load1(v + tid);
+    if (tid == 0) ts.beta = *beta;
+    // wave-level sum of k.q (waves with tid < DK), then one partial per wave
+    if (tid < DK) {
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) kq += __shfl_xor(kq, off, 64);
+        if ((tid & 63) == 0) qk_part[tid >> 6] = kq;
+    }
+}
+
+// One token: S (this thread's RPT x 4 block) is updated in place; returns o for the thread's
+// 4 columns in `o4` (valid for every thread; only row group 0 stores it).
+template <int DK, int DV, int RPT = SerialLayout<DK, DV>::RPT>
+__device__ __forceinline__ void token_update(float (&S)[RPT][4], TokenSmem<DK, DV> &ts, const float *qk_part, int cg,
+                                             int rg, float4 &o4) {
+    using L = SerialLayout<DK, DV>;
+    float pp[4] = {0.f, 0.f, 0.f, 0.f}, aa[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < L::RPT; ++m) {
+        const int i = rg + L::RG * m;
+        const float al = ts.alpha[i], kk = ts.k[i], qq = ts.q[i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            S[m][j] *= al;
+            pp[j] += kk * S[m][j];
+            aa[j] += qq * S[m][j];
+        }
+    }
+    *reinterpret_cast<float4 *>(&ts.red_p[rg][4 * cg]) = make_float4(pp[0], pp[1], pp[2], pp[3]);
+    *reinterpret_cast<float4 *>(&ts.red_a[rg][4 * cg]) = make_float4(aa[0], aa[1], aa[2], aa[3]);
+    __syncthreads();
+    float p4[4] = {0.f, 0.f, 0.f, 0.f}, a4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < L::RG; ++r) {
+        const float4 x = *reinterpret_cast<const float4 *>(&ts.red_p[r][4 * cg]);
+        const float4 y = *reinterpret_cast<const float4 *>(&ts.red_a[r][4 * cg]);
+        p4[0] += x.x; p4[1] += x.y; p4[2] += x.z; p4[3] += x.w;
+        a4[0] += y.x; a4[1] += y.y; a4[2] += y.z; a4[3] += y.w;
+    }
+    float qk = 0.f;
+#pragma unroll
+    for (int w = 0; w < (DK + 63) / 64; ++w) qk += qk_part[w];
+    const float b = ts.beta;
+    float d[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) d[j] = b * (ts.v[4 * cg + j] - p4[j]);
+#pragma unroll
+    for (int m = 0; m < L::RPT; ++m) {
+        const float kk = ts.k[rg + L::RG * m];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) S[m][j] += kk * d[j];
+    }
+    o4 = make_float4(a4[0] + qk * d[0], a4[1] + qk * d[1], a4[2] + qk * d[2], a4[3] + qk * d[3]);
+}
+
+template <typename IO, int DK, int DV>
+__global__ void __launch_bounds__(kSerialThreads) kda_decode_kernel(int32_t H, float scale, const IO *__restrict__ q,
+                                                                    const IO *__restrict__ k, const IO *__restrict__ v,
+                                                                    const float *__restrict__ g,
+                                                                    const float *__restrict__ beta, float *state,
+                                                                    IO *__restrict__ out) {
+    using L = SerialLayout<DK, DV>;
+    __shared__ TokenSmem<DK, DV> ts;
+    __shared__ float qk_part[4];
+    const int tid = threadIdx.x;
+    const int cg = tid % L::CG, rg = tid / L::CG;
+    const int64_t nh = blockIdx.x;  // (sequence, head)
+    float *Sg = state + nh * DK * DV;
+
+    float S[L::RPT][4];
+#pragma unroll
+    for (int m = 0; m < L::RPT; ++m) {
+        const float4 x = *reinterpret_cast<const float4 *>(Sg + (int64_t)(rg + L::RG * m) * DV + 4 * cg);
+        S[m][0] = x.x; S[m][1] = x.y; S[m][2] = x.z; S[m][3] = x.w;
+    }
+    stage_token<IO, DK, DV>(ts, qk_part, q + nh * DK, k + nh * DK, v + nh * DV, g + nh * DK, beta + nh, tid);
+    __syncthreads();
+    float4 o4;
+    token_update<DK, DV>(S, ts, qk_part, cg, rg, o4);
+#pragma unroll
+    for (int m = 0; m < L::RPT; ++m)
+        *reinterpret_cast<float4 *>(Sg + (int64_t)(rg + L::RG * m) * DV + 4 * cg) =
+            make_float4(S[m][0], S[m][1], S[m][2], S[m][3]);
+    if (rg == 0)
+        IoTraits<IO>::store4(out + nh * DV + 4 * cg,
+                             make_float4(o4.x * scale, o4.y * scale, o4.z * scale, o4.w * scale));
+}
+
+template <typename IO, int DK, int DV>
+__global__ void __launch_bounds__(kSerialThreads) kda_recurrent_kernel(FwdParams p) {
+    using L = SerialLayout<DK, DV>;
+    __shared__ TokenSmem<DK, DV> ts[2];
+    __shared__ float qk_part[2][4];
+    const int tid = threadIdx.x;
+    const int cg = tid % L::CG, rg = tid / L::CG;
+    const int H = p.H;
+    const int h = blockIdx.x % H;
+    const int n = blockIdx.x / H;
+    int64_t start;
+    int len;
+    if (p.cu) {
+        start = p.cu[n];
+        len = p.cu[n + 1] - p.cu[n];
+    } else {
+        start = (int64_t)n * p.T;
+        len = p.T;
+    }
+    const IO *Q = static_cast<const IO *>(p.q);
+    const IO *K = static_cast<const IO *>(p.k);
+    const IO *V = static_cast<const IO *>(p.v);
+    IO *O = static_cast<IO *>(p.out);
+    const int64_t sbase = ((int64_t)n * H + h) * DK * DV;
+
+    float S[L::RPT][4];
+#pragma unroll
+    for (int m = 0; m < L::RPT; ++m) {
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (p.s0) x = *reinterpret_cast<const float4 *>(p.s0 + sbase + (int64_t)(rg + L::RG * m) * DV + 4 * cg);
+        S[m][0] = x.x; S[m][1] = x.y; S[m][2] = x.z; S[m][3] = x.w;
+    }
+    for (int t = 0; t < len; ++t) {
+        const int64_t th = (start + t) * H + h;
+        TokenSmem<DK, DV> &cur = ts[t & 1];
+        stage_token<IO, DK, DV>(cur, qk_part[t & 1], Q + th * DK, K + th * DK, V + th * DV, p.g + th * DK, p.beta + th,
+                                tid);
+        __syncthreads();
+        float4 o4;
+        token_update<DK, DV>(S, cur, qk_part[t & 1], cg, rg, o4);
+        if (rg == 0)
+            IoTraits<IO>::store4(O + th * DV + 4 * cg,
+                                 make_float4(o4.x * p.scale, o4.y * p.scale, o4.z * p.scale, o4.w * p.scale));
+    }
+    if (p.sf) {
+#pragma unroll
+        for (int m = 0; m < L::RPT; ++m)
+            *reinterpret_cast<float4 *>(p.sf + sbase + (int64_t)(rg + L::RG * m) * DV + 4 * cg) =
+                make_float4(S[m][0], S[m][1], S[m][2], S[m][3]);
+    }
+}
+
+#define KDA_SERIAL_DIMS(F) F(64, 64) F(64, 128) F(128, 64) F(128, 128)
+
+template <typename IO>
+static hipError_t recurrent_dispatch(const FwdParams &p, hipStream_t stream) {
+    const int64_t blocks = (int64_t)p.num_seqs * p.H;
+    if (blocks <= 0) return hipSuccess;
+#define KDA_REC_CASE(DK_, DV_)                                                                                       \
+    if (p.dk == DK_ && p.dv == DV_) {                                                                                \
+        hipLaunchKernelGGL((kda_recurrent_kernel<IO, DK_, DV_>), dim3((unsigned)blocks), dim3(kSerialThreads), 0, \
+                           stream, p);                                                                               \
+        return hipGetLastError();                                                                                    \
+    }
+    KDA_SERIAL_DIMS(KDA_REC_CASE)
+#undef KDA_REC_CASE
+    return hipErrorInvalidConfiguration;
+}
+
+template <typename IO>
+static hipError_t decode_dispatch(int32_t N, int32_t H, int32_t dk, int32_t dv, float scale, const void *q,
+                                  const void *k, const void *v, const float *g, const float *beta, float *state,
+                                  void *out, hipStream_t stream) {
+    const int64_t blocks = (int64_t)N * H;
+    if (blocks <= 0) return hipSuccess;
+#define KDA_DEC_CASE(DK_, DV_)                                                                                      \
+    if (dk == DK_ && dv == DV_) {                                                                                   \
+        hipLaunchKernelGGL((kda_decode_kernel<IO, DK_, DV_>), dim3((unsigned)blocks), dim3(kSerialThreads), 0,   \
+                           stream, H, scale, static_cast<const IO *>(q), static_cast<const IO *>(k),                \
+                           static_cast<const IO *>(v), g, beta, state, static_cast<IO *>(out));                     \
+        return hipGetLastError();                                                                                   \
+    }
+    KDA_SERIAL_DIMS(KDA_DEC_CASE)
+#undef KDA_DEC_CASE
+    return hipErrorInvalidConfiguration;
+}
+
+hipError_t launch_recurrent_fwd(kda_dtype_t io, const FwdParams &p, hipStream_t stream) {
+    return io == KDA_BF16 ? recurrent_dispatch<uint16_t>(p, stream) : recurrent_dispatch<float>(p, stream);
+}
+
+hipError_t launch_decode_step(kda_dtype_t io, int32_t N, int32_t H, int32_t dk, int32_t dv, float scale,
+                              const void *q, const void *k, const void *v, const float *g, const float *beta,
+                              float *state, void *out, hipStream_t stream) {
+    return io == KDA_BF16 ? decode_dispatch<uint16_t>(N, H, dk, dv, scale, q, k, v, g, beta, state, out, stream)
+                          : decode_dispatch<float>(N, H, dk, dv, scale, q, k, v, g, beta, state, out, stream);
+}
+
+}  // namespace kda

@@ -1,0 +1,164 @@
+/*
+ * kda.h -- C ABI of libkda.so: Kimi Delta Attention (KDA) on AMD Instinct MI355X (gfx950).
+ *
+ * The operator (Kimi Linear summary page, sections "Kimi Delta Attention:
+ * fine-grained memory control" and "From linear attention to Gated DeltaNet"):
+ * per sequence and head, an fp32 state S (d_k x d_v) is decayed per channel and
+ * corrected by a rank-1 delta-rule update for every token t,
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(exp(g_t)) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = scale * S_t^T q_t
+ *
+ * with a per-channel natural-log gate g_t (d_k values, exp(g_t) in (0, 1]) and a
+ * per-head scalar beta_t.  The chunked entry point evaluates the same function
+ * chunk by chunk ("Chunkwise parallel algorithm" section): inside a chunk the
+ * rank-1 updates are packed with a WY/UT representation whose lower-triangular
+ * inverse comes from forward substitution, the state is passed from chunk to
+ * chunk, and the output merges the inter-chunk and intra-chunk parts.
+ *
+ * Conventions shared by every entry point
+ *  - All pointers are device pointers unless the name ends in _host.  The caller
+ *    owns every buffer; the library never frees or keeps a pointer after a call.
+ *  - Tensors are dense, row-major, 16-byte aligned:
+ *        q, k  [tokens, H, d_k]   io dtype (fp32 or bf16)
+ *        v     [tokens, H, d_v]   io dtype
+ *        g     [tokens, H, d_k]   fp32 natural-log gate (alpha = exp(g))
+ *        beta  [tokens, H]        fp32
+ *        out   [tokens, H, d_v]   io dtype
+ *        state [num_seqs, H, d_k, d_v] fp32
+ *    where "tokens" is B*T for a batch (sequence b owns tokens [b*T, (b+1)*T)) or the
+ *    packed token count when cu_seqlens is given.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work is
+ *    queued asynchronously on it; no entry point synchronises.
+ *  - On invalid arguments an entry point returns a status, launches nothing and
+ *    records a message readable with kda_last_error() (thread-local).  Launch
+ *    failures return KDA_ERR_HIP.  Nothing aborts and no C++ exception crosses
+ *    the ABI.
+ *  - q and k are expected to be L2-normalised over d_k (the model does so for
+ *    eigenvalue stability, "Kimi Linear model composition" section); this is not
+ *    checked.  NaN or Inf inputs give undefined results.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_VERSION 100 /* 1.0.0 */
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, negative or inconsistent size */
+    KDA_ERR_UNSUPPORTED = 2,      /* valid but not implemented (head dim, chunk size, dtype) */
+    KDA_ERR_WORKSPACE = 3,        /* workspace smaller than kda_query reports */
+    KDA_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed */
+} kda_status_t;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
+
+/* Problem description shared by kda_chunk_fwd, kda_recurrent_fwd and kda_query. */
+typedef struct {
+    int32_t batch;       /* B: number of sequences of seq_len tokens; must be 1 with cu_seqlens */
+    int32_t seq_len;     /* T per sequence, or the total packed token count with cu_seqlens (>= 0) */
+    int32_t num_heads;   /* H >= 1 */
+    int32_t head_dim_k;  /* d_k in {64, 128} */
+    int32_t head_dim_v;  /* d_v in {64, 128} */
+    int32_t num_seqs;    /* with cu_seqlens: number of sequences (cu_seqlens has num_seqs+1 entries); else ignored */
+    kda_dtype_t io_dtype;/* dtype of q, k, v and out; g, beta and the state are always fp32 */
+    int32_t chunk_size;  /* 16, 32 or 64; 0 = library default (64, or 32 for fp32 with d_k = 128) */
+    float scale;         /* multiplies the output (1.0 for o_t = S_t^T q_t) */
+    int32_t dv_tile;     /* state columns per workgroup: 0 = library choice, else 32, 64 or 128 (tuning) */
+} kda_problem_t;
+
+/*
+ * kda_chunk_fwd -- chunkwise KDA forward (prefill).
+ * Kimi Linear summary page, "Chunkwise parallel algorithm" and "Less compute than
+ * general DPLR" sections.
+ *
+ *  initial_state   [num_seqs, H, d_k, d_v] fp32, or NULL for a zero initial state.
+ *  cu_seqlens      int32 [num_seqs+1] device offsets of a packed batch (cu[0] = 0,
+ *                  non-decreasing, cu[num_seqs] = seq_len), or NULL for a plain batch.
+ *                  Chunks restart at every sequence start and never cross a boundary;
+ *                  a zero-length sequence passes its initial state through.
+ *  cu_seqlens_host optional host copy of cu_seqlens: when given, its contents are
+ *                  validated (otherwise they are a precondition) and used to schedule
+ *                  long sequences first.
+ *  out             [tokens, H, d_v] io dtype (written).
+ *  final_state     [num_seqs, H, d_k, d_v] fp32, or NULL to skip writing it.  It may be
+ *                  the same pointer as initial_state (in-place state cache); no other
+ *                  aliasing between arguments is allowed.
+ *  workspace       device scratch of at least kda_query().workspace_bytes bytes (the
+ *                  current kernels need none: NULL and 0 are accepted).
+ */
+kda_status_t kda_chunk_fwd(const kda_problem_t *problem, const void *q, const void *k, const void *v,
+                           const float *g, const float *beta, const float *initial_state,
+                           const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, void *out,
+                           float *final_state, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kda_recurrent_fwd -- the same function evaluated token by token on the GPU
+ * (reference mode: no chunking, fp32 arithmetic throughout).  Arguments and layouts
+ * as for kda_chunk_fwd; problem->chunk_size is ignored.
+ */
+kda_status_t kda_recurrent_fwd(const kda_problem_t *problem, const void *q, const void *k, const void *v,
+                               const float *g, const float *beta, const float *initial_state,
+                               const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, void *out,
+                               float *final_state, void *stream);
+
+/*
+ * kda_decode_step -- one token for each of num_seqs independent sequences, updating
+ * the per-sequence state in place (the fixed-size state slot that replaces a growing
+ * KV cache; "Kimi Delta Attention" and evaluation sections of the summary page).
+ *
+ *  q, k, g [num_seqs, H, d_k]; v [num_seqs, H, d_v]; beta [num_seqs, H];
+ *  state [num_seqs, H, d_k, d_v] fp32, read and overwritten; out [num_seqs, H, d_v].
+ */
+kda_status_t kda_decode_step(int32_t num_seqs, int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v,
+                             kda_dtype_t io_dtype, float scale, const void *q, const void *k, const void *v,
+                             const float *g, const float *beta, float *state, void *out, void *stream);
+
+/* Result of kda_query. */
+typedef struct {
+    int32_t version;           /* KDA_VERSION of the library */
+    int32_t supported;         /* 1 if kda_chunk_fwd accepts the problem */
+    size_t workspace_bytes;    /* scratch kda_chunk_fwd needs for this problem */
+    int32_t chunk_size;        /* chunk the forward will use */
+    int32_t dv_tile;           /* state columns owned by one workgroup */
+    int32_t threads_per_block; /* workgroup size */
+    int32_t lds_bytes;         /* LDS per workgroup */
+    int64_t grid_blocks;       /* workgroups launched */
+    double flops;              /* algorithmic flops of the call (triangular parts only) */
+    double hbm_bytes;          /* algorithmic HBM bytes: inputs + outputs + state in/out once */
+    int32_t device_ok;         /* 1 if a device was queried (the fields below are valid) */
+    int32_t compute_units;     /* of the current device */
+    char arch[64];             /* gcnArchName of the current device */
+    double peak_bf16_tflops;   /* published dense bf16 matrix peak used for roofline fractions */
+    double peak_hbm_gbps;      /* published HBM peak */
+} kda_query_result_t;
+
+#define KDA_QUERY_DEVICE 1u /* also fill the device fields (one HIP property query, no launch) */
+
+/*
+ * kda_query -- tuning/query entry point: reports how kda_chunk_fwd will run the
+ * problem (chunk, tile, grid, LDS, workspace), its algorithmic flops and bytes, and
+ * optionally the current device.  Launches nothing.  A problem with num_seqs > 0
+ * describes a packed batch (batch must be 1, seq_len is the token count); set
+ * num_seqs = 0 to describe a plain batch of `batch` sequences.
+ */
+kda_status_t kda_query(const kda_problem_t *problem, uint32_t flags, kda_query_result_t *result);
+
+/* Static description of a status code. */
+const char *kda_status_string(kda_status_t status);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char *kda_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,159 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol that
+include/kda.h declares, and rejects invalid calls on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_45_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "kda.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("kda_chunk_fwd", "kda_decode_step", "kda_recurrent_fwd", "kda_query"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = kda.library()
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in kda.h but not exported by libkda.so"
+
+
+def test_exported_symbols_are_c_linkage():
+    # C linkage: the plain name resolves (a C++-mangled symbol would not)
+    lib = ctypes.CDLL(kda.LIB_PATH)
+    assert lib.kda_status_string is not None
+
+
+def test_status_strings():
+    lib = kda.library()
+    assert lib.kda_status_string(0) == b"KDA_OK"
+    assert lib.kda_status_string(2) == b"KDA_ERR_UNSUPPORTED"
+    assert lib.kda_status_string(99) == b"KDA_ERR_UNKNOWN"
+
+
+def problem(**kw):
+    base = dict(batch=1, seq_len=128, num_heads=2, head_dim_k=64, head_dim_v=64, num_seqs=0, io_dtype=kda.KDA_BF16,
+                chunk_size=0, scale=1.0, dv_tile=0)
+    base.update(kw)
+    return kda.Problem(**base)
+
+
+FAKE = ctypes.c_void_p(0x10000)  # 16-byte aligned, never dereferenced: validation fails first or no launch
+fake = lambda i: ctypes.c_void_p(0x100000 * (i + 1))  # distinct aligned addresses, one per argument
+
+
+def call_chunk(p, q=fake(0), k=fake(1), v=fake(2), g=fake(3), beta=fake(4), s0=None, cu=None, cu_host=None,
+               out=fake(5), sf=None):
+    lib = kda.library()
+    return lib.kda_chunk_fwd(ctypes.byref(p) if p is not None else None, q, k, v, g, beta, s0, cu, cu_host, out, sf,
+                             None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_heads=0), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(seq_len=-1), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(batch=-2), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(head_dim_k=96), kda.KDA_ERR_UNSUPPORTED),
+    (dict(head_dim_v=256), kda.KDA_ERR_UNSUPPORTED),
+    (dict(chunk_size=128), kda.KDA_ERR_UNSUPPORTED),
+    (dict(chunk_size=24), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dv_tile=48), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dv_tile=128), kda.KDA_ERR_INVALID_ARGUMENT),  # larger than d_v = 64
+    (dict(io_dtype=7), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(scale=float("nan")), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(io_dtype=kda.KDA_F32, head_dim_k=128, head_dim_v=128, chunk_size=64), kda.KDA_ERR_UNSUPPORTED),
+])
+def test_chunk_fwd_rejects_bad_problems(kw, status):
+    assert call_chunk(problem(**kw)) == status
+    assert kda.library().kda_last_error() != b""
+
+
+def test_chunk_fwd_rejects_null_and_misaligned_pointers():
+    lib = kda.library()
+    assert call_chunk(None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert call_chunk(problem(), q=None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert b"q is NULL" in lib.kda_last_error()
+    assert call_chunk(problem(), out=None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert call_chunk(problem(), g=ctypes.c_void_p(0x10004)) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert b"not 16-byte aligned" in lib.kda_last_error()
+    assert call_chunk(problem(), s0=ctypes.c_void_p(0x10008)) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert call_chunk(problem(), out=FAKE, q=FAKE) == kda.KDA_ERR_INVALID_ARGUMENT  # out aliases q
+    assert b"aliases" in lib.kda_last_error()
+    assert call_chunk(problem(), s0=fake(7), sf=fake(8), out=fake(7)) == kda.KDA_ERR_INVALID_ARGUMENT
+
+
+def test_chunk_fwd_checks_host_cu_seqlens():
+    lens = [3, 5, 0, 7]
+    good = [0, 3, 8, 8, 15]
+    arr = lambda xs: (ctypes.c_int32 * len(xs))(*xs)
+    p = problem(seq_len=15, num_seqs=4)
+    # B != 1 with cu_seqlens
+    assert call_chunk(problem(batch=2, seq_len=15, num_seqs=4), cu=FAKE) == kda.KDA_ERR_INVALID_ARGUMENT
+    bad_start = arr([1, 3, 8, 8, 15])
+    assert call_chunk(p, cu=FAKE, cu_host=bad_start) == kda.KDA_ERR_INVALID_ARGUMENT
+    decreasing = arr([0, 3, 2, 8, 15])
+    assert call_chunk(p, cu=FAKE, cu_host=decreasing) == kda.KDA_ERR_INVALID_ARGUMENT
+    wrong_end = arr([0, 3, 8, 8, 14])
+    assert call_chunk(p, cu=FAKE, cu_host=wrong_end) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert b"expected seq_len" in kda.library().kda_last_error()
+    # host copy without device offsets
+    assert call_chunk(p, cu=None, cu_host=arr(good)) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert sum(lens) == 15
+
+
+def test_empty_problems_launch_nothing_and_succeed():
+    # zero sequences: nothing to do, no HIP call
+    assert call_chunk(problem(batch=0)) == kda.KDA_OK
+    assert call_chunk(problem(seq_len=0, num_seqs=0), cu=FAKE) == kda.KDA_OK
+
+
+def test_decode_step_validation():
+    lib = kda.library()
+    f = lambda *a: lib.kda_decode_step(*a)
+    args = lambda **kw: [kw.get("N", 4), kw.get("H", 2), kw.get("dk", 128), kw.get("dv", 128), kw.get("io", 1), 1.0,
+                         fake(0), fake(1), fake(2), fake(3), fake(4), kw.get("state", ctypes.c_void_p(0x20000)), kw.get("out", ctypes.c_void_p(0x30000)), None]
+    assert f(*args(N=-1)) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert f(*args(H=0)) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert f(*args(dk=32)) == kda.KDA_ERR_UNSUPPORTED
+    assert f(*args(io=3)) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert f(*args(state=None)) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert f(*args(out=ctypes.c_void_p(0x30002))) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert f(*args(N=0)) == kda.KDA_OK
+
+
+def test_recurrent_validation():
+    lib = kda.library()
+    p = problem(head_dim_k=80)
+    st = lib.kda_recurrent_fwd(ctypes.byref(p), fake(0), fake(1), fake(2), fake(3), fake(4), None, None, None,
+                               fake(5), None, None)
+    assert st == kda.KDA_ERR_UNSUPPORTED
+
+
+def test_query_reports_config_and_work():
+    # prefill workload: B=4, T=4096, H=16, d=128, chunk 64, bf16
+    r = kda.query(4, 4096, 16, 128, 128, "bf16")
+    assert r["status"] == kda.KDA_OK and r["supported"] == 1
+    assert r["chunk_size"] == 64 and r["workspace_bytes"] == 0
+    assert r["grid_blocks"] == 4 * 16 * (128 // r["dv_tile"])
+    ht = 4 * 4096 * 16
+    assert r["flops"] == pytest.approx(ht * (2 * 64 * 256 + 64 * 64 / 3 + 6 * 128 * 128))
+    assert r["hbm_bytes"] == pytest.approx(ht * 1540 + 2 * 4 * 128 * 128 * 64)
+    assert 0 < r["lds_bytes"] <= 160 * 1024
+    assert r["peak_hbm_gbps"] == 8000.0 and r["peak_bf16_tflops"] == 2500.0
+    # unsupported variant is reported, not raised
+    r = kda.query(1, 64, 1, 128, 128, "f32", chunk_size=64)
+    assert r["status"] == kda.KDA_ERR_UNSUPPORTED and r["supported"] == 0
+    # packed batch: num_seqs > 0, seq_len = total tokens
+    r = kda.query(1, 1000, 32, 128, 128, "bf16", num_seqs=64)
+    assert r["grid_blocks"] == 64 * 32 * (128 // r["dv_tile"])

@@ -1,0 +1,249 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances (written here, checked per output tensor):
+  fp32 io: max |gpu - oracle| <= 1e-4
+  bf16 io: max |gpu - oracle| / max |oracle| <= 2e-2   (o and the final state separately)
+The state is fp32 in both cases.  Workloads follow kda_inputs.WORKLOADS; full-size
+workloads whose oracle would take minutes are compared on sampled heads.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs as ki
+import oracle
+import gated_delta_rule_45_amd as kda
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TOL_F32_ABS = 1e-4
+TOL_BF16_REL = 2e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def on_dev(inp):
+    t = lambda x: None if x is None else x.to(DEV)
+    return dict(q=t(inp.q), k=t(inp.k), v=t(inp.v), g=t(inp.g), beta=t(inp.beta), initial_state=t(inp.s0),
+                cu_seqlens=t(inp.cu_seqlens))
+
+
+def run_oracle(inp, heads=None, scale=1.0, s0="inp"):
+    a = [ki.to_numpy_io(x) for x in (inp.q, inp.k, inp.v)]
+    s = inp.s0 if s0 == "inp" else s0
+    return oracle.fwd(*a, inp.g.numpy(), inp.beta.numpy(), initial_state=None if s is None else s.numpy(),
+                      cu_seqlens=None if inp.cu_seqlens is None else inp.cu_seqlens.numpy(), scale=scale, heads=heads)
+
+
+def compare(name, got, ref, io):
+    g = got.detach().double().cpu().numpy() if isinstance(got, torch.Tensor) else np.asarray(got, dtype=np.float64)
+    assert g.shape == ref.shape, (name, g.shape, ref.shape)
+    assert np.all(np.isfinite(g)), f"{name}: non-finite values"
+    err = float(np.abs(g - ref).max()) if g.size else 0.0
+    scale = float(np.abs(ref).max()) if ref.size else 0.0
+    rel = err / scale if scale > 0 else err
+    rms = float(np.linalg.norm(g - ref) / max(np.linalg.norm(ref), 1e-300)) if g.size else 0.0
+    say(f"  {name}: max_abs={err:.3e} max_rel={rel:.3e} rms_rel={rms:.3e} (max|ref|={scale:.3e})")
+    if io == "f32":
+        assert err <= TOL_F32_ABS, f"{name}: max abs error {err:.3e} > {TOL_F32_ABS}"
+    else:
+        assert rel <= TOL_BF16_REL, f"{name}: max rel error {rel:.3e} > {TOL_BF16_REL}"
+
+
+def check_fwd(inp, *, heads=None, chunk_size=0, dv_tile=0, scale=1.0, mode="chunk", label=""):
+    say(f"[{label}] mode={mode} io={inp.io} shape={tuple(inp.q.shape)} v={tuple(inp.v.shape)} "
+        f"seqs={inp.num_seqs} chunk={chunk_size} dv_tile={dv_tile} scale={scale} heads={heads}")
+    d = on_dev(inp)
+    if mode == "chunk":
+        out, fin = kda.chunk_fwd(**d, chunk_size=chunk_size, dv_tile=dv_tile, scale=scale)
+    else:
+        out, fin = kda.recurrent_fwd(**d, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, f_ref = run_oracle(inp, heads=heads, scale=scale)
+    if heads is not None:
+        out = out[:, :, heads]
+        fin = fin[:, heads]
+    compare(f"{label} out", out, o_ref, inp.io)
+    compare(f"{label} final_state", fin, f_ref, inp.io)
+    return out, fin
+
+
+# --------------------------------------------------------------- workloads --
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+@pytest.mark.parametrize("dv_tile", [32, 64])
+def test_tiny_fp32_chunk(chunk, dv_tile):
+    check_fwd(ki.workload_inputs("tiny_fp32"), chunk_size=chunk, dv_tile=dv_tile, label="tiny_fp32")
+
+
+def test_tiny_fp32_recurrent():
+    check_fwd(ki.workload_inputs("tiny_fp32"), mode="recurrent", label="tiny_fp32")
+
+
+@pytest.mark.parametrize("dv_tile", [0, 32, 64, 128])
+def test_prefill_full(dv_tile):
+    check_fwd(ki.workload_inputs("prefill"), dv_tile=dv_tile, label="prefill")
+
+
+def test_prefill_recurrent():
+    check_fwd(ki.workload_inputs("prefill"), mode="recurrent", label="prefill")
+
+
+def test_long_prefill_sampled_heads():
+    inp = ki.workload_inputs("long_prefill")
+    check_fwd(inp, heads=[0, 17], label="long_prefill")
+    del inp
+    torch.cuda.empty_cache()
+
+
+def test_varlen_sampled_heads():
+    inp = ki.workload_inputs("varlen")
+    check_fwd(inp, heads=[3, 30], label="varlen")
+
+
+def test_decode_full():
+    inp = ki.workload_inputs("decode")
+    N, _, H, dk = inp.q.shape
+    say(f"[decode] N={N} H={H} dk={dk}")
+    state = inp.s0.to(DEV).clone()
+    sq = lambda x: x[:, 0].contiguous().to(DEV)
+    out = kda.decode_step(sq(inp.q), sq(inp.k), sq(inp.v), sq(inp.g), sq(inp.beta), state)
+    torch.cuda.synchronize()
+    a = [ki.to_numpy_io(x[:, 0].contiguous()) for x in (inp.q, inp.k, inp.v)]
+    o_ref, s_ref = oracle.decode(*a, inp.g[:, 0].contiguous().numpy(), inp.beta[:, 0].contiguous().numpy(),
+                                 inp.s0.numpy())
+    compare("decode out", out, o_ref, "bf16")
+    compare("decode state", state, s_ref, "bf16")
+
+
+# -------------------------------------------------------------- edge cases --
+
+def small(B, T, H, dk, dv, io, seed, **kw):
+    return ki.make_inputs(B, T, H, dk, dv, io, seed, **kw)
+
+
+@pytest.mark.parametrize("io,dk,dv,chunk", [("bf16", 128, 128, 64), ("bf16", 128, 128, 16), ("bf16", 128, 128, 32),
+                                           ("bf16", 64, 128, 64), ("bf16", 128, 64, 32), ("f32", 64, 64, 64),
+                                           ("f32", 128, 128, 32), ("f32", 128, 64, 16)])
+def test_ragged_lengths_and_dims(io, dk, dv, chunk):
+    # T = 203 is not a multiple of any chunk size: every sequence ends in a partial chunk
+    inp = small(2, 203, 3, dk, dv, io, seed=dk + dv + chunk)
+    check_fwd(inp, chunk_size=chunk, label=f"ragged-{io}-{dk}x{dv}-c{chunk}")
+
+
+def test_varlen_with_empty_and_single_token_sequences():
+    lens = [0, 1, 64, 65, 17, 0, 200, 63]
+    inp = ki.make_inputs(1, 0, 4, 128, 128, "bf16", 21, lengths=lens)
+    check_fwd(inp, label="varlen-edge")
+    check_fwd(inp, mode="recurrent", label="varlen-edge")
+
+
+def test_no_initial_state_and_no_final_state():
+    inp = small(2, 150, 2, 128, 128, "bf16", 5, s0_std=None)
+    check_fwd(inp, label="zero-s0")
+    d = on_dev(inp)
+    out, fin = kda.chunk_fwd(**d, output_final_state=False)
+    torch.cuda.synchronize()
+    assert fin is None
+    o_ref, _ = run_oracle(inp)
+    compare("no-final out", out, o_ref, "bf16")
+
+
+def test_in_place_state():
+    inp = small(2, 130, 2, 128, 128, "bf16", 6)
+    d = on_dev(inp)
+    st = d["initial_state"].clone()
+    out, fin = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], st, final_state=st)
+    torch.cuda.synchronize()
+    o_ref, f_ref = run_oracle(inp)
+    compare("inplace out", out, o_ref, "bf16")
+    compare("inplace state", st, f_ref, "bf16")
+
+
+def test_scale():
+    check_fwd(small(1, 100, 2, 64, 64, "f32", 7), scale=0.125, label="scale")
+
+
+def test_zero_beta_is_pure_decay_with_state():
+    # beta == 0 leaves only the decayed initial state; g = -softplus(N(-3, 1)) keeps that
+    # state within fp32 range over 256 tokens (with mu = 0 it decays to ~1e-85)
+    inp = small(2, 256, 2, 128, 128, "bf16", 8, s0_std=1.0, g_mu=-3.0)
+    inp.beta.zero_()
+    check_fwd(inp, label="beta0")
+
+
+def test_unit_gate_deltanet():
+    inp = small(2, 256, 2, 128, 128, "bf16", 9)
+    inp.g.zero_()
+    check_fwd(inp, label="g0")
+
+
+def test_long_memory_gate():
+    inp = small(1, 1024, 2, 128, 128, "bf16", 10, g_mu=-6.0, s0_std=1.0)
+    check_fwd(inp, label="long-memory")
+
+
+def test_strong_gate():
+    # mean per-token log-decay about -2.1: 16-token sub-chunks decay by ~e^-34
+    inp = small(1, 512, 2, 128, 128, "bf16", 11, g_mu=2.0)
+    check_fwd(inp, label="strong-gate")
+
+
+def test_strong_gate_fp32():
+    inp = small(1, 256, 2, 64, 64, "f32", 12, g_mu=2.0)
+    check_fwd(inp, chunk_size=64, label="strong-gate-f32")
+
+
+# ---------------------------------------------------------- cross-checks ----
+
+def test_chunk_equals_recurrent_on_gpu():
+    inp = small(2, 777, 4, 128, 128, "bf16", 13)
+    d = on_dev(inp)
+    o1, f1 = kda.chunk_fwd(**d)
+    o2, f2 = kda.recurrent_fwd(**d)
+    torch.cuda.synchronize()
+    compare("chunk vs recurrent out", o1, o2.double().cpu().numpy(), "bf16")
+    compare("chunk vs recurrent state", f1, f2.double().cpu().numpy(), "bf16")
+
+
+def test_repeated_decode_equals_forward():
+    inp = small(3, 40, 2, 128, 128, "bf16", 14)
+    d = on_dev(inp)
+    o_fwd, f_fwd = kda.chunk_fwd(**d)
+    state = d["initial_state"].clone()
+    outs = []
+    for t in range(inp.q.shape[1]):
+        sl = lambda x: x[:, t].contiguous()
+        outs.append(kda.decode_step(sl(d["q"]), sl(d["k"]), sl(d["v"]), sl(d["g"]), sl(d["beta"]), state))
+    torch.cuda.synchronize()
+    o_dec = torch.stack(outs, dim=1)
+    o_ref, f_ref = run_oracle(inp)
+    compare("decode-seq out", o_dec, o_ref, "bf16")
+    compare("decode-seq state", state, f_ref, "bf16")
+    compare("chunk out (same inputs)", o_fwd, o_ref, "bf16")
+
+
+def test_split_invariance():
+    # running [0, T1) then [T1, T) from the GPU final state equals one run
+    inp = small(1, 300, 2, 128, 128, "bf16", 15)
+    d = on_dev(inp)
+    o, f = kda.chunk_fwd(**d)
+    T1 = 137
+    cut = lambda x, s: x[:, s].contiguous()
+    oa, fa = kda.chunk_fwd(cut(d["q"], slice(0, T1)), cut(d["k"], slice(0, T1)), cut(d["v"], slice(0, T1)),
+                           cut(d["g"], slice(0, T1)), cut(d["beta"], slice(0, T1)), d["initial_state"])
+    ob, fb = kda.chunk_fwd(cut(d["q"], slice(T1, None)), cut(d["k"], slice(T1, None)), cut(d["v"], slice(T1, None)),
+                           cut(d["g"], slice(T1, None)), cut(d["beta"], slice(T1, None)), fa)
+    torch.cuda.synchronize()
+    o_ref, f_ref = run_oracle(inp)
+    compare("split out", torch.cat([oa, ob], dim=1), o_ref, "bf16")
+    compare("split state", fb, f_ref, "bf16")
+
+
+def test_query_on_device():
+    r = kda.query(4, 4096, 16, 128, 128, "bf16", device=True)
+    say(f"  device: {r['arch']} CUs={r['compute_units']}")
+    assert r["device_ok"] == 1 and r["arch"].startswith("gfx950")
