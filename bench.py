@@ -64,6 +64,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--dv-tile", type=int, default=0)
     ap.add_argument("--chunk", type=int, default=64)
+    ap.add_argument("--algo", default="auto", choices=["auto", "fused", "two_pass"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -87,11 +88,13 @@ def main():
     B, T, H = w.B, w.T, w.H
     out = torch.empty((B, T, H, w.dv), dtype=torch.bfloat16, device=dev)
     fin = torch.empty((B, H, w.dk, w.dv), dtype=torch.float32, device=dev)
-    q = kda.query(B, T, H, w.dk, w.dv, "bf16", chunk_size=args.chunk, dv_tile=args.dv_tile, device=True)
+    q = kda.query(B, T, H, w.dk, w.dv, "bf16", chunk_size=args.chunk, dv_tile=args.dv_tile, algo=args.algo,
+                  device=True)
+    ws = torch.empty(max(q["workspace_bytes"], 1), dtype=torch.uint8, device=dev)
 
     def prefill():
         kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], chunk_size=args.chunk,
-                      dv_tile=args.dv_tile, out=out, final_state=fin)
+                      dv_tile=args.dv_tile, algo=args.algo, workspace=ws, out=out, final_state=fin)
 
     # ----------------------------------------------------------------- decode
     wd = ki.WORKLOADS["decode"]
@@ -145,7 +148,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"prefill B={B} T={T} H={H} d_k=d_v={w.dk} chunk={q['chunk_size']} bf16 q/k/v, "
                                f"fp32 gate/beta/state + decode {wd.B} seqs x {wd.H} heads, d=128",
-                   "dv_tile": q["dv_tile"], "device": q["arch"], "compute_units": q["compute_units"]},
+                   "dv_tile": q["dv_tile"], "algo": ["auto", "fused", "two_pass"][q["algo"]],
+                   "workspace_bytes": q["workspace_bytes"], "device": q["arch"], "compute_units": q["compute_units"]},
         "roofline": {"bound": "hbm", "achieved": round(pre_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(pre_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
                      "kernel": "kda_chunk_fwd_kernel", "launch_ms": round(t_pre, 4),

@@ -29,6 +29,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP = range(5)
 KDA_F32, KDA_BF16 = 0, 1
 KDA_QUERY_DEVICE = 1
+KDA_ALGO_AUTO, KDA_ALGO_FUSED, KDA_ALGO_TWO_PASS = 0, 1, 2
+_ALGOS = {"auto": KDA_ALGO_AUTO, "fused": KDA_ALGO_FUSED, "two_pass": KDA_ALGO_TWO_PASS}
 
 
 class KdaError(RuntimeError):
@@ -41,11 +43,12 @@ class Problem(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32), ("num_heads", ctypes.c_int32),
                 ("head_dim_k", ctypes.c_int32), ("head_dim_v", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
                 ("io_dtype", ctypes.c_int), ("chunk_size", ctypes.c_int32), ("scale", ctypes.c_float),
-                ("dv_tile", ctypes.c_int32)]
+                ("dv_tile", ctypes.c_int32), ("algo", ctypes.c_int)]
 
 
 class QueryResult(ctypes.Structure):
-    _fields_ = [("version", ctypes.c_int32), ("supported", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t),
+    _fields_ = [("version", ctypes.c_int32), ("supported", ctypes.c_int32), ("algo", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_size_t),
                 ("chunk_size", ctypes.c_int32), ("dv_tile", ctypes.c_int32), ("threads_per_block", ctypes.c_int32),
                 ("lds_bytes", ctypes.c_int32), ("grid_blocks", ctypes.c_int64), ("flops", ctypes.c_double),
                 ("hbm_bytes", ctypes.c_double), ("device_ok", ctypes.c_int32), ("compute_units", ctypes.c_int32),
@@ -119,7 +122,15 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape, device) -> None
         raise ValueError(f"{name} must be contiguous")
 
 
-def _problem_from(q, v, cu_seqlens, chunk_size, scale, dv_tile) -> Tuple[Problem, int]:
+def _algo_code(algo) -> int:
+    if isinstance(algo, str):
+        if algo not in _ALGOS:
+            raise ValueError(f"algo must be one of {sorted(_ALGOS)}")
+        return _ALGOS[algo]
+    return int(algo)
+
+
+def _problem_from(q, v, cu_seqlens, chunk_size, scale, dv_tile, algo=0) -> Tuple[Problem, int]:
     if q.dim() != 4:
         raise ValueError("q must be [B, T, H, d_k]")
     B, T, H, dk = q.shape
@@ -132,14 +143,22 @@ def _problem_from(q, v, cu_seqlens, chunk_size, scale, dv_tile) -> Tuple[Problem
         n = B
     p = Problem(batch=B, seq_len=T, num_heads=H, head_dim_k=dk, head_dim_v=dv,
                 num_seqs=n if cu_seqlens is not None else 0, io_dtype=_io_code(q.dtype), chunk_size=chunk_size,
-                scale=scale, dv_tile=dv_tile)
+                scale=scale, dv_tile=dv_tile, algo=_algo_code(algo))
     return p, n
 
 
+def workspace_bytes(p: Problem) -> int:
+    """Workspace the two-pass algorithm needs for problem p (0 if it would not be used)."""
+    r = QueryResult()
+    st = library().kda_query(ctypes.byref(p), 0, ctypes.byref(r))
+    _check(st)
+    return int(r.workspace_bytes)
+
+
 def _fwd(entry: str, q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_host, chunk_size, scale, dv_tile, out,
-         final_state, output_final_state, stream):
+         final_state, output_final_state, stream, algo=0, workspace=None):
     dev = q.device
-    p, n = _problem_from(q, v, cu_seqlens, chunk_size, scale, dv_tile)
+    p, n = _problem_from(q, v, cu_seqlens, chunk_size, scale, dv_tile, algo if entry == "chunk" else 0)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     _need(q, "q", q.dtype, (B, T, H, dk), dev)
@@ -167,7 +186,12 @@ def _fwd(entry: str, q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_hos
     common = [ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
               None if host_cu is None else ctypes.c_void_p(host_cu.data_ptr()), _ptr(out), _ptr(final_state)]
     if entry == "chunk":
-        st = lib.kda_chunk_fwd(*common, None, 0, _stream_handle(dev, stream))
+        if workspace is None and p.algo != KDA_ALGO_FUSED:
+            need = workspace_bytes(p)
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+        ws_ptr = None if workspace is None else ctypes.c_void_p(workspace.data_ptr())
+        ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        st = lib.kda_chunk_fwd(*common, ws_ptr, ws_len, _stream_handle(dev, stream))
     else:
         st = lib.kda_recurrent_fwd(*common, _stream_handle(dev, stream))
     _check(st)
@@ -177,13 +201,15 @@ def _fwd(entry: str, q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_hos
 def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
               initial_state: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None, *,
               cu_seqlens_host=None, chunk_size: int = 0, scale: float = 1.0, dv_tile: int = 0,
-              out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
-              output_final_state: bool = True, stream=None):
+              algo="auto", workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+              final_state: Optional[torch.Tensor] = None, output_final_state: bool = True, stream=None):
     """Chunkwise KDA forward.  q, k: [B, T, H, d_k]; v: [B, T, H, d_v] (bf16 or fp32);
     g: [B, T, H, d_k] fp32 log-gate; beta: [B, T, H] fp32; initial_state: [N, H, d_k, d_v]
-    fp32 or None; cu_seqlens: int32 [N+1] (B == 1) or None.  Returns (out, final_state)."""
+    fp32 or None; cu_seqlens: int32 [N+1] (B == 1) or None.  algo: "auto", "fused" or
+    "two_pass"; workspace: uint8 device tensor for the two-pass algorithm (allocated here
+    when None and needed).  Returns (out, final_state)."""
     return _fwd("chunk", q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_host, chunk_size, scale, dv_tile,
-                out, final_state, output_final_state, stream)
+                out, final_state, output_final_state, stream, algo=algo, workspace=workspace)
 
 
 def recurrent_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
@@ -220,12 +246,13 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
 
 
 def query(batch: int, seq_len: int, num_heads: int, head_dim_k: int, head_dim_v: int, io: str = "bf16", *,
-          num_seqs: int = 0, chunk_size: int = 0, dv_tile: int = 0, scale: float = 1.0, device: bool = False) -> dict:
+          num_seqs: int = 0, chunk_size: int = 0, dv_tile: int = 0, scale: float = 1.0, algo="auto",
+          device: bool = False) -> dict:
     """Launch configuration and algorithmic work of chunk_fwd for a problem (num_seqs > 0:
     packed batch with seq_len total tokens)."""
     p = Problem(batch=batch, seq_len=seq_len, num_heads=num_heads, head_dim_k=head_dim_k, head_dim_v=head_dim_v,
                 num_seqs=num_seqs, io_dtype=KDA_BF16 if io == "bf16" else KDA_F32, chunk_size=chunk_size, scale=scale,
-                dv_tile=dv_tile)
+                dv_tile=dv_tile, algo=_algo_code(algo))
     r = QueryResult()
     st = library().kda_query(ctypes.byref(p), KDA_QUERY_DEVICE if device else 0, ctypes.byref(r))
     if st not in (KDA_OK, KDA_ERR_UNSUPPORTED):

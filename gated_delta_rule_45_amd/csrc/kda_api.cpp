@@ -43,8 +43,12 @@ constexpr int kAssumedCUs = 256;
 struct Resolved {
     int64_t tokens = 0;     // flattened token count
     int32_t num_seqs = 0;   // sequences (batch rows or cu_seqlens segments)
-    kda::ChunkConfig cfg{64, 128};
-    int lds = 0;
+    kda::ChunkConfig cfg{64, 128};  // fused algorithm: chunk and d_v tile
+    int lds = 0;                    // fused algorithm: LDS per workgroup (0 = not supported)
+    bool two_pass_ok = false;       // two-pass algorithm supports the problem
+    int nw = 4;                     // two-pass: waves (16 state columns each) per scan workgroup
+    int64_t chunk_upper = 0;        // two-pass: upper bound on the number of chunks
+    size_t ws_bytes = 0;            // two-pass: workspace bytes
 };
 
 int default_chunk(const kda_problem_t &p) {
@@ -80,6 +84,8 @@ kda_status_t check_problem(const kda_problem_t *p, Resolved &r, bool chunked) {
             return fail(KDA_ERR_UNSUPPORTED, "dv_tile %d: supported are 32, 64, 128 (0 = default)", p->dv_tile);
         if (p->dv_tile > p->head_dim_v)
             return fail(KDA_ERR_INVALID_ARGUMENT, "dv_tile %d exceeds d_v %d", p->dv_tile, p->head_dim_v);
+        if (p->algo != KDA_ALGO_AUTO && p->algo != KDA_ALGO_FUSED && p->algo != KDA_ALGO_TWO_PASS)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "algo %d is not a kda_algo_t", (int)p->algo);
     }
     return KDA_OK;
 }
@@ -101,12 +107,49 @@ kda_status_t resolve(const kda_problem_t *p, bool varlen, Resolved &r, bool chun
     if (r.tokens * p->num_heads * (int64_t)std::max(p->head_dim_k, p->head_dim_v) >= (1LL << 62))
         return fail(KDA_ERR_UNSUPPORTED, "tensor too large");
     if (chunked) {
-        r.cfg.chunk = p->chunk_size ? p->chunk_size : default_chunk(*p);
+        const int C = p->chunk_size ? p->chunk_size : default_chunk(*p);
+        r.cfg.chunk = C;
         r.cfg.dv_tile = p->dv_tile ? p->dv_tile : default_dv_tile((int64_t)r.num_seqs * p->num_heads, p->head_dim_v);
         r.lds = kda::chunk_variant_lds_bytes(p->io_dtype, p->head_dim_k, r.cfg.dv_tile, r.cfg.chunk);
-        if (r.lds <= 0)
-            return fail(KDA_ERR_UNSUPPORTED, "no compiled variant for io=%s d_k=%d dv_tile=%d chunk=%d (LDS)",
+        // two-pass: scan workgroups of 16 * nw state columns
+        r.nw = p->dv_tile == 32 ? 2 : 4;
+        r.two_pass_ok = p->dv_tile != 128 && (16 * r.nw) <= p->head_dim_v &&
+                        kda::split_variant_supported(p->io_dtype, p->head_dim_k, C, r.nw);
+        if (r.two_pass_ok) {
+            const int64_t per = ((int64_t)p->seq_len + C - 1) / C;
+            r.chunk_upper = varlen ? per + r.num_seqs : (int64_t)r.num_seqs * per;
+            r.ws_bytes = kda::split_workspace_bytes(p->io_dtype, p->head_dim_k, C, r.chunk_upper, p->num_heads,
+                                                    r.num_seqs);
+        }
+        const bool fused_ok = r.lds > 0;
+        if (p->algo == KDA_ALGO_FUSED && !fused_ok)
+            return fail(KDA_ERR_UNSUPPORTED, "fused: no compiled variant for io=%s d_k=%d dv_tile=%d chunk=%d (LDS)",
                         p->io_dtype == KDA_BF16 ? "bf16" : "fp32", p->head_dim_k, r.cfg.dv_tile, r.cfg.chunk);
+        if (p->algo == KDA_ALGO_TWO_PASS && !r.two_pass_ok)
+            return fail(KDA_ERR_UNSUPPORTED, "two-pass: no compiled variant for io=%s d_k=%d chunk=%d dv_tile=%d",
+                        p->io_dtype == KDA_BF16 ? "bf16" : "fp32", p->head_dim_k, C, p->dv_tile);
+        if (!fused_ok && !r.two_pass_ok)
+            return fail(KDA_ERR_UNSUPPORTED, "no compiled variant for io=%s d_k=%d dv_tile=%d chunk=%d",
+                        p->io_dtype == KDA_BF16 ? "bf16" : "fp32", p->head_dim_k, r.cfg.dv_tile, C);
+    }
+    return KDA_OK;
+}
+
+// Algorithm for this call given the caller's workspace.
+kda_status_t pick_algo(const kda_problem_t *p, const Resolved &r, const void *ws, size_t ws_bytes, int &algo) {
+    const bool ws_ok = ws != nullptr && ws_bytes >= r.ws_bytes && aligned(ws, 256);
+    if (p->algo == KDA_ALGO_TWO_PASS) {
+        if (!ws_ok)
+            return fail(KDA_ERR_WORKSPACE, "two-pass needs a 256-byte aligned workspace of %zu bytes (got %zu at %p)",
+                        r.ws_bytes, ws_bytes, ws);
+        algo = KDA_ALGO_TWO_PASS;
+    } else if (p->algo == KDA_ALGO_FUSED) {
+        algo = KDA_ALGO_FUSED;
+    } else {
+        algo = (r.two_pass_ok && ws_ok) ? KDA_ALGO_TWO_PASS : KDA_ALGO_FUSED;
+        if (algo == KDA_ALGO_FUSED && r.lds <= 0)
+            return fail(KDA_ERR_WORKSPACE, "this problem needs the two-pass algorithm and a workspace of %zu bytes",
+                        r.ws_bytes);
     }
     return KDA_OK;
 }
@@ -184,6 +227,21 @@ kda::FwdParams make_params(const kda_problem_t *p, const Resolved &r, const void
 
 namespace kda {
 
+size_t split_workspace_bytes(kda_dtype_t io, int dk, int chunk, int64_t chunk_upper, int H, int64_t num_seqs) {
+    const size_t rec = io == KDA_BF16 ? split_record_size_bf16(dk, chunk) : split_record_size_f32(dk, chunk);
+    return split_plan_bytes(num_seqs) + (size_t)chunk_upper * H * rec;
+}
+
+bool split_variant_supported(kda_dtype_t io, int dk, int chunk, int nw) {
+    return io == KDA_BF16 ? split_supported_bf16(dk, chunk, nw) : split_supported_f32(dk, chunk, nw);
+}
+
+hipError_t launch_split_fwd(kda_dtype_t io, const FwdParams &p, int chunk, int nw, char *workspace,
+                            int64_t chunk_upper, hipStream_t stream) {
+    return io == KDA_BF16 ? launch_split_bf16(p, chunk, nw, workspace, chunk_upper, stream)
+                          : launch_split_f32(p, chunk, nw, workspace, chunk_upper, stream);
+}
+
 int chunk_variant_lds_bytes(kda_dtype_t io, int dk, int dv_tile, int chunk) {
     return io == KDA_BF16 ? chunk_variant_lds_bytes_bf16(dk, dv_tile, chunk)
                           : chunk_variant_lds_bytes_f32(dk, dv_tile, chunk);
@@ -208,13 +266,19 @@ kda_status_t kda_chunk_fwd(const kda_problem_t *problem, const void *q, const vo
         st = check_tensors(problem, r, q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_host, out,
                            final_state);
         if (st != KDA_OK) return st;
-        (void)workspace;
-        (void)workspace_bytes;  // no kernel needs scratch memory
+        int algo = KDA_ALGO_FUSED;
+        st = pick_algo(problem, r, workspace, workspace_bytes, algo);
+        if (st != KDA_OK) return st;
         if (r.num_seqs == 0) return ok();
         const kda::FwdParams fp =
             make_params(problem, r, q, k, v, g, beta, initial_state, cu_seqlens, out, final_state);
+        if (algo == KDA_ALGO_TWO_PASS)
+            return hip_status(kda::launch_split_fwd(problem->io_dtype, fp, r.cfg.chunk, r.nw,
+                                                    static_cast<char *>(workspace), r.chunk_upper,
+                                                    static_cast<hipStream_t>(stream)),
+                              "kda_chunk_fwd (two-pass) launch");
         return hip_status(kda::launch_chunk_fwd(problem->io_dtype, fp, r.cfg, static_cast<hipStream_t>(stream)),
-                          "kda_chunk_fwd launch");
+                          "kda_chunk_fwd (fused) launch");
     } catch (...) {
         return fail(KDA_ERR_HIP, "unexpected exception in kda_chunk_fwd");
     }
@@ -289,12 +353,21 @@ kda_status_t kda_query(const kda_problem_t *problem, uint32_t flags, kda_query_r
         if (st == KDA_OK) {
             const kda_problem_t &p = *problem;
             res->supported = 1;
-            res->workspace_bytes = 0;
+            const bool two = r.two_pass_ok && p.algo != KDA_ALGO_FUSED;
+            res->algo = two ? KDA_ALGO_TWO_PASS : KDA_ALGO_FUSED;
+            res->workspace_bytes = two ? r.ws_bytes : 0;
             res->chunk_size = r.cfg.chunk;
-            res->dv_tile = r.cfg.dv_tile;
-            res->threads_per_block = kda::kChunkThreads;
-            res->lds_bytes = r.lds;
-            res->grid_blocks = (int64_t)r.num_seqs * p.num_heads * (p.head_dim_v / r.cfg.dv_tile);
+            if (two) {  // the scan pass: one workgroup per (sequence, head, 16*nw columns)
+                res->dv_tile = 16 * r.nw;
+                res->threads_per_block = 64 * r.nw;
+                res->lds_bytes = 0;
+                res->grid_blocks = (int64_t)r.num_seqs * p.num_heads * (p.head_dim_v / (16 * r.nw));
+            } else {
+                res->dv_tile = r.cfg.dv_tile;
+                res->threads_per_block = kda::kChunkThreads;
+                res->lds_bytes = r.lds;
+                res->grid_blocks = (int64_t)r.num_seqs * p.num_heads * (p.head_dim_v / r.cfg.dv_tile);
+            }
             const double C = r.cfg.chunk, dk = p.head_dim_k, dv = p.head_dim_v;
             const double head_tokens = (double)r.tokens * p.num_heads;
             // per head-token, as computed chunk by chunk: A and P (C^2 dk each per chunk, triangular),

@@ -17,21 +17,23 @@
 // The WY factors of the pages are W = T K~ and U = T V; D = U - W S is evaluated here as
 // T (V - K~ S), which gives the same D but costs C*d_k*dvt instead of C^2*d_k per tile.
 //
-// Numerics.  Gates are handled in the log2 domain.  Inside A and P the factor
-// e^{G_r - G_i} is split at 16-token sub-chunk boundaries b_R (G before sub-chunk R):
-//   off-diagonal block (R > I):  [k_r e^{G_r-b_R}] [e^{b_R-b_{I+1}}] [k_i e^{b_{I+1}-G_i}]
-//                                 every factor <= 1;
-//   diagonal block (R == I):     [k_r e^{G_r-b_R} e^{-(b_{R+1}-b_R)}] [k_i e^{b_{R+1}-G_i}]
-//                                 the row factor is >= 1 and overflows only when one
-//                                 16-token sub-chunk decays a channel by more than e^-88.
+// Numerics.  Gates are handled in the log2 domain.  With b_R the cumulative gate before
+// 16-token sub-chunk R, the factor e^{G_r - G_i} inside A and P is split as
+//   off-diagonal block (R > I):  [k_r e^{G_r-b_R}] [k_i e^{b_{I+1}-G_i} e^{b_R-b_{I+1}}]
+//                                 (row factor and both column factors <= 1);
+//   diagonal block (R == I):     [k_r e^{G_r-b_R}] [k_i e^{b_R-G_i}]
+//                                 (the column factor is >= 1 and overflows only when one
+//                                 16-token sub-chunk decays a channel by more than e^-88).
 // The operands of the inter-chunk products (K~, Q~, K-) carry factors <= 1.
 //
-// Work split inside the workgroup (4 waves):
-//   wave R < C/16 owns sub-chunk R for the key-side work (loads, gate scan, operands,
-//   the row-R blocks of A and P, and the diagonal inverse X_RR = (I + A_RR)^{-1});
-//   every wave owns 16-column slices of the state tile for the state-side work.
-// Operands are staged in LDS; all contractions run on the matrix cores (bf16 inputs
-// with fp32 accumulation, or fp32 inputs for fp32 io).
+// Work split inside the workgroup (4 waves, 4 barriers per chunk):
+//   1. wave R < C/16 takes its 16-token sub-chunk from registers (prefetched during the
+//      previous chunk), scans the gate with DPP; all threads stage V and beta in LDS;
+//   2. per-channel boundary factors from the sub-chunk totals;
+//   3. wave R builds the gated operands of its sub-chunk (K~, Q~, K-^T, column operands);
+//   4. wave R computes the row-R blocks of A and P on the matrix cores and inverts its
+//      diagonal block A_RR by forward substitution; the next chunk's loads are issued;
+//   5. every wave updates its 16-column slices of the state tile (matrix cores).
 #pragma once
 
 #include <type_traits>
@@ -53,28 +55,91 @@ struct ChunkLayout {
     static constexpr int PADO = 16 / (int)sizeof(OT);  // 16-byte row padding
     static constexpr int LDO = DK + PADO;               // [C][DK] operand tiles
     static constexpr int LDT = C + PADO;                // [DK][C] transposed K-bar
-    static constexpr int LDA = C + 4;                   // fp32 [C][C]
+    static constexpr int LDM = C + PADO;                // [C][C] A and P in operand type
+    static constexpr int LDD = 16 + 4;                  // fp32 diagonal blocks [16][16]
+    static constexpr int LDV = DVT + PADO;              // [C][DVT] staged V (io type == operand type)
+    static constexpr int NSHIFT = NSUB >= 3 ? (NSUB - 1) * (NSUB - 2) / 2 : 0;  // pairs R >= I + 2
     static_assert(C % 16 == 0 && NSUB >= 1 && NSUB <= NW, "chunk must be 16, 32 or 64");
     static_assert(DK % 32 == 0 && DVT % 16 == 0, "head dims");
     static_assert(NSL <= NW || NSL % NW == 0, "d_v tile");
 
+    // raw-input prefetch: V tile in 16-byte pieces spread over the workgroup
+    static constexpr int V_PIECES = C * DVT * (int)sizeof(IO) / 16;
+    static constexpr int V_PER_THREAD = (V_PIECES + kChunkThreads - 1) / kChunkThreads;
+    static constexpr int V_ELEMS = 16 / (int)sizeof(IO);  // io elements per piece
+
     static constexpr size_t kOp = (size_t)C * LDO * sizeof(OT);
     static constexpr size_t oKb = 0;
-    static constexpr size_t oKt = oKb + kOp;
+    static constexpr size_t oKs = oKb + kOp;
+    static constexpr size_t oKt = oKs + (size_t)NSHIFT * 16 * LDO * sizeof(OT);
     static constexpr size_t oQt = oKt + kOp;
     static constexpr size_t oKbT = oQt + kOp;
     static constexpr size_t oA = oKbT + (size_t)DK * LDT * sizeof(OT);
-    static constexpr size_t oP = oA + (size_t)C * LDA * 4;
-    static constexpr size_t oTot = oP + (size_t)C * LDA * 4;
+    static constexpr size_t oP = oA + (size_t)C * LDM * sizeof(OT);
+    static constexpr size_t oAd = oP + (size_t)C * LDM * sizeof(OT);
+    static constexpr size_t oV = oAd + (size_t)NSUB * 16 * LDD * 4;
+    static constexpr size_t oTot = oV + (size_t)C * LDV * sizeof(OT);
     static constexpr size_t oEB = oTot + (size_t)NSUB * DK * 4;
     static constexpr size_t oED = oEB + (size_t)NSUB * DK * 4;
     static constexpr size_t oEC = oED + (size_t)NSUB * DK * 4;
     static constexpr size_t oSH = oEC + (size_t)NSUB * DK * 4;
-    static constexpr size_t oGam = oSH + (size_t)NSUB * NSUB * DK * 4;
+    static constexpr size_t oGam = oSH + (size_t)(NSHIFT > 0 ? NSHIFT : 1) * DK * 4;
     static constexpr size_t oBeta = oGam + (size_t)DK * 4;
     static constexpr size_t kBytes = oBeta + (size_t)C * 4;
     static constexpr bool kFits = kBytes <= 160 * 1024;
+
+    // index of the shifted column operand for block (R, I), R >= I + 2
+    __host__ __device__ static constexpr int shift_slot(int R, int I) { return (R - 2) * (R - 1) / 2 + I; }
 };
+
+// Raw inputs of one chunk, held in registers between the load and their use.
+template <typename IO, int DK, int DVT, int C>
+struct ChunkRaw {
+    using L = ChunkLayout<IO, DK, DVT, C>;
+    using KQ = typename std::conditional<L::BF, uint2, float4>::type;  // 4 io values
+    float4 g[L::KT];
+    KQ k[L::KT], q[L::KT];
+    uint4 v[L::V_PER_THREAD];
+    float beta;
+};
+
+template <typename IO, int DK, int DVT, int C>
+__device__ __forceinline__ void load_chunk(ChunkRaw<IO, DK, DVT, C> &raw, const FwdParams &p, int64_t tok0, int clen,
+                                           int h, int col0, int tid) {
+    using L = ChunkLayout<IO, DK, DVT, C>;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l16 = lane & 15, q4 = lane >> 4;
+    const int H = p.H;
+    // key side: wave R < NSUB reads its sub-chunk (rows past the end re-read the last row;
+    // their values are masked to zero when used)
+    if (wave < L::NSUB) {
+        const int r = min(16 * wave + l16, clen - 1);
+        const int64_t row = ((tok0 + r) * H + h) * (int64_t)DK + 4 * q4;
+        const float *gp = p.g + row;
+        const IO *kp = static_cast<const IO *>(p.k) + row;
+        const IO *qp = static_cast<const IO *>(p.q) + row;
+#pragma unroll
+        for (int ct = 0; ct < L::KT; ++ct) {
+            raw.g[ct] = *reinterpret_cast<const float4 *>(gp + 16 * ct);
+            using KQ = typename ChunkRaw<IO, DK, DVT, C>::KQ;
+            raw.k[ct] = *reinterpret_cast<const KQ *>(kp + 16 * ct);
+            raw.q[ct] = *reinterpret_cast<const KQ *>(qp + 16 * ct);
+        }
+    }
+    // V tile [C][DVT] in 16-byte pieces
+    constexpr int PPR = DVT / L::V_ELEMS;  // pieces per row
+#pragma unroll
+    for (int i = 0; i < L::V_PER_THREAD; ++i) {
+        const int piece = tid + kChunkThreads * i;
+        if (L::V_PIECES % kChunkThreads == 0 || piece < L::V_PIECES) {
+            const int r = min(piece / PPR, clen - 1);
+            const int cc = (piece % PPR) * L::V_ELEMS;
+            raw.v[i] = *reinterpret_cast<const uint4 *>(static_cast<const IO *>(p.v) +
+                                                        ((tok0 + r) * H + h) * (int64_t)p.dv + col0 + cc);
+        }
+    }
+    if (tid < C) raw.beta = p.beta[(tok0 + min(tid, clen - 1)) * H + h];
+}
 
 template <typename IO, int DK, int DVT, int C>
 __global__ void __launch_bounds__(kChunkThreads) kda_chunk_fwd_kernel(FwdParams p) {
@@ -82,16 +147,19 @@ __global__ void __launch_bounds__(kChunkThreads) kda_chunk_fwd_kernel(FwdParams 
     using OT = typename L::OT;
     constexpr bool BF = L::BF;
     constexpr int NSUB = L::NSUB, KT = L::KT, NSL = L::NSL, SPW = L::SPW;
-    constexpr int LDO = L::LDO, LDT = L::LDT, LDA = L::LDA;
+    constexpr int LDO = L::LDO, LDT = L::LDT, LDM = L::LDM, LDD = L::LDD, LDV = L::LDV;
     using Tr = IoTraits<IO>;
 
     __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
     OT *sKb = reinterpret_cast<OT *>(smem + L::oKb);
+    OT *sKs = reinterpret_cast<OT *>(smem + L::oKs);
     OT *sKt = reinterpret_cast<OT *>(smem + L::oKt);
     OT *sQt = reinterpret_cast<OT *>(smem + L::oQt);
     OT *sKbT = reinterpret_cast<OT *>(smem + L::oKbT);
-    float *sA = reinterpret_cast<float *>(smem + L::oA);
-    float *sP = reinterpret_cast<float *>(smem + L::oP);
+    OT *sA = reinterpret_cast<OT *>(smem + L::oA);
+    OT *sP = reinterpret_cast<OT *>(smem + L::oP);
+    float *sAd = reinterpret_cast<float *>(smem + L::oAd);
+    OT *sV = reinterpret_cast<OT *>(smem + L::oV);
     float *sTot = reinterpret_cast<float *>(smem + L::oTot);
     float *sEB = reinterpret_cast<float *>(smem + L::oEB);
     float *sED = reinterpret_cast<float *>(smem + L::oED);
@@ -101,12 +169,11 @@ __global__ void __launch_bounds__(kChunkThreads) kda_chunk_fwd_kernel(FwdParams 
     float *sBeta = reinterpret_cast<float *>(smem + L::oBeta);
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    // wave index as a scalar: every branch on it is uniform across the wave
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
     const int l16 = lane & 15, q4 = lane >> 4;
 
-    const IO *__restrict__ Q = static_cast<const IO *>(p.q);
-    const IO *__restrict__ K = static_cast<const IO *>(p.k);
-    const IO *__restrict__ V = static_cast<const IO *>(p.v);
     IO *__restrict__ O = static_cast<IO *>(p.out);
     const int H = p.H, DV = p.dv;
 
@@ -128,6 +195,7 @@ __global__ void __launch_bounds__(kChunkThreads) kda_chunk_fwd_kernel(FwdParams 
         start = (int64_t)n * p.T;
         len = p.T;
     }
+    const int col0 = tile * DVT;
 
     // ---- state slices owned by this wave: S[s][ct] holds rows 16ct+4q4+j of column col(s)
     f32x4 S[SPW][KT];
@@ -135,7 +203,7 @@ __global__ void __launch_bounds__(kChunkThreads) kda_chunk_fwd_kernel(FwdParams 
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
         const int sl = wave + L::NW * s;
-        const int col = tile * DVT + 16 * sl + l16;
+        const int col = col0 + 16 * sl + l16;
 #pragma unroll
         for (int ct = 0; ct < KT; ++ct) {
 #pragma unroll
@@ -146,40 +214,65 @@ __global__ void __launch_bounds__(kChunkThreads) kda_chunk_fwd_kernel(FwdParams 
         }
     }
 
+    // The state loads above must land before the chunk loop: otherwise the wait-count
+    // bookkeeping at the loop header still sees them pending and makes the state phase wait
+    // for every outstanding load, including the next chunk's prefetch.
+    __builtin_amdgcn_s_waitcnt(0);
+
+    ChunkRaw<IO, DK, DVT, C> raw;
+    if (len > 0) load_chunk<IO, DK, DVT, C>(raw, p, start, min(C, len), h, col0, tid);
+
     for (int c0 = 0; c0 < len; c0 += C) {
         const int clen = min(C, len - c0);
         const int64_t tok0 = start + c0;
 
-        // ================= phase 1: load the sub-chunk, scan the gate (log2 domain)
+        // ================= 1: gate scan (log2 domain), stage V and beta
         float G[KT][4], kr[KT][4], qr[KT][4];
         if (wave < NSUB) {
             const int R = wave;
-            const int r = 16 * R + l16;
-            const bool valid = r < clen;
-            const int64_t rowk = ((tok0 + r) * H + h) * (int64_t)DK;
+            const bool valid = 16 * R + l16 < clen;
 #pragma unroll
             for (int ct = 0; ct < KT; ++ct) {
                 const int c = 16 * ct + 4 * q4;
-                float4 gv = make_float4(0.f, 0.f, 0.f, 0.f), kv = gv, qv = gv;
-                if (valid) {
-                    gv = *reinterpret_cast<const float4 *>(p.g + rowk + c);
-                    kv = Tr::load4(K + rowk + c);
-                    qv = Tr::load4(Q + rowk + c);
+                const float4 gv = raw.g[ct];
+                float4 kv, qv;
+                if constexpr (BF) {
+                    kv = make_float4(bf16_lo(raw.k[ct].x), bf16_hi(raw.k[ct].x), bf16_lo(raw.k[ct].y), bf16_hi(raw.k[ct].y));
+                    qv = make_float4(bf16_lo(raw.q[ct].x), bf16_hi(raw.q[ct].x), bf16_lo(raw.q[ct].y), bf16_hi(raw.q[ct].y));
+                } else {
+                    kv = raw.k[ct];
+                    qv = raw.q[ct];
                 }
-                G[ct][0] = scan16_add(gv.x * kLog2e);
-                G[ct][1] = scan16_add(gv.y * kLog2e);
-                G[ct][2] = scan16_add(gv.z * kLog2e);
-                G[ct][3] = scan16_add(gv.w * kLog2e);
-                kr[ct][0] = kv.x; kr[ct][1] = kv.y; kr[ct][2] = kv.z; kr[ct][3] = kv.w;
-                qr[ct][0] = qv.x; qr[ct][1] = qv.y; qr[ct][2] = qv.z; qr[ct][3] = qv.w;
+                const float m = valid ? kLog2e : 0.f;
+                G[ct][0] = scan16_add(gv.x * m);
+                G[ct][1] = scan16_add(gv.y * m);
+                G[ct][2] = scan16_add(gv.z * m);
+                G[ct][3] = scan16_add(gv.w * m);
+                kr[ct][0] = valid ? kv.x : 0.f; kr[ct][1] = valid ? kv.y : 0.f;
+                kr[ct][2] = valid ? kv.z : 0.f; kr[ct][3] = valid ? kv.w : 0.f;
+                qr[ct][0] = valid ? qv.x : 0.f; qr[ct][1] = valid ? qv.y : 0.f;
+                qr[ct][2] = valid ? qv.z : 0.f; qr[ct][3] = valid ? qv.w : 0.f;
                 if (l16 == 15)
                     *reinterpret_cast<float4 *>(sTot + R * DK + c) = make_float4(G[ct][0], G[ct][1], G[ct][2], G[ct][3]);
             }
-            if (q4 == 0) sBeta[r] = valid ? p.beta[(tok0 + r) * H + h] : 0.f;
+        }
+        {
+            constexpr int PPR = DVT / L::V_ELEMS;
+#pragma unroll
+            for (int i = 0; i < L::V_PER_THREAD; ++i) {
+                const int piece = tid + kChunkThreads * i;
+                if (L::V_PIECES % kChunkThreads == 0 || piece < L::V_PIECES) {
+                    const int r = piece / PPR;
+                    const int cc = (piece % PPR) * L::V_ELEMS;
+                    const uint4 x = r < clen ? raw.v[i] : make_uint4(0u, 0u, 0u, 0u);
+                    *reinterpret_cast<uint4 *>(sV + r * LDV + cc) = x;
+                }
+            }
+            if (tid < C) sBeta[tid] = tid < clen ? raw.beta : 0.f;
         }
         __syncthreads();
 
-        // ================= phase 2: per-channel boundary factors
+        // ================= 2: per-channel boundary factors
         if (tid < DK) {
             const int c = tid;
             float tot[NSUB], bnd[NSUB + 1];
@@ -196,13 +289,14 @@ __global__ void __launch_bounds__(kChunkThreads) kda_chunk_fwd_kernel(FwdParams 
                 sED[R * DK + c] = fast_exp2(-tot[R]);
                 sEC[R * DK + c] = fast_exp2(gc - bnd[R + 1]);
 #pragma unroll
-                for (int I = 0; I + 1 < R; ++I) sSH[(R * NSUB + I) * DK + c] = fast_exp2(bnd[R] - bnd[I + 1]);
+                for (int I = 0; I + 2 <= R; ++I) sSH[L::shift_slot(R, I) * DK + c] = fast_exp2(bnd[R] - bnd[I + 1]);
             }
             sGam[c] = fast_exp2(gc);
         }
         __syncthreads();
 
-        // ================= phase 3: gated operands
+        // ================= 3: gated operands of sub-chunk R
+        Frag<BF> kdiag[KT];  // k * e^{b_R - G} (>= 1): column operand of the diagonal block
         if (wave < NSUB) {
             const int R = wave;
             const int r = 16 * R + l16;
@@ -211,11 +305,13 @@ __global__ void __launch_bounds__(kChunkThreads) kda_chunk_fwd_kernel(FwdParams 
                 const int c = 16 * ct + 4 * q4;
                 const float4 tot = *reinterpret_cast<const float4 *>(sTot + R * DK + c);
                 const float4 eb = *reinterpret_cast<const float4 *>(sEB + R * DK + c);
+                const float4 ed = *reinterpret_cast<const float4 *>(sED + R * DK + c);
                 const float4 ec = *reinterpret_cast<const float4 *>(sEC + R * DK + c);
                 const float tv[4] = {tot.x, tot.y, tot.z, tot.w};
                 const float ebv[4] = {eb.x, eb.y, eb.z, eb.w};
+                const float edv[4] = {ed.x, ed.y, ed.z, ed.w};
                 const float ecv[4] = {ec.x, ec.y, ec.z, ec.w};
-                float kb[4], kt[4], qt[4], kbar[4];
+                float kb[4], kt[4], qt[4], kbar[4], kd[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const float fr = fast_exp2(G[ct][j]);          // e^{G_r - b_R}     <= 1
@@ -223,102 +319,113 @@ __global__ void __launch_bounds__(kChunkThreads) kda_chunk_fwd_kernel(FwdParams 
                     const float krow = kr[ct][j] * fr;
                     const float qrow = qr[ct][j] * fr;
                     kb[j] = kr[ct][j] * fb;
+                    kd[j] = kb[j] * edv[j];
                     kt[j] = krow * ebv[j];
                     qt[j] = qrow * ebv[j];
                     kbar[j] = kb[j] * ecv[j];
-                    kr[ct][j] = krow;  // keep the row operands for the A / P blocks
+                    kr[ct][j] = krow;  // row operands of the A / P blocks
                     qr[ct][j] = qrow;
                 }
-                if constexpr (BF) {
-                    *reinterpret_cast<uint2 *>(sKb + r * LDO + c) = make_frag<true>(kb[0], kb[1], kb[2], kb[3]).v;
-                    *reinterpret_cast<uint2 *>(sKt + r * LDO + c) = make_frag<true>(kt[0], kt[1], kt[2], kt[3]).v;
-                    *reinterpret_cast<uint2 *>(sQt + r * LDO + c) = make_frag<true>(qt[0], qt[1], qt[2], qt[3]).v;
+                kdiag[ct] = make_frag<BF>(kd[0], kd[1], kd[2], kd[3]);
+                const Frag<BF> fkb = make_frag<BF>(kb[0], kb[1], kb[2], kb[3]);
+                *reinterpret_cast<decltype(fkb.v) *>(sKb + r * LDO + c) = fkb.v;
+                *reinterpret_cast<decltype(fkb.v) *>(sKt + r * LDO + c) = make_frag<BF>(kt[0], kt[1], kt[2], kt[3]).v;
+                *reinterpret_cast<decltype(fkb.v) *>(sQt + r * LDO + c) = make_frag<BF>(qt[0], qt[1], qt[2], qt[3]).v;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) sKbT[(c + j) * LDT + r] = f32_to_bf16(kbar[j]);
-                } else {
-                    *reinterpret_cast<float4 *>(sKb + r * LDO + c) = make_float4(kb[0], kb[1], kb[2], kb[3]);
-                    *reinterpret_cast<float4 *>(sKt + r * LDO + c) = make_float4(kt[0], kt[1], kt[2], kt[3]);
-                    *reinterpret_cast<float4 *>(sQt + r * LDO + c) = make_float4(qt[0], qt[1], qt[2], qt[3]);
+                for (int j = 0; j < 4; ++j) {
+                    if constexpr (BF) sKbT[(c + j) * LDT + r] = f32_to_bf16(kbar[j]);
+                    else sKbT[(c + j) * LDT + r] = kbar[j];
+                }
+                // column operands of blocks (R2, R) with R2 >= R + 2: k e^{b_{R2} - G}
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) sKbT[(c + j) * LDT + r] = kbar[j];
+                for (int R2 = 2; R2 < NSUB; ++R2) {
+                    if (R2 < R + 2) continue;
+                    const float4 sh = *reinterpret_cast<const float4 *>(sSH + L::shift_slot(R2, R) * DK + c);
+                    const Frag<BF> f = make_frag<BF>(kb[0] * sh.x, kb[1] * sh.y, kb[2] * sh.z, kb[3] * sh.w);
+                    *reinterpret_cast<decltype(f.v) *>(sKs + (L::shift_slot(R2, R) * 16 + l16) * LDO + c) = f.v;
                 }
             }
         }
         __syncthreads();
 
-        // ================= phase 4: row-R blocks of A and P (MFMA)
+        // ================= 4: row-R blocks of A and P, diagonal inverse; prefetch next chunk
         if (wave < NSUB) {
             const int R = wave;
+            Frag<BF> ka[KT], qa[KT];
+#pragma unroll
+            for (int ct = 0; ct < KT; ++ct) {
+                ka[ct] = make_frag<BF>(kr[ct][0], kr[ct][1], kr[ct][2], kr[ct][3]);
+                qa[ct] = make_frag<BF>(qr[ct][0], qr[ct][1], qr[ct][2], qr[ct][3]);
+            }
 #pragma unroll
             for (int I = 0; I < NSUB; ++I) {
                 if (I > R) break;
                 f32x4 accA = zero4(), accP = zero4();
+                const OT *colp = (I == R - 1) ? sKb + (16 * I + l16) * LDO
+                                              : sKs + (L::shift_slot(R < 2 ? 2 : R, I) * 16 + l16) * LDO;
 #pragma unroll
                 for (int ct = 0; ct < KT; ct += 2) {
-                    Frag<BF> ka[2], qa[2], kb[2];
-#pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        const int c = 16 * (ct + u) + 4 * q4;
-                        float sh[4] = {1.f, 1.f, 1.f, 1.f};
-                        if (I == R) {
-                            const float4 e = *reinterpret_cast<const float4 *>(sED + R * DK + c);
-                            sh[0] = e.x; sh[1] = e.y; sh[2] = e.z; sh[3] = e.w;
-                        } else if (I + 1 < R) {
-                            const float4 e = *reinterpret_cast<const float4 *>(sSH + (R * NSUB + I) * DK + c);
-                            sh[0] = e.x; sh[1] = e.y; sh[2] = e.z; sh[3] = e.w;
-                        }
-                        const float *kk = kr[ct + u];
-                        const float *qq = qr[ct + u];
-                        ka[u] = make_frag<BF>(kk[0] * sh[0], kk[1] * sh[1], kk[2] * sh[2], kk[3] * sh[3]);
-                        qa[u] = make_frag<BF>(qq[0] * sh[0], qq[1] * sh[1], qq[2] * sh[2], qq[3] * sh[3]);
-                        kb[u] = lds_frag(sKb + (16 * I + l16) * LDO + c);
+                    Frag<BF> b0, b1;
+                    if (I == R) {
+                        b0 = kdiag[ct];
+                        b1 = kdiag[ct + 1];
+                    } else {
+                        b0 = lds_frag(colp + 16 * ct + 4 * q4);
+                        b1 = lds_frag(colp + 16 * (ct + 1) + 4 * q4);
                     }
-                    mma32(accA, ka[0], ka[1], kb[0], kb[1]);
-                    mma32(accP, qa[0], qa[1], kb[0], kb[1]);
+                    mma32(accA, ka[ct], ka[ct + 1], b0, b1);
+                    mma32(accP, qa[ct], qa[ct + 1], b0, b1);
                 }
                 // accumulator: rows rr = 4*q4 + j of block R, column ii = l16 of block I
+                float av[4], pv[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int rr = 4 * q4 + j, ii = l16;
-                    float a = accA[j] * sBeta[16 * R + rr];
-                    float pp = accP[j];
+                    av[j] = accA[j] * sBeta[16 * R + rr];
+                    pv[j] = accP[j];
                     if (I == R) {
-                        if (ii >= rr) a = 0.f;
-                        if (ii > rr) pp = 0.f;
+                        if (ii >= rr) av[j] = 0.f;
+                        if (ii > rr) pv[j] = 0.f;
                     }
-                    sA[(16 * R + rr) * LDA + 16 * I + ii] = a;
-                    sP[(16 * R + rr) * LDA + 16 * I + ii] = pp;
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int rr = 4 * q4 + j;
+                    if constexpr (BF) {
+                        sP[(16 * R + rr) * LDM + 16 * I + l16] = f32_to_bf16(pv[j]);
+                        if (I != R) sA[(16 * R + rr) * LDM + 16 * I + l16] = f32_to_bf16(av[j]);
+                    } else {
+                        sP[(16 * R + rr) * LDM + 16 * I + l16] = pv[j];
+                        if (I != R) sA[(16 * R + rr) * LDM + 16 * I + l16] = av[j];
+                    }
+                    if (I == R) sAd[(R * 16 + rr) * LDD + l16] = av[j];
                 }
             }
-        }
-        __syncthreads();
-
-        // ================= phase 5: diagonal inverses X_RR = (I + A_RR)^{-1}, row by row
-        if (wave < NSUB) {
-            const int R = wave;
-            float *Ab = sA + (16 * R) * LDA + 16 * R;
+            // X_RR = (I + A_RR)^{-1}, row by row: lane l16 owns column l16 (same wave wrote A_RR)
+            float *Ab = sAd + R * 16 * LDD;
             const int jc = l16;
             float x[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 float s = (r == jc) ? 1.f : 0.f;
 #pragma unroll
-                for (int m = 0; m < r; ++m) s -= Ab[r * LDA + m] * x[m];
+                for (int m = 0; m < r; ++m) s -= Ab[r * LDD + m] * x[m];
                 x[r] = s;
             }
             if (q4 == 0) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) Ab[r * LDA + jc] = x[r];
+                for (int r = 0; r < 16; ++r) Ab[r * LDD + jc] = x[r];
             }
         }
+        if (c0 + C < len) load_chunk<IO, DK, DVT, C>(raw, p, tok0 + C, min(C, len - c0 - C), h, col0, tid);
         __syncthreads();
 
-        // ================= phase 6: state slices (each wave: 16-column slices of the tile)
+        // ================= 5: state slices (each wave: 16-column slices of the tile)
 #pragma unroll
         for (int s = 0; s < SPW; ++s) {
             const int sl = wave + L::NW * s;
             if (sl >= NSL) break;
-            const int col = tile * DVT + 16 * sl + l16;
+            const int col = col0 + 16 * sl + l16;
 
             Frag<BF> Sb[KT];
 #pragma unroll
@@ -328,18 +435,19 @@ __global__ void __launch_bounds__(kChunkThreads) kda_chunk_fwd_kernel(FwdParams 
 #pragma unroll
             for (int rt = 0; rt < NSUB; ++rt) {
                 f32x4 ak = zero4(), ao = zero4();
+                const OT *kt = sKt + (16 * rt + l16) * LDO + 4 * q4;
+                const OT *qt = sQt + (16 * rt + l16) * LDO + 4 * q4;
 #pragma unroll
                 for (int ct = 0; ct < KT; ct += 2) {
-                    const int cA = 16 * ct + 4 * q4, cB = cA + 16;
-                    const OT *kt = sKt + (16 * rt + l16) * LDO;
-                    const OT *qt = sQt + (16 * rt + l16) * LDO;
-                    mma32(ak, lds_frag(kt + cA), lds_frag(kt + cB), Sb[ct], Sb[ct + 1]);
-                    mma32(ao, lds_frag(qt + cA), lds_frag(qt + cB), Sb[ct], Sb[ct + 1]);
+                    mma32(ak, lds_frag(kt + 16 * ct), lds_frag(kt + 16 * ct + 16), Sb[ct], Sb[ct + 1]);
+                    mma32(ao, lds_frag(qt + 16 * ct), lds_frag(qt + 16 * ct + 16), Sb[ct], Sb[ct + 1]);
                 }
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int r = 16 * rt + 4 * q4 + j;
-                    const float vv = (r < clen) ? Tr::load1(V + ((tok0 + r) * H + h) * (int64_t)DV + col) : 0.f;
+                    float vv;
+                    if constexpr (BF) vv = bf16_to_f32(sV[r * LDV + 16 * sl + l16]);
+                    else vv = sV[r * LDV + 16 * sl + l16];
                     Y[rt][j] = sBeta[r] * (vv - ak[j]);
                 }
                 Oa[rt] = ao;
@@ -351,10 +459,18 @@ __global__ void __launch_bounds__(kChunkThreads) kda_chunk_fwd_kernel(FwdParams 
             for (int R = 0; R < NSUB; ++R) {
                 f32x4 z = Y[R];
 #pragma unroll
-                for (int I = 0; I < R; ++I)
-                    mma16(z, lds_frag_f32<BF>(sA + (16 * R + l16) * LDA + 16 * I + 4 * q4, -1.f), D[I]);
+                for (int I = 0; I < R; ++I) {
+                    Frag<BF> a = lds_frag(sA + (16 * R + l16) * LDM + 16 * I + 4 * q4);
+                    if constexpr (BF) {
+                        a.v.x ^= 0x80008000u;
+                        a.v.y ^= 0x80008000u;
+                    } else {
+                        a.v = make_float4(-a.v.x, -a.v.y, -a.v.z, -a.v.w);
+                    }
+                    mma16(z, a, D[I]);
+                }
                 f32x4 d = zero4();
-                mma16(d, lds_frag_f32<BF>(sA + (16 * R + l16) * LDA + 16 * R + 4 * q4), frag_from_acc<BF>(z));
+                mma16(d, lds_frag_f32<BF>(sAd + (16 * R + l16) * LDD + 4 * q4), frag_from_acc<BF>(z));
                 D[R] = frag_from_acc<BF>(d);
             }
 
@@ -362,8 +478,7 @@ __global__ void __launch_bounds__(kChunkThreads) kda_chunk_fwd_kernel(FwdParams 
 #pragma unroll
             for (int R = 0; R < NSUB; ++R) {
 #pragma unroll
-                for (int I = 0; I <= R; ++I)
-                    mma16(Oa[R], lds_frag_f32<BF>(sP + (16 * R + l16) * LDA + 16 * I + 4 * q4), D[I]);
+                for (int I = 0; I <= R; ++I) mma16(Oa[R], lds_frag(sP + (16 * R + l16) * LDM + 16 * I + 4 * q4), D[I]);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int r = 16 * R + 4 * q4 + j;
@@ -381,7 +496,8 @@ __global__ void __launch_bounds__(kChunkThreads) kda_chunk_fwd_kernel(FwdParams 
                 S[s][ct][3] *= gm.w;
                 const OT *kb = sKbT + (16 * ct + l16) * LDT + 4 * q4;
 #pragma unroll
-                for (int I = 0; I + 1 < NSUB; I += 2) mma32(S[s][ct], lds_frag(kb + 16 * I), lds_frag(kb + 16 * (I + 1)), D[I], D[I + 1]);
+                for (int I = 0; I + 1 < NSUB; I += 2)
+                    mma32(S[s][ct], lds_frag(kb + 16 * I), lds_frag(kb + 16 * (I + 1)), D[I], D[I + 1]);
                 if constexpr (NSUB % 2 == 1) mma16(S[s][ct], lds_frag(kb + 16 * (NSUB - 1)), D[NSUB - 1]);
             }
         }
@@ -393,7 +509,7 @@ __global__ void __launch_bounds__(kChunkThreads) kda_chunk_fwd_kernel(FwdParams 
         for (int s = 0; s < SPW; ++s) {
             const int sl = wave + L::NW * s;
             if (sl >= NSL) break;
-            const int col = tile * DVT + 16 * sl + l16;
+            const int col = col0 + 16 * sl + l16;
 #pragma unroll
             for (int ct = 0; ct < KT; ++ct) {
 #pragma unroll

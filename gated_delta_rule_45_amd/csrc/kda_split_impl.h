@@ -1,0 +1,707 @@
+// Two-pass chunkwise KDA forward for gfx950.
+//
+// Pass 1 (kda_prep_kernel): one workgroup per (chunk, head), all in parallel.  It does
+// every step that does not depend on the recurrent state (Kimi Linear summary page,
+// "Chunkwise parallel algorithm" and "Less compute than general DPLR" sections):
+// in-chunk cumulative gate, gated operands, the two C x C matrices A (from k, k) and
+// P (from q, k), and the UT transform T = (I + A)^{-1} Diag(beta) with the
+// lower-triangular inverse computed by forward substitution (16 x 16 diagonal blocks row
+// by row, off-diagonal blocks block by block).  It writes one record per chunk-head:
+//
+//   K~ = k e^{G},  Q~ = q e^{G}   [C x d_k]   A operands of K~ S and Q~ S
+//   K-^T, K- = k e^{G_C - G}     [d_k x C]   A operand of K-^T D
+//   T, P                          [C x C]     lower-triangular, A operands of T Y and P D
+//   Gamma = e^{G_C}               [d_k]       per-channel chunk decay
+//
+// in matrix-core fragment order: each 16 x 32 operand tile is 64 lanes x 8 values, so the
+// scan reads every fragment with one 16-byte load per lane.
+//
+// Pass 2 (kda_scan_kernel): one workgroup per (sequence, head, d_v tile); each wave owns a
+// 16-column slice of the fp32 state.  Per chunk, with the record staged in LDS by
+// asynchronous global->LDS copies issued one chunk ahead:
+//
+//   Y = V - K~ S        D = T Y         O = scale (Q~ S + P D)        S <- Gamma S + K-^T D
+//
+// (D = T (V - K~ S) equals the WY form U - W S with W = T K~ and U = T V.)
+#pragma once
+
+#include <type_traits>
+
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+// ------------------------------------------------------------------ record --
+template <typename IO, int DK, int C>
+struct SplitRecord {
+    static constexpr bool BF = IoTraits<IO>::kBf16;
+    static constexpr int NSUB = C / 16;
+    static constexpr int KT = DK / 16;
+    static constexpr int NPAIR = (NSUB + 1) / 2;  // 32-wide token tile pairs
+    static constexpr int FRAG_BYTES = BF ? 8 : 16;
+    static constexpr int PAIR_BYTES = 2 * FRAG_BYTES;
+    static constexpr int TILE_BYTES = 64 * PAIR_BYTES;  // one 16 x 32 operand tile
+    static constexpr size_t oKt = 0;
+    static constexpr size_t oQt = oKt + (size_t)NSUB * (KT / 2) * TILE_BYTES;
+    static constexpr size_t oKbT = oQt + (size_t)NSUB * (KT / 2) * TILE_BYTES;
+    static constexpr size_t oT = oKbT + (size_t)KT * NPAIR * TILE_BYTES;
+    static constexpr size_t oP = oT + (size_t)NSUB * NPAIR * TILE_BYTES;
+    static constexpr size_t oGam = oP + (size_t)NSUB * NPAIR * TILE_BYTES;
+    static constexpr size_t kRaw = oGam + (size_t)DK * 4;
+    static constexpr size_t kBytes = (kRaw + 1023) / 1024 * 1024;  // whole 1 KB copy units
+    static_assert(KT % 2 == 0, "d_k must be a multiple of 32");
+};
+
+// store one lane's two 16-wide fragments of a 16 x 32 tile
+template <bool BF>
+__device__ __forceinline__ void store_pair(char *tile, int lane, const Frag<BF> &a, const Frag<BF> &b) {
+    if constexpr (BF) {
+        *reinterpret_cast<uint4 *>(tile + lane * 16) = make_uint4(a.v.x, a.v.y, b.v.x, b.v.y);
+    } else {
+        *reinterpret_cast<float4 *>(tile + lane * 32) = a.v;
+        *reinterpret_cast<float4 *>(tile + lane * 32 + 16) = b.v;
+    }
+}
+template <bool BF>
+__device__ __forceinline__ void load_pair(const char *tile, int lane, Frag<BF> &a, Frag<BF> &b) {
+    if constexpr (BF) {
+        const uint4 x = *reinterpret_cast<const uint4 *>(tile + lane * 16);
+        a.v = make_uint2(x.x, x.y);
+        b.v = make_uint2(x.z, x.w);
+    } else {
+        a.v = *reinterpret_cast<const float4 *>(tile + lane * 32);
+        b.v = *reinterpret_cast<const float4 *>(tile + lane * 32 + 16);
+    }
+}
+
+// Sequence n and chunk c of global chunk index gidx; false if gidx is past the last chunk.
+__device__ __forceinline__ bool locate_chunk(const FwdParams &p, const int32_t *chunk_off, int C, int64_t gidx,
+                                             int &n, int &c, int64_t &start, int &len) {
+    if (p.cu) {
+        if (gidx >= chunk_off[p.num_seqs]) return false;
+        int lo = 0, hi = p.num_seqs - 1;  // largest n with chunk_off[n] <= gidx
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (chunk_off[mid] <= gidx) lo = mid;
+            else hi = mid - 1;
+        }
+        n = lo;
+        c = (int)(gidx - chunk_off[n]);
+        start = p.cu[n];
+        len = p.cu[n + 1] - p.cu[n];
+    } else {
+        const int per = (p.T + C - 1) / C;
+        if (per == 0 || gidx >= (int64_t)p.num_seqs * per) return false;
+        n = (int)(gidx / per);
+        c = (int)(gidx % per);
+        start = (int64_t)n * p.T;
+        len = p.T;
+    }
+    return true;
+}
+
+__device__ __forceinline__ int64_t first_chunk(const FwdParams &p, const int32_t *chunk_off, int C, int n) {
+    if (p.cu) return chunk_off[n];
+    return (int64_t)n * ((p.T + C - 1) / C);
+}
+
+// ------------------------------------------------------------------- plan ----
+// chunk_off[n] = sum_{m<n} ceil(len_m / C) for a packed batch (one workgroup).
+static __global__ void __launch_bounds__(256) kda_plan_kernel(const int32_t *__restrict__ cu, int32_t num_seqs, int32_t C,
+                                                       int32_t *__restrict__ chunk_off) {
+    __shared__ int32_t part[256];
+    const int t = threadIdx.x;
+    const int per = (num_seqs + 255) / 256;
+    const int n0 = min(t * per, num_seqs), n1 = min(n0 + per, num_seqs);
+    int32_t s = 0;
+    for (int n = n0; n < n1; ++n) s += (cu[n + 1] - cu[n] + C - 1) / C;
+    part[t] = s;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {  // inclusive scan of the partial sums
+        const int32_t x = t >= off ? part[t - off] : 0;
+        __syncthreads();
+        part[t] += x;
+        __syncthreads();
+    }
+    int32_t run = part[t] - s;
+    for (int n = n0; n < n1; ++n) {
+        chunk_off[n] = run;
+        run += (cu[n + 1] - cu[n] + C - 1) / C;
+    }
+    if (t == 255) chunk_off[num_seqs] = part[255];
+}
+
+// ------------------------------------------------------------------- prep ----
+template <typename IO, int DK, int C>
+struct PrepLayout {
+    using Rec = SplitRecord<IO, DK, C>;
+    static constexpr bool BF = Rec::BF;
+    using OT = typename std::conditional<BF, uint16_t, float>::type;
+    static constexpr int NSUB = C / 16, KT = DK / 16;
+    static constexpr int PADO = 16 / (int)sizeof(OT);
+    static constexpr int LDO = DK + PADO;
+    static constexpr int LDT = C + PADO;
+    static constexpr int LDX = C + 4;
+    static constexpr int NSHIFT = NSUB >= 3 ? (NSUB - 1) * (NSUB - 2) / 2 : 0;
+    static constexpr size_t oKb = 0;
+    static constexpr size_t oKs = oKb + (size_t)C * LDO * sizeof(OT);
+    static constexpr size_t oKbT = oKs + (size_t)NSHIFT * 16 * LDO * sizeof(OT);
+    static constexpr size_t oX = oKbT + (size_t)DK * LDT * sizeof(OT);
+    static constexpr size_t oTot = oX + (size_t)C * LDX * 4;
+    static constexpr size_t oEB = oTot + (size_t)NSUB * DK * 4;
+    static constexpr size_t oED = oEB + (size_t)NSUB * DK * 4;
+    static constexpr size_t oEC = oED + (size_t)NSUB * DK * 4;
+    static constexpr size_t oSH = oEC + (size_t)NSUB * DK * 4;
+    static constexpr size_t oBeta = oSH + (size_t)(NSHIFT > 0 ? NSHIFT : 1) * DK * 4;
+    static constexpr size_t kBytes = oBeta + (size_t)C * 4;
+    __host__ __device__ static constexpr int shift_slot(int R, int I) { return (R - 2) * (R - 1) / 2 + I; }
+};
+
+template <typename IO, int DK, int C>
+__global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_t *__restrict__ chunk_off,
+                                                       char *__restrict__ records) {
+    using L = PrepLayout<IO, DK, C>;
+    using Rec = typename L::Rec;
+    using OT = typename L::OT;
+    constexpr bool BF = L::BF;
+    constexpr int NSUB = L::NSUB, KT = L::KT, NPAIR = Rec::NPAIR;
+    constexpr int LDO = L::LDO, LDT = L::LDT, LDX = L::LDX;
+    using Tr = IoTraits<IO>;
+
+    __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
+    OT *sKb = reinterpret_cast<OT *>(smem + L::oKb);
+    OT *sKs = reinterpret_cast<OT *>(smem + L::oKs);
+    OT *sKbT = reinterpret_cast<OT *>(smem + L::oKbT);
+    float *sX = reinterpret_cast<float *>(smem + L::oX);
+    float *sTot = reinterpret_cast<float *>(smem + L::oTot);
+    float *sEB = reinterpret_cast<float *>(smem + L::oEB);
+    float *sED = reinterpret_cast<float *>(smem + L::oED);
+    float *sEC = reinterpret_cast<float *>(smem + L::oEC);
+    float *sSH = reinterpret_cast<float *>(smem + L::oSH);
+    float *sBeta = reinterpret_cast<float *>(smem + L::oBeta);
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l16 = lane & 15, q4 = lane >> 4;
+    const int H = p.H;
+    const int h = (int)(blockIdx.x % H);
+    const int64_t gidx = blockIdx.x / H;
+    int n, c;
+    int64_t start;
+    int len;
+    if (!locate_chunk(p, chunk_off, C, gidx, n, c, start, len)) return;
+    const int clen = min(C, len - c * C);
+    const int64_t tok0 = start + (int64_t)c * C;
+    char *rec = records + (size_t)(gidx * H + h) * Rec::kBytes;
+
+    // ================= 1: load sub-chunk, scan the gate (log2 domain)
+    float G[KT][4], kr[KT][4], qr[KT][4];
+    if (wave < NSUB) {
+        const int R = wave;
+        const bool valid = 16 * R + l16 < clen;
+        const int r = min(16 * R + l16, clen - 1);
+        const int64_t row = ((tok0 + r) * H + h) * (int64_t)DK + 4 * q4;
+        const float m = valid ? kLog2e : 0.f;
+#pragma unroll
+        for (int ct = 0; ct < KT; ++ct) {
+            const float4 gv = *reinterpret_cast<const float4 *>(p.g + row + 16 * ct);
+            const float4 kv = Tr::load4(static_cast<const IO *>(p.k) + row + 16 * ct);
+            const float4 qv = Tr::load4(static_cast<const IO *>(p.q) + row + 16 * ct);
+            G[ct][0] = gv.x * m; G[ct][1] = gv.y * m; G[ct][2] = gv.z * m; G[ct][3] = gv.w * m;
+            kr[ct][0] = valid ? kv.x : 0.f; kr[ct][1] = valid ? kv.y : 0.f;
+            kr[ct][2] = valid ? kv.z : 0.f; kr[ct][3] = valid ? kv.w : 0.f;
+            qr[ct][0] = valid ? qv.x : 0.f; qr[ct][1] = valid ? qv.y : 0.f;
+            qr[ct][2] = valid ? qv.z : 0.f; qr[ct][3] = valid ? qv.w : 0.f;
+        }
+#pragma unroll
+        for (int ct = 0; ct < KT; ++ct) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) G[ct][j] = scan16_add(G[ct][j]);
+            if (l16 == 15)
+                *reinterpret_cast<float4 *>(sTot + R * DK + 16 * ct + 4 * q4) =
+                    make_float4(G[ct][0], G[ct][1], G[ct][2], G[ct][3]);
+        }
+    }
+    if (tid < C) sBeta[tid] = tid < clen ? p.beta[(tok0 + tid) * H + h] : 0.f;
+    __syncthreads();
+
+    // ================= 2: per-channel boundary factors; Gamma = e^{G_C}
+    if (tid < DK) {
+        const int ch = tid;
+        float tot[NSUB], bnd[NSUB + 1];
+        bnd[0] = 0.f;
+#pragma unroll
+        for (int R = 0; R < NSUB; ++R) {
+            tot[R] = sTot[R * DK + ch];
+            bnd[R + 1] = bnd[R] + tot[R];
+        }
+        const float gc = bnd[NSUB];
+#pragma unroll
+        for (int R = 0; R < NSUB; ++R) {
+            sEB[R * DK + ch] = fast_exp2(bnd[R]);
+            sED[R * DK + ch] = fast_exp2(-tot[R]);
+            sEC[R * DK + ch] = fast_exp2(gc - bnd[R + 1]);
+#pragma unroll
+            for (int I = 0; I + 2 <= R; ++I) sSH[L::shift_slot(R, I) * DK + ch] = fast_exp2(bnd[R] - bnd[I + 1]);
+        }
+        reinterpret_cast<float *>(rec + Rec::oGam)[ch] = fast_exp2(gc);
+    }
+    __syncthreads();
+
+    // ================= 3: gated operands; K~ and Q~ go straight to the record
+    Frag<BF> kdiag[KT];
+    if (wave < NSUB) {
+        const int R = wave;
+        const int r = 16 * R + l16;
+        Frag<BF> fkt[KT], fqt[KT];
+#pragma unroll
+        for (int ct = 0; ct < KT; ++ct) {
+            const int ch = 16 * ct + 4 * q4;
+            const float4 tot = *reinterpret_cast<const float4 *>(sTot + R * DK + ch);
+            const float4 eb = *reinterpret_cast<const float4 *>(sEB + R * DK + ch);
+            const float4 ed = *reinterpret_cast<const float4 *>(sED + R * DK + ch);
+            const float4 ec = *reinterpret_cast<const float4 *>(sEC + R * DK + ch);
+            const float tv[4] = {tot.x, tot.y, tot.z, tot.w};
+            const float ebv[4] = {eb.x, eb.y, eb.z, eb.w};
+            const float edv[4] = {ed.x, ed.y, ed.z, ed.w};
+            const float ecv[4] = {ec.x, ec.y, ec.z, ec.w};
+            float kb[4], kt[4], qt[4], kbar[4], kd[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float fr = fast_exp2(G[ct][j]);          // e^{G_r - b_R}     <= 1
+                const float fb = fast_exp2(tv[j] - G[ct][j]);  // e^{b_{R+1} - G_r} <= 1
+                const float krow = kr[ct][j] * fr;
+                const float qrow = qr[ct][j] * fr;
+                kb[j] = kr[ct][j] * fb;
+                kd[j] = kb[j] * edv[j];
+                kt[j] = krow * ebv[j];
+                qt[j] = qrow * ebv[j];
+                kbar[j] = kb[j] * ecv[j];
+                kr[ct][j] = krow;
+                qr[ct][j] = qrow;
+            }
+            kdiag[ct] = make_frag<BF>(kd[0], kd[1], kd[2], kd[3]);
+            fkt[ct] = make_frag<BF>(kt[0], kt[1], kt[2], kt[3]);
+            fqt[ct] = make_frag<BF>(qt[0], qt[1], qt[2], qt[3]);
+            const Frag<BF> fkb = make_frag<BF>(kb[0], kb[1], kb[2], kb[3]);
+            *reinterpret_cast<decltype(fkb.v) *>(sKb + r * LDO + ch) = fkb.v;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (BF) sKbT[(ch + j) * LDT + r] = f32_to_bf16(kbar[j]);
+                else sKbT[(ch + j) * LDT + r] = kbar[j];
+            }
+#pragma unroll
+            for (int R2 = 2; R2 < NSUB; ++R2) {
+                if (R2 < R + 2) continue;
+                const float4 sh = *reinterpret_cast<const float4 *>(sSH + L::shift_slot(R2, R) * DK + ch);
+                const Frag<BF> f = make_frag<BF>(kb[0] * sh.x, kb[1] * sh.y, kb[2] * sh.z, kb[3] * sh.w);
+                *reinterpret_cast<decltype(f.v) *>(sKs + (L::shift_slot(R2, R) * 16 + l16) * LDO + ch) = f.v;
+            }
+        }
+#pragma unroll
+        for (int kp = 0; kp < KT / 2; ++kp) {
+            store_pair<BF>(rec + Rec::oKt + (size_t)(R * (KT / 2) + kp) * Rec::TILE_BYTES, lane, fkt[2 * kp], fkt[2 * kp + 1]);
+            store_pair<BF>(rec + Rec::oQt + (size_t)(R * (KT / 2) + kp) * Rec::TILE_BYTES, lane, fqt[2 * kp], fqt[2 * kp + 1]);
+        }
+    }
+    __syncthreads();
+
+    // ================= 4: row-R blocks of A (to LDS) and P (to the record); X_RR
+    if (wave < NSUB) {
+        const int R = wave;
+        Frag<BF> ka[KT], qa[KT];
+#pragma unroll
+        for (int ct = 0; ct < KT; ++ct) {
+            ka[ct] = make_frag<BF>(kr[ct][0], kr[ct][1], kr[ct][2], kr[ct][3]);
+            qa[ct] = make_frag<BF>(qr[ct][0], qr[ct][1], qr[ct][2], qr[ct][3]);
+        }
+        Frag<BF> pf[2 * NPAIR];
+#pragma unroll
+        for (int I = 0; I < 2 * NPAIR; ++I) pf[I] = make_frag<BF>(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int I = 0; I < NSUB; ++I) {
+            if (I > R) break;
+            const OT *colp = (I == R - 1) ? sKb + (16 * I + l16) * LDO
+                                          : sKs + (L::shift_slot(R < 2 ? 2 : R, I) * 16 + l16) * LDO;
+            f32x4 accA = zero4(), accPt = zero4();
+#pragma unroll
+            for (int ct = 0; ct < KT; ct += 2) {
+                Frag<BF> b0, b1;
+                if (I == R) {
+                    b0 = kdiag[ct];
+                    b1 = kdiag[ct + 1];
+                } else {
+                    b0 = lds_frag(colp + 16 * ct + 4 * q4);
+                    b1 = lds_frag(colp + 16 * (ct + 1) + 4 * q4);
+                }
+                mma32(accA, ka[ct], ka[ct + 1], b0, b1);   // A_RI:  rows r, columns i
+                mma32(accPt, b0, b1, qa[ct], qa[ct + 1]);  // P_RI^T: rows i, columns r
+            }
+            // A_RI: lane holds rows rr = 4*q4 + j, column l16
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int rr = 4 * q4 + j;
+                float a = accA[j] * sBeta[16 * R + rr];
+                if (I == R && l16 >= rr) a = 0.f;
+                sX[(16 * R + rr) * LDX + 16 * I + l16] = a;
+            }
+            // P_RI^T accumulator = P_RI operand fragment: row l16, columns 4*q4 + j
+            float pv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pv[j] = (I == R && 4 * q4 + j > l16) ? 0.f : accPt[j];
+            pf[I] = make_frag<BF>(pv[0], pv[1], pv[2], pv[3]);
+        }
+#pragma unroll
+        for (int pp = 0; pp < NPAIR; ++pp)
+            store_pair<BF>(rec + Rec::oP + (size_t)(R * NPAIR + pp) * Rec::TILE_BYTES, lane, pf[2 * pp], pf[2 * pp + 1]);
+
+        // X_RR = (I + A_RR)^{-1}, row by row; lane l16 owns column l16 (this wave wrote A_RR)
+        float *Ab = sX + (16 * R) * LDX + 16 * R;
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float s = (r == l16) ? 1.f : 0.f;
+#pragma unroll
+            for (int m = 0; m < r; ++m) s -= Ab[r * LDX + m] * x[m];
+            x[r] = s;
+        }
+        if (q4 == 0) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Ab[r * LDX + l16] = x[r];
+        }
+    }
+    __syncthreads();
+
+    // ================= 5: off-diagonal blocks of X, one block diagonal at a time:
+    // X_RI = -X_RR sum_{J=I}^{R-1} A_RJ X_JI  (fp32 matrix-core products).
+    // sX holds A_RI below the diagonal (kept), X_RR on the diagonal, and X_RI transposed in
+    // the otherwise unused upper block (I, R): X_RI[a][b] at sX[(16I + b) * LDX + 16R + a].
+#pragma unroll
+    for (int lvl = 1; lvl < NSUB; ++lvl) {
+        const int R = wave;
+        if (R >= lvl && R < NSUB) {
+            const int I = R - lvl;
+            f32x4 m = zero4();
+#pragma unroll
+            for (int J = 0; J < NSUB; ++J) {
+                if (J < I || J >= R) continue;
+                const Frag<false> a = lds_frag(sX + (16 * R + l16) * LDX + 16 * J + 4 * q4);  // A_RJ rows
+                Frag<false> b;  // X_JI: rows 4*q4 + j, column l16
+                if (J == I) {
+                    const float *xd = sX + (16 * I + 4 * q4) * LDX + 16 * I + l16;
+                    b.v = make_float4(xd[0], xd[LDX], xd[2 * LDX], xd[3 * LDX]);
+                } else {
+                    b = lds_frag(sX + (16 * I + l16) * LDX + 16 * J + 4 * q4);
+                }
+                mma16(m, a, b);
+            }
+            f32x4 xo = zero4();
+            const Frag<false> xrr = lds_frag(sX + (16 * R + l16) * LDX + 16 * R + 4 * q4);
+            Frag<false> mb;
+            mb.v = make_float4(-m[0], -m[1], -m[2], -m[3]);
+            mma16(xo, xrr, mb);
+            // xo holds X_RI rows 4*q4 + j, column l16: store transposed in block (I, R)
+            *reinterpret_cast<float4 *>(sX + (16 * I + l16) * LDX + 16 * R + 4 * q4) = make_float4(xo[0], xo[1], xo[2], xo[3]);
+        }
+        __syncthreads();
+    }
+
+    // ================= 6: T = X Diag(beta) and K-^T fragments to the record
+    if (wave < NSUB) {
+        const int R = wave;
+#pragma unroll
+        for (int pp = 0; pp < NPAIR; ++pp) {
+            Frag<BF> f[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int I = 2 * pp + u;
+                float4 xv = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (I == R) {
+                    xv = *reinterpret_cast<const float4 *>(sX + (16 * R + l16) * LDX + 16 * R + 4 * q4);
+                } else if (I < R) {  // X_RI[l16][4*q4 + j], stored transposed
+                    const float *xt = sX + (16 * I + 4 * q4) * LDX + 16 * R + l16;
+                    xv = make_float4(xt[0], xt[LDX], xt[2 * LDX], xt[3 * LDX]);
+                }
+                const float4 bv = I < NSUB ? *reinterpret_cast<const float4 *>(sBeta + 16 * I + 4 * q4)
+                                           : make_float4(0.f, 0.f, 0.f, 0.f);
+                f[u] = make_frag<BF>(xv.x * bv.x, xv.y * bv.y, xv.z * bv.z, xv.w * bv.w);
+            }
+            store_pair<BF>(rec + Rec::oT + (size_t)(R * NPAIR + pp) * Rec::TILE_BYTES, lane, f[0], f[1]);
+        }
+    }
+    for (int ct = wave; ct < KT; ct += 4) {
+        const OT *row = sKbT + (16 * ct + l16) * LDT + 4 * q4;
+#pragma unroll
+        for (int pp = 0; pp < NPAIR; ++pp) {
+            Frag<BF> f0 = lds_frag(row + 32 * pp), f1;
+            if (2 * pp + 1 < NSUB) f1 = lds_frag(row + 32 * pp + 16);
+            else f1 = make_frag<BF>(0.f, 0.f, 0.f, 0.f);
+            store_pair<BF>(rec + Rec::oKbT + (size_t)(ct * NPAIR + pp) * Rec::TILE_BYTES, lane, f0, f1);
+        }
+    }
+}
+
+// ------------------------------------------------------------------- scan ----
+template <typename IO, int DK, int C, int NW>
+struct ScanLayout {
+    using Rec = SplitRecord<IO, DK, C>;
+    static constexpr int DVT = 16 * NW;
+    static constexpr int NT = 64 * NW;
+    static constexpr size_t kVBytes = (size_t)C * DVT * sizeof(IO);
+    static constexpr int V_PIECES = (int)(kVBytes / 16);
+    static constexpr size_t oRec0 = 0;
+    static constexpr size_t oRec1 = Rec::kBytes;
+    static constexpr size_t oV0 = 2 * Rec::kBytes;
+    static constexpr size_t oV1 = oV0 + kVBytes;
+    static constexpr size_t kBytes = oV1 + kVBytes;
+    static constexpr bool kFits = kBytes <= 160 * 1024;
+    static_assert(Rec::kBytes % (64 * 16) == 0, "record is copied in whole wave units");
+    static_assert(V_PIECES % 64 == 0, "V tile is copied in whole wave units");
+};
+
+// Queue the asynchronous copy of one chunk's record and V tile into LDS.
+template <typename IO, int DK, int C, int NW>
+__device__ __forceinline__ void stage_chunk(char *lds_rec, char *lds_v, const char *rec, const IO *V, int64_t tok0,
+                                            int clen, int H, int h, int DV, int col0, int wave, int lane) {
+    using S = ScanLayout<IO, DK, C, NW>;
+    constexpr int REC_UNITS = (int)(S::Rec::kBytes / 1024);  // one wave instruction = 64 lanes x 16 B
+    for (int u = wave; u < REC_UNITS; u += NW)
+        __builtin_amdgcn_global_load_lds(rec + (size_t)u * 1024 + lane * 16,
+                                         (__attribute__((address_space(3))) void *)(lds_rec + u * 1024), 16, 0, 0);
+    constexpr int PPR = S::DVT * (int)sizeof(IO) / 16;  // 16-byte pieces per V row
+    constexpr int V_UNITS = S::V_PIECES / 64;
+    for (int u = wave; u < V_UNITS; u += NW) {
+        const int piece = u * 64 + lane;
+        const int r = min(piece / PPR, clen - 1);
+        const int cc = (piece % PPR) * (16 / (int)sizeof(IO));
+        __builtin_amdgcn_global_load_lds(V + ((tok0 + r) * H + h) * (int64_t)DV + col0 + cc,
+                                         (__attribute__((address_space(3))) void *)(lds_v + u * 1024), 16, 0, 0);
+    }
+}
+
+template <typename IO, int DK, int C, int NW>
+__global__ void __launch_bounds__(64 * NW) kda_scan_kernel(FwdParams p, const int32_t *__restrict__ chunk_off,
+                                                            const char *__restrict__ records) {
+    using S = ScanLayout<IO, DK, C, NW>;
+    using Rec = typename S::Rec;
+    constexpr bool BF = Rec::BF;
+    constexpr int NSUB = Rec::NSUB, KT = Rec::KT, NPAIR = Rec::NPAIR, DVT = S::DVT;
+    using Tr = IoTraits<IO>;
+
+    __shared__ __attribute__((aligned(16))) char smem[S::kBytes];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l16 = lane & 15, q4 = lane >> 4;
+    const int H = p.H, DV = p.dv;
+    const int ntile = DV / DVT;
+    const int64_t nblocks = (int64_t)p.num_seqs * H * ntile;
+    const int64_t item = xcd_grouped_block(blockIdx.x, nblocks);
+    const int tile = (int)(item % ntile);
+    const int64_t nh = item / ntile;
+    const int h = (int)(nh % H);
+    const int n = (int)(nh / H);
+    int64_t start;
+    int len;
+    if (p.cu) {
+        start = p.cu[n];
+        len = p.cu[n + 1] - p.cu[n];
+    } else {
+        start = (int64_t)n * p.T;
+        len = p.T;
+    }
+    const int nchunks = (len + C - 1) / C;
+    const int64_t g0 = first_chunk(p, chunk_off, C, n);
+    const int col0 = tile * DVT;
+    const int col = col0 + 16 * wave + l16;
+    const IO *V = static_cast<const IO *>(p.v);
+    IO *O = static_cast<IO *>(p.out);
+
+    // state slice of this wave: S[ct] holds rows 16ct + 4*q4 + j of column `col`
+    f32x4 St[KT];
+    const int64_t sbase = ((int64_t)n * H + h) * DK * DV;
+#pragma unroll
+    for (int ct = 0; ct < KT; ++ct)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) St[ct][j] = p.s0 ? p.s0[sbase + (int64_t)(16 * ct + 4 * q4 + j) * DV + col] : 0.f;
+
+    if (nchunks > 0)
+        stage_chunk<IO, DK, C, NW>(smem + S::oRec0, smem + S::oV0, records + (size_t)(g0 * H + h) * Rec::kBytes, V,
+                                   start, min(C, len), H, h, DV, col0, wave, lane);
+
+    for (int c = 0; c < nchunks; ++c) {
+        const int clen = min(C, len - c * C);
+        const int64_t tok0 = start + (int64_t)c * C;
+        const char *rb = smem + ((c & 1) ? S::oRec1 : S::oRec0);
+        const char *vb = smem + ((c & 1) ? S::oV1 : S::oV0);
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of chunk c have landed
+        __syncthreads();                // ... and every other wave's
+        if (c + 1 < nchunks)
+            stage_chunk<IO, DK, C, NW>(smem + ((c & 1) ? S::oRec0 : S::oRec1), smem + ((c & 1) ? S::oV0 : S::oV1),
+                                       records + (size_t)((g0 + c + 1) * H + h) * Rec::kBytes, V, tok0 + C,
+                                       min(C, len - (c + 1) * C), H, h, DV, col0, wave, lane);
+
+        Frag<BF> Sb[KT];
+#pragma unroll
+        for (int ct = 0; ct < KT; ++ct) Sb[ct] = frag_from_acc<BF>(St[ct]);
+
+        // K~ S and Q~ S
+        f32x4 Y[NSUB], Oa[NSUB];
+#pragma unroll
+        for (int rt = 0; rt < NSUB; ++rt) {
+            f32x4 ak = zero4(), ao = zero4();
+#pragma unroll
+            for (int kp = 0; kp < KT / 2; ++kp) {
+                Frag<BF> a0, a1, b0, b1;
+                load_pair<BF>(rb + Rec::oKt + (size_t)(rt * (KT / 2) + kp) * Rec::TILE_BYTES, lane, a0, a1);
+                load_pair<BF>(rb + Rec::oQt + (size_t)(rt * (KT / 2) + kp) * Rec::TILE_BYTES, lane, b0, b1);
+                mma32(ak, a0, a1, Sb[2 * kp], Sb[2 * kp + 1]);
+                mma32(ao, b0, b1, Sb[2 * kp], Sb[2 * kp + 1]);
+            }
+            // Y = V - K~ S  (rows past the chunk end hold finite filler; T zeroes their effect)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * rt + 4 * q4 + j;
+                const float vv = Tr::load1(reinterpret_cast<const IO *>(vb) + r * DVT + 16 * wave + l16);
+                Y[rt][j] = vv - ak[j];
+            }
+            Oa[rt] = ao;
+        }
+        Frag<BF> Yb[2 * NPAIR];
+#pragma unroll
+        for (int rt = 0; rt < 2 * NPAIR; ++rt) Yb[rt] = rt < NSUB ? frag_from_acc<BF>(Y[rt]) : make_frag<BF>(0.f, 0.f, 0.f, 0.f);
+
+        // D = T Y
+        Frag<BF> Db[2 * NPAIR];
+#pragma unroll
+        for (int R = 0; R < NSUB; ++R) {
+            f32x4 d = zero4();
+#pragma unroll
+            for (int pp = 0; pp < NPAIR; ++pp) {
+                if (2 * pp > R) break;
+                Frag<BF> a0, a1;
+                load_pair<BF>(rb + Rec::oT + (size_t)(R * NPAIR + pp) * Rec::TILE_BYTES, lane, a0, a1);
+                mma32(d, a0, a1, Yb[2 * pp], Yb[2 * pp + 1]);
+            }
+            Db[R] = frag_from_acc<BF>(d);
+        }
+        if constexpr (NSUB % 2 == 1) Db[NSUB] = make_frag<BF>(0.f, 0.f, 0.f, 0.f);
+
+        // O = scale (Q~ S + P D)
+#pragma unroll
+        for (int R = 0; R < NSUB; ++R) {
+#pragma unroll
+            for (int pp = 0; pp < NPAIR; ++pp) {
+                if (2 * pp > R) break;
+                Frag<BF> a0, a1;
+                load_pair<BF>(rb + Rec::oP + (size_t)(R * NPAIR + pp) * Rec::TILE_BYTES, lane, a0, a1);
+                mma32(Oa[R], a0, a1, Db[2 * pp], Db[2 * pp + 1]);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * R + 4 * q4 + j;
+                if (r < clen) Tr::store1(O + ((tok0 + r) * H + h) * (int64_t)DV + col, Oa[R][j] * p.scale);
+            }
+        }
+
+        // S <- Gamma S + K-^T D
+        const float *gam = reinterpret_cast<const float *>(rb + Rec::oGam);
+#pragma unroll
+        for (int ct = 0; ct < KT; ++ct) {
+            const float4 gm = *reinterpret_cast<const float4 *>(gam + 16 * ct + 4 * q4);
+            St[ct][0] *= gm.x;
+            St[ct][1] *= gm.y;
+            St[ct][2] *= gm.z;
+            St[ct][3] *= gm.w;
+#pragma unroll
+            for (int pp = 0; pp < NPAIR; ++pp) {
+                Frag<BF> a0, a1;
+                load_pair<BF>(rb + Rec::oKbT + (size_t)(ct * NPAIR + pp) * Rec::TILE_BYTES, lane, a0, a1);
+                mma32(St[ct], a0, a1, Db[2 * pp], Db[2 * pp + 1]);
+            }
+        }
+    }
+
+    if (p.sf) {
+#pragma unroll
+        for (int ct = 0; ct < KT; ++ct)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) p.sf[sbase + (int64_t)(16 * ct + 4 * q4 + j) * DV + col] = St[ct][j];
+    }
+}
+
+// ----------------------------------------------------------------- launch ----
+template <typename IO, int DK, int C>
+constexpr size_t split_record_bytes() {
+    return SplitRecord<IO, DK, C>::kBytes;
+}
+
+template <typename IO, int DK, int C, int NW>
+constexpr bool split_fits() {
+    return ScanLayout<IO, DK, C, NW>::kFits && PrepLayout<IO, DK, C>::kBytes <= 160 * 1024;
+}
+
+// Workspace: [chunk offsets: num_seqs + 1 int32, padded to 256 B][records]
+template <typename IO, int DK, int C, int NW>
+hipError_t launch_split_variant(const FwdParams &p, char *workspace, int64_t chunk_upper, hipStream_t stream) {
+    if constexpr (!split_fits<IO, DK, C, NW>()) {
+        return hipErrorInvalidConfiguration;
+    } else {
+        int32_t *chunk_off = reinterpret_cast<int32_t *>(workspace);
+        char *records = workspace + split_plan_bytes(p.num_seqs);
+        if (p.cu) {
+            hipLaunchKernelGGL(kda_plan_kernel, dim3(1), dim3(256), 0, stream, p.cu, p.num_seqs, C, chunk_off);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        const int64_t prep_blocks = chunk_upper * p.H;
+        if (prep_blocks > 0) {
+            hipLaunchKernelGGL((kda_prep_kernel<IO, DK, C>), dim3((unsigned)prep_blocks), dim3(256), 0, stream, p,
+                               chunk_off, records);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        const int64_t scan_blocks = (int64_t)p.num_seqs * p.H * (p.dv / (16 * NW));
+        if (scan_blocks > 0) {
+            hipLaunchKernelGGL((kda_scan_kernel<IO, DK, C, NW>), dim3((unsigned)scan_blocks), dim3(64 * NW), 0, stream,
+                               p, chunk_off, records);
+            return hipGetLastError();
+        }
+        return hipSuccess;
+    }
+}
+
+#define KDA_SPLIT_VARIANTS(F) \
+    F(64, 16, 4) F(64, 32, 4) F(64, 64, 4) F(128, 16, 4) F(128, 32, 4) F(128, 64, 4) \
+    F(64, 16, 2) F(64, 32, 2) F(64, 64, 2) F(128, 16, 2) F(128, 32, 2) F(128, 64, 2)
+
+template <typename IO>
+size_t split_record_size(int dk, int chunk) {
+#define KDA_REC_CASE(DK_, C_, NW_) \
+    if (dk == DK_ && chunk == C_) return split_record_bytes<IO, DK_, C_>();
+    KDA_SPLIT_VARIANTS(KDA_REC_CASE)
+#undef KDA_REC_CASE
+    return 0;
+}
+
+template <typename IO>
+bool split_supported(int dk, int chunk, int nw) {
+#define KDA_FIT_CASE(DK_, C_, NW_) \
+    if (dk == DK_ && chunk == C_ && nw == NW_) return split_fits<IO, DK_, C_, NW_>();
+    KDA_SPLIT_VARIANTS(KDA_FIT_CASE)
+#undef KDA_FIT_CASE
+    return false;
+}
+
+template <typename IO>
+hipError_t launch_split(const FwdParams &p, int chunk, int nw, char *workspace, int64_t chunk_upper,
+                        hipStream_t stream) {
+#define KDA_SPLIT_CASE(DK_, C_, NW_) \
+    if (p.dk == DK_ && chunk == C_ && nw == NW_) return launch_split_variant<IO, DK_, C_, NW_>(p, workspace, chunk_upper, stream);
+    KDA_SPLIT_VARIANTS(KDA_SPLIT_CASE)
+#undef KDA_SPLIT_CASE
+    return hipErrorInvalidConfiguration;
+}
+
+}  // namespace kda

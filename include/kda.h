@@ -60,6 +60,16 @@ typedef enum {
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
 
+/* How kda_chunk_fwd evaluates the chunks.
+ *  KDA_ALGO_FUSED:    one kernel; each workgroup walks its sequence chunk by chunk and
+ *                     does all per-chunk work itself (no workspace).
+ *  KDA_ALGO_TWO_PASS: a parallel pass over all chunks computes the state-independent
+ *                     chunk operands (gated keys/queries, the UT transform, P) into the
+ *                     workspace, then a scan pass carries the state through the chunks.
+ *  KDA_ALGO_AUTO:     two-pass when the workspace is large enough (kda_query reports the
+ *                     size) and the problem is supported by it, else fused. */
+typedef enum { KDA_ALGO_AUTO = 0, KDA_ALGO_FUSED = 1, KDA_ALGO_TWO_PASS = 2 } kda_algo_t;
+
 /* Problem description shared by kda_chunk_fwd, kda_recurrent_fwd and kda_query. */
 typedef struct {
     int32_t batch;       /* B: number of sequences of seq_len tokens; must be 1 with cu_seqlens */
@@ -71,7 +81,9 @@ typedef struct {
     kda_dtype_t io_dtype;/* dtype of q, k, v and out; g, beta and the state are always fp32 */
     int32_t chunk_size;  /* 16, 32 or 64; 0 = library default (64, or 32 for fp32 with d_k = 128) */
     float scale;         /* multiplies the output (1.0 for o_t = S_t^T q_t) */
-    int32_t dv_tile;     /* state columns per workgroup: 0 = library choice, else 32, 64 or 128 (tuning) */
+    int32_t dv_tile;     /* state columns per workgroup: 0 = library choice; fused: 32, 64 or 128;
+                            two-pass: 32 or 64 (tuning) */
+    int32_t algo;        /* kda_algo_t */
 } kda_problem_t;
 
 /*
@@ -91,8 +103,11 @@ typedef struct {
  *  final_state     [num_seqs, H, d_k, d_v] fp32, or NULL to skip writing it.  It may be
  *                  the same pointer as initial_state (in-place state cache); no other
  *                  aliasing between arguments is allowed.
- *  workspace       device scratch of at least kda_query().workspace_bytes bytes (the
- *                  current kernels need none: NULL and 0 are accepted).
+ *  workspace       device scratch for the two-pass algorithm, at least
+ *                  kda_query().workspace_bytes bytes (256-byte aligned); its contents on
+ *                  entry are ignored and on return unspecified.  With KDA_ALGO_AUTO a
+ *                  smaller (or NULL) workspace selects the fused algorithm; with
+ *                  KDA_ALGO_TWO_PASS it is an error (KDA_ERR_WORKSPACE).
  */
 kda_status_t kda_chunk_fwd(const kda_problem_t *problem, const void *q, const void *k, const void *v,
                            const float *g, const float *beta, const float *initial_state,
@@ -125,7 +140,8 @@ kda_status_t kda_decode_step(int32_t num_seqs, int32_t num_heads, int32_t head_d
 typedef struct {
     int32_t version;           /* KDA_VERSION of the library */
     int32_t supported;         /* 1 if kda_chunk_fwd accepts the problem */
-    size_t workspace_bytes;    /* scratch kda_chunk_fwd needs for this problem */
+    int32_t algo;              /* algorithm used when the reported workspace is supplied */
+    size_t workspace_bytes;    /* scratch the two-pass algorithm needs (0 if it is not used) */
     int32_t chunk_size;        /* chunk the forward will use */
     int32_t dv_tile;           /* state columns owned by one workgroup */
     int32_t threads_per_block; /* workgroup size */

@@ -112,6 +112,17 @@ def test_chunk_fwd_checks_host_cu_seqlens():
     assert sum(lens) == 15
 
 
+def test_algo_and_workspace_validation():
+    lib = kda.library()
+    assert call_chunk(problem(algo=7)) == kda.KDA_ERR_INVALID_ARGUMENT
+    # two-pass requested without a workspace
+    assert call_chunk(problem(algo=kda.KDA_ALGO_TWO_PASS)) == kda.KDA_ERR_WORKSPACE
+    assert b"workspace" in lib.kda_last_error()
+    # two-pass on a 128-column tile does not exist
+    p = problem(head_dim_v=128, dv_tile=128, algo=kda.KDA_ALGO_TWO_PASS)
+    assert call_chunk(p) == kda.KDA_ERR_UNSUPPORTED
+
+
 def test_empty_problems_launch_nothing_and_succeed():
     # zero sequences: nothing to do, no HIP call
     assert call_chunk(problem(batch=0)) == kda.KDA_OK
@@ -144,12 +155,20 @@ def test_query_reports_config_and_work():
     # prefill workload: B=4, T=4096, H=16, d=128, chunk 64, bf16
     r = kda.query(4, 4096, 16, 128, 128, "bf16")
     assert r["status"] == kda.KDA_OK and r["supported"] == 1
-    assert r["chunk_size"] == 64 and r["workspace_bytes"] == 0
+    assert r["algo"] == kda.KDA_ALGO_TWO_PASS and r["chunk_size"] == 64
+    # chunk-offset table (256 B) + one record per chunk-head: K~, Q~, K-^T (16 KB each),
+    # T and P (8 KB each), Gamma (512 B), rounded up to whole KB
+    rec = 3 * 16384 + 2 * 8192 + 512
+    rec = (rec + 1023) // 1024 * 1024
+    assert r["workspace_bytes"] == 256 + 4 * 64 * 16 * rec
     assert r["grid_blocks"] == 4 * 16 * (128 // r["dv_tile"])
+    rf = kda.query(4, 4096, 16, 128, 128, "bf16", algo="fused")
+    assert rf["algo"] == kda.KDA_ALGO_FUSED and rf["workspace_bytes"] == 0
+    assert rf["grid_blocks"] == 4 * 16 * (128 // rf["dv_tile"])
     ht = 4 * 4096 * 16
     assert r["flops"] == pytest.approx(ht * (2 * 64 * 256 + 64 * 64 / 3 + 6 * 128 * 128))
     assert r["hbm_bytes"] == pytest.approx(ht * 1540 + 2 * 4 * 128 * 128 * 64)
-    assert 0 < r["lds_bytes"] <= 160 * 1024
+    assert 0 < rf["lds_bytes"] <= 160 * 1024
     assert r["peak_hbm_gbps"] == 8000.0 and r["peak_bf16_tflops"] == 2500.0
     # unsupported variant is reported, not raised
     r = kda.query(1, 64, 1, 128, 128, "f32", chunk_size=64)

@@ -53,12 +53,25 @@ def compare(name, got, ref, io):
         assert rel <= TOL_BF16_REL, f"{name}: max rel error {rel:.3e} > {TOL_BF16_REL}"
 
 
-def check_fwd(inp, *, heads=None, chunk_size=0, dv_tile=0, scale=1.0, mode="chunk", label=""):
-    say(f"[{label}] mode={mode} io={inp.io} shape={tuple(inp.q.shape)} v={tuple(inp.v.shape)} "
+ALGOS = ["fused", "two_pass"]
+
+
+def skip_unless_supported(inp, chunk_size, dv_tile, algo):
+    B, T, H, dk = inp.q.shape
+    r = kda.query(B, T, H, dk, inp.v.shape[-1], inp.io, num_seqs=inp.num_seqs if inp.cu_seqlens is not None else 0,
+                  chunk_size=chunk_size, dv_tile=dv_tile, algo=algo)
+    if r["status"] == kda.KDA_ERR_UNSUPPORTED:
+        pytest.skip(f"{algo} has no compiled variant for io={inp.io} d_k={dk} chunk={chunk_size} (LDS budget)")
+
+
+def check_fwd(inp, *, heads=None, chunk_size=0, dv_tile=0, scale=1.0, mode="chunk", label="", algo="auto"):
+    say(f"[{label}] mode={mode} algo={algo} io={inp.io} shape={tuple(inp.q.shape)} v={tuple(inp.v.shape)} "
         f"seqs={inp.num_seqs} chunk={chunk_size} dv_tile={dv_tile} scale={scale} heads={heads}")
+    if mode == "chunk":
+        skip_unless_supported(inp, chunk_size, dv_tile, algo)
     d = on_dev(inp)
     if mode == "chunk":
-        out, fin = kda.chunk_fwd(**d, chunk_size=chunk_size, dv_tile=dv_tile, scale=scale)
+        out, fin = kda.chunk_fwd(**d, chunk_size=chunk_size, dv_tile=dv_tile, scale=scale, algo=algo)
     else:
         out, fin = kda.recurrent_fwd(**d, scale=scale)
     torch.cuda.synchronize()
@@ -75,33 +88,37 @@ def check_fwd(inp, *, heads=None, chunk_size=0, dv_tile=0, scale=1.0, mode="chun
 
 @pytest.mark.parametrize("chunk", [16, 32, 64])
 @pytest.mark.parametrize("dv_tile", [32, 64])
-def test_tiny_fp32_chunk(chunk, dv_tile):
-    check_fwd(ki.workload_inputs("tiny_fp32"), chunk_size=chunk, dv_tile=dv_tile, label="tiny_fp32")
+@pytest.mark.parametrize("algo", ALGOS)
+def test_tiny_fp32_chunk(chunk, dv_tile, algo):
+    check_fwd(ki.workload_inputs("tiny_fp32"), chunk_size=chunk, dv_tile=dv_tile, label="tiny_fp32", algo=algo)
 
 
 def test_tiny_fp32_recurrent():
     check_fwd(ki.workload_inputs("tiny_fp32"), mode="recurrent", label="tiny_fp32")
 
 
-@pytest.mark.parametrize("dv_tile", [0, 32, 64, 128])
-def test_prefill_full(dv_tile):
-    check_fwd(ki.workload_inputs("prefill"), dv_tile=dv_tile, label="prefill")
+@pytest.mark.parametrize("algo,dv_tile", [("fused", 0), ("fused", 32), ("fused", 64), ("fused", 128),
+                                          ("two_pass", 0), ("two_pass", 32), ("two_pass", 64)])
+def test_prefill_full(algo, dv_tile):
+    check_fwd(ki.workload_inputs("prefill"), dv_tile=dv_tile, label="prefill", algo=algo)
 
 
 def test_prefill_recurrent():
     check_fwd(ki.workload_inputs("prefill"), mode="recurrent", label="prefill")
 
 
-def test_long_prefill_sampled_heads():
+@pytest.mark.parametrize("algo", ALGOS)
+def test_long_prefill_sampled_heads(algo):
     inp = ki.workload_inputs("long_prefill")
-    check_fwd(inp, heads=[0, 17], label="long_prefill")
+    check_fwd(inp, heads=[0, 17], label="long_prefill", algo=algo)
     del inp
     torch.cuda.empty_cache()
 
 
-def test_varlen_sampled_heads():
+@pytest.mark.parametrize("algo", ALGOS)
+def test_varlen_sampled_heads(algo):
     inp = ki.workload_inputs("varlen")
-    check_fwd(inp, heads=[3, 30], label="varlen")
+    check_fwd(inp, heads=[3, 30], label="varlen", algo=algo)
 
 
 def test_decode_full():
@@ -128,35 +145,39 @@ def small(B, T, H, dk, dv, io, seed, **kw):
 @pytest.mark.parametrize("io,dk,dv,chunk", [("bf16", 128, 128, 64), ("bf16", 128, 128, 16), ("bf16", 128, 128, 32),
                                            ("bf16", 64, 128, 64), ("bf16", 128, 64, 32), ("f32", 64, 64, 64),
                                            ("f32", 128, 128, 32), ("f32", 128, 64, 16)])
-def test_ragged_lengths_and_dims(io, dk, dv, chunk):
+@pytest.mark.parametrize("algo", ALGOS)
+def test_ragged_lengths_and_dims(io, dk, dv, chunk, algo):
     # T = 203 is not a multiple of any chunk size: every sequence ends in a partial chunk
     inp = small(2, 203, 3, dk, dv, io, seed=dk + dv + chunk)
-    check_fwd(inp, chunk_size=chunk, label=f"ragged-{io}-{dk}x{dv}-c{chunk}")
+    check_fwd(inp, chunk_size=chunk, label=f"ragged-{io}-{dk}x{dv}-c{chunk}", algo=algo)
 
 
-def test_varlen_with_empty_and_single_token_sequences():
+@pytest.mark.parametrize("algo", ALGOS)
+def test_varlen_with_empty_and_single_token_sequences(algo):
     lens = [0, 1, 64, 65, 17, 0, 200, 63]
     inp = ki.make_inputs(1, 0, 4, 128, 128, "bf16", 21, lengths=lens)
-    check_fwd(inp, label="varlen-edge")
+    check_fwd(inp, label="varlen-edge", algo=algo)
     check_fwd(inp, mode="recurrent", label="varlen-edge")
 
 
-def test_no_initial_state_and_no_final_state():
+@pytest.mark.parametrize("algo", ALGOS)
+def test_no_initial_state_and_no_final_state(algo):
     inp = small(2, 150, 2, 128, 128, "bf16", 5, s0_std=None)
-    check_fwd(inp, label="zero-s0")
+    check_fwd(inp, label="zero-s0", algo=algo)
     d = on_dev(inp)
-    out, fin = kda.chunk_fwd(**d, output_final_state=False)
+    out, fin = kda.chunk_fwd(**d, output_final_state=False, algo=algo)
     torch.cuda.synchronize()
     assert fin is None
     o_ref, _ = run_oracle(inp)
     compare("no-final out", out, o_ref, "bf16")
 
 
-def test_in_place_state():
+@pytest.mark.parametrize("algo", ALGOS)
+def test_in_place_state(algo):
     inp = small(2, 130, 2, 128, 128, "bf16", 6)
     d = on_dev(inp)
     st = d["initial_state"].clone()
-    out, fin = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], st, final_state=st)
+    out, fin = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], st, final_state=st, algo=algo)
     torch.cuda.synchronize()
     o_ref, f_ref = run_oracle(inp)
     compare("inplace out", out, o_ref, "bf16")
@@ -167,29 +188,33 @@ def test_scale():
     check_fwd(small(1, 100, 2, 64, 64, "f32", 7), scale=0.125, label="scale")
 
 
-def test_zero_beta_is_pure_decay_with_state():
+@pytest.mark.parametrize("algo", ALGOS)
+def test_zero_beta_is_pure_decay_with_state(algo):
     # beta == 0 leaves only the decayed initial state; g = -softplus(N(-3, 1)) keeps that
     # state within fp32 range over 256 tokens (with mu = 0 it decays to ~1e-85)
     inp = small(2, 256, 2, 128, 128, "bf16", 8, s0_std=1.0, g_mu=-3.0)
     inp.beta.zero_()
-    check_fwd(inp, label="beta0")
+    check_fwd(inp, label="beta0", algo=algo)
 
 
-def test_unit_gate_deltanet():
+@pytest.mark.parametrize("algo", ALGOS)
+def test_unit_gate_deltanet(algo):
     inp = small(2, 256, 2, 128, 128, "bf16", 9)
     inp.g.zero_()
-    check_fwd(inp, label="g0")
+    check_fwd(inp, label="g0", algo=algo)
 
 
-def test_long_memory_gate():
+@pytest.mark.parametrize("algo", ALGOS)
+def test_long_memory_gate(algo):
     inp = small(1, 1024, 2, 128, 128, "bf16", 10, g_mu=-6.0, s0_std=1.0)
-    check_fwd(inp, label="long-memory")
+    check_fwd(inp, label="long-memory", algo=algo)
 
 
-def test_strong_gate():
+@pytest.mark.parametrize("algo", ALGOS)
+def test_strong_gate(algo):
     # mean per-token log-decay about -2.1: 16-token sub-chunks decay by ~e^-34
     inp = small(1, 512, 2, 128, 128, "bf16", 11, g_mu=2.0)
-    check_fwd(inp, label="strong-gate")
+    check_fwd(inp, label="strong-gate", algo=algo)
 
 
 def test_strong_gate_fp32():
@@ -199,10 +224,11 @@ def test_strong_gate_fp32():
 
 # ---------------------------------------------------------- cross-checks ----
 
-def test_chunk_equals_recurrent_on_gpu():
+@pytest.mark.parametrize("algo", ALGOS)
+def test_chunk_equals_recurrent_on_gpu(algo):
     inp = small(2, 777, 4, 128, 128, "bf16", 13)
     d = on_dev(inp)
-    o1, f1 = kda.chunk_fwd(**d)
+    o1, f1 = kda.chunk_fwd(**d, algo=algo)
     o2, f2 = kda.recurrent_fwd(**d)
     torch.cuda.synchronize()
     compare("chunk vs recurrent out", o1, o2.double().cpu().numpy(), "bf16")
