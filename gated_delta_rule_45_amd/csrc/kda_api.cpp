@@ -111,9 +111,9 @@ kda_status_t resolve(const kda_problem_t *p, bool varlen, Resolved &r, bool chun
         r.cfg.chunk = C;
         r.cfg.dv_tile = p->dv_tile ? p->dv_tile : default_dv_tile((int64_t)r.num_seqs * p->num_heads, p->head_dim_v);
         r.lds = kda::chunk_variant_lds_bytes(p->io_dtype, p->head_dim_k, r.cfg.dv_tile, r.cfg.chunk);
-        // two-pass: scan workgroups of 16 * nw state columns
-        r.nw = p->dv_tile == 32 ? 2 : 4;
-        r.two_pass_ok = p->dv_tile != 128 && (16 * r.nw) <= p->head_dim_v &&
+        // two-pass: scan workgroups of nw compute waves x 32 state columns
+        r.nw = p->dv_tile == 32 ? 1 : 2;
+        r.two_pass_ok = p->dv_tile != 128 && (32 * r.nw) <= p->head_dim_v &&
                         kda::split_variant_supported(p->io_dtype, p->head_dim_k, C, r.nw);
         if (r.two_pass_ok) {
             const int64_t per = ((int64_t)p->seq_len + C - 1) / C;
@@ -357,11 +357,11 @@ kda_status_t kda_query(const kda_problem_t *problem, uint32_t flags, kda_query_r
             res->algo = two ? KDA_ALGO_TWO_PASS : KDA_ALGO_FUSED;
             res->workspace_bytes = two ? r.ws_bytes : 0;
             res->chunk_size = r.cfg.chunk;
-            if (two) {  // the scan pass: one workgroup per (sequence, head, 16*nw columns)
-                res->dv_tile = 16 * r.nw;
-                res->threads_per_block = 64 * r.nw;
+            if (two) {  // the scan pass: one workgroup per (sequence, head, 32*nw columns)
+                res->dv_tile = 32 * r.nw;
+                res->threads_per_block = 64 * (r.nw + 1);
                 res->lds_bytes = 0;
-                res->grid_blocks = (int64_t)r.num_seqs * p.num_heads * (p.head_dim_v / (16 * r.nw));
+                res->grid_blocks = (int64_t)r.num_seqs * p.num_heads * (p.head_dim_v / (32 * r.nw));
             } else {
                 res->dv_tile = r.cfg.dv_tile;
                 res->threads_per_block = kda::kChunkThreads;

@@ -443,11 +443,15 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
 }
 
 // ------------------------------------------------------------------- scan ----
+// Workgroup = NW compute waves (each owns 32 state columns = two 16-column slices, so
+// every operand fragment read from LDS feeds two matrix-core products) + 1 copy wave
+// that queues the asynchronous global->LDS copies of the next chunk's record and V tile.
 template <typename IO, int DK, int C, int NW>
 struct ScanLayout {
     using Rec = SplitRecord<IO, DK, C>;
-    static constexpr int DVT = 16 * NW;
-    static constexpr int NT = 64 * NW;
+    static constexpr int SPW = 2;               // 16-column slices per compute wave
+    static constexpr int DVT = 16 * SPW * NW;   // state columns per workgroup
+    static constexpr int NT = 64 * (NW + 1);    // threads (compute waves + copy wave)
     static constexpr size_t kVBytes = (size_t)C * DVT * sizeof(IO);
     static constexpr int V_PIECES = (int)(kVBytes / 16);
     static constexpr size_t oRec0 = 0;
@@ -460,33 +464,35 @@ struct ScanLayout {
     static_assert(V_PIECES % 64 == 0, "V tile is copied in whole wave units");
 };
 
-// Queue the asynchronous copy of one chunk's record and V tile into LDS.
+// Copy wave: queue the asynchronous copy of one chunk's record and V tile into LDS.
 template <typename IO, int DK, int C, int NW>
-__device__ __forceinline__ void stage_chunk(char *lds_rec, char *lds_v, const char *rec, const IO *V, int64_t tok0,
-                                            int clen, int H, int h, int DV, int col0, int wave, int lane) {
+__device__ __forceinline__ void stage_chunk(char *lds_rec, char *lds_v, const char *rec, const IO *vrow0, int clen,
+                                            int64_t vstride, int lane) {
     using S = ScanLayout<IO, DK, C, NW>;
-    constexpr int REC_UNITS = (int)(S::Rec::kBytes / 1024);  // one wave instruction = 64 lanes x 16 B
-    for (int u = wave; u < REC_UNITS; u += NW)
+    constexpr int REC_UNITS = (int)(S::Rec::kBytes / 1024);  // one instruction = 64 lanes x 16 B
+#pragma unroll 4
+    for (int u = 0; u < REC_UNITS; ++u)
         __builtin_amdgcn_global_load_lds(rec + (size_t)u * 1024 + lane * 16,
                                          (__attribute__((address_space(3))) void *)(lds_rec + u * 1024), 16, 0, 0);
     constexpr int PPR = S::DVT * (int)sizeof(IO) / 16;  // 16-byte pieces per V row
     constexpr int V_UNITS = S::V_PIECES / 64;
-    for (int u = wave; u < V_UNITS; u += NW) {
+#pragma unroll
+    for (int u = 0; u < V_UNITS; ++u) {
         const int piece = u * 64 + lane;
-        const int r = min(piece / PPR, clen - 1);
+        const int r = min(piece / PPR, clen - 1);  // rows past the end re-read the last row
         const int cc = (piece % PPR) * (16 / (int)sizeof(IO));
-        __builtin_amdgcn_global_load_lds(V + ((tok0 + r) * H + h) * (int64_t)DV + col0 + cc,
+        __builtin_amdgcn_global_load_lds(vrow0 + r * vstride + cc,
                                          (__attribute__((address_space(3))) void *)(lds_v + u * 1024), 16, 0, 0);
     }
 }
 
 template <typename IO, int DK, int C, int NW>
-__global__ void __launch_bounds__(64 * NW) kda_scan_kernel(FwdParams p, const int32_t *__restrict__ chunk_off,
-                                                            const char *__restrict__ records) {
+__global__ void __launch_bounds__(64 * (NW + 1)) kda_scan_kernel(FwdParams p, const int32_t *__restrict__ chunk_off,
+                                                                  const char *__restrict__ records) {
     using S = ScanLayout<IO, DK, C, NW>;
     using Rec = typename S::Rec;
     constexpr bool BF = Rec::BF;
-    constexpr int NSUB = Rec::NSUB, KT = Rec::KT, NPAIR = Rec::NPAIR, DVT = S::DVT;
+    constexpr int NSUB = Rec::NSUB, KT = Rec::KT, NPAIR = Rec::NPAIR, DVT = S::DVT, SPW = S::SPW;
     using Tr = IoTraits<IO>;
 
     __shared__ __attribute__((aligned(16))) char smem[S::kBytes];
@@ -514,81 +520,112 @@ __global__ void __launch_bounds__(64 * NW) kda_scan_kernel(FwdParams p, const in
     const int nchunks = (len + C - 1) / C;
     const int64_t g0 = first_chunk(p, chunk_off, C, n);
     const int col0 = tile * DVT;
-    const int col = col0 + 16 * wave + l16;
-    const IO *V = static_cast<const IO *>(p.v);
-    IO *O = static_cast<IO *>(p.out);
+    const int64_t vstride = (int64_t)H * DV;  // elements between consecutive tokens of one head
+    const IO *vbase = static_cast<const IO *>(p.v) + (start * H + h) * (int64_t)DV + col0;
+    IO *obase = static_cast<IO *>(p.out) + (start * H + h) * (int64_t)DV + col0;
+    const char *rec0 = records + (size_t)(g0 * H + h) * Rec::kBytes;
+    const size_t rec_stride = (size_t)H * Rec::kBytes;
 
-    // state slice of this wave: S[ct] holds rows 16ct + 4*q4 + j of column `col`
-    f32x4 St[KT];
+    if (wave == NW) {
+        // ---------------- copy wave: stays one chunk ahead of the compute waves
+        if (nchunks > 0) stage_chunk<IO, DK, C, NW>(smem + S::oRec0, smem + S::oV0, rec0, vbase, min(C, len), vstride, lane);
+        for (int c = 0; c < nchunks; ++c) {
+            __builtin_amdgcn_s_waitcnt(0);  // chunk c has landed in LDS
+            __syncthreads();                // (A) hand chunk c to the compute waves
+            if (c + 1 < nchunks)
+                stage_chunk<IO, DK, C, NW>(smem + ((c & 1) ? S::oRec0 : S::oRec1), smem + ((c & 1) ? S::oV0 : S::oV1),
+                                           rec0 + (size_t)(c + 1) * rec_stride, vbase + (int64_t)(c + 1) * C * vstride,
+                                           min(C, len - (c + 1) * C), vstride, lane);
+            __syncthreads();  // (B) compute waves are done with chunk c
+        }
+        return;
+    }
+
+    // ---------------- compute waves: slices s = 0, 1 hold columns col0 + 32*wave + 16*s + l16
+    f32x4 St[SPW][KT];
     const int64_t sbase = ((int64_t)n * H + h) * DK * DV;
 #pragma unroll
-    for (int ct = 0; ct < KT; ++ct)
+    for (int s = 0; s < SPW; ++s) {
+        const int col = col0 + 32 * wave + 16 * s + l16;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) St[ct][j] = p.s0 ? p.s0[sbase + (int64_t)(16 * ct + 4 * q4 + j) * DV + col] : 0.f;
-
-    if (nchunks > 0)
-        stage_chunk<IO, DK, C, NW>(smem + S::oRec0, smem + S::oV0, records + (size_t)(g0 * H + h) * Rec::kBytes, V,
-                                   start, min(C, len), H, h, DV, col0, wave, lane);
+        for (int ct = 0; ct < KT; ++ct)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                St[s][ct][j] = p.s0 ? p.s0[sbase + (int64_t)(16 * ct + 4 * q4 + j) * DV + col] : 0.f;
+    }
 
     for (int c = 0; c < nchunks; ++c) {
         const int clen = min(C, len - c * C);
-        const int64_t tok0 = start + (int64_t)c * C;
+        __syncthreads();  // (A) chunk c is in LDS
         const char *rb = smem + ((c & 1) ? S::oRec1 : S::oRec0);
-        const char *vb = smem + ((c & 1) ? S::oV1 : S::oV0);
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of chunk c have landed
-        __syncthreads();                // ... and every other wave's
-        if (c + 1 < nchunks)
-            stage_chunk<IO, DK, C, NW>(smem + ((c & 1) ? S::oRec0 : S::oRec1), smem + ((c & 1) ? S::oV0 : S::oV1),
-                                       records + (size_t)((g0 + c + 1) * H + h) * Rec::kBytes, V, tok0 + C,
-                                       min(C, len - (c + 1) * C), H, h, DV, col0, wave, lane);
+        IO *vb = reinterpret_cast<IO *>(smem + ((c & 1) ? S::oV1 : S::oV0));
 
-        Frag<BF> Sb[KT];
+        Frag<BF> Sb[SPW][KT];
 #pragma unroll
-        for (int ct = 0; ct < KT; ++ct) Sb[ct] = frag_from_acc<BF>(St[ct]);
+        for (int s = 0; s < SPW; ++s)
+#pragma unroll
+            for (int ct = 0; ct < KT; ++ct) Sb[s][ct] = frag_from_acc<BF>(St[s][ct]);
 
-        // K~ S and Q~ S
-        f32x4 Y[NSUB], Oa[NSUB];
+        // K~ S and Q~ S; Y = V - K~ S (rows past the chunk end hold finite filler: T zeroes them)
+        f32x4 Y[SPW][NSUB], Oa[SPW][NSUB];
 #pragma unroll
         for (int rt = 0; rt < NSUB; ++rt) {
-            f32x4 ak = zero4(), ao = zero4();
+            f32x4 ak[SPW], ao[SPW];
+#pragma unroll
+            for (int s = 0; s < SPW; ++s) ak[s] = ao[s] = zero4();
 #pragma unroll
             for (int kp = 0; kp < KT / 2; ++kp) {
                 Frag<BF> a0, a1, b0, b1;
                 load_pair<BF>(rb + Rec::oKt + (size_t)(rt * (KT / 2) + kp) * Rec::TILE_BYTES, lane, a0, a1);
                 load_pair<BF>(rb + Rec::oQt + (size_t)(rt * (KT / 2) + kp) * Rec::TILE_BYTES, lane, b0, b1);
-                mma32(ak, a0, a1, Sb[2 * kp], Sb[2 * kp + 1]);
-                mma32(ao, b0, b1, Sb[2 * kp], Sb[2 * kp + 1]);
-            }
-            // Y = V - K~ S  (rows past the chunk end hold finite filler; T zeroes their effect)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 16 * rt + 4 * q4 + j;
-                const float vv = Tr::load1(reinterpret_cast<const IO *>(vb) + r * DVT + 16 * wave + l16);
-                Y[rt][j] = vv - ak[j];
+                for (int s = 0; s < SPW; ++s) {
+                    mma32(ak[s], a0, a1, Sb[s][2 * kp], Sb[s][2 * kp + 1]);
+                    mma32(ao[s], b0, b1, Sb[s][2 * kp], Sb[s][2 * kp + 1]);
+                }
             }
-            Oa[rt] = ao;
+#pragma unroll
+            for (int s = 0; s < SPW; ++s) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 16 * rt + 4 * q4 + j;
+                    Y[s][rt][j] = Tr::load1(vb + r * DVT + 32 * wave + 16 * s + l16) - ak[s][j];
+                }
+                Oa[s][rt] = ao[s];
+            }
         }
-        Frag<BF> Yb[2 * NPAIR];
-#pragma unroll
-        for (int rt = 0; rt < 2 * NPAIR; ++rt) Yb[rt] = rt < NSUB ? frag_from_acc<BF>(Y[rt]) : make_frag<BF>(0.f, 0.f, 0.f, 0.f);
 
         // D = T Y
-        Frag<BF> Db[2 * NPAIR];
+        Frag<BF> Db[SPW][2 * NPAIR];
+        {
+            Frag<BF> Yb[SPW][2 * NPAIR];
 #pragma unroll
-        for (int R = 0; R < NSUB; ++R) {
-            f32x4 d = zero4();
+            for (int s = 0; s < SPW; ++s)
 #pragma unroll
-            for (int pp = 0; pp < NPAIR; ++pp) {
-                if (2 * pp > R) break;
-                Frag<BF> a0, a1;
-                load_pair<BF>(rb + Rec::oT + (size_t)(R * NPAIR + pp) * Rec::TILE_BYTES, lane, a0, a1);
-                mma32(d, a0, a1, Yb[2 * pp], Yb[2 * pp + 1]);
+                for (int rt = 0; rt < 2 * NPAIR; ++rt)
+                    Yb[s][rt] = rt < NSUB ? frag_from_acc<BF>(Y[s][rt]) : make_frag<BF>(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int R = 0; R < NSUB; ++R) {
+                f32x4 d[SPW];
+#pragma unroll
+                for (int s = 0; s < SPW; ++s) d[s] = zero4();
+#pragma unroll
+                for (int pp = 0; pp < NPAIR; ++pp) {
+                    if (2 * pp > R) break;
+                    Frag<BF> a0, a1;
+                    load_pair<BF>(rb + Rec::oT + (size_t)(R * NPAIR + pp) * Rec::TILE_BYTES, lane, a0, a1);
+#pragma unroll
+                    for (int s = 0; s < SPW; ++s) mma32(d[s], a0, a1, Yb[s][2 * pp], Yb[s][2 * pp + 1]);
+                }
+#pragma unroll
+                for (int s = 0; s < SPW; ++s) Db[s][R] = frag_from_acc<BF>(d[s]);
             }
-            Db[R] = frag_from_acc<BF>(d);
+            if constexpr (NSUB % 2 == 1)
+#pragma unroll
+                for (int s = 0; s < SPW; ++s) Db[s][NSUB] = make_frag<BF>(0.f, 0.f, 0.f, 0.f);
         }
-        if constexpr (NSUB % 2 == 1) Db[NSUB] = make_frag<BF>(0.f, 0.f, 0.f, 0.f);
 
-        // O = scale (Q~ S + P D)
+        // O = scale (Q~ S + P D), staged in this wave's columns of the (consumed) V tile
 #pragma unroll
         for (int R = 0; R < NSUB; ++R) {
 #pragma unroll
@@ -596,12 +633,28 @@ __global__ void __launch_bounds__(64 * NW) kda_scan_kernel(FwdParams p, const in
                 if (2 * pp > R) break;
                 Frag<BF> a0, a1;
                 load_pair<BF>(rb + Rec::oP + (size_t)(R * NPAIR + pp) * Rec::TILE_BYTES, lane, a0, a1);
-                mma32(Oa[R], a0, a1, Db[2 * pp], Db[2 * pp + 1]);
+#pragma unroll
+                for (int s = 0; s < SPW; ++s) mma32(Oa[s][R], a0, a1, Db[s][2 * pp], Db[s][2 * pp + 1]);
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 16 * R + 4 * q4 + j;
-                if (r < clen) Tr::store1(O + ((tok0 + r) * H + h) * (int64_t)DV + col, Oa[R][j] * p.scale);
+            for (int s = 0; s < SPW; ++s)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    Tr::store1(vb + (16 * R + 4 * q4 + j) * DVT + 32 * wave + 16 * s + l16, Oa[s][R][j] * p.scale);
+        }
+        // each lane writes 16-byte pieces of this wave's 32 columns (same wave wrote them)
+        {
+            constexpr int EP = 16 / (int)sizeof(IO);      // io elements per piece
+            constexpr int PPR = 32 / EP;                  // pieces per row of the wave's columns
+            constexpr int PIECES = C * PPR;
+            IO *ob = obase + (int64_t)c * C * vstride + 32 * wave;
+#pragma unroll
+            for (int i = 0; i < (PIECES + 63) / 64; ++i) {
+                const int piece = i * 64 + lane;
+                const int r = piece / PPR, cc = (piece % PPR) * EP;
+                if (piece < PIECES && r < clen)
+                    *reinterpret_cast<uint4 *>(ob + r * vstride + cc) =
+                        *reinterpret_cast<const uint4 *>(vb + r * DVT + 32 * wave + cc);
             }
         }
 
@@ -610,24 +663,33 @@ __global__ void __launch_bounds__(64 * NW) kda_scan_kernel(FwdParams p, const in
 #pragma unroll
         for (int ct = 0; ct < KT; ++ct) {
             const float4 gm = *reinterpret_cast<const float4 *>(gam + 16 * ct + 4 * q4);
-            St[ct][0] *= gm.x;
-            St[ct][1] *= gm.y;
-            St[ct][2] *= gm.z;
-            St[ct][3] *= gm.w;
+#pragma unroll
+            for (int s = 0; s < SPW; ++s) {
+                St[s][ct][0] *= gm.x;
+                St[s][ct][1] *= gm.y;
+                St[s][ct][2] *= gm.z;
+                St[s][ct][3] *= gm.w;
+            }
 #pragma unroll
             for (int pp = 0; pp < NPAIR; ++pp) {
                 Frag<BF> a0, a1;
                 load_pair<BF>(rb + Rec::oKbT + (size_t)(ct * NPAIR + pp) * Rec::TILE_BYTES, lane, a0, a1);
-                mma32(St[ct], a0, a1, Db[2 * pp], Db[2 * pp + 1]);
+#pragma unroll
+                for (int s = 0; s < SPW; ++s) mma32(St[s][ct], a0, a1, Db[s][2 * pp], Db[s][2 * pp + 1]);
             }
         }
+        __syncthreads();  // (B) done with chunk c: the copy wave may refill its buffers
     }
 
     if (p.sf) {
 #pragma unroll
-        for (int ct = 0; ct < KT; ++ct)
+        for (int s = 0; s < SPW; ++s) {
+            const int col = col0 + 32 * wave + 16 * s + l16;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) p.sf[sbase + (int64_t)(16 * ct + 4 * q4 + j) * DV + col] = St[ct][j];
+            for (int ct = 0; ct < KT; ++ct)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) p.sf[sbase + (int64_t)(16 * ct + 4 * q4 + j) * DV + col] = St[s][ct][j];
+        }
     }
 }
 
@@ -662,19 +724,20 @@ hipError_t launch_split_variant(const FwdParams &p, char *workspace, int64_t chu
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
-        const int64_t scan_blocks = (int64_t)p.num_seqs * p.H * (p.dv / (16 * NW));
+        const int64_t scan_blocks = (int64_t)p.num_seqs * p.H * (p.dv / ScanLayout<IO, DK, C, NW>::DVT);
         if (scan_blocks > 0) {
-            hipLaunchKernelGGL((kda_scan_kernel<IO, DK, C, NW>), dim3((unsigned)scan_blocks), dim3(64 * NW), 0, stream,
-                               p, chunk_off, records);
+            hipLaunchKernelGGL((kda_scan_kernel<IO, DK, C, NW>), dim3((unsigned)scan_blocks), dim3(64 * (NW + 1)), 0,
+                               stream, p, chunk_off, records);
             return hipGetLastError();
         }
         return hipSuccess;
     }
 }
 
+// F(DK, C, NW): NW compute waves of 32 state columns each (d_v tile 32 * NW)
 #define KDA_SPLIT_VARIANTS(F) \
-    F(64, 16, 4) F(64, 32, 4) F(64, 64, 4) F(128, 16, 4) F(128, 32, 4) F(128, 64, 4) \
-    F(64, 16, 2) F(64, 32, 2) F(64, 64, 2) F(128, 16, 2) F(128, 32, 2) F(128, 64, 2)
+    F(64, 16, 2) F(64, 32, 2) F(64, 64, 2) F(128, 16, 2) F(128, 32, 2) F(128, 64, 2) \
+    F(64, 16, 1) F(64, 32, 1) F(64, 64, 1) F(128, 16, 1) F(128, 32, 1) F(128, 64, 1)
 
 template <typename IO>
 size_t split_record_size(int dk, int chunk) {
