@@ -10,7 +10,8 @@ One step = one pass of the hot path over one batch of synthetic input:
 reported in GB/s next to it.  Inputs are resident in HBM before the timed region.
 Timing uses HIP events recorded on the stream the kernels are launched on.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--dv-tile T] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--algo auto|fused|two_pass] [--dv-tile T]
+                       [--no-cpu-baseline]
 """
 import argparse
 import json
@@ -32,9 +33,13 @@ def log(*a):
 
 
 def time_launches(fn, n, stream):
-    """Average duration of one call of fn (ms), from HIP events around n back-to-back calls."""
+    """Average duration of one call of fn (ms), from HIP events around n back-to-back calls.
+
+    One call is queued before the start event so the stream is already busy when the event
+    fires: the measured span then holds the n calls' GPU time, not the host's launch delay."""
     import torch
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()
     start.record(stream)
     for _ in range(n):
         fn()
@@ -117,6 +122,7 @@ def main():
     t_dec = time_launches(decode, args.steps, stream)
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    decode()
     start.record(stream)
     for _ in range(args.steps):
         prefill()
@@ -152,7 +158,8 @@ def main():
                    "workspace_bytes": q["workspace_bytes"], "device": q["arch"], "compute_units": q["compute_units"]},
         "roofline": {"bound": "hbm", "achieved": round(pre_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(pre_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
-                     "kernel": "kda_chunk_fwd_kernel", "launch_ms": round(t_pre, 4),
+                     "kernel": "kda_chunk_fwd (" + ["auto", "fused", "two_pass"][q["algo"]] + ")",
+                     "launch_ms": round(t_pre, 4),
                      "bytes_per_launch": pre_bytes},
         "prefill": {"ms": round(t_pre, 4), "tokens_per_s": round(pre_tps, 1), "gb_per_s": round(pre_gbps, 1),
                     "hbm_frac": round(pre_gbps / PEAK_HBM_GBPS, 4), "tflops": round(pre_tflops, 2),
