@@ -446,13 +446,18 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
 // Workgroup = NW compute waves (each owns 32 state columns = two 16-column slices, so
 // every operand fragment read from LDS feeds two matrix-core products) + 1 copy wave
 // that queues the asynchronous global->LDS copies of the next chunk's record and V tile.
+//
+// The output is produced transposed, O^T = S^T Q~^T + D^T P^T: the state's accumulator
+// fragments are exactly the operand fragments of S^T, D's accumulator fragments those of
+// D^T, and the record's Q~ and P fragments serve unchanged as Q~^T and P^T.  Each lane then
+// holds 4 consecutive output columns of one token and stores them with one 8-byte write.
 template <typename IO, int DK, int C, int NW>
 struct ScanLayout {
     using Rec = SplitRecord<IO, DK, C>;
     static constexpr int SPW = 2;               // 16-column slices per compute wave
     static constexpr int DVT = 16 * SPW * NW;   // state columns per workgroup
     static constexpr int NT = 64 * (NW + 1);    // threads (compute waves + copy wave)
-    static constexpr size_t kVBytes = (size_t)C * DVT * sizeof(IO);
+    static constexpr size_t kVBytes = (size_t)C * DVT * sizeof(IO);  // V tile [C][DVT]
     static constexpr int V_PIECES = (int)(kVBytes / 16);
     static constexpr size_t oRec0 = 0;
     static constexpr size_t oRec1 = Rec::kBytes;
@@ -474,14 +479,13 @@ __device__ __forceinline__ void stage_chunk(char *lds_rec, char *lds_v, const ch
     for (int u = 0; u < REC_UNITS; ++u)
         __builtin_amdgcn_global_load_lds(rec + (size_t)u * 1024 + lane * 16,
                                          (__attribute__((address_space(3))) void *)(lds_rec + u * 1024), 16, 0, 0);
-    constexpr int PPR = S::DVT * (int)sizeof(IO) / 16;  // 16-byte pieces per V row
-    constexpr int V_UNITS = S::V_PIECES / 64;
+    constexpr int EP = 16 / (int)sizeof(IO);
+    constexpr int PPR = S::DVT / EP;  // 16-byte pieces per V row
 #pragma unroll
-    for (int u = 0; u < V_UNITS; ++u) {
+    for (int u = 0; u < S::V_PIECES / 64; ++u) {
         const int piece = u * 64 + lane;
         const int r = min(piece / PPR, clen - 1);  // rows past the end re-read the last row
-        const int cc = (piece % PPR) * (16 / (int)sizeof(IO));
-        __builtin_amdgcn_global_load_lds(vrow0 + r * vstride + cc,
+        __builtin_amdgcn_global_load_lds(vrow0 + r * vstride + (piece % PPR) * EP,
                                          (__attribute__((address_space(3))) void *)(lds_v + u * 1024), 16, 0, 0);
     }
 }
@@ -541,7 +545,7 @@ __global__ void __launch_bounds__(64 * (NW + 1)) kda_scan_kernel(FwdParams p, co
         return;
     }
 
-    // ---------------- compute waves: slices s = 0, 1 hold columns col0 + 32*wave + 16*s + l16
+    // ---------------- compute waves: slice s holds state columns col0 + 32*wave + 16*s + l16
     f32x4 St[SPW][KT];
     const int64_t sbase = ((int64_t)n * H + h) * DK * DV;
 #pragma unroll
@@ -553,12 +557,13 @@ __global__ void __launch_bounds__(64 * (NW + 1)) kda_scan_kernel(FwdParams p, co
             for (int j = 0; j < 4; ++j)
                 St[s][ct][j] = p.s0 ? p.s0[sbase + (int64_t)(16 * ct + 4 * q4 + j) * DV + col] : 0.f;
     }
+    __builtin_amdgcn_s_waitcnt(0);
 
     for (int c = 0; c < nchunks; ++c) {
         const int clen = min(C, len - c * C);
         __syncthreads();  // (A) chunk c is in LDS
         const char *rb = smem + ((c & 1) ? S::oRec1 : S::oRec0);
-        IO *vb = reinterpret_cast<IO *>(smem + ((c & 1) ? S::oV1 : S::oV0));
+        const IO *vb = reinterpret_cast<const IO *>(smem + ((c & 1) ? S::oV1 : S::oV0));
 
         Frag<BF> Sb[SPW][KT];
 #pragma unroll
@@ -566,13 +571,16 @@ __global__ void __launch_bounds__(64 * (NW + 1)) kda_scan_kernel(FwdParams p, co
 #pragma unroll
             for (int ct = 0; ct < KT; ++ct) Sb[s][ct] = frag_from_acc<BF>(St[s][ct]);
 
-        // K~ S and Q~ S; Y = V - K~ S (rows past the chunk end hold finite filler: T zeroes them)
-        f32x4 Y[SPW][NSUB], Oa[SPW][NSUB];
+        // Y = V - K~ S   and   O^T = S^T Q~^T   (rows past the chunk end: finite filler, T zeroes them)
+        f32x4 Y[SPW][NSUB], Ot[SPW][NSUB];
 #pragma unroll
         for (int rt = 0; rt < NSUB; ++rt) {
-            f32x4 ak[SPW], ao[SPW];
+            f32x4 ak[SPW];
 #pragma unroll
-            for (int s = 0; s < SPW; ++s) ak[s] = ao[s] = zero4();
+            for (int s = 0; s < SPW; ++s) {
+                ak[s] = zero4();
+                Ot[s][rt] = zero4();
+            }
 #pragma unroll
             for (int kp = 0; kp < KT / 2; ++kp) {
                 Frag<BF> a0, a1, b0, b1;
@@ -581,18 +589,14 @@ __global__ void __launch_bounds__(64 * (NW + 1)) kda_scan_kernel(FwdParams p, co
 #pragma unroll
                 for (int s = 0; s < SPW; ++s) {
                     mma32(ak[s], a0, a1, Sb[s][2 * kp], Sb[s][2 * kp + 1]);
-                    mma32(ao[s], b0, b1, Sb[s][2 * kp], Sb[s][2 * kp + 1]);
+                    mma32(Ot[s][rt], Sb[s][2 * kp], Sb[s][2 * kp + 1], b0, b1);
                 }
             }
 #pragma unroll
-            for (int s = 0; s < SPW; ++s) {
+            for (int s = 0; s < SPW; ++s)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = 16 * rt + 4 * q4 + j;
-                    Y[s][rt][j] = Tr::load1(vb + r * DVT + 32 * wave + 16 * s + l16) - ak[s][j];
-                }
-                Oa[s][rt] = ao[s];
-            }
+                for (int j = 0; j < 4; ++j)
+                    Y[s][rt][j] = Tr::load1(vb + (16 * rt + 4 * q4 + j) * DVT + 32 * wave + 16 * s + l16) - ak[s][j];
         }
 
         // D = T Y
@@ -625,57 +629,57 @@ __global__ void __launch_bounds__(64 * (NW + 1)) kda_scan_kernel(FwdParams p, co
                 for (int s = 0; s < SPW; ++s) Db[s][NSUB] = make_frag<BF>(0.f, 0.f, 0.f, 0.f);
         }
 
-        // O = scale (Q~ S + P D), staged in this wave's columns of the (consumed) V tile
+        // O^T += D^T P^T; lane holds columns 16 s + 4 q4 .. +3 of token 16 R + l16
 #pragma unroll
         for (int R = 0; R < NSUB; ++R) {
 #pragma unroll
             for (int pp = 0; pp < NPAIR; ++pp) {
                 if (2 * pp > R) break;
-                Frag<BF> a0, a1;
-                load_pair<BF>(rb + Rec::oP + (size_t)(R * NPAIR + pp) * Rec::TILE_BYTES, lane, a0, a1);
+                Frag<BF> b0, b1;
+                load_pair<BF>(rb + Rec::oP + (size_t)(R * NPAIR + pp) * Rec::TILE_BYTES, lane, b0, b1);
 #pragma unroll
-                for (int s = 0; s < SPW; ++s) mma32(Oa[s][R], a0, a1, Db[s][2 * pp], Db[s][2 * pp + 1]);
-            }
-#pragma unroll
-            for (int s = 0; s < SPW; ++s)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    Tr::store1(vb + (16 * R + 4 * q4 + j) * DVT + 32 * wave + 16 * s + l16, Oa[s][R][j] * p.scale);
-        }
-        // each lane writes 16-byte pieces of this wave's 32 columns (same wave wrote them)
-        {
-            constexpr int EP = 16 / (int)sizeof(IO);      // io elements per piece
-            constexpr int PPR = 32 / EP;                  // pieces per row of the wave's columns
-            constexpr int PIECES = C * PPR;
-            IO *ob = obase + (int64_t)c * C * vstride + 32 * wave;
-#pragma unroll
-            for (int i = 0; i < (PIECES + 63) / 64; ++i) {
-                const int piece = i * 64 + lane;
-                const int r = piece / PPR, cc = (piece % PPR) * EP;
-                if (piece < PIECES && r < clen)
-                    *reinterpret_cast<uint4 *>(ob + r * vstride + cc) =
-                        *reinterpret_cast<const uint4 *>(vb + r * DVT + 32 * wave + cc);
+                for (int s = 0; s < SPW; ++s) mma32(Ot[s][R], Db[s][2 * pp], Db[s][2 * pp + 1], b0, b1);
             }
         }
 
-        // S <- Gamma S + K-^T D
+        // M = K-^T D (fresh accumulators); the state itself stays in plain registers and is
+        // updated as S <- Gamma * S + M once the products are done
+        f32x4 M[SPW][KT];
+#pragma unroll
+        for (int ct = 0; ct < KT; ++ct) {
+#pragma unroll
+            for (int s = 0; s < SPW; ++s) M[s][ct] = zero4();
+#pragma unroll
+            for (int pp = 0; pp < NPAIR; ++pp) {
+                Frag<BF> a0, a1;
+                load_pair<BF>(rb + Rec::oKbT + (size_t)(ct * NPAIR + pp) * Rec::TILE_BYTES, lane, a0, a1);
+#pragma unroll
+                for (int s = 0; s < SPW; ++s) mma32(M[s][ct], a0, a1, Db[s][2 * pp], Db[s][2 * pp + 1]);
+            }
+        }
+
+        IO *oc = obase + (int64_t)c * C * vstride + 32 * wave + 4 * q4;
+#pragma unroll
+        for (int R = 0; R < NSUB; ++R) {
+            const int r = 16 * R + l16;
+            if (r < clen) {
+#pragma unroll
+                for (int s = 0; s < SPW; ++s)
+                    Tr::store4(oc + r * vstride + 16 * s, make_float4(Ot[s][R][0] * p.scale, Ot[s][R][1] * p.scale,
+                                                                    Ot[s][R][2] * p.scale, Ot[s][R][3] * p.scale));
+            }
+        }
+
         const float *gam = reinterpret_cast<const float *>(rb + Rec::oGam);
 #pragma unroll
         for (int ct = 0; ct < KT; ++ct) {
             const float4 gm = *reinterpret_cast<const float4 *>(gam + 16 * ct + 4 * q4);
 #pragma unroll
             for (int s = 0; s < SPW; ++s) {
-                St[s][ct][0] *= gm.x;
-                St[s][ct][1] *= gm.y;
-                St[s][ct][2] *= gm.z;
-                St[s][ct][3] *= gm.w;
-            }
-#pragma unroll
-            for (int pp = 0; pp < NPAIR; ++pp) {
-                Frag<BF> a0, a1;
-                load_pair<BF>(rb + Rec::oKbT + (size_t)(ct * NPAIR + pp) * Rec::TILE_BYTES, lane, a0, a1);
-#pragma unroll
-                for (int s = 0; s < SPW; ++s) mma32(St[s][ct], a0, a1, Db[s][2 * pp], Db[s][2 * pp + 1]);
+                St[s][ct][0] = fmaf(gm.x, St[s][ct][0], M[s][ct][0]);
+                St[s][ct][1] = fmaf(gm.y, St[s][ct][1], M[s][ct][1]);
+                St[s][ct][2] = fmaf(gm.z, St[s][ct][2], M[s][ct][2]);
+                St[s][ct][3] = fmaf(gm.w, St[s][ct][3], M[s][ct][3]);
             }
         }
         __syncthreads();  // (B) done with chunk c: the copy wave may refill its buffers
