@@ -317,7 +317,7 @@ kda_status_t kda_decode_step(int32_t num_seqs, int32_t num_heads, int32_t head_d
             return fail(KDA_ERR_UNSUPPORTED, "head dims d_k=%d d_v=%d: supported are 64 and 128", head_dim_k,
                         head_dim_v);
         if (!std::isfinite(scale)) return fail(KDA_ERR_INVALID_ARGUMENT, "scale is not finite");
-        if ((int64_t)num_seqs * num_heads > 0x7fffffffLL)
+        if ((int64_t)num_seqs * num_heads * (head_dim_v / 32) > 0x7fffffffLL)
             return fail(KDA_ERR_UNSUPPORTED, "too many (sequence, head) pairs");
         if (num_seqs == 0) return ok();
         const void *req[] = {q, k, v, g, beta, state, out};

@@ -101,37 +101,100 @@ __device__ __forceinline__ void token_update(float (&S)[RPT][4], TokenSmem<DK, D
     o4 = make_float4(a4[0] + qk * d[0], a4[1] + qk * d[1], a4[2] + qk * d[2], a4[3] + qk * d[3]);
 }
 
-template <typename IO, int DK, int DV>
-__global__ void __launch_bounds__(kSerialThreads) kda_decode_kernel(int32_t H, float scale, const IO *__restrict__ q,
-                                                                    const IO *__restrict__ k, const IO *__restrict__ v,
-                                                                    const float *__restrict__ g,
-                                                                    const float *__restrict__ beta, float *state,
-                                                                    IO *__restrict__ out) {
-    using L = SerialLayout<DK, DV>;
-    __shared__ TokenSmem<DK, DV> ts;
-    __shared__ float qk_part[4];
-    const int tid = threadIdx.x;
-    const int cg = tid % L::CG, rg = tid / L::CG;
-    const int64_t nh = blockIdx.x;  // (sequence, head)
-    float *Sg = state + nh * DK * DV;
+// Decode: one 256-thread workgroup per (sequence, head, 32-column block).  The state block
+// (d_k x 32 fp32, 16 KB at d_k = 128) is read once and written once with nontemporal
+// 16-byte accesses, 4 per thread: thread t owns columns 4*(t % 8) .. +3 of the block and
+// rows t/8 + 32*m.  Small per-thread footprints and many workgroups keep HBM busy.
+constexpr int kDecodeCols = 32;
 
-    float S[L::RPT][4];
+typedef float kda_v4f __attribute__((ext_vector_type(4)));
+
+template <typename IO, int DK, int DV>
+__global__ void __launch_bounds__(256) kda_decode_kernel(int32_t H, float scale, const IO *__restrict__ q,
+                                                         const IO *__restrict__ k, const IO *__restrict__ v,
+                                                         const float *__restrict__ g, const float *__restrict__ beta,
+                                                         float *state, IO *__restrict__ out) {
+    constexpr int NCB = DV / kDecodeCols;  // column blocks per (sequence, head)
+    constexpr int RG = 256 / 8;            // row groups
+    constexpr int RPT = DK / RG;           // rows per thread
+    __shared__ float s_alpha[DK], s_k[DK], s_q[DK], s_v[kDecodeCols];
+    __shared__ float s_beta, s_qk[4];
+    __shared__ kda_v4f s_part[2][4][8];  // per-wave partial p and S'^T q per column group
+
+    const int tid = threadIdx.x;
+    const int cg = tid & 7, rg = tid >> 3, wv = tid >> 6;
+    const int64_t nh = blockIdx.x / NCB;
+    const int cb = blockIdx.x % NCB;
+    const int col0 = cb * kDecodeCols;
+    kda_v4f *Sg = reinterpret_cast<kda_v4f *>(state + nh * DK * DV + col0) + cg;
+
+    kda_v4f S[RPT];
 #pragma unroll
-    for (int m = 0; m < L::RPT; ++m) {
-        const float4 x = *reinterpret_cast<const float4 *>(Sg + (int64_t)(rg + L::RG * m) * DV + 4 * cg);
-        S[m][0] = x.x; S[m][1] = x.y; S[m][2] = x.z; S[m][3] = x.w;
+    for (int m = 0; m < RPT; ++m) S[m] = __builtin_nontemporal_load(Sg + (int64_t)(rg + RG * m) * (DV / 4));
+
+    using Tr = IoTraits<IO>;
+    float kq = 0.f;
+    if (tid < DK) {
+        const float kk = Tr::load1(k + nh * DK + tid), qq = Tr::load1(q + nh * DK + tid);
+        s_alpha[tid] = expf(g[nh * DK + tid]);
+        s_k[tid] = kk;
+        s_q[tid] = qq;
+        kq = kk * qq;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) kq += __shfl_xor(kq, off, 64);
+        if ((tid & 63) == 0) s_qk[tid >> 6] = kq;
     }
-    stage_token<IO, DK, DV>(ts, qk_part, q + nh * DK, k + nh * DK, v + nh * DV, g + nh * DK, beta + nh, tid);
+    if (tid < kDecodeCols) s_v[tid] = Tr::load1(v + nh * DV + col0 + tid);
+    if (tid == 0) s_beta = beta[nh];
     __syncthreads();
-    float4 o4;
-    token_update<DK, DV>(S, ts, qk_part, cg, rg, o4);
+
+    // S' = Diag(alpha) S;  partial p = S'^T k and a = S'^T q over this thread's rows, then
+    // summed over the 8 row groups of the wave (lanes 8 apart) and, through LDS, the 4 waves
+    kda_v4f pp = {0.f, 0.f, 0.f, 0.f}, aa = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int m = 0; m < L::RPT; ++m)
-        *reinterpret_cast<float4 *>(Sg + (int64_t)(rg + L::RG * m) * DV + 4 * cg) =
-            make_float4(S[m][0], S[m][1], S[m][2], S[m][3]);
-    if (rg == 0)
-        IoTraits<IO>::store4(out + nh * DV + 4 * cg,
-                             make_float4(o4.x * scale, o4.y * scale, o4.z * scale, o4.w * scale));
+    for (int m = 0; m < RPT; ++m) {
+        const int i = rg + RG * m;
+        S[m] *= s_alpha[i];
+        pp += s_k[i] * S[m];
+        aa += s_q[i] * S[m];
+    }
+#pragma unroll
+    for (int off = 8; off < 64; off <<= 1) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            pp[j] += __shfl_xor(pp[j], off, 64);
+            aa[j] += __shfl_xor(aa[j], off, 64);
+        }
+    }
+    if ((tid & 63) < 8) {
+        s_part[0][wv][cg] = pp;
+        s_part[1][wv][cg] = aa;
+    }
+    __syncthreads();
+    kda_v4f ps = s_part[0][0][cg] + s_part[0][1][cg] + s_part[0][2][cg] + s_part[0][3][cg];
+
+    // d = beta (v - p);  S = S' + k d^T;  o = a + (k.q) d
+    const float b = s_beta;
+    kda_v4f d;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) d[j] = b * (s_v[4 * cg + j] - ps[j]);
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        S[m] += s_k[rg + RG * m] * d;
+        __builtin_nontemporal_store(S[m], Sg + (int64_t)(rg + RG * m) * (DV / 4));
+    }
+    if (rg == 0) {
+        float qk = 0.f;
+#pragma unroll
+        for (int w = 0; w < (DK + 63) / 64; ++w) qk += s_qk[w];
+        const kda_v4f as = s_part[1][0][cg] + s_part[1][1][cg] + s_part[1][2][cg] + s_part[1][3][cg];
+        float4 o;
+        o.x = (as[0] + qk * d[0]) * scale;
+        o.y = (as[1] + qk * d[1]) * scale;
+        o.z = (as[2] + qk * d[2]) * scale;
+        o.w = (as[3] + qk * d[3]) * scale;
+        Tr::store4(out + nh * DV + col0 + 4 * cg, o);
+    }
 }
 
 template <typename IO, int DK, int DV>
@@ -207,11 +270,11 @@ template <typename IO>
 static hipError_t decode_dispatch(int32_t N, int32_t H, int32_t dk, int32_t dv, float scale, const void *q,
                                   const void *k, const void *v, const float *g, const float *beta, float *state,
                                   void *out, hipStream_t stream) {
-    const int64_t blocks = (int64_t)N * H;
+    const int64_t blocks = (int64_t)N * H * (dv / kDecodeCols);
     if (blocks <= 0) return hipSuccess;
 #define KDA_DEC_CASE(DK_, DV_)                                                                                      \
     if (dk == DK_ && dv == DV_) {                                                                                   \
-        hipLaunchKernelGGL((kda_decode_kernel<IO, DK_, DV_>), dim3((unsigned)blocks), dim3(kSerialThreads), 0,   \
+        hipLaunchKernelGGL((kda_decode_kernel<IO, DK_, DV_>), dim3((unsigned)blocks), dim3(256), 0,              \
                            stream, H, scale, static_cast<const IO *>(q), static_cast<const IO *>(k),                \
                            static_cast<const IO *>(v), g, beta, state, static_cast<IO *>(out));                     \
         return hipGetLastError();                                                                                   \
