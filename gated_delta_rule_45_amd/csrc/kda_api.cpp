@@ -46,7 +46,7 @@ struct Resolved {
     kda::ChunkConfig cfg{64, 128};  // fused algorithm: chunk and d_v tile
     int lds = 0;                    // fused algorithm: LDS per workgroup (0 = not supported)
     bool two_pass_ok = false;       // two-pass algorithm supports the problem
-    int nw = 4;                     // two-pass: waves (16 state columns each) per scan workgroup
+    int spw = 1, nw = 2;            // two-pass: scan workgroup = nw compute waves x 16*spw state columns
     int64_t chunk_upper = 0;        // two-pass: upper bound on the number of chunks
     size_t ws_bytes = 0;            // two-pass: workspace bytes
 };
@@ -111,10 +111,13 @@ kda_status_t resolve(const kda_problem_t *p, bool varlen, Resolved &r, bool chun
         r.cfg.chunk = C;
         r.cfg.dv_tile = p->dv_tile ? p->dv_tile : default_dv_tile((int64_t)r.num_seqs * p->num_heads, p->head_dim_v);
         r.lds = kda::chunk_variant_lds_bytes(p->io_dtype, p->head_dim_k, r.cfg.dv_tile, r.cfg.chunk);
-        // two-pass: scan workgroups of nw compute waves x 32 state columns
-        r.nw = p->dv_tile == 32 ? 1 : 2;
-        r.two_pass_ok = p->dv_tile != 128 && (32 * r.nw) <= p->head_dim_v &&
-                        kda::split_variant_supported(p->io_dtype, p->head_dim_k, C, r.nw);
+        // two-pass: scan workgroups of two compute waves, each owning 16 (32-column tiles, the
+        // default) or 32 (64-column tiles) state columns
+        const int scan_cols = p->dv_tile == 64 ? 64 : 32;
+        r.spw = scan_cols == 32 ? 1 : 2;
+        r.nw = 2;
+        r.two_pass_ok = p->dv_tile != 128 && scan_cols <= p->head_dim_v &&
+                        kda::split_variant_supported(p->io_dtype, p->head_dim_k, C, r.spw, r.nw);
         if (r.two_pass_ok) {
             const int64_t per = ((int64_t)p->seq_len + C - 1) / C;
             r.chunk_upper = varlen ? per + r.num_seqs : (int64_t)r.num_seqs * per;
@@ -232,14 +235,14 @@ size_t split_workspace_bytes(kda_dtype_t io, int dk, int chunk, int64_t chunk_up
     return split_plan_bytes(num_seqs) + (size_t)chunk_upper * H * rec;
 }
 
-bool split_variant_supported(kda_dtype_t io, int dk, int chunk, int nw) {
-    return io == KDA_BF16 ? split_supported_bf16(dk, chunk, nw) : split_supported_f32(dk, chunk, nw);
+bool split_variant_supported(kda_dtype_t io, int dk, int chunk, int spw, int nw) {
+    return io == KDA_BF16 ? split_supported_bf16(dk, chunk, spw, nw) : split_supported_f32(dk, chunk, spw, nw);
 }
 
-hipError_t launch_split_fwd(kda_dtype_t io, const FwdParams &p, int chunk, int nw, char *workspace,
+hipError_t launch_split_fwd(kda_dtype_t io, const FwdParams &p, int chunk, int spw, int nw, char *workspace,
                             int64_t chunk_upper, hipStream_t stream) {
-    return io == KDA_BF16 ? launch_split_bf16(p, chunk, nw, workspace, chunk_upper, stream)
-                          : launch_split_f32(p, chunk, nw, workspace, chunk_upper, stream);
+    return io == KDA_BF16 ? launch_split_bf16(p, chunk, spw, nw, workspace, chunk_upper, stream)
+                          : launch_split_f32(p, chunk, spw, nw, workspace, chunk_upper, stream);
 }
 
 int chunk_variant_lds_bytes(kda_dtype_t io, int dk, int dv_tile, int chunk) {
@@ -273,7 +276,7 @@ kda_status_t kda_chunk_fwd(const kda_problem_t *problem, const void *q, const vo
         const kda::FwdParams fp =
             make_params(problem, r, q, k, v, g, beta, initial_state, cu_seqlens, out, final_state);
         if (algo == KDA_ALGO_TWO_PASS)
-            return hip_status(kda::launch_split_fwd(problem->io_dtype, fp, r.cfg.chunk, r.nw,
+            return hip_status(kda::launch_split_fwd(problem->io_dtype, fp, r.cfg.chunk, r.spw, r.nw,
                                                     static_cast<char *>(workspace), r.chunk_upper,
                                                     static_cast<hipStream_t>(stream)),
                               "kda_chunk_fwd (two-pass) launch");
@@ -357,11 +360,11 @@ kda_status_t kda_query(const kda_problem_t *problem, uint32_t flags, kda_query_r
             res->algo = two ? KDA_ALGO_TWO_PASS : KDA_ALGO_FUSED;
             res->workspace_bytes = two ? r.ws_bytes : 0;
             res->chunk_size = r.cfg.chunk;
-            if (two) {  // the scan pass: one workgroup per (sequence, head, 32*nw columns)
-                res->dv_tile = 32 * r.nw;
-                res->threads_per_block = 64 * (r.nw + 1);
+            if (two) {  // the scan pass: one workgroup per (sequence, head, 16*spw*nw columns)
+                res->dv_tile = 16 * r.spw * r.nw;
+                res->threads_per_block = 64 * (r.nw + (r.spw == 1 ? 4 : 2));
                 res->lds_bytes = 0;
-                res->grid_blocks = (int64_t)r.num_seqs * p.num_heads * (p.head_dim_v / (32 * r.nw));
+                res->grid_blocks = (int64_t)r.num_seqs * p.num_heads * (p.head_dim_v / res->dv_tile);
             } else {
                 res->dv_tile = r.cfg.dv_tile;
                 res->threads_per_block = kda::kChunkThreads;

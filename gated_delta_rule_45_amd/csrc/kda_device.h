@@ -25,6 +25,7 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -151,6 +152,7 @@ struct IoTraits<float> {
     // 4 consecutive io values -> fp32
     __device__ static __forceinline__ float4 load4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
     __device__ static __forceinline__ float load1(const float *p) { return *p; }
+    __device__ static __forceinline__ float to_float(float x) { return x; }
     __device__ static __forceinline__ void store1(float *p, float x) { *p = x; }
     __device__ static __forceinline__ void store4(float *p, float4 x) { *reinterpret_cast<float4 *>(p) = x; }
 };
@@ -162,6 +164,7 @@ struct IoTraits<uint16_t> {
         return make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
     }
     __device__ static __forceinline__ float load1(const uint16_t *p) { return bf16_to_f32(*p); }
+    __device__ static __forceinline__ float to_float(uint16_t x) { return bf16_to_f32(x); }
     __device__ static __forceinline__ void store1(uint16_t *p, float x) { *p = f32_to_bf16(x); }
     __device__ static __forceinline__ void store4(uint16_t *p, float4 x) {
         uint2 w;

@@ -47,17 +47,17 @@ constexpr int kChunkThreads = 256;
 // Two-pass forward: bytes of the chunk-offset table at the start of the workspace.
 inline size_t split_plan_bytes(int64_t num_seqs) { return (size_t)(((num_seqs + 1) * 4 + 255) / 256 * 256); }
 size_t split_workspace_bytes(kda_dtype_t io, int dk, int chunk, int64_t chunk_upper, int H, int64_t num_seqs);
-bool split_variant_supported(kda_dtype_t io, int dk, int chunk, int nw);
-hipError_t launch_split_fwd(kda_dtype_t io, const FwdParams &p, int chunk, int nw, char *workspace,
+bool split_variant_supported(kda_dtype_t io, int dk, int chunk, int spw, int nw);
+hipError_t launch_split_fwd(kda_dtype_t io, const FwdParams &p, int chunk, int spw, int nw, char *workspace,
                             int64_t chunk_upper, hipStream_t stream);
 // one entry per io dtype
 size_t split_record_size_f32(int dk, int chunk);
 size_t split_record_size_bf16(int dk, int chunk);
-bool split_supported_f32(int dk, int chunk, int nw);
-bool split_supported_bf16(int dk, int chunk, int nw);
-hipError_t launch_split_f32(const FwdParams &p, int chunk, int nw, char *workspace, int64_t chunk_upper,
+bool split_supported_f32(int dk, int chunk, int spw, int nw);
+bool split_supported_bf16(int dk, int chunk, int spw, int nw);
+hipError_t launch_split_f32(const FwdParams &p, int chunk, int spw, int nw, char *workspace, int64_t chunk_upper,
                             hipStream_t stream);
-hipError_t launch_split_bf16(const FwdParams &p, int chunk, int nw, char *workspace, int64_t chunk_upper,
+hipError_t launch_split_bf16(const FwdParams &p, int chunk, int spw, int nw, char *workspace, int64_t chunk_upper,
                              hipStream_t stream);
 constexpr int kSerialThreads = 256;
 

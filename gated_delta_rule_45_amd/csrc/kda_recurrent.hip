@@ -123,8 +123,11 @@ __global__ void __launch_bounds__(256) kda_decode_kernel(int32_t H, float scale,
 
     const int tid = threadIdx.x;
     const int cg = tid & 7, rg = tid >> 3, wv = tid >> 6;
-    const int64_t nh = blockIdx.x / NCB;
-    const int cb = blockIdx.x % NCB;
+    // the NCB column blocks of one (sequence, head) run on one XCD, so their shared q, k and
+    // gate reads come from HBM once and from that XCD's L2 after
+    const int64_t item = xcd_grouped_block(blockIdx.x, (int64_t)gridDim.x);
+    const int64_t nh = item / NCB;
+    const int cb = (int)(item % NCB);
     const int col0 = cb * kDecodeCols;
     kda_v4f *Sg = reinterpret_cast<kda_v4f *>(state + nh * DK * DV + col0) + cg;
 

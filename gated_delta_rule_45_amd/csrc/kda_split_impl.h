@@ -16,9 +16,9 @@
 // in matrix-core fragment order: each 16 x 32 operand tile is 64 lanes x 8 values, so the
 // scan reads every fragment with one 16-byte load per lane.
 //
-// Pass 2 (kda_scan_kernel): one workgroup per (sequence, head, d_v tile); each wave owns a
-// 16-column slice of the fp32 state.  Per chunk, with the record staged in LDS by
-// asynchronous global->LDS copies issued one chunk ahead:
+// Pass 2 (kda_scan_kernel): one workgroup per (sequence, head, d_v tile); each compute wave
+// owns 16 or 32 columns of the fp32 state, kept in registers.  Per chunk, with the record
+// staged in LDS by copy waves that load it one or two chunks ahead:
 //
 //   Y = V - K~ S        D = T Y         O = scale (Q~ S + P D)        S <- Gamma S + K-^T D
 //
@@ -73,6 +73,17 @@ __device__ __forceinline__ void load_pair(const char *tile, int lane, Frag<BF> &
         a.v = *reinterpret_cast<const float4 *>(tile + lane * 32);
         b.v = *reinterpret_cast<const float4 *>(tile + lane * 32 + 16);
     }
+}
+
+template <bool BF>
+struct FragPair {
+    Frag<BF> a, b;
+};
+template <bool BF>
+__device__ __forceinline__ FragPair<BF> ld_pair(const char *tile, int lane) {
+    FragPair<BF> f;
+    load_pair<BF>(tile, lane, f.a, f.b);
+    return f;
 }
 
 // Sequence n and chunk c of global chunk index gidx; false if gidx is past the last chunk.
@@ -443,20 +454,27 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
 }
 
 // ------------------------------------------------------------------- scan ----
-// Workgroup = NW compute waves (each owns 32 state columns = two 16-column slices, so
-// every operand fragment read from LDS feeds two matrix-core products) + 1 copy wave
-// that queues the asynchronous global->LDS copies of the next chunk's record and V tile.
+// Workgroup = NW compute waves, each owning SPW 16-column slices of the state (with two
+// slices every operand fragment read from LDS feeds two matrix-core products), plus the
+// copy waves that stage each chunk's record and V tile in LDS.
 //
 // The output is produced transposed, O^T = S^T Q~^T + D^T P^T: the state's accumulator
 // fragments are exactly the operand fragments of S^T, D's accumulator fragments those of
 // D^T, and the record's Q~ and P fragments serve unchanged as Q~^T and P^T.  Each lane then
 // holds 4 consecutive output columns of one token and stores them with one 8-byte write.
-template <typename IO, int DK, int C, int NW>
+// Copy waves per scan workgroup.  Each pair of copy waves holds one chunk's record and V tile
+// in registers on the way to LDS.  With 16-column compute waves two pairs take turns, so each
+// chunk's loads are issued two chunks ahead (a third pair measured no faster); the wider
+// compute waves need every register of their SIMD and keep a single pair, one chunk ahead.
+constexpr int scan_copy_waves(int spw) { return spw == 1 ? 4 : 2; }
+
+template <typename IO, int DK, int C, int SPW, int NW>
 struct ScanLayout {
     using Rec = SplitRecord<IO, DK, C>;
-    static constexpr int SPW = 2;               // 16-column slices per compute wave
-    static constexpr int DVT = 16 * SPW * NW;   // state columns per workgroup
-    static constexpr int NT = 64 * (NW + 1);    // threads (compute waves + copy wave)
+    static constexpr int WCOLS = 16 * SPW;      // state columns per compute wave (SPW 16-column slices)
+    static constexpr int DVT = WCOLS * NW;      // state columns per workgroup
+    static constexpr int NCW = scan_copy_waves(SPW);
+    static constexpr int NT = 64 * (NW + NCW);  // threads (compute waves + copy waves)
     static constexpr size_t kVBytes = (size_t)C * DVT * sizeof(IO);  // V tile [C][DVT]
     static constexpr int V_PIECES = (int)(kVBytes / 16);
     static constexpr size_t oRec0 = 0;
@@ -467,36 +485,102 @@ struct ScanLayout {
     static constexpr bool kFits = kBytes <= 160 * 1024;
     static_assert(Rec::kBytes % (64 * 16) == 0, "record is copied in whole wave units");
     static_assert(V_PIECES % 64 == 0, "V tile is copied in whole wave units");
+    static_assert(!kFits || (Rec::kBytes / 1024 + V_PIECES / 64 + 1) / 2 <= 40, "copy wave register budget");
 };
 
-// Copy wave: queue the asynchronous copy of one chunk's record and V tile into LDS.
-template <typename IO, int DK, int C, int NW>
-__device__ __forceinline__ void stage_chunk(char *lds_rec, char *lds_v, const char *rec, const IO *vrow0, int clen,
-                                            int64_t vstride, int lane) {
-    using S = ScanLayout<IO, DK, C, NW>;
-    constexpr int REC_UNITS = (int)(S::Rec::kBytes / 1024);  // one instruction = 64 lanes x 16 B
-#pragma unroll 4
-    for (int u = 0; u < REC_UNITS; ++u)
-        __builtin_amdgcn_global_load_lds(rec + (size_t)u * 1024 + lane * 16,
-                                         (__attribute__((address_space(3))) void *)(lds_rec + u * 1024), 16, 0, 0);
-    constexpr int EP = 16 / (int)sizeof(IO);
-    constexpr int PPR = S::DVT / EP;  // 16-byte pieces per V row
+// One copy wave's half of a chunk's record and V tile (1 KB units dealt alternately to the two
+// waves of a pair).  The units are loaded into registers (16 bytes per lane, all in flight at
+// once) and later written to LDS; on gfx950 this moves about twice the bytes per cycle of the
+// direct global->LDS copy.
+template <typename IO, int DK, int C, int SPW, int NW, int HALF>
+struct ChunkStager {
+    using S = ScanLayout<IO, DK, C, SPW, NW>;
+    static constexpr int REC_UNITS = (int)(S::Rec::kBytes / 1024);
+    static constexpr int UNITS = REC_UNITS + S::V_PIECES / 64;
+    static constexpr int PER = (UNITS - HALF + 1) / 2;  // units of this wave
+    static constexpr int EP = 16 / (int)sizeof(IO);
+    static constexpr int PPR = S::DVT / EP;  // 16-byte pieces per V row
+    // A native vector type: HIP's uint4 is a union that the compiler leaves in scratch
+    // memory when it stays live across the copy loop.
+    u32x4 r[PER];
+
+    __device__ __forceinline__ void load(const char *rec, const IO *vrow0, int clen, int64_t vstride, int lane) {
 #pragma unroll
-    for (int u = 0; u < S::V_PIECES / 64; ++u) {
-        const int piece = u * 64 + lane;
-        const int r = min(piece / PPR, clen - 1);  // rows past the end re-read the last row
-        __builtin_amdgcn_global_load_lds(vrow0 + r * vstride + (piece % PPR) * EP,
-                                         (__attribute__((address_space(3))) void *)(lds_v + u * 1024), 16, 0, 0);
+        for (int i = 0; i < PER; ++i) {
+            const int u = HALF + 2 * i;
+            if (u < REC_UNITS) {
+                r[i] = *reinterpret_cast<const u32x4 *>(rec + (size_t)u * 1024 + lane * 16);
+            } else {
+                const int piece = (u - REC_UNITS) * 64 + lane;
+                const int row = min(piece / PPR, clen - 1);  // rows past the end re-read the last row
+                r[i] = *reinterpret_cast<const u32x4 *>(vrow0 + row * vstride + (piece % PPR) * EP);
+            }
+        }
     }
+    __device__ __forceinline__ void store(char *lds_rec, char *lds_v, int lane) const {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int u = HALF + 2 * i;
+            char *dst = u < REC_UNITS ? lds_rec + u * 1024 : lds_v + (u - REC_UNITS) * 1024;
+            *reinterpret_cast<u32x4 *>(dst + lane * 16) = r[i];
+        }
+    }
+};
+
+// Copy wave CW.  Pair CW / 2 stages the chunks j with j % NPAIR == CW / 2.  Barrier c hands
+// chunk c to the compute waves; passing it also means every compute wave has finished chunk
+// c - 1, so that buffer may take chunk c + 1 (written from the registers of its pair, which
+// then load their next chunk).
+template <typename IO, int DK, int C, int SPW, int NW, int CW>
+__device__ __forceinline__ void copy_wave(char *smem, const char *rec0, size_t rec_stride, const IO *vbase,
+                                          int64_t vstride, int len, int nchunks, int lane) {
+    using S = ScanLayout<IO, DK, C, SPW, NW>;
+    constexpr int NPAIR = S::NCW / 2, PAIR = CW / 2;
+    ChunkStager<IO, DK, C, SPW, NW, CW % 2> st;
+#define KDA_STAGE_LOAD(j) \
+    st.load(rec0 + (size_t)(j) * rec_stride, vbase + (int64_t)(j) * C * vstride, min(C, len - (j) * C), vstride, lane)
+#define KDA_STAGE_STORE(j) \
+    st.store(smem + (((j) & 1) ? S::oRec1 : S::oRec0), smem + (((j) & 1) ? S::oV1 : S::oV0), lane)
+    if constexpr (NPAIR == 1) {
+        if (nchunks > 0) {
+            KDA_STAGE_LOAD(0);
+            KDA_STAGE_STORE(0);
+        }
+        for (int c = 0; c < nchunks; ++c) {
+            __syncthreads();
+            if (c + 1 < nchunks) {
+                KDA_STAGE_LOAD(c + 1);
+                KDA_STAGE_STORE(c + 1);
+            }
+        }
+    } else {
+        // pair p stages the chunks j with j % NPAIR == p, each loaded NPAIR chunks ahead
+        if (PAIR < nchunks) {
+            KDA_STAGE_LOAD(PAIR);
+            if (PAIR == 0) {
+                KDA_STAGE_STORE(0);
+                if (NPAIR < nchunks) KDA_STAGE_LOAD(NPAIR);
+            }
+        }
+        for (int c = 0; c < nchunks; ++c) {
+            __syncthreads();  // barrier c: the buffer of chunk c + 1 is free
+            if ((c + 1) % NPAIR == PAIR && c + 1 < nchunks) {
+                KDA_STAGE_STORE(c + 1);
+                if (c + 1 + NPAIR < nchunks) KDA_STAGE_LOAD(c + 1 + NPAIR);
+            }
+        }
+    }
+#undef KDA_STAGE_LOAD
+#undef KDA_STAGE_STORE
 }
 
-template <typename IO, int DK, int C, int NW>
-__global__ void __launch_bounds__(64 * (NW + 1)) kda_scan_kernel(FwdParams p, const int32_t *__restrict__ chunk_off,
+template <typename IO, int DK, int C, int SPW, int NW>
+__global__ void __launch_bounds__(64 * (NW + scan_copy_waves(SPW))) kda_scan_kernel(FwdParams p, const int32_t *__restrict__ chunk_off,
                                                                   const char *__restrict__ records) {
-    using S = ScanLayout<IO, DK, C, NW>;
+    using S = ScanLayout<IO, DK, C, SPW, NW>;
     using Rec = typename S::Rec;
     constexpr bool BF = Rec::BF;
-    constexpr int NSUB = Rec::NSUB, KT = Rec::KT, NPAIR = Rec::NPAIR, DVT = S::DVT, SPW = S::SPW;
+    constexpr int NSUB = Rec::NSUB, KT = Rec::KT, NPAIR = Rec::NPAIR, DVT = S::DVT, WC = S::WCOLS;
     using Tr = IoTraits<IO>;
 
     __shared__ __attribute__((aligned(16))) char smem[S::kBytes];
@@ -530,27 +614,36 @@ __global__ void __launch_bounds__(64 * (NW + 1)) kda_scan_kernel(FwdParams p, co
     const char *rec0 = records + (size_t)(g0 * H + h) * Rec::kBytes;
     const size_t rec_stride = (size_t)H * Rec::kBytes;
 
-    if (wave == NW) {
-        // ---------------- copy wave: stays one chunk ahead of the compute waves
-        if (nchunks > 0) stage_chunk<IO, DK, C, NW>(smem + S::oRec0, smem + S::oV0, rec0, vbase, min(C, len), vstride, lane);
-        for (int c = 0; c < nchunks; ++c) {
-            __builtin_amdgcn_s_waitcnt(0);  // chunk c has landed in LDS
-            __syncthreads();                // (A) hand chunk c to the compute waves
-            if (c + 1 < nchunks)
-                stage_chunk<IO, DK, C, NW>(smem + ((c & 1) ? S::oRec0 : S::oRec1), smem + ((c & 1) ? S::oV0 : S::oV1),
-                                           rec0 + (size_t)(c + 1) * rec_stride, vbase + (int64_t)(c + 1) * C * vstride,
-                                           min(C, len - (c + 1) * C), vstride, lane);
-            __syncthreads();  // (B) compute waves are done with chunk c
+    if (wave >= NW) {
+        switch (wave - NW) {
+            case 0: copy_wave<IO, DK, C, SPW, NW, 0>(smem, rec0, rec_stride, vbase, vstride, len, nchunks, lane); break;
+            case 1: copy_wave<IO, DK, C, SPW, NW, 1>(smem, rec0, rec_stride, vbase, vstride, len, nchunks, lane); break;
+            case 2:
+                if constexpr (S::NCW > 2)
+                    copy_wave<IO, DK, C, SPW, NW, 2>(smem, rec0, rec_stride, vbase, vstride, len, nchunks, lane);
+                break;
+            case 3:
+                if constexpr (S::NCW > 3)
+                    copy_wave<IO, DK, C, SPW, NW, 3>(smem, rec0, rec_stride, vbase, vstride, len, nchunks, lane);
+                break;
+            case 4:
+                if constexpr (S::NCW > 4)
+                    copy_wave<IO, DK, C, SPW, NW, 4>(smem, rec0, rec_stride, vbase, vstride, len, nchunks, lane);
+                break;
+            default:
+                if constexpr (S::NCW > 5)
+                    copy_wave<IO, DK, C, SPW, NW, 5>(smem, rec0, rec_stride, vbase, vstride, len, nchunks, lane);
+                break;
         }
         return;
     }
 
-    // ---------------- compute waves: slice s holds state columns col0 + 32*wave + 16*s + l16
+    // ---------------- compute waves: slice s holds state columns col0 + WC*wave + 16*s + l16
     f32x4 St[SPW][KT];
     const int64_t sbase = ((int64_t)n * H + h) * DK * DV;
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
-        const int col = col0 + 32 * wave + 16 * s + l16;
+        const int col = col0 + WC * wave + 16 * s + l16;
 #pragma unroll
         for (int ct = 0; ct < KT; ++ct)
 #pragma unroll
@@ -559,47 +652,96 @@ __global__ void __launch_bounds__(64 * (NW + 1)) kda_scan_kernel(FwdParams p, co
     }
     __builtin_amdgcn_s_waitcnt(0);
 
+    // The state as matrix-core B operand (bf16 or fp32), refreshed at the end of every chunk.
+    Frag<BF> Sb[SPW][KT];
+#pragma unroll
+    for (int s = 0; s < SPW; ++s)
+#pragma unroll
+        for (int ct = 0; ct < KT; ++ct) Sb[s][ct] = frag_from_acc<BF>(St[s][ct]);
+
+    // Record fragments are read from LDS in groups issued ahead of the products that use them:
+    // the K~ and Q~ tiles of row tile rt two row tiles ahead, T after the first row tile, P and
+    // the first half of K-^T after the second-to-last, the rest of K-^T after the last, and
+    // Gamma before the state products.  Scheduling fences keep the compiler from sinking the
+    // reads next to their uses.
+    constexpr int KP = KT / 2;                        // 32-wide k pairs of d_k
+    constexpr int GP = NSUB >= 2 ? NSUB - 2 : 0;      // row tile after which P and K-^T reads start
+    constexpr int KT_H = (KT + 1) / 2;                // K-^T row tiles read at GP
+
     for (int c = 0; c < nchunks; ++c) {
         const int clen = min(C, len - c * C);
-        __syncthreads();  // (A) chunk c is in LDS
+        __syncthreads();  // chunk c is in LDS
         const char *rb = smem + ((c & 1) ? S::oRec1 : S::oRec0);
         const IO *vb = reinterpret_cast<const IO *>(smem + ((c & 1) ? S::oV1 : S::oV0));
 
-        Frag<BF> Sb[SPW][KT];
+        FragPair<BF> Kf[NSUB][KP], Qf[NSUB][KP], Tf[NSUB][NPAIR], Pf[NSUB][NPAIR], Bf[KT][NPAIR];
+        IO vv[SPW][NSUB][4];  // V as stored; converted where Y is formed
+        auto read_kq = [&](int rt) {
 #pragma unroll
-        for (int s = 0; s < SPW; ++s)
+            for (int kp = 0; kp < KP; ++kp) {
+                Kf[rt][kp] = ld_pair<BF>(rb + Rec::oKt + (size_t)(rt * KP + kp) * Rec::TILE_BYTES, lane);
+                Qf[rt][kp] = ld_pair<BF>(rb + Rec::oQt + (size_t)(rt * KP + kp) * Rec::TILE_BYTES, lane);
+            }
+        };
+        auto read_kbt = [&](int ct0, int ct1) {
 #pragma unroll
-            for (int ct = 0; ct < KT; ++ct) Sb[s][ct] = frag_from_acc<BF>(St[s][ct]);
+            for (int ct = ct0; ct < ct1; ++ct)
+#pragma unroll
+                for (int pp = 0; pp < NPAIR; ++pp)
+                    Bf[ct][pp] = ld_pair<BF>(rb + Rec::oKbT + (size_t)(ct * NPAIR + pp) * Rec::TILE_BYTES, lane);
+        };
+        read_kq(0);
+        if constexpr (NSUB > 1) read_kq(1);
+        __builtin_amdgcn_sched_barrier(0);
 
-        // Y = V - K~ S   and   O^T = S^T Q~^T   (rows past the chunk end: finite filler, T zeroes them)
-        f32x4 Y[SPW][NSUB], Ot[SPW][NSUB];
+        // K~ S (for Y = V - K~ S) and O^T = S^T Q~^T, one row tile at a time
+        f32x4 AK[SPW][NSUB], Ot[SPW][NSUB];
 #pragma unroll
         for (int rt = 0; rt < NSUB; ++rt) {
-            f32x4 ak[SPW];
 #pragma unroll
             for (int s = 0; s < SPW; ++s) {
-                ak[s] = zero4();
+                AK[s][rt] = zero4();
                 Ot[s][rt] = zero4();
             }
 #pragma unroll
-            for (int kp = 0; kp < KT / 2; ++kp) {
-                Frag<BF> a0, a1, b0, b1;
-                load_pair<BF>(rb + Rec::oKt + (size_t)(rt * (KT / 2) + kp) * Rec::TILE_BYTES, lane, a0, a1);
-                load_pair<BF>(rb + Rec::oQt + (size_t)(rt * (KT / 2) + kp) * Rec::TILE_BYTES, lane, b0, b1);
+            for (int kp = 0; kp < KP; ++kp)
 #pragma unroll
                 for (int s = 0; s < SPW; ++s) {
-                    mma32(ak[s], a0, a1, Sb[s][2 * kp], Sb[s][2 * kp + 1]);
-                    mma32(Ot[s][rt], Sb[s][2 * kp], Sb[s][2 * kp + 1], b0, b1);
+                    mma32(AK[s][rt], Kf[rt][kp].a, Kf[rt][kp].b, Sb[s][2 * kp], Sb[s][2 * kp + 1]);
+                    mma32(Ot[s][rt], Sb[s][2 * kp], Sb[s][2 * kp + 1], Qf[rt][kp].a, Qf[rt][kp].b);
                 }
+            __builtin_amdgcn_sched_barrier(0);
+            if (rt + 2 < NSUB) read_kq(rt + 2);
+            if (rt == 0) {
+#pragma unroll
+                for (int s = 0; s < SPW; ++s)
+#pragma unroll
+                    for (int r2 = 0; r2 < NSUB; ++r2)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            vv[s][r2][j] = vb[(16 * r2 + 4 * q4 + j) * DVT + WC * wave + 16 * s + l16];
+#pragma unroll
+                for (int R = 0; R < NSUB; ++R)
+#pragma unroll
+                    for (int pp = 0; pp < NPAIR; ++pp)
+                        if (2 * pp <= R)
+                            Tf[R][pp] = ld_pair<BF>(rb + Rec::oT + (size_t)(R * NPAIR + pp) * Rec::TILE_BYTES, lane);
             }
+            if (rt == GP) {
 #pragma unroll
-            for (int s = 0; s < SPW; ++s)
+                for (int R = 0; R < NSUB; ++R)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    Y[s][rt][j] = Tr::load1(vb + (16 * rt + 4 * q4 + j) * DVT + 32 * wave + 16 * s + l16) - ak[s][j];
+                    for (int pp = 0; pp < NPAIR; ++pp)
+                        if (2 * pp <= R)
+                            Pf[R][pp] = ld_pair<BF>(rb + Rec::oP + (size_t)(R * NPAIR + pp) * Rec::TILE_BYTES, lane);
+                read_kbt(0, KT_H);
+            }
+            if (rt == NSUB - 1) read_kbt(KT_H, KT);
+            __builtin_amdgcn_sched_barrier(0);
         }
 
-        // D = T Y
+        // Y = V - K~ S as B fragments (rows past the chunk end hold finite filler; T zeroes them),
+        // then D = T Y
         Frag<BF> Db[SPW][2 * NPAIR];
         {
             Frag<BF> Yb[SPW][2 * NPAIR];
@@ -607,20 +749,21 @@ __global__ void __launch_bounds__(64 * (NW + 1)) kda_scan_kernel(FwdParams p, co
             for (int s = 0; s < SPW; ++s)
 #pragma unroll
                 for (int rt = 0; rt < 2 * NPAIR; ++rt)
-                    Yb[s][rt] = rt < NSUB ? frag_from_acc<BF>(Y[s][rt]) : make_frag<BF>(0.f, 0.f, 0.f, 0.f);
+                    Yb[s][rt] = rt < NSUB ? make_frag<BF>(Tr::to_float(vv[s][rt][0]) - AK[s][rt][0],
+                                                          Tr::to_float(vv[s][rt][1]) - AK[s][rt][1],
+                                                          Tr::to_float(vv[s][rt][2]) - AK[s][rt][2],
+                                                          Tr::to_float(vv[s][rt][3]) - AK[s][rt][3])
+                                          : make_frag<BF>(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
             for (int R = 0; R < NSUB; ++R) {
                 f32x4 d[SPW];
 #pragma unroll
                 for (int s = 0; s < SPW; ++s) d[s] = zero4();
 #pragma unroll
-                for (int pp = 0; pp < NPAIR; ++pp) {
-                    if (2 * pp > R) break;
-                    Frag<BF> a0, a1;
-                    load_pair<BF>(rb + Rec::oT + (size_t)(R * NPAIR + pp) * Rec::TILE_BYTES, lane, a0, a1);
+                for (int pp = 0; pp < NPAIR; ++pp)
+                    if (2 * pp <= R)
 #pragma unroll
-                    for (int s = 0; s < SPW; ++s) mma32(d[s], a0, a1, Yb[s][2 * pp], Yb[s][2 * pp + 1]);
-                }
+                        for (int s = 0; s < SPW; ++s) mma32(d[s], Tf[R][pp].a, Tf[R][pp].b, Yb[s][2 * pp], Yb[s][2 * pp + 1]);
 #pragma unroll
                 for (int s = 0; s < SPW; ++s) Db[s][R] = frag_from_acc<BF>(d[s]);
             }
@@ -629,36 +772,46 @@ __global__ void __launch_bounds__(64 * (NW + 1)) kda_scan_kernel(FwdParams p, co
                 for (int s = 0; s < SPW; ++s) Db[s][NSUB] = make_frag<BF>(0.f, 0.f, 0.f, 0.f);
         }
 
-        // O^T += D^T P^T; lane holds columns 16 s + 4 q4 .. +3 of token 16 R + l16
+        // M = K-^T D (fresh accumulators) and O^T += D^T P^T; the state itself stays in plain
+        // registers and is updated as S <- Gamma * S + M once the products are done
+        float4 gm[KT];
+        {
+            const float *gam = reinterpret_cast<const float *>(rb + Rec::oGam);
 #pragma unroll
-        for (int R = 0; R < NSUB; ++R) {
-#pragma unroll
-            for (int pp = 0; pp < NPAIR; ++pp) {
-                if (2 * pp > R) break;
-                Frag<BF> b0, b1;
-                load_pair<BF>(rb + Rec::oP + (size_t)(R * NPAIR + pp) * Rec::TILE_BYTES, lane, b0, b1);
-#pragma unroll
-                for (int s = 0; s < SPW; ++s) mma32(Ot[s][R], Db[s][2 * pp], Db[s][2 * pp + 1], b0, b1);
-            }
+            for (int ct = 0; ct < KT; ++ct) gm[ct] = *reinterpret_cast<const float4 *>(gam + 16 * ct + 4 * q4);
         }
-
-        // M = K-^T D (fresh accumulators); the state itself stays in plain registers and is
-        // updated as S <- Gamma * S + M once the products are done
+        __builtin_amdgcn_sched_barrier(0);
         f32x4 M[SPW][KT];
 #pragma unroll
         for (int ct = 0; ct < KT; ++ct) {
 #pragma unroll
             for (int s = 0; s < SPW; ++s) M[s][ct] = zero4();
 #pragma unroll
-            for (int pp = 0; pp < NPAIR; ++pp) {
-                Frag<BF> a0, a1;
-                load_pair<BF>(rb + Rec::oKbT + (size_t)(ct * NPAIR + pp) * Rec::TILE_BYTES, lane, a0, a1);
+            for (int pp = 0; pp < NPAIR; ++pp)
 #pragma unroll
-                for (int s = 0; s < SPW; ++s) mma32(M[s][ct], a0, a1, Db[s][2 * pp], Db[s][2 * pp + 1]);
-            }
+                for (int s = 0; s < SPW; ++s) mma32(M[s][ct], Bf[ct][pp].a, Bf[ct][pp].b, Db[s][2 * pp], Db[s][2 * pp + 1]);
         }
+#pragma unroll
+        for (int R = 0; R < NSUB; ++R)
+#pragma unroll
+            for (int pp = 0; pp < NPAIR; ++pp)
+                if (2 * pp <= R)
+#pragma unroll
+                    for (int s = 0; s < SPW; ++s) mma32(Ot[s][R], Db[s][2 * pp], Db[s][2 * pp + 1], Pf[R][pp].a, Pf[R][pp].b);
 
-        IO *oc = obase + (int64_t)c * C * vstride + 32 * wave + 4 * q4;
+#pragma unroll
+        for (int ct = 0; ct < KT; ++ct)
+#pragma unroll
+            for (int s = 0; s < SPW; ++s) {
+                St[s][ct][0] = fmaf(gm[ct].x, St[s][ct][0], M[s][ct][0]);
+                St[s][ct][1] = fmaf(gm[ct].y, St[s][ct][1], M[s][ct][1]);
+                St[s][ct][2] = fmaf(gm[ct].z, St[s][ct][2], M[s][ct][2]);
+                St[s][ct][3] = fmaf(gm[ct].w, St[s][ct][3], M[s][ct][3]);
+                Sb[s][ct] = frag_from_acc<BF>(St[s][ct]);
+            }
+
+        // O rows of this chunk; lane holds columns 16 s + 4 q4 .. +3 of token 16 R + l16
+        IO *oc = obase + (int64_t)c * C * vstride + WC * wave + 4 * q4;
 #pragma unroll
         for (int R = 0; R < NSUB; ++R) {
             const int r = 16 * R + l16;
@@ -669,26 +822,12 @@ __global__ void __launch_bounds__(64 * (NW + 1)) kda_scan_kernel(FwdParams p, co
                                                                     Ot[s][R][2] * p.scale, Ot[s][R][3] * p.scale));
             }
         }
-
-        const float *gam = reinterpret_cast<const float *>(rb + Rec::oGam);
-#pragma unroll
-        for (int ct = 0; ct < KT; ++ct) {
-            const float4 gm = *reinterpret_cast<const float4 *>(gam + 16 * ct + 4 * q4);
-#pragma unroll
-            for (int s = 0; s < SPW; ++s) {
-                St[s][ct][0] = fmaf(gm.x, St[s][ct][0], M[s][ct][0]);
-                St[s][ct][1] = fmaf(gm.y, St[s][ct][1], M[s][ct][1]);
-                St[s][ct][2] = fmaf(gm.z, St[s][ct][2], M[s][ct][2]);
-                St[s][ct][3] = fmaf(gm.w, St[s][ct][3], M[s][ct][3]);
-            }
-        }
-        __syncthreads();  // (B) done with chunk c: the copy wave may refill its buffers
     }
 
     if (p.sf) {
 #pragma unroll
         for (int s = 0; s < SPW; ++s) {
-            const int col = col0 + 32 * wave + 16 * s + l16;
+            const int col = col0 + WC * wave + 16 * s + l16;
 #pragma unroll
             for (int ct = 0; ct < KT; ++ct)
 #pragma unroll
@@ -703,15 +842,15 @@ constexpr size_t split_record_bytes() {
     return SplitRecord<IO, DK, C>::kBytes;
 }
 
-template <typename IO, int DK, int C, int NW>
+template <typename IO, int DK, int C, int SPW, int NW>
 constexpr bool split_fits() {
-    return ScanLayout<IO, DK, C, NW>::kFits && PrepLayout<IO, DK, C>::kBytes <= 160 * 1024;
+    return ScanLayout<IO, DK, C, SPW, NW>::kFits && PrepLayout<IO, DK, C>::kBytes <= 160 * 1024;
 }
 
 // Workspace: [chunk offsets: num_seqs + 1 int32, padded to 256 B][records]
-template <typename IO, int DK, int C, int NW>
+template <typename IO, int DK, int C, int SPW, int NW>
 hipError_t launch_split_variant(const FwdParams &p, char *workspace, int64_t chunk_upper, hipStream_t stream) {
-    if constexpr (!split_fits<IO, DK, C, NW>()) {
+    if constexpr (!split_fits<IO, DK, C, SPW, NW>()) {
         return hipErrorInvalidConfiguration;
     } else {
         int32_t *chunk_off = reinterpret_cast<int32_t *>(workspace);
@@ -728,9 +867,9 @@ hipError_t launch_split_variant(const FwdParams &p, char *workspace, int64_t chu
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
-        const int64_t scan_blocks = (int64_t)p.num_seqs * p.H * (p.dv / ScanLayout<IO, DK, C, NW>::DVT);
+        const int64_t scan_blocks = (int64_t)p.num_seqs * p.H * (p.dv / ScanLayout<IO, DK, C, SPW, NW>::DVT);
         if (scan_blocks > 0) {
-            hipLaunchKernelGGL((kda_scan_kernel<IO, DK, C, NW>), dim3((unsigned)scan_blocks), dim3(64 * (NW + 1)), 0,
+            hipLaunchKernelGGL((kda_scan_kernel<IO, DK, C, SPW, NW>), dim3((unsigned)scan_blocks), dim3(ScanLayout<IO, DK, C, SPW, NW>::NT), 0,
                                stream, p, chunk_off, records);
             return hipGetLastError();
         }
@@ -738,14 +877,15 @@ hipError_t launch_split_variant(const FwdParams &p, char *workspace, int64_t chu
     }
 }
 
-// F(DK, C, NW): NW compute waves of 32 state columns each (d_v tile 32 * NW)
-#define KDA_SPLIT_VARIANTS(F) \
-    F(64, 16, 2) F(64, 32, 2) F(64, 64, 2) F(128, 16, 2) F(128, 32, 2) F(128, 64, 2) \
-    F(64, 16, 1) F(64, 32, 1) F(64, 64, 1) F(128, 16, 1) F(128, 32, 1) F(128, 64, 1)
+// F(DK, C, SPW, NW): NW compute waves of 16 * SPW state columns each (d_v tile 16 * SPW * NW)
+#define KDA_SPLIT_SHAPES(F, DK_, C_) F(DK_, C_, 1, 2) F(DK_, C_, 2, 2)
+#define KDA_SPLIT_VARIANTS(F)                                                                          \
+    KDA_SPLIT_SHAPES(F, 64, 16) KDA_SPLIT_SHAPES(F, 64, 32) KDA_SPLIT_SHAPES(F, 64, 64)                \
+    KDA_SPLIT_SHAPES(F, 128, 16) KDA_SPLIT_SHAPES(F, 128, 32) KDA_SPLIT_SHAPES(F, 128, 64)
 
 template <typename IO>
 size_t split_record_size(int dk, int chunk) {
-#define KDA_REC_CASE(DK_, C_, NW_) \
+#define KDA_REC_CASE(DK_, C_, SPW_, NW_) \
     if (dk == DK_ && chunk == C_) return split_record_bytes<IO, DK_, C_>();
     KDA_SPLIT_VARIANTS(KDA_REC_CASE)
 #undef KDA_REC_CASE
@@ -753,19 +893,20 @@ size_t split_record_size(int dk, int chunk) {
 }
 
 template <typename IO>
-bool split_supported(int dk, int chunk, int nw) {
-#define KDA_FIT_CASE(DK_, C_, NW_) \
-    if (dk == DK_ && chunk == C_ && nw == NW_) return split_fits<IO, DK_, C_, NW_>();
+bool split_supported(int dk, int chunk, int spw, int nw) {
+#define KDA_FIT_CASE(DK_, C_, SPW_, NW_) \
+    if (dk == DK_ && chunk == C_ && spw == SPW_ && nw == NW_) return split_fits<IO, DK_, C_, SPW_, NW_>();
     KDA_SPLIT_VARIANTS(KDA_FIT_CASE)
 #undef KDA_FIT_CASE
     return false;
 }
 
 template <typename IO>
-hipError_t launch_split(const FwdParams &p, int chunk, int nw, char *workspace, int64_t chunk_upper,
+hipError_t launch_split(const FwdParams &p, int chunk, int spw, int nw, char *workspace, int64_t chunk_upper,
                         hipStream_t stream) {
-#define KDA_SPLIT_CASE(DK_, C_, NW_) \
-    if (p.dk == DK_ && chunk == C_ && nw == NW_) return launch_split_variant<IO, DK_, C_, NW_>(p, workspace, chunk_upper, stream);
+#define KDA_SPLIT_CASE(DK_, C_, SPW_, NW_)                     \
+    if (p.dk == DK_ && chunk == C_ && spw == SPW_ && nw == NW_) \
+        return launch_split_variant<IO, DK_, C_, SPW_, NW_>(p, workspace, chunk_upper, stream);
     KDA_SPLIT_VARIANTS(KDA_SPLIT_CASE)
 #undef KDA_SPLIT_CASE
     return hipErrorInvalidConfiguration;
