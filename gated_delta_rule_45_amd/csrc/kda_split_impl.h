@@ -152,13 +152,10 @@ struct PrepLayout {
     static constexpr int NSUB = C / 16, KT = DK / 16;
     static constexpr int PADO = 16 / (int)sizeof(OT);
     static constexpr int LDO = DK + PADO;
-    static constexpr int LDT = C + PADO;
     static constexpr int LDX = C + 4;
     static constexpr int NSHIFT = NSUB >= 3 ? (NSUB - 1) * (NSUB - 2) / 2 : 0;
     static constexpr size_t oKb = 0;
-    static constexpr size_t oKs = oKb + (size_t)C * LDO * sizeof(OT);
-    static constexpr size_t oKbT = oKs + (size_t)NSHIFT * 16 * LDO * sizeof(OT);
-    static constexpr size_t oX = oKbT + (size_t)DK * LDT * sizeof(OT);
+    static constexpr size_t oX = oKb + (size_t)C * LDO * sizeof(OT);
     static constexpr size_t oTot = oX + (size_t)C * LDX * 4;
     static constexpr size_t oEB = oTot + (size_t)NSUB * DK * 4;
     static constexpr size_t oED = oEB + (size_t)NSUB * DK * 4;
@@ -177,13 +174,11 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
     using OT = typename L::OT;
     constexpr bool BF = L::BF;
     constexpr int NSUB = L::NSUB, KT = L::KT, NPAIR = Rec::NPAIR;
-    constexpr int LDO = L::LDO, LDT = L::LDT, LDX = L::LDX;
+    constexpr int LDO = L::LDO, LDX = L::LDX;
     using Tr = IoTraits<IO>;
 
     __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
     OT *sKb = reinterpret_cast<OT *>(smem + L::oKb);
-    OT *sKs = reinterpret_cast<OT *>(smem + L::oKs);
-    OT *sKbT = reinterpret_cast<OT *>(smem + L::oKbT);
     float *sX = reinterpret_cast<float *>(smem + L::oX);
     float *sTot = reinterpret_cast<float *>(smem + L::oTot);
     float *sEB = reinterpret_cast<float *>(smem + L::oEB);
@@ -260,85 +255,95 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
     }
     __syncthreads();
 
-    // ================= 3: gated operands; K~ and Q~ go straight to the record
+    // ================= 3: gated operands.  K~ and Q~ go straight to the record; K- is
+    // transposed in registers by a product with the identity (exact: every term is the
+    // operand times 1 or 0), which leaves this sub-chunk's half of each K-^T operand tile in
+    // fragment layout; K_b = k e^{b_{R+1} - G} goes to LDS as the column operand of the
+    // later rows' off-diagonal blocks.
     Frag<BF> kdiag[KT];
     if (wave < NSUB) {
         const int R = wave;
         const int r = 16 * R + l16;
-        Frag<BF> fkt[KT], fqt[KT];
+        Frag<BF> eye;  // identity as a B operand: rows 4*q4 + j, column l16
+        {
+            float e[4];
 #pragma unroll
-        for (int ct = 0; ct < KT; ++ct) {
-            const int ch = 16 * ct + 4 * q4;
-            const float4 tot = *reinterpret_cast<const float4 *>(sTot + R * DK + ch);
-            const float4 eb = *reinterpret_cast<const float4 *>(sEB + R * DK + ch);
-            const float4 ed = *reinterpret_cast<const float4 *>(sED + R * DK + ch);
-            const float4 ec = *reinterpret_cast<const float4 *>(sEC + R * DK + ch);
-            const float tv[4] = {tot.x, tot.y, tot.z, tot.w};
-            const float ebv[4] = {eb.x, eb.y, eb.z, eb.w};
-            const float edv[4] = {ed.x, ed.y, ed.z, ed.w};
-            const float ecv[4] = {ec.x, ec.y, ec.z, ec.w};
-            float kb[4], kt[4], qt[4], kbar[4], kd[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float fr = fast_exp2(G[ct][j]);          // e^{G_r - b_R}     <= 1
-                const float fb = fast_exp2(tv[j] - G[ct][j]);  // e^{b_{R+1} - G_r} <= 1
-                const float krow = kr[ct][j] * fr;
-                const float qrow = qr[ct][j] * fr;
-                kb[j] = kr[ct][j] * fb;
-                kd[j] = kb[j] * edv[j];
-                kt[j] = krow * ebv[j];
-                qt[j] = qrow * ebv[j];
-                kbar[j] = kb[j] * ecv[j];
-                kr[ct][j] = krow;
-                qr[ct][j] = qrow;
-            }
-            kdiag[ct] = make_frag<BF>(kd[0], kd[1], kd[2], kd[3]);
-            fkt[ct] = make_frag<BF>(kt[0], kt[1], kt[2], kt[3]);
-            fqt[ct] = make_frag<BF>(qt[0], qt[1], qt[2], qt[3]);
-            const Frag<BF> fkb = make_frag<BF>(kb[0], kb[1], kb[2], kb[3]);
-            *reinterpret_cast<decltype(fkb.v) *>(sKb + r * LDO + ch) = fkb.v;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if constexpr (BF) sKbT[(ch + j) * LDT + r] = f32_to_bf16(kbar[j]);
-                else sKbT[(ch + j) * LDT + r] = kbar[j];
-            }
-#pragma unroll
-            for (int R2 = 2; R2 < NSUB; ++R2) {
-                if (R2 < R + 2) continue;
-                const float4 sh = *reinterpret_cast<const float4 *>(sSH + L::shift_slot(R2, R) * DK + ch);
-                const Frag<BF> f = make_frag<BF>(kb[0] * sh.x, kb[1] * sh.y, kb[2] * sh.z, kb[3] * sh.w);
-                *reinterpret_cast<decltype(f.v) *>(sKs + (L::shift_slot(R2, R) * 16 + l16) * LDO + ch) = f.v;
-            }
+            for (int j = 0; j < 4; ++j) e[j] = (4 * q4 + j == l16) ? 1.f : 0.f;
+            eye = make_frag<BF>(e[0], e[1], e[2], e[3]);
         }
+        char *kbt_half = rec + Rec::oKbT + (size_t)(R / 2) * Rec::TILE_BYTES + lane * Rec::PAIR_BYTES +
+                         (R % 2) * Rec::FRAG_BYTES;
 #pragma unroll
         for (int kp = 0; kp < KT / 2; ++kp) {
-            store_pair<BF>(rec + Rec::oKt + (size_t)(R * (KT / 2) + kp) * Rec::TILE_BYTES, lane, fkt[2 * kp], fkt[2 * kp + 1]);
-            store_pair<BF>(rec + Rec::oQt + (size_t)(R * (KT / 2) + kp) * Rec::TILE_BYTES, lane, fqt[2 * kp], fqt[2 * kp + 1]);
+            Frag<BF> fkt[2], fqt[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int ct = 2 * kp + u;
+                const int ch = 16 * ct + 4 * q4;
+                const float4 tot = *reinterpret_cast<const float4 *>(sTot + R * DK + ch);
+                const float4 eb = *reinterpret_cast<const float4 *>(sEB + R * DK + ch);
+                const float4 ed = *reinterpret_cast<const float4 *>(sED + R * DK + ch);
+                const float4 ec = *reinterpret_cast<const float4 *>(sEC + R * DK + ch);
+                const float tv[4] = {tot.x, tot.y, tot.z, tot.w};
+                const float ebv[4] = {eb.x, eb.y, eb.z, eb.w};
+                const float edv[4] = {ed.x, ed.y, ed.z, ed.w};
+                const float ecv[4] = {ec.x, ec.y, ec.z, ec.w};
+                float kb[4], kt[4], qt[4], kbar[4], kd[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float fr = fast_exp2(G[ct][j]);          // e^{G_r - b_R}     <= 1
+                    const float fb = fast_exp2(tv[j] - G[ct][j]);  // e^{b_{R+1} - G_r} <= 1
+                    const float krow = kr[ct][j] * fr;
+                    const float qrow = qr[ct][j] * fr;
+                    kb[j] = kr[ct][j] * fb;
+                    kd[j] = kb[j] * edv[j];
+                    kt[j] = krow * ebv[j];
+                    qt[j] = qrow * ebv[j];
+                    kbar[j] = kb[j] * ecv[j];
+                    kr[ct][j] = krow;
+                    qr[ct][j] = qrow;
+                }
+                kdiag[ct] = make_frag<BF>(kd[0], kd[1], kd[2], kd[3]);
+                fkt[u] = make_frag<BF>(kt[0], kt[1], kt[2], kt[3]);
+                fqt[u] = make_frag<BF>(qt[0], qt[1], qt[2], qt[3]);
+                const Frag<BF> fkb = make_frag<BF>(kb[0], kb[1], kb[2], kb[3]);
+                *reinterpret_cast<decltype(fkb.v) *>(sKb + r * LDO + ch) = fkb.v;
+                f32x4 kbt = zero4();
+                mma16(kbt, make_frag<BF>(kbar[0], kbar[1], kbar[2], kbar[3]), eye);
+                const Frag<BF> fkbt = frag_from_acc<BF>(kbt);
+                *reinterpret_cast<decltype(fkbt.v) *>(kbt_half + (size_t)ct * NPAIR * Rec::TILE_BYTES) = fkbt.v;
+            }
+            store_pair<BF>(rec + Rec::oKt + (size_t)(R * (KT / 2) + kp) * Rec::TILE_BYTES, lane, fkt[0], fkt[1]);
+            store_pair<BF>(rec + Rec::oQt + (size_t)(R * (KT / 2) + kp) * Rec::TILE_BYTES, lane, fqt[0], fqt[1]);
+        }
+        if (NSUB % 2 == 1 && R == NSUB - 1) {  // odd sub-chunk count: zero the unused half of the last pair
+            const Frag<BF> z = make_frag<BF>(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int ct = 0; ct < KT; ++ct)
+                *reinterpret_cast<decltype(z.v) *>(kbt_half + Rec::FRAG_BYTES + (size_t)ct * NPAIR * Rec::TILE_BYTES) = z.v;
         }
     }
     __syncthreads();
 
     // ================= 4: row-R blocks of A (to LDS) and P (to the record); X_RR
+    // Block (R, I) pairs the row operands k_r e^{G_r - b_{I+1}} (and the same for q) with the
+    // column operand K_b of sub-chunk I; both factors are at most 1.  For I = R the column
+    // operand is k_i e^{b_R - G_i}, and for I <= R - 2 the row operands take the extra
+    // factor e^{b_R - b_{I+1}} <= 1.
     if (wave < NSUB) {
         const int R = wave;
-        Frag<BF> ka[KT], qa[KT];
-#pragma unroll
-        for (int ct = 0; ct < KT; ++ct) {
-            ka[ct] = make_frag<BF>(kr[ct][0], kr[ct][1], kr[ct][2], kr[ct][3]);
-            qa[ct] = make_frag<BF>(qr[ct][0], qr[ct][1], qr[ct][2], qr[ct][3]);
-        }
         Frag<BF> pf[2 * NPAIR];
 #pragma unroll
         for (int I = 0; I < 2 * NPAIR; ++I) pf[I] = make_frag<BF>(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int I = 0; I < NSUB; ++I) {
             if (I > R) break;
-            const OT *colp = (I == R - 1) ? sKb + (16 * I + l16) * LDO
-                                          : sKs + (L::shift_slot(R < 2 ? 2 : R, I) * 16 + l16) * LDO;
+            const OT *colp = sKb + (16 * I + l16) * LDO;
+            const float *shp = sSH + (I + 2 <= R ? L::shift_slot(R, I) : 0) * DK + 4 * q4;
             f32x4 accA = zero4(), accPt = zero4();
 #pragma unroll
             for (int ct = 0; ct < KT; ct += 2) {
-                Frag<BF> b0, b1;
+                Frag<BF> b0, b1, ka0, ka1, qa0, qa1;
                 if (I == R) {
                     b0 = kdiag[ct];
                     b1 = kdiag[ct + 1];
@@ -346,8 +351,23 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
                     b0 = lds_frag(colp + 16 * ct + 4 * q4);
                     b1 = lds_frag(colp + 16 * (ct + 1) + 4 * q4);
                 }
-                mma32(accA, ka[ct], ka[ct + 1], b0, b1);   // A_RI:  rows r, columns i
-                mma32(accPt, b0, b1, qa[ct], qa[ct + 1]);  // P_RI^T: rows i, columns r
+                if (I + 2 <= R) {
+                    const float4 s0 = *reinterpret_cast<const float4 *>(shp + 16 * ct);
+                    const float4 s1 = *reinterpret_cast<const float4 *>(shp + 16 * (ct + 1));
+                    ka0 = make_frag<BF>(kr[ct][0] * s0.x, kr[ct][1] * s0.y, kr[ct][2] * s0.z, kr[ct][3] * s0.w);
+                    ka1 = make_frag<BF>(kr[ct + 1][0] * s1.x, kr[ct + 1][1] * s1.y, kr[ct + 1][2] * s1.z,
+                                        kr[ct + 1][3] * s1.w);
+                    qa0 = make_frag<BF>(qr[ct][0] * s0.x, qr[ct][1] * s0.y, qr[ct][2] * s0.z, qr[ct][3] * s0.w);
+                    qa1 = make_frag<BF>(qr[ct + 1][0] * s1.x, qr[ct + 1][1] * s1.y, qr[ct + 1][2] * s1.z,
+                                        qr[ct + 1][3] * s1.w);
+                } else {
+                    ka0 = make_frag<BF>(kr[ct][0], kr[ct][1], kr[ct][2], kr[ct][3]);
+                    ka1 = make_frag<BF>(kr[ct + 1][0], kr[ct + 1][1], kr[ct + 1][2], kr[ct + 1][3]);
+                    qa0 = make_frag<BF>(qr[ct][0], qr[ct][1], qr[ct][2], qr[ct][3]);
+                    qa1 = make_frag<BF>(qr[ct + 1][0], qr[ct + 1][1], qr[ct + 1][2], qr[ct + 1][3]);
+                }
+                mma32(accA, ka0, ka1, b0, b1);   // A_RI:  rows r, columns i
+                mma32(accPt, b0, b1, qa0, qa1);  // P_RI^T: rows i, columns r
             }
             // A_RI: lane holds rows rr = 4*q4 + j, column l16
 #pragma unroll
@@ -418,7 +438,7 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
         __syncthreads();
     }
 
-    // ================= 6: T = X Diag(beta) and K-^T fragments to the record
+    // ================= 6: T = X Diag(beta) to the record
     if (wave < NSUB) {
         const int R = wave;
 #pragma unroll
@@ -439,16 +459,6 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
                 f[u] = make_frag<BF>(xv.x * bv.x, xv.y * bv.y, xv.z * bv.z, xv.w * bv.w);
             }
             store_pair<BF>(rec + Rec::oT + (size_t)(R * NPAIR + pp) * Rec::TILE_BYTES, lane, f[0], f[1]);
-        }
-    }
-    for (int ct = wave; ct < KT; ct += 4) {
-        const OT *row = sKbT + (16 * ct + l16) * LDT + 4 * q4;
-#pragma unroll
-        for (int pp = 0; pp < NPAIR; ++pp) {
-            Frag<BF> f0 = lds_frag(row + 32 * pp), f1;
-            if (2 * pp + 1 < NSUB) f1 = lds_frag(row + 32 * pp + 16);
-            else f1 = make_frag<BF>(0.f, 0.f, 0.f, 0.f);
-            store_pair<BF>(rec + Rec::oKbT + (size_t)(ct * NPAIR + pp) * Rec::TILE_BYTES, lane, f0, f1);
         }
     }
 }
