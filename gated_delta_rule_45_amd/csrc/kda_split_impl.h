@@ -45,9 +45,13 @@ struct SplitRecord {
     static constexpr size_t oKt = 0;
     static constexpr size_t oQt = oKt + (size_t)NSUB * (KT / 2) * TILE_BYTES;
     static constexpr size_t oKbT = oQt + (size_t)NSUB * (KT / 2) * TILE_BYTES;
+    // T and P are block lower triangular: row tile R keeps only its 32-wide column pairs
+    // pp <= R / 2, stored row tile after row tile.
+    static constexpr int TP_TILES = (NSUB / 2) * (NSUB / 2 + 1) + (NSUB % 2) * (NSUB / 2 + 1);
+    __host__ __device__ static constexpr int tp_tile(int R, int pp) { return (R / 2) * (R / 2 + 1) + (R % 2) * (R / 2 + 1) + pp; }
     static constexpr size_t oT = oKbT + (size_t)KT * NPAIR * TILE_BYTES;
-    static constexpr size_t oP = oT + (size_t)NSUB * NPAIR * TILE_BYTES;
-    static constexpr size_t oGam = oP + (size_t)NSUB * NPAIR * TILE_BYTES;
+    static constexpr size_t oP = oT + (size_t)TP_TILES * TILE_BYTES;
+    static constexpr size_t oGam = oP + (size_t)TP_TILES * TILE_BYTES;
     static constexpr size_t kRaw = oGam + (size_t)DK * 4;
     static constexpr size_t kBytes = (kRaw + 1023) / 1024 * 1024;  // whole 1 KB copy units
     static_assert(KT % 2 == 0, "d_k must be a multiple of 32");
@@ -385,7 +389,8 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
         }
 #pragma unroll
         for (int pp = 0; pp < NPAIR; ++pp)
-            store_pair<BF>(rec + Rec::oP + (size_t)(R * NPAIR + pp) * Rec::TILE_BYTES, lane, pf[2 * pp], pf[2 * pp + 1]);
+            if (2 * pp <= R)
+                store_pair<BF>(rec + Rec::oP + (size_t)Rec::tp_tile(R, pp) * Rec::TILE_BYTES, lane, pf[2 * pp], pf[2 * pp + 1]);
 
         // X_RR = (I + A_RR)^{-1}, row by row; lane l16 owns column l16 (this wave wrote A_RR)
         float *Ab = sX + (16 * R) * LDX + 16 * R;
@@ -443,6 +448,7 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
         const int R = wave;
 #pragma unroll
         for (int pp = 0; pp < NPAIR; ++pp) {
+            if (2 * pp > R) break;
             Frag<BF> f[2];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
@@ -458,7 +464,7 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
                                            : make_float4(0.f, 0.f, 0.f, 0.f);
                 f[u] = make_frag<BF>(xv.x * bv.x, xv.y * bv.y, xv.z * bv.z, xv.w * bv.w);
             }
-            store_pair<BF>(rec + Rec::oT + (size_t)(R * NPAIR + pp) * Rec::TILE_BYTES, lane, f[0], f[1]);
+            store_pair<BF>(rec + Rec::oT + (size_t)Rec::tp_tile(R, pp) * Rec::TILE_BYTES, lane, f[0], f[1]);
         }
     }
 }
@@ -735,7 +741,7 @@ __global__ void __launch_bounds__(64 * (NW + scan_copy_waves(SPW))) kda_scan_ker
 #pragma unroll
                     for (int pp = 0; pp < NPAIR; ++pp)
                         if (2 * pp <= R)
-                            Tf[R][pp] = ld_pair<BF>(rb + Rec::oT + (size_t)(R * NPAIR + pp) * Rec::TILE_BYTES, lane);
+                            Tf[R][pp] = ld_pair<BF>(rb + Rec::oT + (size_t)Rec::tp_tile(R, pp) * Rec::TILE_BYTES, lane);
             }
             if (rt == GP) {
 #pragma unroll
@@ -743,7 +749,7 @@ __global__ void __launch_bounds__(64 * (NW + scan_copy_waves(SPW))) kda_scan_ker
 #pragma unroll
                     for (int pp = 0; pp < NPAIR; ++pp)
                         if (2 * pp <= R)
-                            Pf[R][pp] = ld_pair<BF>(rb + Rec::oP + (size_t)(R * NPAIR + pp) * Rec::TILE_BYTES, lane);
+                            Pf[R][pp] = ld_pair<BF>(rb + Rec::oP + (size_t)Rec::tp_tile(R, pp) * Rec::TILE_BYTES, lane);
                 read_kbt(0, KT_H);
             }
             if (rt == NSUB - 1) read_kbt(KT_H, KT);

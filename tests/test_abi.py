@@ -157,8 +157,8 @@ def test_query_reports_config_and_work():
     assert r["status"] == kda.KDA_OK and r["supported"] == 1
     assert r["algo"] == kda.KDA_ALGO_TWO_PASS and r["chunk_size"] == 64
     # chunk-offset table (256 B) + one record per chunk-head: K~, Q~, K-^T (16 KB each),
-    # T and P (8 KB each), Gamma (512 B), rounded up to whole KB
-    rec = 3 * 16384 + 2 * 8192 + 512
+    # the 6 lower 16x32 tiles of T and of P (6 KB each), Gamma (512 B), rounded up to whole KB
+    rec = 3 * 16384 + 2 * 6144 + 512
     rec = (rec + 1023) // 1024 * 1024
     assert r["workspace_bytes"] == 256 + 4 * 64 * 16 * rec
     assert r["grid_blocks"] == 4 * 16 * (128 // r["dv_tile"])
