@@ -14,6 +14,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--algo auto|fused|tw
                        [--no-cpu-baseline]
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -30,6 +31,37 @@ PEAK_BF16_TFLOPS = 2500.0
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    """SHA-256 over the kernel sources and the ABI header (file names and contents)."""
+    h = hashlib.sha256()
+    files = [os.path.join(ROOT, "include", "kda.h")]
+    csrc = os.path.join(ROOT, "gated_delta_rule_45_amd", "csrc")
+    files += sorted(os.path.join(csrc, f) for f in os.listdir(csrc))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch recorded from rocprofv3 counters under profiles/, keyed by
+    the kernel-source hash they were taken at; {} when the sources have changed since."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_4x4096x16_decode_256x32.txt")
+    if not os.path.exists(path):
+        return {}
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            line = line.split("#", 1)[0].strip()
+            if "=" in line:
+                k, v = (x.strip() for x in line.split("=", 1))
+                vals[k] = v
+    if vals.get("source_sha256") != kernel_source_hash():
+        return {}
+    return {k: float(v) for k, v in vals.items() if k.endswith("_bytes")}
 
 
 def time_launches(fn, n, stream):
@@ -131,6 +163,7 @@ def main():
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / args.steps
 
+    traffic = measured_traffic()
     tokens = B * T
     pre_tps = tokens / (t_pre * 1e-3)
     pre_bytes = q["hbm_bytes"]
@@ -157,10 +190,15 @@ def main():
                    "dv_tile": q["dv_tile"], "algo": ["auto", "fused", "two_pass"][q["algo"]],
                    "workspace_bytes": q["workspace_bytes"], "device": q["arch"], "compute_units": q["compute_units"]},
         "roofline": {"bound": "hbm", "achieved": round(pre_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(pre_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "frac": round(pre_gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic.get("prefill_bytes") if q["algo"] == 2 else None,
                      "kernel": "kda_chunk_fwd (" + ["auto", "fused", "two_pass"][q["algo"]] + ")",
                      "launch_ms": round(t_pre, 4),
                      "bytes_per_launch": pre_bytes},
+        "decode_roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                            "frac": round(dec_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic.get("decode_bytes"),
+                            "kernel": "kda_decode_step", "launch_ms": round(t_dec, 4),
+                            "bytes_per_launch": dec_bytes},
         "prefill": {"ms": round(t_pre, 4), "tokens_per_s": round(pre_tps, 1), "gb_per_s": round(pre_gbps, 1),
                     "hbm_frac": round(pre_gbps / PEAK_HBM_GBPS, 4), "tflops": round(pre_tflops, 2),
                     "mfma_frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4), "flops_per_launch": q["flops"]},
