@@ -6,6 +6,8 @@ One step = one pass of the hot path over one batch of synthetic input:
     fp32 gate/beta/state, chunk 64, initial state given, final state written), and
   * kda_decode_step over the decode workload (256 sequences x 32 heads, fp32 state
     128x128 updated in place).
+The output epilogue (kda_norm_gate: per-head RMSNorm and output gate) is timed on its own
+over the prefill output shape and reported next to the step.
 `value` is prefill tokens/s (B*T tokens per chunk_fwd launch); the decode step is
 reported in GB/s next to it.  Inputs are resident in HBM before the timed region.
 Timing uses HIP events recorded on the stream the kernels are launched on.
@@ -144,14 +146,23 @@ def main():
     def decode():
         kda.decode_step(dq, dk_, dv_, dg, db, dstate, out=dout)
 
+    # ------------------------------------------- output epilogue (prefill output shape)
+    eo, ez, ew = (x.to(dev) for x in ki.epilogue_inputs((B, T, H, w.dv), "bf16", seed=5))
+    eout = torch.empty_like(eo)
+
+    def epilogue():
+        kda.norm_gate(eo, ez, ew, eps=1e-6, out=eout)
+
     for _ in range(args.warmup):
         prefill()
         decode()
+        epilogue()
     torch.cuda.synchronize()
 
     # timed region: K steps, each = one prefill launch + one decode launch
     t_pre = time_launches(prefill, args.steps, stream)
     t_dec = time_launches(decode, args.steps, stream)
+    t_epi = time_launches(epilogue, args.steps, stream)
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     decode()
@@ -171,6 +182,9 @@ def main():
     pre_tflops = q["flops"] / (t_pre * 1e-3) / 1e12
     dec_bytes = (wd.B * wd.H * (2 * 4 * wd.dk * wd.dv + (2 * wd.dk + 2 * wd.dv) * 2 + 4 * wd.dk + 4))
     dec_gbps = dec_bytes / (t_dec * 1e-3) / 1e9
+    epi_rows = B * T * H
+    epi_bytes = epi_rows * w.dv * 2 * 3 + w.dv * 4  # o and gate read, out written (bf16), weight
+    epi_gbps = epi_bytes / (t_epi * 1e-3) / 1e9
 
     res = {
         "metric": METRIC,
@@ -204,6 +218,9 @@ def main():
                     "mfma_frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4), "flops_per_launch": q["flops"]},
         "decode": {"ms": round(t_dec, 4), "gb_per_s": round(dec_gbps, 1), "hbm_frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
                    "bytes_per_launch": dec_bytes},
+        "epilogue": {"kernel": "kda_norm_gate", "rows": epi_rows, "d": w.dv, "ms": round(t_epi, 4),
+                     "gb_per_s": round(epi_gbps, 1), "hbm_frac": round(epi_gbps / PEAK_HBM_GBPS, 4),
+                     "bytes_per_launch": epi_bytes},
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on the prefill batch ...")

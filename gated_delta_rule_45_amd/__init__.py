@@ -22,7 +22,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["chunk_fwd", "recurrent_fwd", "decode_step", "query", "KdaError", "LIB_PATH", "library"]
+__all__ = ["chunk_fwd", "recurrent_fwd", "decode_step", "norm_gate", "query", "KdaError", "LIB_PATH", "library"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
@@ -76,6 +76,8 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int,
                                     ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.kda_norm_gate.restype = ctypes.c_int
+    lib.kda_norm_gate.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int, ctypes.c_float, _P, _P, _P, _P, _P]
     lib.kda_query.restype = ctypes.c_int
     lib.kda_query.argtypes = [ctypes.POINTER(Problem), ctypes.c_uint32, ctypes.POINTER(QueryResult)]
     lib.kda_status_string.restype = ctypes.c_char_p
@@ -202,14 +204,21 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
               initial_state: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None, *,
               cu_seqlens_host=None, chunk_size: int = 0, scale: float = 1.0, dv_tile: int = 0,
               algo="auto", workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-              final_state: Optional[torch.Tensor] = None, output_final_state: bool = True, stream=None):
+              final_state: Optional[torch.Tensor] = None, output_final_state: bool = True, stream=None,
+              gate: Optional[torch.Tensor] = None, norm_weight: Optional[torch.Tensor] = None,
+              norm_eps: float = 1e-6):
     """Chunkwise KDA forward.  q, k: [B, T, H, d_k]; v: [B, T, H, d_v] (bf16 or fp32);
     g: [B, T, H, d_k] fp32 log-gate; beta: [B, T, H] fp32; initial_state: [N, H, d_k, d_v]
     fp32 or None; cu_seqlens: int32 [N+1] (B == 1) or None.  algo: "auto", "fused" or
     "two_pass"; workspace: uint8 device tensor for the two-pass algorithm (allocated here
-    when None and needed).  Returns (out, final_state)."""
-    return _fwd("chunk", q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_host, chunk_size, scale, dv_tile,
-                out, final_state, output_final_state, stream, algo=algo, workspace=workspace)
+    when None and needed).  With gate (shape and dtype of out) and norm_weight (fp32 [d_v]),
+    the output epilogue (kda_norm_gate) is applied to out in place on the same stream.
+    Returns (out, final_state)."""
+    out, fin = _fwd("chunk", q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_host, chunk_size, scale, dv_tile,
+                    out, final_state, output_final_state, stream, algo=algo, workspace=workspace)
+    if gate is not None or norm_weight is not None:
+        norm_gate(out, gate, norm_weight, eps=norm_eps, out=out, stream=stream)
+    return out, fin
 
 
 def recurrent_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
@@ -222,9 +231,12 @@ def recurrent_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
 
 
 def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
-                state: torch.Tensor, *, scale: float = 1.0, out: Optional[torch.Tensor] = None, stream=None):
+                state: torch.Tensor, *, scale: float = 1.0, out: Optional[torch.Tensor] = None, stream=None,
+                gate: Optional[torch.Tensor] = None, norm_weight: Optional[torch.Tensor] = None,
+                norm_eps: float = 1e-6):
     """One decode token per sequence.  q, k, g: [N, H, d_k]; v: [N, H, d_v]; beta: [N, H];
-    state: [N, H, d_k, d_v] fp32 (updated in place).  Returns out [N, H, d_v]."""
+    state: [N, H, d_k, d_v] fp32 (updated in place).  With gate and norm_weight the output
+    epilogue is applied to out in place.  Returns out [N, H, d_v]."""
     dev = q.device
     if q.dim() != 3:
         raise ValueError("q must be [N, H, d_k]")
@@ -241,6 +253,31 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
     _need(out, "out", q.dtype, (N, H, dv), dev)
     st = library().kda_decode_step(N, H, dk, dv, _io_code(q.dtype), scale, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                    _ptr(beta), _ptr(state), _ptr(out), _stream_handle(dev, stream))
+    _check(st)
+    if gate is not None or norm_weight is not None:
+        norm_gate(out, gate, norm_weight, eps=norm_eps, out=out, stream=stream)
+    return out
+
+
+def norm_gate(o: torch.Tensor, gate: torch.Tensor, weight: torch.Tensor, *, eps: float = 1e-6,
+              out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Output epilogue over the last axis (one head's d values): o / sqrt(mean(o^2) + eps)
+    * weight * sigmoid(gate).  o, gate: same shape and dtype (bf16 or fp32), contiguous;
+    weight: fp32 [d].  out may be o (in place).  Returns out."""
+    if gate is None or weight is None:
+        raise ValueError("the output epilogue needs both gate and norm weight")
+    dev = o.device
+    d = o.shape[-1]
+    _need(gate, "gate", o.dtype, tuple(o.shape), dev)
+    _need(weight, "weight", torch.float32, (d,), dev)
+    if not o.is_contiguous():
+        raise ValueError("o must be contiguous")
+    if out is None:
+        out = torch.empty_like(o)
+    _need(out, "out", o.dtype, tuple(o.shape), dev)
+    rows = o.numel() // d if d else 0
+    st = library().kda_norm_gate(rows, d, _io_code(o.dtype), eps, _ptr(o), _ptr(gate), _ptr(weight), _ptr(out),
+                                 _stream_handle(dev, stream))
     _check(st)
     return out
 

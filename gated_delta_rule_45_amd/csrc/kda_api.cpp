@@ -343,6 +343,32 @@ kda_status_t kda_decode_step(int32_t num_seqs, int32_t num_heads, int32_t head_d
     }
 }
 
+kda_status_t kda_norm_gate(int64_t rows, int32_t d, kda_dtype_t io_dtype, float eps, const void *o,
+                           const void *gate, const float *weight, void *out, void *stream) {
+    try {
+        if (rows < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "rows %lld < 0", (long long)rows);
+        if (io_dtype != KDA_F32 && io_dtype != KDA_BF16)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "io_dtype %d is not KDA_F32 or KDA_BF16", (int)io_dtype);
+        if (!supported_head_dim(d)) return fail(KDA_ERR_UNSUPPORTED, "d=%d: supported are 64 and 128", d);
+        if (!std::isfinite(eps) || eps < 0.f) return fail(KDA_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+        if (kda::norm_gate_blocks(io_dtype, rows, d) > 0x7fffffffLL) return fail(KDA_ERR_UNSUPPORTED, "too many rows");
+        if (rows == 0) return ok();
+        const void *req[] = {o, gate, weight, out};
+        const char *names[] = {"o", "gate", "weight", "out"};
+        for (int i = 0; i < 4; ++i) {
+            if (!req[i]) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
+            if (!aligned(req[i], 16)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", names[i]);
+        }
+        if (out == gate || (const void *)weight == out || (const void *)weight == o || (const void *)weight == gate)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "out may alias o only");
+        return hip_status(kda::launch_norm_gate(io_dtype, rows, d, eps, o, gate, weight, out,
+                                                static_cast<hipStream_t>(stream)),
+                          "kda_norm_gate launch");
+    } catch (...) {
+        return fail(KDA_ERR_HIP, "unexpected exception in kda_norm_gate");
+    }
+}
+
 kda_status_t kda_query(const kda_problem_t *problem, uint32_t flags, kda_query_result_t *res) {
     try {
         if (!res) return fail(KDA_ERR_INVALID_ARGUMENT, "result is NULL");

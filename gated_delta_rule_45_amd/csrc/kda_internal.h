@@ -61,4 +61,9 @@ hipError_t launch_split_bf16(const FwdParams &p, int chunk, int spw, int nw, cha
                              hipStream_t stream);
 constexpr int kSerialThreads = 256;
 
+// Output epilogue (per-head RMSNorm and output gate) over rows of d values.
+int64_t norm_gate_blocks(kda_dtype_t io, int64_t rows, int d);
+hipError_t launch_norm_gate(kda_dtype_t io, int64_t rows, int d, float eps, const void *o, const void *z,
+                            const float *w, void *out, hipStream_t stream);
+
 }  // namespace kda

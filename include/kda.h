@@ -136,6 +136,25 @@ kda_status_t kda_decode_step(int32_t num_seqs, int32_t num_heads, int32_t head_d
                              kda_dtype_t io_dtype, float scale, const void *q, const void *k, const void *v,
                              const float *g, const float *beta, float *state, void *out, void *stream);
 
+/*
+ * kda_norm_gate -- output epilogue: per-head RMSNorm followed by the data-dependent output
+ * gate, applied before the output projection ("Kimi Linear model composition" section of
+ * the summary page; the page gives no formula, this is the reading used): for each of
+ * `rows` rows of d values (one token and head),
+ *
+ *     out[r, :] = o[r, :] / sqrt(mean_j o[r, j]^2 + eps) * weight[:] * sigmoid(gate[r, :])
+ *
+ *  o, gate, out  [rows, d], io_dtype (bf16 results rounded to nearest even), row-major;
+ *  weight        [d] fp32, shared by all heads; gate is the pre-activation (the low-rank
+ *                projection that produces it is outside this operator).
+ *  d is 64 or 128; eps >= 0 and finite.  out may be o itself (in place); no other aliasing.
+ *  All pointers device memory, 16-byte aligned; nothing is allocated or retained.
+ *  Errors: KDA_ERR_INVALID_ARGUMENT (sizes, eps, NULL or misaligned pointers, aliasing),
+ *  KDA_ERR_UNSUPPORTED (d), KDA_ERR_HIP (launch).  rows == 0 launches nothing.
+ */
+kda_status_t kda_norm_gate(int64_t rows, int32_t d, kda_dtype_t io_dtype, float eps, const void *o,
+                           const void *gate, const float *weight, void *out, void *stream);
+
 /* Result of kda_query. */
 typedef struct {
     int32_t version;           /* KDA_VERSION of the library */

@@ -174,3 +174,15 @@ def to_numpy_io(x: torch.Tensor) -> np.ndarray:
     if x.dtype == torch.float32:
         return x.numpy()
     raise TypeError(f"unsupported dtype {x.dtype}")
+
+
+def epilogue_inputs(shape, io: str, seed: int, *, gate_std: float = 2.0):
+    """Inputs of the output epilogue for rows of shape[-1] values: o ~ N(0, 1), the gate
+    pre-activation z ~ N(0, gate_std^2) (cast to the io dtype), norm weight w = 1 + 0.1 N(0, 1)
+    in fp32.  Synthetic stand-ins for a trained layer's output, gate projection and weight."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    dt = _io_dtype(io)
+    o = torch.randn(*shape, generator=gen, dtype=torch.float32).to(dt)
+    z = (gate_std * torch.randn(*shape, generator=gen, dtype=torch.float32)).to(dt)
+    w = 1.0 + 0.1 * torch.randn(shape[-1], generator=gen, dtype=torch.float32)
+    return o, z, w

@@ -176,3 +176,22 @@ def test_query_reports_config_and_work():
     # packed batch: num_seqs > 0, seq_len = total tokens
     r = kda.query(1, 1000, 32, 128, 128, "bf16", num_seqs=64)
     assert r["grid_blocks"] == 64 * 32 * (128 // r["dv_tile"])
+
+
+def call_norm_gate(rows=8, d=128, io=kda.KDA_BF16, eps=1e-6, o=fake(0), gate=fake(1), weight=fake(2), out=fake(3)):
+    return kda.library().kda_norm_gate(rows, d, io, eps, o, gate, weight, out, None)
+
+
+def test_norm_gate_validation():
+    lib = kda.library()
+    assert call_norm_gate(rows=0) == kda.KDA_OK  # nothing to do, nothing launched
+    assert call_norm_gate(rows=-1) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert call_norm_gate(d=96) == kda.KDA_ERR_UNSUPPORTED
+    assert call_norm_gate(io=7) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert call_norm_gate(eps=-1.0) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert call_norm_gate(eps=float("nan")) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert call_norm_gate(gate=None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert b"gate" in lib.kda_last_error()
+    assert call_norm_gate(out=ctypes.c_void_p(0x100008)) == kda.KDA_ERR_INVALID_ARGUMENT  # misaligned
+    assert call_norm_gate(out=fake(1)) == kda.KDA_ERR_INVALID_ARGUMENT  # out aliases gate
+    assert b"alias" in lib.kda_last_error()
