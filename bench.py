@@ -6,8 +6,9 @@ One step = one pass of the hot path over one batch of synthetic input:
     fp32 gate/beta/state, chunk 64, initial state given, final state written), and
   * kda_decode_step over the decode workload (256 sequences x 32 heads, fp32 state
     128x128 updated in place).
-The output epilogue (kda_norm_gate: per-head RMSNorm and output gate) is timed on its own
-over the prefill output shape and reported next to the step.
+The prologue (kda_prologue: short convolution + Swish, q/k L2 norm, gate and beta activations)
+and the output epilogue (kda_norm_gate: per-head RMSNorm and output gate) are timed on their
+own over the prefill shapes and reported next to the step.
 `value` is prefill tokens/s (B*T tokens per chunk_fwd launch); the decode step is
 reported in GB/s next to it.  Inputs are resident in HBM before the timed region.
 Timing uses HIP events recorded on the stream the kernels are launched on.
@@ -146,6 +147,14 @@ def main():
     def decode():
         kda.decode_step(dq, dk_, dv_, dg, db, dstate, out=dout)
 
+    # ------------------------------------------- prologue (raw projections of the prefill shape)
+    pin = ki.prologue_inputs(B, T, H, w.dk, w.dv, 4, "bf16", seed=6)
+    pd = {k: (None if x is None else x.to(dev)) for k, x in pin.items()}
+
+    def prologue():
+        kda.prologue(pd["q_raw"], pd["k_raw"], pd["v_raw"], pd["conv_q"], pd["conv_k"], pd["conv_v"], pd["g_raw"],
+                     pd["beta_raw"])
+
     # ------------------------------------------- output epilogue (prefill output shape)
     eo, ez, ew = (x.to(dev) for x in ki.epilogue_inputs((B, T, H, w.dv), "bf16", seed=5))
     eout = torch.empty_like(eo)
@@ -157,12 +166,14 @@ def main():
         prefill()
         decode()
         epilogue()
+        prologue()
     torch.cuda.synchronize()
 
     # timed region: K steps, each = one prefill launch + one decode launch
     t_pre = time_launches(prefill, args.steps, stream)
     t_dec = time_launches(decode, args.steps, stream)
     t_epi = time_launches(epilogue, args.steps, stream)
+    t_pro = time_launches(prologue, args.steps, stream)
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     decode()
@@ -185,6 +196,9 @@ def main():
     epi_rows = B * T * H
     epi_bytes = epi_rows * w.dv * 2 * 3 + w.dv * 4  # o and gate read, out written (bf16), weight
     epi_gbps = epi_bytes / (t_epi * 1e-3) / 1e9
+    # prologue per (token, head): raw q, k, v (bf16) + g_raw + beta_raw read, the same written
+    pro_bytes = B * T * H * 2 * ((2 * w.dk + w.dv) * 2 + 4 * w.dk + 4) + 4 * H * (2 * w.dk + w.dv) * 4
+    pro_gbps = pro_bytes / (t_pro * 1e-3) / 1e9
 
     res = {
         "metric": METRIC,
@@ -218,6 +232,9 @@ def main():
                     "mfma_frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4), "flops_per_launch": q["flops"]},
         "decode": {"ms": round(t_dec, 4), "gb_per_s": round(dec_gbps, 1), "hbm_frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
                    "bytes_per_launch": dec_bytes},
+        "prologue": {"kernel": "kda_prologue", "conv_width": 4, "ms": round(t_pro, 4),
+                     "gb_per_s": round(pro_gbps, 1), "hbm_frac": round(pro_gbps / PEAK_HBM_GBPS, 4),
+                     "bytes_per_launch": pro_bytes},
         "epilogue": {"kernel": "kda_norm_gate", "rows": epi_rows, "d": w.dv, "ms": round(t_epi, 4),
                      "gb_per_s": round(epi_gbps, 1), "hbm_frac": round(epi_gbps / PEAK_HBM_GBPS, 4),
                      "bytes_per_launch": epi_bytes},

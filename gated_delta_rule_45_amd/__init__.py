@@ -22,7 +22,8 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["chunk_fwd", "recurrent_fwd", "decode_step", "norm_gate", "query", "KdaError", "LIB_PATH", "library"]
+__all__ = ["chunk_fwd", "recurrent_fwd", "decode_step", "prologue", "norm_gate", "query", "KdaError", "LIB_PATH",
+           "library"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
@@ -44,6 +45,12 @@ class Problem(ctypes.Structure):
                 ("head_dim_k", ctypes.c_int32), ("head_dim_v", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
                 ("io_dtype", ctypes.c_int), ("chunk_size", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("dv_tile", ctypes.c_int32), ("algo", ctypes.c_int)]
+
+
+class PrologueProblem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
+                ("num_heads", ctypes.c_int32), ("head_dim_k", ctypes.c_int32), ("head_dim_v", ctypes.c_int32),
+                ("conv_width", ctypes.c_int32), ("io_dtype", ctypes.c_int), ("norm_eps", ctypes.c_float)]
 
 
 class QueryResult(ctypes.Structure):
@@ -76,6 +83,8 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int,
                                     ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.kda_prologue.restype = ctypes.c_int
+    lib.kda_prologue.argtypes = [ctypes.POINTER(PrologueProblem)] + [_P] * 17
     lib.kda_norm_gate.restype = ctypes.c_int
     lib.kda_norm_gate.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int, ctypes.c_float, _P, _P, _P, _P, _P]
     lib.kda_query.restype = ctypes.c_int
@@ -257,6 +266,49 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
     if gate is not None or norm_weight is not None:
         norm_gate(out, gate, norm_weight, eps=norm_eps, out=out, stream=stream)
     return out
+
+
+def prologue(q_raw: torch.Tensor, k_raw: torch.Tensor, v_raw: torch.Tensor, conv_q: torch.Tensor,
+             conv_k: torch.Tensor, conv_v: torch.Tensor, g_raw: torch.Tensor, beta_raw: torch.Tensor,
+             cu_seqlens: Optional[torch.Tensor] = None, *, conv_state: Optional[torch.Tensor] = None,
+             output_conv_state: bool = False, norm_eps: float = 1e-6, stream=None):
+    """Raw projections -> (q, k, v, g, beta[, conv_state_out]).  q_raw, k_raw: [B, T, H, d_k];
+    v_raw: [B, T, H, d_v] (bf16 or fp32); conv_*: fp32 [H, d, W] filter taps; g_raw: fp32
+    [B, T, H, d_k]; beta_raw: fp32 [B, T, H]; cu_seqlens: int32 [N+1] (B == 1) or None;
+    conv_state: [N, W-1, H, 2 d_k + d_v] raw inputs preceding each sequence, or None (zeros)."""
+    dev = q_raw.device
+    if q_raw.dim() != 4:
+        raise ValueError("q_raw must be [B, T, H, d_k]")
+    B, T, H, dk = q_raw.shape
+    dv = v_raw.shape[-1]
+    W = conv_q.shape[-1]
+    dt = q_raw.dtype
+    _need(k_raw, "k_raw", dt, (B, T, H, dk), dev)
+    _need(v_raw, "v_raw", dt, (B, T, H, dv), dev)
+    _need(conv_q, "conv_q", torch.float32, (H, dk, W), dev)
+    _need(conv_k, "conv_k", torch.float32, (H, dk, W), dev)
+    _need(conv_v, "conv_v", torch.float32, (H, dv, W), dev)
+    _need(g_raw, "g_raw", torch.float32, (B, T, H, dk), dev)
+    _need(beta_raw, "beta_raw", torch.float32, (B, T, H), dev)
+    if cu_seqlens is not None:
+        N = cu_seqlens.numel() - 1
+        _need(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
+    else:
+        N = B
+    if conv_state is not None:
+        _need(conv_state, "conv_state", dt, (N, W - 1, H, 2 * dk + dv), dev)
+    st_out = torch.empty((N, W - 1, H, 2 * dk + dv), dtype=dt, device=dev) if output_conv_state else None
+    q, k, v = torch.empty_like(q_raw), torch.empty_like(k_raw), torch.empty_like(v_raw)
+    g = torch.empty_like(g_raw)
+    beta = torch.empty_like(beta_raw)
+    p = PrologueProblem(batch=B, seq_len=T, num_seqs=N if cu_seqlens is not None else 0, num_heads=H, head_dim_k=dk,
+                        head_dim_v=dv, conv_width=W, io_dtype=_io_code(dt), norm_eps=norm_eps)
+    st = library().kda_prologue(ctypes.byref(p), _ptr(q_raw), _ptr(k_raw), _ptr(v_raw), _ptr(conv_q), _ptr(conv_k),
+                                _ptr(conv_v), _ptr(g_raw), _ptr(beta_raw), _ptr(cu_seqlens), _ptr(conv_state),
+                                _ptr(st_out), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                _stream_handle(dev, stream))
+    _check(st)
+    return (q, k, v, g, beta, st_out) if output_conv_state else (q, k, v, g, beta)
 
 
 def norm_gate(o: torch.Tensor, gate: torch.Tensor, weight: torch.Tensor, *, eps: float = 1e-6,

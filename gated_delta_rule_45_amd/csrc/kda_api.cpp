@@ -343,6 +343,65 @@ kda_status_t kda_decode_step(int32_t num_seqs, int32_t num_heads, int32_t head_d
     }
 }
 
+kda_status_t kda_prologue(const kda_prologue_t *p, const void *q_raw, const void *k_raw, const void *v_raw,
+                          const float *conv_q, const float *conv_k, const float *conv_v, const float *g_raw,
+                          const float *beta_raw, const int32_t *cu_seqlens, const void *conv_state,
+                          void *conv_state_out, void *q, void *k, void *v, float *g, float *beta, void *stream) {
+    try {
+        if (!p) return fail(KDA_ERR_INVALID_ARGUMENT, "problem is NULL");
+        if (p->batch < 0 || p->seq_len < 0 || p->num_seqs < 0 || p->num_heads < 1)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "bad sizes: batch=%d seq_len=%d num_seqs=%d num_heads=%d", p->batch,
+                        p->seq_len, p->num_seqs, p->num_heads);
+        if (p->io_dtype != KDA_F32 && p->io_dtype != KDA_BF16)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "io_dtype %d is not KDA_F32 or KDA_BF16", (int)p->io_dtype);
+        if (!supported_head_dim(p->head_dim_k) || !supported_head_dim(p->head_dim_v))
+            return fail(KDA_ERR_UNSUPPORTED, "head dims d_k=%d d_v=%d: supported are 64 and 128", p->head_dim_k,
+                        p->head_dim_v);
+        if (p->conv_width < 1 || p->conv_width > 4)
+            return fail(KDA_ERR_UNSUPPORTED, "conv_width %d: supported are 1..4", p->conv_width);
+        if (!std::isfinite(p->norm_eps) || p->norm_eps < 0.f)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "norm_eps must be finite and >= 0");
+        const bool varlen = p->num_seqs > 0;
+        if (varlen && p->batch != 1) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens needs batch == 1");
+        if (varlen && !cu_seqlens) return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs > 0 needs cu_seqlens");
+        const int64_t tokens = varlen ? (int64_t)p->seq_len : (int64_t)p->batch * p->seq_len;
+        const int32_t nseq = varlen ? p->num_seqs : p->batch;
+        if (tokens * p->num_heads * (int64_t)std::max(p->head_dim_k, p->head_dim_v) >= (1LL << 40))
+            return fail(KDA_ERR_UNSUPPORTED, "tensor too large");
+        if (tokens == 0 && !conv_state_out) return ok();
+        const void *req[] = {q_raw, k_raw, v_raw, conv_q, conv_k, conv_v, g_raw, beta_raw, q, k, v, g, beta};
+        const char *names[] = {"q_raw", "k_raw", "v_raw", "conv_q", "conv_k", "conv_v", "g_raw", "beta_raw",
+                               "q", "k", "v", "g", "beta"};
+        for (int i = 0; i < 13 && tokens > 0; ++i)  // with no tokens only the state is touched
+            if (!req[i]) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
+        const void *al16[] = {q_raw, k_raw, v_raw, g_raw, q, k, v, g, conv_state, conv_state_out, conv_q, conv_k, conv_v};
+        const char *n16[] = {"q_raw", "k_raw", "v_raw", "g_raw", "q", "k", "v", "g", "conv_state", "conv_state_out",
+                             "conv_q", "conv_k", "conv_v"};
+        for (int i = 0; i < 13; ++i)
+            if (!aligned(al16[i], 16)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", n16[i]);
+        const void *al4[] = {beta_raw, beta};
+        for (int i = 0; i < 2; ++i)
+            if (!aligned(al4[i], 4)) return fail(KDA_ERR_INVALID_ARGUMENT, "a 4-byte argument is misaligned");
+        const void *outs[] = {q, k, v, g, beta, conv_state_out};
+        const void *ins[] = {q_raw, k_raw, v_raw, g_raw, beta_raw, conv_state, conv_q, conv_k, conv_v};
+        for (const void *o : outs)
+            for (const void *i : ins)
+                if (o && o == i) return fail(KDA_ERR_INVALID_ARGUMENT, "an output aliases an input");
+        if (cu_seqlens && !aligned(cu_seqlens, 4)) return fail(KDA_ERR_INVALID_ARGUMENT, "cu_seqlens misaligned");
+        const void *raw[3] = {q_raw, k_raw, v_raw};
+        const float *w[3] = {conv_q, conv_k, conv_v};
+        void *out[3] = {q, k, v};
+        return hip_status(kda::launch_prologue(p->io_dtype, tokens, nseq, varlen ? 0 : p->seq_len, p->num_heads,
+                                               p->head_dim_k, p->head_dim_v, p->conv_width,
+                                               varlen ? cu_seqlens : nullptr, p->norm_eps, raw, w, g_raw, beta_raw,
+                                               conv_state, conv_state_out, out, g, beta,
+                                               static_cast<hipStream_t>(stream)),
+                          "kda_prologue launch");
+    } catch (...) {
+        return fail(KDA_ERR_HIP, "unexpected exception in kda_prologue");
+    }
+}
+
 kda_status_t kda_norm_gate(int64_t rows, int32_t d, kda_dtype_t io_dtype, float eps, const void *o,
                            const void *gate, const float *weight, void *out, void *stream) {
     try {

@@ -61,6 +61,12 @@ hipError_t launch_split_bf16(const FwdParams &p, int chunk, int spw, int nw, cha
                              hipStream_t stream);
 constexpr int kSerialThreads = 256;
 
+// Prologue (short convolution + Swish, q/k L2 normalisation, gate and beta activations).
+hipError_t launch_prologue(kda_dtype_t io, int64_t tokens, int32_t num_seqs, int32_t seq_len, int32_t H, int32_t dk,
+                           int32_t dv, int32_t W, const int32_t *cu, float eps, const void *const raw[3],
+                           const float *const w[3], const float *g_raw, const float *b_raw, const void *st_in,
+                           void *st_out, void *const out[3], float *g, float *b, hipStream_t s);
+
 // Output epilogue (per-head RMSNorm and output gate) over rows of d values.
 int64_t norm_gate_blocks(kda_dtype_t io, int64_t rows, int d);
 hipError_t launch_norm_gate(kda_dtype_t io, int64_t rows, int d, float eps, const void *o, const void *z,

@@ -136,6 +136,47 @@ kda_status_t kda_decode_step(int32_t num_seqs, int32_t num_heads, int32_t head_d
                              kda_dtype_t io_dtype, float scale, const void *q, const void *k, const void *v,
                              const float *g, const float *beta, float *state, void *out, void *stream);
 
+/* Shape of a kda_prologue call (same batch / packed conventions as kda_problem_t). */
+typedef struct {
+    int32_t batch;       /* B; must be 1 when num_seqs > 0 */
+    int32_t seq_len;     /* tokens per sequence, or the packed token count when num_seqs > 0 */
+    int32_t num_seqs;    /* 0: B sequences of seq_len tokens; > 0: packed by cu_seqlens */
+    int32_t num_heads;   /* H */
+    int32_t head_dim_k;  /* 64 or 128 */
+    int32_t head_dim_v;  /* 64 or 128 */
+    int32_t conv_width;  /* W, taps of the short convolution: 1..4 */
+    kda_dtype_t io_dtype;/* raw q/k/v, outputs q/k/v and the convolution state */
+    float norm_eps;      /* >= 0: q and k are divided by sqrt(sum x^2 + norm_eps) */
+} kda_prologue_t;
+
+/*
+ * kda_prologue -- the steps before the operator ("Kimi Linear model composition" section of
+ * the summary page: query, key and value pass a short convolution and Swish, query and key an
+ * L2 normalisation, and the decay gate a GDN / Mamba-like decay function; the page gives no
+ * formulas, these are the readings used):
+ *
+ *   c_t = sum_{i<W} w[i] x_{t-W+1+i}     causal depthwise convolution over time per channel
+ *   y   = c sigmoid(c)                   Swish
+ *   q, k = y / sqrt(sum_d y^2 + eps);  v = y
+ *   g = -softplus(g_raw);  beta = sigmoid(beta_raw)
+ *
+ *  q_raw, k_raw [tokens, H, d_k], v_raw [tokens, H, d_v]   io_dtype
+ *  conv_q, conv_k [H, d_k, W], conv_v [H, d_v, W]          fp32 filter taps (tap W-1 = current token)
+ *  g_raw [tokens, H, d_k], beta_raw [tokens, H]            fp32
+ *  cu_seqlens  int32 [num_seqs + 1] device (when num_seqs > 0), as for kda_chunk_fwd
+ *  conv_state  [S, W-1, H, 2 d_k + d_v] io_dtype or NULL: the raw q | k | v inputs of the W-1
+ *              tokens before each of the S sequences (NULL = zeros); conv_state_out, same
+ *              shape or NULL, receives the last W-1 raw inputs of each sequence (so a sequence
+ *              can be continued, one token at a time in decoding)
+ *  q, k, v     outputs, shapes of the raw inputs, io_dtype; g, beta fp32
+ *  Tensors 16-byte aligned (beta_raw and beta 4-byte); no output may alias an input,
+ *  and conv_state_out must not be conv_state.  Errors as for kda_chunk_fwd.
+ */
+kda_status_t kda_prologue(const kda_prologue_t *problem, const void *q_raw, const void *k_raw, const void *v_raw,
+                          const float *conv_q, const float *conv_k, const float *conv_v, const float *g_raw,
+                          const float *beta_raw, const int32_t *cu_seqlens, const void *conv_state,
+                          void *conv_state_out, void *q, void *k, void *v, float *g, float *beta, void *stream);
+
 /*
  * kda_norm_gate -- output epilogue: per-head RMSNorm followed by the data-dependent output
  * gate, applied before the output projection ("Kimi Linear model composition" section of

@@ -186,3 +186,28 @@ def epilogue_inputs(shape, io: str, seed: int, *, gate_std: float = 2.0):
     z = (gate_std * torch.randn(*shape, generator=gen, dtype=torch.float32)).to(dt)
     w = 1.0 + 0.1 * torch.randn(shape[-1], generator=gen, dtype=torch.float32)
     return o, z, w
+
+
+def prologue_inputs(B: int, T: int, H: int, dk: int, dv: int, W: int, io: str, seed: int, *,
+                    lengths: Optional[list] = None, g_mu: float = 0.0, with_state: bool = False):
+    """Raw projections for the prologue.  Draw order: q_raw, k_raw, v_raw ~ N(0, 1) (cast to the
+    io dtype), filter taps for q, k, v ~ N(0, 0.5^2) [H, d, W], g_raw ~ N(g_mu, 1), beta_raw ~
+    N(0, 1), then (with_state) the carried-in convolution state ~ N(0, 1) in the io dtype.
+    With `lengths` the tokens are one packed row (B == 1) and cu_seqlens is returned."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    dt = _io_dtype(io)
+    rn = lambda *s: torch.randn(*s, generator=gen, dtype=torch.float32)
+    Tt = sum(lengths) if lengths is not None else T
+    shape = (1, Tt, H) if lengths is not None else (B, T, H)
+    q, k = rn(*shape, dk).to(dt), rn(*shape, dk).to(dt)
+    v = rn(*shape, dv).to(dt)
+    wq, wk, wv = 0.5 * rn(H, dk, W), 0.5 * rn(H, dk, W), 0.5 * rn(H, dv, W)
+    g = rn(*shape, dk) + g_mu
+    b = rn(*shape)
+    N = len(lengths) if lengths is not None else B
+    st = rn(N, W - 1, H, 2 * dk + dv).to(dt) if with_state else None
+    cu = None
+    if lengths is not None:
+        cu = torch.tensor([0] + list(np.cumsum(lengths)), dtype=torch.int32)
+    return dict(q_raw=q, k_raw=k, v_raw=v, conv_q=wq, conv_k=wk, conv_v=wv, g_raw=g, beta_raw=b, conv_state=st,
+                cu_seqlens=cu)

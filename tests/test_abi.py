@@ -195,3 +195,36 @@ def test_norm_gate_validation():
     assert call_norm_gate(out=ctypes.c_void_p(0x100008)) == kda.KDA_ERR_INVALID_ARGUMENT  # misaligned
     assert call_norm_gate(out=fake(1)) == kda.KDA_ERR_INVALID_ARGUMENT  # out aliases gate
     assert b"alias" in lib.kda_last_error()
+
+
+def prologue_problem(**kw):
+    base = dict(batch=2, seq_len=16, num_seqs=0, num_heads=2, head_dim_k=64, head_dim_v=64, conv_width=4,
+                io_dtype=kda.KDA_BF16, norm_eps=1e-6)
+    base.update(kw)
+    return kda.PrologueProblem(**base)
+
+
+def call_prologue(p, ptrs=None, **over):
+    a = [fake(i) for i in range(17)]  # q_raw k_raw v_raw conv_q conv_k conv_v g_raw beta_raw cu st st_out q k v g beta
+    a[8], a[9], a[10] = None, None, None
+    for i, v in over.items():
+        a[int(i[1:])] = v
+    return kda.library().kda_prologue(ctypes.byref(p) if p is not None else None, *a, None)
+
+
+def test_prologue_validation():
+    lib = kda.library()
+    assert call_prologue(None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert call_prologue(prologue_problem(conv_width=5)) == kda.KDA_ERR_UNSUPPORTED
+    assert call_prologue(prologue_problem(conv_width=0)) == kda.KDA_ERR_UNSUPPORTED
+    assert call_prologue(prologue_problem(head_dim_k=96)) == kda.KDA_ERR_UNSUPPORTED
+    assert call_prologue(prologue_problem(norm_eps=-1.0)) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert call_prologue(prologue_problem(num_seqs=3)) == kda.KDA_ERR_INVALID_ARGUMENT  # batch != 1
+    assert call_prologue(prologue_problem(batch=1, num_seqs=3)) == kda.KDA_ERR_INVALID_ARGUMENT  # no cu_seqlens
+    assert b"cu_seqlens" in lib.kda_last_error()
+    assert call_prologue(prologue_problem(), a11=fake(0)) == kda.KDA_ERR_INVALID_ARGUMENT  # q aliases q_raw
+    assert b"alias" in lib.kda_last_error()
+    assert call_prologue(prologue_problem(), a9=fake(20), a10=fake(20)) == kda.KDA_ERR_INVALID_ARGUMENT  # state in place
+    assert call_prologue(prologue_problem(), a0=None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert call_prologue(prologue_problem(), a6=ctypes.c_void_p(0x100004)) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert call_prologue(prologue_problem(seq_len=0)) == kda.KDA_OK  # no tokens, no state out: nothing to do
