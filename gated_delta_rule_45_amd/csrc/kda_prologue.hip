@@ -9,7 +9,7 @@
 //   q, k = y / sqrt(sum y^2 + eps)        over the head dimension;  v = y
 //   g    = -softplus(g_raw),  beta = sigmoid(beta_raw)
 //
-// Bound: HBM.  Each lane owns one 16-byte segment of a head's rows and walks 16 consecutive
+// Bound: HBM.  Each lane owns one 16-byte segment of a head's rows and walks 8 consecutive
 // tokens, so every raw input is read once.
 #include <algorithm>
 
@@ -79,9 +79,11 @@ __device__ __forceinline__ void find_seq(const PrologueArgs &a, int64_t t, int &
     end = a.cu[lo + 1];
 }
 
+constexpr int kConvTokensPerStream = 8;
+
 // One tensor (q, k or v): rows of D values at column offset `col` of the state's concatenated
 // q | k | v rows.  NORM: L2-normalise each row.  A workgroup takes one head and TT consecutive
-// tokens; each group of LPR lanes streams TT / G of them in order, so a lane keeps its filter
+// tokens; each group of LPR lanes streams L of them in order, so a lane keeps its filter
 // taps and the last W-1 raw inputs of its channels in registers and loads each input once.
 template <typename IO, int D, bool NORM, int W>
 __global__ void __launch_bounds__(256) kda_conv_swish_kernel(PrologueArgs a, const IO *__restrict__ x,
@@ -90,7 +92,7 @@ __global__ void __launch_bounds__(256) kda_conv_swish_kernel(PrologueArgs a, con
     constexpr int N = Seg16<IO>::N;
     constexpr int LPR = D / N;      // lanes per row
     constexpr int G = 256 / LPR;    // token streams per workgroup
-    constexpr int L = 16;           // tokens per stream
+    constexpr int L = kConvTokensPerStream;
     constexpr int TT = G * L;       // tokens per workgroup
     static_assert(LPR <= 64 && 64 % LPR == 0, "a row lives inside one wave");
     const int seg = threadIdx.x % LPR;
@@ -155,7 +157,7 @@ __global__ void __launch_bounds__(256) kda_conv_swish_kernel(PrologueArgs a, con
             float c = 0.f;
 #pragma unroll
             for (int i = 0; i < W; ++i) c = fmaf(wc[j * W + i], win[i][j], c);
-            acc[j] = c / (1.0f + __expf(-c));
+            acc[j] = c * __builtin_amdgcn_rcpf(1.0f + __expf(-c));  // Swish; reciprocal to 1 ulp
         }
         if constexpr (NORM) {
             float ss = 0.f;
@@ -222,7 +224,7 @@ __global__ void __launch_bounds__(256) kda_gate_beta_kernel(int64_t gcount, int6
 template <typename IO, int D, bool NORM>
 hipError_t launch_conv(const PrologueArgs &a, const void *x, const float *w, const void *st_in, void *st_out, int col,
                        void *y, hipStream_t s) {
-    constexpr int TT = 256 / (D / Seg16<IO>::N) * 16;  // tokens per workgroup
+    constexpr int TT = 256 / (D / Seg16<IO>::N) * kConvTokensPerStream;  // tokens per workgroup
     const int64_t blocks = (a.tokens + TT - 1) / TT * a.H;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
