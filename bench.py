@@ -185,6 +185,8 @@ def main():
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / args.steps
 
+    # autotuning over (chunk, d_v tile, algorithm) on the prefill tensors, reported alongside
+    tuned = kda.tune(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], final_state=torch.empty_like(fin))
     traffic = measured_traffic()
     tokens = B * T
     pre_tps = tokens / (t_pre * 1e-3)
@@ -232,6 +234,8 @@ def main():
                     "mfma_frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4), "flops_per_launch": q["flops"]},
         "decode": {"ms": round(t_dec, 4), "gb_per_s": round(dec_gbps, 1), "hbm_frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
                    "bytes_per_launch": dec_bytes},
+        "tuned": {"chunk": tuned["chunk_size"], "dv_tile": tuned["dv_tile"],
+                  "algo": ["auto", "fused", "two_pass"][tuned["algo"]], "ms": round(tuned["tuned_ms"], 4)},
         "prologue": {"kernel": "kda_prologue", "conv_width": 4, "ms": round(t_pro, 4),
                      "gb_per_s": round(pro_gbps, 1), "hbm_frac": round(pro_gbps / PEAK_HBM_GBPS, 4),
                      "bytes_per_launch": pro_bytes},

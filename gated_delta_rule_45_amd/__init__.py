@@ -22,8 +22,8 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["chunk_fwd", "recurrent_fwd", "decode_step", "prologue", "norm_gate", "query", "KdaError", "LIB_PATH",
-           "library"]
+__all__ = ["chunk_fwd", "recurrent_fwd", "decode_step", "prologue", "norm_gate", "query", "tune", "KdaError",
+           "LIB_PATH", "library"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
@@ -60,7 +60,7 @@ class QueryResult(ctypes.Structure):
                 ("lds_bytes", ctypes.c_int32), ("grid_blocks", ctypes.c_int64), ("flops", ctypes.c_double),
                 ("hbm_bytes", ctypes.c_double), ("device_ok", ctypes.c_int32), ("compute_units", ctypes.c_int32),
                 ("arch", ctypes.c_char * 64), ("peak_bf16_tflops", ctypes.c_double),
-                ("peak_hbm_gbps", ctypes.c_double)]
+                ("peak_hbm_gbps", ctypes.c_double), ("tuned_ms", ctypes.c_double)]
 
 
 _lib = None
@@ -83,6 +83,9 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int,
                                     ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.kda_tune.restype = ctypes.c_int
+    lib.kda_tune.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P,
+                             ctypes.POINTER(QueryResult)]
     lib.kda_prologue.restype = ctypes.c_int
     lib.kda_prologue.argtypes = [ctypes.POINTER(PrologueProblem)] + [_P] * 17
     lib.kda_norm_gate.restype = ctypes.c_int
@@ -169,7 +172,7 @@ def workspace_bytes(p: Problem) -> int:
 def _fwd(entry: str, q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_host, chunk_size, scale, dv_tile, out,
          final_state, output_final_state, stream, algo=0, workspace=None):
     dev = q.device
-    p, n = _problem_from(q, v, cu_seqlens, chunk_size, scale, dv_tile, algo if entry == "chunk" else 0)
+    p, n = _problem_from(q, v, cu_seqlens, chunk_size, scale, dv_tile, algo if entry in ("chunk", "tune") else 0)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     _need(q, "q", q.dtype, (B, T, H, dk), dev)
@@ -196,6 +199,24 @@ def _fwd(entry: str, q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_hos
     lib = library()
     common = [ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
               None if host_cu is None else ctypes.c_void_p(host_cu.data_ptr()), _ptr(out), _ptr(final_state)]
+    if entry == "tune":
+        if workspace is None and p.algo != KDA_ALGO_FUSED:  # room for the largest two-pass candidate
+            need = 0
+            for c in ((p.chunk_size,) if p.chunk_size else (16, 32, 64)):
+                q2 = Problem(**{f: getattr(p, f) for f, _ in Problem._fields_})
+                q2.chunk_size, q2.algo, q2.dv_tile = c, KDA_ALGO_TWO_PASS, 32
+                r = QueryResult()
+                if lib.kda_query(ctypes.byref(q2), 0, ctypes.byref(r)) == KDA_OK:
+                    need = max(need, r.workspace_bytes)
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+        ws_ptr = None if workspace is None else ctypes.c_void_p(workspace.data_ptr())
+        ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        res = QueryResult()
+        st = lib.kda_tune(*common, ws_ptr, ws_len, _stream_handle(dev, stream), ctypes.byref(res))
+        _check(st)
+        d = {name: getattr(res, name) for name, _ in QueryResult._fields_}
+        d["arch"] = res.arch.decode()
+        return d, out, final_state
     if entry == "chunk":
         if workspace is None and p.algo != KDA_ALGO_FUSED:
             need = workspace_bytes(p)
@@ -228,6 +249,19 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     if gate is not None or norm_weight is not None:
         norm_gate(out, gate, norm_weight, eps=norm_eps, out=out, stream=stream)
     return out, fin
+
+
+def tune(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+         initial_state: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None, *,
+         cu_seqlens_host=None, chunk_size: int = 0, scale: float = 1.0, dv_tile: int = 0, algo="auto",
+         workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+         final_state: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Time every supported chunk_fwd configuration on these tensors (fields given here stay
+    fixed) and return the fastest as a query dict with 'tuned_ms'.  out / final_state are
+    overwritten; initial_state must not be final_state."""
+    cfg, _, _ = _fwd("tune", q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_host, chunk_size, scale,
+                     dv_tile, out, final_state, True, stream, algo=algo, workspace=workspace)
+    return cfg
 
 
 def recurrent_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,

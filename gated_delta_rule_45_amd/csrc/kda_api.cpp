@@ -287,6 +287,83 @@ kda_status_t kda_chunk_fwd(const kda_problem_t *problem, const void *q, const vo
     }
 }
 
+kda_status_t kda_tune(const kda_problem_t *problem, const void *q, const void *k, const void *v, const float *g,
+                      const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                      const int32_t *cu_seqlens_host, void *out, float *final_state, void *workspace,
+                      size_t workspace_bytes, void *stream, kda_query_result_t *best) {
+    try {
+        if (!best) return fail(KDA_ERR_INVALID_ARGUMENT, "best is NULL");
+        if (!problem) return fail(KDA_ERR_INVALID_ARGUMENT, "problem is NULL");
+        if (initial_state && (const void *)initial_state == (const void *)final_state)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "initial_state aliases final_state (candidates run repeatedly)");
+        {  // the problem as given must be valid (fields left at 0 are tuned)
+            Resolved r;
+            kda_status_t st = resolve(problem, cu_seqlens != nullptr, r, true);
+            if (st != KDA_OK) return st;
+            st = check_tensors(problem, r, q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_host, out,
+                               final_state);
+            if (st != KDA_OK) return st;
+        }
+        const hipStream_t s = static_cast<hipStream_t>(stream);
+        hipEvent_t e0 = nullptr, e1 = nullptr;
+        if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+            if (e0) (void)hipEventDestroy(e0);
+            return fail(KDA_ERR_HIP, "hipEventCreate failed");
+        }
+        const int chunks[3] = {16, 32, 64}, tiles[3] = {32, 64, 128}, algos[2] = {KDA_ALGO_FUSED, KDA_ALGO_TWO_PASS};
+        kda_problem_t winner{};
+        float best_ms = -1.f;
+        kda_status_t err = KDA_OK;
+        for (int ci = 0; ci < 3 && err == KDA_OK; ++ci) {
+            if (problem->chunk_size && chunks[ci] != problem->chunk_size) continue;
+            for (int ai = 0; ai < 2 && err == KDA_OK; ++ai) {
+                if (problem->algo != KDA_ALGO_AUTO && algos[ai] != problem->algo) continue;
+                for (int ti = 0; ti < 3 && err == KDA_OK; ++ti) {
+                    if (problem->dv_tile && tiles[ti] != problem->dv_tile) continue;
+                    kda_problem_t c = *problem;
+                    c.chunk_size = chunks[ci];
+                    c.algo = algos[ai];
+                    c.dv_tile = tiles[ti];
+                    Resolved r;
+                    if (resolve(&c, cu_seqlens != nullptr, r, true) != KDA_OK) continue;  // variant not built
+                    if (c.algo == KDA_ALGO_TWO_PASS &&
+                        (workspace == nullptr || workspace_bytes < r.ws_bytes || !aligned(workspace, 256)))
+                        continue;
+                    auto call = [&]() {
+                        return kda_chunk_fwd(&c, q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_host, out,
+                                             final_state, workspace, workspace_bytes, stream);
+                    };
+                    if ((err = call()) != KDA_OK) break;
+                    if (hipEventRecord(e0, s) != hipSuccess) { err = fail(KDA_ERR_HIP, "hipEventRecord failed"); break; }
+                    for (int rep = 0; rep < 3 && err == KDA_OK; ++rep) err = call();
+                    if (err != KDA_OK) break;
+                    float ms = 0.f;
+                    if (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+                        hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {
+                        err = fail(KDA_ERR_HIP, "timing the candidate failed");
+                        break;
+                    }
+                    ms /= 3.f;
+                    if (best_ms < 0.f || ms < best_ms) {
+                        best_ms = ms;
+                        winner = c;
+                    }
+                }
+            }
+        }
+        (void)hipEventDestroy(e0);
+        (void)hipEventDestroy(e1);
+        if (err != KDA_OK) return err;
+        if (best_ms < 0.f) return fail(KDA_ERR_UNSUPPORTED, "no candidate configuration runs this problem");
+        kda_status_t st = kda_query(&winner, KDA_QUERY_DEVICE, best);
+        if (st != KDA_OK) return st;
+        best->tuned_ms = best_ms;
+        return ok();
+    } catch (...) {
+        return fail(KDA_ERR_HIP, "unexpected exception in kda_tune");
+    }
+}
+
 kda_status_t kda_recurrent_fwd(const kda_problem_t *problem, const void *q, const void *k, const void *v,
                                const float *g, const float *beta, const float *initial_state,
                                const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, void *out,

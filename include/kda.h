@@ -214,6 +214,7 @@ typedef struct {
     char arch[64];             /* gcnArchName of the current device */
     double peak_bf16_tflops;   /* published dense bf16 matrix peak used for roofline fractions */
     double peak_hbm_gbps;      /* published HBM peak */
+    double tuned_ms;           /* kda_tune: measured time of one call with this configuration (0 otherwise) */
 } kda_query_result_t;
 
 #define KDA_QUERY_DEVICE 1u /* also fill the device fields (one HIP property query, no launch) */
@@ -226,6 +227,22 @@ typedef struct {
  * num_seqs = 0 to describe a plain batch of `batch` sequences.
  */
 kda_status_t kda_query(const kda_problem_t *problem, uint32_t flags, kda_query_result_t *result);
+
+/*
+ * kda_tune -- autotuning: runs kda_chunk_fwd on the caller's own tensors with every supported
+ * candidate configuration (chunk size 16 / 32 / 64, d_v tile, fused or two-pass algorithm;
+ * problem fields that are set are kept fixed), times each with HIP events on `stream`
+ * (one warm-up call, then three timed calls), synchronises, and reports the fastest one in
+ * *best as kda_query would for it, with tuned_ms set.  The outputs are overwritten by the
+ * candidate runs (the last run leaves the result of the last candidate); initial_state must
+ * not alias final_state.  Two-pass candidates need a workspace as large as kda_query reports
+ * for them; smaller ones are skipped.  Nothing is allocated.  Same arguments and errors as
+ * kda_chunk_fwd, plus KDA_ERR_UNSUPPORTED when no candidate runs.
+ */
+kda_status_t kda_tune(const kda_problem_t *problem, const void *q, const void *k, const void *v, const float *g,
+                      const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                      const int32_t *cu_seqlens_host, void *out, float *final_state, void *workspace,
+                      size_t workspace_bytes, void *stream, kda_query_result_t *best);
 
 /* Static description of a status code. */
 const char *kda_status_string(kda_status_t status);

@@ -228,3 +228,21 @@ def test_prologue_validation():
     assert call_prologue(prologue_problem(), a0=None) == kda.KDA_ERR_INVALID_ARGUMENT
     assert call_prologue(prologue_problem(), a6=ctypes.c_void_p(0x100004)) == kda.KDA_ERR_INVALID_ARGUMENT
     assert call_prologue(prologue_problem(seq_len=0)) == kda.KDA_OK  # no tokens, no state out: nothing to do
+
+
+def test_tune_validation():
+    lib = kda.library()
+    res = kda.QueryResult()
+    p = problem()
+    args = [fake(i) for i in range(5)]
+    # no result struct
+    assert lib.kda_tune(ctypes.byref(p), *args, None, None, None, fake(5), None, None, 0, None, None) == \
+        kda.KDA_ERR_INVALID_ARGUMENT
+    # initial state aliasing the final state
+    assert lib.kda_tune(ctypes.byref(p), *args, fake(6), None, None, fake(5), fake(6), None, 0, None,
+                        ctypes.byref(res)) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert b"alias" in lib.kda_last_error()
+    # invalid problem is reported before any launch
+    bad = problem(head_dim_k=96)
+    assert lib.kda_tune(ctypes.byref(bad), *args, None, None, None, fake(5), None, None, 0, None,
+                        ctypes.byref(res)) == kda.KDA_ERR_UNSUPPORTED

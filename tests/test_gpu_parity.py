@@ -273,3 +273,18 @@ def test_query_on_device():
     r = kda.query(4, 4096, 16, 128, 128, "bf16", device=True)
     say(f"  device: {r['arch']} CUs={r['compute_units']}")
     assert r["device_ok"] == 1 and r["arch"].startswith("gfx950")
+
+
+def test_tune_picks_a_configuration_that_matches_the_oracle():
+    inp = ki.make_inputs(2, 300, 4, 128, 128, "bf16", seed=31)
+    say("tune B=2 T=300 H=4 d=128 bf16")
+    d = on_dev(inp)
+    cfg = kda.tune(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"])
+    say(f"  chosen: chunk={cfg['chunk_size']} dv_tile={cfg['dv_tile']} algo={cfg['algo']} {cfg['tuned_ms']:.4f} ms")
+    assert cfg["supported"] == 1 and cfg["tuned_ms"] > 0 and cfg["chunk_size"] in (16, 32, 64)
+    algo = {kda.KDA_ALGO_FUSED: "fused", kda.KDA_ALGO_TWO_PASS: "two_pass"}[cfg["algo"]]
+    out, fin = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"],
+                             chunk_size=cfg["chunk_size"], dv_tile=cfg["dv_tile"], algo=algo)
+    o_ref, s_ref = run_oracle(inp)
+    compare("o", out, o_ref, "bf16")
+    compare("final_state", fin, s_ref, "bf16")
