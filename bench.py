@@ -23,6 +23,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -83,6 +85,32 @@ def time_launches(fn, n, stream):
     return start.elapsed_time(end) / n
 
 
+def time_each(fn, n, stream):
+    """Median and minimum duration (ms) of n calls, each bracketed by its own pair of HIP events
+    on the launch stream (the calls still run back to back)."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    fn()
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    ev[-1][1].synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    return t[len(t) // 2], t[0]
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp):
     import oracle
     import kda_inputs as ki
@@ -92,9 +120,19 @@ def cpu_baseline(inp):
     oracle.fwd(*a, inp.g.numpy(), inp.beta.numpy(), initial_state=inp.s0.numpy(), threads=threads)
     dt = time.perf_counter() - t0
     B, T = inp.q.shape[0], inp.q.shape[1]
-    return {"value": B * T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    # decode leg: 10 steps of the decode workload through the same oracle
+    dinp = ki.workload_inputs("decode")
+    sq = lambda x: x[:, 0].contiguous()
+    dq, dk, dv = (ki.to_numpy_io(sq(x)) for x in (dinp.q, dinp.k, dinp.v))
+    dg, db, st = sq(dinp.g).numpy(), sq(dinp.beta).numpy(), dinp.s0.numpy()
+    t1 = time.perf_counter()
+    for _ in range(10):
+        _, st = oracle.decode(dq, dk, dv, dg, db, st.astype(np.float32), threads=threads)
+    ddt = (time.perf_counter() - t1) / 10
+    return {"value": B * T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"the whole prefill batch (B={B}, T={T}, H={inp.q.shape[2]}), fp64 token recurrence, "
-                      f"{dt:.2f} s wall"}
+                      f"{dt:.2f} s wall; decode leg: 10 steps of the decode workload",
+            "decode_ms_per_step": round(ddt * 1e3, 2)}
 
 
 def main():
@@ -173,6 +211,8 @@ def main():
     t_pre = time_launches(prefill, args.steps, stream)
     t_dec = time_launches(decode, args.steps, stream)
     t_epi = time_launches(epilogue, args.steps, stream)
+    pre_med, pre_min = time_each(prefill, args.steps, stream)
+    dec_med, dec_min = time_each(decode, args.steps, stream)
     t_pro = time_launches(prologue, args.steps, stream)
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -229,19 +269,21 @@ def main():
                             "frac": round(dec_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic.get("decode_bytes"),
                             "kernel": "kda_decode_step", "launch_ms": round(t_dec, 4),
                             "bytes_per_launch": dec_bytes},
-        "prefill": {"ms": round(t_pre, 4), "tokens_per_s": round(pre_tps, 1), "gb_per_s": round(pre_gbps, 1),
+        "prefill": {"ms": round(t_pre, 4), "ms_median": round(pre_med, 4), "ms_min": round(pre_min, 4),
+                    "tokens_per_s": round(pre_tps, 1), "gb_per_s": round(pre_gbps, 1),
                     "hbm_frac": round(pre_gbps / PEAK_HBM_GBPS, 4), "tflops": round(pre_tflops, 2),
                     "mfma_frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4), "flops_per_launch": q["flops"]},
-        "decode": {"ms": round(t_dec, 4), "gb_per_s": round(dec_gbps, 1), "hbm_frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
+        "decode": {"ms": round(t_dec, 4), "ms_median": round(dec_med, 4), "ms_min": round(dec_min, 4),
+                   "gb_per_s": round(dec_gbps, 1), "hbm_frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
                    "bytes_per_launch": dec_bytes},
         "tuned": {"chunk": tuned["chunk_size"], "dv_tile": tuned["dv_tile"],
                   "algo": ["auto", "fused", "two_pass"][tuned["algo"]], "ms": round(tuned["tuned_ms"], 4)},
         "prologue": {"kernel": "kda_prologue", "conv_width": 4, "ms": round(t_pro, 4),
                      "gb_per_s": round(pro_gbps, 1), "hbm_frac": round(pro_gbps / PEAK_HBM_GBPS, 4),
-                     "bytes_per_launch": pro_bytes},
+                     "bytes_per_launch": pro_bytes, "traffic": traffic.get("prologue_bytes")},
         "epilogue": {"kernel": "kda_norm_gate", "rows": epi_rows, "d": w.dv, "ms": round(t_epi, 4),
                      "gb_per_s": round(epi_gbps, 1), "hbm_frac": round(epi_gbps / PEAK_HBM_GBPS, 4),
-                     "bytes_per_launch": epi_bytes},
+                     "bytes_per_launch": epi_bytes, "traffic": traffic.get("epilogue_bytes")},
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on the prefill batch ...")
