@@ -8,6 +8,8 @@ Two independent implementations live here:
 
 * ``fwd`` / ``decode``: the token-by-token recurrence in C (``kda_oracle.c``),
   threaded over (sequence, head) units; the definition of the operator.
+* ``bwd``: its gradients for a loss linear in the outputs and the final state, by the
+  chain rule through the same recurrence, token by token in reverse (``kda_oracle.c``).
 * ``chunkwise.py``: the chunkwise form (WY/UT transform, forward-substitution
   inverse, inter-chunk state passing) in numpy fp64, used to pin that the chunk
   algebra reaches the recurrence exactly.
@@ -58,6 +60,10 @@ def _load(path: str = LIB_PATH):
     P = ctypes.c_void_p
     f.argtypes = [ctypes.c_int64, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
                   P, P, P, P, P, P, ctypes.c_int, P, P, P, ctypes.c_int]
+    b = lib.kda_oracle_bwd
+    b.restype = ctypes.c_int
+    b.argtypes = [ctypes.c_int64, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                  P, P, P, P, P, P, P, P, ctypes.c_int, P, P, P, P, P, P, P, ctypes.c_int]
     _libs[path] = lib
     return lib
 
@@ -141,3 +147,59 @@ def decode(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray, beta: np.
     o, fin = fwd(q[:, None], k[:, None], v[:, None], g[:, None], beta[:, None], initial_state=state, scale=scale,
                  heads=heads, threads=threads, lib_path=lib_path)
     return o[:, 0], fin
+
+
+def _seq_layout(B, T, cu_seqlens):
+    if cu_seqlens is not None:
+        assert B == 1, "packed batches use B == 1"
+        cu = np.asarray(cu_seqlens, dtype=np.int64)
+        starts = np.ascontiguousarray(cu[:-1])
+        lens = np.ascontiguousarray(cu[1:] - cu[:-1])
+        assert cu[0] == 0 and cu[-1] == T and np.all(lens >= 0)
+    else:
+        starts = np.arange(B, dtype=np.int64) * T
+        lens = np.full(B, T, dtype=np.int64)
+    return starts, lens
+
+
+def bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray, beta: np.ndarray, d_out: np.ndarray, *,
+        initial_state: Optional[np.ndarray] = None, d_final_state: Optional[np.ndarray] = None,
+        cu_seqlens: Optional[np.ndarray] = None, scale: float = 1.0, heads: Optional[Sequence[int]] = None,
+        threads: Optional[int] = None, lib_path: str = LIB_PATH):
+    """Gradients of the token-by-token KDA, in fp64.
+
+    The loss is L = sum(d_out * o) + sum(d_final_state * final_state): ``d_out`` has v's
+    shape and dtype (float32, or uint16 bf16 bits), ``d_final_state`` is [N, H, dk, dv]
+    float32 or None (zero).  Other arguments as ``fwd``.
+
+    Returns a dict of float64 arrays over the selected heads: dq, dk, dg [B, T, nsel, dk];
+    dv [B, T, nsel, dv]; dbeta [B, T, nsel]; d_initial_state [N, nsel, dk, dv].
+    """
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    io = _io_kind(q, k, v, d_out)
+    q, k, v, d_out = (np.ascontiguousarray(x) for x in (q, k, v, d_out))
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    beta = np.ascontiguousarray(beta, dtype=np.float32)
+    assert k.shape == q.shape and v.shape[:3] == q.shape[:3] and g.shape == q.shape and d_out.shape == v.shape
+    assert beta.shape == (B, T, H)
+    starts, lens = _seq_layout(B, T, cu_seqlens)
+    N = len(starts)
+    sel = np.arange(H, dtype=np.int32) if heads is None else np.asarray(heads, dtype=np.int32)
+    assert sel.ndim == 1 and len(sel) > 0 and np.all((sel >= 0) & (sel < H))
+    s0 = None if initial_state is None else np.ascontiguousarray(initial_state, dtype=np.float32)
+    dsf = None if d_final_state is None else np.ascontiguousarray(d_final_state, dtype=np.float32)
+    for x in (s0, dsf):
+        assert x is None or x.shape == (N, H, dk, dv)
+    ns = len(sel)
+    out = {"dq": np.zeros((B, T, ns, dk)), "dk": np.zeros((B, T, ns, dk)), "dv": np.zeros((B, T, ns, dv)),
+           "dg": np.zeros((B, T, ns, dk)), "dbeta": np.zeros((B, T, ns)),
+           "d_initial_state": np.zeros((N, ns, dk, dv))}
+    lib = _load(lib_path)
+    rc = lib.kda_oracle_bwd(N, _ptr(starts), _ptr(lens), H, dk, dv, io, float(scale), _ptr(q), _ptr(k), _ptr(v),
+                            _ptr(g), _ptr(beta), _ptr(s0), _ptr(d_out), _ptr(dsf), ns, _ptr(sel),
+                            _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]),
+                            _ptr(out["d_initial_state"]), threads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_bwd failed with code {rc}")
+    return out
