@@ -119,3 +119,64 @@ def fwd_one(q, k, v, g, beta, S0: Optional[np.ndarray], chunk: int, scale: float
         sl = slice(c0, min(c0 + chunk, T))
         O[sl], S = chunk_step(q[sl], k[sl], v[sl], g[sl], beta[sl], S, scale, anchor, sub)
     return O, S
+
+
+def bwd_one(q, k, v, g, beta, S0: Optional[np.ndarray], d_out, d_final: Optional[np.ndarray], chunk: int,
+            scale: float = 1.0):
+    """Gradients of ``fwd_one`` for L = sum(d_out * O) + sum(d_final * S_T), chunk by chunk
+    (fp64; q, k, g, d... [T, d]).  Returns dict(dq, dk, dv, dg, dbeta, d_initial_state).
+
+    Reverse-mode through the chunk equations above.  With X = (I + A)^{-1} and per chunk
+    S (its initial state) and dS (the gradient of the state it hands on):
+        dD = scale P^T dO + Kb dS             dU = X^T dD        dY = beta * dU  (= dv)
+        dS <- Diag(exp(G_C)) dS + scale Qt^T dO - Kt^T dY        (gradient of S)
+    and, inside the chunk, with E[r, i, c] = exp(G_rc - G_ic):
+        dP = scale lower_incl(dO D^T)         dA = -strictly_lower(dU D^T)   dL = beta * dA
+        dq_r  = scale e^{G_r} (S dO_r) + sum_i dP_ri k_i E_ri
+        dk_r  = -beta_r e^{G_r} (S dU_r) + sum_i dL_ri k_i E_ri           (through Kt)
+              + sum_r' (dP_r'r q_r' + dL_r'r k_r') E_r'r                  (through Kh)
+              + e^{G_C - G_r} (dS D_r)                                    (through Kb)
+        dG    = q dq + k (dk through Kt) - k (dk through Kh) - k (dk through Kb),
+                plus sum_i k_i (dk_i through Kb) + e^{G_C} rowsum(dS .* S) at the last row
+        dg    = reverse cumulative sum of dG over the chunk
+        dbeta = rowsum(dU .* (V - Kt S)) + rowsum(dA .* strictly_lower(Kt Kh^T))
+    """
+    T, dk = q.shape
+    dv = v.shape[1]
+    S = np.zeros((dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    chunks = [slice(c0, min(c0 + chunk, T)) for c0 in range(0, T, chunk)]
+    saved = []
+    for sl in chunks:  # forward sweep: keep each chunk's operands and initial state
+        G = np.cumsum(g[sl], axis=0)
+        Kt, Qt, Kh, Kb = k[sl] * np.exp(G), q[sl] * np.exp(G), k[sl] * np.exp(-G), k[sl] * np.exp(G[-1] - G)
+        Lm = np.tril(Kt @ Kh.T, -1)
+        X = forward_substitution_inverse(np.eye(sl.stop - sl.start) + beta[sl][:, None] * Lm)
+        Y = v[sl] - Kt @ S
+        D = X @ (beta[sl][:, None] * Y)
+        saved.append(dict(G=G, Kt=Kt, Qt=Qt, Kh=Kh, Kb=Kb, L=Lm, X=X, P=np.tril(Qt @ Kh.T), Y=Y, D=D, S=S.copy()))
+        S = np.exp(G[-1])[:, None] * S + Kb.T @ D
+    out = {"dq": np.zeros((T, dk)), "dk": np.zeros((T, dk)), "dv": np.zeros((T, dv)), "dg": np.zeros((T, dk)),
+           "dbeta": np.zeros(T)}
+    dS = np.zeros((dk, dv)) if d_final is None else np.array(d_final, dtype=np.float64)
+    for sl, o in reversed(list(zip(chunks, saved))):
+        b, do, G = beta[sl], d_out[sl], o["G"]
+        dD = scale * o["P"].T @ do + o["Kb"] @ dS
+        dU = o["X"].T @ dD
+        dY = b[:, None] * dU
+        E = np.exp(G[:, None, :] - G[None, :, :])
+        dP = scale * np.tril(do @ o["D"].T)
+        dA = -np.tril(dU @ o["D"].T, -1)
+        dL = b[:, None] * dA
+        Sc = o["S"]
+        dq = scale * np.exp(G) * (do @ Sc.T) + np.einsum("ri,ic,ric->rc", dP, k[sl], E)
+        dk_t = -b[:, None] * np.exp(G) * (dU @ Sc.T) + np.einsum("ri,ic,ric->rc", dL, k[sl], E)
+        dk_h = np.einsum("ri,rc,ric->ic", dP, q[sl], E) + np.einsum("ri,rc,ric->ic", dL, k[sl], E)
+        dk_b = np.exp(G[-1] - G) * (o["D"] @ dS.T)
+        dG = q[sl] * dq + k[sl] * (dk_t - dk_h - dk_b)
+        dG[-1] += np.sum(k[sl] * dk_b, axis=0) + np.exp(G[-1]) * np.sum(dS * Sc, axis=1)
+        out["dq"][sl], out["dk"][sl], out["dv"][sl] = dq, dk_t + dk_h + dk_b, dY
+        out["dg"][sl] = np.cumsum(dG[::-1], axis=0)[::-1]
+        out["dbeta"][sl] = np.sum(dU * o["Y"], axis=1) + np.sum(dA * o["L"], axis=1)
+        dS = np.exp(G[-1])[:, None] * dS + scale * o["Qt"].T @ do - o["Kt"].T @ dY
+    out["d_initial_state"] = dS
+    return out

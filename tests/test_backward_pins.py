@@ -273,3 +273,19 @@ def test_planted_backward_mistakes_are_caught(tmp_path, mutant):
 
 def test_unmutated_backward_passes_the_same_checks():
     assert _bwd_pin_failures(oracle.LIB_PATH) == []
+
+
+@pytest.mark.parametrize("chunk", [1, 3, 16, 64])
+def test_chunkwise_backward_equals_recurrent_backward(chunk):
+    """The chunkwise reverse pass (oracle/chunkwise.py, written from the chunk equations)
+    reaches the token-serial gradients, including a partial last chunk."""
+    from oracle import chunkwise
+    rng = np.random.default_rng(40 + chunk)
+    c = rand_case(rng, 1, 70, 1, 8, 6)
+    ref = grads(c, scale=0.9)
+    f = lambda x: x[0, :, 0].astype(np.float64)
+    got = chunkwise.bwd_one(f(c["q"]), f(c["k"]), f(c["v"]), f(c["g"]), f(c["beta"]), c["S0"][0, 0], f(c["do"]),
+                            c["dsf"][0, 0], chunk, scale=0.9)
+    for key in ("dq", "dk", "dv", "dg", "dbeta"):
+        np.testing.assert_allclose(got[key], ref[key][0, :, 0], rtol=0, atol=1e-10)
+    np.testing.assert_allclose(got["d_initial_state"], ref["d_initial_state"][0, 0], rtol=0, atol=1e-10)
