@@ -22,7 +22,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["chunk_fwd", "recurrent_fwd", "decode_step", "prologue", "norm_gate", "query", "tune", "KdaError",
+__all__ = ["chunk_fwd", "chunk_bwd", "recurrent_fwd", "decode_step", "prologue", "norm_gate", "query", "tune", "KdaError",
            "LIB_PATH", "library"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
@@ -90,6 +90,10 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_prologue.argtypes = [ctypes.POINTER(PrologueProblem)] + [_P] * 17
     lib.kda_norm_gate.restype = ctypes.c_int
     lib.kda_norm_gate.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int, ctypes.c_float, _P, _P, _P, _P, _P]
+    lib.kda_chunk_bwd.restype = ctypes.c_int
+    lib.kda_chunk_bwd.argtypes = [ctypes.POINTER(Problem)] + [_P] * 17 + [ctypes.c_size_t, _P]
+    lib.kda_chunk_bwd_workspace.restype = ctypes.c_int
+    lib.kda_chunk_bwd_workspace.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(ctypes.c_size_t)]
     lib.kda_query.restype = ctypes.c_int
     lib.kda_query.argtypes = [ctypes.POINTER(Problem), ctypes.c_uint32, ctypes.POINTER(QueryResult)]
     lib.kda_status_string.restype = ctypes.c_char_p
@@ -249,6 +253,59 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     if gate is not None or norm_weight is not None:
         norm_gate(out, gate, norm_weight, eps=norm_eps, out=out, stream=stream)
     return out, fin
+
+
+def bwd_workspace_bytes(p: Problem) -> int:
+    """Workspace kda_chunk_bwd needs for problem p."""
+    n = ctypes.c_size_t(0)
+    _check(library().kda_chunk_bwd_workspace(ctypes.byref(p), ctypes.byref(n)))
+    return int(n.value)
+
+
+def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+              d_out: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+              d_final_state: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None, *,
+              cu_seqlens_host=None, chunk_size: int = 0, scale: float = 1.0, need_d_initial_state: bool = True,
+              workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Gradients of chunk_fwd for L = sum(d_out * out) + sum(d_final_state * final_state).
+    Arguments as chunk_fwd; d_out has out's shape and dtype, d_final_state is [N, H, d_k, d_v]
+    fp32 or None.  Returns dict(dq, dk, dv (io dtype), dg, dbeta, d_initial_state (fp32 or None))."""
+    dev = q.device
+    p, n = _problem_from(q, v, cu_seqlens, chunk_size, scale, 0, 0)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    _need(q, "q", q.dtype, (B, T, H, dk), dev)
+    _need(k, "k", q.dtype, (B, T, H, dk), dev)
+    _need(v, "v", q.dtype, (B, T, H, dv), dev)
+    _need(g, "g", torch.float32, (B, T, H, dk), dev)
+    _need(beta, "beta", torch.float32, (B, T, H), dev)
+    _need(d_out, "d_out", q.dtype, (B, T, H, dv), dev)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (n, H, dk, dv), dev)
+    if d_final_state is not None:
+        _need(d_final_state, "d_final_state", torch.float32, (n, H, dk, dv), dev)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, (n + 1,), dev)
+    host_cu = None
+    if cu_seqlens_host is not None:
+        host_cu = torch.as_tensor(cu_seqlens_host, dtype=torch.int32).contiguous().cpu()
+        if host_cu.numel() != n + 1:
+            raise ValueError("cu_seqlens_host has the wrong length")
+    out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+           "dg": torch.empty((B, T, H, dk), dtype=torch.float32, device=dev),
+           "dbeta": torch.empty((B, T, H), dtype=torch.float32, device=dev),
+           "d_initial_state": torch.empty((n, H, dk, dv), dtype=torch.float32, device=dev)
+           if need_d_initial_state else None}
+    if workspace is None:
+        workspace = torch.empty(bwd_workspace_bytes(p), dtype=torch.uint8, device=dev)
+    lib = library()
+    st = lib.kda_chunk_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                           _ptr(cu_seqlens), None if host_cu is None else ctypes.c_void_p(host_cu.data_ptr()),
+                           _ptr(d_out), _ptr(d_final_state), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                           _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["d_initial_state"]),
+                           ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream_handle(dev, stream))
+    _check(st)
+    return out
 
 
 def tune(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,

@@ -14,7 +14,7 @@ LIB = os.path.join(HERE, "libkda.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
 SOURCES = ["kda_api.cpp", "kda_recurrent.hip", "kda_chunk_bf16.hip", "kda_chunk_f32.hip", "kda_split_bf16.hip",
-           "kda_split_f32.hip", "kda_epilogue.hip", "kda_prologue.hip"]
+           "kda_split_f32.hip", "kda_epilogue.hip", "kda_prologue.hip", "kda_bwd_bf16.hip", "kda_bwd_f32.hip"]
 ARCH = "gfx950"
 # Packed fp32 VALU ops are disabled for every device pass.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

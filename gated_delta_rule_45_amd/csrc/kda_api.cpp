@@ -226,6 +226,80 @@ kda::FwdParams make_params(const kda_problem_t *p, const Resolved &r, const void
     return fp;
 }
 
+// ----------------------------------------------------------------- backward --
+struct BwdResolved {
+    Resolved r;
+    int chunk = 64;
+    int fwd_dv_tile = 32;  // d_v tile of the forward pass that keeps the chunk states
+    int64_t slots = 0;     // chunk slots (upper bound for a packed batch)
+    size_t off_hs = 0, off_dhs = 0, off_dch = 0, off_duch = 0, ws_bytes = 0;
+};
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+bool bwd_variant_supported(kda_dtype_t io, int dk, int dv, int chunk) {
+    return io == KDA_BF16 ? kda::bwd_supported_bf16(dk, dv, chunk) : kda::bwd_supported_f32(dk, dv, chunk);
+}
+
+kda_status_t resolve_bwd(const kda_problem_t *p, bool varlen, BwdResolved &b) {
+    kda_status_t st = resolve(p, varlen, b.r, false);
+    if (st != KDA_OK) return st;
+    if (p->chunk_size != 0 && p->chunk_size != 16 && p->chunk_size != 32 && p->chunk_size != 64)
+        return fail(KDA_ERR_UNSUPPORTED, "chunk_size %d: supported are 16, 32, 64 (0 = default)", p->chunk_size);
+    const int dk = p->head_dim_k, dv = p->head_dim_v;
+    if (p->chunk_size) {
+        b.chunk = p->chunk_size;
+    } else {  // largest chunk with a compiled variant
+        b.chunk = 0;
+        for (int c : {64, 32, 16})
+            if (bwd_variant_supported(p->io_dtype, dk, dv, c) &&
+                kda::chunk_variant_lds_bytes(p->io_dtype, dk, 32, c) > 0) {
+                b.chunk = c;
+                break;
+            }
+        if (b.chunk == 0) return fail(KDA_ERR_UNSUPPORTED, "backward: no compiled variant for d_k=%d d_v=%d", dk, dv);
+    }
+    if (!bwd_variant_supported(p->io_dtype, dk, dv, b.chunk))
+        return fail(KDA_ERR_UNSUPPORTED, "backward: no compiled variant for io=%s d_k=%d d_v=%d chunk=%d (LDS)",
+                    p->io_dtype == KDA_BF16 ? "bf16" : "fp32", dk, dv, b.chunk);
+    b.fwd_dv_tile = 0;
+    for (int t : {default_dv_tile((int64_t)b.r.num_seqs * p->num_heads, dv), 32})
+        if (t <= dv && kda::chunk_variant_lds_bytes(p->io_dtype, dk, t, b.chunk) > 0) {
+            b.fwd_dv_tile = t;
+            break;
+        }
+    if (b.fwd_dv_tile == 0)
+        return fail(KDA_ERR_UNSUPPORTED, "backward: no forward variant keeps the states for d_k=%d chunk=%d", dk,
+                    b.chunk);
+    const int64_t per = ((int64_t)p->seq_len + b.chunk - 1) / b.chunk;
+    b.slots = varlen ? per + b.r.num_seqs : (int64_t)b.r.num_seqs * per;
+    if (b.slots * p->num_heads > 0x7fffffffLL) return fail(KDA_ERR_UNSUPPORTED, "too many chunks");
+    const size_t s_io = p->io_dtype == KDA_BF16 ? 2 : 4;
+    const size_t states = align256((size_t)b.slots * p->num_heads * dk * dv * 4);
+    const size_t tiles = align256((size_t)b.slots * p->num_heads * b.chunk * dv * s_io);
+    b.off_hs = kda::split_plan_bytes(b.r.num_seqs);
+    b.off_dhs = b.off_hs + states;
+    b.off_dch = b.off_dhs + states;
+    b.off_duch = b.off_dch + tiles;
+    b.ws_bytes = b.off_duch + tiles;
+    return KDA_OK;
+}
+
+kda_status_t check_bwd_tensors(const BwdResolved &b, const void *const in[], const char *const in_names[], int n_in,
+                               const void *const outs[], const char *const out_names[], int n_out) {
+    for (int i = 0; i < n_out; ++i) {
+        if (!outs[i]) continue;
+        for (int j = 0; j < n_in; ++j)
+            if (outs[i] == in[j])
+                return fail(KDA_ERR_INVALID_ARGUMENT, "%s aliases input %s", out_names[i], in_names[j]);
+        for (int j = 0; j < i; ++j)
+            if (outs[i] == outs[j])
+                return fail(KDA_ERR_INVALID_ARGUMENT, "%s aliases %s", out_names[i], out_names[j]);
+    }
+    (void)b;
+    return KDA_OK;
+}
+
 }  // namespace
 
 namespace kda {
@@ -284,6 +358,97 @@ kda_status_t kda_chunk_fwd(const kda_problem_t *problem, const void *q, const vo
                           "kda_chunk_fwd (fused) launch");
     } catch (...) {
         return fail(KDA_ERR_HIP, "unexpected exception in kda_chunk_fwd");
+    }
+}
+
+kda_status_t kda_chunk_bwd_workspace(const kda_problem_t *problem, size_t *bytes) {
+    try {
+        if (!bytes) return fail(KDA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+        *bytes = 0;
+        BwdResolved b;
+        kda_status_t st = resolve_bwd(problem, problem && problem->num_seqs > 0, b);
+        if (st != KDA_OK) return st;
+        *bytes = b.ws_bytes;
+        return ok();
+    } catch (...) {
+        return fail(KDA_ERR_HIP, "unexpected exception in kda_chunk_bwd_workspace");
+    }
+}
+
+kda_status_t kda_chunk_bwd(const kda_problem_t *problem, const void *q, const void *k, const void *v,
+                           const float *g, const float *beta, const float *initial_state,
+                           const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, const void *d_out,
+                           const float *d_final_state, void *dq, void *dk, void *dv, float *dg, float *dbeta,
+                           float *d_initial_state, void *workspace, size_t workspace_bytes, void *stream) {
+    try {
+        BwdResolved b;
+        const bool varlen = cu_seqlens != nullptr;
+        kda_status_t st = resolve_bwd(problem, varlen, b);
+        if (st != KDA_OK) return st;
+        const Resolved &r = b.r;
+        if (r.tokens > 0) {
+            const void *req[] = {d_out, dq, dk, dv, dg, dbeta};
+            const char *names[] = {"d_out", "dq", "dk", "dv", "dg", "dbeta"};
+            for (int i = 0; i < 6; ++i)
+                if (!req[i]) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
+            const void *al16[] = {d_out, dq, dk, dv, dg};
+            const char *n16[] = {"d_out", "dq", "dk", "dv", "dg"};
+            for (int i = 0; i < 5; ++i)
+                if (!aligned(al16[i], 16)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", n16[i]);
+            if (!aligned(dbeta, 4)) return fail(KDA_ERR_INVALID_ARGUMENT, "dbeta is not 4-byte aligned");
+        }
+        // the forward-side checks (inputs, alignment, cu_seqlens), dq in the place of out
+        st = check_tensors(problem, r, q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_host, dq, nullptr);
+        if (st != KDA_OK) return st;
+        if (d_final_state && !aligned(d_final_state, 16))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "d_final_state is not 16-byte aligned");
+        if (d_initial_state && !aligned(d_initial_state, 16))
+            return fail(KDA_ERR_INVALID_ARGUMENT, "d_initial_state is not 16-byte aligned");
+        const void *ins[] = {q, k, v, g, beta, initial_state, d_out, d_final_state, cu_seqlens};
+        const char *in_names[] = {"q", "k", "v", "g", "beta", "initial_state", "d_out", "d_final_state", "cu_seqlens"};
+        const void *outs[] = {dq, dk, dv, dg, dbeta, d_initial_state};
+        const char *out_names[] = {"dq", "dk", "dv", "dg", "dbeta", "d_initial_state"};
+        st = check_bwd_tensors(b, ins, in_names, 9, outs, out_names, 6);
+        if (st != KDA_OK) return st;
+        if (!workspace || workspace_bytes < b.ws_bytes || !aligned(workspace, 256))
+            return fail(KDA_ERR_WORKSPACE, "kda_chunk_bwd needs a 256-byte aligned workspace of %zu bytes (got %zu at %p)",
+                        b.ws_bytes, workspace_bytes, workspace);
+        if (r.num_seqs == 0) return ok();
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        char *ws = static_cast<char *>(workspace);
+        int32_t *chunk_off = reinterpret_cast<int32_t *>(ws);
+        if (varlen) {
+            st = hip_status(kda::launch_chunk_plan(cu_seqlens, r.num_seqs, b.chunk, chunk_off, s),
+                            "kda_chunk_bwd plan launch");
+            if (st != KDA_OK) return st;
+        }
+        kda::FwdParams fp = make_params(problem, r, q, k, v, g, beta, initial_state, cu_seqlens, nullptr, nullptr);
+        fp.hs = reinterpret_cast<float *>(ws + b.off_hs);
+        fp.dch = ws + b.off_dch;
+        fp.chunk_off = varlen ? chunk_off : nullptr;
+        st = hip_status(kda::launch_chunk_fwd(problem->io_dtype, fp, kda::ChunkConfig{b.chunk, b.fwd_dv_tile}, s),
+                        "kda_chunk_bwd forward launch");
+        if (st != KDA_OK) return st;
+        kda::BwdParams bp;
+        bp.f = fp;
+        bp.d_out = d_out;
+        bp.d_sf = d_final_state;
+        bp.dq = dq;
+        bp.dk = dk;
+        bp.dv = dv;
+        bp.dg = dg;
+        bp.dbeta = dbeta;
+        bp.ds0 = d_initial_state;
+        bp.hs = fp.hs;
+        bp.dhs = reinterpret_cast<float *>(ws + b.off_dhs);
+        bp.dch = fp.dch;
+        bp.duch = ws + b.off_duch;
+        bp.slots = b.slots;
+        const hipError_t e = problem->io_dtype == KDA_BF16 ? kda::launch_bwd_bf16(bp, b.chunk, s)
+                                                           : kda::launch_bwd_f32(bp, b.chunk, s);
+        return hip_status(e, "kda_chunk_bwd launch");
+    } catch (...) {
+        return fail(KDA_ERR_HIP, "unexpected exception in kda_chunk_bwd");
     }
 }
 

@@ -1,0 +1,19 @@
+// bf16-io backward variants (bf16 matrix-core operands, fp32 accumulation and states),
+// and the chunk-offset plan launch used by the backward.
+#include "kda_bwd_impl.h"
+#include "kda_plan.h"
+
+namespace kda {
+
+bool bwd_supported_bf16(int dk, int dv, int chunk) { return bwd_supported<uint16_t>(dk, dv, chunk); }
+hipError_t launch_bwd_bf16(const BwdParams &bp, int chunk, hipStream_t stream) {
+    return launch_bwd<uint16_t>(bp, chunk, stream);
+}
+
+hipError_t launch_chunk_plan(const int32_t *cu, int32_t num_seqs, int32_t chunk, int32_t *chunk_off,
+                             hipStream_t stream) {
+    hipLaunchKernelGGL(kda_plan_kernel, dim3(1), dim3(256), 0, stream, cu, num_seqs, chunk, chunk_off);
+    return hipGetLastError();
+}
+
+}  // namespace kda

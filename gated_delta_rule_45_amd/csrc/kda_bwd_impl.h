@@ -1,0 +1,992 @@
+// Chunkwise KDA backward for gfx950.
+//
+// Gradients of L = <dO, O> + <dS_final, S_T> with respect to q, k, v, g, beta and the
+// initial state, by reverse-mode differentiation of the chunk equations (Kimi Linear
+// summary page, "Chunkwise parallel algorithm": chunk-level state passing, the WY/UT
+// transform with one triangular inverse per chunk, and the inter/intra-chunk output
+// split; the UT form exists for training throughput).  Per chunk, with its initial
+// state S, D = X Diag(beta)(V - K~ S), X = (I + A)^{-1}, and dS the gradient of the
+// state the chunk hands on:
+//
+//   dD = scale P^T dO + K- dS        dU = X^T dD        dY = beta * dU   (= dv)
+//   dS <- Diag(e^{G_C}) dS + scale Q~^T dO - K~^T dY                      (reverse scan)
+//
+//   dP = scale lower_incl(dO D^T)    dA = -strictly_lower(dU D^T)    dL = beta * dA
+//   dq_r = scale e^{G_r} (S dO_r) + sum_i dP_ri k_i e^{G_r - G_i}
+//   dk_r = beta_r [ sum_i dA_ri k_i e^{G_r - G_i} - e^{G_r} (S dU_r) ]           (via K~)
+//        + sum_r' (dP_r'r q_r' + dL_r'r k_r') e^{G_r' - G_r}                      (via K^)
+//        + e^{G_C - G_r} (dS D_r)                                                 (via K-)
+//   dG   = q dq + k (dk via K~) - k (dk via K^) - k (dk via K-), and at the chunk's last
+//          token also sum_i k_i (dk_i via K-) + e^{G_C} rowsum(dS .* S);  dg = reverse
+//          cumulative sum of dG over the chunk
+//   dbeta_r = sum_j dU_rj V_rj - sum_c e^{G_rc} k_rc (S dU_r)_c + sum_c k_rc W_rc,
+//          W_rc = sum_i dA_ri k_ic e^{G_rc - G_ic}
+//
+// Three launches:
+//   1. the fused forward (kda_chunk_impl.h) keeps each chunk's initial state S and D;
+//   2. kda_bwd_scan_kernel: one workgroup per (sequence, head, d_v tile), chunks in
+//      reverse order; rebuilds the chunk's operands, keeps dS in registers, writes dv,
+//      dU and the chunk-end dS of every chunk, and d(initial state);
+//   3. kda_bwd_grad_kernel: one workgroup per (chunk, head), all chunks in parallel;
+//      each wave owns 16 key channels for every token of the chunk, so the gate
+//      factors stay in registers and no cross-wave reduction over channels is needed
+//      except for dbeta (a sum over channels).
+//
+// The exponentials e^{G_r - G_i} inside the C x C products are split at 16-token
+// sub-chunk boundaries b_R (as in the forward): e^{G_r - G_i} = e^{G_r - b_R} *
+// e^{b_R - b_{I+1}} * e^{b_{I+1} - G_i} for r in sub-chunk R >= I, i in I; the outer two
+// factors are <= 1 and the middle one is a per-channel constant of the block pair.
+#pragma once
+
+#include <type_traits>
+
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+
+__device__ __forceinline__ int64_t bwd_slot0(const FwdParams &p, int n, int C) {
+    return p.cu ? (int64_t)p.chunk_off[n] : (int64_t)n * ((p.T + C - 1) / C);
+}
+
+// ======================================================================= scan ====
+template <typename IO, int DK, int DVT, int C>
+struct BwdScanLayout {
+    static constexpr bool BF = IoTraits<IO>::kBf16;
+    using OT = typename std::conditional<BF, uint16_t, float>::type;
+    static constexpr int NW = 4;
+    static constexpr int NSUB = C / 16;
+    static constexpr int KT = DK / 16;
+    static constexpr int NSL = DVT / 16;
+    static constexpr int SPW = NSL > NW ? NSL / NW : 1;
+    static constexpr int PADO = 16 / (int)sizeof(OT);
+    static constexpr int LDO = DK + PADO;  // [C][DK] row operands
+    static constexpr int LDT = C + PADO;   // [DK][C] transposed operands
+    static constexpr int LDM = C + PADO;   // [C][C] transposed A and P
+    static constexpr int LDD = 16 + 4;     // fp32 diagonal inverses [16][16]
+    static constexpr int LDV = DVT + PADO; // [C][DVT] staged dO
+    static constexpr int NSHIFT = NSUB >= 3 ? (NSUB - 1) * (NSUB - 2) / 2 : 0;
+    static_assert(C % 16 == 0 && NSUB >= 1 && NSUB <= NW, "chunk must be 16, 32 or 64");
+    static_assert(DK % 32 == 0 && DVT % 16 == 0, "head dims");
+    static_assert(NSL <= NW || NSL % NW == 0, "d_v tile");
+
+    static constexpr int V_PIECES = C * DVT * (int)sizeof(IO) / 16;
+    static constexpr int V_PER_THREAD = (V_PIECES + kChunkThreads - 1) / kChunkThreads;
+    static constexpr int V_ELEMS = 16 / (int)sizeof(IO);
+
+    static constexpr size_t kOp = (size_t)C * LDO * sizeof(OT);
+    static constexpr size_t kOpT = (size_t)DK * LDT * sizeof(OT);
+    static constexpr size_t oKb = 0;
+    static constexpr size_t oKs = oKb + kOp;
+    static constexpr size_t oKbar = oKs + (size_t)NSHIFT * 16 * LDO * sizeof(OT);
+    static constexpr size_t oQtT = oKbar + kOp;
+    static constexpr size_t oKtT = oQtT + kOpT;
+    static constexpr size_t oPT = oKtT + kOpT;
+    static constexpr size_t oAT = oPT + (size_t)C * LDM * sizeof(OT);
+    static constexpr size_t oXT = oAT + (size_t)C * LDM * sizeof(OT);
+    static constexpr size_t oO = oXT + (size_t)NSUB * 16 * LDD * 4;
+    static constexpr size_t oTot = oO + (size_t)C * LDV * sizeof(OT);
+    static constexpr size_t oEB = oTot + (size_t)NSUB * DK * 4;
+    static constexpr size_t oED = oEB + (size_t)NSUB * DK * 4;
+    static constexpr size_t oEC = oED + (size_t)NSUB * DK * 4;
+    static constexpr size_t oSH = oEC + (size_t)NSUB * DK * 4;
+    static constexpr size_t oGam = oSH + (size_t)(NSHIFT > 0 ? NSHIFT : 1) * DK * 4;
+    static constexpr size_t oBeta = oGam + (size_t)DK * 4;
+    static constexpr size_t kBytes = oBeta + (size_t)C * 4;
+    static constexpr bool kFits = kBytes <= 160 * 1024;
+
+    __host__ __device__ static constexpr int shift_slot(int R, int I) { return (R - 2) * (R - 1) / 2 + I; }
+};
+
+// Raw inputs of one chunk: the key side (q, k, g) of sub-chunk R = wave, a dO tile, beta.
+template <typename IO, int DK, int DVT, int C>
+struct BwdRaw {
+    using L = BwdScanLayout<IO, DK, DVT, C>;
+    using KQ = typename std::conditional<L::BF, uint2, float4>::type;
+    float4 g[L::KT];
+    KQ k[L::KT], q[L::KT];
+    uint4 o[L::V_PER_THREAD];
+    float beta;
+};
+
+template <typename IO, int DK, int DVT, int C>
+__device__ __forceinline__ void bwd_load_chunk(BwdRaw<IO, DK, DVT, C> &raw, const BwdParams &bp, int64_t tok0,
+                                               int clen, int h, int col0, int tid) {
+    using L = BwdScanLayout<IO, DK, DVT, C>;
+    using KQ = typename BwdRaw<IO, DK, DVT, C>::KQ;
+    const FwdParams &p = bp.f;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l16 = lane & 15, q4 = lane >> 4;
+    const int H = p.H;
+    if (wave < L::NSUB) {
+        const int r = min(16 * wave + l16, clen - 1);
+        const int64_t row = ((tok0 + r) * H + h) * (int64_t)DK + 4 * q4;
+#pragma unroll
+        for (int ct = 0; ct < L::KT; ++ct) {
+            raw.g[ct] = *reinterpret_cast<const float4 *>(p.g + row + 16 * ct);
+            raw.k[ct] = *reinterpret_cast<const KQ *>(static_cast<const IO *>(p.k) + row + 16 * ct);
+            raw.q[ct] = *reinterpret_cast<const KQ *>(static_cast<const IO *>(p.q) + row + 16 * ct);
+        }
+    }
+    constexpr int PPR = DVT / L::V_ELEMS;
+#pragma unroll
+    for (int i = 0; i < L::V_PER_THREAD; ++i) {
+        const int piece = tid + kChunkThreads * i;
+        if (L::V_PIECES % kChunkThreads == 0 || piece < L::V_PIECES) {
+            const int r = min(piece / PPR, clen - 1);
+            const int cc = (piece % PPR) * L::V_ELEMS;
+            raw.o[i] = *reinterpret_cast<const uint4 *>(static_cast<const IO *>(bp.d_out) +
+                                                        ((tok0 + r) * H + h) * (int64_t)p.dv + col0 + cc);
+        }
+    }
+    if (tid < C) raw.beta = p.beta[(tok0 + min(tid, clen - 1)) * H + h];
+}
+
+template <typename IO, int DK, int DVT, int C>
+__global__ void __launch_bounds__(kChunkThreads) kda_bwd_scan_kernel(BwdParams bp) {
+    using L = BwdScanLayout<IO, DK, DVT, C>;
+    using OT = typename L::OT;
+    constexpr bool BF = L::BF;
+    constexpr int NSUB = L::NSUB, KT = L::KT, NSL = L::NSL, SPW = L::SPW;
+    constexpr int LDO = L::LDO, LDT = L::LDT, LDM = L::LDM, LDD = L::LDD, LDV = L::LDV;
+    using Tr = IoTraits<IO>;
+    const FwdParams &p = bp.f;
+
+    __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
+    OT *sKb = reinterpret_cast<OT *>(smem + L::oKb);
+    OT *sKs = reinterpret_cast<OT *>(smem + L::oKs);
+    OT *sKbar = reinterpret_cast<OT *>(smem + L::oKbar);
+    OT *sQtT = reinterpret_cast<OT *>(smem + L::oQtT);
+    OT *sKtT = reinterpret_cast<OT *>(smem + L::oKtT);
+    OT *sPT = reinterpret_cast<OT *>(smem + L::oPT);
+    OT *sAT = reinterpret_cast<OT *>(smem + L::oAT);
+    float *sXT = reinterpret_cast<float *>(smem + L::oXT);
+    OT *sO = reinterpret_cast<OT *>(smem + L::oO);
+    float *sTot = reinterpret_cast<float *>(smem + L::oTot);
+    float *sEB = reinterpret_cast<float *>(smem + L::oEB);
+    float *sED = reinterpret_cast<float *>(smem + L::oED);
+    float *sEC = reinterpret_cast<float *>(smem + L::oEC);
+    float *sSH = reinterpret_cast<float *>(smem + L::oSH);
+    float *sGam = reinterpret_cast<float *>(smem + L::oGam);
+    float *sBeta = reinterpret_cast<float *>(smem + L::oBeta);
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int l16 = lane & 15, q4 = lane >> 4;
+    const int H = p.H, DV = p.dv;
+
+    const int ntile = DV / DVT;
+    const int64_t nblocks = (int64_t)p.num_seqs * H * ntile;
+    const int64_t item = xcd_grouped_block(blockIdx.x, nblocks);
+    const int tile = (int)(item % ntile);
+    const int64_t nh = item / ntile;
+    const int h = (int)(nh % H);
+    const int n = (int)(nh / H);
+    int64_t start;
+    int len;
+    if (p.cu) {
+        start = p.cu[n];
+        len = p.cu[n + 1] - p.cu[n];
+    } else {
+        start = (int64_t)n * p.T;
+        len = p.T;
+    }
+    const int col0 = tile * DVT;
+    const int64_t slot0 = bwd_slot0(p, n, C);
+    const int nchunks = (len + C - 1) / C;
+
+    // ---- dS slices owned by this wave (accumulator layout), from the final-state gradient
+    f32x4 dS[SPW][KT];
+    const int64_t state_base = ((int64_t)n * H + h) * DK * DV;
+#pragma unroll
+    for (int s = 0; s < SPW; ++s) {
+        const int sl = wave + L::NW * s;
+        const int col = col0 + 16 * sl + l16;
+#pragma unroll
+        for (int ct = 0; ct < KT; ++ct)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * ct + 4 * q4 + j;
+                dS[s][ct][j] = (bp.d_sf && sl < NSL) ? bp.d_sf[state_base + (int64_t)row * DV + col] : 0.f;
+            }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+
+    BwdRaw<IO, DK, DVT, C> raw;
+    if (nchunks > 0) {
+        const int c0 = (nchunks - 1) * C;
+        bwd_load_chunk<IO, DK, DVT, C>(raw, bp, start + c0, min(C, len - c0), h, col0, tid);
+    }
+
+    for (int ci = nchunks - 1; ci >= 0; --ci) {
+        const int c0 = ci * C;
+        const int clen = min(C, len - c0);
+        const int64_t tok0 = start + c0;
+
+        // ================= 1: gate scan (log2 domain), stage dO and beta
+        float G[KT][4], kr[KT][4], qr[KT][4];
+        if (wave < NSUB) {
+            const int R = wave;
+            const bool valid = 16 * R + l16 < clen;
+#pragma unroll
+            for (int ct = 0; ct < KT; ++ct) {
+                const int c = 16 * ct + 4 * q4;
+                const float4 gv = raw.g[ct];
+                float4 kv, qv;
+                if constexpr (BF) {
+                    kv = make_float4(bf16_lo(raw.k[ct].x), bf16_hi(raw.k[ct].x), bf16_lo(raw.k[ct].y), bf16_hi(raw.k[ct].y));
+                    qv = make_float4(bf16_lo(raw.q[ct].x), bf16_hi(raw.q[ct].x), bf16_lo(raw.q[ct].y), bf16_hi(raw.q[ct].y));
+                } else {
+                    kv = raw.k[ct];
+                    qv = raw.q[ct];
+                }
+                const float m = valid ? kLog2e : 0.f;
+                G[ct][0] = scan16_add(gv.x * m);
+                G[ct][1] = scan16_add(gv.y * m);
+                G[ct][2] = scan16_add(gv.z * m);
+                G[ct][3] = scan16_add(gv.w * m);
+                kr[ct][0] = valid ? kv.x : 0.f; kr[ct][1] = valid ? kv.y : 0.f;
+                kr[ct][2] = valid ? kv.z : 0.f; kr[ct][3] = valid ? kv.w : 0.f;
+                qr[ct][0] = valid ? qv.x : 0.f; qr[ct][1] = valid ? qv.y : 0.f;
+                qr[ct][2] = valid ? qv.z : 0.f; qr[ct][3] = valid ? qv.w : 0.f;
+                if (l16 == 15)
+                    *reinterpret_cast<float4 *>(sTot + R * DK + c) = make_float4(G[ct][0], G[ct][1], G[ct][2], G[ct][3]);
+            }
+        }
+        {
+            constexpr int PPR = DVT / L::V_ELEMS;
+#pragma unroll
+            for (int i = 0; i < L::V_PER_THREAD; ++i) {
+                const int piece = tid + kChunkThreads * i;
+                if (L::V_PIECES % kChunkThreads == 0 || piece < L::V_PIECES) {
+                    const int r = piece / PPR;
+                    const int cc = (piece % PPR) * L::V_ELEMS;
+                    const uint4 x = r < clen ? raw.o[i] : make_uint4(0u, 0u, 0u, 0u);
+                    *reinterpret_cast<uint4 *>(sO + r * LDV + cc) = x;
+                }
+            }
+            if (tid < C) sBeta[tid] = tid < clen ? raw.beta : 0.f;
+        }
+        __syncthreads();
+
+        // ================= 2: per-channel boundary factors
+        if (tid < DK) {
+            const int c = tid;
+            float tot[NSUB], bnd[NSUB + 1];
+            bnd[0] = 0.f;
+#pragma unroll
+            for (int R = 0; R < NSUB; ++R) {
+                tot[R] = sTot[R * DK + c];
+                bnd[R + 1] = bnd[R] + tot[R];
+            }
+            const float gc = bnd[NSUB];
+#pragma unroll
+            for (int R = 0; R < NSUB; ++R) {
+                sEB[R * DK + c] = fast_exp2(bnd[R]);
+                sED[R * DK + c] = fast_exp2(-tot[R]);
+                sEC[R * DK + c] = fast_exp2(gc - bnd[R + 1]);
+#pragma unroll
+                for (int I = 0; I + 2 <= R; ++I) sSH[L::shift_slot(R, I) * DK + c] = fast_exp2(bnd[R] - bnd[I + 1]);
+            }
+            sGam[c] = fast_exp2(gc);
+        }
+        __syncthreads();
+
+        // ================= 3: gated operands of sub-chunk R
+        Frag<BF> kdiag[KT];
+        if (wave < NSUB) {
+            const int R = wave;
+            const int r = 16 * R + l16;
+#pragma unroll
+            for (int ct = 0; ct < KT; ++ct) {
+                const int c = 16 * ct + 4 * q4;
+                const float4 tot = *reinterpret_cast<const float4 *>(sTot + R * DK + c);
+                const float4 eb = *reinterpret_cast<const float4 *>(sEB + R * DK + c);
+                const float4 ed = *reinterpret_cast<const float4 *>(sED + R * DK + c);
+                const float4 ec = *reinterpret_cast<const float4 *>(sEC + R * DK + c);
+                const float tv[4] = {tot.x, tot.y, tot.z, tot.w};
+                const float ebv[4] = {eb.x, eb.y, eb.z, eb.w};
+                const float edv[4] = {ed.x, ed.y, ed.z, ed.w};
+                const float ecv[4] = {ec.x, ec.y, ec.z, ec.w};
+                float kb[4], kt[4], qt[4], kbar[4], kd[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float fr = fast_exp2(G[ct][j]);
+                    const float fb = fast_exp2(tv[j] - G[ct][j]);
+                    const float krow = kr[ct][j] * fr;
+                    const float qrow = qr[ct][j] * fr;
+                    kb[j] = kr[ct][j] * fb;
+                    kd[j] = kb[j] * edv[j];
+                    kt[j] = krow * ebv[j];
+                    qt[j] = qrow * ebv[j];
+                    kbar[j] = kb[j] * ecv[j];
+                    kr[ct][j] = krow;
+                    qr[ct][j] = qrow;
+                }
+                kdiag[ct] = make_frag<BF>(kd[0], kd[1], kd[2], kd[3]);
+                const Frag<BF> fkb = make_frag<BF>(kb[0], kb[1], kb[2], kb[3]);
+                *reinterpret_cast<decltype(fkb.v) *>(sKb + r * LDO + c) = fkb.v;
+                *reinterpret_cast<decltype(fkb.v) *>(sKbar + r * LDO + c) =
+                    make_frag<BF>(kbar[0], kbar[1], kbar[2], kbar[3]).v;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if constexpr (BF) {
+                        sKtT[(c + j) * LDT + r] = f32_to_bf16(kt[j]);
+                        sQtT[(c + j) * LDT + r] = f32_to_bf16(qt[j]);
+                    } else {
+                        sKtT[(c + j) * LDT + r] = kt[j];
+                        sQtT[(c + j) * LDT + r] = qt[j];
+                    }
+                }
+#pragma unroll
+                for (int R2 = 2; R2 < NSUB; ++R2) {
+                    if (R2 < R + 2) continue;
+                    const float4 sh = *reinterpret_cast<const float4 *>(sSH + L::shift_slot(R2, R) * DK + c);
+                    const Frag<BF> f = make_frag<BF>(kb[0] * sh.x, kb[1] * sh.y, kb[2] * sh.z, kb[3] * sh.w);
+                    *reinterpret_cast<decltype(f.v) *>(sKs + (L::shift_slot(R2, R) * 16 + l16) * LDO + c) = f.v;
+                }
+            }
+        }
+        __syncthreads();
+
+        // ================= 4: row-R blocks of A and P (stored transposed), diagonal inverse
+        if (wave < NSUB) {
+            const int R = wave;
+            Frag<BF> ka[KT], qa[KT];
+#pragma unroll
+            for (int ct = 0; ct < KT; ++ct) {
+                ka[ct] = make_frag<BF>(kr[ct][0], kr[ct][1], kr[ct][2], kr[ct][3]);
+                qa[ct] = make_frag<BF>(qr[ct][0], qr[ct][1], qr[ct][2], qr[ct][3]);
+            }
+#pragma unroll
+            for (int I = 0; I < NSUB; ++I) {
+                if (I > R) break;
+                f32x4 accA = zero4(), accP = zero4();
+                const OT *colp = (I == R - 1) ? sKb + (16 * I + l16) * LDO
+                                              : sKs + (L::shift_slot(R < 2 ? 2 : R, I) * 16 + l16) * LDO;
+#pragma unroll
+                for (int ct = 0; ct < KT; ct += 2) {
+                    Frag<BF> b0, b1;
+                    if (I == R) {
+                        b0 = kdiag[ct];
+                        b1 = kdiag[ct + 1];
+                    } else {
+                        b0 = lds_frag(colp + 16 * ct + 4 * q4);
+                        b1 = lds_frag(colp + 16 * (ct + 1) + 4 * q4);
+                    }
+                    mma32(accA, ka[ct], ka[ct + 1], b0, b1);
+                    mma32(accP, qa[ct], qa[ct + 1], b0, b1);
+                }
+                // accumulator: rows rr = 4*q4 + j of block R, column ii = l16 of block I
+                float av[4], pv[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int rr = 4 * q4 + j, ii = l16;
+                    av[j] = accA[j] * sBeta[16 * R + rr];
+                    pv[j] = accP[j];
+                    if (I == R) {
+                        if (ii >= rr) av[j] = 0.f;
+                        if (ii > rr) pv[j] = 0.f;
+                    }
+                }
+                // transposed stores: element (row 16R+rr, column 16I+ii) goes to [16I+ii][16R+rr]
+                const Frag<BF> fp = make_frag<BF>(pv[0], pv[1], pv[2], pv[3]);
+                *reinterpret_cast<decltype(fp.v) *>(sPT + (16 * I + l16) * LDM + 16 * R + 4 * q4) = fp.v;
+                if (I != R) {
+                    const Frag<BF> fa = make_frag<BF>(av[0], av[1], av[2], av[3]);
+                    *reinterpret_cast<decltype(fa.v) *>(sAT + (16 * I + l16) * LDM + 16 * R + 4 * q4) = fa.v;
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) sXT[(R * 16 + 4 * q4 + j) * LDD + l16] = av[j];
+                }
+            }
+            // X_RR = (I + A_RR)^{-1}: lane l16 computes column l16 by forward substitution,
+            // then the block is stored transposed (row l16 of X_RR^T)
+            float *Ab = sXT + R * 16 * LDD;
+            const int jc = l16;
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float s = (r == jc) ? 1.f : 0.f;
+#pragma unroll
+                for (int m = 0; m < r; ++m) s -= Ab[r * LDD + m] * x[m];
+                x[r] = s;
+            }
+            if (q4 == 0) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) Ab[jc * LDD + r] = x[r];
+            }
+        }
+        if (ci > 0) {
+            const int pc0 = (ci - 1) * C;
+            bwd_load_chunk<IO, DK, DVT, C>(raw, bp, start + pc0, min(C, len - pc0), h, col0, tid);
+        }
+        __syncthreads();
+
+        // ================= 5: reverse step for each 16-column slice of the tile
+        const int64_t slot_base = (slot0 + ci) * H + h;
+#pragma unroll
+        for (int s = 0; s < SPW; ++s) {
+            const int sl = wave + L::NW * s;
+            if (sl >= NSL) break;
+            const int col = col0 + 16 * sl + l16;
+
+            // gradient of the state this chunk hands on, kept for the gradient kernel
+            {
+                float *dh = bp.dhs + slot_base * DK * DV + col;
+#pragma unroll
+                for (int ct = 0; ct < KT; ++ct)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) dh[(int64_t)(16 * ct + 4 * q4 + j) * DV] = dS[s][ct][j];
+            }
+            Frag<BF> Sb[KT];
+#pragma unroll
+            for (int ct = 0; ct < KT; ++ct) Sb[ct] = frag_from_acc<BF>(dS[s][ct]);
+
+            // scale * dO as B operands: rows 16I + 4q4 + j, column l16 of the slice
+            Frag<BF> dOf[NSUB];
+#pragma unroll
+            for (int I = 0; I < NSUB; ++I) {
+                float t[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const OT x = sO[(16 * I + 4 * q4 + j) * LDV + 16 * sl + l16];
+                    if constexpr (BF) t[j] = bf16_to_f32(x) * p.scale;
+                    else t[j] = x * p.scale;
+                }
+                dOf[I] = make_frag<BF>(t[0], t[1], t[2], t[3]);
+            }
+
+            // dD_R = sum_{I>=R} (P_IR)^T dO_I + K-_R dS;  dU_R = X_RR^T (dD_R - sum_{I>R} (A_IR)^T dU_I)
+            f32x4 dU[NSUB];
+            Frag<BF> dUf[NSUB];
+#pragma unroll
+            for (int R = NSUB - 1; R >= 0; --R) {
+                f32x4 z = zero4();
+#pragma unroll
+                for (int I = R; I < NSUB; ++I) mma16(z, lds_frag(sPT + (16 * R + l16) * LDM + 16 * I + 4 * q4), dOf[I]);
+                const OT *kb = sKbar + (16 * R + l16) * LDO + 4 * q4;
+#pragma unroll
+                for (int ct = 0; ct < KT; ct += 2)
+                    mma32(z, lds_frag(kb + 16 * ct), lds_frag(kb + 16 * ct + 16), Sb[ct], Sb[ct + 1]);
+#pragma unroll
+                for (int I = R + 1; I < NSUB; ++I) {
+                    Frag<BF> a = lds_frag(sAT + (16 * R + l16) * LDM + 16 * I + 4 * q4);
+                    if constexpr (BF) {
+                        a.v.x ^= 0x80008000u;
+                        a.v.y ^= 0x80008000u;
+                    } else {
+                        a.v = make_float4(-a.v.x, -a.v.y, -a.v.z, -a.v.w);
+                    }
+                    mma16(z, a, dUf[I]);
+                }
+                f32x4 d = zero4();
+                mma16(d, lds_frag_f32<BF>(sXT + (16 * R + l16) * LDD + 4 * q4), frag_from_acc<BF>(z));
+                dU[R] = d;
+                dUf[R] = frag_from_acc<BF>(d);
+            }
+
+            // dY = beta * dU: the value gradient; dU kept per chunk for the gradient kernel
+            Frag<BF> nY[NSUB];
+            OT *du = static_cast<OT *>(bp.duch) + slot_base * C * DV + col;
+#pragma unroll
+            for (int R = 0; R < NSUB; ++R) {
+                float y[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 16 * R + 4 * q4 + j;
+                    y[j] = sBeta[r] * dU[R][j];
+                    if (r < clen) Tr::store1(static_cast<IO *>(bp.dv) + ((tok0 + r) * H + h) * (int64_t)DV + col, y[j]);
+                    if constexpr (BF) du[(int64_t)r * DV] = f32_to_bf16(dU[R][j]);
+                    else du[(int64_t)r * DV] = dU[R][j];
+                }
+                nY[R] = make_frag<BF>(-y[0], -y[1], -y[2], -y[3]);
+            }
+
+            // dS <- Diag(e^{G_C}) dS + Q~^T (scale dO) - K~^T dY
+#pragma unroll
+            for (int ct = 0; ct < KT; ++ct) {
+                const float4 gm = *reinterpret_cast<const float4 *>(sGam + 16 * ct + 4 * q4);
+                dS[s][ct][0] *= gm.x;
+                dS[s][ct][1] *= gm.y;
+                dS[s][ct][2] *= gm.z;
+                dS[s][ct][3] *= gm.w;
+                const OT *qt = sQtT + (16 * ct + l16) * LDT + 4 * q4;
+                const OT *kt = sKtT + (16 * ct + l16) * LDT + 4 * q4;
+#pragma unroll
+                for (int R = 0; R + 1 < NSUB; R += 2) {
+                    mma32(dS[s][ct], lds_frag(qt + 16 * R), lds_frag(qt + 16 * (R + 1)), dOf[R], dOf[R + 1]);
+                    mma32(dS[s][ct], lds_frag(kt + 16 * R), lds_frag(kt + 16 * (R + 1)), nY[R], nY[R + 1]);
+                }
+                if constexpr (NSUB % 2 == 1) {
+                    mma16(dS[s][ct], lds_frag(qt + 16 * (NSUB - 1)), dOf[NSUB - 1]);
+                    mma16(dS[s][ct], lds_frag(kt + 16 * (NSUB - 1)), nY[NSUB - 1]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    if (bp.ds0) {
+#pragma unroll
+        for (int s = 0; s < SPW; ++s) {
+            const int sl = wave + L::NW * s;
+            if (sl >= NSL) break;
+            const int col = col0 + 16 * sl + l16;
+#pragma unroll
+            for (int ct = 0; ct < KT; ++ct)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) bp.ds0[state_base + (int64_t)(16 * ct + 4 * q4 + j) * DV + col] = dS[s][ct][j];
+        }
+    }
+}
+
+// ================================================================== gradients ====
+template <typename IO, int DK, int DV, int C>
+struct BwdGradLayout {
+    static constexpr bool BF = IoTraits<IO>::kBf16;
+    using OT = typename std::conditional<BF, uint16_t, float>::type;
+    static constexpr int NW = DK / 16;  // one 16-channel key tile per wave
+    static constexpr int NT = 64 * NW;
+    static constexpr int NSUB = C / 16;
+    static constexpr int NPAIR = NSUB * (NSUB + 1) / 2;  // sub-chunk pairs R >= I
+    static constexpr int PADO = 16 / (int)sizeof(OT);
+    static constexpr int LDV = DV + PADO;  // [C][DV] staged dO, dU, D
+    static constexpr int LDC = C + PADO;   // [C][C] gradient blocks
+    static constexpr int PIECES = C * DV * (int)sizeof(OT) / 16;  // 16-byte pieces of one [C][DV] tile
+    static constexpr int PPR = DV * (int)sizeof(OT) / 16;         // pieces per row
+    static constexpr int ELEMS = 16 / (int)sizeof(OT);
+    static_assert(sizeof(IO) == sizeof(OT), "operand type follows the io type");
+    static_assert(NT % PPR == 0 && PIECES % PPR == 0 && PPR <= 64, "staging split: whole rows per lane group");
+    static_assert(DV % 32 == 0 && C % 16 == 0 && NSUB <= 4, "tile sizes");
+
+    static constexpr size_t kTile = (size_t)C * LDV * sizeof(OT);
+    static constexpr size_t kBlk = (size_t)C * LDC * sizeof(OT);
+    static constexpr size_t oO = 0;
+    static constexpr size_t oU = oO + kTile;
+    static constexpr size_t oD = oU + kTile;
+    static constexpr size_t oP = oD + kTile;    // dP   [r][i]
+    static constexpr size_t oPT = oP + kBlk;    // dP   [i][r]
+    static constexpr size_t oA = oPT + kBlk;    // dA   [r][i]
+    static constexpr size_t oLT = oA + kBlk;    // dL   [i][r]  (dL = beta_r dA)
+    static constexpr size_t oBeta = oLT + kBlk;
+    static constexpr size_t oUV = oBeta + (size_t)C * 4;
+    static constexpr size_t oGam = oUV + (size_t)C * 4;
+    static constexpr size_t oDb = oGam + (size_t)DK * 4;
+    static constexpr size_t kBytes = oDb + (size_t)NW * C * 4;
+    static constexpr bool kFits = kBytes <= 160 * 1024;
+
+    __host__ __device__ static constexpr int pair_r(int pi) {
+        int R = 0;
+        while ((R + 1) * (R + 2) / 2 <= pi) ++R;
+        return R;
+    }
+    __host__ __device__ static constexpr int pair_i(int pi) { return pi - pair_r(pi) * (pair_r(pi) + 1) / 2; }
+};
+
+// Sequence and chunk of a chunk slot (the inverse of bwd_slot0); false past the last chunk.
+__device__ __forceinline__ bool bwd_slot_chunk(const FwdParams &p, int C, int64_t slot, int &n, int &ci) {
+    if (p.cu) {
+        if (slot >= p.chunk_off[p.num_seqs]) return false;
+        int lo = 0, hi = p.num_seqs - 1;  // last n with chunk_off[n] <= slot
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (p.chunk_off[mid] <= slot) lo = mid;
+            else hi = mid - 1;
+        }
+        n = lo;
+        ci = (int)(slot - p.chunk_off[lo]);
+        return true;
+    }
+    const int64_t per = (p.T + C - 1) / C;
+    if (per == 0 || slot >= per * p.num_seqs) return false;
+    n = (int)(slot / per);
+    ci = (int)(slot % per);
+    return true;
+}
+
+template <typename IO, int DK, int DV, int C>
+__global__ void __launch_bounds__(64 * (DK / 16)) kda_bwd_grad_kernel(BwdParams bp) {
+    using L = BwdGradLayout<IO, DK, DV, C>;
+    using OT = typename L::OT;
+    constexpr bool BF = L::BF;
+    constexpr int NSUB = L::NSUB, NW = L::NW, NT = L::NT, LDV = L::LDV, LDC = L::LDC;
+    using Tr = IoTraits<IO>;
+    const FwdParams &p = bp.f;
+
+    __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
+    OT *sO = reinterpret_cast<OT *>(smem + L::oO);
+    OT *sU = reinterpret_cast<OT *>(smem + L::oU);
+    OT *sD = reinterpret_cast<OT *>(smem + L::oD);
+    OT *sP = reinterpret_cast<OT *>(smem + L::oP);
+    OT *sPT = reinterpret_cast<OT *>(smem + L::oPT);
+    OT *sA = reinterpret_cast<OT *>(smem + L::oA);
+    OT *sLT = reinterpret_cast<OT *>(smem + L::oLT);
+    float *sBeta = reinterpret_cast<float *>(smem + L::oBeta);
+    float *sUV = reinterpret_cast<float *>(smem + L::oUV);
+    float *sGam = reinterpret_cast<float *>(smem + L::oGam);
+    float *sDb = reinterpret_cast<float *>(smem + L::oDb);
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l16 = lane & 15, q4 = lane >> 4;
+    const int H = p.H;
+
+    const int64_t slot = blockIdx.x / H;
+    const int h = (int)(blockIdx.x % H);
+    int n, ci;
+    if (!bwd_slot_chunk(p, C, slot, n, ci)) return;
+    const int64_t start = p.cu ? (int64_t)p.cu[n] : (int64_t)n * p.T;
+    const int len = p.cu ? p.cu[n + 1] - p.cu[n] : p.T;
+    const int clen = min(C, len - ci * C);
+    const int64_t tok0 = start + (int64_t)ci * C;
+    const int64_t base = slot * H + h;
+    const int cw = 16 * wave;  // first key channel of this wave
+
+    // ---- key side of the wave's channels for every token: lane (token 16R + l16, channels cw + 4q4 + j)
+    float G[NSUB][4], kk[NSUB][4], qq[NSUB][4];
+#pragma unroll
+    for (int R = 0; R < NSUB; ++R) {
+        const int r = 16 * R + l16;
+        const bool valid = r < clen;
+        const int64_t row = ((tok0 + min(r, clen - 1)) * H + h) * (int64_t)DK + cw + 4 * q4;
+        const float4 gv = *reinterpret_cast<const float4 *>(p.g + row);
+        const float4 kv = Tr::load4(static_cast<const IO *>(p.k) + row);
+        const float4 qv = Tr::load4(static_cast<const IO *>(p.q) + row);
+        const float m = valid ? kLog2e : 0.f;
+        G[R][0] = scan16_add(gv.x * m);
+        G[R][1] = scan16_add(gv.y * m);
+        G[R][2] = scan16_add(gv.z * m);
+        G[R][3] = scan16_add(gv.w * m);
+        kk[R][0] = valid ? kv.x : 0.f; kk[R][1] = valid ? kv.y : 0.f;
+        kk[R][2] = valid ? kv.z : 0.f; kk[R][3] = valid ? kv.w : 0.f;
+        qq[R][0] = valid ? qv.x : 0.f; qq[R][1] = valid ? qv.y : 0.f;
+        qq[R][2] = valid ? qv.z : 0.f; qq[R][3] = valid ? qv.w : 0.f;
+    }
+
+    // ---- stage dO, dU, D ([C][DV]); sum_j dU_rj V_rj per token
+    if (tid < C) sBeta[tid] = tid < clen ? p.beta[(tok0 + tid) * H + h] : 0.f;
+    {
+        const IO *dO = static_cast<const IO *>(bp.d_out);
+        const OT *dU = static_cast<const OT *>(bp.duch) + base * C * DV;
+        const OT *Dc = static_cast<const OT *>(bp.dch) + base * C * DV;
+        const IO *V = static_cast<const IO *>(p.v);
+#pragma unroll
+        for (int i = 0; i < (L::PIECES + NT - 1) / NT; ++i) {
+            const int piece = tid + NT * i;
+            // a row's PPR pieces sit in PPR consecutive lanes, all inside or all outside
+            if (L::PIECES % NT != 0 && piece >= L::PIECES) break;
+            const int r = piece / L::PPR;
+            const int cc = (piece % L::PPR) * L::ELEMS;
+            const bool valid = r < clen;
+            const int64_t grow = ((tok0 + min(r, clen - 1)) * H + h) * (int64_t)DV + cc;
+            const uint4 xo = valid ? *reinterpret_cast<const uint4 *>(dO + grow) : make_uint4(0u, 0u, 0u, 0u);
+            const uint4 xu = *reinterpret_cast<const uint4 *>(dU + (int64_t)r * DV + cc);
+            const uint4 xd = *reinterpret_cast<const uint4 *>(Dc + (int64_t)r * DV + cc);
+            const uint4 xv = *reinterpret_cast<const uint4 *>(V + grow);
+            *reinterpret_cast<uint4 *>(sO + r * LDV + cc) = xo;
+            *reinterpret_cast<uint4 *>(sU + r * LDV + cc) = xu;
+            *reinterpret_cast<uint4 *>(sD + r * LDV + cc) = xd;
+            float uv = 0.f;
+            if constexpr (BF) {
+                const uint32_t a[4] = {xu.x, xu.y, xu.z, xu.w}, b[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) uv += bf16_lo(a[e]) * bf16_lo(b[e]) + bf16_hi(a[e]) * bf16_hi(b[e]);
+            } else {
+                uv = __uint_as_float(xu.x) * __uint_as_float(xv.x) + __uint_as_float(xu.y) * __uint_as_float(xv.y) +
+                     __uint_as_float(xu.z) * __uint_as_float(xv.z) + __uint_as_float(xu.w) * __uint_as_float(xv.w);
+            }
+            // the PPR pieces of a row sit in PPR consecutive lanes of one wave
+#pragma unroll
+            for (int o = 1; o < L::PPR; o <<= 1) uv += __shfl_xor(uv, o);
+            if (piece % L::PPR == 0) sUV[r] = valid ? uv : 0.f;
+        }
+    }
+    __syncthreads();
+
+    // ---- dP = scale lower_incl(dO D^T), dA = -strictly_lower(dU D^T), block pairs R >= I
+#pragma unroll
+    for (int pi0 = 0; pi0 < L::NPAIR; pi0 += NW) {
+        const int pi = pi0 + wave;
+        if (pi >= L::NPAIR) break;
+        const int R = L::pair_r(pi), I = L::pair_i(pi);
+        f32x4 accP = zero4(), accA = zero4();
+        const OT *ao = sO + (16 * R + l16) * LDV + 4 * q4;
+        const OT *au = sU + (16 * R + l16) * LDV + 4 * q4;
+        const OT *bd = sD + (16 * I + l16) * LDV + 4 * q4;
+#pragma unroll
+        for (int kt = 0; kt < DV; kt += 32) {
+            const Frag<BF> b0 = lds_frag(bd + kt), b1 = lds_frag(bd + kt + 16);
+            mma32(accP, lds_frag(ao + kt), lds_frag(ao + kt + 16), b0, b1);
+            mma32(accA, lds_frag(au + kt), lds_frag(au + kt + 16), b0, b1);
+        }
+        // accumulator: row r = 16R + 4q4 + j, column i = 16I + l16
+        float vp[4], va[4], vl[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int rr = 4 * q4 + j;
+            vp[j] = (R == I && l16 > rr) ? 0.f : accP[j] * p.scale;
+            va[j] = (R == I && l16 >= rr) ? 0.f : -accA[j];
+            vl[j] = va[j] * sBeta[16 * R + rr];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * R + 4 * q4 + j;
+            if constexpr (BF) {
+                sP[r * LDC + 16 * I + l16] = f32_to_bf16(vp[j]);
+                sA[r * LDC + 16 * I + l16] = f32_to_bf16(va[j]);
+            } else {
+                sP[r * LDC + 16 * I + l16] = vp[j];
+                sA[r * LDC + 16 * I + l16] = va[j];
+            }
+        }
+        const Frag<BF> fp = make_frag<BF>(vp[0], vp[1], vp[2], vp[3]);
+        const Frag<BF> fl = make_frag<BF>(vl[0], vl[1], vl[2], vl[3]);
+        *reinterpret_cast<decltype(fp.v) *>(sPT + (16 * I + l16) * LDC + 16 * R + 4 * q4) = fp.v;
+        *reinterpret_cast<decltype(fl.v) *>(sLT + (16 * I + l16) * LDC + 16 * R + 4 * q4) = fl.v;
+    }
+
+    // ---- S dO^T, S dU^T, dS D^T for the wave's channels (rows c = cw + l16 of S and dS as
+    //      A operands straight from the chunk states), and rowsum(dS .* S)
+    f32x4 Zq[NSUB], Zu[NSUB], Zs[NSUB];
+    {
+        const float *Sr = bp.hs + base * DK * DV + (int64_t)(cw + l16) * DV + 4 * q4;
+        const float *dSr = bp.dhs + base * DK * DV + (int64_t)(cw + l16) * DV + 4 * q4;
+        Frag<BF> sf[DV / 16], dsf[DV / 16];
+        float gam = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < DV / 16; ++kt) {
+            const float4 a = *reinterpret_cast<const float4 *>(Sr + 16 * kt);
+            const float4 b = *reinterpret_cast<const float4 *>(dSr + 16 * kt);
+            gam += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+            sf[kt] = make_frag<BF>(a.x, a.y, a.z, a.w);
+            dsf[kt] = make_frag<BF>(b.x, b.y, b.z, b.w);
+        }
+        gam += __shfl_xor(gam, 16);
+        gam += __shfl_xor(gam, 32);
+        if (q4 == 0) sGam[cw + l16] = gam;
+        __syncthreads();  // dP / dA blocks complete
+#pragma unroll
+        for (int R = 0; R < NSUB; ++R) {
+            Zq[R] = zero4();
+            Zu[R] = zero4();
+            Zs[R] = zero4();
+            const OT *bo = sO + (16 * R + l16) * LDV + 4 * q4;
+            const OT *bu = sU + (16 * R + l16) * LDV + 4 * q4;
+            const OT *bdd = sD + (16 * R + l16) * LDV + 4 * q4;
+#pragma unroll
+            for (int kt = 0; kt < DV / 16; kt += 2) {
+                mma32(Zq[R], sf[kt], sf[kt + 1], lds_frag(bo + 16 * kt), lds_frag(bo + 16 * kt + 16));
+                mma32(Zu[R], sf[kt], sf[kt + 1], lds_frag(bu + 16 * kt), lds_frag(bu + 16 * kt + 16));
+                mma32(Zs[R], dsf[kt], dsf[kt + 1], lds_frag(bdd + 16 * kt), lds_frag(bdd + 16 * kt + 16));
+            }
+        }
+    }
+
+    // ---- gate factors (log2 domain; per lane and channel j): b_R sub-chunk boundaries
+    float bnd[NSUB + 1][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bnd[0][j] = 0.f;
+#pragma unroll
+    for (int R = 0; R < NSUB; ++R)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bnd[R + 1][j] = bnd[R][j] + __shfl(G[R][j], 16 * q4 + 15);
+
+    // transposed operands through the identity: A operands with rows = channels
+    Frag<BF> kbT[NSUB], qrT[NSUB], krT[NSUB];
+    {
+        const Frag<BF> eye = make_frag<BF>(4 * q4 == l16 ? 1.f : 0.f, 4 * q4 + 1 == l16 ? 1.f : 0.f,
+                                           4 * q4 + 2 == l16 ? 1.f : 0.f, 4 * q4 + 3 == l16 ? 1.f : 0.f);
+#pragma unroll
+        for (int R = 0; R < NSUB; ++R) {
+            float kb[4], kr[4], qr[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float tot = bnd[R + 1][j] - bnd[R][j];
+                kb[j] = kk[R][j] * fast_exp2(tot - G[R][j]);  // k e^{b_{R+1} - G}  (<= 1)
+                const float fr = fast_exp2(G[R][j]);          // e^{G - b_R}        (<= 1)
+                kr[j] = kk[R][j] * fr;
+                qr[j] = qq[R][j] * fr;
+            }
+            f32x4 t = zero4();
+            mma16(t, make_frag<BF>(kb[0], kb[1], kb[2], kb[3]), eye);
+            kbT[R] = frag_from_acc<BF>(t);
+            t = zero4();
+            mma16(t, make_frag<BF>(kr[0], kr[1], kr[2], kr[3]), eye);
+            krT[R] = frag_from_acc<BF>(t);
+            t = zero4();
+            mma16(t, make_frag<BF>(qr[0], qr[1], qr[2], qr[3]), eye);
+            qrT[R] = frag_from_acc<BF>(t);
+        }
+    }
+
+    // ---- C x C contractions; outputs (channel x token) in the lane layout above
+    f32x4 RowP[NSUB], RowA[NSUB], Col[NSUB];
+#pragma unroll
+    for (int R = 0; R < NSUB; ++R) {
+        RowP[R] = zero4();
+        RowA[R] = zero4();
+        Col[R] = zero4();
+    }
+#pragma unroll
+    for (int R = 0; R < NSUB; ++R) {
+#pragma unroll
+        for (int I = 0; I <= R; ++I) {
+            // row side (tokens of R): sum_{i in I} kb_i dP_ri, kb_i dA_ri
+            f32x4 tp = zero4(), ta = zero4();
+            mma16(tp, kbT[I], lds_frag(sP + (16 * R + l16) * LDC + 16 * I + 4 * q4));
+            mma16(ta, kbT[I], lds_frag(sA + (16 * R + l16) * LDC + 16 * I + 4 * q4));
+            // column side (tokens of I): sum_{r in R} qrow_r dP_ri + krow_r dL_ri
+            f32x4 tc = zero4();
+            mma16(tc, qrT[R], lds_frag(sPT + (16 * I + l16) * LDC + 16 * R + 4 * q4));
+            mma16(tc, krT[R], lds_frag(sLT + (16 * I + l16) * LDC + 16 * R + 4 * q4));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float sh = fast_exp2(bnd[R][j] - bnd[I + 1][j]);  // e^{b_R - b_{I+1}}
+                RowP[R][j] += sh * tp[j];
+                RowA[R][j] += sh * ta[j];
+                Col[I][j] += sh * tc[j];
+            }
+        }
+    }
+
+    // ---- combine per (token, channel)
+    float dG[NSUB][4], gcs[4] = {0.f, 0.f, 0.f, 0.f};
+    float dbp[NSUB];
+    IO *dqo = static_cast<IO *>(bp.dq);
+    IO *dko = static_cast<IO *>(bp.dk);
+#pragma unroll
+    for (int R = 0; R < NSUB; ++R) {
+        const int r = 16 * R + l16;
+        const float b = sBeta[r];
+        float dq4[4], dk4[4];
+        dbp[R] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float fr = fast_exp2(G[R][j]);
+            const float fb = fast_exp2(bnd[R + 1][j] - bnd[R][j] - G[R][j]);
+            const float eG = fast_exp2(bnd[R][j] + G[R][j]);
+            const float ekb = fast_exp2(bnd[NSUB][j] - bnd[R][j] - G[R][j]);
+            const float W = fr * RowA[R][j];
+            const float dq = p.scale * eG * Zq[R][j] + fr * RowP[R][j];
+            const float dk1 = b * (W - eG * Zu[R][j]);
+            const float dk2 = fb * Col[R][j];
+            const float dk3 = ekb * Zs[R][j];
+            dq4[j] = dq;
+            dk4[j] = dk1 + dk2 + dk3;
+            dG[R][j] = qq[R][j] * dq + kk[R][j] * (dk1 - dk2 - dk3);
+            gcs[j] += kk[R][j] * dk3;
+            dbp[R] += kk[R][j] * (W - eG * Zu[R][j]);
+        }
+        if (r < clen) {
+            const int64_t row = ((tok0 + r) * H + h) * (int64_t)DK + cw + 4 * q4;
+            Tr::store4(dqo + row, make_float4(dq4[0], dq4[1], dq4[2], dq4[3]));
+            Tr::store4(dko + row, make_float4(dk4[0], dk4[1], dk4[2], dk4[3]));
+        }
+    }
+    // gradient of the chunk's total gate G_C: sum over tokens, plus e^{G_C} rowsum(dS .* S)
+    const int rl = clen - 1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float x = gcs[j];
+        x += __shfl_xor(x, 1);
+        x += __shfl_xor(x, 2);
+        x += __shfl_xor(x, 4);
+        x += __shfl_xor(x, 8);
+        x += fast_exp2(bnd[NSUB][j]) * sGam[cw + 4 * q4 + j];
+#pragma unroll
+        for (int R = 0; R < NSUB; ++R)
+            if (16 * R + l16 == rl) dG[R][j] += x;
+    }
+    // dg = reverse cumulative sum of dG over the chunk's tokens
+    float carry[4] = {0.f, 0.f, 0.f, 0.f};
+    float *dgo = bp.dg;
+#pragma unroll
+    for (int R = NSUB - 1; R >= 0; --R) {
+        float out4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float incl = scan16_add(dG[R][j]);
+            const float tot = __shfl(incl, 16 * q4 + 15);
+            out4[j] = tot - incl + dG[R][j] + carry[j];
+            carry[j] += tot;
+        }
+        const int r = 16 * R + l16;
+        if (r < clen)
+            *reinterpret_cast<float4 *>(dgo + ((tok0 + r) * H + h) * (int64_t)DK + cw + 4 * q4) =
+                make_float4(out4[0], out4[1], out4[2], out4[3]);
+    }
+    // dbeta: this wave's channels, then the sum over waves and the value term
+#pragma unroll
+    for (int R = 0; R < NSUB; ++R) {
+        float x = dbp[R];
+        x += __shfl_xor(x, 16);
+        x += __shfl_xor(x, 32);
+        if (q4 == 0) sDb[wave * C + 16 * R + l16] = x;
+    }
+    __syncthreads();
+    if (tid < clen) {
+        float x = sUV[tid];
+#pragma unroll
+        for (int w = 0; w < NW; ++w) x += sDb[w * C + tid];
+        bp.dbeta[(tok0 + tid) * H + h] = x;
+    }
+}
+
+// ================================================================== launch ====
+constexpr int kBwdScanTile = 32;  // d_v columns per reverse-scan workgroup
+
+template <typename IO, int DK, int DV, int C>
+constexpr bool bwd_fits() {
+    return BwdScanLayout<IO, DK, kBwdScanTile, C>::kFits && BwdGradLayout<IO, DK, DV, C>::kFits;
+}
+
+template <typename IO, int DK, int DV, int C>
+hipError_t launch_bwd_variant(const BwdParams &bp, hipStream_t stream) {
+    if constexpr (!bwd_fits<IO, DK, DV, C>()) {
+        return hipErrorInvalidConfiguration;
+    } else {
+        const FwdParams &p = bp.f;
+        const int64_t scan_blocks = (int64_t)p.num_seqs * p.H * (DV / kBwdScanTile);
+        if (scan_blocks > 0) {
+            hipLaunchKernelGGL((kda_bwd_scan_kernel<IO, DK, kBwdScanTile, C>), dim3((unsigned)scan_blocks),
+                               dim3(kChunkThreads), 0, stream, bp);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        const int64_t grad_blocks = bp.slots * p.H;
+        if (grad_blocks > 0) {
+            hipLaunchKernelGGL((kda_bwd_grad_kernel<IO, DK, DV, C>), dim3((unsigned)grad_blocks),
+                               dim3(BwdGradLayout<IO, DK, DV, C>::NT), 0, stream, bp);
+            return hipGetLastError();
+        }
+        return hipSuccess;
+    }
+}
+
+// F(DK, DV, C)
+#define KDA_BWD_VARIANTS(F)                                                                \
+    F(64, 64, 16) F(64, 64, 32) F(64, 64, 64) F(64, 128, 16) F(64, 128, 32) F(64, 128, 64) \
+    F(128, 64, 16) F(128, 64, 32) F(128, 64, 64) F(128, 128, 16) F(128, 128, 32) F(128, 128, 64)
+
+template <typename IO>
+bool bwd_supported(int dk, int dv, int chunk) {
+#define KDA_BWD_FIT_CASE(DK_, DV_, C_) \
+    if (dk == DK_ && dv == DV_ && chunk == C_) return bwd_fits<IO, DK_, DV_, C_>();
+    KDA_BWD_VARIANTS(KDA_BWD_FIT_CASE)
+#undef KDA_BWD_FIT_CASE
+    return false;
+}
+
+template <typename IO>
+hipError_t launch_bwd(const BwdParams &bp, int chunk, hipStream_t stream) {
+#define KDA_BWD_CASE(DK_, DV_, C_) \
+    if (bp.f.dk == DK_ && bp.f.dv == DV_ && chunk == C_) return launch_bwd_variant<IO, DK_, DV_, C_>(bp, stream);
+    KDA_BWD_VARIANTS(KDA_BWD_CASE)
+#undef KDA_BWD_CASE
+    return hipErrorInvalidConfiguration;
+}
+
+}  // namespace kda

@@ -196,6 +196,9 @@ __global__ void __launch_bounds__(kChunkThreads) kda_chunk_fwd_kernel(FwdParams 
         len = p.T;
     }
     const int col0 = tile * DVT;
+    // first chunk slot of this sequence in the optional per-chunk outputs
+    int64_t slot0 = 0;
+    if (p.hs || p.dch) slot0 = p.cu ? (int64_t)p.chunk_off[n] : (int64_t)n * ((p.T + C - 1) / C);
 
     // ---- state slices owned by this wave: S[s][ct] holds rows 16ct+4q4+j of column col(s)
     f32x4 S[SPW][KT];
@@ -426,6 +429,14 @@ __global__ void __launch_bounds__(kChunkThreads) kda_chunk_fwd_kernel(FwdParams 
             const int sl = wave + L::NW * s;
             if (sl >= NSL) break;
             const int col = col0 + 16 * sl + l16;
+            const int64_t slot_base = ((slot0 + c0 / C) * H + h);
+            if (p.hs) {
+                float *hs = p.hs + slot_base * DK * DV + col;
+#pragma unroll
+                for (int ct = 0; ct < KT; ++ct)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) hs[(int64_t)(16 * ct + 4 * q4 + j) * DV] = S[s][ct][j];
+            }
 
             Frag<BF> Sb[KT];
 #pragma unroll
@@ -472,6 +483,20 @@ __global__ void __launch_bounds__(kChunkThreads) kda_chunk_fwd_kernel(FwdParams 
                 f32x4 d = zero4();
                 mma16(d, lds_frag_f32<BF>(sAd + (16 * R + l16) * LDD + 4 * q4), frag_from_acc<BF>(z));
                 D[R] = frag_from_acc<BF>(d);
+                if (p.dch) {
+                    OT *dc = static_cast<OT *>(p.dch) + slot_base * C * DV + (int64_t)(16 * R + 4 * q4) * DV + col;
+                    if constexpr (BF) {
+                        dc[0] = (uint16_t)(D[R].v.x & 0xffffu);
+                        dc[DV] = (uint16_t)(D[R].v.x >> 16);
+                        dc[2 * DV] = (uint16_t)(D[R].v.y & 0xffffu);
+                        dc[3 * DV] = (uint16_t)(D[R].v.y >> 16);
+                    } else {
+                        dc[0] = D[R].v.x;
+                        dc[DV] = D[R].v.y;
+                        dc[2 * DV] = D[R].v.z;
+                        dc[3 * DV] = D[R].v.w;
+                    }
+                }
             }
 
             // O = scale (Q~ S + P D)
@@ -482,7 +507,7 @@ __global__ void __launch_bounds__(kChunkThreads) kda_chunk_fwd_kernel(FwdParams 
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int r = 16 * R + 4 * q4 + j;
-                    if (r < clen) Tr::store1(O + ((tok0 + r) * H + h) * (int64_t)DV + col, Oa[R][j] * p.scale);
+                    if (O && r < clen) Tr::store1(O + ((tok0 + r) * H + h) * (int64_t)DV + col, Oa[R][j] * p.scale);
                 }
             }
 

@@ -19,6 +19,14 @@ struct FwdParams {
     float *sf;           // [num_seqs, H, DK, DV] or null
     int32_t num_seqs, T, H, dk, dv;
     float scale;
+    // Optional per-chunk outputs of the fused forward, kept for the backward pass:
+    // hs [slot, H, DK, DV] fp32 state entering each chunk, dch [slot, H, C, DV] the
+    // chunk's delta-rule corrections D (operand type).  slot = chunk_off[n] + chunk index
+    // for a packed batch (chunk_off from the plan kernel), n * ceil(T / C) + chunk index
+    // otherwise.
+    float *hs = nullptr;
+    void *dch = nullptr;
+    const int32_t *chunk_off = nullptr;
 };
 
 // Chunk-forward configuration chosen by the host.
@@ -60,6 +68,29 @@ hipError_t launch_split_f32(const FwdParams &p, int chunk, int spw, int nw, char
 hipError_t launch_split_bf16(const FwdParams &p, int chunk, int spw, int nw, char *workspace, int64_t chunk_upper,
                              hipStream_t stream);
 constexpr int kSerialThreads = 256;
+
+// Backward: reverse chunk scan + per-chunk gradients (kda_bwd_*.hip); the forward pass
+// that keeps the chunk states is the fused forward with FwdParams::hs / dch set.
+struct BwdParams {
+    FwdParams f;          // forward inputs and sizes (f.out, f.sf unused)
+    const void *d_out;    // dO [tokens, H, DV] io dtype
+    const float *d_sf;    // [num_seqs, H, DK, DV] or null (zero)
+    void *dq, *dk, *dv;   // [tokens, H, DK|DV] io dtype
+    float *dg;            // [tokens, H, DK]
+    float *dbeta;         // [tokens, H]
+    float *ds0;           // [num_seqs, H, DK, DV] or null
+    const float *hs;      // [slot, H, DK, DV] chunk initial states (written by the forward pass)
+    float *dhs;           // [slot, H, DK, DV] gradient of each chunk's final state
+    const void *dch;      // [slot, H, C, DV] D per chunk (operand type)
+    void *duch;           // [slot, H, C, DV] dU per chunk (operand type)
+    int64_t slots;        // upper bound on the number of chunk slots
+};
+bool bwd_supported_bf16(int dk, int dv, int chunk);
+bool bwd_supported_f32(int dk, int dv, int chunk);
+hipError_t launch_bwd_bf16(const BwdParams &bp, int chunk, hipStream_t stream);
+hipError_t launch_bwd_f32(const BwdParams &bp, int chunk, hipStream_t stream);
+hipError_t launch_chunk_plan(const int32_t *cu, int32_t num_seqs, int32_t chunk, int32_t *chunk_off,
+                             hipStream_t stream);
 
 // Prologue (short convolution + Swish, q/k L2 normalisation, gate and beta activations).
 hipError_t launch_prologue(kda_dtype_t io, int64_t tokens, int32_t num_seqs, int32_t seq_len, int32_t H, int32_t dk,

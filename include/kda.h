@@ -125,6 +125,46 @@ kda_status_t kda_recurrent_fwd(const kda_problem_t *problem, const void *q, cons
                                float *final_state, void *stream);
 
 /*
+ * kda_chunk_bwd -- gradients of the chunkwise forward (training).
+ * Kimi Linear summary page, "Chunkwise parallel algorithm" section: the WY/UT chunk form
+ * is what makes the operator trainable at matrix-core speed; the gradients are the
+ * reverse-mode derivative of the same chunk equations (one triangular inverse per chunk,
+ * reused for its transpose), exact up to rounding.
+ *
+ * For the loss L = sum(d_out * out) + sum(d_final_state * final_state) of the forward with
+ * the same arguments, writes dq, dk, dv, dg, dbeta and (optionally) d_initial_state.
+ *  problem, q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_host
+ *                  as for kda_chunk_fwd (the forward is recomputed; out is not needed).
+ *                  problem->chunk_size: 16, 32 or 64 (0 = default); problem->algo and
+ *                  dv_tile are ignored.
+ *  d_out           [tokens, H, d_v] io dtype: gradient of out.
+ *  d_final_state   [num_seqs, H, d_k, d_v] fp32, or NULL for zero.
+ *  dq, dk          [tokens, H, d_k] io dtype (written).
+ *  dv              [tokens, H, d_v] io dtype (written).
+ *  dg              [tokens, H, d_k] fp32 (written): gradient of the log-gate g.
+ *  dbeta           [tokens, H] fp32 (written).
+ *  d_initial_state [num_seqs, H, d_k, d_v] fp32, or NULL to skip it.
+ *  workspace       device scratch of at least kda_chunk_bwd_workspace() bytes, 256-byte
+ *                  aligned (chunk states, their gradients and two per-chunk d_v tiles);
+ *                  contents on entry ignored, on return unspecified.  Required.
+ * No output may alias an input or another output.  Status and error behaviour as for
+ * kda_chunk_fwd; KDA_ERR_UNSUPPORTED when no compiled variant fits (fp32 io with
+ * chunk 64 at d_v = 128, for instance).
+ */
+kda_status_t kda_chunk_bwd(const kda_problem_t *problem, const void *q, const void *k, const void *v,
+                           const float *g, const float *beta, const float *initial_state,
+                           const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, const void *d_out,
+                           const float *d_final_state, void *dq, void *dk, void *dv, float *dg, float *dbeta,
+                           float *d_initial_state, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kda_chunk_bwd_workspace -- workspace bytes kda_chunk_bwd needs for `problem` (packed
+ * batch when problem->num_seqs > 0, as in kda_query).  Writes *bytes; returns
+ * KDA_ERR_UNSUPPORTED (and *bytes = 0) for problems kda_chunk_bwd does not support.
+ */
+kda_status_t kda_chunk_bwd_workspace(const kda_problem_t *problem, size_t *bytes);
+
+/*
  * kda_decode_step -- one token for each of num_seqs independent sequences, updating
  * the per-sequence state in place (the fixed-size state slot that replaces a growing
  * KV cache; "Kimi Delta Attention" and evaluation sections of the summary page).

@@ -211,3 +211,17 @@ def prologue_inputs(B: int, T: int, H: int, dk: int, dv: int, W: int, io: str, s
         cu = torch.tensor([0] + list(np.cumsum(lengths)), dtype=torch.int32)
     return dict(q_raw=q, k_raw=k, v_raw=v, conv_q=wq, conv_k=wk, conv_v=wv, g_raw=g, beta_raw=b, conv_state=st,
                 cu_seqlens=cu)
+
+
+def grad_inputs(inp: Inputs, seed: int, *, dsf_std: Optional[float] = 0.1):
+    """Upstream gradients for the backward: d_out ~ N(0, 1) with out's shape, cast to the io
+    dtype, then (dsf_std not None) the final-state gradient ~ N(0, dsf_std^2) [N, H, dk, dv]
+    fp32.  Synthetic stand-ins for what the next layer sends back in training."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    B, T, H, _ = inp.q.shape
+    dv = inp.v.shape[-1]
+    d_out = torch.randn(B, T, H, dv, generator=gen).to(inp.q.dtype)
+    dsf = None
+    if dsf_std is not None:
+        dsf = dsf_std * torch.randn(inp.num_seqs, H, inp.q.shape[-1], dv, generator=gen)
+    return d_out, dsf

@@ -246,3 +246,64 @@ def test_tune_validation():
     bad = problem(head_dim_k=96)
     assert lib.kda_tune(ctypes.byref(bad), *args, None, None, None, fake(5), None, None, 0, None,
                         ctypes.byref(res)) == kda.KDA_ERR_UNSUPPORTED
+
+
+def _bwd_problem(**kw):
+    base = dict(batch=2, seq_len=100, num_heads=2, head_dim_k=128, head_dim_v=128, num_seqs=0,
+                io_dtype=kda.KDA_BF16, chunk_size=64, scale=1.0, dv_tile=0, algo=0)
+    base.update(kw)
+    return kda.Problem(**base)
+
+
+def test_bwd_workspace_query():
+    lib = kda.library()
+    n = ctypes.c_size_t(0)
+    assert lib.kda_chunk_bwd_workspace(ctypes.byref(_bwd_problem()), ctypes.byref(n)) == kda.KDA_OK
+    # plan + chunk states and their gradients (fp32) + D and dU tiles (bf16), 256-byte sections
+    slots = 2 * 2  # 2 sequences x ceil(100 / 64)
+    assert n.value == 256 + 2 * slots * 2 * 128 * 128 * 4 + 2 * slots * 2 * 64 * 128 * 2
+    # a packed batch reserves one partial chunk per sequence
+    assert lib.kda_chunk_bwd_workspace(ctypes.byref(_bwd_problem(batch=1, seq_len=300, num_seqs=5)),
+                                       ctypes.byref(n)) == kda.KDA_OK
+    assert n.value == 256 + 2 * (5 + 5) * 2 * 128 * 128 * 4 + 2 * (5 + 5) * 2 * 64 * 128 * 2
+    assert lib.kda_chunk_bwd_workspace(ctypes.byref(_bwd_problem(chunk_size=48)), ctypes.byref(n)) == \
+        kda.KDA_ERR_UNSUPPORTED
+    assert n.value == 0
+    assert lib.kda_chunk_bwd_workspace(ctypes.byref(_bwd_problem()), None) == kda.KDA_ERR_INVALID_ARGUMENT
+
+
+def test_bwd_validation():
+    lib = kda.library()
+    p = _bwd_problem()
+    P = lambda a: ctypes.c_void_p(a)
+    good = [P(0x10000 * (i + 1)) for i in range(16)]
+    ws_ok = 1 << 30
+
+    def call(ptrs, ws=P(0x100000), ws_bytes=ws_ok, prob=p):
+        return lib.kda_chunk_bwd(ctypes.byref(prob), *ptrs, ws, ws_bytes, None)
+
+    # q k v g beta s0 cu cu_host d_out d_sf dq dk dv dg dbeta ds0
+    ptrs = good[:6] + [None, None] + good[8:16]
+    for i, name in [(0, "q"), (8, "d_out"), (10, "dq"), (11, "dk"), (12, "dv"), (13, "dg"), (14, "dbeta")]:
+        bad = list(ptrs)
+        bad[i] = None
+        assert call(bad) == kda.KDA_ERR_INVALID_ARGUMENT, name
+        assert name in lib.kda_last_error().decode()
+    bad = list(ptrs)
+    bad[13] = P(0x10008)  # dg misaligned
+    assert call(bad) == kda.KDA_ERR_INVALID_ARGUMENT
+    bad = list(ptrs)
+    bad[11] = ptrs[1]  # dk aliases k
+    assert call(bad) == kda.KDA_ERR_INVALID_ARGUMENT
+    bad = list(ptrs)
+    bad[15] = ptrs[10]  # d_initial_state aliases dq
+    assert call(bad) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert call(ptrs, ws=None) == kda.KDA_ERR_WORKSPACE
+    assert call(ptrs, ws_bytes=1000) == kda.KDA_ERR_WORKSPACE
+    assert call(ptrs, ws=P(0x100010)) == kda.KDA_ERR_WORKSPACE  # misaligned
+    assert call(ptrs, prob=_bwd_problem(head_dim_k=96)) == kda.KDA_ERR_UNSUPPORTED
+    assert call(ptrs, prob=_bwd_problem(chunk_size=128)) == kda.KDA_ERR_UNSUPPORTED
+    # fp32 at chunk 64 with d = 128 does not fit the LDS budget
+    assert call(ptrs, prob=_bwd_problem(io_dtype=kda.KDA_F32)) == kda.KDA_ERR_UNSUPPORTED
+    # empty batch: nothing to do
+    assert call(ptrs, prob=_bwd_problem(batch=0)) == kda.KDA_OK
