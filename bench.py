@@ -8,13 +8,14 @@ One step = one pass of the hot path over one batch of synthetic input:
     128x128 updated in place).
 The prologue (kda_prologue: short convolution + Swish, q/k L2 norm, gate and beta activations)
 and the output epilogue (kda_norm_gate: per-head RMSNorm and output gate) are timed on their
-own over the prefill shapes and reported next to the step.
+own over the prefill shapes and reported next to the step, and so is the backward (kda_chunk_bwd:
+the gradients for a synthetic output gradient and final-state gradient on the prefill tensors).
 `value` is prefill tokens/s (B*T tokens per chunk_fwd launch); the decode step is
 reported in GB/s next to it.  Inputs are resident in HBM before the timed region.
 Timing uses HIP events recorded on the stream the kernels are launched on.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--algo auto|fused|two_pass] [--dv-tile T]
-                       [--no-cpu-baseline]
+                       [--no-cpu-baseline] [--no-tune]
 """
 import argparse
 import hashlib
@@ -144,6 +145,9 @@ def main():
     ap.add_argument("--chunk", type=int, default=64)
     ap.add_argument("--algo", default="auto", choices=["auto", "fused", "two_pass"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-tune", action="store_true",
+                    help="skip the autotuning sweep (profiling runs: it launches the same fused kernel "
+                         "instantiation as the backward's forward pass)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the KDA path has no multi-GPU mode (heads and sequences are "
@@ -200,7 +204,19 @@ def main():
     def epilogue():
         kda.norm_gate(eo, ez, ew, eps=1e-6, out=eout)
 
+    # ------------------------------------------- backward (training) on the prefill tensors
+    d_out_b, dsf_b = (None if x is None else x.to(dev) for x in ki.grad_inputs(inp, 8))
+    bp, _ = kda._problem_from(d["q"], d["v"], None, args.chunk, 1.0, 0, 0)
+    bws = torch.empty(kda.bwd_workspace_bytes(bp), dtype=torch.uint8, device=dev)
+    bout = kda.chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d_out_b, initial_state=d["s0"],
+                         d_final_state=dsf_b, chunk_size=args.chunk, workspace=bws)
+
+    def backward():
+        kda.chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d_out_b, initial_state=d["s0"], d_final_state=dsf_b,
+                      chunk_size=args.chunk, workspace=bws, out=bout)
+
     for _ in range(args.warmup):
+        backward()
         prefill()
         decode()
         epilogue()
@@ -214,6 +230,7 @@ def main():
     pre_med, pre_min = time_each(prefill, args.steps, stream)
     dec_med, dec_min = time_each(decode, args.steps, stream)
     t_pro = time_launches(prologue, args.steps, stream)
+    t_bwd = time_launches(backward, args.steps, stream)
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     decode()
@@ -226,7 +243,8 @@ def main():
     ms_step = start.elapsed_time(end) / args.steps
 
     # autotuning over (chunk, d_v tile, algorithm) on the prefill tensors, reported alongside
-    tuned = kda.tune(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], final_state=torch.empty_like(fin))
+    tuned = None if args.no_tune else kda.tune(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"],
+                                                final_state=torch.empty_like(fin))
     traffic = measured_traffic()
     tokens = B * T
     pre_tps = tokens / (t_pre * 1e-3)
@@ -241,6 +259,11 @@ def main():
     # prologue per (token, head): raw q, k, v (bf16) + g_raw + beta_raw read, the same written
     pro_bytes = B * T * H * 2 * ((2 * w.dk + w.dv) * 2 + 4 * w.dk + 4) + 4 * H * (2 * w.dk + w.dv) * 4
     pro_gbps = pro_bytes / (t_pro * 1e-3) / 1e9
+    # backward per (token, head): q, k, v, dO (bf16), g (fp32), beta read; dq, dk, dv (bf16), dg (fp32),
+    # dbeta written; per (sequence, head): initial state and final-state gradient read, d(initial state) written
+    bwd_bytes = B * T * H * 2 * ((2 * w.dk + w.dv) * 2 + 4 * w.dk + 4) + B * T * H * w.dv * 2 + \
+        3 * B * H * w.dk * w.dv * 4
+    bwd_gbps = bwd_bytes / (t_bwd * 1e-3) / 1e9
 
     res = {
         "metric": METRIC,
@@ -276,8 +299,13 @@ def main():
         "decode": {"ms": round(t_dec, 4), "ms_median": round(dec_med, 4), "ms_min": round(dec_min, 4),
                    "gb_per_s": round(dec_gbps, 1), "hbm_frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
                    "bytes_per_launch": dec_bytes},
-        "tuned": {"chunk": tuned["chunk_size"], "dv_tile": tuned["dv_tile"],
-                  "algo": ["auto", "fused", "two_pass"][tuned["algo"]], "ms": round(tuned["tuned_ms"], 4)},
+        "tuned": None if tuned is None else {"chunk": tuned["chunk_size"], "dv_tile": tuned["dv_tile"],
+                                             "algo": ["auto", "fused", "two_pass"][tuned["algo"]],
+                                             "ms": round(tuned["tuned_ms"], 4)},
+        "backward": {"kernel": "kda_chunk_bwd", "chunk": args.chunk, "ms": round(t_bwd, 4),
+                     "tokens_per_s": round(tokens / (t_bwd * 1e-3), 1), "gb_per_s": round(bwd_gbps, 1),
+                     "hbm_frac": round(bwd_gbps / PEAK_HBM_GBPS, 4), "bytes_per_launch": bwd_bytes,
+                     "traffic": traffic.get("backward_bytes")},
         "prologue": {"kernel": "kda_prologue", "conv_width": 4, "ms": round(t_pro, 4),
                      "gb_per_s": round(pro_gbps, 1), "hbm_frac": round(pro_gbps / PEAK_HBM_GBPS, 4),
                      "bytes_per_launch": pro_bytes, "traffic": traffic.get("prologue_bytes")},

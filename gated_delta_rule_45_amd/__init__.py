@@ -266,10 +266,11 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
               d_out: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
               d_final_state: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None, *,
               cu_seqlens_host=None, chunk_size: int = 0, scale: float = 1.0, need_d_initial_state: bool = True,
-              workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+              workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None, stream=None) -> dict:
     """Gradients of chunk_fwd for L = sum(d_out * out) + sum(d_final_state * final_state).
     Arguments as chunk_fwd; d_out has out's shape and dtype, d_final_state is [N, H, d_k, d_v]
-    fp32 or None.  Returns dict(dq, dk, dv (io dtype), dg, dbeta, d_initial_state (fp32 or None))."""
+    fp32 or None.  Returns dict(dq, dk, dv (io dtype), dg, dbeta, d_initial_state (fp32 or None));
+    `out` (a dict returned by an earlier call of the same shape) is written in place."""
     dev = q.device
     p, n = _problem_from(q, v, cu_seqlens, chunk_size, scale, 0, 0)
     B, T, H, dk = q.shape
@@ -291,11 +292,19 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
         host_cu = torch.as_tensor(cu_seqlens_host, dtype=torch.int32).contiguous().cpu()
         if host_cu.numel() != n + 1:
             raise ValueError("cu_seqlens_host has the wrong length")
-    out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
-           "dg": torch.empty((B, T, H, dk), dtype=torch.float32, device=dev),
-           "dbeta": torch.empty((B, T, H), dtype=torch.float32, device=dev),
-           "d_initial_state": torch.empty((n, H, dk, dv), dtype=torch.float32, device=dev)
-           if need_d_initial_state else None}
+    if out is None:
+        out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+               "dg": torch.empty((B, T, H, dk), dtype=torch.float32, device=dev),
+               "dbeta": torch.empty((B, T, H), dtype=torch.float32, device=dev),
+               "d_initial_state": torch.empty((n, H, dk, dv), dtype=torch.float32, device=dev)
+               if need_d_initial_state else None}
+    else:
+        for key, dt, shape in (("dq", q.dtype, (B, T, H, dk)), ("dk", q.dtype, (B, T, H, dk)),
+                               ("dv", q.dtype, (B, T, H, dv)), ("dg", torch.float32, (B, T, H, dk)),
+                               ("dbeta", torch.float32, (B, T, H))):
+            _need(out[key], key, dt, shape, dev)
+        if out.get("d_initial_state") is not None:
+            _need(out["d_initial_state"], "d_initial_state", torch.float32, (n, H, dk, dv), dev)
     if workspace is None:
         workspace = torch.empty(bwd_workspace_bytes(p), dtype=torch.uint8, device=dev)
     lib = library()
