@@ -10,6 +10,8 @@ Two independent implementations live here:
   threaded over (sequence, head) units; the definition of the operator.
 * ``bwd``: its gradients for a loss linear in the outputs and the final state, by the
   chain rule through the same recurrence, token by token in reverse (``kda_oracle.c``).
+* ``dplr_fwd``: the general diagonal-plus-low-rank recurrence KDA specialises ("Less
+  compute than general DPLR" section), token by token (``kda_oracle.c``); the comparator.
 * ``chunkwise.py``: the chunkwise form (WY/UT transform, forward-substitution
   inverse, inter-chunk state passing) in numpy fp64, used to pin that the chunk
   algebra reaches the recurrence exactly.
@@ -64,6 +66,10 @@ def _load(path: str = LIB_PATH):
     b.restype = ctypes.c_int
     b.argtypes = [ctypes.c_int64, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
                   P, P, P, P, P, P, P, P, ctypes.c_int, P, P, P, P, P, P, P, ctypes.c_int]
+    d = lib.kda_oracle_dplr_fwd
+    d.restype = ctypes.c_int
+    d.argtypes = [ctypes.c_int64, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                  P, P, P, P, P, P, P, P, P, ctypes.c_int]
     _libs[path] = lib
     return lib
 
@@ -203,3 +209,29 @@ def bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray, beta: np.nda
     if rc != 0:
         raise RuntimeError(f"kda_oracle_bwd failed with code {rc}")
     return out
+
+
+def dplr_fwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, a: np.ndarray, b: np.ndarray, g: np.ndarray, *,
+             initial_state: Optional[np.ndarray] = None, cu_seqlens: Optional[np.ndarray] = None,
+             scale: float = 1.0, threads: Optional[int] = None, lib_path: str = LIB_PATH):
+    """General DPLR recurrence in fp64: S_t = (Diag(exp g_t) + a_t b_t^T) S_{t-1} + k_t v_t^T,
+    o_t = scale S_t^T q_t.  q, k, a, b: [B, T, H, dk]; v: [B, T, H, dv] (all float32, or all
+    uint16 bf16 bits); g: [B, T, H, dk] float32.  Returns (o [B, T, H, dv], final [N, H, dk, dv])."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    io = _io_kind(q, k, v, a, b)
+    q, k, v, a, b = (np.ascontiguousarray(x) for x in (q, k, v, a, b))
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    assert k.shape == q.shape == a.shape == b.shape == g.shape and v.shape[:3] == q.shape[:3]
+    starts, lens = _seq_layout(B, T, cu_seqlens)
+    N = len(starts)
+    s0 = None if initial_state is None else np.ascontiguousarray(initial_state, dtype=np.float32)
+    assert s0 is None or s0.shape == (N, H, dk, dv)
+    o = np.zeros((B, T, H, dv))
+    fin = np.zeros((N, H, dk, dv))
+    rc = _load(lib_path).kda_oracle_dplr_fwd(N, _ptr(starts), _ptr(lens), H, dk, dv, io, float(scale), _ptr(q),
+                                             _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(g), _ptr(s0), _ptr(o),
+                                             _ptr(fin), threads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_dplr_fwd failed with code {rc}")
+    return o, fin

@@ -180,3 +180,46 @@ def bwd_one(q, k, v, g, beta, S0: Optional[np.ndarray], d_out, d_final: Optional
         dS = np.exp(G[-1])[:, None] * dS + scale * o["Qt"].T @ do - o["Kt"].T @ dY
     out["d_initial_state"] = dS
     return out
+
+
+def dplr_chunk_step(q, k, v, a, b, g, S, scale: float = 1.0):
+    """One chunk of the general DPLR recurrence S_i = (Diag(e^{g_i}) + a_i b_i^T) S_{i-1} + k_i v_i^T
+    (fp64; q, k, a, b, g [C, dk]; v [C, dv]; S [dk, dv]).  Returns (O [C, dv], S_next).
+
+    Unrolling the chunk from its initial state S with G = cumsum(g):
+        S_r = Diag(e^{G_r}) S + sum_{i<=r} Diag(e^{G_r - G_i}) (a_i u_i + k_i v_i),  u_i = b_i^T S_{i-1}.
+    With Bt_r = b_r e^{G_{r-1}} (G_{-1} = 0), Qt = q e^{G}, Ah = a e^{-G}, Kh = k e^{-G},
+    Ab = a e^{G_C - G}, Kb = k e^{G_C - G}, the four chunk matrices are
+        M_ba = strictly_lower(Bt Ah^T)    M_bk = strictly_lower(Bt Kh^T)
+        M_qa = lower_incl(Qt Ah^T)        M_qk = lower_incl(Qt Kh^T)
+    and
+        U  = (I - M_ba)^{-1} (Bt S + M_bk V)           (the low-rank read-outs u_i)
+        O  = scale (Qt S + M_qa U + M_qk V)
+        S' = Diag(e^{G_C}) S + Ab^T U + Kb^T V
+    KDA ties a = -beta k, b = e^{g} k and writes with beta k, so M_ba and M_bk (and M_qa and
+    M_qk) collapse into one matrix each ("Less compute than general DPLR" section)."""
+    C = q.shape[0]
+    G = np.cumsum(g, axis=0)
+    Gp = np.vstack([np.zeros((1, G.shape[1])), G[:-1]])
+    Bt, Qt = b * np.exp(Gp), q * np.exp(G)
+    Ah, Kh = a * np.exp(-G), k * np.exp(-G)
+    Ab, Kb = a * np.exp(G[-1] - G), k * np.exp(G[-1] - G)
+    Mba, Mbk = np.tril(Bt @ Ah.T, -1), np.tril(Bt @ Kh.T, -1)
+    Mqa, Mqk = np.tril(Qt @ Ah.T), np.tril(Qt @ Kh.T)
+    Xinv = forward_substitution_inverse(np.eye(C) - Mba)
+    U = Xinv @ (Bt @ S + Mbk @ v)
+    O = scale * (Qt @ S + Mqa @ U + Mqk @ v)
+    S_next = np.exp(G[-1])[:, None] * S + Ab.T @ U + Kb.T @ v
+    return O, S_next
+
+
+def dplr_fwd_one(q, k, v, a, b, g, S0: Optional[np.ndarray], chunk: int, scale: float = 1.0):
+    """One (sequence, head) of the general DPLR recurrence, chunk by chunk."""
+    T, dk = q.shape
+    dv = v.shape[1]
+    S = np.zeros((dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    O = np.zeros((T, dv))
+    for c0 in range(0, T, chunk):
+        sl = slice(c0, min(c0 + chunk, T))
+        O[sl], S = dplr_chunk_step(q[sl], k[sl], v[sl], a[sl], b[sl], g[sl], S, scale)
+    return O, S

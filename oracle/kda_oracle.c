@@ -508,4 +508,149 @@ int kda_oracle_bwd(int64_t num_seqs, const int64_t *starts, const int64_t *lens,
     return 0;
 }
 
+/* ------------------------------------------------------- general DPLR comparator --
+ *
+ * The general diagonal-plus-low-rank recurrence that KDA specialises (Kimi Linear summary
+ * page, "Less compute than general DPLR" section: both support fine-grained decay; KDA
+ * ties both low-rank vectors to the key):
+ *
+ *   S_t = (Diag(exp(g_t)) + a_t b_t^T) S_{t-1} + k_t v_t^T,     o_t = scale * S_t^T q_t
+ *
+ * with independent per-token vectors a_t, b_t (d_k).  KDA is the case a = -beta k,
+ * b = exp(g) * k and a write key beta k.  Same layouts as kda_oracle_fwd; a and b share
+ * the io dtype of q and k.
+ */
+typedef struct {
+    int64_t num_seqs;
+    const int64_t *starts, *lens;
+    int H, dk, dv, io_bf16;
+    double scale;
+    const void *q, *k, *v, *a, *b;
+    const float *g, *s0;
+    double *o, *s_final;
+    int64_t next_unit;
+    pthread_mutex_t lock;
+} djob_t;
+
+static void run_unit_dplr(djob_t *J, int64_t unit, double *S, double *buf) {
+    const int64_t n = unit / J->H;
+    const int h = (int)(unit % J->H);
+    const int H = J->H, dk = J->dk, dv = J->dv;
+    const int dmax = dk > dv ? dk : dv;
+    double *qv = buf, *kv = buf + dmax, *av = buf + 2 * dmax, *bv = buf + 3 * dmax, *al = buf + 4 * dmax,
+           *vv = buf + 5 * dmax, *u = buf + 6 * dmax;
+    if (J->s0) {
+        const float *src = J->s0 + ((n * H + h) * (int64_t)dk) * dv;
+        for (int64_t e = 0; e < (int64_t)dk * dv; ++e) S[e] = (double)src[e];
+    } else {
+        memset(S, 0, sizeof(double) * (size_t)dk * dv);
+    }
+    const int64_t t0 = J->starts[n], len = J->lens[n];
+    for (int64_t t = t0; t < t0 + len; ++t) {
+        const int64_t row_k = (t * H + h) * (int64_t)dk, row_v = (t * H + h) * (int64_t)dv;
+        for (int i = 0; i < dk; ++i) {
+            qv[i] = load_io(J->q, J->io_bf16, row_k + i);
+            kv[i] = load_io(J->k, J->io_bf16, row_k + i);
+            av[i] = load_io(J->a, J->io_bf16, row_k + i);
+            bv[i] = load_io(J->b, J->io_bf16, row_k + i);
+            al[i] = exp((double)J->g[row_k + i]);
+        }
+        for (int j = 0; j < dv; ++j) vv[j] = load_io(J->v, J->io_bf16, row_v + j);
+        /* u = b^T S_{t-1} (uses the state before the decay) */
+        for (int j = 0; j < dv; ++j) u[j] = 0.0;
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j) u[j] += bv[i] * S[(int64_t)i * dv + j];
+#if KDA_ORACLE_MUTANT == 21 /* planted: low-rank term against the decayed state */
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j) S[(int64_t)i * dv + j] *= al[i];
+        for (int j = 0; j < dv; ++j) u[j] = 0.0;
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j) u[j] += bv[i] * S[(int64_t)i * dv + j];
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j) S[(int64_t)i * dv + j] += av[i] * u[j] + kv[i] * vv[j];
+#else
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j)
+                S[(int64_t)i * dv + j] = al[i] * S[(int64_t)i * dv + j] + av[i] * u[j] + kv[i] * vv[j];
+#endif
+        for (int j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < dk; ++i) acc += S[(int64_t)i * dv + j] * qv[i];
+            J->o[(t * H + h) * (int64_t)dv + j] = J->scale * acc;
+        }
+    }
+    if (J->s_final) memcpy(J->s_final + ((n * H + h) * (int64_t)dk) * dv, S, sizeof(double) * (size_t)dk * dv);
+}
+
+static void *worker_dplr(void *arg) {
+    djob_t *J = (djob_t *)arg;
+    const int dmax = J->dk > J->dv ? J->dk : J->dv;
+    double *S = (double *)malloc(sizeof(double) * (size_t)J->dk * J->dv);
+    double *buf = (double *)malloc(sizeof(double) * (size_t)dmax * 7);
+    if (!S || !buf) {
+        free(S);
+        free(buf);
+        return (void *)1;
+    }
+    const int64_t units = J->num_seqs * J->H;
+    for (;;) {
+        pthread_mutex_lock(&J->lock);
+        const int64_t u = J->next_unit++;
+        pthread_mutex_unlock(&J->lock);
+        if (u >= units) break;
+        run_unit_dplr(J, u, S, buf);
+    }
+    free(S);
+    free(buf);
+    return NULL;
+}
+
+/* General DPLR forward, token by token (fp64).  o [tokens, H, dv]; s_final
+ * [num_seqs, H, dk, dv] or NULL.  Returns 0, -1 (arguments) or -2 (memory / threads). */
+int kda_oracle_dplr_fwd(int64_t num_seqs, const int64_t *starts, const int64_t *lens, int H, int dk, int dv,
+                        int io_bf16, double scale, const void *q, const void *k, const void *v, const void *a,
+                        const void *b, const float *g, const float *s0, double *o, double *s_final, int nthreads) {
+    if (num_seqs < 0 || H <= 0 || dk <= 0 || dv <= 0 || !o || !starts || !lens) return -1;
+    if (num_seqs > 0 && (!q || !k || !v || !a || !b || !g)) return -1;
+    djob_t J;
+    memset(&J, 0, sizeof J);
+    J.num_seqs = num_seqs;
+    J.starts = starts;
+    J.lens = lens;
+    J.H = H;
+    J.dk = dk;
+    J.dv = dv;
+    J.io_bf16 = io_bf16;
+    J.scale = scale;
+    J.q = q;
+    J.k = k;
+    J.v = v;
+    J.a = a;
+    J.b = b;
+    J.g = g;
+    J.s0 = s0;
+    J.o = o;
+    J.s_final = s_final;
+    pthread_mutex_init(&J.lock, NULL);
+    if (nthreads < 1) nthreads = 1;
+    const int64_t units = num_seqs * H;
+    if (nthreads > units) nthreads = units > 0 ? (int)units : 1;
+    pthread_t *tid = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    if (!tid) return -2;
+    int started = 0, rc = 0;
+    for (int i = 0; i < nthreads; ++i) {
+        if (pthread_create(&tid[i], NULL, worker_dplr, &J) != 0) break;
+        ++started;
+    }
+    if (started == 0) rc = -2;
+    for (int i = 0; i < started; ++i) {
+        void *res = NULL;
+        pthread_join(tid[i], &res);
+        if (res) rc = -2;
+    }
+    free(tid);
+    pthread_mutex_destroy(&J.lock);
+    return rc;
+}
+
 int kda_oracle_mutant(void) { return KDA_ORACLE_MUTANT; }
