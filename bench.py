@@ -136,6 +136,39 @@ def cpu_baseline(inp):
             "decode_ms_per_step": round(ddt * 1e3, 2)}
 
 
+def dplr_sweep(kda, ki, torch, dev, stream, steps):
+    """KDA (fused and two-pass) against the general-DPLR comparator over sequence lengths,
+    4 sequences x 16 heads, d = 128, chunk 64, bf16."""
+    rows = []
+    for T in (1024, 4096, 16384):
+        inp = ki.make_inputs(4, T, 16, 128, 128, "bf16", seed=11)
+        t = {k: x.to(dev) for k, x in dict(q=inp.q, k=inp.k, v=inp.v, g=inp.g, beta=inp.beta, s0=inp.s0).items()}
+        a, b, kw = (x.to(dev) for x in ki.dplr_inputs(inp, 9))
+        o = torch.empty_like(t["v"])
+        f = torch.empty_like(t["s0"])
+        ws = torch.empty(max(kda.query(4, T, 16, 128, 128, "bf16", chunk_size=64)["workspace_bytes"], 1),
+                         dtype=torch.uint8, device=dev)
+        calls = {
+            "dplr_fused": lambda: kda.dplr_chunk_fwd(t["q"], kw, t["v"], a, b, t["g"], t["s0"], chunk_size=64,
+                                                     dv_tile=32, out=o, final_state=f),
+            "kda_fused": lambda: kda.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["s0"], chunk_size=64,
+                                               dv_tile=32, algo="fused", out=o, final_state=f),
+            "kda_two_pass": lambda: kda.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], t["s0"], chunk_size=64,
+                                                  algo="two_pass", workspace=ws, out=o, final_state=f),
+        }
+        row = {"T": T}
+        for name, fn in calls.items():
+            fn()
+            row[name + "_ms"] = round(time_launches(fn, max(3, steps // 4), stream), 4)
+        row["kda_speedup_same_design"] = round(row["dplr_fused_ms"] / row["kda_fused_ms"], 3)
+        row["kda_speedup_vs_default"] = round(row["dplr_fused_ms"] / row["kda_two_pass_ms"], 3)
+        log(f"dplr sweep T={T}: {row}")
+        rows.append(row)
+        del t, a, b, kw, o, f, ws
+        torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -145,6 +178,8 @@ def main():
     ap.add_argument("--chunk", type=int, default=64)
     ap.add_argument("--algo", default="auto", choices=["auto", "fused", "two_pass"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dplr-sweep", action="store_true",
+                    help="also time the general-DPLR comparator against KDA over sequence lengths 1K..16K")
     ap.add_argument("--no-tune", action="store_true",
                     help="skip the autotuning sweep (profiling runs: it launches the same fused kernel "
                          "instantiation as the backward's forward pass)")
@@ -215,7 +250,21 @@ def main():
         kda.chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d_out_b, initial_state=d["s0"], d_final_state=dsf_b,
                       chunk_size=args.chunk, workspace=bws, out=bout)
 
+    # ------------------------------------------- general-DPLR comparator on the prefill tensors
+    a_d, b_d, kw_d = (x.to(dev) for x in ki.dplr_inputs(inp, 9))
+    cmp_out, cmp_fin = torch.empty_like(out), torch.empty_like(fin)
+
+    def dplr_fused():
+        kda.dplr_chunk_fwd(d["q"], kw_d, d["v"], a_d, b_d, d["g"], d["s0"], chunk_size=64, dv_tile=32, out=cmp_out,
+                           final_state=cmp_fin)
+
+    def kda_fused():
+        kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], chunk_size=64, dv_tile=32, algo="fused",
+                      out=cmp_out, final_state=cmp_fin)
+
     for _ in range(args.warmup):
+        dplr_fused()
+        kda_fused()
         backward()
         prefill()
         decode()
@@ -231,6 +280,8 @@ def main():
     dec_med, dec_min = time_each(decode, args.steps, stream)
     t_pro = time_launches(prologue, args.steps, stream)
     t_bwd = time_launches(backward, args.steps, stream)
+    t_dplr = time_launches(dplr_fused, args.steps, stream)
+    t_kfused = time_launches(kda_fused, args.steps, stream)
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     decode()
@@ -306,6 +357,11 @@ def main():
                      "tokens_per_s": round(tokens / (t_bwd * 1e-3), 1), "gb_per_s": round(bwd_gbps, 1),
                      "hbm_frac": round(bwd_gbps / PEAK_HBM_GBPS, 4), "bytes_per_launch": bwd_bytes,
                      "traffic": traffic.get("backward_bytes")},
+        "dplr_comparator": {"shape": "prefill", "chunk": 64, "dv_tile": 32,
+                            "dplr_fused_ms": round(t_dplr, 4), "kda_fused_ms": round(t_kfused, 4),
+                            "kda_two_pass_ms": round(t_pre, 4),
+                            "kda_speedup_same_design": round(t_dplr / t_kfused, 3),
+                            "kda_speedup_vs_default": round(t_dplr / t_pre, 3)},
         "prologue": {"kernel": "kda_prologue", "conv_width": 4, "ms": round(t_pro, 4),
                      "gb_per_s": round(pro_gbps, 1), "hbm_frac": round(pro_gbps / PEAK_HBM_GBPS, 4),
                      "bytes_per_launch": pro_bytes, "traffic": traffic.get("prologue_bytes")},
@@ -313,6 +369,8 @@ def main():
                      "gb_per_s": round(epi_gbps, 1), "hbm_frac": round(epi_gbps / PEAK_HBM_GBPS, 4),
                      "bytes_per_launch": epi_bytes, "traffic": traffic.get("epilogue_bytes")},
     }
+    if args.dplr_sweep:
+        res["dplr_sweep"] = dplr_sweep(kda, ki, torch, dev, stream, args.steps)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on the prefill batch ...")
         res["cpu_baseline"] = cpu_baseline(inp)

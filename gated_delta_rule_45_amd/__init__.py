@@ -22,7 +22,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_bwd", "recurrent_fwd", "decode_step", "prologue", "norm_gate", "query", "tune", "KdaError",
+__all__ = ["chunk_fwd", "chunk_bwd", "dplr_chunk_fwd", "recurrent_fwd", "decode_step", "prologue", "norm_gate", "query", "tune", "KdaError",
            "LIB_PATH", "library"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
@@ -90,6 +90,8 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_prologue.argtypes = [ctypes.POINTER(PrologueProblem)] + [_P] * 17
     lib.kda_norm_gate.restype = ctypes.c_int
     lib.kda_norm_gate.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int, ctypes.c_float, _P, _P, _P, _P, _P]
+    lib.kda_dplr_chunk_fwd.restype = ctypes.c_int
+    lib.kda_dplr_chunk_fwd.argtypes = [ctypes.POINTER(Problem)] + [_P] * 12
     lib.kda_chunk_bwd.restype = ctypes.c_int
     lib.kda_chunk_bwd.argtypes = [ctypes.POINTER(Problem)] + [_P] * 17 + [ctypes.c_size_t, _P]
     lib.kda_chunk_bwd_workspace.restype = ctypes.c_int
@@ -315,6 +317,42 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
                            ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream_handle(dev, stream))
     _check(st)
     return out
+
+
+def dplr_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, a: torch.Tensor, b: torch.Tensor,
+                   g: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+                   cu_seqlens: Optional[torch.Tensor] = None, *, cu_seqlens_host=None, chunk_size: int = 0,
+                   scale: float = 1.0, dv_tile: int = 0, out: Optional[torch.Tensor] = None,
+                   final_state: Optional[torch.Tensor] = None, output_final_state: bool = True, stream=None):
+    """General-DPLR comparator: S_t = (Diag(exp g_t) + a_t b_t^T) S_{t-1} + k_t v_t^T, o_t = scale S_t^T q_t.
+    q, k, a, b: [B, T, H, d_k]; v: [B, T, H, d_v] (same dtype); g fp32 [B, T, H, d_k].
+    Returns (out, final_state)."""
+    dev = q.device
+    p, n = _problem_from(q, v, cu_seqlens, chunk_size, scale, dv_tile, 0)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    for t, name in ((q, "q"), (k, "k"), (a, "a"), (b, "b")):
+        _need(t, name, q.dtype, (B, T, H, dk), dev)
+    _need(v, "v", q.dtype, (B, T, H, dv), dev)
+    _need(g, "g", torch.float32, (B, T, H, dk), dev)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (n, H, dk, dv), dev)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, (n + 1,), dev)
+    host_cu = None
+    if cu_seqlens_host is not None:
+        host_cu = torch.as_tensor(cu_seqlens_host, dtype=torch.int32).contiguous().cpu()
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    _need(out, "out", q.dtype, (B, T, H, dv), dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((n, H, dk, dv), dtype=torch.float32, device=dev)
+    st = library().kda_dplr_chunk_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(g),
+                                      _ptr(initial_state), _ptr(cu_seqlens),
+                                      None if host_cu is None else ctypes.c_void_p(host_cu.data_ptr()), _ptr(out),
+                                      _ptr(final_state), _stream_handle(dev, stream))
+    _check(st)
+    return out, final_state
 
 
 def tune(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,

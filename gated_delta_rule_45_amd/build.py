@@ -14,12 +14,19 @@ LIB = os.path.join(HERE, "libkda.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
 SOURCES = ["kda_api.cpp", "kda_recurrent.hip", "kda_chunk_bf16.hip", "kda_chunk_f32.hip", "kda_split_bf16.hip",
-           "kda_split_f32.hip", "kda_epilogue.hip", "kda_prologue.hip", "kda_bwd_bf16.hip", "kda_bwd_f32.hip"]
+           "kda_split_f32.hip", "kda_epilogue.hip", "kda_prologue.hip", "kda_bwd_bf16.hip", "kda_bwd_f32.hip",
+           "kda_dplr.hip"]
 ARCH = "gfx950"
 # Packed fp32 VALU ops are disabled for every device pass.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall",
           "-Wno-unused-command-line-argument"]
+# Per-source code-generation flags.  The general-DPLR kernel is built with MFMA destinations
+# and accumulator inputs in ordinary VGPRs: built with them in accumulation registers
+# (the compiler's default at its register pressure), its bf16 variants with chunks of 32 and
+# 64 computed wrong low-rank read-outs (a deterministic, schedule-dependent error that no
+# operand explained and that s_nop padding did not remove).
+EXTRA = {"kda_dplr.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc() -> str:
@@ -29,7 +36,7 @@ def _hipcc() -> str:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *COMMON, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *COMMON, *DEVICE_FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)

@@ -452,6 +452,44 @@ kda_status_t kda_chunk_bwd(const kda_problem_t *problem, const void *q, const vo
     }
 }
 
+kda_status_t kda_dplr_chunk_fwd(const kda_problem_t *problem, const void *q, const void *k, const void *v,
+                                const void *a, const void *b, const float *g, const float *initial_state,
+                                const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, void *out,
+                                float *final_state, void *stream) {
+    try {
+        Resolved r;
+        kda_status_t st = resolve(problem, cu_seqlens != nullptr, r, false);
+        if (st != KDA_OK) return st;
+        const int C = problem->chunk_size ? problem->chunk_size : 64;
+        const int dvt = problem->dv_tile ? problem->dv_tile : 32;
+        if (dvt > problem->head_dim_v)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "dv_tile %d exceeds d_v %d", dvt, problem->head_dim_v);
+        if (!kda::dplr_variant_supported(problem->io_dtype, problem->head_dim_k, dvt, C))
+            return fail(KDA_ERR_UNSUPPORTED, "dplr: no compiled variant for io=%s d_k=%d dv_tile=%d chunk=%d",
+                        problem->io_dtype == KDA_BF16 ? "bf16" : "fp32", problem->head_dim_k, dvt, C);
+        // q, k, v, g, out checks as the forward (beta is not an input here: g stands in for it)
+        st = check_tensors(problem, r, q, k, v, g, g, initial_state, cu_seqlens, cu_seqlens_host, out, final_state);
+        if (st != KDA_OK) return st;
+        if (r.tokens > 0) {
+            if (!a || !b) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is NULL", !a ? "a" : "b");
+            if (!aligned(a, 16) || !aligned(b, 16))
+                return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", !aligned(a, 16) ? "a" : "b");
+        }
+        const void *outs[] = {out, final_state};
+        for (const void *o : outs)
+            if (o && (o == a || o == b)) return fail(KDA_ERR_INVALID_ARGUMENT, "an output aliases a or b");
+        if (r.num_seqs == 0) return ok();
+        kda::DplrParams dp;
+        dp.f = make_params(problem, r, q, k, v, g, nullptr, initial_state, cu_seqlens, out, final_state);
+        dp.a = a;
+        dp.b = b;
+        return hip_status(kda::launch_dplr_fwd(problem->io_dtype, dp, dvt, C, static_cast<hipStream_t>(stream)),
+                          "kda_dplr_chunk_fwd launch");
+    } catch (...) {
+        return fail(KDA_ERR_HIP, "unexpected exception in kda_dplr_chunk_fwd");
+    }
+}
+
 kda_status_t kda_tune(const kda_problem_t *problem, const void *q, const void *k, const void *v, const float *g,
                       const float *beta, const float *initial_state, const int32_t *cu_seqlens,
                       const int32_t *cu_seqlens_host, void *out, float *final_state, void *workspace,

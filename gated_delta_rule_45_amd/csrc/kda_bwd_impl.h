@@ -40,6 +40,7 @@
 
 #include <type_traits>
 
+#include "kda_chunk_impl.h"
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -226,31 +227,20 @@ __global__ void __launch_bounds__(kChunkThreads) kda_bwd_scan_kernel(BwdParams b
         const int64_t tok0 = start + c0;
 
         // ================= 1: gate scan (log2 domain), stage dO and beta
-        float G[KT][4], kr[KT][4], qr[KT][4];
+        // (k and q stay packed in the raw registers; phases 3 and 4 unpack them where used)
+        float G[KT][4];
+        const bool valid = 16 * wave + l16 < clen;
         if (wave < NSUB) {
             const int R = wave;
-            const bool valid = 16 * R + l16 < clen;
 #pragma unroll
             for (int ct = 0; ct < KT; ++ct) {
                 const int c = 16 * ct + 4 * q4;
                 const float4 gv = raw.g[ct];
-                float4 kv, qv;
-                if constexpr (BF) {
-                    kv = make_float4(bf16_lo(raw.k[ct].x), bf16_hi(raw.k[ct].x), bf16_lo(raw.k[ct].y), bf16_hi(raw.k[ct].y));
-                    qv = make_float4(bf16_lo(raw.q[ct].x), bf16_hi(raw.q[ct].x), bf16_lo(raw.q[ct].y), bf16_hi(raw.q[ct].y));
-                } else {
-                    kv = raw.k[ct];
-                    qv = raw.q[ct];
-                }
                 const float m = valid ? kLog2e : 0.f;
                 G[ct][0] = scan16_add(gv.x * m);
                 G[ct][1] = scan16_add(gv.y * m);
                 G[ct][2] = scan16_add(gv.z * m);
                 G[ct][3] = scan16_add(gv.w * m);
-                kr[ct][0] = valid ? kv.x : 0.f; kr[ct][1] = valid ? kv.y : 0.f;
-                kr[ct][2] = valid ? kv.z : 0.f; kr[ct][3] = valid ? kv.w : 0.f;
-                qr[ct][0] = valid ? qv.x : 0.f; qr[ct][1] = valid ? qv.y : 0.f;
-                qr[ct][2] = valid ? qv.z : 0.f; qr[ct][3] = valid ? qv.w : 0.f;
                 if (l16 == 15)
                     *reinterpret_cast<float4 *>(sTot + R * DK + c) = make_float4(G[ct][0], G[ct][1], G[ct][2], G[ct][3]);
             }
@@ -310,20 +300,18 @@ __global__ void __launch_bounds__(kChunkThreads) kda_bwd_scan_kernel(BwdParams b
                 const float ebv[4] = {eb.x, eb.y, eb.z, eb.w};
                 const float edv[4] = {ed.x, ed.y, ed.z, ed.w};
                 const float ecv[4] = {ec.x, ec.y, ec.z, ec.w};
+                const float4 kv = unpack4<BF>(raw.k[ct]), qv = unpack4<BF>(raw.q[ct]);
+                const float kx[4] = {kv.x, kv.y, kv.z, kv.w}, qx[4] = {qv.x, qv.y, qv.z, qv.w};
                 float kb[4], kt[4], qt[4], kbar[4], kd[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float fr = fast_exp2(G[ct][j]);
-                    const float fb = fast_exp2(tv[j] - G[ct][j]);
-                    const float krow = kr[ct][j] * fr;
-                    const float qrow = qr[ct][j] * fr;
-                    kb[j] = kr[ct][j] * fb;
+                    const float fr = valid ? fast_exp2(G[ct][j]) : 0.f;
+                    const float fb = valid ? fast_exp2(tv[j] - G[ct][j]) : 0.f;
+                    kb[j] = kx[j] * fb;
                     kd[j] = kb[j] * edv[j];
-                    kt[j] = krow * ebv[j];
-                    qt[j] = qrow * ebv[j];
+                    kt[j] = kx[j] * fr * ebv[j];
+                    qt[j] = qx[j] * fr * ebv[j];
                     kbar[j] = kb[j] * ecv[j];
-                    kr[ct][j] = krow;
-                    qr[ct][j] = qrow;
                 }
                 kdiag[ct] = make_frag<BF>(kd[0], kd[1], kd[2], kd[3]);
                 const Frag<BF> fkb = make_frag<BF>(kb[0], kb[1], kb[2], kb[3]);
@@ -357,8 +345,12 @@ __global__ void __launch_bounds__(kChunkThreads) kda_bwd_scan_kernel(BwdParams b
             Frag<BF> ka[KT], qa[KT];
 #pragma unroll
             for (int ct = 0; ct < KT; ++ct) {
-                ka[ct] = make_frag<BF>(kr[ct][0], kr[ct][1], kr[ct][2], kr[ct][3]);
-                qa[ct] = make_frag<BF>(qr[ct][0], qr[ct][1], qr[ct][2], qr[ct][3]);
+                const float4 kv = unpack4<BF>(raw.k[ct]), qv = unpack4<BF>(raw.q[ct]);
+                float fr[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) fr[j] = valid ? fast_exp2(G[ct][j]) : 0.f;
+                ka[ct] = make_frag<BF>(kv.x * fr[0], kv.y * fr[1], kv.z * fr[2], kv.w * fr[3]);
+                qa[ct] = make_frag<BF>(qv.x * fr[0], qv.y * fr[1], qv.z * fr[2], qv.w * fr[3]);
             }
 #pragma unroll
             for (int I = 0; I < NSUB; ++I) {

@@ -92,6 +92,14 @@ hipError_t launch_bwd_f32(const BwdParams &bp, int chunk, hipStream_t stream);
 hipError_t launch_chunk_plan(const int32_t *cu, int32_t num_seqs, int32_t chunk, int32_t *chunk_off,
                              hipStream_t stream);
 
+// General-DPLR comparator (kda_dplr.hip).
+struct DplrParams {
+    FwdParams f;        // q, k (write key), v, g, s0, cu, out, sf, sizes, scale (f.beta unused)
+    const void *a, *b;  // [tokens, H, DK] io dtype
+};
+bool dplr_variant_supported(kda_dtype_t io, int dk, int dvt, int chunk);
+hipError_t launch_dplr_fwd(kda_dtype_t io, const DplrParams &dp, int dvt, int chunk, hipStream_t stream);
+
 // Prologue (short convolution + Swish, q/k L2 normalisation, gate and beta activations).
 hipError_t launch_prologue(kda_dtype_t io, int64_t tokens, int32_t num_seqs, int32_t seq_len, int32_t H, int32_t dk,
                            int32_t dv, int32_t W, const int32_t *cu, float eps, const void *const raw[3],

@@ -158,6 +158,26 @@ kda_status_t kda_chunk_bwd(const kda_problem_t *problem, const void *q, const vo
                            float *d_initial_state, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * kda_dplr_chunk_fwd -- the general DPLR recurrence that KDA specialises, evaluated with the
+ * same chunked single-pass kernel design as KDA's fused forward; a comparator for the
+ * operator-speed claim of the Kimi Linear summary page ("Less compute than general DPLR"
+ * section: KDA ties both low-rank vectors of the transition to the key, which leaves two
+ * C x C chunk matrices instead of four and three fewer matrix products).
+ *
+ *     S_t = (Diag(exp(g_t)) + a_t b_t^T) S_{t-1} + k_t v_t^T,     o_t = scale * S_t^T q_t
+ *
+ *  a, b            [tokens, H, d_k] io dtype (the two low-rank vectors); k is the write key.
+ *  Everything else as kda_chunk_fwd (no beta: KDA's beta is folded into a and k).
+ *  problem->chunk_size: 16, 32 or 64 (0 = 64); problem->dv_tile: 32 or 64 (0 = 32);
+ *  problem->algo is ignored.  Needs no workspace.
+ * KDA is the case a = -beta k, b = exp(g) * k with write key beta k.
+ */
+kda_status_t kda_dplr_chunk_fwd(const kda_problem_t *problem, const void *q, const void *k, const void *v,
+                                const void *a, const void *b, const float *g, const float *initial_state,
+                                const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, void *out,
+                                float *final_state, void *stream);
+
+/*
  * kda_chunk_bwd_workspace -- workspace bytes kda_chunk_bwd needs for `problem` (packed
  * batch when problem->num_seqs > 0, as in kda_query).  Writes *bytes; returns
  * KDA_ERR_UNSUPPORTED (and *bytes = 0) for problems kda_chunk_bwd does not support.

@@ -225,3 +225,20 @@ def grad_inputs(inp: Inputs, seed: int, *, dsf_std: Optional[float] = 0.1):
     if dsf_std is not None:
         dsf = dsf_std * torch.randn(inp.num_seqs, H, inp.q.shape[-1], dv, generator=gen)
     return d_out, dsf
+
+
+def dplr_inputs(inp: Inputs, seed: int):
+    """Low-rank vectors and write key for the general-DPLR comparator on the tensors of `inp`.
+    Draws, in order: a removal direction kappa = randn / |randn| over d_k (independent of the
+    write key), lam, sig ~ U[0.5, 1] per (token, head, channel).  Returns
+    a = -beta * lam * kappa, b = sig * kappa and the write key beta * k (cast to the io dtype).
+    The transition's rank-1 part has b . a in [-beta, 0], so Diag(e^g) + a b^T stays
+    contractive; with kappa = k, lam = 1 and sig = e^{g} the vectors would be KDA's."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    k = inp.k.float()
+    kappa = _unit_rows(torch.randn(k.shape, generator=gen))
+    lam = 0.5 + 0.5 * torch.rand(k.shape, generator=gen)
+    sig = 0.5 + 0.5 * torch.rand(k.shape, generator=gen)
+    beta = inp.beta[..., None]
+    dt = inp.q.dtype
+    return (-beta * lam * kappa).to(dt), (sig * kappa).to(dt), (beta * k).to(dt)

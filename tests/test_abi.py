@@ -307,3 +307,22 @@ def test_bwd_validation():
     assert call(ptrs, prob=_bwd_problem(io_dtype=kda.KDA_F32)) == kda.KDA_ERR_UNSUPPORTED
     # empty batch: nothing to do
     assert call(ptrs, prob=_bwd_problem(batch=0)) == kda.KDA_OK
+
+
+def test_dplr_validation():
+    lib = kda.library()
+    P = lambda a: ctypes.c_void_p(a)
+    ptrs = [P(0x10000 * (i + 1)) for i in range(6)] + [None, None, None, P(0x90000), None]
+    # q k v a b g s0 cu cu_host out sf
+    call = lambda prob, pp: lib.kda_dplr_chunk_fwd(ctypes.byref(prob), *pp, None)
+    assert call(_bwd_problem(chunk_size=48), ptrs) == kda.KDA_ERR_UNSUPPORTED
+    assert call(_bwd_problem(dv_tile=128), ptrs) == kda.KDA_ERR_UNSUPPORTED
+    for i, name in [(3, "a"), (4, "b")]:
+        bad = list(ptrs)
+        bad[i] = None
+        assert call(_bwd_problem(), bad) == kda.KDA_ERR_INVALID_ARGUMENT
+        assert name in lib.kda_last_error().decode()
+    bad = list(ptrs)
+    bad[9] = ptrs[3]  # out aliases a
+    assert call(_bwd_problem(), bad) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert call(_bwd_problem(batch=0), ptrs) == kda.KDA_OK
