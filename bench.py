@@ -15,7 +15,7 @@ reported in GB/s next to it.  Inputs are resident in HBM before the timed region
 Timing uses HIP events recorded on the stream the kernels are launched on.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--algo auto|fused|two_pass] [--dv-tile T]
-                       [--no-cpu-baseline] [--no-tune]
+                       [--no-cpu-baseline] [--no-tune] [--no-compare] [--dplr-sweep]
 """
 import argparse
 import hashlib
@@ -180,6 +180,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dplr-sweep", action="store_true",
                     help="also time the general-DPLR comparator against KDA over sequence lengths 1K..16K")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="skip the general-DPLR comparison (profiling runs: its fused-KDA timing launches the same "
+                         "kernel instantiation as the backward's forward pass)")
     ap.add_argument("--no-tune", action="store_true",
                     help="skip the autotuning sweep (profiling runs: it launches the same fused kernel "
                          "instantiation as the backward's forward pass)")
@@ -263,8 +266,9 @@ def main():
                       out=cmp_out, final_state=cmp_fin)
 
     for _ in range(args.warmup):
-        dplr_fused()
-        kda_fused()
+        if not args.no_compare:
+            dplr_fused()
+            kda_fused()
         backward()
         prefill()
         decode()
@@ -280,8 +284,10 @@ def main():
     dec_med, dec_min = time_each(decode, args.steps, stream)
     t_pro = time_launches(prologue, args.steps, stream)
     t_bwd = time_launches(backward, args.steps, stream)
-    t_dplr = time_launches(dplr_fused, args.steps, stream)
-    t_kfused = time_launches(kda_fused, args.steps, stream)
+    t_dplr = t_kfused = None
+    if not args.no_compare:
+        t_dplr = time_launches(dplr_fused, args.steps, stream)
+        t_kfused = time_launches(kda_fused, args.steps, stream)
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     decode()
@@ -357,11 +363,10 @@ def main():
                      "tokens_per_s": round(tokens / (t_bwd * 1e-3), 1), "gb_per_s": round(bwd_gbps, 1),
                      "hbm_frac": round(bwd_gbps / PEAK_HBM_GBPS, 4), "bytes_per_launch": bwd_bytes,
                      "traffic": traffic.get("backward_bytes")},
-        "dplr_comparator": {"shape": "prefill", "chunk": 64, "dv_tile": 32,
-                            "dplr_fused_ms": round(t_dplr, 4), "kda_fused_ms": round(t_kfused, 4),
-                            "kda_two_pass_ms": round(t_pre, 4),
-                            "kda_speedup_same_design": round(t_dplr / t_kfused, 3),
-                            "kda_speedup_vs_default": round(t_dplr / t_pre, 3)},
+        "dplr_comparator": None if t_dplr is None else {
+            "shape": "prefill", "chunk": 64, "dv_tile": 32, "dplr_fused_ms": round(t_dplr, 4),
+            "kda_fused_ms": round(t_kfused, 4), "kda_two_pass_ms": round(t_pre, 4),
+            "kda_speedup_same_design": round(t_dplr / t_kfused, 3), "kda_speedup_vs_default": round(t_dplr / t_pre, 3)},
         "prologue": {"kernel": "kda_prologue", "conv_width": 4, "ms": round(t_pro, 4),
                      "gb_per_s": round(pro_gbps, 1), "hbm_frac": round(pro_gbps / PEAK_HBM_GBPS, 4),
                      "bytes_per_launch": pro_bytes, "traffic": traffic.get("prologue_bytes")},
