@@ -230,8 +230,10 @@ kda::FwdParams make_params(const kda_problem_t *p, const Resolved &r, const void
 struct BwdResolved {
     Resolved r;
     int chunk = 64;
-    int fwd_dv_tile = 32;  // d_v tile of the forward pass that keeps the chunk states
-    int64_t slots = 0;     // chunk slots (upper bound for a packed batch)
+    bool two_pass = false;  // the forward pass that keeps the chunk states: two-pass (64-column
+                            // scan tiles) when compiled for the problem, else fused
+    int fwd_dv_tile = 32;   // fused: d_v tile
+    int64_t slots = 0;      // chunk slots (upper bound for a packed batch)
     size_t off_hs = 0, off_dhs = 0, off_dch = 0, off_duch = 0, ws_bytes = 0;
 };
 
@@ -262,22 +264,28 @@ kda_status_t resolve_bwd(const kda_problem_t *p, bool varlen, BwdResolved &b) {
     if (!bwd_variant_supported(p->io_dtype, dk, dv, b.chunk))
         return fail(KDA_ERR_UNSUPPORTED, "backward: no compiled variant for io=%s d_k=%d d_v=%d chunk=%d (LDS)",
                     p->io_dtype == KDA_BF16 ? "bf16" : "fp32", dk, dv, b.chunk);
+    b.two_pass = dv % 64 == 0 && kda::split_variant_supported(p->io_dtype, dk, b.chunk, 2, 2);
     b.fwd_dv_tile = 0;
-    for (int t : {default_dv_tile((int64_t)b.r.num_seqs * p->num_heads, dv), 32})
-        if (t <= dv && kda::chunk_variant_lds_bytes(p->io_dtype, dk, t, b.chunk) > 0) {
-            b.fwd_dv_tile = t;
-            break;
-        }
-    if (b.fwd_dv_tile == 0)
-        return fail(KDA_ERR_UNSUPPORTED, "backward: no forward variant keeps the states for d_k=%d chunk=%d", dk,
-                    b.chunk);
+    if (!b.two_pass) {
+        for (int t : {default_dv_tile((int64_t)b.r.num_seqs * p->num_heads, dv), 32})
+            if (t <= dv && kda::chunk_variant_lds_bytes(p->io_dtype, dk, t, b.chunk) > 0) {
+                b.fwd_dv_tile = t;
+                break;
+            }
+        if (b.fwd_dv_tile == 0)
+            return fail(KDA_ERR_UNSUPPORTED, "backward: no forward variant keeps the states for d_k=%d chunk=%d", dk,
+                        b.chunk);
+    }
     const int64_t per = ((int64_t)p->seq_len + b.chunk - 1) / b.chunk;
     b.slots = varlen ? per + b.r.num_seqs : (int64_t)b.r.num_seqs * per;
     if (b.slots * p->num_heads > 0x7fffffffLL) return fail(KDA_ERR_UNSUPPORTED, "too many chunks");
     const size_t s_io = p->io_dtype == KDA_BF16 ? 2 : 4;
     const size_t states = align256((size_t)b.slots * p->num_heads * dk * dv * 4);
     const size_t tiles = align256((size_t)b.slots * p->num_heads * b.chunk * dv * s_io);
-    b.off_hs = kda::split_plan_bytes(b.r.num_seqs);
+    // [chunk offsets][two-pass records (when two-pass)][states][state gradients][D][dU]
+    b.off_hs = b.two_pass ? align256(kda::split_workspace_bytes(p->io_dtype, dk, b.chunk, b.slots, p->num_heads,
+                                                                b.r.num_seqs))
+                          : kda::split_plan_bytes(b.r.num_seqs);
     b.off_dhs = b.off_hs + states;
     b.off_dch = b.off_dhs + states;
     b.off_duch = b.off_dch + tiles;
@@ -417,17 +425,22 @@ kda_status_t kda_chunk_bwd(const kda_problem_t *problem, const void *q, const vo
         hipStream_t s = static_cast<hipStream_t>(stream);
         char *ws = static_cast<char *>(workspace);
         int32_t *chunk_off = reinterpret_cast<int32_t *>(ws);
-        if (varlen) {
-            st = hip_status(kda::launch_chunk_plan(cu_seqlens, r.num_seqs, b.chunk, chunk_off, s),
-                            "kda_chunk_bwd plan launch");
-            if (st != KDA_OK) return st;
-        }
         kda::FwdParams fp = make_params(problem, r, q, k, v, g, beta, initial_state, cu_seqlens, nullptr, nullptr);
         fp.hs = reinterpret_cast<float *>(ws + b.off_hs);
         fp.dch = ws + b.off_dch;
         fp.chunk_off = varlen ? chunk_off : nullptr;
-        st = hip_status(kda::launch_chunk_fwd(problem->io_dtype, fp, kda::ChunkConfig{b.chunk, b.fwd_dv_tile}, s),
-                        "kda_chunk_bwd forward launch");
+        if (b.two_pass) {  // the two-pass forward builds the chunk-offset table itself
+            st = hip_status(kda::launch_split_fwd(problem->io_dtype, fp, b.chunk, 2, 2, ws, b.slots, s),
+                            "kda_chunk_bwd forward launch");
+        } else {
+            if (varlen) {
+                st = hip_status(kda::launch_chunk_plan(cu_seqlens, r.num_seqs, b.chunk, chunk_off, s),
+                                "kda_chunk_bwd plan launch");
+                if (st != KDA_OK) return st;
+            }
+            st = hip_status(kda::launch_chunk_fwd(problem->io_dtype, fp, kda::ChunkConfig{b.chunk, b.fwd_dv_tile}, s),
+                            "kda_chunk_bwd forward launch");
+        }
         if (st != KDA_OK) return st;
         kda::BwdParams bp;
         bp.f = fp;

@@ -565,7 +565,9 @@ __device__ __forceinline__ void copy_wave(char *smem, const char *rec0, size_t r
 #undef KDA_STAGE_STORE
 }
 
-template <typename IO, int DK, int C, int SPW, int NW>
+// KEEP: also write each chunk's initial state and D (FwdParams::hs / dch) for the backward
+// pass; a separate instantiation so the forward's register allocation is not affected.
+template <typename IO, int DK, int C, int SPW, int NW, bool KEEP>
 __global__ void __launch_bounds__(64 * (NW + scan_copy_waves(SPW))) kda_scan_kernel(FwdParams p, const int32_t *__restrict__ chunk_off,
                                                                   const char *__restrict__ records) {
     using S = ScanLayout<IO, DK, C, SPW, NW>;
@@ -662,6 +664,18 @@ __global__ void __launch_bounds__(64 * (NW + scan_copy_waves(SPW))) kda_scan_ker
     for (int c = 0; c < nchunks; ++c) {
         const int clen = min(C, len - c * C);
         __syncthreads();  // chunk c is in LDS
+        // optional: the state entering this chunk, kept for the backward pass
+        const int64_t slot_base = (g0 + c) * H + h;
+        if constexpr (KEEP) {
+#pragma unroll
+            for (int s = 0; s < SPW; ++s) {
+                float *hs = p.hs + slot_base * DK * DV + col0 + WC * wave + 16 * s + l16;
+#pragma unroll
+                for (int ct = 0; ct < KT; ++ct)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) hs[(int64_t)(16 * ct + 4 * q4 + j) * DV] = St[s][ct][j];
+            }
+        }
         const char *rb = smem + ((c & 1) ? S::oRec1 : S::oRec0);
         const IO *vb = reinterpret_cast<const IO *>(smem + ((c & 1) ? S::oV1 : S::oV0));
 
@@ -756,7 +770,25 @@ __global__ void __launch_bounds__(64 * (NW + scan_copy_waves(SPW))) kda_scan_ker
 #pragma unroll
                         for (int s = 0; s < SPW; ++s) mma32(d[s], Tf[R][pp].a, Tf[R][pp].b, Yb[s][2 * pp], Yb[s][2 * pp + 1]);
 #pragma unroll
-                for (int s = 0; s < SPW; ++s) Db[s][R] = frag_from_acc<BF>(d[s]);
+                for (int s = 0; s < SPW; ++s) {
+                    Db[s][R] = frag_from_acc<BF>(d[s]);
+                    if constexpr (KEEP) {  // D of this chunk for the backward pass (operand type)
+                        using OT = typename std::conditional<BF, uint16_t, float>::type;
+                        OT *dc = static_cast<OT *>(p.dch) + slot_base * C * DV + (int64_t)(16 * R + 4 * q4) * DV +
+                                 col0 + WC * wave + 16 * s + l16;
+                        if constexpr (BF) {
+                            dc[0] = (uint16_t)(Db[s][R].v.x & 0xffffu);
+                            dc[DV] = (uint16_t)(Db[s][R].v.x >> 16);
+                            dc[2 * DV] = (uint16_t)(Db[s][R].v.y & 0xffffu);
+                            dc[3 * DV] = (uint16_t)(Db[s][R].v.y >> 16);
+                        } else {
+                            dc[0] = Db[s][R].v.x;
+                            dc[DV] = Db[s][R].v.y;
+                            dc[2 * DV] = Db[s][R].v.z;
+                            dc[3 * DV] = Db[s][R].v.w;
+                        }
+                    }
+                }
             }
             if constexpr (NSUB % 2 == 1)
 #pragma unroll
@@ -806,7 +838,7 @@ __global__ void __launch_bounds__(64 * (NW + scan_copy_waves(SPW))) kda_scan_ker
 #pragma unroll
         for (int R = 0; R < NSUB; ++R) {
             const int r = 16 * R + l16;
-            if (r < clen) {
+            if ((!KEEP || p.out) && r < clen) {
 #pragma unroll
                 for (int s = 0; s < SPW; ++s)
                     Tr::store4(oc + r * vstride + 16 * s, make_float4(Ot[s][R][0] * p.scale, Ot[s][R][1] * p.scale,
@@ -841,6 +873,7 @@ constexpr bool split_fits() {
 // Workspace: [chunk offsets: num_seqs + 1 int32, padded to 256 B][records]
 template <typename IO, int DK, int C, int SPW, int NW>
 hipError_t launch_split_variant(const FwdParams &p, char *workspace, int64_t chunk_upper, hipStream_t stream) {
+    const bool keep = p.hs != nullptr;
     if constexpr (!split_fits<IO, DK, C, SPW, NW>()) {
         return hipErrorInvalidConfiguration;
     } else {
@@ -860,8 +893,12 @@ hipError_t launch_split_variant(const FwdParams &p, char *workspace, int64_t chu
         }
         const int64_t scan_blocks = (int64_t)p.num_seqs * p.H * (p.dv / ScanLayout<IO, DK, C, SPW, NW>::DVT);
         if (scan_blocks > 0) {
-            hipLaunchKernelGGL((kda_scan_kernel<IO, DK, C, SPW, NW>), dim3((unsigned)scan_blocks), dim3(ScanLayout<IO, DK, C, SPW, NW>::NT), 0,
-                               stream, p, chunk_off, records);
+            if (keep)
+                hipLaunchKernelGGL((kda_scan_kernel<IO, DK, C, SPW, NW, true>), dim3((unsigned)scan_blocks),
+                                   dim3(ScanLayout<IO, DK, C, SPW, NW>::NT), 0, stream, p, chunk_off, records);
+            else
+                hipLaunchKernelGGL((kda_scan_kernel<IO, DK, C, SPW, NW, false>), dim3((unsigned)scan_blocks),
+                                   dim3(ScanLayout<IO, DK, C, SPW, NW>::NT), 0, stream, p, chunk_off, records);
             return hipGetLastError();
         }
         return hipSuccess;
