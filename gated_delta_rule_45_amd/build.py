@@ -21,12 +21,8 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall",
           "-Wno-unused-command-line-argument"]
-# Per-source code-generation flags.  The general-DPLR kernel is built with MFMA destinations
-# and accumulator inputs in ordinary VGPRs: built with them in accumulation registers
-# (the compiler's default at its register pressure), its bf16 variants with chunks of 32 and
-# 64 computed wrong low-rank read-outs (a deterministic, schedule-dependent error that no
-# operand explained and that s_nop padding did not remove).
-EXTRA = {"kda_dplr.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source code-generation flags (none at present).
+EXTRA: dict = {}
 
 
 def _hipcc() -> str:

@@ -234,7 +234,7 @@ struct BwdResolved {
                             // scan tiles) when compiled for the problem, else fused
     int fwd_dv_tile = 32;   // fused: d_v tile
     int64_t slots = 0;      // chunk slots (upper bound for a packed batch)
-    size_t off_hs = 0, off_dhs = 0, off_dch = 0, off_duch = 0, ws_bytes = 0;
+    size_t off_hs = 0, off_dhs = 0, off_dch = 0, off_duch = 0, off_brec = 0, ws_bytes = 0;
 };
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -289,7 +289,10 @@ kda_status_t resolve_bwd(const kda_problem_t *p, bool varlen, BwdResolved &b) {
     b.off_dhs = b.off_hs + states;
     b.off_dch = b.off_dhs + states;
     b.off_duch = b.off_dch + tiles;
-    b.ws_bytes = b.off_duch + tiles;
+    b.off_brec = b.off_duch + tiles;
+    const size_t rec = p->io_dtype == KDA_BF16 ? kda::bwd_record_bytes_bf16(dk, b.chunk)
+                                               : kda::bwd_record_bytes_f32(dk, b.chunk);
+    b.ws_bytes = b.off_brec + align256((size_t)b.slots * p->num_heads * rec);
     return KDA_OK;
 }
 
@@ -456,6 +459,7 @@ kda_status_t kda_chunk_bwd(const kda_problem_t *problem, const void *q, const vo
         bp.dhs = reinterpret_cast<float *>(ws + b.off_dhs);
         bp.dch = fp.dch;
         bp.duch = ws + b.off_duch;
+        bp.brec = ws + b.off_brec;
         bp.slots = b.slots;
         const hipError_t e = problem->io_dtype == KDA_BF16 ? kda::launch_bwd_bf16(bp, b.chunk, s)
                                                            : kda::launch_bwd_f32(bp, b.chunk, s);

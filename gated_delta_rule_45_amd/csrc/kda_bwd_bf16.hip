@@ -6,6 +6,7 @@
 namespace kda {
 
 bool bwd_supported_bf16(int dk, int dv, int chunk) { return bwd_supported<uint16_t>(dk, dv, chunk); }
+size_t bwd_record_bytes_bf16(int dk, int chunk) { return bwd_record_bytes<uint16_t>(dk, chunk); }
 hipError_t launch_bwd_bf16(const BwdParams &bp, int chunk, hipStream_t stream) {
     return launch_bwd<uint16_t>(bp, chunk, stream);
 }

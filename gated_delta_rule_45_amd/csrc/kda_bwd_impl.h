@@ -22,12 +22,15 @@
 //   dbeta_r = sum_j dU_rj V_rj - sum_c e^{G_rc} k_rc (S dU_r)_c + sum_c k_rc W_rc,
 //          W_rc = sum_i dA_ri k_ic e^{G_rc - G_ic}
 //
-// Three launches:
-//   1. the fused forward (kda_chunk_impl.h) keeps each chunk's initial state S and D;
-//   2. kda_bwd_scan_kernel: one workgroup per (sequence, head, d_v tile), chunks in
-//      reverse order; rebuilds the chunk's operands, keeps dS in registers, writes dv,
-//      dU and the chunk-end dS of every chunk, and d(initial state);
-//   3. kda_bwd_grad_kernel: one workgroup per (chunk, head), all chunks in parallel;
+// Four launches:
+//   1. the forward again (two-pass, or the fused kernel where no two-pass variant exists)
+//      keeps each chunk's initial state S and D;
+//   2. kda_bwd_prep_kernel: one workgroup per (chunk, head), all chunks in parallel; builds
+//      the chunk's gated operands, A^T, P^T and the diagonal blocks of X^T as one record;
+//   3. kda_bwd_scan_kernel: one workgroup per (sequence, head, d_v tile), chunks in
+//      reverse order; streams the records, keeps dS in registers, writes dv, dU and the
+//      chunk-end dS of every chunk, and d(initial state);
+//   4. kda_bwd_grad_kernel: one workgroup per (chunk, head), all chunks in parallel;
 //      each wave owns 16 key channels for every token of the chunk, so the gate
 //      factors stay in registers and no cross-wave reduction over channels is needed
 //      except for dbeta (a sum over channels).
@@ -50,6 +53,29 @@ namespace kda {
 __device__ __forceinline__ int64_t bwd_slot0(const FwdParams &p, int n, int C) {
     return p.cu ? (int64_t)p.chunk_off[n] : (int64_t)n * ((p.T + C - 1) / C);
 }
+
+// Sequence and chunk of a chunk slot (the inverse of bwd_slot0); false past the last chunk.
+__device__ __forceinline__ bool bwd_slot_chunk(const FwdParams &p, int C, int64_t slot, int &n, int &ci) {
+    if (p.cu) {
+        if (slot >= p.chunk_off[p.num_seqs]) return false;
+        int lo = 0, hi = p.num_seqs - 1;  // last n with chunk_off[n] <= slot
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (p.chunk_off[mid] <= slot) lo = mid;
+            else hi = mid - 1;
+        }
+        n = lo;
+        ci = (int)(slot - p.chunk_off[lo]);
+        return true;
+    }
+    const int64_t per = (p.T + C - 1) / C;
+    if (per == 0 || slot >= per * p.num_seqs) return false;
+    n = (int)(slot / per);
+    ci = (int)(slot % per);
+    return true;
+}
+
+constexpr int kBwdScanTile = 32;  // d_v columns per reverse-scan workgroup
 
 // ======================================================================= scan ====
 template <typename IO, int DK, int DVT, int C>
@@ -111,7 +137,7 @@ struct BwdRaw {
     float beta;
 };
 
-template <typename IO, int DK, int DVT, int C>
+template <typename IO, int DK, int DVT, int C, bool WITH_O = true>
 __device__ __forceinline__ void bwd_load_chunk(BwdRaw<IO, DK, DVT, C> &raw, const BwdParams &bp, int64_t tok0,
                                                int clen, int h, int col0, int tid) {
     using L = BwdScanLayout<IO, DK, DVT, C>;
@@ -130,28 +156,85 @@ __device__ __forceinline__ void bwd_load_chunk(BwdRaw<IO, DK, DVT, C> &raw, cons
             raw.q[ct] = *reinterpret_cast<const KQ *>(static_cast<const IO *>(p.q) + row + 16 * ct);
         }
     }
-    constexpr int PPR = DVT / L::V_ELEMS;
+    if constexpr (WITH_O) {
+        constexpr int PPR = DVT / L::V_ELEMS;
 #pragma unroll
-    for (int i = 0; i < L::V_PER_THREAD; ++i) {
-        const int piece = tid + kChunkThreads * i;
-        if (L::V_PIECES % kChunkThreads == 0 || piece < L::V_PIECES) {
-            const int r = min(piece / PPR, clen - 1);
-            const int cc = (piece % PPR) * L::V_ELEMS;
-            raw.o[i] = *reinterpret_cast<const uint4 *>(static_cast<const IO *>(bp.d_out) +
-                                                        ((tok0 + r) * H + h) * (int64_t)p.dv + col0 + cc);
+        for (int i = 0; i < L::V_PER_THREAD; ++i) {
+            const int piece = tid + kChunkThreads * i;
+            if (L::V_PIECES % kChunkThreads == 0 || piece < L::V_PIECES) {
+                const int r = min(piece / PPR, clen - 1);
+                const int cc = (piece % PPR) * L::V_ELEMS;
+                raw.o[i] = *reinterpret_cast<const uint4 *>(static_cast<const IO *>(bp.d_out) +
+                                                            ((tok0 + r) * H + h) * (int64_t)p.dv + col0 + cc);
+            }
         }
     }
     if (tid < C) raw.beta = p.beta[(tok0 + min(tid, clen - 1)) * H + h];
 }
 
+// Per-chunk operands of the reverse scan, built by kda_bwd_prep_kernel for every
+// (chunk, head) in parallel and streamed by kda_bwd_scan_kernel.  Compact in HBM; the rows are
+// padded again when a record is copied into LDS (the layout of BwdScanLayout).  Sections:
+//   K- rows [C][DK], Q~^T and K~^T [DK][C], P^T and A^T [C][C] (operand type);
+//   X_RR^T blocks [NSUB][16][16] fp32; e^{G_C} [DK] and beta [C] fp32 as one run.
 template <typename IO, int DK, int DVT, int C>
-__global__ void __launch_bounds__(kChunkThreads) kda_bwd_scan_kernel(BwdParams bp) {
+struct BwdRec {
     using L = BwdScanLayout<IO, DK, DVT, C>;
+    static constexpr int S_OT = L::BF ? 2 : 4;
+    static constexpr int NSUB = C / 16;
+    static constexpr int NSEC = 7;
+    static constexpr int kRows[NSEC] = {C, DK, DK, C, C, NSUB * 16, 1};
+    static constexpr int kRowBytes[NSEC] = {DK * S_OT, C * S_OT, C * S_OT, C * S_OT, C * S_OT, 16 * 4, (DK + C) * 4};
+    static constexpr int kLdsOff[NSEC] = {(int)L::oKbar, (int)L::oQtT, (int)L::oKtT, (int)L::oPT,
+                                          (int)L::oAT,   (int)L::oXT,  (int)L::oGam};
+    static constexpr int kLdsRow[NSEC] = {L::LDO * S_OT, L::LDT * S_OT, L::LDT * S_OT, L::LDM * S_OT,
+                                          L::LDM * S_OT, L::LDD * 4,    0};
+    static_assert(L::oBeta == L::oGam + (size_t)DK * 4, "e^{G_C} and beta are one run in LDS");
+    static constexpr int pieces(int k) { return kRows[k] * kRowBytes[k] / 16; }
+    static constexpr int per_thread(int k) { return (pieces(k) + kChunkThreads - 1) / kChunkThreads; }
+    static constexpr int sec_off(int k) {
+        int o = 0;
+        for (int j = 0; j < k; ++j) o += kRows[j] * kRowBytes[j];
+        return o;
+    }
+    static constexpr int first_reg(int k) {
+        int r = 0;
+        for (int j = 0; j < k; ++j) r += per_thread(j);
+        return r;
+    }
+    static constexpr int kRegs = first_reg(NSEC);  // 16-byte pieces one thread moves
+    static constexpr size_t kUsed = (size_t)sec_off(NSEC);
+    static constexpr size_t kBytes = (kUsed + 255) / 256 * 256;
+};
+
+// Calls f(reg, record byte, LDS byte) for every 16-byte piece of a record that thread tid
+// moves; every offset but tid's share is a compile-time constant.
+template <typename Rec, int K = 0, typename F>
+__device__ __forceinline__ void bwd_rec_pieces(int tid, F &&f) {
+    if constexpr (K < Rec::NSEC) {
+        constexpr int NP = Rec::pieces(K), PPR = Rec::kRowBytes[K] / 16;
+#pragma unroll
+        for (int i = 0; i < Rec::per_thread(K); ++i) {
+            const int pc = tid + kChunkThreads * i;
+            if (NP % kChunkThreads == 0 || pc < NP) {
+                const int lds = Rec::kRows[K] == 1 ? Rec::kLdsOff[K] + pc * 16
+                                                   : Rec::kLdsOff[K] + (pc / PPR) * Rec::kLdsRow[K] + (pc % PPR) * 16;
+                f(Rec::first_reg(K) + i, Rec::sec_off(K) + pc * 16, lds);
+            }
+        }
+        bwd_rec_pieces<Rec, K + 1>(tid, f);
+    }
+}
+
+template <typename IO, int DK, int C>
+__global__ void __launch_bounds__(kChunkThreads) kda_bwd_prep_kernel(BwdParams bp, char *__restrict__ records) {
+    constexpr int DVT = kBwdScanTile;
+    using L = BwdScanLayout<IO, DK, DVT, C>;
+    using R = BwdRec<IO, DK, DVT, C>;
     using OT = typename L::OT;
     constexpr bool BF = L::BF;
-    constexpr int NSUB = L::NSUB, KT = L::KT, NSL = L::NSL, SPW = L::SPW;
-    constexpr int LDO = L::LDO, LDT = L::LDT, LDM = L::LDM, LDD = L::LDD, LDV = L::LDV;
-    using Tr = IoTraits<IO>;
+    constexpr int NSUB = L::NSUB, KT = L::KT;
+    constexpr int LDO = L::LDO, LDT = L::LDT, LDM = L::LDM, LDD = L::LDD;
     const FwdParams &p = bp.f;
 
     __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
@@ -163,7 +246,6 @@ __global__ void __launch_bounds__(kChunkThreads) kda_bwd_scan_kernel(BwdParams b
     OT *sPT = reinterpret_cast<OT *>(smem + L::oPT);
     OT *sAT = reinterpret_cast<OT *>(smem + L::oAT);
     float *sXT = reinterpret_cast<float *>(smem + L::oXT);
-    OT *sO = reinterpret_cast<OT *>(smem + L::oO);
     float *sTot = reinterpret_cast<float *>(smem + L::oTot);
     float *sEB = reinterpret_cast<float *>(smem + L::oEB);
     float *sED = reinterpret_cast<float *>(smem + L::oED);
@@ -176,57 +258,19 @@ __global__ void __launch_bounds__(kChunkThreads) kda_bwd_scan_kernel(BwdParams b
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int l16 = lane & 15, q4 = lane >> 4;
-    const int H = p.H, DV = p.dv;
-
-    const int ntile = DV / DVT;
-    const int64_t nblocks = (int64_t)p.num_seqs * H * ntile;
-    const int64_t item = xcd_grouped_block(blockIdx.x, nblocks);
-    const int tile = (int)(item % ntile);
-    const int64_t nh = item / ntile;
-    const int h = (int)(nh % H);
-    const int n = (int)(nh / H);
-    int64_t start;
-    int len;
-    if (p.cu) {
-        start = p.cu[n];
-        len = p.cu[n + 1] - p.cu[n];
-    } else {
-        start = (int64_t)n * p.T;
-        len = p.T;
-    }
-    const int col0 = tile * DVT;
-    const int64_t slot0 = bwd_slot0(p, n, C);
-    const int nchunks = (len + C - 1) / C;
-
-    // ---- dS slices owned by this wave (accumulator layout), from the final-state gradient
-    f32x4 dS[SPW][KT];
-    const int64_t state_base = ((int64_t)n * H + h) * DK * DV;
-#pragma unroll
-    for (int s = 0; s < SPW; ++s) {
-        const int sl = wave + L::NW * s;
-        const int col = col0 + 16 * sl + l16;
-#pragma unroll
-        for (int ct = 0; ct < KT; ++ct)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = 16 * ct + 4 * q4 + j;
-                dS[s][ct][j] = (bp.d_sf && sl < NSL) ? bp.d_sf[state_base + (int64_t)row * DV + col] : 0.f;
-            }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
+    const int H = p.H;
+    const int64_t slot = blockIdx.x / H;
+    const int h = (int)(blockIdx.x % H);
+    int n, ci;
+    if (!bwd_slot_chunk(p, C, slot, n, ci)) return;
+    const int64_t start = p.cu ? (int64_t)p.cu[n] : (int64_t)n * p.T;
+    const int len = p.cu ? p.cu[n + 1] - p.cu[n] : p.T;
+    const int clen = min(C, len - ci * C);
 
     BwdRaw<IO, DK, DVT, C> raw;
-    if (nchunks > 0) {
-        const int c0 = (nchunks - 1) * C;
-        bwd_load_chunk<IO, DK, DVT, C>(raw, bp, start + c0, min(C, len - c0), h, col0, tid);
-    }
-
-    for (int ci = nchunks - 1; ci >= 0; --ci) {
-        const int c0 = ci * C;
-        const int clen = min(C, len - c0);
-        const int64_t tok0 = start + c0;
-
-        // ================= 1: gate scan (log2 domain), stage dO and beta
+    bwd_load_chunk<IO, DK, DVT, C, false>(raw, bp, start + (int64_t)ci * C, clen, h, 0, tid);
+    {
+        // ================= 1: gate scan (log2 domain), stage beta
         // (k and q stay packed in the raw registers; phases 3 and 4 unpack them where used)
         float G[KT][4];
         const bool valid = 16 * wave + l16 < clen;
@@ -245,20 +289,7 @@ __global__ void __launch_bounds__(kChunkThreads) kda_bwd_scan_kernel(BwdParams b
                     *reinterpret_cast<float4 *>(sTot + R * DK + c) = make_float4(G[ct][0], G[ct][1], G[ct][2], G[ct][3]);
             }
         }
-        {
-            constexpr int PPR = DVT / L::V_ELEMS;
-#pragma unroll
-            for (int i = 0; i < L::V_PER_THREAD; ++i) {
-                const int piece = tid + kChunkThreads * i;
-                if (L::V_PIECES % kChunkThreads == 0 || piece < L::V_PIECES) {
-                    const int r = piece / PPR;
-                    const int cc = (piece % PPR) * L::V_ELEMS;
-                    const uint4 x = r < clen ? raw.o[i] : make_uint4(0u, 0u, 0u, 0u);
-                    *reinterpret_cast<uint4 *>(sO + r * LDV + cc) = x;
-                }
-            }
-            if (tid < C) sBeta[tid] = tid < clen ? raw.beta : 0.f;
-        }
+        if (tid < C) sBeta[tid] = tid < clen ? raw.beta : 0.f;
         __syncthreads();
 
         // ================= 2: per-channel boundary factors
@@ -411,11 +442,123 @@ __global__ void __launch_bounds__(kChunkThreads) kda_bwd_scan_kernel(BwdParams b
                 for (int r = 0; r < 16; ++r) Ab[jc * LDD + r] = x[r];
             }
         }
-        if (ci > 0) {
-            const int pc0 = (ci - 1) * C;
-            bwd_load_chunk<IO, DK, DVT, C>(raw, bp, start + pc0, min(C, len - pc0), h, col0, tid);
+    }
+    __syncthreads();
+    // the operands the reverse scan needs, rows compacted
+    char *rec = records + (size_t)(slot * H + h) * R::kBytes;
+    bwd_rec_pieces<R>(tid, [&](int, int rb, int lb) {
+        *reinterpret_cast<u32x4 *>(rec + rb) = *reinterpret_cast<const u32x4 *>(smem + lb);
+    });
+}
+
+template <typename IO, int DK, int DVT, int C>
+__global__ void __launch_bounds__(kChunkThreads) kda_bwd_scan_kernel(BwdParams bp, const char *__restrict__ records) {
+    using L = BwdScanLayout<IO, DK, DVT, C>;
+    using R = BwdRec<IO, DK, DVT, C>;
+    using OT = typename L::OT;
+    constexpr bool BF = L::BF;
+    constexpr int NSUB = L::NSUB, KT = L::KT, NSL = L::NSL, SPW = L::SPW;
+    constexpr int LDO = L::LDO, LDT = L::LDT, LDM = L::LDM, LDD = L::LDD, LDV = L::LDV;
+    using Tr = IoTraits<IO>;
+    const FwdParams &p = bp.f;
+
+    __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
+    OT *sKbar = reinterpret_cast<OT *>(smem + L::oKbar);
+    OT *sQtT = reinterpret_cast<OT *>(smem + L::oQtT);
+    OT *sKtT = reinterpret_cast<OT *>(smem + L::oKtT);
+    OT *sPT = reinterpret_cast<OT *>(smem + L::oPT);
+    OT *sAT = reinterpret_cast<OT *>(smem + L::oAT);
+    float *sXT = reinterpret_cast<float *>(smem + L::oXT);
+    OT *sO = reinterpret_cast<OT *>(smem + L::oO);
+    float *sGam = reinterpret_cast<float *>(smem + L::oGam);
+    float *sBeta = reinterpret_cast<float *>(smem + L::oBeta);
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int l16 = lane & 15, q4 = lane >> 4;
+    const int H = p.H, DV = p.dv;
+
+    const int ntile = DV / DVT;
+    const int64_t nblocks = (int64_t)p.num_seqs * H * ntile;
+    const int64_t item = xcd_grouped_block(blockIdx.x, nblocks);
+    const int tile = (int)(item % ntile);
+    const int64_t nh = item / ntile;
+    const int h = (int)(nh % H);
+    const int n = (int)(nh / H);
+    int64_t start;
+    int len;
+    if (p.cu) {
+        start = p.cu[n];
+        len = p.cu[n + 1] - p.cu[n];
+    } else {
+        start = (int64_t)n * p.T;
+        len = p.T;
+    }
+    const int col0 = tile * DVT;
+    const int64_t slot0 = bwd_slot0(p, n, C);
+    const int nchunks = (len + C - 1) / C;
+
+    // ---- dS slices owned by this wave (accumulator layout), from the final-state gradient
+    f32x4 dS[SPW][KT];
+    const int64_t state_base = ((int64_t)n * H + h) * DK * DV;
+#pragma unroll
+    for (int s = 0; s < SPW; ++s) {
+        const int sl = wave + L::NW * s;
+        const int col = col0 + 16 * sl + l16;
+#pragma unroll
+        for (int ct = 0; ct < KT; ++ct)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * ct + 4 * q4 + j;
+                dS[s][ct][j] = (bp.d_sf && sl < NSL) ? bp.d_sf[state_base + (int64_t)row * DV + col] : 0.f;
+            }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+
+    // a chunk's record and dO tile, in flight in registers while the previous chunk computes
+    u32x4 rv[R::kRegs];
+    u32x4 ov[L::V_PER_THREAD];
+    auto prefetch = [&](int c) {
+        const char *rec = records + (size_t)((slot0 + c) * H + h) * R::kBytes;
+        bwd_rec_pieces<R>(tid, [&](int j, int rb, int) { rv[j] = *reinterpret_cast<const u32x4 *>(rec + rb); });
+        const int64_t t0 = start + (int64_t)c * C;
+        const int cl = min(C, len - c * C);
+        constexpr int PPR = DVT / L::V_ELEMS;
+#pragma unroll
+        for (int i = 0; i < L::V_PER_THREAD; ++i) {
+            const int piece = tid + kChunkThreads * i;
+            if (L::V_PIECES % kChunkThreads == 0 || piece < L::V_PIECES) {
+                const int r = min(piece / PPR, cl - 1);
+                const int cc = (piece % PPR) * L::V_ELEMS;
+                ov[i] = *reinterpret_cast<const u32x4 *>(static_cast<const IO *>(bp.d_out) +
+                                                         ((t0 + r) * H + h) * (int64_t)DV + col0 + cc);
+            }
+        }
+    };
+    if (nchunks > 0) prefetch(nchunks - 1);
+
+    for (int ci = nchunks - 1; ci >= 0; --ci) {
+        const int c0 = ci * C;
+        const int clen = min(C, len - c0);
+        const int64_t tok0 = start + c0;
+        __syncthreads();  // the previous chunk's products are done with LDS
+        bwd_rec_pieces<R>(tid, [&](int j, int, int lb) { *reinterpret_cast<u32x4 *>(smem + lb) = rv[j]; });
+        {
+            constexpr int PPR = DVT / L::V_ELEMS;
+#pragma unroll
+            for (int i = 0; i < L::V_PER_THREAD; ++i) {
+                const int piece = tid + kChunkThreads * i;
+                if (L::V_PIECES % kChunkThreads == 0 || piece < L::V_PIECES) {
+                    const int r = piece / PPR;
+                    const int cc = (piece % PPR) * L::V_ELEMS;
+                    const u32x4 z = {0u, 0u, 0u, 0u};
+                    *reinterpret_cast<u32x4 *>(sO + r * LDV + cc) = r < clen ? ov[i] : z;
+                }
+            }
         }
         __syncthreads();
+        if (ci > 0) prefetch(ci - 1);
 
         // ================= 5: reverse step for each 16-column slice of the tile
         const int64_t slot_base = (slot0 + ci) * H + h;
@@ -535,6 +678,7 @@ __global__ void __launch_bounds__(kChunkThreads) kda_bwd_scan_kernel(BwdParams b
     }
 }
 
+
 // ================================================================== gradients ====
 template <typename IO, int DK, int DV, int C>
 struct BwdGradLayout {
@@ -578,26 +722,6 @@ struct BwdGradLayout {
     __host__ __device__ static constexpr int pair_i(int pi) { return pi - pair_r(pi) * (pair_r(pi) + 1) / 2; }
 };
 
-// Sequence and chunk of a chunk slot (the inverse of bwd_slot0); false past the last chunk.
-__device__ __forceinline__ bool bwd_slot_chunk(const FwdParams &p, int C, int64_t slot, int &n, int &ci) {
-    if (p.cu) {
-        if (slot >= p.chunk_off[p.num_seqs]) return false;
-        int lo = 0, hi = p.num_seqs - 1;  // last n with chunk_off[n] <= slot
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (p.chunk_off[mid] <= slot) lo = mid;
-            else hi = mid - 1;
-        }
-        n = lo;
-        ci = (int)(slot - p.chunk_off[lo]);
-        return true;
-    }
-    const int64_t per = (p.T + C - 1) / C;
-    if (per == 0 || slot >= per * p.num_seqs) return false;
-    n = (int)(slot / per);
-    ci = (int)(slot % per);
-    return true;
-}
 
 template <typename IO, int DK, int DV, int C>
 __global__ void __launch_bounds__(64 * (DK / 16)) kda_bwd_grad_kernel(BwdParams bp) {
@@ -928,7 +1052,6 @@ __global__ void __launch_bounds__(64 * (DK / 16)) kda_bwd_grad_kernel(BwdParams 
 }
 
 // ================================================================== launch ====
-constexpr int kBwdScanTile = 32;  // d_v columns per reverse-scan workgroup
 
 template <typename IO, int DK, int DV, int C>
 constexpr bool bwd_fits() {
@@ -941,10 +1064,17 @@ hipError_t launch_bwd_variant(const BwdParams &bp, hipStream_t stream) {
         return hipErrorInvalidConfiguration;
     } else {
         const FwdParams &p = bp.f;
+        const int64_t prep_blocks = bp.slots * p.H;
+        if (prep_blocks > 0) {
+            hipLaunchKernelGGL((kda_bwd_prep_kernel<IO, DK, C>), dim3((unsigned)prep_blocks), dim3(kChunkThreads), 0,
+                               stream, bp, bp.brec);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
         const int64_t scan_blocks = (int64_t)p.num_seqs * p.H * (DV / kBwdScanTile);
         if (scan_blocks > 0) {
             hipLaunchKernelGGL((kda_bwd_scan_kernel<IO, DK, kBwdScanTile, C>), dim3((unsigned)scan_blocks),
-                               dim3(kChunkThreads), 0, stream, bp);
+                               dim3(kChunkThreads), 0, stream, bp, (const char *)bp.brec);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
@@ -962,6 +1092,15 @@ hipError_t launch_bwd_variant(const BwdParams &bp, hipStream_t stream) {
 #define KDA_BWD_VARIANTS(F)                                                                \
     F(64, 64, 16) F(64, 64, 32) F(64, 64, 64) F(64, 128, 16) F(64, 128, 32) F(64, 128, 64) \
     F(128, 64, 16) F(128, 64, 32) F(128, 64, 64) F(128, 128, 16) F(128, 128, 32) F(128, 128, 64)
+
+template <typename IO>
+size_t bwd_record_bytes(int dk, int chunk) {
+#define KDA_BWD_REC_CASE(DK_, DV_, C_) \
+    if (dk == DK_ && chunk == C_) return BwdRec<IO, DK_, kBwdScanTile, C_>::kBytes;
+    KDA_BWD_VARIANTS(KDA_BWD_REC_CASE)
+#undef KDA_BWD_REC_CASE
+    return 0;
+}
 
 template <typename IO>
 bool bwd_supported(int dk, int dv, int chunk) {

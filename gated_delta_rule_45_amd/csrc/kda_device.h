@@ -12,8 +12,8 @@
 // lanes, and operands stored row-major by their non-contracted index (A as [m][k],
 // B as [n][k]) are read as 4 consecutive elements per lane.  The sum over k does not
 // depend on which hardware k slot a value occupies, only that A and B agree, so the
-// same fragments drive v_mfma_f32_16x16x4_f32 (4 slots of 1), v_mfma_f32_16x16x16_bf16
-// (one tile) and v_mfma_f32_16x16x32_bf16 (two tiles).
+// same fragments drive v_mfma_f32_16x16x4_f32 (4 slots of 1) and v_mfma_f32_16x16x32_bf16
+// (two tiles, or one tile with the other half zero).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -24,7 +24,6 @@ namespace kda {
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -112,10 +111,15 @@ __device__ __forceinline__ Frag<BF16> lds_frag_f32(const float *p, float s = 1.0
     return make_frag<BF16>(x.x * s, x.y * s, x.z * s, x.w * s);
 }
 
-// acc += A * B over one 16-wide k tile.
+// acc += A * B over one 16-wide k tile.  bf16 uses the K=32 instruction with a zero second
+// half: code built for gfx950 with v_mfma_f32_16x16x16_bf16 computed wrong results that varied
+// from run to run where its result was read back soon after (the backward reverse scan at
+// d_k = 64), and the same code with the K=32 instruction is exact and repeatable.
 __device__ __forceinline__ void mma16(f32x4 &acc, const Frag<true> &a, const Frag<true> &b) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a.v), __builtin_bit_cast(s16x4, b.v),
-                                                    acc, 0, 0, 0);
+    const uint4 av = make_uint4(a.v.x, a.v.y, 0u, 0u);
+    const uint4 bv = make_uint4(b.v.x, b.v.y, 0u, 0u);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv), acc,
+                                                  0, 0, 0);
 }
 __device__ __forceinline__ void mma16(f32x4 &acc, const Frag<false> &a, const Frag<false> &b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v.x, b.v.x, acc, 0, 0, 0);

@@ -83,9 +83,12 @@ struct BwdParams {
     float *dhs;           // [slot, H, DK, DV] gradient of each chunk's final state
     const void *dch;      // [slot, H, C, DV] D per chunk (operand type)
     void *duch;           // [slot, H, C, DV] dU per chunk (operand type)
+    char *brec;           // [slot, H] reverse-scan records (kda_bwd_prep_kernel)
     int64_t slots;        // upper bound on the number of chunk slots
 };
 bool bwd_supported_bf16(int dk, int dv, int chunk);
+size_t bwd_record_bytes_bf16(int dk, int chunk);
+size_t bwd_record_bytes_f32(int dk, int chunk);
 bool bwd_supported_f32(int dk, int dv, int chunk);
 hipError_t launch_bwd_bf16(const BwdParams &bp, int chunk, hipStream_t stream);
 hipError_t launch_bwd_f32(const BwdParams &bp, int chunk, hipStream_t stream);

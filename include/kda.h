@@ -145,7 +145,8 @@ kda_status_t kda_recurrent_fwd(const kda_problem_t *problem, const void *q, cons
  *  dbeta           [tokens, H] fp32 (written).
  *  d_initial_state [num_seqs, H, d_k, d_v] fp32, or NULL to skip it.
  *  workspace       device scratch of at least kda_chunk_bwd_workspace() bytes, 256-byte
- *                  aligned (chunk states, their gradients and two per-chunk d_v tiles);
+ *                  aligned (chunk states, their gradients, two per-chunk d_v tiles and
+ *                  one record of per-chunk operands for the reverse scan);
  *                  contents on entry ignored, on return unspecified.  Required.
  * No output may alias an input or another output.  Status and error behaviour as for
  * kda_chunk_fwd; KDA_ERR_UNSUPPORTED when no compiled variant fits (fp32 io with

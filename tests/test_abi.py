@@ -263,13 +263,18 @@ def test_bwd_workspace_query():
     # states and their gradients (fp32) and D and dU tiles (bf16), in 256-byte sections
     a256 = lambda x: (x + 255) // 256 * 256
     rec = (3 * 16384 + 2 * 6144 + 512 + 1023) // 1024 * 1024  # whole KB: 62,464
+    # reverse-scan records: K- rows, Q~^T, K~^T (16 KB each), P^T, A^T (8 KB each), the inverted
+    # diagonal blocks (4 KB fp32), e^{G_C} and beta: 70,400 B per chunk and head
+    brec = 3 * 16384 + 2 * 8192 + 4096 + 512 + 256
     slots = 2 * 2  # 2 sequences x ceil(100 / 64)
-    assert n.value == a256(256 + slots * 2 * rec) + 2 * slots * 2 * 128 * 128 * 4 + 2 * slots * 2 * 64 * 128 * 2
+    assert n.value == a256(256 + slots * 2 * rec) + 2 * slots * 2 * 128 * 128 * 4 + 2 * slots * 2 * 64 * 128 * 2 + \
+        a256(slots * 2 * brec)
     # a packed batch reserves one partial chunk per sequence
     assert lib.kda_chunk_bwd_workspace(ctypes.byref(_bwd_problem(batch=1, seq_len=300, num_seqs=5)),
                                        ctypes.byref(n)) == kda.KDA_OK
     slots = 5 + 5
-    assert n.value == a256(256 + slots * 2 * rec) + 2 * slots * 2 * 128 * 128 * 4 + 2 * slots * 2 * 64 * 128 * 2
+    assert n.value == a256(256 + slots * 2 * rec) + 2 * slots * 2 * 128 * 128 * 4 + 2 * slots * 2 * 64 * 128 * 2 + \
+        a256(slots * 2 * brec)
     assert lib.kda_chunk_bwd_workspace(ctypes.byref(_bwd_problem(chunk_size=48)), ctypes.byref(n)) == \
         kda.KDA_ERR_UNSUPPORTED
     assert n.value == 0
