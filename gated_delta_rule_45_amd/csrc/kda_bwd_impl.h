@@ -75,184 +75,144 @@ __device__ __forceinline__ bool bwd_slot_chunk(const FwdParams &p, int C, int64_
     return true;
 }
 
-constexpr int kBwdScanTile = 32;  // d_v columns per reverse-scan workgroup
+constexpr int kBwdScanTile = 32;  // d_v columns per reverse-scan workgroup (two 16-column compute waves)
+constexpr int kBwdScanCopyWaves = 4;
+constexpr int kBwdScanThreads = 64 * (kBwdScanTile / 16 + kBwdScanCopyWaves);
 
-// ======================================================================= scan ====
-template <typename IO, int DK, int DVT, int C>
-struct BwdScanLayout {
+// ==================================================================== record ====
+// Per-chunk operands of the reverse scan, built by kda_bwd_prep_kernel for every (chunk, head)
+// in parallel and streamed by kda_bwd_scan_kernel.  With X = (I + A)^{-1} the chunk's part of
+// the reverse chain is
+//     dU = M dS + N (scale dO),        M = X^T K-,  N = X^T P^T,
+//     dS <- Diag(e^{G_C}) dS + Q~^T (scale dO) - (Diag(beta) K~)^T dU,
+// so the only products left in the sequential chain are against dS and dU.  The record holds
+// M [C][DK], N [C][C], Q~^T and (Diag(beta) K~)^T [DK][C] (operand type), e^{G_C} [DK] and
+// beta [C] (fp32).  It is stored exactly as the scan keeps it in LDS, every row padded by 16
+// bytes so that the fragment reads spread over the banks, and the scan copies it verbatim; the
+// size is rounded up to whole KB (the copy waves move 1 KB per wave instruction).  Padding bytes
+// are not written.
+template <typename IO, int DK, int C>
+struct BwdRec {
     static constexpr bool BF = IoTraits<IO>::kBf16;
     using OT = typename std::conditional<BF, uint16_t, float>::type;
-    static constexpr int NW = 4;
-    static constexpr int NSUB = C / 16;
-    static constexpr int KT = DK / 16;
-    static constexpr int NSL = DVT / 16;
-    static constexpr int SPW = NSL > NW ? NSL / NW : 1;
-    static constexpr int PADO = 16 / (int)sizeof(OT);
-    static constexpr int LDO = DK + PADO;  // [C][DK] row operands
-    static constexpr int LDT = C + PADO;   // [DK][C] transposed operands
-    static constexpr int LDM = C + PADO;   // [C][C] transposed A and P
-    static constexpr int LDD = 16 + 4;     // fp32 diagonal inverses [16][16]
-    static constexpr int LDV = DVT + PADO; // [C][DVT] staged dO
+    static constexpr int S = (int)sizeof(OT);
+    static constexpr int NSUB = C / 16, KT = DK / 16;
+    static constexpr int PAD = 16 / S;
+    static constexpr int LDO = DK + PAD;  // [C][DK] rows
+    static constexpr int LDT = C + PAD;   // [DK][C] rows
+    static constexpr int LDM = C + PAD;   // [C][C] rows
+    static constexpr size_t oM = 0;
+    static constexpr size_t oN = oM + (size_t)C * LDO * S;
+    static constexpr size_t oQtT = oN + (size_t)C * LDM * S;
+    static constexpr size_t oBKtT = oQtT + (size_t)DK * LDT * S;
+    static constexpr size_t oGam = oBKtT + (size_t)DK * LDT * S;
+    static constexpr size_t oBeta = oGam + (size_t)DK * 4;
+    static constexpr size_t kUsed = oBeta + (size_t)C * 4;
+    static constexpr size_t kBytes = (kUsed + 1023) / 1024 * 1024;
+    static_assert(C % 16 == 0 && NSUB >= 1 && NSUB <= 4, "chunk must be 16, 32 or 64");
+    static_assert(DK % 64 == 0, "d_k must be 64 or 128");
+};
+
+// ====================================================================== prep ====
+template <typename IO, int DK, int C>
+struct BwdPrepLayout {
+    using Rec = BwdRec<IO, DK, C>;
+    using OT = typename Rec::OT;
+    static constexpr bool BF = Rec::BF;
+    static constexpr int S = Rec::S;
+    static constexpr int NSUB = C / 16, KT = DK / 16;
+    static constexpr int LDO = Rec::LDO, LDT = Rec::LDT, LDM = Rec::LDM;
+    static constexpr int LDX = C + 4;  // fp32 [C][C]: A, then X in place
     static constexpr int NSHIFT = NSUB >= 3 ? (NSUB - 1) * (NSUB - 2) / 2 : 0;
-    static_assert(C % 16 == 0 && NSUB >= 1 && NSUB <= NW, "chunk must be 16, 32 or 64");
-    static_assert(DK % 32 == 0 && DVT % 16 == 0, "head dims");
-    static_assert(NSL <= NW || NSL % NW == 0, "d_v tile");
-
-    static constexpr int V_PIECES = C * DVT * (int)sizeof(IO) / 16;
-    static constexpr int V_PER_THREAD = (V_PIECES + kChunkThreads - 1) / kChunkThreads;
-    static constexpr int V_ELEMS = 16 / (int)sizeof(IO);
-
-    static constexpr size_t kOp = (size_t)C * LDO * sizeof(OT);
-    static constexpr size_t kOpT = (size_t)DK * LDT * sizeof(OT);
-    static constexpr size_t oKb = 0;
-    static constexpr size_t oKs = oKb + kOp;
-    static constexpr size_t oKbar = oKs + (size_t)NSHIFT * 16 * LDO * sizeof(OT);
-    static constexpr size_t oQtT = oKbar + kOp;
-    static constexpr size_t oKtT = oQtT + kOpT;
-    static constexpr size_t oPT = oKtT + kOpT;
-    static constexpr size_t oAT = oPT + (size_t)C * LDM * sizeof(OT);
-    static constexpr size_t oXT = oAT + (size_t)C * LDM * sizeof(OT);
-    static constexpr size_t oO = oXT + (size_t)NSUB * 16 * LDD * 4;
-    static constexpr size_t oTot = oO + (size_t)C * LDV * sizeof(OT);
+    // The record image comes first and is copied out verbatim.  The K_b rows take M's place:
+    // they are dead before M is formed.
+    static constexpr size_t oKb = Rec::oM;
+    static constexpr size_t oKs = Rec::kBytes;
+    static constexpr size_t oKbarT = oKs + (size_t)NSHIFT * 16 * LDO * S;
+    static constexpr size_t oX = oKbarT + (size_t)DK * LDT * S;
+    static constexpr size_t oP = oX + (size_t)C * LDX * 4;
+    static constexpr size_t oTot = oP + (size_t)C * LDM * S;
     static constexpr size_t oEB = oTot + (size_t)NSUB * DK * 4;
     static constexpr size_t oED = oEB + (size_t)NSUB * DK * 4;
     static constexpr size_t oEC = oED + (size_t)NSUB * DK * 4;
     static constexpr size_t oSH = oEC + (size_t)NSUB * DK * 4;
-    static constexpr size_t oGam = oSH + (size_t)(NSHIFT > 0 ? NSHIFT : 1) * DK * 4;
-    static constexpr size_t oBeta = oGam + (size_t)DK * 4;
-    static constexpr size_t kBytes = oBeta + (size_t)C * 4;
+    static constexpr size_t kBytes = oSH + (size_t)(NSHIFT > 0 ? NSHIFT : 1) * DK * 4;
     static constexpr bool kFits = kBytes <= 160 * 1024;
 
     __host__ __device__ static constexpr int shift_slot(int R, int I) { return (R - 2) * (R - 1) / 2 + I; }
 };
 
-// Raw inputs of one chunk: the key side (q, k, g) of sub-chunk R = wave, a dO tile, beta.
-template <typename IO, int DK, int DVT, int C>
+// Raw key side of one chunk: q, k, g of sub-chunk R = wave, and beta.
+template <typename IO, int DK>
 struct BwdRaw {
-    using L = BwdScanLayout<IO, DK, DVT, C>;
-    using KQ = typename std::conditional<L::BF, uint2, float4>::type;
-    float4 g[L::KT];
-    KQ k[L::KT], q[L::KT];
-    uint4 o[L::V_PER_THREAD];
+    using KQ = typename std::conditional<IoTraits<IO>::kBf16, uint2, float4>::type;
+    float4 g[DK / 16];
+    KQ k[DK / 16], q[DK / 16];
     float beta;
 };
 
-template <typename IO, int DK, int DVT, int C, bool WITH_O = true>
-__device__ __forceinline__ void bwd_load_chunk(BwdRaw<IO, DK, DVT, C> &raw, const BwdParams &bp, int64_t tok0,
-                                               int clen, int h, int col0, int tid) {
-    using L = BwdScanLayout<IO, DK, DVT, C>;
-    using KQ = typename BwdRaw<IO, DK, DVT, C>::KQ;
-    const FwdParams &p = bp.f;
+template <typename IO, int DK, int C>
+__device__ __forceinline__ void bwd_load_keys(BwdRaw<IO, DK> &raw, const FwdParams &p, int64_t tok0, int clen, int h,
+                                              int tid) {
+    using KQ = typename BwdRaw<IO, DK>::KQ;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l16 = lane & 15, q4 = lane >> 4;
-    const int H = p.H;
-    if (wave < L::NSUB) {
+    if (wave < C / 16) {
         const int r = min(16 * wave + l16, clen - 1);
-        const int64_t row = ((tok0 + r) * H + h) * (int64_t)DK + 4 * q4;
+        const int64_t row = ((tok0 + r) * p.H + h) * (int64_t)DK + 4 * q4;
 #pragma unroll
-        for (int ct = 0; ct < L::KT; ++ct) {
+        for (int ct = 0; ct < DK / 16; ++ct) {
             raw.g[ct] = *reinterpret_cast<const float4 *>(p.g + row + 16 * ct);
             raw.k[ct] = *reinterpret_cast<const KQ *>(static_cast<const IO *>(p.k) + row + 16 * ct);
             raw.q[ct] = *reinterpret_cast<const KQ *>(static_cast<const IO *>(p.q) + row + 16 * ct);
         }
     }
-    if constexpr (WITH_O) {
-        constexpr int PPR = DVT / L::V_ELEMS;
-#pragma unroll
-        for (int i = 0; i < L::V_PER_THREAD; ++i) {
-            const int piece = tid + kChunkThreads * i;
-            if (L::V_PIECES % kChunkThreads == 0 || piece < L::V_PIECES) {
-                const int r = min(piece / PPR, clen - 1);
-                const int cc = (piece % PPR) * L::V_ELEMS;
-                raw.o[i] = *reinterpret_cast<const uint4 *>(static_cast<const IO *>(bp.d_out) +
-                                                            ((tok0 + r) * H + h) * (int64_t)p.dv + col0 + cc);
-            }
-        }
-    }
-    if (tid < C) raw.beta = p.beta[(tok0 + min(tid, clen - 1)) * H + h];
+    if (tid < C) raw.beta = p.beta[(tok0 + min(tid, clen - 1)) * p.H + h];
 }
 
-// Per-chunk operands of the reverse scan, built by kda_bwd_prep_kernel for every
-// (chunk, head) in parallel and streamed by kda_bwd_scan_kernel.  Compact in HBM; the rows are
-// padded again when a record is copied into LDS (the layout of BwdScanLayout).  Sections:
-//   K- rows [C][DK], Q~^T and K~^T [DK][C], P^T and A^T [C][C] (operand type);
-//   X_RR^T blocks [NSUB][16][16] fp32; e^{G_C} [DK] and beta [C] fp32 as one run.
-template <typename IO, int DK, int DVT, int C>
-struct BwdRec {
-    using L = BwdScanLayout<IO, DK, DVT, C>;
-    static constexpr int S_OT = L::BF ? 2 : 4;
-    static constexpr int NSUB = C / 16;
-    static constexpr int NSEC = 7;
-    static constexpr int kRows[NSEC] = {C, DK, DK, C, C, NSUB * 16, 1};
-    static constexpr int kRowBytes[NSEC] = {DK * S_OT, C * S_OT, C * S_OT, C * S_OT, C * S_OT, 16 * 4, (DK + C) * 4};
-    static constexpr int kLdsOff[NSEC] = {(int)L::oKbar, (int)L::oQtT, (int)L::oKtT, (int)L::oPT,
-                                          (int)L::oAT,   (int)L::oXT,  (int)L::oGam};
-    static constexpr int kLdsRow[NSEC] = {L::LDO * S_OT, L::LDT * S_OT, L::LDT * S_OT, L::LDM * S_OT,
-                                          L::LDM * S_OT, L::LDD * 4,    0};
-    static_assert(L::oBeta == L::oGam + (size_t)DK * 4, "e^{G_C} and beta are one run in LDS");
-    static constexpr int pieces(int k) { return kRows[k] * kRowBytes[k] / 16; }
-    static constexpr int per_thread(int k) { return (pieces(k) + kChunkThreads - 1) / kChunkThreads; }
-    static constexpr int sec_off(int k) {
-        int o = 0;
-        for (int j = 0; j < k; ++j) o += kRows[j] * kRowBytes[j];
-        return o;
+// X_IR (I >= R) as a B operand: rows 4*q4 + j, column l16.  X is kept with its diagonal blocks
+// in place and the blocks below the diagonal transposed in the unused upper blocks:
+// X_IR[a][b] at sX[(16R + b) * LDX + 16I + a] for I > R.
+template <bool BF, int LDX>
+__device__ __forceinline__ Frag<BF> bwd_x_frag(const float *sX, int I, int R, int l16, int q4) {
+    float4 x;
+    if (I == R) {
+        const float *d = sX + (16 * R + 4 * q4) * LDX + 16 * R + l16;
+        x = make_float4(d[0], d[LDX], d[2 * LDX], d[3 * LDX]);
+    } else {
+        x = *reinterpret_cast<const float4 *>(sX + (16 * R + l16) * LDX + 16 * I + 4 * q4);
     }
-    static constexpr int first_reg(int k) {
-        int r = 0;
-        for (int j = 0; j < k; ++j) r += per_thread(j);
-        return r;
-    }
-    static constexpr int kRegs = first_reg(NSEC);  // 16-byte pieces one thread moves
-    static constexpr size_t kUsed = (size_t)sec_off(NSEC);
-    static constexpr size_t kBytes = (kUsed + 255) / 256 * 256;
-};
-
-// Calls f(reg, record byte, LDS byte) for every 16-byte piece of a record that thread tid
-// moves; every offset but tid's share is a compile-time constant.
-template <typename Rec, int K = 0, typename F>
-__device__ __forceinline__ void bwd_rec_pieces(int tid, F &&f) {
-    if constexpr (K < Rec::NSEC) {
-        constexpr int NP = Rec::pieces(K), PPR = Rec::kRowBytes[K] / 16;
-#pragma unroll
-        for (int i = 0; i < Rec::per_thread(K); ++i) {
-            const int pc = tid + kChunkThreads * i;
-            if (NP % kChunkThreads == 0 || pc < NP) {
-                const int lds = Rec::kRows[K] == 1 ? Rec::kLdsOff[K] + pc * 16
-                                                   : Rec::kLdsOff[K] + (pc / PPR) * Rec::kLdsRow[K] + (pc % PPR) * 16;
-                f(Rec::first_reg(K) + i, Rec::sec_off(K) + pc * 16, lds);
-            }
-        }
-        bwd_rec_pieces<Rec, K + 1>(tid, f);
-    }
+    return make_frag<BF>(x.x, x.y, x.z, x.w);
 }
 
 template <typename IO, int DK, int C>
 __global__ void __launch_bounds__(kChunkThreads) kda_bwd_prep_kernel(BwdParams bp, char *__restrict__ records) {
-    constexpr int DVT = kBwdScanTile;
-    using L = BwdScanLayout<IO, DK, DVT, C>;
-    using R = BwdRec<IO, DK, DVT, C>;
+    using L = BwdPrepLayout<IO, DK, C>;
+    using Rec = typename L::Rec;
     using OT = typename L::OT;
     constexpr bool BF = L::BF;
     constexpr int NSUB = L::NSUB, KT = L::KT;
-    constexpr int LDO = L::LDO, LDT = L::LDT, LDM = L::LDM, LDD = L::LDD;
+    constexpr int LDO = L::LDO, LDT = L::LDT, LDM = L::LDM, LDX = L::LDX;
+    static_assert(KT % 4 == 0 && NSUB <= 4, "four waves share the d_k tiles of M");
     const FwdParams &p = bp.f;
 
     __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
     OT *sKb = reinterpret_cast<OT *>(smem + L::oKb);
     OT *sKs = reinterpret_cast<OT *>(smem + L::oKs);
-    OT *sKbar = reinterpret_cast<OT *>(smem + L::oKbar);
-    OT *sQtT = reinterpret_cast<OT *>(smem + L::oQtT);
-    OT *sKtT = reinterpret_cast<OT *>(smem + L::oKtT);
-    OT *sPT = reinterpret_cast<OT *>(smem + L::oPT);
-    OT *sAT = reinterpret_cast<OT *>(smem + L::oAT);
-    float *sXT = reinterpret_cast<float *>(smem + L::oXT);
+    OT *sKbarT = reinterpret_cast<OT *>(smem + L::oKbarT);
+    float *sX = reinterpret_cast<float *>(smem + L::oX);
+    OT *sP = reinterpret_cast<OT *>(smem + L::oP);
     float *sTot = reinterpret_cast<float *>(smem + L::oTot);
     float *sEB = reinterpret_cast<float *>(smem + L::oEB);
     float *sED = reinterpret_cast<float *>(smem + L::oED);
     float *sEC = reinterpret_cast<float *>(smem + L::oEC);
     float *sSH = reinterpret_cast<float *>(smem + L::oSH);
-    float *sGam = reinterpret_cast<float *>(smem + L::oGam);
-    float *sBeta = reinterpret_cast<float *>(smem + L::oBeta);
+    OT *sM = reinterpret_cast<OT *>(smem + Rec::oM);
+    OT *sN = reinterpret_cast<OT *>(smem + Rec::oN);
+    OT *sQtT = reinterpret_cast<OT *>(smem + Rec::oQtT);
+    OT *sBKtT = reinterpret_cast<OT *>(smem + Rec::oBKtT);
+    float *sGam = reinterpret_cast<float *>(smem + Rec::oGam);
+    float *sBeta = reinterpret_cast<float *>(smem + Rec::oBeta);
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -267,211 +227,374 @@ __global__ void __launch_bounds__(kChunkThreads) kda_bwd_prep_kernel(BwdParams b
     const int len = p.cu ? p.cu[n + 1] - p.cu[n] : p.T;
     const int clen = min(C, len - ci * C);
 
-    BwdRaw<IO, DK, DVT, C> raw;
-    bwd_load_chunk<IO, DK, DVT, C, false>(raw, bp, start + (int64_t)ci * C, clen, h, 0, tid);
-    {
-        // ================= 1: gate scan (log2 domain), stage beta
-        // (k and q stay packed in the raw registers; phases 3 and 4 unpack them where used)
-        float G[KT][4];
-        const bool valid = 16 * wave + l16 < clen;
-        if (wave < NSUB) {
-            const int R = wave;
-#pragma unroll
-            for (int ct = 0; ct < KT; ++ct) {
-                const int c = 16 * ct + 4 * q4;
-                const float4 gv = raw.g[ct];
-                const float m = valid ? kLog2e : 0.f;
-                G[ct][0] = scan16_add(gv.x * m);
-                G[ct][1] = scan16_add(gv.y * m);
-                G[ct][2] = scan16_add(gv.z * m);
-                G[ct][3] = scan16_add(gv.w * m);
-                if (l16 == 15)
-                    *reinterpret_cast<float4 *>(sTot + R * DK + c) = make_float4(G[ct][0], G[ct][1], G[ct][2], G[ct][3]);
-            }
-        }
-        if (tid < C) sBeta[tid] = tid < clen ? raw.beta : 0.f;
-        __syncthreads();
+    BwdRaw<IO, DK> raw;
+    bwd_load_keys<IO, DK, C>(raw, p, start + (int64_t)ci * C, clen, h, tid);
 
-        // ================= 2: per-channel boundary factors
-        if (tid < DK) {
-            const int c = tid;
-            float tot[NSUB], bnd[NSUB + 1];
-            bnd[0] = 0.f;
+    // ================= 1: gate scan (log2 domain), stage beta
+    // (k and q stay packed in the raw registers; phases 3 and 4 unpack them where used)
+    float G[KT][4];
+    const bool valid = 16 * wave + l16 < clen;
+    if (wave < NSUB) {
+        const int R = wave;
 #pragma unroll
-            for (int R = 0; R < NSUB; ++R) {
-                tot[R] = sTot[R * DK + c];
-                bnd[R + 1] = bnd[R] + tot[R];
-            }
-            const float gc = bnd[NSUB];
-#pragma unroll
-            for (int R = 0; R < NSUB; ++R) {
-                sEB[R * DK + c] = fast_exp2(bnd[R]);
-                sED[R * DK + c] = fast_exp2(-tot[R]);
-                sEC[R * DK + c] = fast_exp2(gc - bnd[R + 1]);
-#pragma unroll
-                for (int I = 0; I + 2 <= R; ++I) sSH[L::shift_slot(R, I) * DK + c] = fast_exp2(bnd[R] - bnd[I + 1]);
-            }
-            sGam[c] = fast_exp2(gc);
+        for (int ct = 0; ct < KT; ++ct) {
+            const int c = 16 * ct + 4 * q4;
+            const float4 gv = raw.g[ct];
+            const float m = valid ? kLog2e : 0.f;
+            G[ct][0] = scan16_add(gv.x * m);
+            G[ct][1] = scan16_add(gv.y * m);
+            G[ct][2] = scan16_add(gv.z * m);
+            G[ct][3] = scan16_add(gv.w * m);
+            if (l16 == 15)
+                *reinterpret_cast<float4 *>(sTot + R * DK + c) = make_float4(G[ct][0], G[ct][1], G[ct][2], G[ct][3]);
         }
-        __syncthreads();
+    }
+    if (tid < C) sBeta[tid] = tid < clen ? raw.beta : 0.f;
+    __syncthreads();
 
-        // ================= 3: gated operands of sub-chunk R
-        Frag<BF> kdiag[KT];
-        if (wave < NSUB) {
-            const int R = wave;
-            const int r = 16 * R + l16;
+    // ================= 2: per-channel boundary factors
+    if (tid < DK) {
+        const int c = tid;
+        float tot[NSUB], bnd[NSUB + 1];
+        bnd[0] = 0.f;
 #pragma unroll
-            for (int ct = 0; ct < KT; ++ct) {
-                const int c = 16 * ct + 4 * q4;
-                const float4 tot = *reinterpret_cast<const float4 *>(sTot + R * DK + c);
-                const float4 eb = *reinterpret_cast<const float4 *>(sEB + R * DK + c);
-                const float4 ed = *reinterpret_cast<const float4 *>(sED + R * DK + c);
-                const float4 ec = *reinterpret_cast<const float4 *>(sEC + R * DK + c);
-                const float tv[4] = {tot.x, tot.y, tot.z, tot.w};
-                const float ebv[4] = {eb.x, eb.y, eb.z, eb.w};
-                const float edv[4] = {ed.x, ed.y, ed.z, ed.w};
-                const float ecv[4] = {ec.x, ec.y, ec.z, ec.w};
-                const float4 kv = unpack4<BF>(raw.k[ct]), qv = unpack4<BF>(raw.q[ct]);
-                const float kx[4] = {kv.x, kv.y, kv.z, kv.w}, qx[4] = {qv.x, qv.y, qv.z, qv.w};
-                float kb[4], kt[4], qt[4], kbar[4], kd[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float fr = valid ? fast_exp2(G[ct][j]) : 0.f;
-                    const float fb = valid ? fast_exp2(tv[j] - G[ct][j]) : 0.f;
-                    kb[j] = kx[j] * fb;
-                    kd[j] = kb[j] * edv[j];
-                    kt[j] = kx[j] * fr * ebv[j];
-                    qt[j] = qx[j] * fr * ebv[j];
-                    kbar[j] = kb[j] * ecv[j];
-                }
-                kdiag[ct] = make_frag<BF>(kd[0], kd[1], kd[2], kd[3]);
-                const Frag<BF> fkb = make_frag<BF>(kb[0], kb[1], kb[2], kb[3]);
-                *reinterpret_cast<decltype(fkb.v) *>(sKb + r * LDO + c) = fkb.v;
-                *reinterpret_cast<decltype(fkb.v) *>(sKbar + r * LDO + c) =
-                    make_frag<BF>(kbar[0], kbar[1], kbar[2], kbar[3]).v;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if constexpr (BF) {
-                        sKtT[(c + j) * LDT + r] = f32_to_bf16(kt[j]);
-                        sQtT[(c + j) * LDT + r] = f32_to_bf16(qt[j]);
-                    } else {
-                        sKtT[(c + j) * LDT + r] = kt[j];
-                        sQtT[(c + j) * LDT + r] = qt[j];
-                    }
-                }
-#pragma unroll
-                for (int R2 = 2; R2 < NSUB; ++R2) {
-                    if (R2 < R + 2) continue;
-                    const float4 sh = *reinterpret_cast<const float4 *>(sSH + L::shift_slot(R2, R) * DK + c);
-                    const Frag<BF> f = make_frag<BF>(kb[0] * sh.x, kb[1] * sh.y, kb[2] * sh.z, kb[3] * sh.w);
-                    *reinterpret_cast<decltype(f.v) *>(sKs + (L::shift_slot(R2, R) * 16 + l16) * LDO + c) = f.v;
-                }
-            }
+        for (int R = 0; R < NSUB; ++R) {
+            tot[R] = sTot[R * DK + c];
+            bnd[R + 1] = bnd[R] + tot[R];
         }
-        __syncthreads();
+        const float gc = bnd[NSUB];
+#pragma unroll
+        for (int R = 0; R < NSUB; ++R) {
+            sEB[R * DK + c] = fast_exp2(bnd[R]);
+            sED[R * DK + c] = fast_exp2(-tot[R]);
+            sEC[R * DK + c] = fast_exp2(gc - bnd[R + 1]);
+#pragma unroll
+            for (int I = 0; I + 2 <= R; ++I) sSH[L::shift_slot(R, I) * DK + c] = fast_exp2(bnd[R] - bnd[I + 1]);
+        }
+        sGam[c] = fast_exp2(gc);
+    }
+    __syncthreads();
 
-        // ================= 4: row-R blocks of A and P (stored transposed), diagonal inverse
-        if (wave < NSUB) {
-            const int R = wave;
-            Frag<BF> ka[KT], qa[KT];
+    // ================= 3: gated operands of sub-chunk R: K_b rows (and their shifted copies),
+    // K-^T, and the record's Q~^T and (Diag(beta) K~)^T
+    Frag<BF> kdiag[KT];
+    if (wave < NSUB) {
+        const int R = wave;
+        const int r = 16 * R + l16;
+        const float br = sBeta[r];
 #pragma unroll
-            for (int ct = 0; ct < KT; ++ct) {
-                const float4 kv = unpack4<BF>(raw.k[ct]), qv = unpack4<BF>(raw.q[ct]);
-                float fr[4];
+        for (int ct = 0; ct < KT; ++ct) {
+            const int c = 16 * ct + 4 * q4;
+            const float4 tot = *reinterpret_cast<const float4 *>(sTot + R * DK + c);
+            const float4 eb = *reinterpret_cast<const float4 *>(sEB + R * DK + c);
+            const float4 ed = *reinterpret_cast<const float4 *>(sED + R * DK + c);
+            const float4 ec = *reinterpret_cast<const float4 *>(sEC + R * DK + c);
+            const float tv[4] = {tot.x, tot.y, tot.z, tot.w};
+            const float ebv[4] = {eb.x, eb.y, eb.z, eb.w};
+            const float edv[4] = {ed.x, ed.y, ed.z, ed.w};
+            const float ecv[4] = {ec.x, ec.y, ec.z, ec.w};
+            const float4 kv = unpack4<BF>(raw.k[ct]), qv = unpack4<BF>(raw.q[ct]);
+            const float kx[4] = {kv.x, kv.y, kv.z, kv.w}, qx[4] = {qv.x, qv.y, qv.z, qv.w};
+            float kb[4], kt[4], qt[4], kbar[4], kd[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) fr[j] = valid ? fast_exp2(G[ct][j]) : 0.f;
-                ka[ct] = make_frag<BF>(kv.x * fr[0], kv.y * fr[1], kv.z * fr[2], kv.w * fr[3]);
-                qa[ct] = make_frag<BF>(qv.x * fr[0], qv.y * fr[1], qv.z * fr[2], qv.w * fr[3]);
+            for (int j = 0; j < 4; ++j) {
+                const float fr = valid ? fast_exp2(G[ct][j]) : 0.f;
+                const float fb = valid ? fast_exp2(tv[j] - G[ct][j]) : 0.f;
+                kb[j] = kx[j] * fb;
+                kd[j] = kb[j] * edv[j];
+                kt[j] = kx[j] * fr * ebv[j];
+                qt[j] = qx[j] * fr * ebv[j];
+                kbar[j] = kb[j] * ecv[j];
             }
+            kdiag[ct] = make_frag<BF>(kd[0], kd[1], kd[2], kd[3]);
+            const Frag<BF> fkb = make_frag<BF>(kb[0], kb[1], kb[2], kb[3]);
+            *reinterpret_cast<decltype(fkb.v) *>(sKb + r * LDO + c) = fkb.v;
 #pragma unroll
-            for (int I = 0; I < NSUB; ++I) {
-                if (I > R) break;
-                f32x4 accA = zero4(), accP = zero4();
-                const OT *colp = (I == R - 1) ? sKb + (16 * I + l16) * LDO
-                                              : sKs + (L::shift_slot(R < 2 ? 2 : R, I) * 16 + l16) * LDO;
-#pragma unroll
-                for (int ct = 0; ct < KT; ct += 2) {
-                    Frag<BF> b0, b1;
-                    if (I == R) {
-                        b0 = kdiag[ct];
-                        b1 = kdiag[ct + 1];
-                    } else {
-                        b0 = lds_frag(colp + 16 * ct + 4 * q4);
-                        b1 = lds_frag(colp + 16 * (ct + 1) + 4 * q4);
-                    }
-                    mma32(accA, ka[ct], ka[ct + 1], b0, b1);
-                    mma32(accP, qa[ct], qa[ct + 1], b0, b1);
-                }
-                // accumulator: rows rr = 4*q4 + j of block R, column ii = l16 of block I
-                float av[4], pv[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int rr = 4 * q4 + j, ii = l16;
-                    av[j] = accA[j] * sBeta[16 * R + rr];
-                    pv[j] = accP[j];
-                    if (I == R) {
-                        if (ii >= rr) av[j] = 0.f;
-                        if (ii > rr) pv[j] = 0.f;
-                    }
-                }
-                // transposed stores: element (row 16R+rr, column 16I+ii) goes to [16I+ii][16R+rr]
-                const Frag<BF> fp = make_frag<BF>(pv[0], pv[1], pv[2], pv[3]);
-                *reinterpret_cast<decltype(fp.v) *>(sPT + (16 * I + l16) * LDM + 16 * R + 4 * q4) = fp.v;
-                if (I != R) {
-                    const Frag<BF> fa = make_frag<BF>(av[0], av[1], av[2], av[3]);
-                    *reinterpret_cast<decltype(fa.v) *>(sAT + (16 * I + l16) * LDM + 16 * R + 4 * q4) = fa.v;
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (BF) {
+                    sKbarT[(c + j) * LDT + r] = f32_to_bf16(kbar[j]);
+                    sQtT[(c + j) * LDT + r] = f32_to_bf16(qt[j]);
+                    sBKtT[(c + j) * LDT + r] = f32_to_bf16(kt[j] * br);
                 } else {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) sXT[(R * 16 + 4 * q4 + j) * LDD + l16] = av[j];
+                    sKbarT[(c + j) * LDT + r] = kbar[j];
+                    sQtT[(c + j) * LDT + r] = qt[j];
+                    sBKtT[(c + j) * LDT + r] = kt[j] * br;
                 }
             }
-            // X_RR = (I + A_RR)^{-1}: lane l16 computes column l16 by forward substitution,
-            // then the block is stored transposed (row l16 of X_RR^T)
-            float *Ab = sXT + R * 16 * LDD;
-            const int jc = l16;
-            float x[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float s = (r == jc) ? 1.f : 0.f;
-#pragma unroll
-                for (int m = 0; m < r; ++m) s -= Ab[r * LDD + m] * x[m];
-                x[r] = s;
-            }
-            if (q4 == 0) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) Ab[jc * LDD + r] = x[r];
+            for (int R2 = 2; R2 < NSUB; ++R2) {
+                if (R2 < R + 2) continue;
+                const float4 sh = *reinterpret_cast<const float4 *>(sSH + L::shift_slot(R2, R) * DK + c);
+                const Frag<BF> f = make_frag<BF>(kb[0] * sh.x, kb[1] * sh.y, kb[2] * sh.z, kb[3] * sh.w);
+                *reinterpret_cast<decltype(f.v) *>(sKs + (L::shift_slot(R2, R) * 16 + l16) * LDO + c) = f.v;
             }
         }
     }
     __syncthreads();
-    // the operands the reverse scan needs, rows compacted
-    char *rec = records + (size_t)(slot * H + h) * R::kBytes;
-    bwd_rec_pieces<R>(tid, [&](int, int rb, int lb) {
-        *reinterpret_cast<u32x4 *>(rec + rb) = *reinterpret_cast<const u32x4 *>(smem + lb);
-    });
+
+    // ================= 4: row-R blocks of A (fp32, to sX) and P (to sP, zero above the block
+    // diagonal), then X_RR = (I + A_RR)^{-1} in place
+    if (wave < NSUB) {
+        const int R = wave;
+        Frag<BF> ka[KT], qa[KT];
+#pragma unroll
+        for (int ct = 0; ct < KT; ++ct) {
+            const float4 kv = unpack4<BF>(raw.k[ct]), qv = unpack4<BF>(raw.q[ct]);
+            float fr[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) fr[j] = valid ? fast_exp2(G[ct][j]) : 0.f;
+            ka[ct] = make_frag<BF>(kv.x * fr[0], kv.y * fr[1], kv.z * fr[2], kv.w * fr[3]);
+            qa[ct] = make_frag<BF>(qv.x * fr[0], qv.y * fr[1], qv.z * fr[2], qv.w * fr[3]);
+        }
+#pragma unroll
+        for (int I = 0; I < NSUB; ++I) {
+            if (I > R) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sP[(16 * R + 4 * q4 + j) * LDM + 16 * I + l16] = OT(0);
+                continue;
+            }
+            f32x4 accA = zero4(), accP = zero4();
+            const OT *colp = (I == R - 1) ? sKb + (16 * I + l16) * LDO
+                                          : sKs + (L::shift_slot(R < 2 ? 2 : R, I) * 16 + l16) * LDO;
+#pragma unroll
+            for (int ct = 0; ct < KT; ct += 2) {
+                Frag<BF> b0, b1;
+                if (I == R) {
+                    b0 = kdiag[ct];
+                    b1 = kdiag[ct + 1];
+                } else {
+                    b0 = lds_frag(colp + 16 * ct + 4 * q4);
+                    b1 = lds_frag(colp + 16 * (ct + 1) + 4 * q4);
+                }
+                mma32(accA, ka[ct], ka[ct + 1], b0, b1);
+                mma32(accP, qa[ct], qa[ct + 1], b0, b1);
+            }
+            // accumulator: rows rr = 4*q4 + j of block R, column ii = l16 of block I
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int rr = 4 * q4 + j, ii = l16;
+                float av = accA[j] * sBeta[16 * R + rr], pv = accP[j];
+                if (I == R) {
+                    if (ii >= rr) av = 0.f;
+                    if (ii > rr) pv = 0.f;
+                }
+                sX[(16 * R + rr) * LDX + 16 * I + ii] = av;
+                if constexpr (BF) sP[(16 * R + rr) * LDM + 16 * I + ii] = f32_to_bf16(pv);
+                else sP[(16 * R + rr) * LDM + 16 * I + ii] = pv;
+            }
+        }
+        // lane l16 computes column l16 of X_RR by forward substitution (this wave wrote A_RR)
+        float *Ab = sX + (16 * R) * LDX + 16 * R;
+        float x[16];
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            float s = (rr == l16) ? 1.f : 0.f;
+#pragma unroll
+            for (int m = 0; m < rr; ++m) s -= Ab[rr * LDX + m] * x[m];
+            x[rr] = s;
+        }
+        if (q4 == 0) {
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) Ab[rr * LDX + l16] = x[rr];
+        }
+    }
+    __syncthreads();
+
+    // ================= 5: blocks of X below the diagonal, one block diagonal at a time:
+    // X_RI = -X_RR sum_{J=I}^{R-1} A_RJ X_JI (fp32 matrix-core products), stored transposed in
+    // the upper block (I, R).
+#pragma unroll
+    for (int lvl = 1; lvl < NSUB; ++lvl) {
+        const int R = wave;
+        if (R >= lvl && R < NSUB) {
+            const int I = R - lvl;
+            f32x4 m = zero4();
+#pragma unroll
+            for (int J = 0; J < NSUB; ++J) {
+                if (J < I || J >= R) continue;
+                const Frag<false> a = lds_frag(sX + (16 * R + l16) * LDX + 16 * J + 4 * q4);  // A_RJ rows
+                mma16(m, a, bwd_x_frag<false, LDX>(sX, J, I, l16, q4));
+            }
+            f32x4 xo = zero4();
+            const Frag<false> xrr = lds_frag(sX + (16 * R + l16) * LDX + 16 * R + 4 * q4);
+            Frag<false> mb;
+            mb.v = make_float4(-m[0], -m[1], -m[2], -m[3]);
+            mma16(xo, xrr, mb);
+            // xo holds X_RI rows 4*q4 + j, column l16
+            *reinterpret_cast<float4 *>(sX + (16 * I + l16) * LDX + 16 * R + 4 * q4) = make_float4(xo[0], xo[1], xo[2], xo[3]);
+        }
+        __syncthreads();
+    }
+
+    // ================= 6: M^T = K-^T X in tiles (16 channels x 16 tokens), each accumulator
+    // holding 4 consecutive channels of one token, i.e. a 4-element piece of a row of M.  Wave w
+    // takes d_k tiles w*KT/4 ...; sub-chunk R of X's columns needs its rows I >= R.
+    {
+        constexpr int CPW = KT / 4;
+#pragma unroll
+        for (int cc = 0; cc < CPW; ++cc) {
+            const int ct = wave * CPW + cc;
+            const OT *kr = sKbarT + (16 * ct + l16) * LDT + 4 * q4;
+#pragma unroll
+            for (int R = 0; R < NSUB; ++R) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int I = R; I < NSUB; ++I) mma16(acc, lds_frag(kr + 16 * I), bwd_x_frag<BF, LDX>(sX, I, R, l16, q4));
+                const Frag<BF> f = make_frag<BF>(acc[0], acc[1], acc[2], acc[3]);
+                *reinterpret_cast<decltype(f.v) *>(sM + (16 * R + l16) * LDO + 16 * ct + 4 * q4) = f.v;
+            }
+        }
+    }
+    // N^T = P X: wave I forms the tiles of row block I, (P X)_IR = sum_{J=R}^{I} P_IJ X_JR, and
+    // stores them as rows of N (zero for R > I)
+    if (wave < NSUB) {
+        const int I = wave;
+        const OT *pr = sP + (16 * I + l16) * LDM + 4 * q4;
+#pragma unroll
+        for (int R = 0; R < NSUB; ++R) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int J = 0; J < NSUB; ++J) {
+                if (J < R || J > I) continue;
+                mma16(acc, lds_frag(pr + 16 * J), bwd_x_frag<BF, LDX>(sX, J, R, l16, q4));
+            }
+            const Frag<BF> f = make_frag<BF>(acc[0], acc[1], acc[2], acc[3]);
+            *reinterpret_cast<decltype(f.v) *>(sN + (16 * R + l16) * LDM + 16 * I + 4 * q4) = f.v;
+        }
+    }
+    __syncthreads();
+
+    // ================= 7: the record out, verbatim
+    char *rec = records + (size_t)(slot * H + h) * Rec::kBytes;
+    for (int pc = tid; pc < (int)(Rec::kBytes / 16); pc += kChunkThreads)
+        reinterpret_cast<u32x4 *>(rec)[pc] = reinterpret_cast<const u32x4 *>(smem)[pc];
 }
 
-template <typename IO, int DK, int DVT, int C>
-__global__ void __launch_bounds__(kChunkThreads) kda_bwd_scan_kernel(BwdParams bp, const char *__restrict__ records) {
-    using L = BwdScanLayout<IO, DK, DVT, C>;
-    using R = BwdRec<IO, DK, DVT, C>;
+// ====================================================================== scan ====
+// Workgroup = two compute waves (16 state columns each, dS in registers) + four copy waves
+// that stage each chunk's record and dO tile in LDS, in two pairs that take turns, each pair
+// loading its chunk two chunks ahead (the forward scan's arrangement).  Copy waves keep their
+// own memory counters, so the compute waves' stores never delay a load being waited for.
+// The compute waves keep their stores few and wide (a wave stalls once it has 63 memory
+// operations in flight): dU is formed transposed, dU^T = dS^T M^T + (scale dO)^T N^T, so that a
+// lane holds 4 consecutive columns of one token (one 8-byte dv and dU store per 16x16 tile;
+// the accumulator fragments of dS and dO are the operand fragments of their transposes), an
+// exact product with the identity turns it back for the dS update, and dS leaves through a
+// per-wave LDS tile as 16-byte row segments.
+template <typename IO, int DK, int C>
+struct BwdScanLayout {
+    using Rec = BwdRec<IO, DK, C>;
+    using OT = typename Rec::OT;
+    static constexpr bool BF = Rec::BF;
+    static constexpr int S = Rec::S;
+    static constexpr int DVT = kBwdScanTile;
+    static constexpr int NW = DVT / 16;  // compute waves
+    static constexpr int NCW = kBwdScanCopyWaves;
+    static constexpr int NT = kBwdScanThreads;
+    static constexpr int LDV = DVT + Rec::PAD;  // staged dO [C][LDV]
+    static constexpr int EP = 16 / S;           // elements per 16-byte piece
+    static constexpr int PPR = DVT / EP;        // pieces per dO row
+    static constexpr int V_PIECES = C * PPR;
+    static constexpr int REC_UNITS = (int)(Rec::kBytes / 1024);
+    static constexpr int V_UNITS = V_PIECES / 64;
+    static_assert(V_PIECES % 64 == 0, "dO tile is copied in whole wave units");
+    static_assert(sizeof(IO) == sizeof(OT), "operand type follows the io type");
+    static constexpr int LDH = 16 + 4;  // per-wave fp32 [DK][LDH] tile that turns dS around for its stores
+    static constexpr size_t kVBytes = (size_t)C * LDV * S;
+    static constexpr size_t oRec0 = 0;
+    static constexpr size_t oRec1 = Rec::kBytes;
+    static constexpr size_t oV0 = 2 * Rec::kBytes;
+    static constexpr size_t oV1 = oV0 + kVBytes;
+    static constexpr size_t oH = oV1 + kVBytes;
+    static constexpr size_t kBytes = oH + (size_t)NW * DK * LDH * 4;
+    static constexpr bool kFits = kBytes <= 160 * 1024;
+};
+
+// One copy wave's half of a chunk (record units and dO pieces dealt alternately to the two
+// waves of a pair), held in registers between its loads and its LDS writes.
+template <typename IO, int DK, int C, int HALF>
+struct BwdStager {
+    using L = BwdScanLayout<IO, DK, C>;
+    using OT = typename L::OT;
+    static constexpr int UNITS = L::REC_UNITS + L::V_UNITS;
+    static constexpr int PER = (UNITS - HALF + 1) / 2;
+    u32x4 r[PER];
+
+    __device__ __forceinline__ void load(const char *rec, const IO *orow0, int clen, int64_t ostride, int lane) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int u = HALF + 2 * i;
+            if (u < L::REC_UNITS) {
+                r[i] = *reinterpret_cast<const u32x4 *>(rec + (size_t)u * 1024 + lane * 16);
+            } else {
+                const int piece = (u - L::REC_UNITS) * 64 + lane;
+                const int row = min(piece / L::PPR, clen - 1);  // rows past the end re-read the last row
+                r[i] = *reinterpret_cast<const u32x4 *>(orow0 + row * ostride + (piece % L::PPR) * L::EP);
+            }
+        }
+    }
+    __device__ __forceinline__ void store(char *lds_rec, OT *lds_o, int lane) const {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int u = HALF + 2 * i;
+            if (u < L::REC_UNITS) {
+                *reinterpret_cast<u32x4 *>(lds_rec + u * 1024 + lane * 16) = r[i];
+            } else {
+                const int piece = (u - L::REC_UNITS) * 64 + lane;
+                *reinterpret_cast<u32x4 *>(lds_o + (piece / L::PPR) * L::LDV + (piece % L::PPR) * L::EP) = r[i];
+            }
+        }
+    }
+};
+
+// Copy wave CW.  Stream element j is chunk nchunks - 1 - j.  Pair CW / 2 stages the elements
+// with j % 2 == CW / 2.  Barrier j hands element j to the compute waves; passing it also means
+// that both compute waves are done with element j - 1, whose buffer may take element j + 1.
+template <typename IO, int DK, int C, int CW>
+__device__ __forceinline__ void bwd_copy_wave(char *smem, const char *records, int64_t slot0, int H, int h,
+                                              const IO *obase, int64_t ostride, int len, int nchunks, int lane) {
+    using L = BwdScanLayout<IO, DK, C>;
+    using Rec = typename L::Rec;
+    using OT = typename L::OT;
+    constexpr int NPAIR = L::NCW / 2, PAIR = CW / 2;
+    BwdStager<IO, DK, C, CW % 2> st;
+    auto load = [&](int j) {
+        const int c = nchunks - 1 - j;
+        st.load(records + (size_t)((slot0 + c) * H + h) * Rec::kBytes, obase + (int64_t)c * C * ostride,
+                min(C, len - c * C), ostride, lane);
+    };
+    auto store = [&](int j) {
+        st.store(smem + ((j & 1) ? L::oRec1 : L::oRec0), reinterpret_cast<OT *>(smem + ((j & 1) ? L::oV1 : L::oV0)),
+                 lane);
+    };
+    if (PAIR < nchunks) {
+        load(PAIR);
+        if (PAIR == 0) {
+            store(0);
+            if (NPAIR < nchunks) load(NPAIR);
+        }
+    }
+    for (int j = 0; j < nchunks; ++j) {
+        __syncthreads();  // barrier j: the buffer of element j + 1 is free
+        if ((j + 1) % NPAIR == PAIR && j + 1 < nchunks) {
+            store(j + 1);
+            if (j + 1 + NPAIR < nchunks) load(j + 1 + NPAIR);
+        }
+    }
+}
+
+template <typename IO, int DK, int C>
+__global__ void __launch_bounds__(kBwdScanThreads) kda_bwd_scan_kernel(BwdParams bp, const char *__restrict__ records) {
+    using L = BwdScanLayout<IO, DK, C>;
+    using Rec = typename L::Rec;
     using OT = typename L::OT;
     constexpr bool BF = L::BF;
-    constexpr int NSUB = L::NSUB, KT = L::KT, NSL = L::NSL, SPW = L::SPW;
-    constexpr int LDO = L::LDO, LDT = L::LDT, LDM = L::LDM, LDD = L::LDD, LDV = L::LDV;
+    constexpr int NSUB = Rec::NSUB, KT = Rec::KT, NW = L::NW, DVT = L::DVT;
+    constexpr int LDO = Rec::LDO, LDT = Rec::LDT, LDM = Rec::LDM, LDV = L::LDV, LDH = L::LDH;
     using Tr = IoTraits<IO>;
     const FwdParams &p = bp.f;
 
     __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
-    OT *sKbar = reinterpret_cast<OT *>(smem + L::oKbar);
-    OT *sQtT = reinterpret_cast<OT *>(smem + L::oQtT);
-    OT *sKtT = reinterpret_cast<OT *>(smem + L::oKtT);
-    OT *sPT = reinterpret_cast<OT *>(smem + L::oPT);
-    OT *sAT = reinterpret_cast<OT *>(smem + L::oAT);
-    float *sXT = reinterpret_cast<float *>(smem + L::oXT);
-    OT *sO = reinterpret_cast<OT *>(smem + L::oO);
-    float *sGam = reinterpret_cast<float *>(smem + L::oGam);
-    float *sBeta = reinterpret_cast<float *>(smem + L::oBeta);
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -498,186 +621,154 @@ __global__ void __launch_bounds__(kChunkThreads) kda_bwd_scan_kernel(BwdParams b
     const int col0 = tile * DVT;
     const int64_t slot0 = bwd_slot0(p, n, C);
     const int nchunks = (len + C - 1) / C;
+    const int64_t ostride = (int64_t)H * DV;  // elements between consecutive tokens of one head
+    const IO *obase = static_cast<const IO *>(bp.d_out) + (start * H + h) * (int64_t)DV + col0;
 
-    // ---- dS slices owned by this wave (accumulator layout), from the final-state gradient
-    f32x4 dS[SPW][KT];
+    if (wave >= NW) {
+        switch (wave - NW) {
+            case 0: bwd_copy_wave<IO, DK, C, 0>(smem, records, slot0, H, h, obase, ostride, len, nchunks, lane); break;
+            case 1: bwd_copy_wave<IO, DK, C, 1>(smem, records, slot0, H, h, obase, ostride, len, nchunks, lane); break;
+            case 2: bwd_copy_wave<IO, DK, C, 2>(smem, records, slot0, H, h, obase, ostride, len, nchunks, lane); break;
+            default: bwd_copy_wave<IO, DK, C, 3>(smem, records, slot0, H, h, obase, ostride, len, nchunks, lane); break;
+        }
+        return;
+    }
+
+    // ---- compute wave: state columns col0 + 16*wave + l16; dS in the accumulator layout
+    const int col = col0 + 16 * wave + l16;
+    f32x4 dS[KT];
     const int64_t state_base = ((int64_t)n * H + h) * DK * DV;
 #pragma unroll
-    for (int s = 0; s < SPW; ++s) {
-        const int sl = wave + L::NW * s;
-        const int col = col0 + 16 * sl + l16;
+    for (int ct = 0; ct < KT; ++ct)
 #pragma unroll
-        for (int ct = 0; ct < KT; ++ct)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = 16 * ct + 4 * q4 + j;
-                dS[s][ct][j] = (bp.d_sf && sl < NSL) ? bp.d_sf[state_base + (int64_t)row * DV + col] : 0.f;
-            }
-    }
+        for (int j = 0; j < 4; ++j)
+            dS[ct][j] = bp.d_sf ? bp.d_sf[state_base + (int64_t)(16 * ct + 4 * q4 + j) * DV + col] : 0.f;
     __builtin_amdgcn_s_waitcnt(0);
 
-    // a chunk's record and dO tile, in flight in registers while the previous chunk computes
-    u32x4 rv[R::kRegs];
-    u32x4 ov[L::V_PER_THREAD];
-    auto prefetch = [&](int c) {
-        const char *rec = records + (size_t)((slot0 + c) * H + h) * R::kBytes;
-        bwd_rec_pieces<R>(tid, [&](int j, int rb, int) { rv[j] = *reinterpret_cast<const u32x4 *>(rec + rb); });
-        const int64_t t0 = start + (int64_t)c * C;
-        const int cl = min(C, len - c * C);
-        constexpr int PPR = DVT / L::V_ELEMS;
-#pragma unroll
-        for (int i = 0; i < L::V_PER_THREAD; ++i) {
-            const int piece = tid + kChunkThreads * i;
-            if (L::V_PIECES % kChunkThreads == 0 || piece < L::V_PIECES) {
-                const int r = min(piece / PPR, cl - 1);
-                const int cc = (piece % PPR) * L::V_ELEMS;
-                ov[i] = *reinterpret_cast<const u32x4 *>(static_cast<const IO *>(bp.d_out) +
-                                                         ((t0 + r) * H + h) * (int64_t)DV + col0 + cc);
-            }
-        }
-    };
-    if (nchunks > 0) prefetch(nchunks - 1);
+    float *sH = reinterpret_cast<float *>(smem + L::oH) + wave * DK * LDH;
+    // identity as a B operand: rows 4q4 + jj, column l16
+    const Frag<BF> ident = make_frag<BF>(4 * q4 == l16 ? 1.f : 0.f, 4 * q4 + 1 == l16 ? 1.f : 0.f,
+                                         4 * q4 + 2 == l16 ? 1.f : 0.f, 4 * q4 + 3 == l16 ? 1.f : 0.f);
 
-    for (int ci = nchunks - 1; ci >= 0; --ci) {
-        const int c0 = ci * C;
-        const int clen = min(C, len - c0);
-        const int64_t tok0 = start + c0;
-        __syncthreads();  // the previous chunk's products are done with LDS
-        bwd_rec_pieces<R>(tid, [&](int j, int, int lb) { *reinterpret_cast<u32x4 *>(smem + lb) = rv[j]; });
-        {
-            constexpr int PPR = DVT / L::V_ELEMS;
-#pragma unroll
-            for (int i = 0; i < L::V_PER_THREAD; ++i) {
-                const int piece = tid + kChunkThreads * i;
-                if (L::V_PIECES % kChunkThreads == 0 || piece < L::V_PIECES) {
-                    const int r = piece / PPR;
-                    const int cc = (piece % PPR) * L::V_ELEMS;
-                    const u32x4 z = {0u, 0u, 0u, 0u};
-                    *reinterpret_cast<u32x4 *>(sO + r * LDV + cc) = r < clen ? ov[i] : z;
-                }
-            }
-        }
-        __syncthreads();
-        if (ci > 0) prefetch(ci - 1);
-
-        // ================= 5: reverse step for each 16-column slice of the tile
+    for (int j = 0; j < nchunks; ++j) {
+        const int ci = nchunks - 1 - j;
+        const int clen = min(C, len - ci * C);
+        const int64_t tok0 = start + (int64_t)ci * C;
+        __syncthreads();  // element j is in its buffer
+        const char *rb = smem + ((j & 1) ? L::oRec1 : L::oRec0);
+        const OT *sO = reinterpret_cast<const OT *>(smem + ((j & 1) ? L::oV1 : L::oV0));
+        const OT *sM = reinterpret_cast<const OT *>(rb + Rec::oM);
+        const OT *sN = reinterpret_cast<const OT *>(rb + Rec::oN);
+        const OT *sQtT = reinterpret_cast<const OT *>(rb + Rec::oQtT);
+        const OT *sBKtT = reinterpret_cast<const OT *>(rb + Rec::oBKtT);
+        const float *sGam = reinterpret_cast<const float *>(rb + Rec::oGam);
+        const float *sBeta = reinterpret_cast<const float *>(rb + Rec::oBeta);
         const int64_t slot_base = (slot0 + ci) * H + h;
-#pragma unroll
-        for (int s = 0; s < SPW; ++s) {
-            const int sl = wave + L::NW * s;
-            if (sl >= NSL) break;
-            const int col = col0 + 16 * sl + l16;
 
-            // gradient of the state this chunk hands on, kept for the gradient kernel
-            {
-                float *dh = bp.dhs + slot_base * DK * DV + col;
+        // gradient of the state this chunk hands on, kept for the gradient kernel: written to the
+        // wave's LDS tile in the accumulator layout, read back as 4 consecutive columns of a row
+        {
 #pragma unroll
-                for (int ct = 0; ct < KT; ++ct)
+            for (int ct = 0; ct < KT; ++ct)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) dh[(int64_t)(16 * ct + 4 * q4 + j) * DV] = dS[s][ct][j];
-            }
-            Frag<BF> Sb[KT];
-#pragma unroll
-            for (int ct = 0; ct < KT; ++ct) Sb[ct] = frag_from_acc<BF>(dS[s][ct]);
-
-            // scale * dO as B operands: rows 16I + 4q4 + j, column l16 of the slice
-            Frag<BF> dOf[NSUB];
-#pragma unroll
-            for (int I = 0; I < NSUB; ++I) {
-                float t[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const OT x = sO[(16 * I + 4 * q4 + j) * LDV + 16 * sl + l16];
-                    if constexpr (BF) t[j] = bf16_to_f32(x) * p.scale;
-                    else t[j] = x * p.scale;
-                }
-                dOf[I] = make_frag<BF>(t[0], t[1], t[2], t[3]);
-            }
-
-            // dD_R = sum_{I>=R} (P_IR)^T dO_I + K-_R dS;  dU_R = X_RR^T (dD_R - sum_{I>R} (A_IR)^T dU_I)
-            f32x4 dU[NSUB];
-            Frag<BF> dUf[NSUB];
-#pragma unroll
-            for (int R = NSUB - 1; R >= 0; --R) {
-                f32x4 z = zero4();
-#pragma unroll
-                for (int I = R; I < NSUB; ++I) mma16(z, lds_frag(sPT + (16 * R + l16) * LDM + 16 * I + 4 * q4), dOf[I]);
-                const OT *kb = sKbar + (16 * R + l16) * LDO + 4 * q4;
-#pragma unroll
-                for (int ct = 0; ct < KT; ct += 2)
-                    mma32(z, lds_frag(kb + 16 * ct), lds_frag(kb + 16 * ct + 16), Sb[ct], Sb[ct + 1]);
-#pragma unroll
-                for (int I = R + 1; I < NSUB; ++I) {
-                    Frag<BF> a = lds_frag(sAT + (16 * R + l16) * LDM + 16 * I + 4 * q4);
-                    if constexpr (BF) {
-                        a.v.x ^= 0x80008000u;
-                        a.v.y ^= 0x80008000u;
-                    } else {
-                        a.v = make_float4(-a.v.x, -a.v.y, -a.v.z, -a.v.w);
-                    }
-                    mma16(z, a, dUf[I]);
-                }
-                f32x4 d = zero4();
-                mma16(d, lds_frag_f32<BF>(sXT + (16 * R + l16) * LDD + 4 * q4), frag_from_acc<BF>(z));
-                dU[R] = d;
-                dUf[R] = frag_from_acc<BF>(d);
-            }
-
-            // dY = beta * dU: the value gradient; dU kept per chunk for the gradient kernel
-            Frag<BF> nY[NSUB];
-            OT *du = static_cast<OT *>(bp.duch) + slot_base * C * DV + col;
-#pragma unroll
-            for (int R = 0; R < NSUB; ++R) {
-                float y[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = 16 * R + 4 * q4 + j;
-                    y[j] = sBeta[r] * dU[R][j];
-                    if (r < clen) Tr::store1(static_cast<IO *>(bp.dv) + ((tok0 + r) * H + h) * (int64_t)DV + col, y[j]);
-                    if constexpr (BF) du[(int64_t)r * DV] = f32_to_bf16(dU[R][j]);
-                    else du[(int64_t)r * DV] = dU[R][j];
-                }
-                nY[R] = make_frag<BF>(-y[0], -y[1], -y[2], -y[3]);
-            }
-
-            // dS <- Diag(e^{G_C}) dS + Q~^T (scale dO) - K~^T dY
+                for (int jj = 0; jj < 4; ++jj) sH[(16 * ct + 4 * q4 + jj) * LDH + l16] = dS[ct][jj];
+            float *dh = bp.dhs + slot_base * DK * DV + col0 + 16 * wave + 4 * (lane & 3);
 #pragma unroll
             for (int ct = 0; ct < KT; ++ct) {
-                const float4 gm = *reinterpret_cast<const float4 *>(sGam + 16 * ct + 4 * q4);
-                dS[s][ct][0] *= gm.x;
-                dS[s][ct][1] *= gm.y;
-                dS[s][ct][2] *= gm.z;
-                dS[s][ct][3] *= gm.w;
-                const OT *qt = sQtT + (16 * ct + l16) * LDT + 4 * q4;
-                const OT *kt = sKtT + (16 * ct + l16) * LDT + 4 * q4;
-#pragma unroll
-                for (int R = 0; R + 1 < NSUB; R += 2) {
-                    mma32(dS[s][ct], lds_frag(qt + 16 * R), lds_frag(qt + 16 * (R + 1)), dOf[R], dOf[R + 1]);
-                    mma32(dS[s][ct], lds_frag(kt + 16 * R), lds_frag(kt + 16 * (R + 1)), nY[R], nY[R + 1]);
-                }
-                if constexpr (NSUB % 2 == 1) {
-                    mma16(dS[s][ct], lds_frag(qt + 16 * (NSUB - 1)), dOf[NSUB - 1]);
-                    mma16(dS[s][ct], lds_frag(kt + 16 * (NSUB - 1)), nY[NSUB - 1]);
-                }
+                const int row = 16 * ct + (lane >> 2);
+                *reinterpret_cast<float4 *>(dh + (int64_t)row * DV) =
+                    *reinterpret_cast<const float4 *>(sH + row * LDH + 4 * (lane & 3));
             }
         }
-        __syncthreads();
+        Frag<BF> Sb[KT];
+#pragma unroll
+        for (int ct = 0; ct < KT; ++ct) Sb[ct] = frag_from_acc<BF>(dS[ct]);
+
+        // scale * dO: rows 16I + 4q4 + jj (zero past the chunk's end), column l16
+        Frag<BF> dOf[NSUB];
+#pragma unroll
+        for (int I = 0; I < NSUB; ++I) {
+            float t[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int r = 16 * I + 4 * q4 + jj;
+                const OT x = sO[r * LDV + 16 * wave + l16];
+                float v;
+                if constexpr (BF) v = bf16_to_f32(x);
+                else v = x;
+                t[jj] = r < clen ? v * p.scale : 0.f;
+            }
+            dOf[I] = make_frag<BF>(t[0], t[1], t[2], t[3]);
+        }
+
+        // dU^T = dS^T M^T + (scale dO)^T N^T; N is zero left of its block diagonal.  Lane holds
+        // dU[16R + l16][16*wave + 4q4 + jj].
+        f32x4 dUt[NSUB];
+#pragma unroll
+        for (int R = 0; R < NSUB; ++R) {
+            f32x4 z = zero4();
+            const OT *mr = sM + (16 * R + l16) * LDO + 4 * q4;
+#pragma unroll
+            for (int kp = 0; kp < KT; kp += 2) mma32(z, Sb[kp], Sb[kp + 1], lds_frag(mr + 16 * kp), lds_frag(mr + 16 * kp + 16));
+            const OT *nr = sN + (16 * R + l16) * LDM + 4 * q4;
+#pragma unroll
+            for (int I = R & ~1; I + 1 < NSUB; I += 2)
+                mma32(z, dOf[I], dOf[I + 1], lds_frag(nr + 16 * I), lds_frag(nr + 16 * I + 16));
+            if constexpr (NSUB % 2 == 1) mma16(z, dOf[NSUB - 1], lds_frag(nr + 16 * (NSUB - 1)));
+            dUt[R] = z;
+        }
+
+        // dv = beta * dU and dU (kept per chunk for the gradient kernel): one store each per tile;
+        // -dU back in the accumulator layout (rows 16R + 4q4 + jj, column l16) for the dS update
+        Frag<BF> nU[NSUB];
+        {
+            const int cq = col0 + 16 * wave + 4 * q4;
+            OT *du = static_cast<OT *>(bp.duch) + slot_base * C * DV + cq;
+#pragma unroll
+            for (int R = 0; R < NSUB; ++R) {
+                const int r = 16 * R + l16;
+                const float b = sBeta[r];
+                if (r < clen)
+                    Tr::store4(static_cast<IO *>(bp.dv) + ((tok0 + r) * H + h) * (int64_t)DV + cq,
+                               make_float4(b * dUt[R][0], b * dUt[R][1], b * dUt[R][2], b * dUt[R][3]));
+                const Frag<BF> u = make_frag<BF>(dUt[R][0], dUt[R][1], dUt[R][2], dUt[R][3]);
+                *reinterpret_cast<decltype(u.v) *>(du + (int64_t)r * DV) = u.v;
+                f32x4 t = zero4();
+                mma16(t, make_frag<BF>(-dUt[R][0], -dUt[R][1], -dUt[R][2], -dUt[R][3]), ident);
+                nU[R] = frag_from_acc<BF>(t);
+            }
+        }
+
+        // dS <- Diag(e^{G_C}) dS + Q~^T (scale dO) - (Diag(beta) K~)^T dU
+#pragma unroll
+        for (int ct = 0; ct < KT; ++ct) {
+            const float4 gm = *reinterpret_cast<const float4 *>(sGam + 16 * ct + 4 * q4);
+            dS[ct][0] *= gm.x;
+            dS[ct][1] *= gm.y;
+            dS[ct][2] *= gm.z;
+            dS[ct][3] *= gm.w;
+            const OT *qt = sQtT + (16 * ct + l16) * LDT + 4 * q4;
+            const OT *kt = sBKtT + (16 * ct + l16) * LDT + 4 * q4;
+#pragma unroll
+            for (int R = 0; R + 1 < NSUB; R += 2) {
+                mma32(dS[ct], lds_frag(qt + 16 * R), lds_frag(qt + 16 * (R + 1)), dOf[R], dOf[R + 1]);
+                mma32(dS[ct], lds_frag(kt + 16 * R), lds_frag(kt + 16 * (R + 1)), nU[R], nU[R + 1]);
+            }
+            if constexpr (NSUB % 2 == 1) {
+                mma16(dS[ct], lds_frag(qt + 16 * (NSUB - 1)), dOf[NSUB - 1]);
+                mma16(dS[ct], lds_frag(kt + 16 * (NSUB - 1)), nU[NSUB - 1]);
+            }
+        }
     }
 
     if (bp.ds0) {
 #pragma unroll
-        for (int s = 0; s < SPW; ++s) {
-            const int sl = wave + L::NW * s;
-            if (sl >= NSL) break;
-            const int col = col0 + 16 * sl + l16;
+        for (int ct = 0; ct < KT; ++ct)
 #pragma unroll
-            for (int ct = 0; ct < KT; ++ct)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) bp.ds0[state_base + (int64_t)(16 * ct + 4 * q4 + j) * DV + col] = dS[s][ct][j];
-        }
+            for (int jj = 0; jj < 4; ++jj)
+                bp.ds0[state_base + (int64_t)(16 * ct + 4 * q4 + jj) * DV + col] = dS[ct][jj];
     }
 }
-
 
 // ================================================================== gradients ====
 template <typename IO, int DK, int DV, int C>
@@ -1055,7 +1146,7 @@ __global__ void __launch_bounds__(64 * (DK / 16)) kda_bwd_grad_kernel(BwdParams 
 
 template <typename IO, int DK, int DV, int C>
 constexpr bool bwd_fits() {
-    return BwdScanLayout<IO, DK, kBwdScanTile, C>::kFits && BwdGradLayout<IO, DK, DV, C>::kFits;
+    return BwdPrepLayout<IO, DK, C>::kFits && BwdScanLayout<IO, DK, C>::kFits && BwdGradLayout<IO, DK, DV, C>::kFits;
 }
 
 template <typename IO, int DK, int DV, int C>
@@ -1073,8 +1164,8 @@ hipError_t launch_bwd_variant(const BwdParams &bp, hipStream_t stream) {
         }
         const int64_t scan_blocks = (int64_t)p.num_seqs * p.H * (DV / kBwdScanTile);
         if (scan_blocks > 0) {
-            hipLaunchKernelGGL((kda_bwd_scan_kernel<IO, DK, kBwdScanTile, C>), dim3((unsigned)scan_blocks),
-                               dim3(kChunkThreads), 0, stream, bp, (const char *)bp.brec);
+            hipLaunchKernelGGL((kda_bwd_scan_kernel<IO, DK, C>), dim3((unsigned)scan_blocks),
+                               dim3(BwdScanLayout<IO, DK, C>::NT), 0, stream, bp, (const char *)bp.brec);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
@@ -1096,7 +1187,7 @@ hipError_t launch_bwd_variant(const BwdParams &bp, hipStream_t stream) {
 template <typename IO>
 size_t bwd_record_bytes(int dk, int chunk) {
 #define KDA_BWD_REC_CASE(DK_, DV_, C_) \
-    if (dk == DK_ && chunk == C_) return BwdRec<IO, DK_, kBwdScanTile, C_>::kBytes;
+    if (dk == DK_ && chunk == C_) return BwdRec<IO, DK_, C_>::kBytes;
     KDA_BWD_VARIANTS(KDA_BWD_REC_CASE)
 #undef KDA_BWD_REC_CASE
     return 0;

@@ -263,9 +263,10 @@ def test_bwd_workspace_query():
     # states and their gradients (fp32) and D and dU tiles (bf16), in 256-byte sections
     a256 = lambda x: (x + 255) // 256 * 256
     rec = (3 * 16384 + 2 * 6144 + 512 + 1023) // 1024 * 1024  # whole KB: 62,464
-    # reverse-scan records: K- rows, Q~^T, K~^T (16 KB each), P^T, A^T (8 KB each), the inverted
-    # diagonal blocks (4 KB fp32), e^{G_C} and beta: 70,400 B per chunk and head
-    brec = 3 * 16384 + 2 * 8192 + 4096 + 512 + 256
+    # reverse-scan records as the scan keeps them in LDS (rows padded by 16 B): M [64][136] and
+    # N [64][72], Q~^T and (beta K~)^T [128][72] (bf16), e^{G_C} and beta (fp32): 64,256 B,
+    # rounded up to whole KB
+    brec = (64 * 136 * 2 + 64 * 72 * 2 + 2 * 128 * 72 * 2 + 512 + 256 + 1023) // 1024 * 1024
     slots = 2 * 2  # 2 sequences x ceil(100 / 64)
     assert n.value == a256(256 + slots * 2 * rec) + 2 * slots * 2 * 128 * 128 * 4 + 2 * slots * 2 * 64 * 128 * 2 + \
         a256(slots * 2 * brec)
