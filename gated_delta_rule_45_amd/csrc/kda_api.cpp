@@ -264,7 +264,7 @@ kda_status_t resolve_bwd(const kda_problem_t *p, bool varlen, BwdResolved &b) {
     if (!bwd_variant_supported(p->io_dtype, dk, dv, b.chunk))
         return fail(KDA_ERR_UNSUPPORTED, "backward: no compiled variant for io=%s d_k=%d d_v=%d chunk=%d (LDS)",
                     p->io_dtype == KDA_BF16 ? "bf16" : "fp32", dk, dv, b.chunk);
-    b.two_pass = dv % 64 == 0 && kda::split_variant_supported(p->io_dtype, dk, b.chunk, 2, 2);
+    b.two_pass = dv % 64 == 0 && kda::split_variant_supported(p->io_dtype, dk, b.chunk, 2, 2, true);
     b.fwd_dv_tile = 0;
     if (!b.two_pass) {
         for (int t : {default_dv_tile((int64_t)b.r.num_seqs * p->num_heads, dv), 32})
@@ -280,7 +280,7 @@ kda_status_t resolve_bwd(const kda_problem_t *p, bool varlen, BwdResolved &b) {
     b.slots = varlen ? per + b.r.num_seqs : (int64_t)b.r.num_seqs * per;
     if (b.slots * p->num_heads > 0x7fffffffLL) return fail(KDA_ERR_UNSUPPORTED, "too many chunks");
     const size_t s_io = p->io_dtype == KDA_BF16 ? 2 : 4;
-    const size_t states = align256((size_t)b.slots * p->num_heads * dk * dv * 4);
+    const size_t states = align256((size_t)b.slots * p->num_heads * dk * dv * s_io);  // operand type
     const size_t tiles = align256((size_t)b.slots * p->num_heads * b.chunk * dv * s_io);
     // [chunk offsets][two-pass records (when two-pass)][states][state gradients][D][dU]
     b.off_hs = b.two_pass ? align256(kda::split_workspace_bytes(p->io_dtype, dk, b.chunk, b.slots, p->num_heads,
@@ -320,8 +320,8 @@ size_t split_workspace_bytes(kda_dtype_t io, int dk, int chunk, int64_t chunk_up
     return split_plan_bytes(num_seqs) + (size_t)chunk_upper * H * rec;
 }
 
-bool split_variant_supported(kda_dtype_t io, int dk, int chunk, int spw, int nw) {
-    return io == KDA_BF16 ? split_supported_bf16(dk, chunk, spw, nw) : split_supported_f32(dk, chunk, spw, nw);
+bool split_variant_supported(kda_dtype_t io, int dk, int chunk, int spw, int nw, bool keep) {
+    return io == KDA_BF16 ? split_supported_bf16(dk, chunk, spw, nw, keep) : split_supported_f32(dk, chunk, spw, nw, keep);
 }
 
 hipError_t launch_split_fwd(kda_dtype_t io, const FwdParams &p, int chunk, int spw, int nw, char *workspace,
@@ -429,7 +429,7 @@ kda_status_t kda_chunk_bwd(const kda_problem_t *problem, const void *q, const vo
         char *ws = static_cast<char *>(workspace);
         int32_t *chunk_off = reinterpret_cast<int32_t *>(ws);
         kda::FwdParams fp = make_params(problem, r, q, k, v, g, beta, initial_state, cu_seqlens, nullptr, nullptr);
-        fp.hs = reinterpret_cast<float *>(ws + b.off_hs);
+        fp.hs = ws + b.off_hs;
         fp.dch = ws + b.off_dch;
         fp.chunk_off = varlen ? chunk_off : nullptr;
         if (b.two_pass) {  // the two-pass forward builds the chunk-offset table itself
@@ -456,7 +456,7 @@ kda_status_t kda_chunk_bwd(const kda_problem_t *problem, const void *q, const vo
         bp.dbeta = dbeta;
         bp.ds0 = d_initial_state;
         bp.hs = fp.hs;
-        bp.dhs = reinterpret_cast<float *>(ws + b.off_dhs);
+        bp.dhs = ws + b.off_dhs;
         bp.dch = fp.dch;
         bp.duch = ws + b.off_duch;
         bp.brec = ws + b.off_brec;

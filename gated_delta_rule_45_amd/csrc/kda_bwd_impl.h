@@ -665,20 +665,16 @@ __global__ void __launch_bounds__(kBwdScanThreads) kda_bwd_scan_kernel(BwdParams
         const float *sBeta = reinterpret_cast<const float *>(rb + Rec::oBeta);
         const int64_t slot_base = (slot0 + ci) * H + h;
 
-        // gradient of the state this chunk hands on, kept for the gradient kernel: written to the
-        // wave's LDS tile in the accumulator layout, read back as 4 consecutive columns of a row
+        // gradient of the state this chunk hands on, kept for the gradient kernel (operand type):
+        // written to the wave's LDS tile in the accumulator layout, read back as row segments
         {
 #pragma unroll
             for (int ct = 0; ct < KT; ++ct)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) sH[(16 * ct + 4 * q4 + jj) * LDH + l16] = dS[ct][jj];
-            float *dh = bp.dhs + slot_base * DK * DV + col0 + 16 * wave + 4 * (lane & 3);
+            OT *dh = static_cast<OT *>(bp.dhs) + slot_base * DK * DV + col0 + 16 * wave;
 #pragma unroll
-            for (int ct = 0; ct < KT; ++ct) {
-                const int row = 16 * ct + (lane >> 2);
-                *reinterpret_cast<float4 *>(dh + (int64_t)row * DV) =
-                    *reinterpret_cast<const float4 *>(sH + row * LDH + 4 * (lane & 3));
-            }
+            for (int ct = 0; ct < KT; ++ct) keep_rows<OT, 16, LDH>(dh + (int64_t)16 * ct * DV, DV, sH + 16 * ct * LDH, lane);
         }
         Frag<BF> Sb[KT];
 #pragma unroll
@@ -959,17 +955,17 @@ __global__ void __launch_bounds__(64 * (DK / 16)) kda_bwd_grad_kernel(BwdParams 
     //      A operands straight from the chunk states), and rowsum(dS .* S)
     f32x4 Zq[NSUB], Zu[NSUB], Zs[NSUB];
     {
-        const float *Sr = bp.hs + base * DK * DV + (int64_t)(cw + l16) * DV + 4 * q4;
-        const float *dSr = bp.dhs + base * DK * DV + (int64_t)(cw + l16) * DV + 4 * q4;
+        // the states are stored in the operand type: 4 consecutive columns are an A fragment
+        const OT *Sr = static_cast<const OT *>(bp.hs) + base * DK * DV + (int64_t)(cw + l16) * DV + 4 * q4;
+        const OT *dSr = static_cast<const OT *>(bp.dhs) + base * DK * DV + (int64_t)(cw + l16) * DV + 4 * q4;
         Frag<BF> sf[DV / 16], dsf[DV / 16];
         float gam = 0.f;
 #pragma unroll
         for (int kt = 0; kt < DV / 16; ++kt) {
-            const float4 a = *reinterpret_cast<const float4 *>(Sr + 16 * kt);
-            const float4 b = *reinterpret_cast<const float4 *>(dSr + 16 * kt);
+            sf[kt] = lds_frag(Sr + 16 * kt);
+            dsf[kt] = lds_frag(dSr + 16 * kt);
+            const float4 a = unpack4<BF>(sf[kt].v), b = unpack4<BF>(dsf[kt].v);
             gam += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
-            sf[kt] = make_frag<BF>(a.x, a.y, a.z, a.w);
-            dsf[kt] = make_frag<BF>(b.x, b.y, b.z, b.w);
         }
         gam += __shfl_xor(gam, 16);
         gam += __shfl_xor(gam, 32);

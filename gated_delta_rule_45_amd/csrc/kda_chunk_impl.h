@@ -429,12 +429,15 @@ __global__ void __launch_bounds__(kChunkThreads) kda_chunk_fwd_kernel(FwdParams 
             if (sl >= NSL) break;
             const int col = col0 + 16 * sl + l16;
             const int64_t slot_base = ((slot0 + c0 / C) * H + h);
-            if (p.hs) {
-                float *hs = p.hs + slot_base * DK * DV + col;
+            if (p.hs) {  // operand type, as the backward reads it
+                OT *hs = static_cast<OT *>(p.hs) + slot_base * DK * DV + col;
 #pragma unroll
                 for (int ct = 0; ct < KT; ++ct)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) hs[(int64_t)(16 * ct + 4 * q4 + j) * DV] = S[s][ct][j];
+                    for (int j = 0; j < 4; ++j) {
+                        if constexpr (BF) hs[(int64_t)(16 * ct + 4 * q4 + j) * DV] = f32_to_bf16(S[s][ct][j]);
+                        else hs[(int64_t)(16 * ct + 4 * q4 + j) * DV] = S[s][ct][j];
+                    }
             }
 
             Frag<BF> Sb[KT];

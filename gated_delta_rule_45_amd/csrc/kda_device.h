@@ -146,6 +146,31 @@ __device__ __forceinline__ f32x4 zero4() {
     return z;
 }
 
+// Writes a 16 x WC fp32 tile held in LDS (row stride LDK floats) to dst (row stride ld elements,
+// element type OT: bf16 bits or fp32) as 16-byte row segments spread over the lanes of one wave.
+// Used to turn accumulator fragments (4 rows of one column per lane) into few wide stores.
+template <typename OT, int WC, int LDK>
+__device__ __forceinline__ void keep_rows(OT *dst, int64_t ld, const float *tile, int lane) {
+    constexpr int EPS = 16 / (int)sizeof(OT), SPR = WC / EPS, NSEG = 16 * SPR;
+    static_assert(WC % EPS == 0 && LDK % 4 == 0, "whole 16-byte segments");
+#pragma unroll
+    for (int i = 0; i < (NSEG + 63) / 64; ++i) {
+        const int sg = lane + 64 * i;
+        if (NSEG % 64 == 0 || sg < NSEG) {
+            const int row = sg / SPR, c0 = (sg % SPR) * EPS;
+            const float *src = tile + row * LDK + c0;
+            if constexpr (sizeof(OT) == 2) {
+                const float4 a = *reinterpret_cast<const float4 *>(src);
+                const float4 b = *reinterpret_cast<const float4 *>(src + 4);
+                const uint2 lo = make_frag<true>(a.x, a.y, a.z, a.w).v, hi = make_frag<true>(b.x, b.y, b.z, b.w).v;
+                *reinterpret_cast<uint4 *>(dst + row * ld + c0) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            } else {
+                *reinterpret_cast<float4 *>(dst + row * ld + c0) = *reinterpret_cast<const float4 *>(src);
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------ io element types --
 // q, k, v and out are fp32 or bf16 in memory; g, beta and states are fp32.
 template <typename IO>

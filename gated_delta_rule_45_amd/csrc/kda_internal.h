@@ -19,12 +19,12 @@ struct FwdParams {
     float *sf;           // [num_seqs, H, DK, DV] or null
     int32_t num_seqs, T, H, dk, dv;
     float scale;
-    // Optional per-chunk outputs of the fused forward, kept for the backward pass:
-    // hs [slot, H, DK, DV] fp32 state entering each chunk, dch [slot, H, C, DV] the
-    // chunk's delta-rule corrections D (operand type).  slot = chunk_off[n] + chunk index
+    // Optional per-chunk outputs of the forward, kept for the backward pass:
+    // hs [slot, H, DK, DV] the state entering each chunk, dch [slot, H, C, DV] the
+    // chunk's delta-rule corrections D (both in the operand type: bf16 for bf16 io).  slot = chunk_off[n] + chunk index
     // for a packed batch (chunk_off from the plan kernel), n * ceil(T / C) + chunk index
     // otherwise.
-    float *hs = nullptr;
+    void *hs = nullptr;
     void *dch = nullptr;
     const int32_t *chunk_off = nullptr;
 };
@@ -55,14 +55,14 @@ constexpr int kChunkThreads = 256;
 // Two-pass forward: bytes of the chunk-offset table at the start of the workspace.
 inline size_t split_plan_bytes(int64_t num_seqs) { return (size_t)(((num_seqs + 1) * 4 + 255) / 256 * 256); }
 size_t split_workspace_bytes(kda_dtype_t io, int dk, int chunk, int64_t chunk_upper, int H, int64_t num_seqs);
-bool split_variant_supported(kda_dtype_t io, int dk, int chunk, int spw, int nw);
+bool split_variant_supported(kda_dtype_t io, int dk, int chunk, int spw, int nw, bool keep = false);
 hipError_t launch_split_fwd(kda_dtype_t io, const FwdParams &p, int chunk, int spw, int nw, char *workspace,
                             int64_t chunk_upper, hipStream_t stream);
 // one entry per io dtype
 size_t split_record_size_f32(int dk, int chunk);
 size_t split_record_size_bf16(int dk, int chunk);
-bool split_supported_f32(int dk, int chunk, int spw, int nw);
-bool split_supported_bf16(int dk, int chunk, int spw, int nw);
+bool split_supported_f32(int dk, int chunk, int spw, int nw, bool keep);
+bool split_supported_bf16(int dk, int chunk, int spw, int nw, bool keep);
 hipError_t launch_split_f32(const FwdParams &p, int chunk, int spw, int nw, char *workspace, int64_t chunk_upper,
                             hipStream_t stream);
 hipError_t launch_split_bf16(const FwdParams &p, int chunk, int spw, int nw, char *workspace, int64_t chunk_upper,
@@ -79,8 +79,8 @@ struct BwdParams {
     float *dg;            // [tokens, H, DK]
     float *dbeta;         // [tokens, H]
     float *ds0;           // [num_seqs, H, DK, DV] or null
-    const float *hs;      // [slot, H, DK, DV] chunk initial states (written by the forward pass)
-    float *dhs;           // [slot, H, DK, DV] gradient of each chunk's final state
+    const void *hs;       // [slot, H, DK, DV] chunk initial states (operand type; forward pass)
+    void *dhs;            // [slot, H, DK, DV] gradient of each chunk's final state (operand type)
     const void *dch;      // [slot, H, C, DV] D per chunk (operand type)
     void *duch;           // [slot, H, C, DV] dU per chunk (operand type)
     char *brec;           // [slot, H] reverse-scan records (kda_bwd_prep_kernel)

@@ -477,6 +477,11 @@ struct ScanLayout {
     static_assert(Rec::kBytes % (64 * 16) == 0, "record is copied in whole wave units");
     static_assert(V_PIECES % 64 == 0, "V tile is copied in whole wave units");
     static_assert(!kFits || (Rec::kBytes / 1024 + V_PIECES / 64 + 1) / 2 <= 40, "copy wave register budget");
+    // KEEP only: a per-compute-wave fp32 tile [16][LDK] through which the kept state and D leave
+    // as 16-byte row segments (a few wide stores instead of one per accumulator element)
+    static constexpr int LDK = WCOLS + 4;
+    static constexpr size_t kKeepBytes = (size_t)NW * 16 * LDK * 4;
+    static constexpr bool kFitsKeep = kFits && kBytes + kKeepBytes <= 160 * 1024;
 };
 
 // One copy wave's half of a chunk's record and V tile (1 KB units dealt alternately to the two
@@ -576,7 +581,7 @@ __global__ void __launch_bounds__(64 * (NW + scan_copy_waves(SPW))) kda_scan_ker
     constexpr int NSUB = Rec::NSUB, KT = Rec::KT, NPAIR = Rec::NPAIR, DVT = S::DVT, WC = S::WCOLS;
     using Tr = IoTraits<IO>;
 
-    __shared__ __attribute__((aligned(16))) char smem[S::kBytes];
+    __shared__ __attribute__((aligned(16))) char smem[S::kBytes + (KEEP ? S::kKeepBytes : 0)];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -633,6 +638,7 @@ __global__ void __launch_bounds__(64 * (NW + scan_copy_waves(SPW))) kda_scan_ker
 
     // ---------------- compute waves: slice s holds state columns col0 + WC*wave + 16*s + l16
     f32x4 St[SPW][KT];
+    [[maybe_unused]] float *keep_tile = KEEP ? reinterpret_cast<float *>(smem + S::kBytes) + wave * 16 * S::LDK : nullptr;
     const int64_t sbase = ((int64_t)n * H + h) * DK * DV;
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
@@ -667,13 +673,15 @@ __global__ void __launch_bounds__(64 * (NW + scan_copy_waves(SPW))) kda_scan_ker
         // optional: the state entering this chunk, kept for the backward pass
         const int64_t slot_base = (g0 + c) * H + h;
         if constexpr (KEEP) {
+            using OT = typename std::conditional<BF, uint16_t, float>::type;
+            OT *hs = static_cast<OT *>(p.hs) + slot_base * DK * DV + col0 + WC * wave;
 #pragma unroll
-            for (int s = 0; s < SPW; ++s) {
-                float *hs = p.hs + slot_base * DK * DV + col0 + WC * wave + 16 * s + l16;
+            for (int ct = 0; ct < KT; ++ct) {
 #pragma unroll
-                for (int ct = 0; ct < KT; ++ct)
+                for (int s = 0; s < SPW; ++s)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) hs[(int64_t)(16 * ct + 4 * q4 + j) * DV] = St[s][ct][j];
+                    for (int j = 0; j < 4; ++j) keep_tile[(4 * q4 + j) * S::LDK + 16 * s + l16] = St[s][ct][j];
+                keep_rows<OT, WC, S::LDK>(hs + (int64_t)16 * ct * DV, DV, keep_tile, lane);
             }
         }
         const char *rb = smem + ((c & 1) ? S::oRec1 : S::oRec0);
@@ -770,24 +778,16 @@ __global__ void __launch_bounds__(64 * (NW + scan_copy_waves(SPW))) kda_scan_ker
 #pragma unroll
                         for (int s = 0; s < SPW; ++s) mma32(d[s], Tf[R][pp].a, Tf[R][pp].b, Yb[s][2 * pp], Yb[s][2 * pp + 1]);
 #pragma unroll
-                for (int s = 0; s < SPW; ++s) {
-                    Db[s][R] = frag_from_acc<BF>(d[s]);
-                    if constexpr (KEEP) {  // D of this chunk for the backward pass (operand type)
-                        using OT = typename std::conditional<BF, uint16_t, float>::type;
-                        OT *dc = static_cast<OT *>(p.dch) + slot_base * C * DV + (int64_t)(16 * R + 4 * q4) * DV +
-                                 col0 + WC * wave + 16 * s + l16;
-                        if constexpr (BF) {
-                            dc[0] = (uint16_t)(Db[s][R].v.x & 0xffffu);
-                            dc[DV] = (uint16_t)(Db[s][R].v.x >> 16);
-                            dc[2 * DV] = (uint16_t)(Db[s][R].v.y & 0xffffu);
-                            dc[3 * DV] = (uint16_t)(Db[s][R].v.y >> 16);
-                        } else {
-                            dc[0] = Db[s][R].v.x;
-                            dc[DV] = Db[s][R].v.y;
-                            dc[2 * DV] = Db[s][R].v.z;
-                            dc[3 * DV] = Db[s][R].v.w;
-                        }
-                    }
+                for (int s = 0; s < SPW; ++s) Db[s][R] = frag_from_acc<BF>(d[s]);
+                if constexpr (KEEP) {  // D of this chunk for the backward pass (operand type)
+                    using OT = typename std::conditional<BF, uint16_t, float>::type;
+#pragma unroll
+                    for (int s = 0; s < SPW; ++s)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) keep_tile[(4 * q4 + j) * S::LDK + 16 * s + l16] = d[s][j];
+                    keep_rows<OT, WC, S::LDK>(static_cast<OT *>(p.dch) + slot_base * C * DV + (int64_t)16 * R * DV +
+                                                  col0 + WC * wave,
+                                              DV, keep_tile, lane);
                 }
             }
             if constexpr (NSUB % 2 == 1)
@@ -877,6 +877,7 @@ hipError_t launch_split_variant(const FwdParams &p, char *workspace, int64_t chu
     if constexpr (!split_fits<IO, DK, C, SPW, NW>()) {
         return hipErrorInvalidConfiguration;
     } else {
+        if (keep && !ScanLayout<IO, DK, C, SPW, NW>::kFitsKeep) return hipErrorInvalidConfiguration;
         int32_t *chunk_off = reinterpret_cast<int32_t *>(workspace);
         char *records = workspace + split_plan_bytes(p.num_seqs);
         if (p.cu) {
@@ -921,9 +922,11 @@ size_t split_record_size(int dk, int chunk) {
 }
 
 template <typename IO>
-bool split_supported(int dk, int chunk, int spw, int nw) {
-#define KDA_FIT_CASE(DK_, C_, SPW_, NW_) \
-    if (dk == DK_ && chunk == C_ && spw == SPW_ && nw == NW_) return split_fits<IO, DK_, C_, SPW_, NW_>();
+bool split_supported(int dk, int chunk, int spw, int nw, bool keep) {
+#define KDA_FIT_CASE(DK_, C_, SPW_, NW_)                                       \
+    if (dk == DK_ && chunk == C_ && spw == SPW_ && nw == NW_)                 \
+        return split_fits<IO, DK_, C_, SPW_, NW_>() &&                        \
+               (!keep || ScanLayout<IO, DK_, C_, SPW_, NW_>::kFitsKeep);
     KDA_SPLIT_VARIANTS(KDA_FIT_CASE)
 #undef KDA_FIT_CASE
     return false;

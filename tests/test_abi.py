@@ -260,7 +260,7 @@ def test_bwd_workspace_query():
     n = ctypes.c_size_t(0)
     assert lib.kda_chunk_bwd_workspace(ctypes.byref(_bwd_problem()), ctypes.byref(n)) == kda.KDA_OK
     # plan + two-pass records (62,464 B per chunk and head at bf16, d_k = 128, chunk 64), then chunk
-    # states and their gradients (fp32) and D and dU tiles (bf16), in 256-byte sections
+    # states and their gradients, D and dU tiles (all bf16, the operand type), in 256-byte sections
     a256 = lambda x: (x + 255) // 256 * 256
     rec = (3 * 16384 + 2 * 6144 + 512 + 1023) // 1024 * 1024  # whole KB: 62,464
     # reverse-scan records as the scan keeps them in LDS (rows padded by 16 B): M [64][136] and
@@ -268,13 +268,13 @@ def test_bwd_workspace_query():
     # rounded up to whole KB
     brec = (64 * 136 * 2 + 64 * 72 * 2 + 2 * 128 * 72 * 2 + 512 + 256 + 1023) // 1024 * 1024
     slots = 2 * 2  # 2 sequences x ceil(100 / 64)
-    assert n.value == a256(256 + slots * 2 * rec) + 2 * slots * 2 * 128 * 128 * 4 + 2 * slots * 2 * 64 * 128 * 2 + \
+    assert n.value == a256(256 + slots * 2 * rec) + 2 * slots * 2 * 128 * 128 * 2 + 2 * slots * 2 * 64 * 128 * 2 + \
         a256(slots * 2 * brec)
     # a packed batch reserves one partial chunk per sequence
     assert lib.kda_chunk_bwd_workspace(ctypes.byref(_bwd_problem(batch=1, seq_len=300, num_seqs=5)),
                                        ctypes.byref(n)) == kda.KDA_OK
     slots = 5 + 5
-    assert n.value == a256(256 + slots * 2 * rec) + 2 * slots * 2 * 128 * 128 * 4 + 2 * slots * 2 * 64 * 128 * 2 + \
+    assert n.value == a256(256 + slots * 2 * rec) + 2 * slots * 2 * 128 * 128 * 2 + 2 * slots * 2 * 64 * 128 * 2 + \
         a256(slots * 2 * brec)
     assert lib.kda_chunk_bwd_workspace(ctypes.byref(_bwd_problem(chunk_size=48)), ctypes.byref(n)) == \
         kda.KDA_ERR_UNSUPPORTED
