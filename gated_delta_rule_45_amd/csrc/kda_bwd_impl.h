@@ -849,25 +849,33 @@ __global__ void __launch_bounds__(64 * (DK / 16)) kda_bwd_grad_kernel(BwdParams 
     const int cw = 16 * wave;  // first key channel of this wave
 
     // ---- key side of the wave's channels for every token: lane (token 16R + l16, channels cw + 4q4 + j)
-    float G[NSUB][4], kk[NSUB][4], qq[NSUB][4];
+    // (k and q stay packed as loaded and are unpacked where used)
+    using KQ = typename std::conditional<BF, uint2, float4>::type;
+    float G[NSUB][4];
+    KQ kraw[NSUB], qraw[NSUB];
 #pragma unroll
     for (int R = 0; R < NSUB; ++R) {
         const int r = 16 * R + l16;
         const bool valid = r < clen;
         const int64_t row = ((tok0 + min(r, clen - 1)) * H + h) * (int64_t)DK + cw + 4 * q4;
         const float4 gv = *reinterpret_cast<const float4 *>(p.g + row);
-        const float4 kv = Tr::load4(static_cast<const IO *>(p.k) + row);
-        const float4 qv = Tr::load4(static_cast<const IO *>(p.q) + row);
+        const KQ kv = *reinterpret_cast<const KQ *>(static_cast<const IO *>(p.k) + row);
+        const KQ qv = *reinterpret_cast<const KQ *>(static_cast<const IO *>(p.q) + row);
         const float m = valid ? kLog2e : 0.f;
         G[R][0] = scan16_add(gv.x * m);
         G[R][1] = scan16_add(gv.y * m);
         G[R][2] = scan16_add(gv.z * m);
         G[R][3] = scan16_add(gv.w * m);
-        kk[R][0] = valid ? kv.x : 0.f; kk[R][1] = valid ? kv.y : 0.f;
-        kk[R][2] = valid ? kv.z : 0.f; kk[R][3] = valid ? kv.w : 0.f;
-        qq[R][0] = valid ? qv.x : 0.f; qq[R][1] = valid ? qv.y : 0.f;
-        qq[R][2] = valid ? qv.z : 0.f; qq[R][3] = valid ? qv.w : 0.f;
+        kraw[R] = valid ? kv : KQ{};
+        qraw[R] = valid ? qv : KQ{};
     }
+    auto unpk = [](const KQ &x, float (&o)[4]) {
+        const float4 v = unpack4<BF>(x);
+        o[0] = v.x;
+        o[1] = v.y;
+        o[2] = v.z;
+        o[3] = v.w;
+    };
 
     // ---- stage dO, dU, D ([C][DV]); sum_j dU_rj V_rj per token
     if (tid < C) sBeta[tid] = tid < clen ? p.beta[(tok0 + tid) * H + h] : 0.f;
@@ -951,14 +959,15 @@ __global__ void __launch_bounds__(64 * (DK / 16)) kda_bwd_grad_kernel(BwdParams 
         *reinterpret_cast<decltype(fl.v) *>(sLT + (16 * I + l16) * LDC + 16 * R + 4 * q4) = fl.v;
     }
 
-    // ---- S dO^T, S dU^T, dS D^T for the wave's channels (rows c = cw + l16 of S and dS as
-    //      A operands straight from the chunk states), and rowsum(dS .* S)
-    f32x4 Zq[NSUB], Zu[NSUB], Zs[NSUB];
+    // ---- rows c = cw + l16 of S and dS (A operands straight from the chunk states), rowsum(dS .* S),
+    //      and dS D^T; S dO^T and S dU^T are formed later, just before the row side needs them
+    Frag<BF> sf[DV / 16];
+    f32x4 Zs[NSUB];
     {
         // the states are stored in the operand type: 4 consecutive columns are an A fragment
         const OT *Sr = static_cast<const OT *>(bp.hs) + base * DK * DV + (int64_t)(cw + l16) * DV + 4 * q4;
         const OT *dSr = static_cast<const OT *>(bp.dhs) + base * DK * DV + (int64_t)(cw + l16) * DV + 4 * q4;
-        Frag<BF> sf[DV / 16], dsf[DV / 16];
+        Frag<BF> dsf[DV / 16];
         float gam = 0.f;
 #pragma unroll
         for (int kt = 0; kt < DV / 16; ++kt) {
@@ -973,18 +982,11 @@ __global__ void __launch_bounds__(64 * (DK / 16)) kda_bwd_grad_kernel(BwdParams 
         __syncthreads();  // dP / dA blocks complete
 #pragma unroll
         for (int R = 0; R < NSUB; ++R) {
-            Zq[R] = zero4();
-            Zu[R] = zero4();
             Zs[R] = zero4();
-            const OT *bo = sO + (16 * R + l16) * LDV + 4 * q4;
-            const OT *bu = sU + (16 * R + l16) * LDV + 4 * q4;
             const OT *bdd = sD + (16 * R + l16) * LDV + 4 * q4;
 #pragma unroll
-            for (int kt = 0; kt < DV / 16; kt += 2) {
-                mma32(Zq[R], sf[kt], sf[kt + 1], lds_frag(bo + 16 * kt), lds_frag(bo + 16 * kt + 16));
-                mma32(Zu[R], sf[kt], sf[kt + 1], lds_frag(bu + 16 * kt), lds_frag(bu + 16 * kt + 16));
+            for (int kt = 0; kt < DV / 16; kt += 2)
                 mma32(Zs[R], dsf[kt], dsf[kt + 1], lds_frag(bdd + 16 * kt), lds_frag(bdd + 16 * kt + 16));
-            }
         }
     }
 
@@ -998,90 +1000,121 @@ __global__ void __launch_bounds__(64 * (DK / 16)) kda_bwd_grad_kernel(BwdParams 
         for (int j = 0; j < 4; ++j) bnd[R + 1][j] = bnd[R][j] + __shfl(G[R][j], 16 * q4 + 15);
 
     // transposed operands through the identity: A operands with rows = channels
-    Frag<BF> kbT[NSUB], qrT[NSUB], krT[NSUB];
+    const Frag<BF> eye = make_frag<BF>(4 * q4 == l16 ? 1.f : 0.f, 4 * q4 + 1 == l16 ? 1.f : 0.f,
+                                       4 * q4 + 2 == l16 ? 1.f : 0.f, 4 * q4 + 3 == l16 ? 1.f : 0.f);
+    Frag<BF> kbT[NSUB];
+#pragma unroll
+    for (int R = 0; R < NSUB; ++R) {
+        float kb[4], kk[4];
+        unpk(kraw[R], kk);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kb[j] = kk[j] * fast_exp2(bnd[R + 1][j] - bnd[R][j] - G[R][j]);  // k e^{b_{R+1} - G}
+        f32x4 t = zero4();
+        mma16(t, make_frag<BF>(kb[0], kb[1], kb[2], kb[3]), eye);
+        kbT[R] = frag_from_acc<BF>(t);
+    }
+
+    // ---- column side (tokens of I): Col_I = sum_{R >= I} e^{b_R - b_{I+1}} (q_r dP_ri + k_r dL_ri),
+    //      finished into the parts of dk that do not need the row side (via K^ and via K-)
+    float dkc[NSUB][4], dG[NSUB][4], gcs[4] = {0.f, 0.f, 0.f, 0.f};
     {
-        const Frag<BF> eye = make_frag<BF>(4 * q4 == l16 ? 1.f : 0.f, 4 * q4 + 1 == l16 ? 1.f : 0.f,
-                                           4 * q4 + 2 == l16 ? 1.f : 0.f, 4 * q4 + 3 == l16 ? 1.f : 0.f);
+        Frag<BF> qrT[NSUB], krT[NSUB];
 #pragma unroll
         for (int R = 0; R < NSUB; ++R) {
-            float kb[4], kr[4], qr[4];
+            float kr[4], qr[4], kk[4], qq[4];
+            unpk(kraw[R], kk);
+            unpk(qraw[R], qq);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float tot = bnd[R + 1][j] - bnd[R][j];
-                kb[j] = kk[R][j] * fast_exp2(tot - G[R][j]);  // k e^{b_{R+1} - G}  (<= 1)
-                const float fr = fast_exp2(G[R][j]);          // e^{G - b_R}        (<= 1)
-                kr[j] = kk[R][j] * fr;
-                qr[j] = qq[R][j] * fr;
+                const float fr = fast_exp2(G[R][j]);  // e^{G - b_R} (<= 1)
+                kr[j] = kk[j] * fr;
+                qr[j] = qq[j] * fr;
             }
             f32x4 t = zero4();
-            mma16(t, make_frag<BF>(kb[0], kb[1], kb[2], kb[3]), eye);
-            kbT[R] = frag_from_acc<BF>(t);
-            t = zero4();
             mma16(t, make_frag<BF>(kr[0], kr[1], kr[2], kr[3]), eye);
             krT[R] = frag_from_acc<BF>(t);
             t = zero4();
             mma16(t, make_frag<BF>(qr[0], qr[1], qr[2], qr[3]), eye);
             qrT[R] = frag_from_acc<BF>(t);
         }
-    }
-
-    // ---- C x C contractions; outputs (channel x token) in the lane layout above
-    f32x4 RowP[NSUB], RowA[NSUB], Col[NSUB];
+        f32x4 Col[NSUB];
 #pragma unroll
-    for (int R = 0; R < NSUB; ++R) {
-        RowP[R] = zero4();
-        RowA[R] = zero4();
-        Col[R] = zero4();
-    }
+        for (int I = 0; I < NSUB; ++I) Col[I] = zero4();
 #pragma unroll
-    for (int R = 0; R < NSUB; ++R) {
+        for (int R = 0; R < NSUB; ++R) {
 #pragma unroll
-        for (int I = 0; I <= R; ++I) {
-            // row side (tokens of R): sum_{i in I} kb_i dP_ri, kb_i dA_ri
-            f32x4 tp = zero4(), ta = zero4();
-            mma16(tp, kbT[I], lds_frag(sP + (16 * R + l16) * LDC + 16 * I + 4 * q4));
-            mma16(ta, kbT[I], lds_frag(sA + (16 * R + l16) * LDC + 16 * I + 4 * q4));
-            // column side (tokens of I): sum_{r in R} qrow_r dP_ri + krow_r dL_ri
-            f32x4 tc = zero4();
-            mma16(tc, qrT[R], lds_frag(sPT + (16 * I + l16) * LDC + 16 * R + 4 * q4));
-            mma16(tc, krT[R], lds_frag(sLT + (16 * I + l16) * LDC + 16 * R + 4 * q4));
+            for (int I = 0; I <= R; ++I) {
+                f32x4 tc = zero4();
+                mma16(tc, qrT[R], lds_frag(sPT + (16 * I + l16) * LDC + 16 * R + 4 * q4));
+                mma16(tc, krT[R], lds_frag(sLT + (16 * I + l16) * LDC + 16 * R + 4 * q4));
+#pragma unroll
+                for (int j = 0; j < 4; ++j) Col[I][j] += fast_exp2(bnd[R][j] - bnd[I + 1][j]) * tc[j];
+            }
+        }
+#pragma unroll
+        for (int R = 0; R < NSUB; ++R) {
+            float kk[4];
+            unpk(kraw[R], kk);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float sh = fast_exp2(bnd[R][j] - bnd[I + 1][j]);  // e^{b_R - b_{I+1}}
-                RowP[R][j] += sh * tp[j];
-                RowA[R][j] += sh * ta[j];
-                Col[I][j] += sh * tc[j];
+                const float fb = fast_exp2(bnd[R + 1][j] - bnd[R][j] - G[R][j]);
+                const float ekb = fast_exp2(bnd[NSUB][j] - bnd[R][j] - G[R][j]);
+                const float dk2 = fb * Col[R][j];
+                const float dk3 = ekb * Zs[R][j];
+                dkc[R][j] = dk2 + dk3;
+                dG[R][j] = -kk[j] * (dk2 + dk3);
+                gcs[j] += kk[j] * dk3;
             }
         }
     }
 
-    // ---- combine per (token, channel)
-    float dG[NSUB][4], gcs[4] = {0.f, 0.f, 0.f, 0.f};
+    // ---- row side (tokens of R), one token tile at a time, and the outputs dq, dk:
+    //      RowP_R = sum_{I <= R} e^{b_R - b_{I+1}} kb_i dP_ri, RowA_R likewise with dA
     float dbp[NSUB];
     IO *dqo = static_cast<IO *>(bp.dq);
     IO *dko = static_cast<IO *>(bp.dk);
 #pragma unroll
     for (int R = 0; R < NSUB; ++R) {
+        f32x4 Zq = zero4(), Zu = zero4();
+        {
+            const OT *bo = sO + (16 * R + l16) * LDV + 4 * q4;
+            const OT *bu = sU + (16 * R + l16) * LDV + 4 * q4;
+#pragma unroll
+            for (int kt = 0; kt < DV / 16; kt += 2) {
+                mma32(Zq, sf[kt], sf[kt + 1], lds_frag(bo + 16 * kt), lds_frag(bo + 16 * kt + 16));
+                mma32(Zu, sf[kt], sf[kt + 1], lds_frag(bu + 16 * kt), lds_frag(bu + 16 * kt + 16));
+            }
+        }
+        f32x4 RowP = zero4(), RowA = zero4();
+#pragma unroll
+        for (int I = 0; I <= R; ++I) {
+            f32x4 tp = zero4(), ta = zero4();
+            mma16(tp, kbT[I], lds_frag(sP + (16 * R + l16) * LDC + 16 * I + 4 * q4));
+            mma16(ta, kbT[I], lds_frag(sA + (16 * R + l16) * LDC + 16 * I + 4 * q4));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float sh = fast_exp2(bnd[R][j] - bnd[I + 1][j]);  // e^{b_R - b_{I+1}}
+                RowP[j] += sh * tp[j];
+                RowA[j] += sh * ta[j];
+            }
+        }
         const int r = 16 * R + l16;
         const float b = sBeta[r];
-        float dq4[4], dk4[4];
+        float dq4[4], dk4[4], kk[4], qq[4];
+        unpk(kraw[R], kk);
+        unpk(qraw[R], qq);
         dbp[R] = 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const float fr = fast_exp2(G[R][j]);
-            const float fb = fast_exp2(bnd[R + 1][j] - bnd[R][j] - G[R][j]);
             const float eG = fast_exp2(bnd[R][j] + G[R][j]);
-            const float ekb = fast_exp2(bnd[NSUB][j] - bnd[R][j] - G[R][j]);
-            const float W = fr * RowA[R][j];
-            const float dq = p.scale * eG * Zq[R][j] + fr * RowP[R][j];
-            const float dk1 = b * (W - eG * Zu[R][j]);
-            const float dk2 = fb * Col[R][j];
-            const float dk3 = ekb * Zs[R][j];
+            const float W = fr * RowA[j];
+            const float dq = p.scale * eG * Zq[j] + fr * RowP[j];
+            const float dk1 = b * (W - eG * Zu[j]);
             dq4[j] = dq;
-            dk4[j] = dk1 + dk2 + dk3;
-            dG[R][j] = qq[R][j] * dq + kk[R][j] * (dk1 - dk2 - dk3);
-            gcs[j] += kk[R][j] * dk3;
-            dbp[R] += kk[R][j] * (W - eG * Zu[R][j]);
+            dk4[j] = dk1 + dkc[R][j];
+            dG[R][j] += qq[j] * dq + kk[j] * dk1;
+            dbp[R] += kk[j] * (W - eG * Zu[j]);
         }
         if (r < clen) {
             const int64_t row = ((tok0 + r) * H + h) * (int64_t)DK + cw + 4 * q4;
