@@ -114,6 +114,10 @@ struct BwdRec {
 };
 
 // ====================================================================== prep ====
+// LDS of the prep kernel.  M and N are formed in LDS at their record offsets and copied out
+// with e^{G_C} and beta; Q~^T and (Diag(beta) K~)^T go from registers straight to the record.
+// The K_b rows take M's place (dead before M is formed), and the per-channel gate tables take
+// X's place (dead before A is written there).
 template <typename IO, int DK, int C>
 struct BwdPrepLayout {
     using Rec = BwdRec<IO, DK, C>;
@@ -124,20 +128,22 @@ struct BwdPrepLayout {
     static constexpr int LDO = Rec::LDO, LDT = Rec::LDT, LDM = Rec::LDM;
     static constexpr int LDX = C + 4;  // fp32 [C][C]: A, then X in place
     static constexpr int NSHIFT = NSUB >= 3 ? (NSUB - 1) * (NSUB - 2) / 2 : 0;
-    // The record image comes first and is copied out verbatim.  The K_b rows take M's place:
-    // they are dead before M is formed.
     static constexpr size_t oKb = Rec::oM;
-    static constexpr size_t oKs = Rec::kBytes;
-    static constexpr size_t oKbarT = oKs + (size_t)NSHIFT * 16 * LDO * S;
+    static constexpr size_t oKbarT = Rec::oQtT;  // right after M and N
+    static constexpr size_t kXBytes = (size_t)C * LDX * 4;
+    static constexpr size_t kTabBytes = (size_t)4 * NSUB * DK * 4;  // Tot, EB, ED, EC
     static constexpr size_t oX = oKbarT + (size_t)DK * LDT * S;
-    static constexpr size_t oP = oX + (size_t)C * LDX * 4;
-    static constexpr size_t oTot = oP + (size_t)C * LDM * S;
+    static constexpr size_t oTot = oX;
     static constexpr size_t oEB = oTot + (size_t)NSUB * DK * 4;
     static constexpr size_t oED = oEB + (size_t)NSUB * DK * 4;
     static constexpr size_t oEC = oED + (size_t)NSUB * DK * 4;
-    static constexpr size_t oSH = oEC + (size_t)NSUB * DK * 4;
-    static constexpr size_t kBytes = oSH + (size_t)(NSHIFT > 0 ? NSHIFT : 1) * DK * 4;
+    static constexpr size_t oP = oX + (kXBytes > kTabBytes ? kXBytes : kTabBytes);
+    static constexpr size_t oSH = oP + (size_t)C * LDM * S;
+    static constexpr size_t oGam = oSH + (size_t)(NSHIFT > 0 ? NSHIFT : 1) * DK * 4;  // e^{G_C} then beta, as in the record
+    static constexpr size_t oBeta = oGam + (size_t)DK * 4;
+    static constexpr size_t kBytes = oBeta + (size_t)C * 4;
     static constexpr bool kFits = kBytes <= 160 * 1024;
+    static_assert(Rec::oBeta == Rec::oGam + (size_t)DK * 4, "e^{G_C} and beta are one run in the record");
 
     __host__ __device__ static constexpr int shift_slot(int R, int I) { return (R - 2) * (R - 1) / 2 + I; }
 };
@@ -185,6 +191,16 @@ __device__ __forceinline__ Frag<BF> bwd_x_frag(const float *sX, int I, int R, in
     return make_frag<BF>(x.x, x.y, x.z, x.w);
 }
 
+// A 16x16 tile given as an A operand (row l16, columns 4*q4 + j) turned into the accumulator
+// layout (rows 4*q4 + j, column l16), i.e. each lane then holds 4 consecutive rows of one column:
+// an exact product with the identity.
+template <bool BF>
+__device__ __forceinline__ Frag<BF> bwd_turn(const Frag<BF> &a, const Frag<BF> &eye) {
+    f32x4 t = zero4();
+    mma16(t, a, eye);
+    return frag_from_acc<BF>(t);
+}
+
 template <typename IO, int DK, int C>
 __global__ void __launch_bounds__(kChunkThreads) kda_bwd_prep_kernel(BwdParams bp, char *__restrict__ records) {
     using L = BwdPrepLayout<IO, DK, C>;
@@ -198,7 +214,6 @@ __global__ void __launch_bounds__(kChunkThreads) kda_bwd_prep_kernel(BwdParams b
 
     __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
     OT *sKb = reinterpret_cast<OT *>(smem + L::oKb);
-    OT *sKs = reinterpret_cast<OT *>(smem + L::oKs);
     OT *sKbarT = reinterpret_cast<OT *>(smem + L::oKbarT);
     float *sX = reinterpret_cast<float *>(smem + L::oX);
     OT *sP = reinterpret_cast<OT *>(smem + L::oP);
@@ -209,10 +224,8 @@ __global__ void __launch_bounds__(kChunkThreads) kda_bwd_prep_kernel(BwdParams b
     float *sSH = reinterpret_cast<float *>(smem + L::oSH);
     OT *sM = reinterpret_cast<OT *>(smem + Rec::oM);
     OT *sN = reinterpret_cast<OT *>(smem + Rec::oN);
-    OT *sQtT = reinterpret_cast<OT *>(smem + Rec::oQtT);
-    OT *sBKtT = reinterpret_cast<OT *>(smem + Rec::oBKtT);
-    float *sGam = reinterpret_cast<float *>(smem + Rec::oGam);
-    float *sBeta = reinterpret_cast<float *>(smem + Rec::oBeta);
+    float *sGam = reinterpret_cast<float *>(smem + L::oGam);
+    float *sBeta = reinterpret_cast<float *>(smem + L::oBeta);
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -226,9 +239,12 @@ __global__ void __launch_bounds__(kChunkThreads) kda_bwd_prep_kernel(BwdParams b
     const int64_t start = p.cu ? (int64_t)p.cu[n] : (int64_t)n * p.T;
     const int len = p.cu ? p.cu[n + 1] - p.cu[n] : p.T;
     const int clen = min(C, len - ci * C);
+    char *rec = records + (size_t)(slot * H + h) * Rec::kBytes;
 
     BwdRaw<IO, DK> raw;
     bwd_load_keys<IO, DK, C>(raw, p, start + (int64_t)ci * C, clen, h, tid);
+    const Frag<BF> eye = make_frag<BF>(4 * q4 == l16 ? 1.f : 0.f, 4 * q4 + 1 == l16 ? 1.f : 0.f,
+                                       4 * q4 + 2 == l16 ? 1.f : 0.f, 4 * q4 + 3 == l16 ? 1.f : 0.f);
 
     // ================= 1: gate scan (log2 domain), stage beta
     // (k and q stay packed in the raw registers; phases 3 and 4 unpack them where used)
@@ -275,13 +291,15 @@ __global__ void __launch_bounds__(kChunkThreads) kda_bwd_prep_kernel(BwdParams b
     }
     __syncthreads();
 
-    // ================= 3: gated operands of sub-chunk R: K_b rows (and their shifted copies),
-    // K-^T, and the record's Q~^T and (Diag(beta) K~)^T
+    // ================= 3: gated operands of sub-chunk R: K_b rows, and K-^T, Q~^T,
+    // (Diag(beta) K~)^T turned through the identity so that a lane holds 4 consecutive tokens of
+    // one channel (8-byte pieces of their [DK][C] rows: K-^T to LDS, the other two to the record)
     Frag<BF> kdiag[KT];
     if (wave < NSUB) {
         const int R = wave;
-        const int r = 16 * R + l16;
-        const float br = sBeta[r];
+        const float br = sBeta[16 * R + l16];
+        OT *rq = reinterpret_cast<OT *>(rec + Rec::oQtT);
+        OT *rk = reinterpret_cast<OT *>(rec + Rec::oBKtT);
 #pragma unroll
         for (int ct = 0; ct < KT; ++ct) {
             const int c = 16 * ct + 4 * q4;
@@ -302,49 +320,43 @@ __global__ void __launch_bounds__(kChunkThreads) kda_bwd_prep_kernel(BwdParams b
                 const float fb = valid ? fast_exp2(tv[j] - G[ct][j]) : 0.f;
                 kb[j] = kx[j] * fb;
                 kd[j] = kb[j] * edv[j];
-                kt[j] = kx[j] * fr * ebv[j];
+                kt[j] = kx[j] * fr * ebv[j] * br;
                 qt[j] = qx[j] * fr * ebv[j];
                 kbar[j] = kb[j] * ecv[j];
             }
             kdiag[ct] = make_frag<BF>(kd[0], kd[1], kd[2], kd[3]);
             const Frag<BF> fkb = make_frag<BF>(kb[0], kb[1], kb[2], kb[3]);
-            *reinterpret_cast<decltype(fkb.v) *>(sKb + r * LDO + c) = fkb.v;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if constexpr (BF) {
-                    sKbarT[(c + j) * LDT + r] = f32_to_bf16(kbar[j]);
-                    sQtT[(c + j) * LDT + r] = f32_to_bf16(qt[j]);
-                    sBKtT[(c + j) * LDT + r] = f32_to_bf16(kt[j] * br);
-                } else {
-                    sKbarT[(c + j) * LDT + r] = kbar[j];
-                    sQtT[(c + j) * LDT + r] = qt[j];
-                    sBKtT[(c + j) * LDT + r] = kt[j] * br;
-                }
-            }
-#pragma unroll
-            for (int R2 = 2; R2 < NSUB; ++R2) {
-                if (R2 < R + 2) continue;
-                const float4 sh = *reinterpret_cast<const float4 *>(sSH + L::shift_slot(R2, R) * DK + c);
-                const Frag<BF> f = make_frag<BF>(kb[0] * sh.x, kb[1] * sh.y, kb[2] * sh.z, kb[3] * sh.w);
-                *reinterpret_cast<decltype(f.v) *>(sKs + (L::shift_slot(R2, R) * 16 + l16) * LDO + c) = f.v;
-            }
+            *reinterpret_cast<decltype(fkb.v) *>(sKb + (16 * R + l16) * LDO + c) = fkb.v;
+            // turned: lane holds tokens 16R + 4q4 .. +3 of channel 16ct + l16
+            const int64_t toff = (int64_t)(16 * ct + l16) * LDT + 16 * R + 4 * q4;
+            const Frag<BF> tb = bwd_turn<BF>(make_frag<BF>(kbar[0], kbar[1], kbar[2], kbar[3]), eye);
+            *reinterpret_cast<decltype(tb.v) *>(sKbarT + toff) = tb.v;
+            const Frag<BF> tq = bwd_turn<BF>(make_frag<BF>(qt[0], qt[1], qt[2], qt[3]), eye);
+            *reinterpret_cast<decltype(tq.v) *>(rq + toff) = tq.v;
+            const Frag<BF> tk = bwd_turn<BF>(make_frag<BF>(kt[0], kt[1], kt[2], kt[3]), eye);
+            *reinterpret_cast<decltype(tk.v) *>(rk + toff) = tk.v;
         }
     }
     __syncthreads();
 
     // ================= 4: row-R blocks of A (fp32, to sX) and P (to sP, zero above the block
-    // diagonal), then X_RR = (I + A_RR)^{-1} in place
+    // diagonal), then X_RR = (I + A_RR)^{-1} in place.  Block (R, I) pairs the row operands
+    // k_r e^{G_r - b_R} (and the same for q) with the column operand K_b of sub-chunk I; for
+    // I <= R - 2 the row operands take the extra factor e^{b_R - b_{I+1}} (all factors <= 1), and
+    // for I = R the column operand is k_i e^{b_R - G_i}.
     if (wave < NSUB) {
         const int R = wave;
-        Frag<BF> ka[KT], qa[KT];
+        float kr[KT][4], qr[KT][4];
 #pragma unroll
         for (int ct = 0; ct < KT; ++ct) {
             const float4 kv = unpack4<BF>(raw.k[ct]), qv = unpack4<BF>(raw.q[ct]);
-            float fr[4];
+            const float kx[4] = {kv.x, kv.y, kv.z, kv.w}, qx[4] = {qv.x, qv.y, qv.z, qv.w};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) fr[j] = valid ? fast_exp2(G[ct][j]) : 0.f;
-            ka[ct] = make_frag<BF>(kv.x * fr[0], kv.y * fr[1], kv.z * fr[2], kv.w * fr[3]);
-            qa[ct] = make_frag<BF>(qv.x * fr[0], qv.y * fr[1], qv.z * fr[2], qv.w * fr[3]);
+            for (int j = 0; j < 4; ++j) {
+                const float fr = valid ? fast_exp2(G[ct][j]) : 0.f;
+                kr[ct][j] = kx[j] * fr;
+                qr[ct][j] = qx[j] * fr;
+            }
         }
 #pragma unroll
         for (int I = 0; I < NSUB; ++I) {
@@ -353,21 +365,36 @@ __global__ void __launch_bounds__(kChunkThreads) kda_bwd_prep_kernel(BwdParams b
                 for (int j = 0; j < 4; ++j) sP[(16 * R + 4 * q4 + j) * LDM + 16 * I + l16] = OT(0);
                 continue;
             }
+            const OT *colp = sKb + (16 * I + l16) * LDO + 4 * q4;
+            const float *shp = sSH + (I + 2 <= R ? L::shift_slot(R, I) : 0) * DK + 4 * q4;
             f32x4 accA = zero4(), accP = zero4();
-            const OT *colp = (I == R - 1) ? sKb + (16 * I + l16) * LDO
-                                          : sKs + (L::shift_slot(R < 2 ? 2 : R, I) * 16 + l16) * LDO;
 #pragma unroll
             for (int ct = 0; ct < KT; ct += 2) {
-                Frag<BF> b0, b1;
+                Frag<BF> b0, b1, ka0, ka1, qa0, qa1;
                 if (I == R) {
                     b0 = kdiag[ct];
                     b1 = kdiag[ct + 1];
                 } else {
-                    b0 = lds_frag(colp + 16 * ct + 4 * q4);
-                    b1 = lds_frag(colp + 16 * (ct + 1) + 4 * q4);
+                    b0 = lds_frag(colp + 16 * ct);
+                    b1 = lds_frag(colp + 16 * (ct + 1));
                 }
-                mma32(accA, ka[ct], ka[ct + 1], b0, b1);
-                mma32(accP, qa[ct], qa[ct + 1], b0, b1);
+                if (I + 2 <= R) {
+                    const float4 s0 = *reinterpret_cast<const float4 *>(shp + 16 * ct);
+                    const float4 s1 = *reinterpret_cast<const float4 *>(shp + 16 * (ct + 1));
+                    ka0 = make_frag<BF>(kr[ct][0] * s0.x, kr[ct][1] * s0.y, kr[ct][2] * s0.z, kr[ct][3] * s0.w);
+                    ka1 = make_frag<BF>(kr[ct + 1][0] * s1.x, kr[ct + 1][1] * s1.y, kr[ct + 1][2] * s1.z,
+                                        kr[ct + 1][3] * s1.w);
+                    qa0 = make_frag<BF>(qr[ct][0] * s0.x, qr[ct][1] * s0.y, qr[ct][2] * s0.z, qr[ct][3] * s0.w);
+                    qa1 = make_frag<BF>(qr[ct + 1][0] * s1.x, qr[ct + 1][1] * s1.y, qr[ct + 1][2] * s1.z,
+                                        qr[ct + 1][3] * s1.w);
+                } else {
+                    ka0 = make_frag<BF>(kr[ct][0], kr[ct][1], kr[ct][2], kr[ct][3]);
+                    ka1 = make_frag<BF>(kr[ct + 1][0], kr[ct + 1][1], kr[ct + 1][2], kr[ct + 1][3]);
+                    qa0 = make_frag<BF>(qr[ct][0], qr[ct][1], qr[ct][2], qr[ct][3]);
+                    qa1 = make_frag<BF>(qr[ct + 1][0], qr[ct + 1][1], qr[ct + 1][2], qr[ct + 1][3]);
+                }
+                mma32(accA, ka0, ka1, b0, b1);
+                mma32(accP, qa0, qa1, b0, b1);
             }
             // accumulator: rows rr = 4*q4 + j of block R, column ii = l16 of block I
 #pragma unroll
@@ -383,7 +410,11 @@ __global__ void __launch_bounds__(kChunkThreads) kda_bwd_prep_kernel(BwdParams b
                 else sP[(16 * R + rr) * LDM + 16 * I + ii] = pv;
             }
         }
-        // lane l16 computes column l16 of X_RR by forward substitution (this wave wrote A_RR)
+    }
+    __syncthreads();  // A is complete in sX (the gate tables that shared its place are dead)
+    if (wave < NSUB) {
+        // X_RR = (I + A_RR)^{-1}: lane l16 computes column l16 by forward substitution
+        const int R = wave;
         float *Ab = sX + (16 * R) * LDX + 16 * R;
         float x[16];
 #pragma unroll
@@ -464,10 +495,11 @@ __global__ void __launch_bounds__(kChunkThreads) kda_bwd_prep_kernel(BwdParams b
     }
     __syncthreads();
 
-    // ================= 7: the record out, verbatim
-    char *rec = records + (size_t)(slot * H + h) * Rec::kBytes;
-    for (int pc = tid; pc < (int)(Rec::kBytes / 16); pc += kChunkThreads)
+    // ================= 7: M and N (the record's first bytes, formed in place), then e^{G_C} and beta
+    for (int pc = tid; pc < (int)(Rec::oQtT / 16); pc += kChunkThreads)
         reinterpret_cast<u32x4 *>(rec)[pc] = reinterpret_cast<const u32x4 *>(smem)[pc];
+    for (int pc = tid; pc < (int)((DK + C) * 4 / 16); pc += kChunkThreads)
+        reinterpret_cast<u32x4 *>(rec + Rec::oGam)[pc] = reinterpret_cast<const u32x4 *>(smem + L::oGam)[pc];
 }
 
 // ====================================================================== scan ====
