@@ -264,7 +264,8 @@ kda_status_t resolve_bwd(const kda_problem_t *p, bool varlen, BwdResolved &b) {
     if (!bwd_variant_supported(p->io_dtype, dk, dv, b.chunk))
         return fail(KDA_ERR_UNSUPPORTED, "backward: no compiled variant for io=%s d_k=%d d_v=%d chunk=%d (LDS)",
                     p->io_dtype == KDA_BF16 ? "bf16" : "fp32", dk, dv, b.chunk);
-    b.two_pass = dv % 64 == 0 && kda::split_variant_supported(p->io_dtype, dk, b.chunk, 2, 2, true);
+    // the forward again with the 32-column scan (twice the workgroups of the 64-column one)
+    b.two_pass = dv % 32 == 0 && kda::split_variant_supported(p->io_dtype, dk, b.chunk, 1, 2, true);
     b.fwd_dv_tile = 0;
     if (!b.two_pass) {
         for (int t : {default_dv_tile((int64_t)b.r.num_seqs * p->num_heads, dv), 32})
@@ -433,7 +434,7 @@ kda_status_t kda_chunk_bwd(const kda_problem_t *problem, const void *q, const vo
         fp.dch = ws + b.off_dch;
         fp.chunk_off = varlen ? chunk_off : nullptr;
         if (b.two_pass) {  // the two-pass forward builds the chunk-offset table itself
-            st = hip_status(kda::launch_split_fwd(problem->io_dtype, fp, b.chunk, 2, 2, ws, b.slots, s),
+            st = hip_status(kda::launch_split_fwd(problem->io_dtype, fp, b.chunk, 1, 2, ws, b.slots, s),
                             "kda_chunk_bwd forward launch");
         } else {
             if (varlen) {
