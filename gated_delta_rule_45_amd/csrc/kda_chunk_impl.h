@@ -404,6 +404,7 @@ __global__ void __launch_bounds__(kChunkThreads) kda_chunk_fwd_kernel(FwdParams 
                 }
             }
             // X_RR = (I + A_RR)^{-1}, row by row: lane l16 owns column l16 (same wave wrote A_RR)
+            wave_lds_sync();
             float *Ab = sAd + R * 16 * LDD;
             const int jc = l16;
             float x[16];

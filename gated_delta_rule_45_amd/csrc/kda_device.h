@@ -146,21 +146,29 @@ __device__ __forceinline__ f32x4 zero4() {
     return z;
 }
 
+// Orders LDS accesses between the lanes of one wave: a wave barrier (convergent, so code around
+// it cannot be duplicated into divergent branches) and a wavefront-scope fence (no LDS access is
+// moved across it).  A wave's LDS operations execute in order, so no instruction is emitted; it
+// is needed wherever lanes read what other lanes of the same wave wrote without a workgroup
+// barrier in between.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
 // Writes a 16 x WC fp32 tile held in LDS (row stride LDK floats) to dst (row stride ld elements,
 // element type OT: bf16 bits or fp32) as 16-byte row segments spread over the lanes of one wave.
 // Used to turn accumulator fragments (4 rows of one column per lane) into few wide stores.  The
 // tile is written by other lanes of the same wave just before and rewritten just after, so the
-// read-back is fenced on both sides by a wave barrier (convergent: the code after the partial-wave
-// read-back cannot be duplicated into its divergent branches, which had let the lanes with no
-// segment write the next tile before the other lanes read this one) and a wavefront-scope fence
-// (no LDS access moves across).  A wave's LDS operations execute in order, so neither emits an
-// instruction.
+// read-back is bracketed by wave_lds_sync (without it the compiler duplicated the code after the
+// partial-wave read-back into its divergent branches, and the lanes with no segment wrote the
+// next tile before the other lanes had read this one).
 template <typename OT, int WC, int LDK>
 __device__ __forceinline__ void keep_rows(OT *dst, int64_t ld, const float *tile, int lane) {
     constexpr int EPS = 16 / (int)sizeof(OT), SPR = WC / EPS, NSEG = 16 * SPR;
     static_assert(WC % EPS == 0 && LDK % 4 == 0, "whole 16-byte segments");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    wave_lds_sync();
 #pragma unroll
     for (int i = 0; i < (NSEG + 63) / 64; ++i) {
         const int sg = lane + 64 * i;
@@ -177,8 +185,7 @@ __device__ __forceinline__ void keep_rows(OT *dst, int64_t ld, const float *tile
             }
         }
     }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
+    wave_lds_sync();
 }
 
 // ------------------------------------------------------------ io element types --

@@ -369,6 +369,7 @@ __global__ void __launch_bounds__(kChunkThreads) kda_dplr_fwd_kernel(DplrParams 
                 }
             }
             // X_RR = (I - M_ba,RR)^{-1}: lane l16 computes column l16 by forward substitution
+            wave_lds_sync();  // this wave's lanes wrote the block
             float *Ab = sAd + R * 16 * LDD;
             const int jc = l16;
             float x[16];

@@ -368,6 +368,7 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
                 store_pair<BF>(rec + Rec::oP + (size_t)Rec::tp_tile(R, pp) * Rec::TILE_BYTES, lane, pf[2 * pp], pf[2 * pp + 1]);
 
         // X_RR = (I + A_RR)^{-1}, row by row; lane l16 owns column l16 (this wave wrote A_RR)
+        wave_lds_sync();
         float *Ab = sX + (16 * R) * LDX + 16 * R;
         float x[16];
 #pragma unroll
