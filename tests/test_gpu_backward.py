@@ -127,14 +127,23 @@ def test_bwd_prefill_full_size_sampled_heads():
     check_bwd(inp, chunk=64, heads=[0, 9], label="prefill")
 
 
-def test_bwd_repeatable():
-    """Two calls on the same inputs give bit-identical gradients (no races, no atomics)."""
-    inp = ki.make_inputs(2, 300, 4, 128, 128, "bf16", seed=34, s0_std=0.1)
+@pytest.mark.parametrize("dk,chunk", [(128, 64), (64, 64), (64, 32), (128, 16)])
+def test_bwd_repeatable(dk, chunk):
+    """Two calls on the same inputs give bit-identical gradients (no races, no atomics; a matrix-core
+    result read back too early would show as run-to-run differences)."""
+    inp = ki.make_inputs(2, 300, 4, dk, 128, "bf16", seed=34, s0_std=0.1)
     d_out, dsf = ki.grad_inputs(inp, 7)
     dev = lambda x: None if x is None else x.to(DEV)
     args = (dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.g), dev(inp.beta), dev(d_out))
-    a = kda.chunk_bwd(*args, initial_state=dev(inp.s0), d_final_state=dev(dsf))
-    b = kda.chunk_bwd(*args, initial_state=dev(inp.s0), d_final_state=dev(dsf))
+    a = kda.chunk_bwd(*args, initial_state=dev(inp.s0), d_final_state=dev(dsf), chunk_size=chunk)
+    b = kda.chunk_bwd(*args, initial_state=dev(inp.s0), d_final_state=dev(dsf), chunk_size=chunk)
     torch.cuda.synchronize()
     for key in KEYS:
         assert torch.equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_bwd_fp32_packed_sequences(chunk):
+    """fp32 packed batch with an empty, a single-token and a ragged sequence."""
+    inp = ki.make_inputs(1, 0, 2, 64, 64, "f32", seed=35, s0_std=0.1, lengths=[33, 1, 0, 47])
+    check_bwd(inp, chunk=chunk, label=f"fp32 packed c{chunk}")
