@@ -81,3 +81,16 @@ def test_dplr_key_tied_case_equals_kda():
 
 def test_dplr_prefill_full_size():
     check(ki.workload_inputs("prefill"), label="prefill")
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_dplr_repeatable(chunk):
+    """Two calls on the same inputs give bit-identical outputs and final states."""
+    inp = ki.make_inputs(2, 150, 2, 128, 128, "bf16", seed=37, s0_std=0.1)
+    a, b, kw = ki.dplr_inputs(inp, 9)
+    dev = lambda x: None if x is None else x.to(DEV)
+    args = (dev(inp.q), dev(kw), dev(inp.v), dev(a), dev(b), dev(inp.g), dev(inp.s0), None)
+    o1, f1 = kda.dplr_chunk_fwd(*args, chunk_size=chunk, dv_tile=32)
+    o2, f2 = kda.dplr_chunk_fwd(*args, chunk_size=chunk, dv_tile=32)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)

@@ -288,3 +288,17 @@ def test_tune_picks_a_configuration_that_matches_the_oracle():
     o_ref, s_ref = run_oracle(inp)
     compare("o", out, o_ref, "bf16")
     compare("final_state", fin, s_ref, "bf16")
+
+
+@pytest.mark.parametrize("dk,chunk", [(128, 64), (64, 64), (128, 32), (64, 16)])
+@pytest.mark.parametrize("algo", ALGOS)
+def test_forward_repeatable(dk, chunk, algo):
+    """Two calls on the same inputs give bit-identical outputs and final states (a race or a
+    matrix-core result read back too early would show as run-to-run differences)."""
+    inp = ki.make_inputs(2, 300, 4, dk, 128, "bf16", seed=36, s0_std=0.1)
+    t = lambda x: None if x is None else x.to(DEV)
+    args = (t(inp.q), t(inp.k), t(inp.v), t(inp.g), t(inp.beta), t(inp.s0))
+    o1, f1 = kda.chunk_fwd(*args, chunk_size=chunk, algo=algo)
+    o2, f2 = kda.chunk_fwd(*args, chunk_size=chunk, algo=algo)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
