@@ -173,7 +173,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--dv-tile", type=int, default=0)
     ap.add_argument("--chunk", type=int, default=64)
     ap.add_argument("--algo", default="auto", choices=["auto", "fused", "two_pass"])

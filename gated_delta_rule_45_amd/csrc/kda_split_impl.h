@@ -22,7 +22,10 @@
 //
 //   Y = V - K~ S        D = T Y         O = scale (Q~ S + P D)        S <- Gamma S + K-^T D
 //
-// (D = T (V - K~ S) equals the WY form U - W S with W = T K~ and U = T V.)
+// (D = T (V - K~ S) equals the WY form U - W S with W = T K~ and U = T V.)  Where LDS allows,
+// kda_scan_ow_kernel runs the same algebra with the state chain and the output on separate
+// waves; the KEEP instantiation (chunk states for the backward pass) and shapes whose extra
+// LDS slots do not fit use kda_scan_kernel.
 #pragma once
 
 #include <type_traits>
@@ -860,6 +863,341 @@ __global__ void __launch_bounds__(64 * (NW + scan_copy_waves(SPW))) kda_scan_ker
     }
 }
 
+// ------------------------------------------------ scan with output waves ----
+// The same per-chunk algebra as kda_scan_kernel with the work split by what the recurrence
+// needs: NW chain waves carry the state (Y = V - K~ S, D = T Y, S <- Gamma S + K-^T D), and NW
+// output waves, one chunk behind, form O = scale (Q~ S + P D) for the same columns.  The chain
+// waves hand S (at the start of each chunk) and D over through LDS slots that alternate with
+// the chunk parity; an output wave reads Q~ and P of chunk c while chunk c is staged, keeps P in
+// registers, and finishes O of chunk c after the next barrier, once D of chunk c is in its slot.
+// The chain's share of each chunk drops from 5 to 3 products per 16-column slice and it issues
+// no output stores.
+template <typename IO, int DK, int C, int SPW, int NW>
+struct ScanOwLayout {
+    using S = ScanLayout<IO, DK, C, SPW, NW>;
+    using Rec = typename S::Rec;
+    static constexpr int FB = Rec::FRAG_BYTES;
+    static constexpr int SB_UNITS = SPW * Rec::KT * FB / 16;           // 16-byte units per lane: S operand
+    static constexpr int DB_UNITS = SPW * 2 * Rec::NPAIR * FB / 16;    // 16-byte units per lane: D operand
+    static constexpr int NT = 64 * (2 * NW + S::NCW);
+    static constexpr size_t oSb = S::kBytes;                                     // [parity][wave][unit][lane]
+    static constexpr size_t oDb = oSb + (size_t)2 * NW * SB_UNITS * 64 * 16;
+    static constexpr size_t kBytes = oDb + (size_t)2 * NW * DB_UNITS * 64 * 16;
+    static constexpr bool kFits = S::kFits && kBytes <= 160 * 1024;
+    static_assert((Rec::KT * FB) % 16 == 0 && (2 * Rec::NPAIR * FB) % 16 == 0, "slot units");
+};
+
+// N operand fragments of one lane to / from an LDS slot laid out as [unit][lane] 16-byte units
+template <bool BF, int N>
+__device__ __forceinline__ void slot_put(char *slot, int lane, const Frag<BF> *f) {
+    if constexpr (BF) {
+#pragma unroll
+        for (int u = 0; u < N / 2; ++u)
+            *reinterpret_cast<uint4 *>(slot + (u * 64 + lane) * 16) =
+                make_uint4(f[2 * u].v.x, f[2 * u].v.y, f[2 * u + 1].v.x, f[2 * u + 1].v.y);
+    } else {
+#pragma unroll
+        for (int u = 0; u < N; ++u) *reinterpret_cast<float4 *>(slot + (u * 64 + lane) * 16) = f[u].v;
+    }
+}
+template <bool BF, int N>
+__device__ __forceinline__ void slot_get(const char *slot, int lane, Frag<BF> *f) {
+    if constexpr (BF) {
+#pragma unroll
+        for (int u = 0; u < N / 2; ++u) {
+            const uint4 x = *reinterpret_cast<const uint4 *>(slot + (u * 64 + lane) * 16);
+            f[2 * u].v = make_uint2(x.x, x.y);
+            f[2 * u + 1].v = make_uint2(x.z, x.w);
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < N; ++u) f[u].v = *reinterpret_cast<const float4 *>(slot + (u * 64 + lane) * 16);
+    }
+}
+
+template <typename IO, int DK, int C, int SPW, int NW>
+__global__ void __launch_bounds__(64 * (2 * NW + scan_copy_waves(SPW))) kda_scan_ow_kernel(FwdParams p, const int32_t *__restrict__ chunk_off,
+                                                                     const char *__restrict__ records) {
+    using S = ScanLayout<IO, DK, C, SPW, NW>;
+    using SO = ScanOwLayout<IO, DK, C, SPW, NW>;
+    using Rec = typename S::Rec;
+    constexpr bool BF = Rec::BF;
+    constexpr int NSUB = Rec::NSUB, KT = Rec::KT, NPAIR = Rec::NPAIR, DVT = S::DVT, WC = S::WCOLS;
+    using Tr = IoTraits<IO>;
+
+    __shared__ __attribute__((aligned(16))) char smem[SO::kBytes];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l16 = lane & 15, q4 = lane >> 4;
+    const int H = p.H, DV = p.dv;
+    const int ntile = DV / DVT;
+    const int64_t nblocks = (int64_t)p.num_seqs * H * ntile;
+    const int64_t item = xcd_grouped_block(blockIdx.x, nblocks);
+    const int tile = (int)(item % ntile);
+    const int64_t nh = item / ntile;
+    const int h = (int)(nh % H);
+    const int n = (int)(nh / H);
+    int64_t start;
+    int len;
+    if (p.cu) {
+        start = p.cu[n];
+        len = p.cu[n + 1] - p.cu[n];
+    } else {
+        start = (int64_t)n * p.T;
+        len = p.T;
+    }
+    const int nchunks = (len + C - 1) / C;
+    const int64_t g0 = first_chunk(p, chunk_off, C, n);
+    const int col0 = tile * DVT;
+    const int64_t vstride = (int64_t)H * DV;
+    const IO *vbase = static_cast<const IO *>(p.v) + (start * H + h) * (int64_t)DV + col0;
+    const char *rec0 = records + (size_t)(g0 * H + h) * Rec::kBytes;
+    const size_t rec_stride = (size_t)H * Rec::kBytes;
+    constexpr int KP = KT / 2;
+    constexpr int SBN = SPW * KT, DBN = SPW * 2 * NPAIR;  // fragments per lane in the S / D slots
+    // Every wave passes nchunks + 1 barriers: one per chunk and a last one after which the
+    // output waves finish the final chunk.
+    if (wave >= 2 * NW) {
+        switch (wave - 2 * NW) {
+            case 0: copy_wave<IO, DK, C, SPW, NW, 0>(smem, rec0, rec_stride, vbase, vstride, len, nchunks, lane); break;
+            case 1: copy_wave<IO, DK, C, SPW, NW, 1>(smem, rec0, rec_stride, vbase, vstride, len, nchunks, lane); break;
+            case 2:
+                if constexpr (S::NCW > 2)
+                    copy_wave<IO, DK, C, SPW, NW, 2>(smem, rec0, rec_stride, vbase, vstride, len, nchunks, lane);
+                break;
+            default:
+                if constexpr (S::NCW > 3)
+                    copy_wave<IO, DK, C, SPW, NW, 3>(smem, rec0, rec_stride, vbase, vstride, len, nchunks, lane);
+                break;
+        }
+        __syncthreads();
+        return;
+    }
+    static_assert(S::NCW <= 4, "copy wave count");
+
+    if (wave >= NW) {
+        // ---------------- output waves: slice s holds columns col0 + WC*ow + 16*s + l16
+        const int ow = wave - NW;
+        IO *obase = static_cast<IO *>(p.out) + (start * H + h) * (int64_t)DV + col0 + WC * ow + 4 * q4;
+        f32x4 Ot[SPW][NSUB];
+        FragPair<BF> Pf[NSUB][NPAIR];
+        // O of chunk cp: add P D (D from its slot), scale, store; lane holds 4 columns of a token
+        auto finish = [&](int cp) {
+            Frag<BF> Db[SPW * 2 * NPAIR];
+            slot_get<BF, DBN>(smem + SO::oDb + (size_t)(((cp & 1) * NW + ow) * SO::DB_UNITS) * 64 * 16, lane, Db);
+#pragma unroll
+            for (int R = 0; R < NSUB; ++R)
+#pragma unroll
+                for (int pp = 0; pp < NPAIR; ++pp)
+                    if (2 * pp <= R)
+#pragma unroll
+                        for (int s = 0; s < SPW; ++s)
+                            mma32(Ot[s][R], Db[s * 2 * NPAIR + 2 * pp], Db[s * 2 * NPAIR + 2 * pp + 1], Pf[R][pp].a,
+                                  Pf[R][pp].b);
+            const int clen = min(C, len - cp * C);
+            IO *oc = obase + (int64_t)cp * C * vstride;
+#pragma unroll
+            for (int R = 0; R < NSUB; ++R) {
+                const int r = 16 * R + l16;
+                if (r < clen) {
+#pragma unroll
+                    for (int s = 0; s < SPW; ++s)
+                        Tr::store4(oc + r * vstride + 16 * s, make_float4(Ot[s][R][0] * p.scale, Ot[s][R][1] * p.scale,
+                                                                        Ot[s][R][2] * p.scale, Ot[s][R][3] * p.scale));
+                }
+            }
+        };
+        for (int c = 0; c < nchunks; ++c) {
+            __syncthreads();  // chunk c is in LDS; S of chunk c and D of chunk c - 1 are in their slots
+            if (c > 0) finish(c - 1);
+            const char *rb = smem + ((c & 1) ? S::oRec1 : S::oRec0);
+            Frag<BF> Sb[SPW * KT];
+            slot_get<BF, SBN>(smem + SO::oSb + (size_t)(((c & 1) * NW + ow) * SO::SB_UNITS) * 64 * 16, lane, Sb);
+            FragPair<BF> Qf[NSUB][KP];
+#pragma unroll
+            for (int rt = 0; rt < NSUB; ++rt)
+#pragma unroll
+                for (int kp = 0; kp < KP; ++kp)
+                    Qf[rt][kp] = ld_pair<BF>(rb + Rec::oQt + (size_t)(rt * KP + kp) * Rec::TILE_BYTES, lane);
+#pragma unroll
+            for (int R = 0; R < NSUB; ++R)
+#pragma unroll
+                for (int pp = 0; pp < NPAIR; ++pp)
+                    if (2 * pp <= R)
+                        Pf[R][pp] = ld_pair<BF>(rb + Rec::oP + (size_t)Rec::tp_tile(R, pp) * Rec::TILE_BYTES, lane);
+            // O^T = S^T Q~^T, one row tile at a time
+#pragma unroll
+            for (int rt = 0; rt < NSUB; ++rt) {
+#pragma unroll
+                for (int s = 0; s < SPW; ++s) Ot[s][rt] = zero4();
+#pragma unroll
+                for (int kp = 0; kp < KP; ++kp)
+#pragma unroll
+                    for (int s = 0; s < SPW; ++s)
+                        mma32(Ot[s][rt], Sb[s * KT + 2 * kp], Sb[s * KT + 2 * kp + 1], Qf[rt][kp].a, Qf[rt][kp].b);
+            }
+        }
+        __syncthreads();  // D of the last chunk is in its slot
+        if (nchunks > 0) finish(nchunks - 1);
+        return;
+    }
+
+    // ---------------- chain waves: slice s holds state columns col0 + WC*wave + 16*s + l16
+    f32x4 St[SPW][KT];
+    const int64_t sbase = ((int64_t)n * H + h) * DK * DV;
+#pragma unroll
+    for (int s = 0; s < SPW; ++s) {
+        const int col = col0 + WC * wave + 16 * s + l16;
+#pragma unroll
+        for (int ct = 0; ct < KT; ++ct)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                St[s][ct][j] = p.s0 ? p.s0[sbase + (int64_t)(16 * ct + 4 * q4 + j) * DV + col] : 0.f;
+    }
+    Frag<BF> Sb[SPW * KT];
+#pragma unroll
+    for (int s = 0; s < SPW; ++s)
+#pragma unroll
+        for (int ct = 0; ct < KT; ++ct) Sb[s * KT + ct] = frag_from_acc<BF>(St[s][ct]);
+    slot_put<BF, SBN>(smem + SO::oSb + (size_t)(wave * SO::SB_UNITS) * 64 * 16, lane, Sb);
+
+    constexpr int GP = NSUB >= 2 ? NSUB - 2 : 0;  // row tile after which the K-^T reads start
+    constexpr int KT_H = (KT + 1) / 2;
+    for (int c = 0; c < nchunks; ++c) {
+        __syncthreads();  // chunk c is in LDS
+        const char *rb = smem + ((c & 1) ? S::oRec1 : S::oRec0);
+        const IO *vb = reinterpret_cast<const IO *>(smem + ((c & 1) ? S::oV1 : S::oV0));
+
+        FragPair<BF> Kf[NSUB][KP], Tf[NSUB][NPAIR], Bf[KT][NPAIR];
+        IO vv[SPW][NSUB][4];
+        auto read_k = [&](int rt) {
+#pragma unroll
+            for (int kp = 0; kp < KP; ++kp)
+                Kf[rt][kp] = ld_pair<BF>(rb + Rec::oKt + (size_t)(rt * KP + kp) * Rec::TILE_BYTES, lane);
+        };
+        auto read_kbt = [&](int ct0, int ct1) {
+#pragma unroll
+            for (int ct = ct0; ct < ct1; ++ct)
+#pragma unroll
+                for (int pp = 0; pp < NPAIR; ++pp)
+                    Bf[ct][pp] = ld_pair<BF>(rb + Rec::oKbT + (size_t)(ct * NPAIR + pp) * Rec::TILE_BYTES, lane);
+        };
+        read_k(0);
+        if constexpr (NSUB > 1) read_k(1);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // K~ S for Y = V - K~ S, one row tile at a time
+        f32x4 AK[SPW][NSUB];
+#pragma unroll
+        for (int rt = 0; rt < NSUB; ++rt) {
+#pragma unroll
+            for (int s = 0; s < SPW; ++s) AK[s][rt] = zero4();
+#pragma unroll
+            for (int kp = 0; kp < KP; ++kp)
+#pragma unroll
+                for (int s = 0; s < SPW; ++s)
+                    mma32(AK[s][rt], Kf[rt][kp].a, Kf[rt][kp].b, Sb[s * KT + 2 * kp], Sb[s * KT + 2 * kp + 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (rt + 2 < NSUB) read_k(rt + 2);
+            if (rt == 0) {
+#pragma unroll
+                for (int s = 0; s < SPW; ++s)
+#pragma unroll
+                    for (int r2 = 0; r2 < NSUB; ++r2)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            vv[s][r2][j] = vb[(16 * r2 + 4 * q4 + j) * DVT + WC * wave + 16 * s + l16];
+#pragma unroll
+                for (int R = 0; R < NSUB; ++R)
+#pragma unroll
+                    for (int pp = 0; pp < NPAIR; ++pp)
+                        if (2 * pp <= R)
+                            Tf[R][pp] = ld_pair<BF>(rb + Rec::oT + (size_t)Rec::tp_tile(R, pp) * Rec::TILE_BYTES, lane);
+            }
+            if (rt == GP) read_kbt(0, KT_H);
+            if (rt == NSUB - 1) read_kbt(KT_H, KT);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // Y = V - K~ S as B fragments (rows past the chunk end hold finite filler; T zeroes them),
+        // then D = T Y, handed to the output waves
+        Frag<BF> Db[SPW * 2 * NPAIR];
+        {
+            Frag<BF> Yb[SPW][2 * NPAIR];
+#pragma unroll
+            for (int s = 0; s < SPW; ++s)
+#pragma unroll
+                for (int rt = 0; rt < 2 * NPAIR; ++rt)
+                    Yb[s][rt] = rt < NSUB ? make_frag<BF>(Tr::to_float(vv[s][rt][0]) - AK[s][rt][0],
+                                                          Tr::to_float(vv[s][rt][1]) - AK[s][rt][1],
+                                                          Tr::to_float(vv[s][rt][2]) - AK[s][rt][2],
+                                                          Tr::to_float(vv[s][rt][3]) - AK[s][rt][3])
+                                          : make_frag<BF>(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int R = 0; R < NSUB; ++R) {
+                f32x4 d[SPW];
+#pragma unroll
+                for (int s = 0; s < SPW; ++s) d[s] = zero4();
+#pragma unroll
+                for (int pp = 0; pp < NPAIR; ++pp)
+                    if (2 * pp <= R)
+#pragma unroll
+                        for (int s = 0; s < SPW; ++s) mma32(d[s], Tf[R][pp].a, Tf[R][pp].b, Yb[s][2 * pp], Yb[s][2 * pp + 1]);
+#pragma unroll
+                for (int s = 0; s < SPW; ++s) Db[s * 2 * NPAIR + R] = frag_from_acc<BF>(d[s]);
+            }
+            if constexpr (NSUB % 2 == 1)
+#pragma unroll
+                for (int s = 0; s < SPW; ++s) Db[s * 2 * NPAIR + NSUB] = make_frag<BF>(0.f, 0.f, 0.f, 0.f);
+        }
+        slot_put<BF, DBN>(smem + SO::oDb + (size_t)(((c & 1) * NW + wave) * SO::DB_UNITS) * 64 * 16, lane, Db);
+
+        // M = K-^T D, then S <- Gamma * S + M; the new S goes to the output waves' next slot
+        float4 gm[KT];
+        {
+            const float *gam = reinterpret_cast<const float *>(rb + Rec::oGam);
+#pragma unroll
+            for (int ct = 0; ct < KT; ++ct) gm[ct] = *reinterpret_cast<const float4 *>(gam + 16 * ct + 4 * q4);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 M[SPW][KT];
+#pragma unroll
+        for (int ct = 0; ct < KT; ++ct) {
+#pragma unroll
+            for (int s = 0; s < SPW; ++s) M[s][ct] = zero4();
+#pragma unroll
+            for (int pp = 0; pp < NPAIR; ++pp)
+#pragma unroll
+                for (int s = 0; s < SPW; ++s)
+                    mma32(M[s][ct], Bf[ct][pp].a, Bf[ct][pp].b, Db[s * 2 * NPAIR + 2 * pp], Db[s * 2 * NPAIR + 2 * pp + 1]);
+        }
+#pragma unroll
+        for (int ct = 0; ct < KT; ++ct)
+#pragma unroll
+            for (int s = 0; s < SPW; ++s) {
+                St[s][ct][0] = fmaf(gm[ct].x, St[s][ct][0], M[s][ct][0]);
+                St[s][ct][1] = fmaf(gm[ct].y, St[s][ct][1], M[s][ct][1]);
+                St[s][ct][2] = fmaf(gm[ct].z, St[s][ct][2], M[s][ct][2]);
+                St[s][ct][3] = fmaf(gm[ct].w, St[s][ct][3], M[s][ct][3]);
+                Sb[s * KT + ct] = frag_from_acc<BF>(St[s][ct]);
+            }
+        slot_put<BF, SBN>(smem + SO::oSb + (size_t)((((c + 1) & 1) * NW + wave) * SO::SB_UNITS) * 64 * 16, lane, Sb);
+    }
+    __syncthreads();  // matches the output waves' last barrier
+
+    if (p.sf) {
+#pragma unroll
+        for (int s = 0; s < SPW; ++s) {
+            const int col = col0 + WC * wave + 16 * s + l16;
+#pragma unroll
+            for (int ct = 0; ct < KT; ++ct)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) p.sf[sbase + (int64_t)(16 * ct + 4 * q4 + j) * DV + col] = St[s][ct][j];
+        }
+    }
+}
+
 // ----------------------------------------------------------------- launch ----
 template <typename IO, int DK, int C>
 constexpr size_t split_record_bytes() {
@@ -895,12 +1233,16 @@ hipError_t launch_split_variant(const FwdParams &p, char *workspace, int64_t chu
         }
         const int64_t scan_blocks = (int64_t)p.num_seqs * p.H * (p.dv / ScanLayout<IO, DK, C, SPW, NW>::DVT);
         if (scan_blocks > 0) {
-            if (keep)
+            if (keep) {
                 hipLaunchKernelGGL((kda_scan_kernel<IO, DK, C, SPW, NW, true>), dim3((unsigned)scan_blocks),
                                    dim3(ScanLayout<IO, DK, C, SPW, NW>::NT), 0, stream, p, chunk_off, records);
-            else
+            } else if constexpr (ScanOwLayout<IO, DK, C, SPW, NW>::kFits) {
+                hipLaunchKernelGGL((kda_scan_ow_kernel<IO, DK, C, SPW, NW>), dim3((unsigned)scan_blocks),
+                                   dim3(ScanOwLayout<IO, DK, C, SPW, NW>::NT), 0, stream, p, chunk_off, records);
+            } else {
                 hipLaunchKernelGGL((kda_scan_kernel<IO, DK, C, SPW, NW, false>), dim3((unsigned)scan_blocks),
                                    dim3(ScanLayout<IO, DK, C, SPW, NW>::NT), 0, stream, p, chunk_off, records);
+            }
             return hipGetLastError();
         }
         return hipSuccess;
