@@ -491,12 +491,27 @@ struct ScanLayout {
 // One copy wave's half of a chunk's record and V tile (1 KB units dealt alternately to the two
 // waves of a pair).  The units are loaded into registers (16 bytes per lane, all in flight at
 // once) and later written to LDS; on gfx950 this moves about twice the bytes per cycle of the
-// direct global->LDS copy.
-template <typename IO, int DK, int C, int SPW, int NW, int HALF>
+// direct global->LDS copy.  With SKIP_QP the Q~ and P sections, which only the output uses,
+// are not copied (their LDS stays stale and unread).
+template <typename IO, int DK, int C, int SPW, int NW, int HALF, bool SKIP_QP = false>
 struct ChunkStager {
     using S = ScanLayout<IO, DK, C, SPW, NW>;
-    static constexpr int REC_UNITS = (int)(S::Rec::kBytes / 1024);
-    static constexpr int UNITS = REC_UNITS + S::V_PIECES / 64;
+    using Rec = typename S::Rec;
+    static constexpr int REC_UNITS = (int)(Rec::kBytes / 1024);
+    static constexpr int Q0 = (int)(Rec::oQt / 1024), Q1 = (int)(Rec::oKbT / 1024);
+    static constexpr int P0 = (int)(Rec::oP / 1024), P1 = (int)(Rec::oGam / 1024);
+    static_assert(Rec::oQt % 1024 == 0 && Rec::oKbT % 1024 == 0 && Rec::oP % 1024 == 0 && Rec::oGam % 1024 == 0,
+                  "record sections start on copy units");
+    static constexpr int USED = REC_UNITS - (SKIP_QP ? (Q1 - Q0) + (P1 - P0) : 0);  // record units copied
+    static constexpr int UNITS = USED + S::V_PIECES / 64;
+    // record unit of the j-th copied unit: the sections in order, Q~ and P left out with SKIP_QP
+    __device__ static constexpr int rec_unit(int j) {
+        if (SKIP_QP) {
+            if (j >= Q0) j += Q1 - Q0;
+            if (j >= P0) j += P1 - P0;
+        }
+        return j;
+    }
     static constexpr int PER = (UNITS - HALF + 1) / 2;  // units of this wave
     static constexpr int EP = 16 / (int)sizeof(IO);
     static constexpr int PPR = S::DVT / EP;  // 16-byte pieces per V row
@@ -508,10 +523,10 @@ struct ChunkStager {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int u = HALF + 2 * i;
-            if (u < REC_UNITS) {
-                r[i] = *reinterpret_cast<const u32x4 *>(rec + (size_t)u * 1024 + lane * 16);
+            if (u < USED) {
+                r[i] = *reinterpret_cast<const u32x4 *>(rec + (size_t)rec_unit(u) * 1024 + lane * 16);
             } else {
-                const int piece = (u - REC_UNITS) * 64 + lane;
+                const int piece = (u - USED) * 64 + lane;
                 const int row = min(piece / PPR, clen - 1);  // rows past the end re-read the last row
                 r[i] = *reinterpret_cast<const u32x4 *>(vrow0 + row * vstride + (piece % PPR) * EP);
             }
@@ -521,7 +536,7 @@ struct ChunkStager {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int u = HALF + 2 * i;
-            char *dst = u < REC_UNITS ? lds_rec + u * 1024 : lds_v + (u - REC_UNITS) * 1024;
+            char *dst = u < USED ? lds_rec + rec_unit(u) * 1024 : lds_v + (u - USED) * 1024;
             *reinterpret_cast<u32x4 *>(dst + lane * 16) = r[i];
         }
     }
@@ -531,12 +546,12 @@ struct ChunkStager {
 // chunk c to the compute waves; passing it also means every compute wave has finished chunk
 // c - 1, so that buffer may take chunk c + 1 (written from the registers of its pair, which
 // then load their next chunk).
-template <typename IO, int DK, int C, int SPW, int NW, int CW>
+template <typename IO, int DK, int C, int SPW, int NW, int CW, bool SKIP_QP = false>
 __device__ __forceinline__ void copy_wave(char *smem, const char *rec0, size_t rec_stride, const IO *vbase,
                                           int64_t vstride, int len, int nchunks, int lane) {
     using S = ScanLayout<IO, DK, C, SPW, NW>;
     constexpr int NPAIR = S::NCW / 2, PAIR = CW / 2;
-    ChunkStager<IO, DK, C, SPW, NW, CW % 2> st;
+    ChunkStager<IO, DK, C, SPW, NW, CW % 2, SKIP_QP> st;
 #define KDA_STAGE_LOAD(j) \
     st.load(rec0 + (size_t)(j) * rec_stride, vbase + (int64_t)(j) * C * vstride, min(C, len - (j) * C), vstride, lane)
 #define KDA_STAGE_STORE(j) \
@@ -574,8 +589,9 @@ __device__ __forceinline__ void copy_wave(char *smem, const char *rec0, size_t r
 #undef KDA_STAGE_STORE
 }
 
-// KEEP: also write each chunk's initial state and D (FwdParams::hs / dch) for the backward
-// pass; a separate instantiation so the forward's register allocation is not affected.
+// KEEP: write each chunk's initial state and D (FwdParams::hs / dch) for the backward pass and
+// no output (Q~ and P are neither staged nor used); a separate instantiation so the forward's
+// register allocation is not affected.
 template <typename IO, int DK, int C, int SPW, int NW, bool KEEP>
 __global__ void __launch_bounds__(64 * (NW + scan_copy_waves(SPW))) kda_scan_kernel(FwdParams p, const int32_t *__restrict__ chunk_off,
                                                                   const char *__restrict__ records) {
@@ -618,23 +634,23 @@ __global__ void __launch_bounds__(64 * (NW + scan_copy_waves(SPW))) kda_scan_ker
 
     if (wave >= NW) {
         switch (wave - NW) {
-            case 0: copy_wave<IO, DK, C, SPW, NW, 0>(smem, rec0, rec_stride, vbase, vstride, len, nchunks, lane); break;
-            case 1: copy_wave<IO, DK, C, SPW, NW, 1>(smem, rec0, rec_stride, vbase, vstride, len, nchunks, lane); break;
+            case 0: copy_wave<IO, DK, C, SPW, NW, 0, KEEP>(smem, rec0, rec_stride, vbase, vstride, len, nchunks, lane); break;
+            case 1: copy_wave<IO, DK, C, SPW, NW, 1, KEEP>(smem, rec0, rec_stride, vbase, vstride, len, nchunks, lane); break;
             case 2:
                 if constexpr (S::NCW > 2)
-                    copy_wave<IO, DK, C, SPW, NW, 2>(smem, rec0, rec_stride, vbase, vstride, len, nchunks, lane);
+                    copy_wave<IO, DK, C, SPW, NW, 2, KEEP>(smem, rec0, rec_stride, vbase, vstride, len, nchunks, lane);
                 break;
             case 3:
                 if constexpr (S::NCW > 3)
-                    copy_wave<IO, DK, C, SPW, NW, 3>(smem, rec0, rec_stride, vbase, vstride, len, nchunks, lane);
+                    copy_wave<IO, DK, C, SPW, NW, 3, KEEP>(smem, rec0, rec_stride, vbase, vstride, len, nchunks, lane);
                 break;
             case 4:
                 if constexpr (S::NCW > 4)
-                    copy_wave<IO, DK, C, SPW, NW, 4>(smem, rec0, rec_stride, vbase, vstride, len, nchunks, lane);
+                    copy_wave<IO, DK, C, SPW, NW, 4, KEEP>(smem, rec0, rec_stride, vbase, vstride, len, nchunks, lane);
                 break;
             default:
                 if constexpr (S::NCW > 5)
-                    copy_wave<IO, DK, C, SPW, NW, 5>(smem, rec0, rec_stride, vbase, vstride, len, nchunks, lane);
+                    copy_wave<IO, DK, C, SPW, NW, 5, KEEP>(smem, rec0, rec_stride, vbase, vstride, len, nchunks, lane);
                 break;
         }
         return;
@@ -697,7 +713,8 @@ __global__ void __launch_bounds__(64 * (NW + scan_copy_waves(SPW))) kda_scan_ker
 #pragma unroll
             for (int kp = 0; kp < KP; ++kp) {
                 Kf[rt][kp] = ld_pair<BF>(rb + Rec::oKt + (size_t)(rt * KP + kp) * Rec::TILE_BYTES, lane);
-                Qf[rt][kp] = ld_pair<BF>(rb + Rec::oQt + (size_t)(rt * KP + kp) * Rec::TILE_BYTES, lane);
+                if constexpr (!KEEP)  // the kept forward computes no output: Q~ and P are not staged
+                    Qf[rt][kp] = ld_pair<BF>(rb + Rec::oQt + (size_t)(rt * KP + kp) * Rec::TILE_BYTES, lane);
             }
         };
         auto read_kbt = [&](int ct0, int ct1) {
@@ -725,7 +742,7 @@ __global__ void __launch_bounds__(64 * (NW + scan_copy_waves(SPW))) kda_scan_ker
 #pragma unroll
                 for (int s = 0; s < SPW; ++s) {
                     mma32(AK[s][rt], Kf[rt][kp].a, Kf[rt][kp].b, Sb[s][2 * kp], Sb[s][2 * kp + 1]);
-                    mma32(Ot[s][rt], Sb[s][2 * kp], Sb[s][2 * kp + 1], Qf[rt][kp].a, Qf[rt][kp].b);
+                    if constexpr (!KEEP) mma32(Ot[s][rt], Sb[s][2 * kp], Sb[s][2 * kp + 1], Qf[rt][kp].a, Qf[rt][kp].b);
                 }
             __builtin_amdgcn_sched_barrier(0);
             if (rt + 2 < NSUB) read_kq(rt + 2);
@@ -745,12 +762,13 @@ __global__ void __launch_bounds__(64 * (NW + scan_copy_waves(SPW))) kda_scan_ker
                             Tf[R][pp] = ld_pair<BF>(rb + Rec::oT + (size_t)Rec::tp_tile(R, pp) * Rec::TILE_BYTES, lane);
             }
             if (rt == GP) {
+                if constexpr (!KEEP)
 #pragma unroll
-                for (int R = 0; R < NSUB; ++R)
+                    for (int R = 0; R < NSUB; ++R)
 #pragma unroll
-                    for (int pp = 0; pp < NPAIR; ++pp)
-                        if (2 * pp <= R)
-                            Pf[R][pp] = ld_pair<BF>(rb + Rec::oP + (size_t)Rec::tp_tile(R, pp) * Rec::TILE_BYTES, lane);
+                        for (int pp = 0; pp < NPAIR; ++pp)
+                            if (2 * pp <= R)
+                                Pf[R][pp] = ld_pair<BF>(rb + Rec::oP + (size_t)Rec::tp_tile(R, pp) * Rec::TILE_BYTES, lane);
                 read_kbt(0, KT_H);
             }
             if (rt == NSUB - 1) read_kbt(KT_H, KT);
@@ -818,13 +836,14 @@ __global__ void __launch_bounds__(64 * (NW + scan_copy_waves(SPW))) kda_scan_ker
 #pragma unroll
                 for (int s = 0; s < SPW; ++s) mma32(M[s][ct], Bf[ct][pp].a, Bf[ct][pp].b, Db[s][2 * pp], Db[s][2 * pp + 1]);
         }
+        if constexpr (!KEEP)
 #pragma unroll
-        for (int R = 0; R < NSUB; ++R)
+            for (int R = 0; R < NSUB; ++R)
 #pragma unroll
-            for (int pp = 0; pp < NPAIR; ++pp)
-                if (2 * pp <= R)
+                for (int pp = 0; pp < NPAIR; ++pp)
+                    if (2 * pp <= R)
 #pragma unroll
-                    for (int s = 0; s < SPW; ++s) mma32(Ot[s][R], Db[s][2 * pp], Db[s][2 * pp + 1], Pf[R][pp].a, Pf[R][pp].b);
+                        for (int s = 0; s < SPW; ++s) mma32(Ot[s][R], Db[s][2 * pp], Db[s][2 * pp + 1], Pf[R][pp].a, Pf[R][pp].b);
 
 #pragma unroll
         for (int ct = 0; ct < KT; ++ct)
@@ -842,7 +861,7 @@ __global__ void __launch_bounds__(64 * (NW + scan_copy_waves(SPW))) kda_scan_ker
 #pragma unroll
         for (int R = 0; R < NSUB; ++R) {
             const int r = 16 * R + l16;
-            if ((!KEEP || p.out) && r < clen) {
+            if (!KEEP && r < clen) {
 #pragma unroll
                 for (int s = 0; s < SPW; ++s)
                     Tr::store4(oc + r * vstride + 16 * s, make_float4(Ot[s][R][0] * p.scale, Ot[s][R][1] * p.scale,
@@ -871,7 +890,9 @@ __global__ void __launch_bounds__(64 * (NW + scan_copy_waves(SPW))) kda_scan_ker
 // the chunk parity; an output wave reads Q~ and P of chunk c while chunk c is staged, keeps P in
 // registers, and finishes O of chunk c after the next barrier, once D of chunk c is in its slot.
 // The chain's share of each chunk drops from 5 to 3 products per 16-column slice and it issues
-// no output stores.
+// no output stores.  The KEEP instantiation (the forward pass of the backward) has no output:
+// its second group of waves writes each chunk's initial state and D to the workspace instead,
+// from the same slots, and the copy waves leave Q~ and P out.
 template <typename IO, int DK, int C, int SPW, int NW>
 struct ScanOwLayout {
     using S = ScanLayout<IO, DK, C, SPW, NW>;
@@ -884,6 +905,8 @@ struct ScanOwLayout {
     static constexpr size_t oDb = oSb + (size_t)2 * NW * SB_UNITS * 64 * 16;
     static constexpr size_t kBytes = oDb + (size_t)2 * NW * DB_UNITS * 64 * 16;
     static constexpr bool kFits = S::kFits && kBytes <= 160 * 1024;
+    // KEEP: after the slots, one fp32 [16][LDK] tile per writer wave (kept rows leave through it)
+    static constexpr bool kFitsKeep = S::kFits && kBytes + S::kKeepBytes <= 160 * 1024;
     static_assert((Rec::KT * FB) % 16 == 0 && (2 * Rec::NPAIR * FB) % 16 == 0, "slot units");
 };
 
@@ -915,7 +938,7 @@ __device__ __forceinline__ void slot_get(const char *slot, int lane, Frag<BF> *f
     }
 }
 
-template <typename IO, int DK, int C, int SPW, int NW>
+template <typename IO, int DK, int C, int SPW, int NW, bool KEEP>
 __global__ void __launch_bounds__(64 * (2 * NW + scan_copy_waves(SPW))) kda_scan_ow_kernel(FwdParams p, const int32_t *__restrict__ chunk_off,
                                                                      const char *__restrict__ records) {
     using S = ScanLayout<IO, DK, C, SPW, NW>;
@@ -925,7 +948,7 @@ __global__ void __launch_bounds__(64 * (2 * NW + scan_copy_waves(SPW))) kda_scan
     constexpr int NSUB = Rec::NSUB, KT = Rec::KT, NPAIR = Rec::NPAIR, DVT = S::DVT, WC = S::WCOLS;
     using Tr = IoTraits<IO>;
 
-    __shared__ __attribute__((aligned(16))) char smem[SO::kBytes];
+    __shared__ __attribute__((aligned(16))) char smem[SO::kBytes + (KEEP ? S::kKeepBytes : 0)];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -960,15 +983,15 @@ __global__ void __launch_bounds__(64 * (2 * NW + scan_copy_waves(SPW))) kda_scan
     // output waves finish the final chunk.
     if (wave >= 2 * NW) {
         switch (wave - 2 * NW) {
-            case 0: copy_wave<IO, DK, C, SPW, NW, 0>(smem, rec0, rec_stride, vbase, vstride, len, nchunks, lane); break;
-            case 1: copy_wave<IO, DK, C, SPW, NW, 1>(smem, rec0, rec_stride, vbase, vstride, len, nchunks, lane); break;
+            case 0: copy_wave<IO, DK, C, SPW, NW, 0, KEEP>(smem, rec0, rec_stride, vbase, vstride, len, nchunks, lane); break;
+            case 1: copy_wave<IO, DK, C, SPW, NW, 1, KEEP>(smem, rec0, rec_stride, vbase, vstride, len, nchunks, lane); break;
             case 2:
                 if constexpr (S::NCW > 2)
-                    copy_wave<IO, DK, C, SPW, NW, 2>(smem, rec0, rec_stride, vbase, vstride, len, nchunks, lane);
+                    copy_wave<IO, DK, C, SPW, NW, 2, KEEP>(smem, rec0, rec_stride, vbase, vstride, len, nchunks, lane);
                 break;
             default:
                 if constexpr (S::NCW > 3)
-                    copy_wave<IO, DK, C, SPW, NW, 3>(smem, rec0, rec_stride, vbase, vstride, len, nchunks, lane);
+                    copy_wave<IO, DK, C, SPW, NW, 3, KEEP>(smem, rec0, rec_stride, vbase, vstride, len, nchunks, lane);
                 break;
         }
         __syncthreads();
@@ -976,7 +999,56 @@ __global__ void __launch_bounds__(64 * (2 * NW + scan_copy_waves(SPW))) kda_scan
     }
     static_assert(S::NCW <= 4, "copy wave count");
 
-    if (wave >= NW) {
+    if (KEEP && wave >= NW) {
+        // ---------------- writer waves (KEEP): the state entering chunk c and D of chunk c, in
+        // the operand type, as 16-byte row segments of [slot, H, d_k, d_v] and [slot, H, C, d_v]
+        using OT = typename std::conditional<BF, uint16_t, float>::type;
+        const int ow = wave - NW;
+        float *tile = reinterpret_cast<float *>(smem + SO::kBytes) + ow * 16 * S::LDK;
+        const int64_t cbase = g0 * H + h;  // slot of chunk 0
+        // one 16 x 16 fragment per slice into the tile (rows 4 q4 + j, column 16 s + l16), then out
+        auto put = [&](const Frag<BF> &f, int s) {
+            float x[4];
+            if constexpr (BF) {
+                x[0] = __uint_as_float(f.v.x << 16);
+                x[1] = __uint_as_float(f.v.x & 0xffff0000u);
+                x[2] = __uint_as_float(f.v.y << 16);
+                x[3] = __uint_as_float(f.v.y & 0xffff0000u);
+            } else {
+                x[0] = f.v.x; x[1] = f.v.y; x[2] = f.v.z; x[3] = f.v.w;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) tile[(4 * q4 + j) * S::LDK + 16 * s + l16] = x[j];
+        };
+        auto write_d = [&](int cp) {
+            Frag<BF> Db[SPW * 2 * NPAIR];
+            slot_get<BF, DBN>(smem + SO::oDb + (size_t)(((cp & 1) * NW + ow) * SO::DB_UNITS) * 64 * 16, lane, Db);
+            OT *dd = static_cast<OT *>(p.dch) + (cbase + (int64_t)cp * H) * C * DV + col0 + WC * ow;
+#pragma unroll
+            for (int R = 0; R < NSUB; ++R) {
+#pragma unroll
+                for (int s = 0; s < SPW; ++s) put(Db[s * 2 * NPAIR + R], s);
+                keep_rows<OT, WC, S::LDK>(dd + (int64_t)16 * R * DV, DV, tile, lane);
+            }
+        };
+        for (int c = 0; c < nchunks; ++c) {
+            __syncthreads();  // S of chunk c and D of chunk c - 1 are in their slots
+            if (c > 0) write_d(c - 1);
+            Frag<BF> Sb[SPW * KT];
+            slot_get<BF, SBN>(smem + SO::oSb + (size_t)(((c & 1) * NW + ow) * SO::SB_UNITS) * 64 * 16, lane, Sb);
+            OT *hs = static_cast<OT *>(p.hs) + (cbase + (int64_t)c * H) * DK * DV + col0 + WC * ow;
+#pragma unroll
+            for (int ct = 0; ct < KT; ++ct) {
+#pragma unroll
+                for (int s = 0; s < SPW; ++s) put(Sb[s * KT + ct], s);
+                keep_rows<OT, WC, S::LDK>(hs + (int64_t)16 * ct * DV, DV, tile, lane);
+            }
+        }
+        __syncthreads();  // D of the last chunk is in its slot
+        if (nchunks > 0) write_d(nchunks - 1);
+        return;
+    }
+    if (!KEEP && wave >= NW) {
         // ---------------- output waves: slice s holds columns col0 + WC*ow + 16*s + l16
         const int ow = wave - NW;
         IO *obase = static_cast<IO *>(p.out) + (start * H + h) * (int64_t)DV + col0 + WC * ow + 4 * q4;
@@ -1216,7 +1288,8 @@ hipError_t launch_split_variant(const FwdParams &p, char *workspace, int64_t chu
     if constexpr (!split_fits<IO, DK, C, SPW, NW>()) {
         return hipErrorInvalidConfiguration;
     } else {
-        if (keep && !ScanLayout<IO, DK, C, SPW, NW>::kFitsKeep) return hipErrorInvalidConfiguration;
+        if (keep && (!ScanLayout<IO, DK, C, SPW, NW>::kFitsKeep || p.out != nullptr))
+            return hipErrorInvalidConfiguration;  // the kept forward writes S and D, never O
         int32_t *chunk_off = reinterpret_cast<int32_t *>(workspace);
         char *records = workspace + split_plan_bytes(p.num_seqs);
         if (p.cu) {
@@ -1234,10 +1307,14 @@ hipError_t launch_split_variant(const FwdParams &p, char *workspace, int64_t chu
         const int64_t scan_blocks = (int64_t)p.num_seqs * p.H * (p.dv / ScanLayout<IO, DK, C, SPW, NW>::DVT);
         if (scan_blocks > 0) {
             if (keep) {
-                hipLaunchKernelGGL((kda_scan_kernel<IO, DK, C, SPW, NW, true>), dim3((unsigned)scan_blocks),
-                                   dim3(ScanLayout<IO, DK, C, SPW, NW>::NT), 0, stream, p, chunk_off, records);
+                if constexpr (ScanOwLayout<IO, DK, C, SPW, NW>::kFitsKeep)
+                    hipLaunchKernelGGL((kda_scan_ow_kernel<IO, DK, C, SPW, NW, true>), dim3((unsigned)scan_blocks),
+                                       dim3(ScanOwLayout<IO, DK, C, SPW, NW>::NT), 0, stream, p, chunk_off, records);
+                else
+                    hipLaunchKernelGGL((kda_scan_kernel<IO, DK, C, SPW, NW, true>), dim3((unsigned)scan_blocks),
+                                       dim3(ScanLayout<IO, DK, C, SPW, NW>::NT), 0, stream, p, chunk_off, records);
             } else if constexpr (ScanOwLayout<IO, DK, C, SPW, NW>::kFits) {
-                hipLaunchKernelGGL((kda_scan_ow_kernel<IO, DK, C, SPW, NW>), dim3((unsigned)scan_blocks),
+                hipLaunchKernelGGL((kda_scan_ow_kernel<IO, DK, C, SPW, NW, false>), dim3((unsigned)scan_blocks),
                                    dim3(ScanOwLayout<IO, DK, C, SPW, NW>::NT), 0, stream, p, chunk_off, records);
             } else {
                 hipLaunchKernelGGL((kda_scan_kernel<IO, DK, C, SPW, NW, false>), dim3((unsigned)scan_blocks),
