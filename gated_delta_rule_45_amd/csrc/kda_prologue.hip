@@ -82,23 +82,26 @@ __device__ __forceinline__ void find_seq(const PrologueArgs &a, int64_t t, int &
 constexpr int kConvTokensPerStream = 8;
 
 // One tensor (q, k or v): rows of D values at column offset `col` of the state's concatenated
-// q | k | v rows.  NORM: L2-normalise each row.  A workgroup takes one head and TT consecutive
-// tokens; each group of LPR lanes streams L of them in order, so a lane keeps its filter
-// taps and the last W-1 raw inputs of its channels in registers and loads each input once.
+// q | k | v rows.  NORM: L2-normalise each row.  Workgroup `bid` of the tensor takes one head
+// and TT consecutive tokens; each group of LPR lanes streams L of them in order, so a lane
+// keeps its filter taps and the last W-1 raw inputs of its channels in registers and loads
+// each input once.
+template <typename IO, int D>
+constexpr int conv_tokens_per_block() { return 256 / (D / Seg16<IO>::N) * kConvTokensPerStream; }
+
 template <typename IO, int D, bool NORM, int W>
-__global__ void __launch_bounds__(256) kda_conv_swish_kernel(PrologueArgs a, const IO *__restrict__ x,
-                                                            const float *__restrict__ w, const IO *__restrict__ st_in,
-                                                            IO *__restrict__ st_out, int col, IO *__restrict__ y) {
+__device__ __forceinline__ void conv_swish_rows(const PrologueArgs &a, int64_t bid, const IO *__restrict__ x,
+                                                const float *__restrict__ w, const IO *__restrict__ st_in,
+                                                IO *__restrict__ st_out, int col, IO *__restrict__ y) {
     constexpr int N = Seg16<IO>::N;
     constexpr int LPR = D / N;      // lanes per row
-    constexpr int G = 256 / LPR;    // token streams per workgroup
     constexpr int L = kConvTokensPerStream;
-    constexpr int TT = G * L;       // tokens per workgroup
+    constexpr int TT = conv_tokens_per_block<IO, D>();  // tokens per workgroup
     static_assert(LPR <= 64 && 64 % LPR == 0, "a row lives inside one wave");
     const int seg = threadIdx.x % LPR;
     const int stream = threadIdx.x / LPR;
-    const int h = (int)(blockIdx.x % a.H);
-    const int64_t t0 = (int64_t)(blockIdx.x / a.H) * TT + (int64_t)stream * L;
+    const int h = (int)(bid % a.H);
+    const int64_t t0 = (bid / a.H) * TT + (int64_t)stream * L;
     const int SD = 2 * a.dk + a.dv;  // state row width per head
 
     float wc[N * W];  // taps of this lane's N channels: N * W consecutive floats
@@ -181,6 +184,29 @@ __global__ void __launch_bounds__(256) kda_conv_swish_kernel(PrologueArgs a, con
     }
 }
 
+// q, k and v in one launch: workgroups [0, nb_k) take q, [nb_k, 2 nb_k) take k and the rest v,
+// so that the loads of some workgroups overlap the stores of others across the three tensors.
+template <typename IO>
+struct ConvQkv {
+    const IO *x[3];
+    const float *w[3];
+    IO *y[3];
+    const IO *st_in;
+    IO *st_out;
+    int64_t nb_k;  // workgroups per key-width tensor (q, k)
+};
+
+template <typename IO, int DK, int DV, int W>
+__global__ void __launch_bounds__(256) kda_conv_swish_kernel(PrologueArgs a, ConvQkv<IO> j) {
+    const int64_t b = blockIdx.x;
+    if (b < 2 * j.nb_k) {
+        const int t = b < j.nb_k ? 0 : 1;
+        conv_swish_rows<IO, DK, true, W>(a, b - t * j.nb_k, j.x[t], j.w[t], j.st_in, j.st_out, t * DK, j.y[t]);
+    } else {
+        conv_swish_rows<IO, DV, false, W>(a, b - 2 * j.nb_k, j.x[2], j.w[2], j.st_in, j.st_out, 2 * DK, j.y[2]);
+    }
+}
+
 // State rows of sequences shorter than W - 1: positions before the first token are carried over
 // from the incoming state (or zero).  One thread per (sequence, state row, head, 16-byte piece).
 template <typename IO>
@@ -221,22 +247,29 @@ __global__ void __launch_bounds__(256) kda_gate_beta_kernel(int64_t gcount, int6
     if (i < bcount) b[i] = 1.0f / (1.0f + __expf(-b_raw[i]));
 }
 
-template <typename IO, int D, bool NORM>
-hipError_t launch_conv(const PrologueArgs &a, const void *x, const float *w, const void *st_in, void *st_out, int col,
-                       void *y, hipStream_t s) {
-    constexpr int TT = 256 / (D / Seg16<IO>::N) * kConvTokensPerStream;  // tokens per workgroup
-    const int64_t blocks = (a.tokens + TT - 1) / TT * a.H;
+template <typename IO, int DK, int DV>
+hipError_t launch_conv(const PrologueArgs &a, const void *const raw[3], const float *const w[3], const void *st_in,
+                       void *st_out, void *const out[3], hipStream_t s) {
+    constexpr int TK = conv_tokens_per_block<IO, DK>(), TV = conv_tokens_per_block<IO, DV>();
+    const int64_t nb_k = (a.tokens + TK - 1) / TK * a.H;
+    const int64_t blocks = 2 * nb_k + (a.tokens + TV - 1) / TV * a.H;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    const IO *xi = static_cast<const IO *>(x);
-    const IO *si = static_cast<const IO *>(st_in);
-    IO *so = static_cast<IO *>(st_out), *yo = static_cast<IO *>(y);
+    ConvQkv<IO> j;
+    for (int i = 0; i < 3; ++i) {
+        j.x[i] = static_cast<const IO *>(raw[i]);
+        j.w[i] = w[i];
+        j.y[i] = static_cast<IO *>(out[i]);
+    }
+    j.st_in = static_cast<const IO *>(st_in);
+    j.st_out = static_cast<IO *>(st_out);
+    j.nb_k = nb_k;
     const dim3 g((unsigned)blocks), b(256);
     switch (a.W) {
-        case 1: hipLaunchKernelGGL((kda_conv_swish_kernel<IO, D, NORM, 1>), g, b, 0, s, a, xi, w, si, so, col, yo); break;
-        case 2: hipLaunchKernelGGL((kda_conv_swish_kernel<IO, D, NORM, 2>), g, b, 0, s, a, xi, w, si, so, col, yo); break;
-        case 3: hipLaunchKernelGGL((kda_conv_swish_kernel<IO, D, NORM, 3>), g, b, 0, s, a, xi, w, si, so, col, yo); break;
-        default: hipLaunchKernelGGL((kda_conv_swish_kernel<IO, D, NORM, 4>), g, b, 0, s, a, xi, w, si, so, col, yo); break;
+        case 1: hipLaunchKernelGGL((kda_conv_swish_kernel<IO, DK, DV, 1>), g, b, 0, s, a, j); break;
+        case 2: hipLaunchKernelGGL((kda_conv_swish_kernel<IO, DK, DV, 2>), g, b, 0, s, a, j); break;
+        case 3: hipLaunchKernelGGL((kda_conv_swish_kernel<IO, DK, DV, 3>), g, b, 0, s, a, j); break;
+        default: hipLaunchKernelGGL((kda_conv_swish_kernel<IO, DK, DV, 4>), g, b, 0, s, a, j); break;
     }
     return hipGetLastError();
 }
@@ -246,16 +279,11 @@ hipError_t launch_prologue_t(const PrologueArgs &a, const void *const raw[3], co
                              const float *g_raw, const float *b_raw, const void *st_in, void *st_out, void *const out[3],
                              float *g, float *b, hipStream_t s) {
     hipError_t e;
-    const int cols[3] = {0, a.dk, 2 * a.dk};
-    for (int j = 0; j < 3; ++j) {
-        const int D = j < 2 ? a.dk : a.dv;
-        const bool norm = j < 2;
-        if (D == 128) e = norm ? launch_conv<IO, 128, true>(a, raw[j], w[j], st_in, st_out, cols[j], out[j], s)
-                               : launch_conv<IO, 128, false>(a, raw[j], w[j], st_in, st_out, cols[j], out[j], s);
-        else e = norm ? launch_conv<IO, 64, true>(a, raw[j], w[j], st_in, st_out, cols[j], out[j], s)
-                      : launch_conv<IO, 64, false>(a, raw[j], w[j], st_in, st_out, cols[j], out[j], s);
-        if (e != hipSuccess) return e;
-    }
+    if (a.dk == 128) e = a.dv == 128 ? launch_conv<IO, 128, 128>(a, raw, w, st_in, st_out, out, s)
+                                     : launch_conv<IO, 128, 64>(a, raw, w, st_in, st_out, out, s);
+    else e = a.dv == 128 ? launch_conv<IO, 64, 128>(a, raw, w, st_in, st_out, out, s)
+                         : launch_conv<IO, 64, 64>(a, raw, w, st_in, st_out, out, s);
+    if (e != hipSuccess) return e;
     if (st_out && a.W > 1 && a.num_seqs > 0) {
         const int64_t total = (int64_t)a.num_seqs * (a.W - 1) * a.H * ((2 * a.dk + a.dv) / Seg16<IO>::N);
         hipLaunchKernelGGL(kda_conv_state_carry_kernel<IO>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a,
