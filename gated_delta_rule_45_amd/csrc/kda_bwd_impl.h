@@ -705,8 +705,7 @@ __global__ void __launch_bounds__(kBwdScanThreads) kda_bwd_scan_kernel(BwdParams
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) sH[(16 * ct + 4 * q4 + jj) * LDH + l16] = dS[ct][jj];
             OT *dh = static_cast<OT *>(bp.dhs) + slot_base * DK * DV + col0 + 16 * wave;
-#pragma unroll
-            for (int ct = 0; ct < KT; ++ct) keep_rows<OT, 16, LDH>(dh + (int64_t)16 * ct * DV, DV, sH + 16 * ct * LDH, lane);
+            keep_rows<OT, 16, LDH, DK>(dh, DV, sH, lane);  // all d_k rows: every read in flight together
         }
         Frag<BF> Sb[KT];
 #pragma unroll

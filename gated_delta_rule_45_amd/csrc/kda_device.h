@@ -157,16 +157,17 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_wave_barrier();
 }
 
-// Writes a 16 x WC fp32 tile held in LDS (row stride LDK floats) to dst (row stride ld elements,
-// element type OT: bf16 bits or fp32) as 16-byte row segments spread over the lanes of one wave.
-// Used to turn accumulator fragments (4 rows of one column per lane) into few wide stores.  The
-// tile is written by other lanes of the same wave just before and rewritten just after, so the
-// read-back is bracketed by wave_lds_sync (without it the compiler duplicated the code after the
-// partial-wave read-back into its divergent branches, and the lanes with no segment wrote the
-// next tile before the other lanes had read this one).
-template <typename OT, int WC, int LDK>
+// Writes a ROWS x WC fp32 tile held in LDS (row stride LDK floats) to dst (row stride ld
+// elements, element type OT: bf16 bits or fp32) as 16-byte row segments spread over the lanes of
+// one wave.  Used to turn accumulator fragments (4 rows of one column per lane) into few wide
+// stores; a tile of many rows keeps all of its LDS reads in flight at once.  The tile is written
+// by other lanes of the same wave just before and rewritten just after, so the read-back is
+// bracketed by wave_lds_sync (without it the compiler duplicated the code after the partial-wave
+// read-back into its divergent branches, and the lanes with no segment wrote the next tile before
+// the other lanes had read this one).
+template <typename OT, int WC, int LDK, int ROWS = 16>
 __device__ __forceinline__ void keep_rows(OT *dst, int64_t ld, const float *tile, int lane) {
-    constexpr int EPS = 16 / (int)sizeof(OT), SPR = WC / EPS, NSEG = 16 * SPR;
+    constexpr int EPS = 16 / (int)sizeof(OT), SPR = WC / EPS, NSEG = ROWS * SPR;
     static_assert(WC % EPS == 0 && LDK % 4 == 0, "whole 16-byte segments");
     wave_lds_sync();
 #pragma unroll
