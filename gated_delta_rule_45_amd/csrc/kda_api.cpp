@@ -331,6 +331,10 @@ size_t split_workspace_bytes(kda_dtype_t io, int dk, int chunk, int64_t chunk_up
     return split_plan_bytes(num_seqs) + (size_t)chunk_upper * H * rec;
 }
 
+bool split_scan_shape(kda_dtype_t io, int dk, int chunk, int spw, int nw, int &threads, int &lds) {
+    return io == KDA_BF16 ? split_scan_shape_bf16(dk, chunk, spw, nw, threads, lds)
+                          : split_scan_shape_f32(dk, chunk, spw, nw, threads, lds);
+}
 bool split_variant_supported(kda_dtype_t io, int dk, int chunk, int spw, int nw, bool keep) {
     return io == KDA_BF16 ? split_supported_bf16(dk, chunk, spw, nw, keep) : split_supported_f32(dk, chunk, spw, nw, keep);
 }
@@ -755,8 +759,10 @@ kda_status_t kda_query(const kda_problem_t *problem, uint32_t flags, kda_query_r
             res->chunk_size = r.cfg.chunk;
             if (two) {  // the scan pass: one workgroup per (sequence, head, 16*spw*nw columns)
                 res->dv_tile = 16 * r.spw * r.nw;
-                res->threads_per_block = 64 * (r.nw + (r.spw == 1 ? 4 : 2));
-                res->lds_bytes = 0;
+                int threads = 0, lds = 0;
+                kda::split_scan_shape(p.io_dtype, p.head_dim_k, r.cfg.chunk, r.spw, r.nw, threads, lds);
+                res->threads_per_block = threads;
+                res->lds_bytes = lds;
                 res->grid_blocks = (int64_t)r.num_seqs * p.num_heads * (p.head_dim_v / res->dv_tile);
             } else {
                 res->dv_tile = r.cfg.dv_tile;

@@ -56,12 +56,16 @@ constexpr int kChunkThreads = 256;
 inline size_t split_plan_bytes(int64_t num_seqs) { return (size_t)(((num_seqs + 1) * 4 + 255) / 256 * 256); }
 size_t split_workspace_bytes(kda_dtype_t io, int dk, int chunk, int64_t chunk_upper, int H, int64_t num_seqs);
 bool split_variant_supported(kda_dtype_t io, int dk, int chunk, int spw, int nw, bool keep = false);
+// workgroup size and LDS of the forward's scan kernel for a shape; false if not compiled
+bool split_scan_shape(kda_dtype_t io, int dk, int chunk, int spw, int nw, int &threads, int &lds);
 hipError_t launch_split_fwd(kda_dtype_t io, const FwdParams &p, int chunk, int spw, int nw, char *workspace,
                             int64_t chunk_upper, hipStream_t stream);
 // one entry per io dtype
 size_t split_record_size_f32(int dk, int chunk);
 size_t split_record_size_bf16(int dk, int chunk);
 bool split_supported_f32(int dk, int chunk, int spw, int nw, bool keep);
+bool split_scan_shape_f32(int dk, int chunk, int spw, int nw, int &threads, int &lds);
+bool split_scan_shape_bf16(int dk, int chunk, int spw, int nw, int &threads, int &lds);
 bool split_supported_bf16(int dk, int chunk, int spw, int nw, bool keep);
 hipError_t launch_split_f32(const FwdParams &p, int chunk, int spw, int nw, char *workspace, int64_t chunk_upper,
                             hipStream_t stream);

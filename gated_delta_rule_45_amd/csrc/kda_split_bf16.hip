@@ -4,6 +4,9 @@
 namespace kda {
 
 size_t split_record_size_bf16(int dk, int chunk) { return split_record_size<uint16_t>(dk, chunk); }
+bool split_scan_shape_bf16(int dk, int chunk, int spw, int nw, int &threads, int &lds) {
+    return split_scan_shape<uint16_t>(dk, chunk, spw, nw, threads, lds);
+}
 bool split_supported_bf16(int dk, int chunk, int spw, int nw, bool keep) {
     return split_supported<uint16_t>(dk, chunk, spw, nw, keep);
 }

@@ -4,6 +4,9 @@
 namespace kda {
 
 size_t split_record_size_f32(int dk, int chunk) { return split_record_size<float>(dk, chunk); }
+bool split_scan_shape_f32(int dk, int chunk, int spw, int nw, int &threads, int &lds) {
+    return split_scan_shape<float>(dk, chunk, spw, nw, threads, lds);
+}
 bool split_supported_f32(int dk, int chunk, int spw, int nw, bool keep) {
     return split_supported<float>(dk, chunk, spw, nw, keep);
 }

@@ -1352,6 +1352,24 @@ bool split_supported(int dk, int chunk, int spw, int nw, bool keep) {
     return false;
 }
 
+// Workgroup size and LDS of the scan kernel the forward launches for a shape (the output-wave
+// scan where its slots fit, else the single-role scan); false if the shape is not compiled.
+template <typename IO>
+bool split_scan_shape(int dk, int chunk, int spw, int nw, int &threads, int &lds) {
+#define KDA_SHAPE_CASE(DK_, C_, SPW_, NW_)                                                   \
+    if (dk == DK_ && chunk == C_ && spw == SPW_ && nw == NW_) {                              \
+        if (!split_fits<IO, DK_, C_, SPW_, NW_>()) return false;                             \
+        using SO = ScanOwLayout<IO, DK_, C_, SPW_, NW_>;                                     \
+        using SL = ScanLayout<IO, DK_, C_, SPW_, NW_>;                                       \
+        threads = SO::kFits ? SO::NT : SL::NT;                                               \
+        lds = (int)(SO::kFits ? SO::kBytes : SL::kBytes);                                    \
+        return true;                                                                         \
+    }
+    KDA_SPLIT_VARIANTS(KDA_SHAPE_CASE)
+#undef KDA_SHAPE_CASE
+    return false;
+}
+
 template <typename IO>
 hipError_t launch_split(const FwdParams &p, int chunk, int spw, int nw, char *workspace, int64_t chunk_upper,
                         hipStream_t stream) {

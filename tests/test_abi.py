@@ -169,6 +169,11 @@ def test_query_reports_config_and_work():
     assert r["flops"] == pytest.approx(ht * (2 * 64 * 256 + 64 * 64 / 3 + 6 * 128 * 128))
     assert r["hbm_bytes"] == pytest.approx(ht * 1540 + 2 * 4 * 128 * 128 * 64)
     assert 0 < rf["lds_bytes"] <= 160 * 1024
+    # the two-pass scan at this shape: 2 chain + 2 output + 4 copy waves; two double-buffered
+    # records and V tiles [64][32] bf16, then the parity-alternating S (8 bf16 fragments per lane)
+    # and D (4 fragments per lane) slots of the two chain waves
+    assert r["threads_per_block"] == 64 * 8
+    assert r["lds_bytes"] == 2 * rec + 2 * 64 * 32 * 2 + 2 * 2 * 64 * (64 + 32)
     assert r["peak_hbm_gbps"] == 8000.0 and r["peak_bf16_tflops"] == 2500.0
     # unsupported variant is reported, not raised
     r = kda.query(1, 64, 1, 128, 128, "f32", chunk_size=64)
