@@ -302,3 +302,30 @@ def test_forward_repeatable(dk, chunk, algo):
     o2, f2 = kda.chunk_fwd(*args, chunk_size=chunk, algo=algo)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(f1, f2)
+
+
+@pytest.mark.parametrize("io,dk,chunk", [("bf16", 128, 64), ("bf16", 64, 32), ("bf16", 128, 16), ("f32", 64, 32)])
+def test_scan_tilings_agree(io, dk, chunk):
+    """The two-pass forward with 32- and 64-column tiles (one or two 16-column slices per wave;
+    at d_k = 128, chunk 64 also two different scan kernels: chain and output on separate waves
+    with S and D handed over through LDS, against waves that do the whole chunk) rounds the same
+    operands and accumulates in the same order, so the two agree bit for bit; both are also
+    checked against the oracle.  Packed sequences with an empty and a one-token sequence
+    exercise the first and last chunk of each."""
+    lens = [0, 1, 77, 3 * chunk + 5, 2 * chunk]
+    inp = ki.make_inputs(1, 0, 3, dk, 128, io, seed=41, s0_std=0.1, lengths=lens)
+    d = on_dev(inp)
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"], d["cu_seqlens"])
+    out = {}
+    for tile in (32, 64):
+        if not kda.query(1, inp.q.shape[1], 3, dk, 128, io, chunk_size=chunk, dv_tile=tile, algo="two_pass",
+                         num_seqs=len(lens))["supported"]:
+            pytest.skip(f"two-pass {io} d_k={dk} chunk={chunk} tile={tile} not compiled")
+        out[tile] = kda.chunk_fwd(*args, chunk_size=chunk, dv_tile=tile, algo="two_pass")
+    torch.cuda.synchronize()
+    o_ref, s_ref = run_oracle(inp)
+    for tile in (32, 64):
+        compare(f"o (tile {tile})", out[tile][0], o_ref, io)
+        compare(f"final_state (tile {tile})", out[tile][1], s_ref, io)
+    assert torch.equal(out[32][0], out[64][0]), "outputs differ between the 32- and 64-column scans"
+    assert torch.equal(out[32][1], out[64][1]), "final states differ between the 32- and 64-column scans"
