@@ -108,17 +108,19 @@ def test_prefill_recurrent():
 
 
 @pytest.mark.parametrize("algo", ALGOS)
-def test_long_prefill_sampled_heads(algo):
+@pytest.mark.parametrize("chunk", [0, 64])  # the library's choice for this shape (32) and the workload's 64
+def test_long_prefill_sampled_heads(algo, chunk):
     inp = ki.workload_inputs("long_prefill")
-    check_fwd(inp, heads=[0, 17], label="long_prefill", algo=algo)
+    check_fwd(inp, heads=[0, 17], label="long_prefill", algo=algo, chunk_size=chunk)
     del inp
     torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("algo", ALGOS)
-def test_varlen_sampled_heads(algo):
+@pytest.mark.parametrize("chunk,dv_tile", [(0, 0), (32, 32)])  # default (chunk 64, 64 columns) and the other scan
+def test_varlen_sampled_heads(algo, chunk, dv_tile):
     inp = ki.workload_inputs("varlen")
-    check_fwd(inp, heads=[3, 30], label="varlen", algo=algo)
+    check_fwd(inp, heads=[3, 30], label="varlen", algo=algo, chunk_size=chunk, dv_tile=dv_tile if algo == "two_pass" else 0)
 
 
 def test_decode_full():
