@@ -50,12 +50,19 @@ struct SplitRecord {
     static constexpr size_t oQt = oKt + (size_t)NSUB * (KT / 2) * TILE_BYTES;
     static constexpr size_t oKbT = oQt + (size_t)NSUB * (KT / 2) * TILE_BYTES;
     // T and P are block lower triangular: row tile R keeps only its 32-wide column pairs
-    // pp <= R / 2, stored row tile after row tile.
-    static constexpr int TP_TILES = (NSUB / 2) * (NSUB / 2 + 1) + (NSUB % 2) * (NSUB / 2 + 1);
-    __host__ __device__ static constexpr int tp_tile(int R, int pp) { return (R / 2) * (R / 2 + 1) + (R % 2) * (R / 2 + 1) + pp; }
+    // pp <= R / 2, stored row tile after row tile.  For even R the last pair's right 16 columns
+    // lie above the diagonal, so that tile keeps only its left fragment (a half tile).
+    static constexpr int HALF_BYTES = 64 * FRAG_BYTES;
+    __host__ __device__ static constexpr bool tp_half(int R, int pp) { return R % 2 == 0 && 2 * pp == R; }
+    __host__ __device__ static constexpr int tp_off(int R, int pp) {  // byte offset inside T or P
+        int off = 0;
+        for (int r = 0; r < R; ++r) off += (r / 2) * TILE_BYTES + (r % 2 == 0 ? HALF_BYTES : TILE_BYTES);
+        return off + pp * TILE_BYTES;
+    }
+    static constexpr int TP_BYTES = (tp_off(NSUB, 0) + 1023) / 1024 * 1024;  // whole copy units
     static constexpr size_t oT = oKbT + (size_t)KT * NPAIR * TILE_BYTES;
-    static constexpr size_t oP = oT + (size_t)TP_TILES * TILE_BYTES;
-    static constexpr size_t oGam = oP + (size_t)TP_TILES * TILE_BYTES;
+    static constexpr size_t oP = oT + (size_t)TP_BYTES;
+    static constexpr size_t oGam = oP + (size_t)TP_BYTES;
     static constexpr size_t kRaw = oGam + (size_t)DK * 4;
     static constexpr size_t kBytes = (kRaw + 1023) / 1024 * 1024;  // whole 1 KB copy units
     static_assert(KT % 2 == 0, "d_k must be a multiple of 32");
@@ -83,6 +90,12 @@ __device__ __forceinline__ void load_pair(const char *tile, int lane, Frag<BF> &
     }
 }
 
+// one lane's left fragment of a half tile
+template <bool BF>
+__device__ __forceinline__ void store_frag(char *tile, int lane, const Frag<BF> &a) {
+    *reinterpret_cast<decltype(a.v) *>(tile + lane * (int)sizeof(a.v)) = a.v;
+}
+
 template <bool BF>
 struct FragPair {
     Frag<BF> a, b;
@@ -92,6 +105,31 @@ __device__ __forceinline__ FragPair<BF> ld_pair(const char *tile, int lane) {
     FragPair<BF> f;
     load_pair<BF>(tile, lane, f.a, f.b);
     return f;
+}
+// tile (R, pp) of T or P at `base`: a full pair, or a half tile's left fragment (b is zero)
+template <bool BF, typename Rec>
+__device__ __forceinline__ FragPair<BF> ld_tp(const char *base, int R, int pp, int lane) {
+    if (Rec::tp_half(R, pp)) {
+        FragPair<BF> f;
+        f.a.v = *reinterpret_cast<const decltype(f.a.v) *>(base + Rec::tp_off(R, pp) + lane * (int)sizeof(f.a.v));
+        f.b = make_frag<BF>(0.f, 0.f, 0.f, 0.f);
+        return f;
+    }
+    return ld_pair<BF>(base + Rec::tp_off(R, pp), lane);
+}
+// acc += (tile (R, pp) of T or P) x (the matching two 16-token operand fragments), and its
+// transpose-side twin; a half tile contracts over its left 16 tokens only
+template <bool BF, typename Rec>
+__device__ __forceinline__ void mma_tp_left(f32x4 &acc, const FragPair<BF> &t, const Frag<BF> &y0, const Frag<BF> &y1,
+                                            int R, int pp) {
+    if (Rec::tp_half(R, pp)) mma16(acc, t.a, y0);
+    else mma32(acc, t.a, t.b, y0, y1);
+}
+template <bool BF, typename Rec>
+__device__ __forceinline__ void mma_tp_right(f32x4 &acc, const Frag<BF> &x0, const Frag<BF> &x1, const FragPair<BF> &t,
+                                             int R, int pp) {
+    if (Rec::tp_half(R, pp)) mma16(acc, x0, t.a);
+    else mma32(acc, x0, x1, t.a, t.b);
 }
 
 // Sequence n and chunk c of global chunk index gidx; false if gidx is past the last chunk.
@@ -368,7 +406,10 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
 #pragma unroll
         for (int pp = 0; pp < NPAIR; ++pp)
             if (2 * pp <= R)
-                store_pair<BF>(rec + Rec::oP + (size_t)Rec::tp_tile(R, pp) * Rec::TILE_BYTES, lane, pf[2 * pp], pf[2 * pp + 1]);
+            {
+                if (Rec::tp_half(R, pp)) store_frag<BF>(rec + Rec::oP + Rec::tp_off(R, pp), lane, pf[2 * pp]);
+                else store_pair<BF>(rec + Rec::oP + Rec::tp_off(R, pp), lane, pf[2 * pp], pf[2 * pp + 1]);
+            }
 
         // X_RR = (I + A_RR)^{-1}, row by row; lane l16 owns column l16 (this wave wrote A_RR)
         wave_lds_sync();
@@ -443,7 +484,8 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
                                            : make_float4(0.f, 0.f, 0.f, 0.f);
                 f[u] = make_frag<BF>(xv.x * bv.x, xv.y * bv.y, xv.z * bv.z, xv.w * bv.w);
             }
-            store_pair<BF>(rec + Rec::oT + (size_t)Rec::tp_tile(R, pp) * Rec::TILE_BYTES, lane, f[0], f[1]);
+            if (Rec::tp_half(R, pp)) store_frag<BF>(rec + Rec::oT + Rec::tp_off(R, pp), lane, f[0]);
+            else store_pair<BF>(rec + Rec::oT + Rec::tp_off(R, pp), lane, f[0], f[1]);
         }
     }
 }
@@ -759,7 +801,7 @@ __global__ void __launch_bounds__(64 * (NW + scan_copy_waves(SPW))) kda_scan_ker
 #pragma unroll
                     for (int pp = 0; pp < NPAIR; ++pp)
                         if (2 * pp <= R)
-                            Tf[R][pp] = ld_pair<BF>(rb + Rec::oT + (size_t)Rec::tp_tile(R, pp) * Rec::TILE_BYTES, lane);
+                            Tf[R][pp] = ld_tp<BF, Rec>(rb + Rec::oT, R, pp, lane);
             }
             if (rt == GP) {
                 if constexpr (!KEEP)
@@ -768,7 +810,7 @@ __global__ void __launch_bounds__(64 * (NW + scan_copy_waves(SPW))) kda_scan_ker
 #pragma unroll
                         for (int pp = 0; pp < NPAIR; ++pp)
                             if (2 * pp <= R)
-                                Pf[R][pp] = ld_pair<BF>(rb + Rec::oP + (size_t)Rec::tp_tile(R, pp) * Rec::TILE_BYTES, lane);
+                                Pf[R][pp] = ld_tp<BF, Rec>(rb + Rec::oP, R, pp, lane);
                 read_kbt(0, KT_H);
             }
             if (rt == NSUB - 1) read_kbt(KT_H, KT);
@@ -798,7 +840,7 @@ __global__ void __launch_bounds__(64 * (NW + scan_copy_waves(SPW))) kda_scan_ker
                 for (int pp = 0; pp < NPAIR; ++pp)
                     if (2 * pp <= R)
 #pragma unroll
-                        for (int s = 0; s < SPW; ++s) mma32(d[s], Tf[R][pp].a, Tf[R][pp].b, Yb[s][2 * pp], Yb[s][2 * pp + 1]);
+                        for (int s = 0; s < SPW; ++s) mma_tp_left<BF, Rec>(d[s], Tf[R][pp], Yb[s][2 * pp], Yb[s][2 * pp + 1], R, pp);
 #pragma unroll
                 for (int s = 0; s < SPW; ++s) Db[s][R] = frag_from_acc<BF>(d[s]);
                 if constexpr (KEEP) {  // D of this chunk for the backward pass (operand type)
@@ -843,7 +885,7 @@ __global__ void __launch_bounds__(64 * (NW + scan_copy_waves(SPW))) kda_scan_ker
                 for (int pp = 0; pp < NPAIR; ++pp)
                     if (2 * pp <= R)
 #pragma unroll
-                        for (int s = 0; s < SPW; ++s) mma32(Ot[s][R], Db[s][2 * pp], Db[s][2 * pp + 1], Pf[R][pp].a, Pf[R][pp].b);
+                        for (int s = 0; s < SPW; ++s) mma_tp_right<BF, Rec>(Ot[s][R], Db[s][2 * pp], Db[s][2 * pp + 1], Pf[R][pp], R, pp);
 
 #pragma unroll
         for (int ct = 0; ct < KT; ++ct)
@@ -1065,8 +1107,8 @@ __global__ void __launch_bounds__(64 * (2 * NW + scan_copy_waves(SPW))) kda_scan
                     if (2 * pp <= R)
 #pragma unroll
                         for (int s = 0; s < SPW; ++s)
-                            mma32(Ot[s][R], Db[s * 2 * NPAIR + 2 * pp], Db[s * 2 * NPAIR + 2 * pp + 1], Pf[R][pp].a,
-                                  Pf[R][pp].b);
+                            mma_tp_right<BF, Rec>(Ot[s][R], Db[s * 2 * NPAIR + 2 * pp], Db[s * 2 * NPAIR + 2 * pp + 1],
+                                                  Pf[R][pp], R, pp);
             const int clen = min(C, len - cp * C);
             IO *oc = obase + (int64_t)cp * C * vstride;
 #pragma unroll
@@ -1097,7 +1139,7 @@ __global__ void __launch_bounds__(64 * (2 * NW + scan_copy_waves(SPW))) kda_scan
 #pragma unroll
                 for (int pp = 0; pp < NPAIR; ++pp)
                     if (2 * pp <= R)
-                        Pf[R][pp] = ld_pair<BF>(rb + Rec::oP + (size_t)Rec::tp_tile(R, pp) * Rec::TILE_BYTES, lane);
+                        Pf[R][pp] = ld_tp<BF, Rec>(rb + Rec::oP, R, pp, lane);
             // O^T = S^T Q~^T, one row tile at a time
 #pragma unroll
             for (int rt = 0; rt < NSUB; ++rt) {
@@ -1185,7 +1227,7 @@ __global__ void __launch_bounds__(64 * (2 * NW + scan_copy_waves(SPW))) kda_scan
 #pragma unroll
                     for (int pp = 0; pp < NPAIR; ++pp)
                         if (2 * pp <= R)
-                            Tf[R][pp] = ld_pair<BF>(rb + Rec::oT + (size_t)Rec::tp_tile(R, pp) * Rec::TILE_BYTES, lane);
+                            Tf[R][pp] = ld_tp<BF, Rec>(rb + Rec::oT, R, pp, lane);
             }
             if (rt == GP) read_kbt(0, KT_H);
             if (rt == NSUB - 1) read_kbt(KT_H, KT);
@@ -1215,7 +1257,7 @@ __global__ void __launch_bounds__(64 * (2 * NW + scan_copy_waves(SPW))) kda_scan
                 for (int pp = 0; pp < NPAIR; ++pp)
                     if (2 * pp <= R)
 #pragma unroll
-                        for (int s = 0; s < SPW; ++s) mma32(d[s], Tf[R][pp].a, Tf[R][pp].b, Yb[s][2 * pp], Yb[s][2 * pp + 1]);
+                        for (int s = 0; s < SPW; ++s) mma_tp_left<BF, Rec>(d[s], Tf[R][pp], Yb[s][2 * pp], Yb[s][2 * pp + 1], R, pp);
 #pragma unroll
                 for (int s = 0; s < SPW; ++s) Db[s * 2 * NPAIR + R] = frag_from_acc<BF>(d[s]);
             }

@@ -157,8 +157,9 @@ def test_query_reports_config_and_work():
     assert r["status"] == kda.KDA_OK and r["supported"] == 1
     assert r["algo"] == kda.KDA_ALGO_TWO_PASS and r["chunk_size"] == 64
     # chunk-offset table (256 B) + one record per chunk-head: K~, Q~, K-^T (16 KB each),
-    # the 6 lower 16x32 tiles of T and of P (6 KB each), Gamma (512 B), rounded up to whole KB
-    rec = 3 * 16384 + 2 * 6144 + 512
+    # the lower 16x32 tiles of T and of P (5 KB each: the two diagonal tiles of even row tiles
+    # keep only their left 16 columns), Gamma (512 B), rounded up to whole KB
+    rec = 3 * 16384 + 2 * 5120 + 512
     rec = (rec + 1023) // 1024 * 1024
     assert r["workspace_bytes"] == 256 + 4 * 64 * 16 * rec
     assert r["grid_blocks"] == 4 * 16 * (128 // r["dv_tile"])
@@ -264,10 +265,10 @@ def test_bwd_workspace_query():
     lib = kda.library()
     n = ctypes.c_size_t(0)
     assert lib.kda_chunk_bwd_workspace(ctypes.byref(_bwd_problem()), ctypes.byref(n)) == kda.KDA_OK
-    # plan + two-pass records (62,464 B per chunk and head at bf16, d_k = 128, chunk 64), then chunk
+    # plan + two-pass records (60,416 B per chunk and head at bf16, d_k = 128, chunk 64), then chunk
     # states and their gradients, D and dU tiles (all bf16, the operand type), in 256-byte sections
     a256 = lambda x: (x + 255) // 256 * 256
-    rec = (3 * 16384 + 2 * 6144 + 512 + 1023) // 1024 * 1024  # whole KB: 62,464
+    rec = (3 * 16384 + 2 * 5120 + 512 + 1023) // 1024 * 1024  # whole KB: 60,416
     # reverse-scan records as the scan keeps them in LDS (rows padded by 16 B): M [64][136] and
     # N [64][72], Q~^T and (beta K~)^T [128][72] (bf16), e^{G_C} and beta (fp32): 64,256 B,
     # rounded up to whole KB
