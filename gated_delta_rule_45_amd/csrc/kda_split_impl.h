@@ -68,14 +68,18 @@ struct SplitRecord {
     static_assert(KT % 2 == 0, "d_k must be a multiple of 32");
 };
 
-// store one lane's two 16-wide fragments of a 16 x 32 tile
+// store one lane's two 16-wide fragments of a 16 x 32 tile.  Record writes are nontemporal:
+// the scan reads them only after this kernel ends, and dirty record lines left in L2 slowed the
+// scan's first loads (prefill call 222 -> 218 us with these stores nontemporal).
 template <bool BF>
 __device__ __forceinline__ void store_pair(char *tile, int lane, const Frag<BF> &a, const Frag<BF> &b) {
     if constexpr (BF) {
-        *reinterpret_cast<uint4 *>(tile + lane * 16) = make_uint4(a.v.x, a.v.y, b.v.x, b.v.y);
+        const u32x4 w = {a.v.x, a.v.y, b.v.x, b.v.y};
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(tile + lane * 16));
     } else {
-        *reinterpret_cast<float4 *>(tile + lane * 32) = a.v;
-        *reinterpret_cast<float4 *>(tile + lane * 32 + 16) = b.v;
+        const f32x4 x = {a.v.x, a.v.y, a.v.z, a.v.w}, y = {b.v.x, b.v.y, b.v.z, b.v.w};
+        __builtin_nontemporal_store(x, reinterpret_cast<f32x4 *>(tile + lane * 32));
+        __builtin_nontemporal_store(y, reinterpret_cast<f32x4 *>(tile + lane * 32 + 16));
     }
 }
 template <bool BF>
