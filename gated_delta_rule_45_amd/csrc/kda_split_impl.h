@@ -951,8 +951,11 @@ struct ScanOwLayout {
     static constexpr size_t oDb = oSb + (size_t)2 * NW * SB_UNITS * 64 * 16;
     static constexpr size_t kBytes = oDb + (size_t)2 * NW * DB_UNITS * 64 * 16;
     static constexpr bool kFits = S::kFits && kBytes <= 160 * 1024;
-    // KEEP: after the slots, one fp32 [16][LDK] tile per writer wave (kept rows leave through it)
-    static constexpr bool kFitsKeep = S::kFits && kBytes + S::kKeepBytes <= 160 * 1024;
+    // KEEP: after the slots, one fp32 [KROWS][LDK] tile per writer wave (kept rows leave through
+    // it): 64 rows where they fit, so a chunk's state and D leave in 3 read-backs, else 16
+    static constexpr int KROWS = kBytes + (size_t)NW * 64 * S::LDK * 4 <= 160 * 1024 ? 64 : 16;
+    static constexpr size_t kKeepBytes = (size_t)NW * KROWS * S::LDK * 4;
+    static constexpr bool kFitsKeep = S::kFits && kBytes + kKeepBytes <= 160 * 1024;
     static_assert((Rec::KT * FB) % 16 == 0 && (2 * Rec::NPAIR * FB) % 16 == 0, "slot units");
 };
 
@@ -994,7 +997,7 @@ __global__ void __launch_bounds__(64 * (2 * NW + scan_copy_waves(SPW))) kda_scan
     constexpr int NSUB = Rec::NSUB, KT = Rec::KT, NPAIR = Rec::NPAIR, DVT = S::DVT, WC = S::WCOLS;
     using Tr = IoTraits<IO>;
 
-    __shared__ __attribute__((aligned(16))) char smem[SO::kBytes + (KEEP ? S::kKeepBytes : 0)];
+    __shared__ __attribute__((aligned(16))) char smem[SO::kBytes + (KEEP ? SO::kKeepBytes : 0)];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1050,10 +1053,12 @@ __global__ void __launch_bounds__(64 * (2 * NW + scan_copy_waves(SPW))) kda_scan
         // the operand type, as 16-byte row segments of [slot, H, d_k, d_v] and [slot, H, C, d_v]
         using OT = typename std::conditional<BF, uint16_t, float>::type;
         const int ow = wave - NW;
-        float *tile = reinterpret_cast<float *>(smem + SO::kBytes) + ow * 16 * S::LDK;
+        constexpr int KR = SO::KROWS, TPR = KR / 16;  // tile rows, 16-row fragments per read-back
+        float *tile = reinterpret_cast<float *>(smem + SO::kBytes) + ow * KR * S::LDK;
         const int64_t cbase = g0 * H + h;  // slot of chunk 0
-        // one 16 x 16 fragment per slice into the tile (rows 4 q4 + j, column 16 s + l16), then out
-        auto put = [&](const Frag<BF> &f, int s) {
+        // one 16 x 16 fragment per slice into 16-row block b of the tile (rows 16 b + 4 q4 + j,
+        // column 16 s + l16); every TPR blocks the tile goes out as row segments
+        auto put = [&](const Frag<BF> &f, int s, int b) {
             float x[4];
             if constexpr (BF) {
                 x[0] = __uint_as_float(f.v.x << 16);
@@ -1064,17 +1069,19 @@ __global__ void __launch_bounds__(64 * (2 * NW + scan_copy_waves(SPW))) kda_scan
                 x[0] = f.v.x; x[1] = f.v.y; x[2] = f.v.z; x[3] = f.v.w;
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) tile[(4 * q4 + j) * S::LDK + 16 * s + l16] = x[j];
+            for (int j = 0; j < 4; ++j) tile[(16 * b + 4 * q4 + j) * S::LDK + 16 * s + l16] = x[j];
         };
         auto write_d = [&](int cp) {
             Frag<BF> Db[SPW * 2 * NPAIR];
             slot_get<BF, DBN>(smem + SO::oDb + (size_t)(((cp & 1) * NW + ow) * SO::DB_UNITS) * 64 * 16, lane, Db);
             OT *dd = static_cast<OT *>(p.dch) + (cbase + (int64_t)cp * H) * C * DV + col0 + WC * ow;
+            constexpr int DG = NSUB < TPR ? NSUB : TPR;  // 16-row blocks of D per read-back (divides NSUB)
 #pragma unroll
             for (int R = 0; R < NSUB; ++R) {
 #pragma unroll
-                for (int s = 0; s < SPW; ++s) put(Db[s * 2 * NPAIR + R], s);
-                keep_rows<OT, WC, S::LDK>(dd + (int64_t)16 * R * DV, DV, tile, lane);
+                for (int s = 0; s < SPW; ++s) put(Db[s * 2 * NPAIR + R], s, R % DG);
+                if (R % DG == DG - 1)
+                    keep_rows<OT, WC, S::LDK, 16 * DG>(dd + (int64_t)16 * (R - DG + 1) * DV, DV, tile, lane);
             }
         };
         for (int c = 0; c < nchunks; ++c) {
@@ -1086,8 +1093,9 @@ __global__ void __launch_bounds__(64 * (2 * NW + scan_copy_waves(SPW))) kda_scan
 #pragma unroll
             for (int ct = 0; ct < KT; ++ct) {
 #pragma unroll
-                for (int s = 0; s < SPW; ++s) put(Sb[s * KT + ct], s);
-                keep_rows<OT, WC, S::LDK>(hs + (int64_t)16 * ct * DV, DV, tile, lane);
+                for (int s = 0; s < SPW; ++s) put(Sb[s * KT + ct], s, ct % TPR);
+                if (ct % TPR == TPR - 1)  // d_k / 16 is a multiple of TPR (d_k is 64 or 128)
+                    keep_rows<OT, WC, S::LDK, KR>(hs + (int64_t)16 * (ct - TPR + 1) * DV, DV, tile, lane);
             }
         }
         __syncthreads();  // D of the last chunk is in its slot
