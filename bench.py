@@ -189,7 +189,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the KDA path has no multi-GPU mode (heads and sequences are "
-              "independent; see the sharding note in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+              "independent, so more GPUs would each take a share of them). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
