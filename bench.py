@@ -6,6 +6,9 @@ One step = one pass of the hot path over one batch of synthetic input:
     fp32 gate/beta/state, chunk 64, initial state given, final state written), and
   * kda_decode_step over the decode workload (256 sequences x 32 heads, fp32 state
     128x128 updated in place).
+The long-prefill (1 x 131,072 tokens x 32 heads) and packed-varlen (64 sequences, lengths
+U[1, 8192], 32 heads) workloads are timed as their own legs (`long_prefill`, `varlen`), each with
+its CPU-oracle rate on a sample of heads.
 The prologue (kda_prologue: short convolution + Swish, q/k L2 norm, gate and beta activations)
 and the output epilogue (kda_norm_gate: per-head RMSNorm and output gate) are timed on their
 own over the prefill shapes and reported next to the step, and so is the backward (kda_chunk_bwd:
@@ -15,7 +18,7 @@ reported in GB/s next to it.  Inputs are resident in HBM before the timed region
 Timing uses HIP events recorded on the stream the kernels are launched on.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--algo auto|fused|two_pass] [--dv-tile T]
-                       [--no-cpu-baseline] [--no-tune] [--no-compare] [--dplr-sweep]
+                       [--no-cpu-baseline] [--no-tune] [--no-compare] [--no-workloads] [--dplr-sweep]
 """
 import argparse
 import hashlib
@@ -136,6 +139,64 @@ def cpu_baseline(inp):
             "decode_ms_per_step": round(ddt * 1e3, 2)}
 
 
+def workload_leg(name, kda, ki, torch, dev, stream, steps, cpu_heads, want_cpu):
+    """kda_chunk_fwd over one of the other full-size chunked workloads (long prefill, packed varlen),
+    inputs drawn on the GPU with the workload's recipe and seed (kda_inputs.workload_inputs_on),
+    library-default configuration, initial state given and final state written.  The CPU oracle is
+    timed on `cpu_heads` of its heads (all sequences, all tokens of those heads)."""
+    w = ki.WORKLOADS[name]
+    inp = ki.workload_inputs_on(name, dev)
+    B, T, H = inp.q.shape[0], inp.q.shape[1], inp.q.shape[2]
+    n = inp.num_seqs
+    varlen = inp.cu_seqlens is not None
+    out = torch.empty_like(inp.v)
+    fin = torch.empty((n, H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    cu_host = inp.cu_seqlens.cpu() if varlen else None
+    q = kda.query(B, T, H, w.dk, w.dv, w.io, num_seqs=n if varlen else 0, device=True)
+    ws = torch.empty(max(q["workspace_bytes"], 1), dtype=torch.uint8, device=dev)
+
+    def call():
+        kda.chunk_fwd(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.s0, inp.cu_seqlens, cu_seqlens_host=cu_host,
+                      workspace=ws, out=out, final_state=fin)
+
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    reps = max(3, steps // 4)
+    ms = time_launches(call, reps, stream)
+    tokens = B * T
+    gbps = q["hbm_bytes"] / (ms * 1e-3) / 1e9
+    leg = {"workload": f"{name}: " + (f"{n} packed sequences, {T} tokens" if varlen else f"B={B} T={T}") +
+                       f", H={H}, d_k=d_v={w.dk}, {w.io} q/k/v, fp32 gate/beta/state",
+           "chunk": q["chunk_size"], "dv_tile": q["dv_tile"], "algo": ["auto", "fused", "two_pass"][q["algo"]],
+           "calls_timed": reps, "ms": round(ms, 4), "tokens_per_s": round(tokens / (ms * 1e-3), 1),
+           "bytes_per_launch": q["hbm_bytes"], "gb_per_s": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
+           "tflops": round(q["flops"] / (ms * 1e-3) / 1e12, 2),
+           "data": "synthetic, drawn on the GPU with the workload's recipe and seed"}
+    log(f"{name}: {leg['ms']} ms per call, {leg['tokens_per_s'] / 1e6:.1f} M tokens/s, hbm_frac {leg['hbm_frac']}")
+    if want_cpu:
+        import oracle
+        sel = list(range(min(cpu_heads, H)))
+        host = lambda x: x[:, :, sel].contiguous().cpu()
+        a = [ki.to_numpy_io(host(x)) for x in (inp.q, inp.k, inp.v)]
+        g, beta = host(inp.g).numpy(), host(inp.beta).numpy()
+        s0 = inp.s0[:, sel].contiguous().cpu().numpy()
+        threads = oracle.default_threads()
+        t0 = time.perf_counter()
+        oracle.fwd(*a, g, beta, initial_state=s0, cu_seqlens=None if cu_host is None else cu_host.numpy(),
+                   threads=threads)
+        dt = time.perf_counter() - t0
+        # tokens/s of the whole workload at the sample's rate (the oracle's cost is linear in heads)
+        leg["cpu_baseline"] = {"value": round(tokens * len(sel) / H / dt, 1), "unit": "tokens/s", "cores": threads,
+                               "kind": "oracle",
+                               "sample": f"{len(sel)} of {H} heads, every sequence and token, fp64 token recurrence, "
+                                         f"{dt:.2f} s wall, scaled to the whole workload"}
+        log(f"{name}: CPU oracle on {len(sel)} heads took {dt:.1f} s")
+    del inp, out, fin, ws
+    torch.cuda.empty_cache()
+    return leg
+
+
 def dplr_sweep(kda, ki, torch, dev, stream, steps):
     """KDA (fused and two-pass) against the general-DPLR comparator over sequence lengths,
     4 sequences x 16 heads, d = 128, chunk 64, bf16."""
@@ -178,6 +239,8 @@ def main():
     ap.add_argument("--chunk", type=int, default=64)
     ap.add_argument("--algo", default="auto", choices=["auto", "fused", "two_pass"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the long-prefill and packed-varlen legs (profiling runs of the prefill shape)")
     ap.add_argument("--dplr-sweep", action="store_true",
                     help="also time the general-DPLR comparator against KDA over sequence lengths 1K..16K")
     ap.add_argument("--no-compare", action="store_true",
@@ -374,6 +437,12 @@ def main():
                      "gb_per_s": round(epi_gbps, 1), "hbm_frac": round(epi_gbps / PEAK_HBM_GBPS, 4),
                      "bytes_per_launch": epi_bytes, "traffic": traffic.get("epilogue_bytes")},
     }
+    if not args.no_workloads:
+        del d, d_out_b, dsf_b, bws, bout, a_d, b_d, kw_d, cmp_out, cmp_fin, ws, pd, eo, ez, ew, eout
+        torch.cuda.empty_cache()
+        res["long_prefill"] = workload_leg("long_prefill", kda, ki, torch, dev, stream, args.steps, 16,
+                                           not args.no_cpu_baseline)
+        res["varlen"] = workload_leg("varlen", kda, ki, torch, dev, stream, args.steps, 8, not args.no_cpu_baseline)
     if args.dplr_sweep:
         res["dplr_sweep"] = dplr_sweep(kda, ki, torch, dev, stream, args.steps)
     if not args.no_cpu_baseline:

@@ -121,6 +121,14 @@ def _stream_handle(device: torch.device, stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _keep_for_stream(t: Optional[torch.Tensor], device: torch.device, stream) -> None:
+    """A scratch tensor allocated here (on the current stream) and dropped on return: tell the
+    caching allocator that the launch stream still uses it, so the block is not handed to a new
+    allocation before the kernels queued on that stream have finished with it."""
+    if t is not None and stream is not None and stream != torch.cuda.current_stream(device):
+        t.record_stream(stream)
+
+
 def _io_code(dtype: torch.dtype) -> int:
     if dtype == torch.bfloat16:
         return KDA_BF16
@@ -219,17 +227,19 @@ def _fwd(entry: str, q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_hos
         ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
         res = QueryResult()
         st = lib.kda_tune(*common, ws_ptr, ws_len, _stream_handle(dev, stream), ctypes.byref(res))
-        _check(st)
+        _check(st)  # kda_tune synchronises the stream before it returns
         d = {name: getattr(res, name) for name, _ in QueryResult._fields_}
         d["arch"] = res.arch.decode()
         return d, out, final_state
     if entry == "chunk":
+        own_ws = None
         if workspace is None and p.algo != KDA_ALGO_FUSED:
             need = workspace_bytes(p)
-            workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+            workspace = own_ws = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
         ws_ptr = None if workspace is None else ctypes.c_void_p(workspace.data_ptr())
         ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
         st = lib.kda_chunk_fwd(*common, ws_ptr, ws_len, _stream_handle(dev, stream))
+        _keep_for_stream(own_ws, dev, stream)
     else:
         st = lib.kda_recurrent_fwd(*common, _stream_handle(dev, stream))
     _check(st)
@@ -307,14 +317,16 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
             _need(out[key], key, dt, shape, dev)
         if out.get("d_initial_state") is not None:
             _need(out["d_initial_state"], "d_initial_state", torch.float32, (n, H, dk, dv), dev)
+    own_ws = None
     if workspace is None:
-        workspace = torch.empty(bwd_workspace_bytes(p), dtype=torch.uint8, device=dev)
+        workspace = own_ws = torch.empty(bwd_workspace_bytes(p), dtype=torch.uint8, device=dev)
     lib = library()
     st = lib.kda_chunk_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
                            _ptr(cu_seqlens), None if host_cu is None else ctypes.c_void_p(host_cu.data_ptr()),
                            _ptr(d_out), _ptr(d_final_state), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
                            _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["d_initial_state"]),
                            ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream_handle(dev, stream))
+    _keep_for_stream(own_ws, dev, stream)
     _check(st)
     return out
 

@@ -116,8 +116,14 @@ kda_status_t kda_chunk_fwd(const kda_problem_t *problem, const void *q, const vo
 
 /*
  * kda_recurrent_fwd -- the same function evaluated token by token on the GPU
- * (reference mode: no chunking, fp32 arithmetic throughout).  Arguments and layouts
- * as for kda_chunk_fwd; problem->chunk_size is ignored.
+ * (reference mode: no chunking, fp32 arithmetic throughout).  Kimi Linear summary page,
+ * "Kimi Delta Attention: fine-grained memory control" section (the per-token recurrence with
+ * a per-channel decay and the delta-rule correction) and "From linear attention to Gated
+ * DeltaNet" (the rank-1 update read as one step of online gradient descent).  This is the
+ * definition the chunked form re-associates exactly, evaluated without chunking: a GPU
+ * second opinion for kda_chunk_fwd and the path for very short sequences.
+ * Arguments, layouts, ownership and errors as for kda_chunk_fwd; problem->chunk_size,
+ * dv_tile and algo are ignored and no workspace is used.
  */
 kda_status_t kda_recurrent_fwd(const kda_problem_t *problem, const void *q, const void *k, const void *v,
                                const float *g, const float *beta, const float *initial_state,
@@ -283,9 +289,15 @@ typedef struct {
 /*
  * kda_query -- tuning/query entry point: reports how kda_chunk_fwd will run the
  * problem (chunk, tile, grid, LDS, workspace), its algorithmic flops and bytes, and
- * optionally the current device.  Launches nothing.  A problem with num_seqs > 0
- * describes a packed batch (batch must be 1, seq_len is the token count); set
- * num_seqs = 0 to describe a plain batch of `batch` sequences.
+ * optionally the current device.  Kimi Linear summary page, "Chunkwise parallel algorithm"
+ * section: the chunk length is a free parameter of the chunked evaluation (the result does
+ * not depend on it, only the speed), and the intra-chunk work is matrix products sized by it;
+ * this call reports the choice and the work it implies.  Launches nothing and allocates
+ * nothing.  A problem with num_seqs > 0 describes a packed batch (batch must be 1, seq_len is
+ * the token count); set num_seqs = 0 to describe a plain batch of `batch` sequences.
+ * Returns KDA_OK (result filled, supported = 1), KDA_ERR_UNSUPPORTED (result->supported = 0;
+ * the version, peaks and, with KDA_QUERY_DEVICE, the device fields are still filled) or
+ * KDA_ERR_INVALID_ARGUMENT (NULL result or an invalid problem).
  */
 kda_status_t kda_query(const kda_problem_t *problem, uint32_t flags, kda_query_result_t *result);
 

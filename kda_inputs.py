@@ -166,6 +166,40 @@ def workload_inputs(name: str, *, seed: Optional[int] = None) -> Inputs:
     return make_inputs(w.B, w.T, w.H, w.dk, w.dv, w.io, s, g_mu=w.g_mu, s0_std=w.s0_std)
 
 
+def workload_inputs_on(name: str, device, *, seed: Optional[int] = None) -> Inputs:
+    """One named workload drawn on `device` by a generator of that device: the recipe, shapes and
+    draw order of ``workload_inputs`` (a packed workload's lengths still come from the CPU
+    generator, so they are the same lengths), but different random values.  Used to time the
+    full-size workloads without drawing several GB on the host."""
+    w = WORKLOADS[name]
+    s = w.seed if seed is None else seed
+    lengths = None
+    if w.varlen_seqs:
+        lengths = varlen_lengths(w.varlen_seqs, w.varlen_max, torch.Generator("cpu").manual_seed(s))
+    gen = torch.Generator(device).manual_seed(s)
+    B, T = (1, int(sum(lengths))) if lengths is not None else (w.B, 1 if w.decode else w.T)
+    n = len(lengths) if lengths is not None else B
+    dt = _io_dtype(w.io)
+    rn = lambda *shape: torch.randn(*shape, generator=gen, device=device)
+    q = _unit_rows(rn(B, T, w.H, w.dk)).to(dt)
+    k = _unit_rows(rn(B, T, w.H, w.dk)).to(dt)
+    v = rn(B, T, w.H, w.dv).to(dt)
+    g = rn(B, T, w.H, w.dk).add_(w.g_mu)
+    g = -torch.nn.functional.softplus(g)
+    beta = torch.sigmoid(rn(B, T, w.H))
+    s0 = None if w.s0_std is None else w.s0_std * rn(n, w.H, w.dk, w.dv)
+    cu = None
+    if lengths is not None:
+        cu = torch.zeros(len(lengths) + 1, dtype=torch.int32)
+        cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
+        cu = cu.to(device)
+    inp = Inputs(q=q, k=k, v=v, g=g.contiguous(), beta=beta.contiguous(), s0=s0, cu_seqlens=cu, io=w.io,
+                 meta=dict(seed=s, g_mu=w.g_mu, s0_std=w.s0_std, device=str(device)))
+    if lengths is not None:
+        inp.meta["lengths"] = lengths
+    return inp
+
+
 def to_numpy_io(x: torch.Tensor) -> np.ndarray:
     """CPU tensor -> numpy: fp32 stays float32, bf16 becomes its raw uint16 bit pattern."""
     x = x.contiguous()
