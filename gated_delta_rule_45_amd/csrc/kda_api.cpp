@@ -244,7 +244,7 @@ struct BwdResolved {
                             // scan tiles) when compiled for the problem, else fused
     int fwd_dv_tile = 32;   // fused: d_v tile
     int64_t slots = 0;      // chunk slots (upper bound for a packed batch)
-    size_t off_hs = 0, off_dhs = 0, off_dch = 0, off_duch = 0, off_brec = 0, ws_bytes = 0;
+    size_t off_hs = 0, off_dhs = 0, off_dch = 0, off_duch = 0, off_brec = 0, off_flag = 0, ws_bytes = 0;
 };
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -293,7 +293,7 @@ kda_status_t resolve_bwd(const kda_problem_t *p, bool varlen, BwdResolved &b) {
     const size_t s_io = p->io_dtype == KDA_BF16 ? 2 : 4;
     const size_t states = align256((size_t)b.slots * p->num_heads * dk * dv * s_io);  // operand type
     const size_t tiles = align256((size_t)b.slots * p->num_heads * b.chunk * dv * s_io);
-    // [chunk offsets][two-pass records (when two-pass)][states][state gradients][D][dU]
+    // [chunk offsets][two-pass records (when two-pass)][states][state gradients][D][dU][records][flags]
     b.off_hs = b.two_pass ? align256(kda::split_workspace_bytes(p->io_dtype, dk, b.chunk, b.slots, p->num_heads,
                                                                 b.r.num_seqs))
                           : kda::split_plan_bytes(b.r.num_seqs);
@@ -303,7 +303,8 @@ kda_status_t resolve_bwd(const kda_problem_t *p, bool varlen, BwdResolved &b) {
     b.off_brec = b.off_duch + tiles;
     const size_t rec = p->io_dtype == KDA_BF16 ? kda::bwd_record_bytes_bf16(dk, b.chunk)
                                                : kda::bwd_record_bytes_f32(dk, b.chunk);
-    b.ws_bytes = b.off_brec + align256((size_t)b.slots * p->num_heads * rec);
+    b.off_flag = b.off_brec + align256((size_t)b.slots * p->num_heads * rec);
+    b.ws_bytes = b.off_flag + align256((size_t)b.slots * p->num_heads * sizeof(int32_t));
     return KDA_OK;
 }
 
@@ -475,6 +476,7 @@ kda_status_t kda_chunk_bwd(const kda_problem_t *problem, const void *q, const vo
         bp.dch = fp.dch;
         bp.duch = ws + b.off_duch;
         bp.brec = ws + b.off_brec;
+        bp.split_flag = reinterpret_cast<int32_t *>(ws + b.off_flag);
         bp.slots = b.slots;
         const hipError_t e = problem->io_dtype == KDA_BF16 ? kda::launch_bwd_bf16(bp, b.chunk, s)
                                                            : kda::launch_bwd_f32(bp, b.chunk, s);

@@ -201,6 +201,81 @@ __device__ __forceinline__ Frag<BF> bwd_turn(const Frag<BF> &a, const Frag<BF> &
     return frag_from_acc<BF>(t);
 }
 
+// Diagonal-block terms of one sub-chunk for the gradient kernel, exact under any decay: the split
+// levels of kda_device.h (split_anchor), here in products that contract over the tokens.  The lane
+// holds token l16 of the sub-chunk and channels 4*q4 + j of its wave's 16: raw k and q (kk, qq) and
+// the in-sub-chunk cumulative log2 gate G.  P, A (rows r) and PT, LT (rows i) point at the
+// sub-chunk's diagonal 16 x 16 tiles of dP, dA, dP^T and dL^T (row stride LDC):
+//   ROW: rowP[j] += sum_{i <= r} k_i dP_ri e^{G_r - G_i},  rowA[j] += sum_{i < r} k_i dA_ri e^{G_r - G_i}
+//        (r the lane's token)
+//   COL: col[j]  += sum_{r >= i} (q_r dP_ri + k_r dL_ri) e^{G_r - G_i}  (i the lane's token)
+// Per level, the tiles are masked to the pairs with both tokens in one block, the row-side token in
+// its second half and the column-side token in its first half, and the token operands carry
+// e^{-|G - a|} <= 1 (a the level's anchor); the diagonal pairs (factor 1) are added apart.
+template <bool BF, bool ROW, bool COL, typename OT>
+__device__ __forceinline__ void grad_diag_split(f32x4 &rowP, f32x4 &rowA, f32x4 &col, const float (&kk)[4],
+                                                const float (&qq)[4], const float (&G)[4], const OT *P, const OT *A,
+                                                const OT *PT, const OT *LT, int LDC, const Frag<BF> &eye, int l16,
+                                                int q4, int lane) {
+    // the level loop stays rolled (anchors by lane shuffle): the common path of this kernel uses
+    // every register, and an unrolled rare path would add code and temporaries to it
+#pragma unroll 1
+    for (int lvl = 0; lvl < 4; ++lvl) {
+        const int hs = 8 >> lvl;
+        const int src = (lane & ~15) | ((l16 & ~(2 * hs - 1)) + hs - 1);  // the level's anchor token
+        float f[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f[j] = fast_exp2(-fabsf(G[j] - __shfl(G[j], src)));
+        // B fragment of tokens x = 4*q4 + j (contracted) against the lane's token l16: keep x where
+        // both lie in one block and the lane's token is in the half `lane_second`, x in the other
+        auto masked = [&](const OT *t, bool lane_second) {
+            const float4 v = unpack4<BF>(lds_frag(t + l16 * LDC + 4 * q4).v);
+            const float x[4] = {v.x, v.y, v.z, v.w};
+            float o[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int tx = 4 * q4 + j;
+                const bool same = (tx >> (4 - lvl)) == (l16 >> (4 - lvl));
+                const bool lane_sec = (l16 & hs) != 0, x_sec = (tx & hs) != 0;
+                o[j] = (same && lane_sec == lane_second && x_sec != lane_second) ? x[j] : 0.f;
+            }
+            return make_frag<BF>(o[0], o[1], o[2], o[3]);
+        };
+        const Frag<BF> kT = bwd_turn<BF>(make_frag<BF>(kk[0] * f[0], kk[1] * f[1], kk[2] * f[2], kk[3] * f[3]), eye);
+        if constexpr (ROW) {
+            f32x4 tp = zero4(), ta = zero4();
+            mma16(tp, kT, masked(P, true));
+            mma16(ta, kT, masked(A, true));
+            mfma_settle(tp, ta);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                rowP[j] += f[j] * tp[j];
+                rowA[j] += f[j] * ta[j];
+            }
+        }
+        if constexpr (COL) {
+            const Frag<BF> qT =
+                bwd_turn<BF>(make_frag<BF>(qq[0] * f[0], qq[1] * f[1], qq[2] * f[2], qq[3] * f[3]), eye);
+            f32x4 tc = zero4();
+            mma16(tc, qT, masked(PT, false));
+            mma16(tc, kT, masked(LT, false));
+            mfma_settle(tc);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) col[j] += f[j] * tc[j];
+        }
+    }
+    // diagonal pairs: dP_rr (dA and dL are strictly lower)
+    OT d = P[l16 * LDC + l16];
+    float dpp;
+    if constexpr (BF) dpp = bf16_to_f32(d);
+    else dpp = d;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if constexpr (ROW) rowP[j] += kk[j] * dpp;
+        if constexpr (COL) col[j] += qq[j] * dpp;
+    }
+}
+
 template <typename IO, int DK, int C>
 __global__ void __launch_bounds__(kChunkThreads) kda_bwd_prep_kernel(BwdParams bp, char *__restrict__ records) {
     using L = BwdPrepLayout<IO, DK, C>;
@@ -250,6 +325,7 @@ __global__ void __launch_bounds__(kChunkThreads) kda_bwd_prep_kernel(BwdParams b
     // (k and q stay packed in the raw registers; phases 3 and 4 unpack them where used)
     float G[KT][4];
     const bool valid = 16 * wave + l16 < clen;
+    bool split = false;  // the sub-chunk decays too strongly for a single-anchor diagonal block
     if (wave < NSUB) {
         const int R = wave;
 #pragma unroll
@@ -264,9 +340,13 @@ __global__ void __launch_bounds__(kChunkThreads) kda_bwd_prep_kernel(BwdParams b
             if (l16 == 15)
                 *reinterpret_cast<float4 *>(sTot + R * DK + c) = make_float4(G[ct][0], G[ct][1], G[ct][2], G[ct][3]);
         }
+        split = diag_needs_split<KT>(G);
     }
     if (tid < C) sBeta[tid] = tid < clen ? raw.beta : 0.f;
-    __syncthreads();
+    // the gradient kernel handles this chunk in its split-capable instantiation when any sub-chunk
+    // needs the split levels
+    const int any_split = __syncthreads_or(split ? 1 : 0);
+    if (tid == 0) bp.split_flag[slot * H + h] = any_split;
 
     // ================= 2: per-channel boundary factors
     if (tid < DK) {
@@ -397,17 +477,35 @@ __global__ void __launch_bounds__(kChunkThreads) kda_bwd_prep_kernel(BwdParams b
                 mma32(accP, qa0, qa1, b0, b1);
             }
             // accumulator: rows rr = 4*q4 + j of block R, column ii = l16 of block I
+            if (I == R && split) {
+                // Decay beyond 2^-96 inside the sub-chunk: the diagonal block from the split levels
+                // (all factors <= 1), operands reloaded; this wave's product above is discarded.
+                const int64_t tok0 = start + (int64_t)ci * C;
+                const int64_t row = ((tok0 + min(16 * R + l16, clen - 1)) * H + h) * (int64_t)DK + 4 * q4;
+                f32x4 dA, dPt;
+                diag_block_split_rolled<IO>(dA, dPt, static_cast<const IO *>(p.k) + row,
+                                            static_cast<const IO *>(p.q) + row, p.g + row, valid, KT, l16, q4, lane);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int rr = 4 * q4 + j, ii = l16;
-                float av = accA[j] * sBeta[16 * R + rr], pv = accP[j];
-                if (I == R) {
-                    if (ii >= rr) av = 0.f;
-                    if (ii > rr) pv = 0.f;
+                for (int j = 0; j < 4; ++j) {
+                    const int rr = 4 * q4 + j;
+                    sX[(16 * R + rr) * LDX + 16 * R + l16] = l16 < rr ? dA[j] * sBeta[16 * R + rr] : 0.f;
+                    // dPt holds P_RR[l16][4 q4 + j]
+                    if constexpr (BF) sP[(16 * R + l16) * LDM + 16 * R + rr] = f32_to_bf16(dPt[j]);
+                    else sP[(16 * R + l16) * LDM + 16 * R + rr] = dPt[j];
                 }
-                sX[(16 * R + rr) * LDX + 16 * I + ii] = av;
-                if constexpr (BF) sP[(16 * R + rr) * LDM + 16 * I + ii] = f32_to_bf16(pv);
-                else sP[(16 * R + rr) * LDM + 16 * I + ii] = pv;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int rr = 4 * q4 + j, ii = l16;
+                    float av = accA[j] * sBeta[16 * R + rr], pv = accP[j];
+                    if (I == R) {
+                        if (ii >= rr) av = 0.f;
+                        if (ii > rr) pv = 0.f;
+                    }
+                    sX[(16 * R + rr) * LDX + 16 * I + ii] = av;
+                    if constexpr (BF) sP[(16 * R + rr) * LDM + 16 * I + ii] = f32_to_bf16(pv);
+                    else sP[(16 * R + rr) * LDM + 16 * I + ii] = pv;
+                }
             }
         }
     }
@@ -841,7 +939,10 @@ struct BwdGradLayout {
 };
 
 
-template <typename IO, int DK, int DV, int C>
+// SPLIT: this instantiation takes the chunks kda_bwd_prep_kernel flagged (some sub-chunk decays beyond
+// the single-anchor limit of the diagonal blocks) and forms their diagonal-block terms from the split
+// levels; the other instantiation takes every other chunk with no trace of that path in its code.
+template <typename IO, int DK, int DV, int C, bool SPLIT>
 __global__ void __launch_bounds__(64 * (DK / 16)) kda_bwd_grad_kernel(BwdParams bp) {
     using L = BwdGradLayout<IO, DK, DV, C>;
     using OT = typename L::OT;
@@ -872,6 +973,7 @@ __global__ void __launch_bounds__(64 * (DK / 16)) kda_bwd_grad_kernel(BwdParams 
     const int h = (int)(blockIdx.x % H);
     int n, ci;
     if (!bwd_slot_chunk(p, C, slot, n, ci)) return;
+    if ((bp.split_flag[slot * H + h] != 0) != SPLIT) return;  // the other instantiation's chunk
     const int64_t start = p.cu ? (int64_t)p.cu[n] : (int64_t)n * p.T;
     const int len = p.cu ? p.cu[n + 1] - p.cu[n] : p.T;
     const int clen = min(C, len - ci * C);
@@ -899,6 +1001,16 @@ __global__ void __launch_bounds__(64 * (DK / 16)) kda_bwd_grad_kernel(BwdParams 
         G[R][3] = scan16_add(gv.w * m);
         kraw[R] = valid ? kv : KQ{};
         qraw[R] = valid ? qv : KQ{};
+    }
+    // sub-chunks whose decay (in this wave's channels) is too strong for the single-anchor split of
+    // the diagonal blocks
+    bool split[NSUB];
+#pragma unroll
+    for (int R = 0; R < NSUB; ++R) {
+        bool big = false;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) big |= G[R][j] < -kDiagAnchorMaxDecay;
+        split[R] = SPLIT && __builtin_amdgcn_ballot_w64(big) != 0;
     }
     auto unpk = [](const KQ &x, float (&o)[4]) {
         const float4 v = unpack4<BF>(x);
@@ -1042,6 +1154,7 @@ __global__ void __launch_bounds__(64 * (DK / 16)) kda_bwd_grad_kernel(BwdParams 
         for (int j = 0; j < 4; ++j) kb[j] = kk[j] * fast_exp2(bnd[R + 1][j] - bnd[R][j] - G[R][j]);  // k e^{b_{R+1} - G}
         f32x4 t = zero4();
         mma16(t, make_frag<BF>(kb[0], kb[1], kb[2], kb[3]), eye);
+        if constexpr (SPLIT) mfma_settle(t);  // the split path's branches put joins before some reads
         kbT[R] = frag_from_acc<BF>(t);
     }
 
@@ -1063,9 +1176,11 @@ __global__ void __launch_bounds__(64 * (DK / 16)) kda_bwd_grad_kernel(BwdParams 
             }
             f32x4 t = zero4();
             mma16(t, make_frag<BF>(kr[0], kr[1], kr[2], kr[3]), eye);
+            if constexpr (SPLIT) mfma_settle(t);
             krT[R] = frag_from_acc<BF>(t);
             t = zero4();
             mma16(t, make_frag<BF>(qr[0], qr[1], qr[2], qr[3]), eye);
+            if constexpr (SPLIT) mfma_settle(t);
             qrT[R] = frag_from_acc<BF>(t);
         }
         f32x4 Col[NSUB];
@@ -1075,6 +1190,7 @@ __global__ void __launch_bounds__(64 * (DK / 16)) kda_bwd_grad_kernel(BwdParams 
         for (int R = 0; R < NSUB; ++R) {
 #pragma unroll
             for (int I = 0; I <= R; ++I) {
+                if (I == R && split[R]) continue;  // the diagonal block comes from the split levels below
                 f32x4 tc = zero4();
                 mma16(tc, qrT[R], lds_frag(sPT + (16 * I + l16) * LDC + 16 * R + 4 * q4));
                 mma16(tc, krT[R], lds_frag(sLT + (16 * I + l16) * LDC + 16 * R + 4 * q4));
@@ -1086,11 +1202,20 @@ __global__ void __launch_bounds__(64 * (DK / 16)) kda_bwd_grad_kernel(BwdParams 
         for (int R = 0; R < NSUB; ++R) {
             float kk[4];
             unpk(kraw[R], kk);
+            f32x4 colD = zero4();  // diagonal-block part with its whole factor (split sub-chunks)
+            if (split[R]) {
+                float qq[4];
+                unpk(qraw[R], qq);
+                f32x4 unused = zero4();
+                grad_diag_split<BF, false, true>(unused, unused, colD, kk, qq, G[R], sP + 16 * R * LDC + 16 * R,
+                                                 sA + 16 * R * LDC + 16 * R, sPT + 16 * R * LDC + 16 * R,
+                                                 sLT + 16 * R * LDC + 16 * R, LDC, eye, l16, q4, lane);
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const float fb = fast_exp2(bnd[R + 1][j] - bnd[R][j] - G[R][j]);
                 const float ekb = fast_exp2(bnd[NSUB][j] - bnd[R][j] - G[R][j]);
-                const float dk2 = fb * Col[R][j];
+                const float dk2 = fb * Col[R][j] + colD[j];
                 const float dk3 = ekb * Zs[R][j];
                 dkc[R][j] = dk2 + dk3;
                 dG[R][j] = -kk[j] * (dk2 + dk3);
@@ -1116,9 +1241,19 @@ __global__ void __launch_bounds__(64 * (DK / 16)) kda_bwd_grad_kernel(BwdParams 
                 mma32(Zu, sf[kt], sf[kt + 1], lds_frag(bu + 16 * kt), lds_frag(bu + 16 * kt + 16));
             }
         }
-        f32x4 RowP = zero4(), RowA = zero4();
+        f32x4 RowP = zero4(), RowA = zero4(), RowPD = zero4(), RowAD = zero4();
+        if (split[R]) {  // diagonal-block part with its whole factor
+            float kk[4], qq[4];
+            unpk(kraw[R], kk);
+            unpk(qraw[R], qq);
+            f32x4 unused = zero4();
+            grad_diag_split<BF, true, false>(RowPD, RowAD, unused, kk, qq, G[R], sP + 16 * R * LDC + 16 * R,
+                                             sA + 16 * R * LDC + 16 * R, sPT + 16 * R * LDC + 16 * R,
+                                             sLT + 16 * R * LDC + 16 * R, LDC, eye, l16, q4, lane);
+        }
 #pragma unroll
         for (int I = 0; I <= R; ++I) {
+            if (I == R && split[R]) continue;
             f32x4 tp = zero4(), ta = zero4();
             mma16(tp, kbT[I], lds_frag(sP + (16 * R + l16) * LDC + 16 * I + 4 * q4));
             mma16(ta, kbT[I], lds_frag(sA + (16 * R + l16) * LDC + 16 * I + 4 * q4));
@@ -1139,8 +1274,8 @@ __global__ void __launch_bounds__(64 * (DK / 16)) kda_bwd_grad_kernel(BwdParams 
         for (int j = 0; j < 4; ++j) {
             const float fr = fast_exp2(G[R][j]);
             const float eG = fast_exp2(bnd[R][j] + G[R][j]);
-            const float W = fr * RowA[j];
-            const float dq = p.scale * eG * Zq[j] + fr * RowP[j];
+            const float W = fr * RowA[j] + RowAD[j];
+            const float dq = p.scale * eG * Zq[j] + fr * RowP[j] + RowPD[j];
             const float dk1 = b * (W - eG * Zu[j]);
             dq4[j] = dq;
             dk4[j] = dk1 + dkc[R][j];
@@ -1231,7 +1366,12 @@ hipError_t launch_bwd_variant(const BwdParams &bp, hipStream_t stream) {
         }
         const int64_t grad_blocks = bp.slots * p.H;
         if (grad_blocks > 0) {
-            hipLaunchKernelGGL((kda_bwd_grad_kernel<IO, DK, DV, C>), dim3((unsigned)grad_blocks),
+            hipLaunchKernelGGL((kda_bwd_grad_kernel<IO, DK, DV, C, false>), dim3((unsigned)grad_blocks),
+                               dim3(BwdGradLayout<IO, DK, DV, C>::NT), 0, stream, bp);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            // chunks with strong decay (flagged by the prep kernel); the other workgroups exit at once
+            hipLaunchKernelGGL((kda_bwd_grad_kernel<IO, DK, DV, C, true>), dim3((unsigned)grad_blocks),
                                dim3(BwdGradLayout<IO, DK, DV, C>::NT), 0, stream, bp);
             return hipGetLastError();
         }

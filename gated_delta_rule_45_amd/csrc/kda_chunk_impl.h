@@ -148,8 +148,13 @@ __device__ __forceinline__ void load_chunk(ChunkRaw<IO, DK, DVT, C> &raw, const 
     if (tid < C) raw.beta = p.beta[(tok0 + min(tid, clen - 1)) * H + h];
 }
 
+// bf16 at d_k = 64 with chunk 16 fits two workgroups' registers per CU without spilling; the other
+// shapes take every register of one.
+template <typename IO, int DK, int C>
+constexpr int fused_min_waves() { return IoTraits<IO>::kBf16 && DK == 64 && C == 16 ? 2 : 1; }
+
 template <typename IO, int DK, int DVT, int C>
-__global__ void __launch_bounds__(kChunkThreads) kda_chunk_fwd_kernel(FwdParams p) {
+__global__ void __launch_bounds__(kChunkThreads, (fused_min_waves<IO, DK, C>())) kda_chunk_fwd_kernel(FwdParams p) {
     using L = ChunkLayout<IO, DK, DVT, C>;
     using OT = typename L::OT;
     constexpr bool BF = L::BF;
@@ -240,6 +245,7 @@ __global__ void __launch_bounds__(kChunkThreads) kda_chunk_fwd_kernel(FwdParams 
         // (k and q stay packed in the raw registers; phases 3 and 4 unpack them where used)
         float G[KT][4];
         const bool valid = 16 * wave + l16 < clen;
+        bool split = false;  // the sub-chunk decays too strongly for a single-anchor diagonal block
         if (wave < NSUB) {
             const int R = wave;
 #pragma unroll
@@ -254,6 +260,7 @@ __global__ void __launch_bounds__(kChunkThreads) kda_chunk_fwd_kernel(FwdParams 
                 if (l16 == 15)
                     *reinterpret_cast<float4 *>(sTot + R * DK + c) = make_float4(G[ct][0], G[ct][1], G[ct][2], G[ct][3]);
             }
+            split = diag_needs_split<KT>(G);
         }
         {
             constexpr int PPR = DVT / L::V_ELEMS;
@@ -293,6 +300,25 @@ __global__ void __launch_bounds__(kChunkThreads) kda_chunk_fwd_kernel(FwdParams 
             sGam[c] = fast_exp2(gc);
         }
         __syncthreads();
+
+        // Decay beyond 2^-96 inside the sub-chunk: A_RR and P_RR from the split levels (all factors
+        // <= 1), written to their LDS places here (phase 4 writes only the other blocks of these rows)
+        if (split) {
+            const int R = wave;
+            const int64_t row = ((tok0 + min(16 * R + l16, clen - 1)) * H + h) * (int64_t)DK + 4 * q4;
+            f32x4 dA, dPt;
+            diag_block_split_rolled<IO>(dA, dPt, static_cast<const IO *>(p.k) + row, static_cast<const IO *>(p.q) + row,
+                                        p.g + row, valid, KT, l16, q4, lane);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int rr = 4 * q4 + j;
+                const float b = 16 * R + rr < clen ? p.beta[(tok0 + 16 * R + rr) * H + h] : 0.f;
+                sAd[(R * 16 + rr) * LDD + l16] = l16 < rr ? dA[j] * b : 0.f;
+                // dPt holds P_RR[l16][4 q4 + j]
+                if constexpr (BF) sP[(16 * R + l16) * LDM + 16 * R + rr] = f32_to_bf16(dPt[j]);
+                else sP[(16 * R + l16) * LDM + 16 * R + rr] = dPt[j];
+            }
+        }
 
         // ================= 3: gated operands of sub-chunk R
         Frag<BF> kdiag[KT];  // k * e^{b_R - G} (>= 1): column operand of the diagonal block
@@ -390,17 +416,20 @@ __global__ void __launch_bounds__(kChunkThreads) kda_chunk_fwd_kernel(FwdParams 
                         if (ii > rr) pv[j] = 0.f;
                     }
                 }
+                // with `split` the diagonal block was written in phase 1 (this product is discarded)
+                if (!(I == R && split)) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int rr = 4 * q4 + j;
-                    if constexpr (BF) {
-                        sP[(16 * R + rr) * LDM + 16 * I + l16] = f32_to_bf16(pv[j]);
-                        if (I != R) sA[(16 * R + rr) * LDM + 16 * I + l16] = f32_to_bf16(av[j]);
-                    } else {
-                        sP[(16 * R + rr) * LDM + 16 * I + l16] = pv[j];
-                        if (I != R) sA[(16 * R + rr) * LDM + 16 * I + l16] = av[j];
+                    for (int j = 0; j < 4; ++j) {
+                        const int rr = 4 * q4 + j;
+                        if constexpr (BF) {
+                            sP[(16 * R + rr) * LDM + 16 * I + l16] = f32_to_bf16(pv[j]);
+                            if (I != R) sA[(16 * R + rr) * LDM + 16 * I + l16] = f32_to_bf16(av[j]);
+                        } else {
+                            sP[(16 * R + rr) * LDM + 16 * I + l16] = pv[j];
+                            if (I != R) sA[(16 * R + rr) * LDM + 16 * I + l16] = av[j];
+                        }
+                        if (I == R) sAd[(R * 16 + rr) * LDD + l16] = av[j];
                     }
-                    if (I == R) sAd[(R * 16 + rr) * LDD + l16] = av[j];
                 }
             }
             // X_RR = (I + A_RR)^{-1}, row by row: lane l16 owns column l16 (same wave wrote A_RR)

@@ -60,6 +60,59 @@ __device__ __forceinline__ float scan16_add(float x) {
     return x;
 }
 
+// ------------------------------------------ diagonal blocks under strong decay --
+// Inside one 16-token sub-chunk the gated products need e^{G_r - G_i} (i <= r) per channel.  With
+// one anchor per sub-chunk one factor of that split grows like e^{-(total decay)} and overflows
+// once a channel decays by more than about e^{-88} within 16 tokens.  The exact alternative used
+// there splits the 16 tokens in halves, quarters, eighths and pairs: tokens r > i lie in the same
+// block but in different halves at exactly one of these four levels, and at that level the anchor
+// a = G at the last token of the first half gives e^{G_r - G_i} = e^{G_r - a} e^{a - G_i} with both
+// factors <= 1.  Per level, the row operand keeps only second-half tokens and the column operand
+// only first-half tokens, so every product pairs tokens split at that level and the four level
+// products sum to the strictly lower part of the block (the diagonal, factor 1, is added apart).
+
+// True when the lane's token (l16, in its row of 16 lanes) lies in the second half of its block at
+// level LVL (block sizes 16, 8, 4, 2 for LVL 0..3).
+template <int LVL>
+__device__ __forceinline__ bool split_second(int l16) {
+    return (l16 >> (3 - LVL)) & 1;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// G at the anchor token of the lane's block at level LVL: the last token of the block's first half
+// (tokens 7 | 3, 11 | 1, 5, 9, 13 | 0, 2, ..., 14), gathered within each row of 16 lanes by DPP
+// (quad_perm 0xA0 = [0,0,2,2], 0x55 = [1,1,1,1], 0xFF = [3,3,3,3]; row_half_mirror 0x141 takes
+// lane 7 - x of each half row, row_mirror 0x140 lane 15 - x of the row).
+template <int LVL>
+__device__ __forceinline__ float split_anchor(float G, int l16) {
+    if constexpr (LVL == 3) {
+        return dpp_mov<0xA0>(G);
+    } else if constexpr (LVL == 2) {
+        return dpp_mov<0x55>(G);
+    } else {
+        const float t = dpp_mov<0xFF>(G);        // quad q: G of token 4q + 3
+        const float u = dpp_mov<0x141>(t);       // lane x: t of lane 7 - x in its half row
+        if constexpr (LVL == 1) {
+            return (l16 & 4) ? u : t;            // tokens 3 (lanes 0-7) and 11 (lanes 8-15)
+        } else {
+            const float v = (l16 & 4) ? t : u;   // lanes 0-7: token 7
+            const float w = dpp_mov<0x140>(v);   // lanes 8-15: lane 15 - x, i.e. lanes 7-0
+            return (l16 & 8) ? w : v;
+        }
+    }
+}
+
+// Factor of a token at level LVL: e^{G - a} for a second-half token, e^{a - G} for a first-half one
+// (both <= 1 since the cumulative log-gate G does not increase along the tokens).
+template <int LVL>
+__device__ __forceinline__ float split_factor(float G, int l16) {
+    return __builtin_amdgcn_exp2f(-fabsf(G - split_anchor<LVL>(G, l16)));
+}
+
 // ---------------------------------------------------------------- fragments --
 // One lane's share of one 16-wide k tile: 4 values, as packed bf16 or fp32.
 template <bool BF16>
@@ -141,6 +194,20 @@ __device__ __forceinline__ void mma32(f32x4 &acc, const Frag<false> &a0, const F
     mma16(acc, a1, b1);
 }
 
+// Wait states between matrix-core products and reads of their results that may sit in another basic
+// block.  A VALU read (or v_accvgpr_read) of an MFMA result needs 11 wait states after an 8-pass
+// instruction (16x16x32 bf16, 16x16x4 f32 on gfx950) and 19 after a 16-pass one.  The compiler
+// inserts them within a block, but across a join was seen to leave none: the last product of a chain
+// ended its block, a branch led to a block reached also from a path that did have the wait states,
+// and the first instruction there read the accumulator's stale value (wrong results, no fault).
+// The accumulators pass through this asm as operands, so it sits after their last product and before
+// every read, and its three s_nop 7 give 24 wait states.  Used where a chain's results are consumed
+// after a branch or a loop exit.
+__device__ __forceinline__ void mfma_settle(f32x4 &a) { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a)); }
+__device__ __forceinline__ void mfma_settle(f32x4 &a, f32x4 &b) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b));
+}
+
 __device__ __forceinline__ f32x4 zero4() {
     f32x4 z = {0.f, 0.f, 0.f, 0.f};
     return z;
@@ -187,6 +254,163 @@ __device__ __forceinline__ void keep_rows(OT *dst, int64_t ld, const float *tile
         }
     }
     wave_lds_sync();
+}
+
+template <typename IO>
+struct IoTraits;  // fp32 / bf16 io element access, below
+
+// ------------------------------------------------- split-level diagonal blocks --
+// A wave's own 16 x 16 diagonal block of the chunk matrices for one sub-chunk, exact under any
+// decay: per split level (see split_anchor), row operands keep the second-half tokens scaled by
+// e^{G - a} and column operands the first-half tokens scaled by e^{a - G}, all factors <= 1.  A
+// level's product also pairs tokens of different blocks (with each other's anchors, so still
+// bounded by 1); those entries are dropped before the level is added.
+//   accA [j] = sum_c k_rc k_ic e^{G_rc - G_ic}   for r = 4*q4 + j, i = l16, i < r (else 0)
+//   accPt[j] = sum_c q_rc k_ic e^{G_rc - G_ic}   for r = l16, i = 4*q4 + j, i <= r (else 0)
+// i.e. the accumulator layouts of the strictly lower part of K K^T and of the transpose of the
+// lower part (with diagonal) of Q K^T, before beta.  kqg(ct, k, q, G) gives the lane's raw k and q
+// for channels 16 ct + 4 q4 .. + 3 of its token (zero past the chunk end) and the in-sub-chunk
+// cumulative log2 gate G of the same channels; it is called once per channel tile.
+template <bool BF, int LVL, int KT, bool WA, bool WP, typename KQG>
+__device__ __forceinline__ void split_level_add(f32x4 &accA, f32x4 &accPt, const KQG &kqg, int l16, int q4) {
+    const bool sec = split_second<LVL>(l16);
+    f32x4 tA = zero4(), tPt = zero4();
+    // one 16-channel tile per product keeps few operands live at a time (a rare path)
+#pragma unroll
+    for (int ct = 0; ct < KT; ++ct) {
+        float4 kv, qv, gv;
+        kqg(ct, kv, qv, gv);
+        const float kx[4] = {kv.x, kv.y, kv.z, kv.w}, qx[4] = {qv.x, qv.y, qv.z, qv.w};
+        const float gx[4] = {gv.x, gv.y, gv.z, gv.w};
+        float a[4], b[4], c[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float f = split_factor<LVL>(gx[j], l16);
+            a[j] = sec ? kx[j] * f : 0.f;
+            b[j] = sec ? qx[j] * f : 0.f;
+            c[j] = sec ? 0.f : kx[j] * f;
+        }
+        const Frag<BF> ck = make_frag<BF>(c[0], c[1], c[2], c[3]);
+        if constexpr (WA) mma16(tA, make_frag<BF>(a[0], a[1], a[2], a[3]), ck);
+        if constexpr (WP) mma16(tPt, ck, make_frag<BF>(b[0], b[1], b[2], b[3]));
+    }
+    mfma_settle(tA, tPt);
+    // keep the pairs of tokens in the same block of 16 >> LVL (an entry's two token indices are
+    // 4*q4 + j and l16 in both layouts)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const bool same = ((4 * q4 + j) >> (4 - LVL)) == (l16 >> (4 - LVL));
+        if constexpr (WA) accA[j] += same ? tA[j] : 0.f;
+        if constexpr (WP) accPt[j] += same ? tPt[j] : 0.f;
+    }
+}
+
+// WA / WP select the blocks to form (both by default; one at a time where registers are short).
+template <bool BF, int KT, typename KQG, bool WA = true, bool WP = true>
+__device__ __forceinline__ void diag_block_split(f32x4 &accA, f32x4 &accPt, const KQG &kqg, int l16, int q4) {
+    accA = zero4();
+    accPt = zero4();
+    split_level_add<BF, 0, KT, WA, WP>(accA, accPt, kqg, l16, q4);
+    split_level_add<BF, 1, KT, WA, WP>(accA, accPt, kqg, l16, q4);
+    split_level_add<BF, 2, KT, WA, WP>(accA, accPt, kqg, l16, q4);
+    split_level_add<BF, 3, KT, WA, WP>(accA, accPt, kqg, l16, q4);
+    if constexpr (WP) {
+        float dot = 0.f;  // q_r . k_r of the lane's token over its channels (the diagonal, factor 1)
+#pragma unroll
+        for (int ct = 0; ct < KT; ++ct) {
+            float4 kv, qv, gv;
+            kqg(ct, kv, qv, gv);
+            dot += kv.x * qv.x + kv.y * qv.y + kv.z * qv.z + kv.w * qv.w;
+        }
+        // the four lanes of a token (q4 = 0..3) hold disjoint channels
+        dot += __shfl_xor(dot, 16);
+        dot += __shfl_xor(dot, 32);
+        if (q4 == (l16 >> 2)) {  // P_RR[r][r] sits at r = l16, i = 4*q4 + j with j = l16 % 4
+            const int jd = l16 & 3;
+            accPt[0] += jd == 0 ? dot : 0.f;
+            accPt[1] += jd == 1 ? dot : 0.f;
+            accPt[2] += jd == 2 ? dot : 0.f;
+            accPt[3] += jd == 3 ? dot : 0.f;
+        }
+    }
+}
+
+// The same blocks with every loop rolled and the operands reloaded from memory: a few hundred
+// instructions and few live registers, for kernels whose common path already uses every register
+// (there the unrolled form's code and temporaries slow the common path down).  k, q and g point at
+// the lane's token row (channels 4*q4 ...: tile ct at + 16 ct), valid is false past the chunk end.
+template <typename IO>
+__device__ __forceinline__ void diag_block_split_rolled(f32x4 &accA, f32x4 &accPt, const IO *k, const IO *q,
+                                                        const float *g, bool valid, int KT, int l16, int q4,
+                                                        int lane) {
+    constexpr bool BF = IoTraits<IO>::kBf16;
+    accA = zero4();
+    accPt = zero4();
+    float dot = 0.f;
+#pragma unroll 1
+    for (int lvl = 0; lvl < 4; ++lvl) {
+        const int hs = 8 >> lvl;
+        const bool sec = (l16 & hs) != 0;
+        const int src = (lane & ~15) | ((l16 & ~(2 * hs - 1)) + hs - 1);  // the level's anchor token
+        f32x4 tA = zero4(), tPt = zero4();
+#pragma unroll 1
+        for (int ct = 0; ct < KT; ++ct) {
+            const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+            const float4 kv = valid ? IoTraits<IO>::load4(k + 16 * ct) : z;
+            const float4 qv = valid ? IoTraits<IO>::load4(q + 16 * ct) : z;
+            const float4 gr = *reinterpret_cast<const float4 *>(g + 16 * ct);
+            const float m = valid ? kLog2e : 0.f;
+            const float G[4] = {scan16_add(gr.x * m), scan16_add(gr.y * m), scan16_add(gr.z * m),
+                                scan16_add(gr.w * m)};
+            const float kx[4] = {kv.x, kv.y, kv.z, kv.w}, qx[4] = {qv.x, qv.y, qv.z, qv.w};
+            float a[4], b[4], c[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float f = __builtin_amdgcn_exp2f(-fabsf(G[j] - __shfl(G[j], src)));
+                a[j] = sec ? kx[j] * f : 0.f;
+                b[j] = sec ? qx[j] * f : 0.f;
+                c[j] = sec ? 0.f : kx[j] * f;
+                if (lvl == 0) dot += kx[j] * qx[j];
+            }
+            const Frag<BF> ck = make_frag<BF>(c[0], c[1], c[2], c[3]);
+            mma16(tA, make_frag<BF>(a[0], a[1], a[2], a[3]), ck);
+            mma16(tPt, ck, make_frag<BF>(b[0], b[1], b[2], b[3]));
+        }
+        mfma_settle(tA, tPt);  // read after the loop's exit
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bool same = ((4 * q4 + j) >> (4 - lvl)) == (l16 >> (4 - lvl));
+            accA[j] += same ? tA[j] : 0.f;
+            accPt[j] += same ? tPt[j] : 0.f;
+        }
+    }
+    dot += __shfl_xor(dot, 16);
+    dot += __shfl_xor(dot, 32);
+    if (q4 == (l16 >> 2)) {
+        const int jd = l16 & 3;
+        accPt[0] += jd == 0 ? dot : 0.f;
+        accPt[1] += jd == 1 ? dot : 0.f;
+        accPt[2] += jd == 2 ? dot : 0.f;
+        accPt[3] += jd == 3 ? dot : 0.f;
+    }
+}
+
+// Largest in-sub-chunk decay (log2 units) for which the single-anchor diagonal blocks stay exact:
+// their column factor e^{b_R - G_i} is then at most 2^96 and the row factor at least 2^-96, far
+// inside the normal range of fp32 and bf16.  Waves whose sub-chunk decays further in some channel
+// use diag_block_split.
+constexpr float kDiagAnchorMaxDecay = 96.f;
+
+// True (uniformly across the wave) when some channel of the lanes' sub-chunks has an in-sub-chunk
+// cumulative log2 gate below -kDiagAnchorMaxDecay.
+template <int KT>
+__device__ __forceinline__ bool diag_needs_split(const float (&G)[KT][4]) {
+    bool big = false;
+#pragma unroll
+    for (int ct = 0; ct < KT; ++ct)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) big |= G[ct][j] < -kDiagAnchorMaxDecay;
+    return __builtin_amdgcn_ballot_w64(big) != 0;
 }
 
 // ------------------------------------------------------------ io element types --

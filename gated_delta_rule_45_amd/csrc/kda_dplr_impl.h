@@ -129,6 +129,63 @@ __device__ __forceinline__ float4 dplr_unpack(const KQ &x) {
     else return x;
 }
 
+// One of the four chunk matrices' diagonal 16 x 16 blocks of a sub-chunk, exact under any decay:
+// the split levels of kda_device.h (split_anchor) with the loops rolled, the operands reloaded from
+// memory and the matrix chosen at run time (one copy of this rare path's code: the kernel's common
+// path uses every register).  ROWB: the row vector is b with the
+// exclusive gate G_{r-1}, else q with G_r; COLA: the column vector is a, else k.  For a second-half
+// row token the level's anchor token is at or before r - 1, so e^{G_{r-1} - a} and e^{G_r - a} are
+// both <= 1.  Returns the accumulator layout (rows r = 4*q4 + j, column i = l16) of the strictly
+// lower part plus, for q rows, the diagonal (factor 1).  q, k, a, b, g point at the lane's token row
+// (channels 4*q4 ...: tile ct at + 16 ct); valid is false past the chunk end.
+template <typename IO>
+__device__ __forceinline__ f32x4 dplr_diag_split(const IO *q, const IO *k, const IO *a, const IO *b, const float *g,
+                                                 bool valid, int KT, int l16, int q4, int lane, bool ROWB, bool COLA) {
+    using Tr = IoTraits<IO>;
+    constexpr bool BF = Tr::kBf16;
+    f32x4 acc = zero4();
+    float d = 0.f;
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 1
+    for (int lvl = 0; lvl < 4; ++lvl) {
+        const int hs = 8 >> lvl;
+        const bool sec = (l16 & hs) != 0;
+        const int src = (lane & ~15) | ((l16 & ~(2 * hs - 1)) + hs - 1);  // the level's anchor token
+        f32x4 t = zero4();
+#pragma unroll 1
+        for (int ct = 0; ct < KT; ++ct) {
+            const float4 rv = valid ? Tr::load4((ROWB ? b : q) + 16 * ct) : z;
+            const float4 cv = valid ? Tr::load4((COLA ? a : k) + 16 * ct) : z;
+            const float4 gr = valid ? *reinterpret_cast<const float4 *>(g + 16 * ct) : z;
+            const float G[4] = {scan16_add(gr.x * kLog2e), scan16_add(gr.y * kLog2e), scan16_add(gr.z * kLog2e),
+                                scan16_add(gr.w * kLog2e)};
+            const float gx[4] = {gr.x, gr.y, gr.z, gr.w};
+            const float rx[4] = {rv.x, rv.y, rv.z, rv.w}, cx[4] = {cv.x, cv.y, cv.z, cv.w};
+            float ro[4], co[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float an = __shfl(G[j], src);
+                const float Gr = ROWB ? G[j] - gx[j] * kLog2e : G[j];
+                ro[j] = sec ? rx[j] * fast_exp2(fminf(Gr - an, 0.f)) : 0.f;     // e^{G_{r(-1)} - a}
+                co[j] = sec ? 0.f : cx[j] * fast_exp2(fminf(an - G[j], 0.f));  // e^{a - G_i}
+                if (!ROWB && lvl == 0) d += rx[j] * cx[j];
+            }
+            mma16(t, make_frag<BF>(ro[0], ro[1], ro[2], ro[3]), make_frag<BF>(co[0], co[1], co[2], co[3]));
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] += ((4 * q4 + j) >> (4 - lvl)) == (l16 >> (4 - lvl)) ? t[j] : 0.f;
+    }
+    if (!ROWB) {  // diagonal of the q rows: q_r . (a_r or k_r) of the lane's token
+        d += __shfl_xor(d, 16);
+        d += __shfl_xor(d, 32);
+        if (q4 == (l16 >> 2)) {  // entry [r = l16][i = l16] sits at j = l16 % 4
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] += (l16 & 3) == j ? d : 0.f;
+        }
+    }
+    return acc;
+}
+
 template <typename IO, int DK, int DVT, int C>
 __global__ void __launch_bounds__(kChunkThreads) kda_dplr_fwd_kernel(DplrParams dp) {
     using L = DplrLayout<IO, DK, DVT, C>;
@@ -211,6 +268,7 @@ __global__ void __launch_bounds__(kChunkThreads) kda_dplr_fwd_kernel(DplrParams 
         // ================= 1: gate scan (log2), stage V
         float G[KT][4];
         const bool valid = 16 * wave + l16 < clen;
+        bool split = false;  // the sub-chunk decays too strongly for a single-anchor diagonal block
         if (wave < NSUB) {
             const int R = wave;
 #pragma unroll
@@ -224,6 +282,7 @@ __global__ void __launch_bounds__(kChunkThreads) kda_dplr_fwd_kernel(DplrParams 
                 if (l16 == 15)
                     *reinterpret_cast<float4 *>(sTot + R * DK + c) = make_float4(G[ct][0], G[ct][1], G[ct][2], G[ct][3]);
             }
+            split = diag_needs_split<KT>(G);
         }
         {
             constexpr int PPR = DVT / L::V_ELEMS;
@@ -234,6 +293,33 @@ __global__ void __launch_bounds__(kChunkThreads) kda_dplr_fwd_kernel(DplrParams 
                     const int r = piece / PPR;
                     const int cc = (piece % PPR) * L::V_ELEMS;
                     *reinterpret_cast<uint4 *>(sV + r * LDV + cc) = r < clen ? raw.v[i] : make_uint4(0u, 0u, 0u, 0u);
+                }
+            }
+        }
+        if (split) {
+            // Decay beyond 2^-96 inside the sub-chunk: the diagonal blocks from the split levels (all
+            // factors <= 1), written to their LDS places here; phase 4a discards its own products.
+            const int R = wave;
+            const int64_t row = ((tok0 + min(16 * R + l16, clen - 1)) * H + h) * (int64_t)DK + 4 * q4;
+            const IO *qp = static_cast<const IO *>(p.q) + row, *kp = static_cast<const IO *>(p.k) + row;
+            const IO *ap = static_cast<const IO *>(dp.a) + row, *bp = static_cast<const IO *>(dp.b) + row;
+            const float *gp = p.g + row;
+            // matrices 0..3: M_ba (fp32 to sAd for the inverse), M_bk, M_qa, M_qk
+#pragma unroll 1
+            for (int mi = 0; mi < 4; ++mi) {
+                const bool rowb = mi < 2, cola = (mi & 1) == 0;
+                const f32x4 v = dplr_diag_split<IO>(qp, kp, ap, bp, gp, valid, KT, l16, q4, lane, rowb, cola);
+                OT *m = mi == 1 ? sMbk : mi == 2 ? sMqa : sMqk;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int rr = 4 * q4 + j;
+                    const float x = (rowb ? l16 < rr : l16 <= rr) ? v[j] : 0.f;
+                    if (mi == 0) {
+                        sAd[(R * 16 + rr) * LDD + l16] = x;
+                    } else {
+                        if constexpr (BF) m[(16 * R + rr) * LDM + 16 * R + l16] = f32_to_bf16(x);
+                        else m[(16 * R + rr) * LDM + 16 * R + l16] = x;
+                    }
                 }
             }
         }
@@ -344,7 +430,9 @@ __global__ void __launch_bounds__(kChunkThreads) kda_dplr_fwd_kernel(DplrParams 
                     mma32(mqa, qa[ct], qa[ct + 1], a0, a1);
                     mma32(mqk, qa[ct], qa[ct + 1], k0, k1);
                 }
-                // accumulator: rows rr = 4 q4 + j of block R, column ii = l16 of block I
+                // accumulator: rows rr = 4 q4 + j of block R, column ii = l16 of block I (with `split`
+                // the diagonal block was written in phase 1 and this product is discarded)
+                if (!(I == R && split))
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int rr = 4 * q4 + j, ii = l16;

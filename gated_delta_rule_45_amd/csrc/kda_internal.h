@@ -88,6 +88,8 @@ struct BwdParams {
     const void *dch;      // [slot, H, C, DV] D per chunk (operand type)
     void *duch;           // [slot, H, C, DV] dU per chunk (operand type)
     char *brec;           // [slot, H] reverse-scan records (kda_bwd_prep_kernel)
+    int32_t *split_flag;  // [slot, H] 1 where a sub-chunk of the chunk decays beyond the single-anchor
+                          // limit of the diagonal blocks (kda_bwd_prep_kernel writes every entry)
     int64_t slots;        // upper bound on the number of chunk slots
 };
 bool bwd_supported_bf16(int dk, int dv, int chunk);

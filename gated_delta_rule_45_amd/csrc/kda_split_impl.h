@@ -190,6 +190,8 @@ struct PrepLayout {
     __host__ __device__ static constexpr int shift_slot(int R, int I) { return (R - 2) * (R - 1) / 2 + I; }
 };
 
+// Three workgroups per CU (4 waves each): the kernel is bound by memory latency, and the waves of
+// the other workgroups hide it.
 template <typename IO, int DK, int C>
 __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_t *__restrict__ chunk_off,
                                                        char *__restrict__ records) {
@@ -227,6 +229,7 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
 
     // ================= 1: load sub-chunk, scan the gate (log2 domain)
     float G[KT][4], kr[KT][4], qr[KT][4];
+    bool split = false;  // the sub-chunk decays too strongly for a single-anchor diagonal block
     if (wave < NSUB) {
         const int R = wave;
         const bool valid = 16 * R + l16 < clen;
@@ -251,6 +254,27 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
             if (l16 == 15)
                 *reinterpret_cast<float4 *>(sTot + R * DK + 16 * ct + 4 * q4) =
                     make_float4(G[ct][0], G[ct][1], G[ct][2], G[ct][3]);
+        }
+        split = diag_needs_split<KT>(G);
+        if (split) {
+            // This sub-chunk decays by more than 2^-96 in some channel: its diagonal blocks of A and
+            // P come from the split levels (all factors <= 1, operands reloaded).  A_RR (times beta)
+            // goes to its place in sX; P_RR to its fragment of the record (phase 4 skips both).
+            f32x4 dA, dPt;
+            const int64_t row = ((tok0 + min(16 * R + l16, clen - 1)) * H + h) * (int64_t)DK + 4 * q4;
+            diag_block_split_rolled<IO>(dA, dPt, static_cast<const IO *>(p.k) + row, static_cast<const IO *>(p.q) + row,
+                                        p.g + row, valid, KT, l16, q4, lane);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int rr = 4 * q4 + j;
+                const float b = 16 * R + rr < clen ? p.beta[(tok0 + 16 * R + rr) * H + h] : 0.f;
+                sX[(16 * R + rr) * LDX + 16 * R + l16] = l16 < rr ? dA[j] * b : 0.f;
+            }
+            const Frag<BF> fp = make_frag<BF>(dPt[0], dPt[1], dPt[2], dPt[3]);
+            char *tile = rec + Rec::oP + Rec::tp_off(R, R / 2);
+            // even R: the half tile is this fragment alone; odd R: the right fragment of the pair
+            if (Rec::tp_half(R, R / 2)) store_frag<BF>(tile, lane, fp);
+            else *reinterpret_cast<decltype(fp.v) *>(tile + lane * Rec::PAIR_BYTES + Rec::FRAG_BYTES) = fp.v;
         }
     }
     if (tid < C) sBeta[tid] = tid < clen ? p.beta[(tok0 + tid) * H + h] : 0.f;
@@ -352,8 +376,9 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
     // ================= 4: row-R blocks of A (to LDS) and P (to the record); X_RR
     // Block (R, I) pairs the row operands k_r e^{G_r - b_{I+1}} (and the same for q) with the
     // column operand K_b of sub-chunk I; both factors are at most 1.  For I = R the column
-    // operand is k_i e^{b_R - G_i}, and for I <= R - 2 the row operands take the extra
-    // factor e^{b_R - b_{I+1}} <= 1.
+    // operand is k_i e^{b_R - G_i} (at most 2^96 unless `split`, when the block comes from the
+    // split levels instead), and for I <= R - 2 the row operands take the extra factor
+    // e^{b_R - b_{I+1}} <= 1.
     if (wave < NSUB) {
         const int R = wave;
         Frag<BF> pf[2 * NPAIR];
@@ -365,6 +390,7 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
             const OT *colp = sKb + (16 * I + l16) * LDO;
             const float *shp = sSH + (I + 2 <= R ? L::shift_slot(R, I) : 0) * DK + 4 * q4;
             f32x4 accA = zero4(), accPt = zero4();
+            // (with `split` the diagonal block was formed in phase 1: this product is discarded)
 #pragma unroll
             for (int ct = 0; ct < KT; ct += 2) {
                 Frag<BF> b0, b1, ka0, ka1, qa0, qa1;
@@ -393,13 +419,16 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
                 mma32(accA, ka0, ka1, b0, b1);   // A_RI:  rows r, columns i
                 mma32(accPt, b0, b1, qa0, qa1);  // P_RI^T: rows i, columns r
             }
+            mfma_settle(accA, accPt);  // read below, partly behind the `split` branches
             // A_RI: lane holds rows rr = 4*q4 + j, column l16
+            if (!(I == R && split)) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int rr = 4 * q4 + j;
-                float a = accA[j] * sBeta[16 * R + rr];
-                if (I == R && l16 >= rr) a = 0.f;
-                sX[(16 * R + rr) * LDX + 16 * I + l16] = a;
+                for (int j = 0; j < 4; ++j) {
+                    const int rr = 4 * q4 + j;
+                    float a = accA[j] * sBeta[16 * R + rr];
+                    if (I == R && l16 >= rr) a = 0.f;
+                    sX[(16 * R + rr) * LDX + 16 * I + l16] = a;
+                }
             }
             // P_RI^T accumulator = P_RI operand fragment: row l16, columns 4*q4 + j
             float pv[4];
@@ -411,8 +440,15 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
         for (int pp = 0; pp < NPAIR; ++pp)
             if (2 * pp <= R)
             {
-                if (Rec::tp_half(R, pp)) store_frag<BF>(rec + Rec::oP + Rec::tp_off(R, pp), lane, pf[2 * pp]);
-                else store_pair<BF>(rec + Rec::oP + Rec::tp_off(R, pp), lane, pf[2 * pp], pf[2 * pp + 1]);
+                char *tile = rec + Rec::oP + Rec::tp_off(R, pp);
+                if (split && 2 * pp + 1 >= R) {  // the tile holding P_RR, whose fragment phase 1 wrote
+                    if (!Rec::tp_half(R, pp))     // odd R: the left fragment, P_R,R-1
+                        *reinterpret_cast<decltype(pf[0].v) *>(tile + lane * Rec::PAIR_BYTES) = pf[2 * pp].v;
+                } else if (Rec::tp_half(R, pp)) {
+                    store_frag<BF>(tile, lane, pf[2 * pp]);
+                } else {
+                    store_pair<BF>(tile, lane, pf[2 * pp], pf[2 * pp + 1]);
+                }
             }
 
         // X_RR = (I + A_RR)^{-1}, row by row; lane l16 owns column l16 (this wave wrote A_RR)

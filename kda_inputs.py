@@ -200,6 +200,24 @@ def workload_inputs_on(name: str, device, *, seed: Optional[int] = None) -> Inpu
     return inp
 
 
+def plant_strong_decay(inp: Inputs) -> Inputs:
+    """Stress gates for decay inside a chunk far beyond the workloads' (the workloads' strongest
+    16-token decay is about e^-40): in every head, channel 5 takes log-gate -100 at token 37,
+    channel 9 takes -20 per token over tokens 70..109, channel 11 takes -7 per token throughout
+    (e^-112 per 16 tokens), channel 13 takes -4 per token throughout (e^-64 per 16 tokens) and
+    channel 2 takes -60 at every 16th token.  Tokens past the sequence are skipped; g is
+    changed in place (the layout is the token-major [B, T, H, d_k] of every workload)."""
+    g = inp.g
+    T = g.shape[1]
+    g[:, 37:38, :, 5] = -100.0
+    g[:, 70:110, :, 9] = -20.0
+    g[:, :, :, 11] = -7.0
+    g[:, :, :, 13] = -4.0
+    g[:, 7:T:16, :, 2] = -60.0
+    inp.meta["strong_decay"] = True
+    return inp
+
+
 def to_numpy_io(x: torch.Tensor) -> np.ndarray:
     """CPU tensor -> numpy: fp32 stays float32, bf16 becomes its raw uint16 bit pattern."""
     x = x.contiguous()

@@ -273,15 +273,16 @@ def test_bwd_workspace_query():
     # N [64][72], Q~^T and (beta K~)^T [128][72] (bf16), e^{G_C} and beta (fp32): 64,256 B,
     # rounded up to whole KB
     brec = (64 * 136 * 2 + 64 * 72 * 2 + 2 * 128 * 72 * 2 + 512 + 256 + 1023) // 1024 * 1024
+    # and one int32 flag per chunk and head (strong decay inside the chunk), in a 256-byte section
     slots = 2 * 2  # 2 sequences x ceil(100 / 64)
     assert n.value == a256(256 + slots * 2 * rec) + 2 * slots * 2 * 128 * 128 * 2 + 2 * slots * 2 * 64 * 128 * 2 + \
-        a256(slots * 2 * brec)
+        a256(slots * 2 * brec) + a256(slots * 2 * 4)
     # a packed batch reserves one partial chunk per sequence
     assert lib.kda_chunk_bwd_workspace(ctypes.byref(_bwd_problem(batch=1, seq_len=300, num_seqs=5)),
                                        ctypes.byref(n)) == kda.KDA_OK
     slots = 5 + 5
     assert n.value == a256(256 + slots * 2 * rec) + 2 * slots * 2 * 128 * 128 * 2 + 2 * slots * 2 * 64 * 128 * 2 + \
-        a256(slots * 2 * brec)
+        a256(slots * 2 * brec) + a256(slots * 2 * 4)
     assert lib.kda_chunk_bwd_workspace(ctypes.byref(_bwd_problem(chunk_size=48)), ctypes.byref(n)) == \
         kda.KDA_ERR_UNSUPPORTED
     assert n.value == 0

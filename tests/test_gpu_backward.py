@@ -170,3 +170,14 @@ def test_bwd_side_stream_workspace():
     for r in got[0::2]:
         for key in KEYS:
             assert torch.equal(r[key], ref[key]), key
+
+
+@pytest.mark.parametrize("io,dk,chunk", [("bf16", 128, 64), ("bf16", 128, 16), ("bf16", 64, 32), ("f32", 64, 16),
+                                         ("f32", 64, 32)])
+def test_bwd_strong_decay_inside_a_chunk(io, dk, chunk):
+    """Gradients under the stress gates of kda_inputs.plant_strong_decay (decay of e^-100 in one
+    token, e^-112 per sub-chunk, ...): finite and within the bars."""
+    inp = ki.plant_strong_decay(ki.make_inputs(2, 203, 2, dk, 128 if io == "bf16" else 64, io, seed=61 + chunk,
+                                               s0_std=0.5))
+    skip_unsupported(inp, chunk)
+    check_bwd(inp, chunk=chunk, label=f"strong decay {io} d{dk} c{chunk}")

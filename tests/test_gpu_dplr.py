@@ -94,3 +94,12 @@ def test_dplr_repeatable(chunk):
     o2, f2 = kda.dplr_chunk_fwd(*args, chunk_size=chunk, dv_tile=32)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(f1, f2)
+
+
+@pytest.mark.parametrize("io,dk,chunk", [("bf16", 128, 64), ("bf16", 128, 16), ("bf16", 64, 32), ("f32", 64, 64)])
+def test_dplr_strong_decay_inside_a_chunk(io, dk, chunk):
+    """The comparator under the stress gates of kda_inputs.plant_strong_decay: finite outputs and
+    final states within the bars."""
+    inp = ki.plant_strong_decay(ki.make_inputs(2, 203, 2, dk, 128 if io == "bf16" else 64, io, seed=71 + chunk,
+                                               s0_std=0.5))
+    check(inp, chunk=chunk, label=f"strong decay {io} d{dk} c{chunk}")

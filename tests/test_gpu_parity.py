@@ -396,3 +396,23 @@ def test_side_stream_workspace():
     for out, fin, _ in results:
         compare("side-stream out", out, o_ref, "bf16")
         compare("side-stream final_state", fin, f_ref, "bf16")
+
+
+@pytest.mark.parametrize("io,dk,chunk", [("bf16", 128, 64), ("bf16", 128, 32), ("bf16", 128, 16), ("bf16", 64, 64),
+                                         ("f32", 64, 64), ("f32", 128, 32), ("f32", 64, 16)])
+@pytest.mark.parametrize("algo", ALGOS)
+def test_strong_decay_inside_a_chunk(io, dk, chunk, algo):
+    """Channels that decay by e^-100 in one token, e^-20 per token over 40 tokens, e^-112 and
+    e^-64 per 16-token sub-chunk and e^-60 every 16th token (kda_inputs.plant_strong_decay):
+    outputs and final states stay finite and within the bars (the diagonal blocks of the chunk
+    matrices switch to the split-level factors where a sub-chunk decays beyond 2^-96)."""
+    inp = ki.plant_strong_decay(small(2, 203, 2, dk, 128, io, 51 + dk + chunk, s0_std=0.5))
+    check_fwd(inp, chunk_size=chunk, label=f"strong-decay-{io}-d{dk}-c{chunk}", algo=algo)
+
+
+def test_strong_decay_recurrent_and_packed():
+    inp = ki.plant_strong_decay(ki.make_inputs(1, 0, 3, 128, 128, "bf16", 52, s0_std=0.5,
+                                               lengths=[150, 1, 0, 64, 90]))
+    check_fwd(inp, mode="recurrent", label="strong-decay recurrent")
+    for algo in ALGOS:
+        check_fwd(inp, label="strong-decay packed", algo=algo)
