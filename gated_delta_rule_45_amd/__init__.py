@@ -22,7 +22,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_bwd", "dplr_chunk_fwd", "recurrent_fwd", "decode_step", "prologue", "norm_gate", "query", "tune", "KdaError",
+__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "noalloc_scratch_bytes", "chunk_bwd", "dplr_chunk_fwd", "recurrent_fwd", "decode_step", "prologue", "norm_gate", "query", "tune", "KdaError",
            "LIB_PATH", "library"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
@@ -94,6 +94,10 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_dplr_chunk_fwd.argtypes = [ctypes.POINTER(Problem)] + [_P] * 12
     lib.kda_chunk_bwd.restype = ctypes.c_int
     lib.kda_chunk_bwd.argtypes = [ctypes.POINTER(Problem)] + [_P] * 17 + [ctypes.c_size_t, _P]
+    lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
+    lib.kda_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(Problem)] + [_P] * 11
+    lib.kda_noalloc_scratch_bytes.restype = ctypes.c_size_t
+    lib.kda_noalloc_scratch_bytes.argtypes = []
     lib.kda_chunk_bwd_workspace.restype = ctypes.c_int
     lib.kda_chunk_bwd_workspace.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(ctypes.c_size_t)]
     lib.kda_query.restype = ctypes.c_int
@@ -265,6 +269,47 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     if gate is not None or norm_weight is not None:
         norm_gate(out, gate, norm_weight, eps=norm_eps, out=out, stream=stream)
     return out, fin
+
+
+def chunk_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+                      initial_state: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None, *,
+                      cu_seqlens_host=None, chunk_size: int = 0, scale: float = 1.0, dv_tile: int = 0,
+                      out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+                      output_final_state: bool = True, stream=None):
+    """chunk_fwd (two-pass) with the library's fixed scratch array instead of a workspace
+    (kda_chunk_fwd_noalloc): the library allocates nothing.  Pass `out` and `final_state` to
+    allocate nothing here either.  Returns (out, final_state)."""
+    dev = q.device
+    p, n = _problem_from(q, v, cu_seqlens, chunk_size, scale, dv_tile, KDA_ALGO_TWO_PASS)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    for t, name, dt, shape in ((q, "q", q.dtype, (B, T, H, dk)), (k, "k", q.dtype, (B, T, H, dk)),
+                               (v, "v", q.dtype, (B, T, H, dv)), (g, "g", torch.float32, (B, T, H, dk)),
+                               (beta, "beta", torch.float32, (B, T, H))):
+        _need(t, name, dt, shape, dev)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (n, H, dk, dv), dev)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, (n + 1,), dev)
+    host_cu = None if cu_seqlens_host is None else torch.as_tensor(cu_seqlens_host, dtype=torch.int32).contiguous()
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    _need(out, "out", q.dtype, (B, T, H, dv), dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((n, H, dk, dv), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _need(final_state, "final_state", torch.float32, (n, H, dk, dv), dev)
+    st = library().kda_chunk_fwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                         _ptr(initial_state), _ptr(cu_seqlens),
+                                         None if host_cu is None else ctypes.c_void_p(host_cu.data_ptr()),
+                                         _ptr(out), _ptr(final_state), _stream_handle(dev, stream))
+    _check(st)
+    return out, final_state
+
+
+def noalloc_scratch_bytes() -> int:
+    """Bytes of the fixed per-device scratch array chunk_fwd_noalloc uses."""
+    return int(library().kda_noalloc_scratch_bytes())
 
 
 def bwd_workspace_bytes(p: Problem) -> int:

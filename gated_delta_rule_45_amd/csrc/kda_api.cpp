@@ -31,6 +31,20 @@ kda_status_t ok() {
     return KDA_OK;
 }
 
+}  // namespace
+
+kda_status_t kda::set_error(kda_status_t st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+namespace {
+
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 bool supported_head_dim(int d) { return d == 64 || d == 128; }

@@ -8,6 +8,9 @@
 
 namespace kda {
 
+// Records a status message readable with kda_last_error() (this thread) and returns the status.
+kda_status_t set_error(kda_status_t st, const char *fmt, ...);
+
 // Everything a forward launch needs; pointers are device pointers.
 struct FwdParams {
     const void *q, *k, *v;

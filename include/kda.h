@@ -317,6 +317,26 @@ kda_status_t kda_tune(const kda_problem_t *problem, const void *q, const void *k
                       const int32_t *cu_seqlens_host, void *out, float *final_state, void *workspace,
                       size_t workspace_bytes, void *stream, kda_query_result_t *best);
 
+/*
+ * kda_chunk_fwd_noalloc -- kda_chunk_fwd (two-pass algorithm) for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The chunk-offset table and per-chunk records live in a fixed array of the library on
+ * each device (kda_noalloc_scratch_bytes(), 64 MiB, held until the process ends); nothing is
+ * allocated or freed.  Arguments, layouts and errors as for kda_chunk_fwd, without the workspace;
+ * problem->algo is ignored (always two-pass).  A problem whose workspace (kda_query with
+ * KDA_ALGO_TWO_PASS) exceeds the array returns KDA_ERR_WORKSPACE before touching the device
+ * (64 MiB holds, for instance, 4,096 tokens x 16 heads at d = 128, chunk 64).  All calls on one
+ * device share its array: calls that overlap on a device (concurrent streams, threads) race and
+ * must be ordered by the caller.
+ */
+kda_status_t kda_chunk_fwd_noalloc(const kda_problem_t *problem, const void *q, const void *k, const void *v,
+                                   const float *g, const float *beta, const float *initial_state,
+                                   const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, void *out,
+                                   float *final_state, void *stream);
+
+/* Bytes of the fixed scratch array kda_chunk_fwd_noalloc uses on each device. */
+size_t kda_noalloc_scratch_bytes(void);
+
 /* Static description of a status code. */
 const char *kda_status_string(kda_status_t status);
 

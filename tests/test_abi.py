@@ -343,3 +343,22 @@ def test_dplr_validation():
     bad[9] = ptrs[3]  # out aliases a
     assert call(_bwd_problem(), bad) == kda.KDA_ERR_INVALID_ARGUMENT
     assert call(_bwd_problem(batch=0), ptrs) == kda.KDA_OK
+
+
+def test_noalloc_refuses_problems_beyond_its_array_on_the_host():
+    """kda_chunk_fwd_noalloc validates and sizes the problem before touching the device: NULL problem
+    and a workspace beyond its fixed 64 MiB array are refused with a message (no GPU needed)."""
+    lib = kda.library()
+    assert lib.kda_noalloc_scratch_bytes() == 64 << 20
+    P = ctypes.c_void_p(256)
+    assert lib.kda_chunk_fwd_noalloc(None, P, P, P, P, P, None, None, None, P, None, None) == \
+        kda.KDA_ERR_INVALID_ARGUMENT
+    p = kda.Problem(batch=4, seq_len=4096, num_heads=16, head_dim_k=128, head_dim_v=128, num_seqs=0,
+                    io_dtype=kda.KDA_BF16, chunk_size=64, scale=1.0, dv_tile=0, algo=0)
+    assert lib.kda_chunk_fwd_noalloc(ctypes.byref(p), P, P, P, P, P, None, None, None, P, None, None) == \
+        kda.KDA_ERR_WORKSPACE
+    msg = lib.kda_last_error().decode()
+    assert "247464192" in msg and str(64 << 20) in msg
+    p.chunk_size = 48
+    assert lib.kda_chunk_fwd_noalloc(ctypes.byref(p), P, P, P, P, P, None, None, None, P, None, None) == \
+        kda.KDA_ERR_UNSUPPORTED
