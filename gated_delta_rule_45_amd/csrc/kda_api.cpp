@@ -462,12 +462,13 @@ kda_status_t kda_chunk_bwd(const kda_problem_t *problem, const void *q, const vo
         fp.hs = ws + b.off_hs;
         fp.dch = ws + b.off_dch;
         fp.chunk_off = varlen ? chunk_off : nullptr;
+        fp.order = varlen ? kda::plan_order(ws, r.num_seqs) : nullptr;  // longest sequences first
         if (b.two_pass) {  // the two-pass forward builds the chunk-offset table itself
             st = hip_status(kda::launch_split_fwd(problem->io_dtype, fp, b.chunk, 1, 2, ws, b.slots, s),
                             "kda_chunk_bwd forward launch");
         } else {
             if (varlen) {
-                st = hip_status(kda::launch_chunk_plan(cu_seqlens, r.num_seqs, b.chunk, chunk_off, s),
+                st = hip_status(kda::launch_chunk_plan(cu_seqlens, r.num_seqs, b.chunk, ws, s),
                                 "kda_chunk_bwd plan launch");
                 if (st != KDA_OK) return st;
             }

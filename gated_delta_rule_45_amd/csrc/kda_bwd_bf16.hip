@@ -11,10 +11,8 @@ hipError_t launch_bwd_bf16(const BwdParams &bp, int chunk, hipStream_t stream) {
     return launch_bwd<uint16_t>(bp, chunk, stream);
 }
 
-hipError_t launch_chunk_plan(const int32_t *cu, int32_t num_seqs, int32_t chunk, int32_t *chunk_off,
-                             hipStream_t stream) {
-    hipLaunchKernelGGL(kda_plan_kernel, dim3(1), dim3(256), 0, stream, cu, num_seqs, chunk, chunk_off);
-    return hipGetLastError();
+hipError_t launch_chunk_plan(const int32_t *cu, int32_t num_seqs, int32_t chunk, void *plan, hipStream_t stream) {
+    return launch_plan(cu, num_seqs, chunk, plan, stream);
 }
 
 }  // namespace kda

@@ -733,12 +733,8 @@ __global__ void __launch_bounds__(kBwdScanThreads) kda_bwd_scan_kernel(BwdParams
     const int H = p.H, DV = p.dv;
 
     const int ntile = DV / DVT;
-    const int64_t nblocks = (int64_t)p.num_seqs * H * ntile;
-    const int64_t item = xcd_grouped_block(blockIdx.x, nblocks);
-    const int tile = (int)(item % ntile);
-    const int64_t nh = item / ntile;
-    const int h = (int)(nh % H);
-    const int n = (int)(nh / H);
+    const SeqItem item = seq_item(blockIdx.x, p.num_seqs, H, ntile, p.order);
+    const int tile = item.tile, h = item.h, n = item.n;
     int64_t start;
     int len;
     if (p.cu) {

@@ -191,13 +191,8 @@ __global__ void __launch_bounds__(kChunkThreads, (fused_min_waves<IO, DK, C>()))
 
     // ---- which (sequence, head, d_v tile) this workgroup owns
     const int ntile = DV / DVT;
-    const int64_t nblocks = (int64_t)p.num_seqs * H * ntile;
-    const int64_t item = xcd_grouped_block(blockIdx.x, nblocks);
-    const int tile = (int)(item % ntile);
-    const int64_t nh = item / ntile;
-    const int h = (int)(nh % H);
-    int n = (int)(nh / H);
-    if (p.order) n = p.order[n];
+    const SeqItem item = seq_item(blockIdx.x, p.num_seqs, H, ntile, p.order);
+    const int tile = item.tile, h = item.h, n = item.n;
     int64_t start;
     int len;
     if (p.cu) {

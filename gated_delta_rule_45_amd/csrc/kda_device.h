@@ -455,4 +455,30 @@ __device__ __forceinline__ int64_t xcd_grouped_block(int64_t b, int64_t nblocks)
     return (b & 7) * per + (b >> 3);
 }
 
+// Workgroup -> (sequence, head, d_v tile) for the kernels that walk one sequence's chunks in order.
+// A unit is a (sequence rank, head) pair; its ntile d_v tiles run next to each other on one XCD,
+// since they read the same per-chunk inputs through its L2.  When the unit count is a multiple of 8
+// the units are dealt to the XCDs in turn, in rank order: workgroups start in id order, so with
+// `order` listing the sequences most chunks first the longest chains start first and every XCD
+// gets every 8th of them.  Without `order` the rank is the sequence index.
+struct SeqItem {
+    int n, h, tile;
+};
+__device__ __forceinline__ SeqItem seq_item(int64_t b, int num_seqs, int H, int ntile, const int32_t *order) {
+    const int64_t units = (int64_t)num_seqs * H;
+    int64_t u;
+    int tile;
+    if ((units & 7) == 0) {
+        const int64_t j = b >> 3;  // position on XCD b % 8
+        u = (j / ntile) * 8 + (b & 7);
+        tile = (int)(j % ntile);
+    } else {
+        const int64_t item = xcd_grouped_block(b, units * ntile);
+        u = item / ntile;
+        tile = (int)(item % ntile);
+    }
+    const int r = (int)(u / H);
+    return SeqItem{order ? order[r] : r, (int)(u % H), tile};
+}
+
 }  // namespace kda

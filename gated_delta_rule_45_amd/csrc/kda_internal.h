@@ -17,7 +17,7 @@ struct FwdParams {
     const float *g, *beta;
     const float *s0;     // [num_seqs, H, DK, DV] or null
     const int32_t *cu;   // [num_seqs + 1] or null (then sequence n is tokens [n*T, (n+1)*T))
-    const int32_t *order;// optional schedule: order[i] = sequence processed by the i-th group of blocks
+    const int32_t *order;// optional schedule: order[r] = sequence of rank r, most chunks first
     void *out;
     float *sf;           // [num_seqs, H, DK, DV] or null
     int32_t num_seqs, T, H, dk, dv;
@@ -55,8 +55,15 @@ hipError_t launch_decode_step(kda_dtype_t io, int32_t N, int32_t H, int32_t dk, 
 
 constexpr int kChunkThreads = 256;
 
-// Two-pass forward: bytes of the chunk-offset table at the start of the workspace.
-inline size_t split_plan_bytes(int64_t num_seqs) { return (size_t)(((num_seqs + 1) * 4 + 255) / 256 * 256); }
+// Plan of a packed batch at the start of the two-pass forward's and the backward's workspace:
+// [chunk offsets: num_seqs + 1 int32][longest-first order: num_seqs int32], each padded to 256 bytes.
+inline size_t plan_offsets_bytes(int64_t num_seqs) { return (size_t)(((num_seqs + 1) * 4 + 255) / 256 * 256); }
+inline size_t split_plan_bytes(int64_t num_seqs) {
+    return plan_offsets_bytes(num_seqs) + (size_t)((num_seqs * 4 + 255) / 256 * 256);
+}
+inline int32_t *plan_order(void *plan, int64_t num_seqs) {
+    return reinterpret_cast<int32_t *>(static_cast<char *>(plan) + plan_offsets_bytes(num_seqs));
+}
 size_t split_workspace_bytes(kda_dtype_t io, int dk, int chunk, int64_t chunk_upper, int H, int64_t num_seqs);
 bool split_variant_supported(kda_dtype_t io, int dk, int chunk, int spw, int nw, bool keep = false);
 // workgroup size and LDS of the forward's scan kernel for a shape; false if not compiled
@@ -101,8 +108,8 @@ size_t bwd_record_bytes_f32(int dk, int chunk);
 bool bwd_supported_f32(int dk, int dv, int chunk);
 hipError_t launch_bwd_bf16(const BwdParams &bp, int chunk, hipStream_t stream);
 hipError_t launch_bwd_f32(const BwdParams &bp, int chunk, hipStream_t stream);
-hipError_t launch_chunk_plan(const int32_t *cu, int32_t num_seqs, int32_t chunk, int32_t *chunk_off,
-                             hipStream_t stream);
+// writes the plan (chunk offsets and order) of a packed batch to `plan`
+hipError_t launch_chunk_plan(const int32_t *cu, int32_t num_seqs, int32_t chunk, void *plan, hipStream_t stream);
 
 // General-DPLR comparator (kda_dplr.hip).
 struct DplrParams {

@@ -690,12 +690,8 @@ __global__ void __launch_bounds__(64 * (NW + scan_copy_waves(SPW))) kda_scan_ker
     const int lane = tid & 63, l16 = lane & 15, q4 = lane >> 4;
     const int H = p.H, DV = p.dv;
     const int ntile = DV / DVT;
-    const int64_t nblocks = (int64_t)p.num_seqs * H * ntile;
-    const int64_t item = xcd_grouped_block(blockIdx.x, nblocks);
-    const int tile = (int)(item % ntile);
-    const int64_t nh = item / ntile;
-    const int h = (int)(nh % H);
-    const int n = (int)(nh / H);
+    const SeqItem item = seq_item(blockIdx.x, p.num_seqs, H, ntile, p.order);
+    const int tile = item.tile, h = item.h, n = item.n;
     int64_t start;
     int len;
     if (p.cu) {
@@ -1040,12 +1036,8 @@ __global__ void __launch_bounds__(64 * (2 * NW + scan_copy_waves(SPW))) kda_scan
     const int lane = tid & 63, l16 = lane & 15, q4 = lane >> 4;
     const int H = p.H, DV = p.dv;
     const int ntile = DV / DVT;
-    const int64_t nblocks = (int64_t)p.num_seqs * H * ntile;
-    const int64_t item = xcd_grouped_block(blockIdx.x, nblocks);
-    const int tile = (int)(item % ntile);
-    const int64_t nh = item / ntile;
-    const int h = (int)(nh % H);
-    const int n = (int)(nh / H);
+    const SeqItem item = seq_item(blockIdx.x, p.num_seqs, H, ntile, p.order);
+    const int tile = item.tile, h = item.h, n = item.n;
     int64_t start;
     int len;
     if (p.cu) {
@@ -1371,9 +1363,11 @@ constexpr bool split_fits() {
     return ScanLayout<IO, DK, C, SPW, NW>::kFits && PrepLayout<IO, DK, C>::kBytes <= 160 * 1024;
 }
 
-// Workspace: [chunk offsets: num_seqs + 1 int32, padded to 256 B][records]
+// Workspace: [plan: chunk offsets and longest-first order, split_plan_bytes][records]
 template <typename IO, int DK, int C, int SPW, int NW>
-hipError_t launch_split_variant(const FwdParams &p, char *workspace, int64_t chunk_upper, hipStream_t stream) {
+hipError_t launch_split_variant(const FwdParams &params, char *workspace, int64_t chunk_upper, hipStream_t stream) {
+    FwdParams p = params;
+    if (p.cu) p.order = plan_order(workspace, p.num_seqs);  // the scan runs the longest sequences first
     const bool keep = p.hs != nullptr;
     if constexpr (!split_fits<IO, DK, C, SPW, NW>()) {
         return hipErrorInvalidConfiguration;
@@ -1383,8 +1377,7 @@ hipError_t launch_split_variant(const FwdParams &p, char *workspace, int64_t chu
         int32_t *chunk_off = reinterpret_cast<int32_t *>(workspace);
         char *records = workspace + split_plan_bytes(p.num_seqs);
         if (p.cu) {
-            hipLaunchKernelGGL(kda_plan_kernel, dim3(1), dim3(256), 0, stream, p.cu, p.num_seqs, C, chunk_off);
-            hipError_t e = hipGetLastError();
+            hipError_t e = launch_plan(p.cu, p.num_seqs, C, workspace, stream);
             if (e != hipSuccess) return e;
         }
         const int64_t prep_blocks = chunk_upper * p.H;

@@ -95,10 +95,13 @@ typedef struct {
  *  cu_seqlens      int32 [num_seqs+1] device offsets of a packed batch (cu[0] = 0,
  *                  non-decreasing, cu[num_seqs] = seq_len), or NULL for a plain batch.
  *                  Chunks restart at every sequence start and never cross a boundary;
- *                  a zero-length sequence passes its initial state through.
+ *                  a zero-length sequence passes its initial state through.  The
+ *                  two-pass algorithm ranks the sequences on the device by chunk count
+ *                  and starts the state scans of the longest ones first (the fused
+ *                  algorithm, which has no workspace for the ranking, runs them in
+ *                  batch order).
  *  cu_seqlens_host optional host copy of cu_seqlens: when given, its contents are
- *                  validated (otherwise they are a precondition) and used to schedule
- *                  long sequences first.
+ *                  validated (otherwise they are a precondition).
  *  out             [tokens, H, d_v] io dtype (written).
  *  final_state     [num_seqs, H, d_k, d_v] fp32, or NULL to skip writing it.  It may be
  *                  the same pointer as initial_state (in-place state cache); no other
@@ -140,7 +143,9 @@ kda_status_t kda_recurrent_fwd(const kda_problem_t *problem, const void *q, cons
  * For the loss L = sum(d_out * out) + sum(d_final_state * final_state) of the forward with
  * the same arguments, writes dq, dk, dv, dg, dbeta and (optionally) d_initial_state.
  *  problem, q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_host
- *                  as for kda_chunk_fwd (the forward is recomputed; out is not needed).
+ *                  as for kda_chunk_fwd (the forward is recomputed; out is not needed;
+ *                  the forward and reverse state scans of a packed batch run the
+ *                  longest sequences first).
  *                  problem->chunk_size: 16, 32 or 64 (0 = default); problem->algo and
  *                  dv_tile are ignored.
  *  d_out           [tokens, H, d_v] io dtype: gradient of out.

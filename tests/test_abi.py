@@ -156,12 +156,13 @@ def test_query_reports_config_and_work():
     r = kda.query(4, 4096, 16, 128, 128, "bf16")
     assert r["status"] == kda.KDA_OK and r["supported"] == 1
     assert r["algo"] == kda.KDA_ALGO_TWO_PASS and r["chunk_size"] == 64
-    # chunk-offset table (256 B) + one record per chunk-head: K~, Q~, K-^T (16 KB each),
+    # plan (chunk-offset table and longest-first order, 256 B each) + one record per chunk-head:
+    # K~, Q~, K-^T (16 KB each),
     # the lower 16x32 tiles of T and of P (5 KB each: the two diagonal tiles of even row tiles
     # keep only their left 16 columns), Gamma (512 B), rounded up to whole KB
     rec = 3 * 16384 + 2 * 5120 + 512
     rec = (rec + 1023) // 1024 * 1024
-    assert r["workspace_bytes"] == 256 + 4 * 64 * 16 * rec
+    assert r["workspace_bytes"] == 2 * 256 + 4 * 64 * 16 * rec
     assert r["grid_blocks"] == 4 * 16 * (128 // r["dv_tile"])
     rf = kda.query(4, 4096, 16, 128, 128, "bf16", algo="fused")
     assert rf["algo"] == kda.KDA_ALGO_FUSED and rf["workspace_bytes"] == 0
@@ -275,13 +276,13 @@ def test_bwd_workspace_query():
     brec = (64 * 136 * 2 + 64 * 72 * 2 + 2 * 128 * 72 * 2 + 512 + 256 + 1023) // 1024 * 1024
     # and one int32 flag per chunk and head (strong decay inside the chunk), in a 256-byte section
     slots = 2 * 2  # 2 sequences x ceil(100 / 64)
-    assert n.value == a256(256 + slots * 2 * rec) + 2 * slots * 2 * 128 * 128 * 2 + 2 * slots * 2 * 64 * 128 * 2 + \
+    assert n.value == a256(2 * 256 + slots * 2 * rec) + 2 * slots * 2 * 128 * 128 * 2 + 2 * slots * 2 * 64 * 128 * 2 + \
         a256(slots * 2 * brec) + a256(slots * 2 * 4)
     # a packed batch reserves one partial chunk per sequence
     assert lib.kda_chunk_bwd_workspace(ctypes.byref(_bwd_problem(batch=1, seq_len=300, num_seqs=5)),
                                        ctypes.byref(n)) == kda.KDA_OK
     slots = 5 + 5
-    assert n.value == a256(256 + slots * 2 * rec) + 2 * slots * 2 * 128 * 128 * 2 + 2 * slots * 2 * 64 * 128 * 2 + \
+    assert n.value == a256(2 * 256 + slots * 2 * rec) + 2 * slots * 2 * 128 * 128 * 2 + 2 * slots * 2 * 64 * 128 * 2 + \
         a256(slots * 2 * brec) + a256(slots * 2 * 4)
     assert lib.kda_chunk_bwd_workspace(ctypes.byref(_bwd_problem(chunk_size=48)), ctypes.byref(n)) == \
         kda.KDA_ERR_UNSUPPORTED
@@ -358,7 +359,7 @@ def test_noalloc_refuses_problems_beyond_its_array_on_the_host():
     assert lib.kda_chunk_fwd_noalloc(ctypes.byref(p), P, P, P, P, P, None, None, None, P, None, None) == \
         kda.KDA_ERR_WORKSPACE
     msg = lib.kda_last_error().decode()
-    assert "247464192" in msg and str(64 << 20) in msg
+    assert "247464448" in msg and str(64 << 20) in msg  # 512 B of plan + 4 x 64 x 16 records of 60,416 B
     p.chunk_size = 48
     assert lib.kda_chunk_fwd_noalloc(ctypes.byref(p), P, P, P, P, P, None, None, None, P, None, None) == \
         kda.KDA_ERR_UNSUPPORTED

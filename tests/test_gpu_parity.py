@@ -205,6 +205,36 @@ def test_varlen_with_empty_and_single_token_sequences(algo):
     check_fwd(inp, mode="recurrent", label="varlen-edge")
 
 
+def test_packed_plan_ranks_longest_first():
+    """The two-pass plan of a packed batch (300 sequences: two ranking workgroups, empty ones and
+    many equal chunk counts): the chunk-offset table is the prefix sum of ceil(len / C) and the
+    order lists the sequences most chunks first, equal counts in batch order (integers: exact);
+    the outputs, scanned in that order, still match the oracle."""
+    rng = np.random.default_rng(300)
+    lens = [int(x) for x in rng.integers(0, 400, size=300)]
+    lens[::17] = [0] * len(lens[::17])
+    lens[5::23] = [64] * len(lens[5::23])
+    C = 64
+    inp = ki.make_inputs(1, 0, 2, 64, 64, "bf16", 22, lengths=lens)
+    T = sum(lens)
+    ws_bytes = kda.query(1, T, 2, 64, 64, "bf16", num_seqs=len(lens), chunk_size=C,
+                         algo="two_pass")["workspace_bytes"]
+    ws = torch.full((ws_bytes,), 0xAB, dtype=torch.uint8, device=DEV)
+    d = on_dev(inp)
+    out, fin = kda.chunk_fwd(**d, chunk_size=C, algo="two_pass", workspace=ws)
+    torch.cuda.synchronize()
+    n = len(lens)
+    a256 = lambda x: (x + 255) // 256 * 256
+    words = ws[: a256((n + 1) * 4) + a256(n * 4)].view(torch.int32).cpu().numpy()
+    nc = [(x + C - 1) // C for x in lens]
+    assert words[: n + 1].tolist() == [0] + list(np.cumsum(nc))
+    off = a256((n + 1) * 4) // 4  # int32 index of the order table
+    assert words[off: off + n].tolist() == sorted(range(n), key=lambda i: (-nc[i], i))
+    o_ref, f_ref = run_oracle(inp)
+    compare("plan out", out, o_ref, "bf16")
+    compare("plan final_state", fin, f_ref, "bf16")
+
+
 @pytest.mark.parametrize("algo", ALGOS)
 def test_no_initial_state_and_no_final_state(algo):
     inp = small(2, 150, 2, 128, 128, "bf16", 5, s0_std=None)
