@@ -43,14 +43,14 @@ class KdaError(RuntimeError):
 class Problem(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32), ("num_heads", ctypes.c_int32),
                 ("head_dim_k", ctypes.c_int32), ("head_dim_v", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
-                ("io_dtype", ctypes.c_int), ("chunk_size", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("io_dtype", ctypes.c_int32), ("chunk_size", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("dv_tile", ctypes.c_int32), ("algo", ctypes.c_int)]
 
 
 class PrologueProblem(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
                 ("num_heads", ctypes.c_int32), ("head_dim_k", ctypes.c_int32), ("head_dim_v", ctypes.c_int32),
-                ("conv_width", ctypes.c_int32), ("io_dtype", ctypes.c_int), ("norm_eps", ctypes.c_float)]
+                ("conv_width", ctypes.c_int32), ("io_dtype", ctypes.c_int32), ("norm_eps", ctypes.c_float)]
 
 
 class QueryResult(ctypes.Structure):
@@ -81,7 +81,7 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_recurrent_fwd.restype = ctypes.c_int
     lib.kda_recurrent_fwd.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
     lib.kda_decode_step.restype = ctypes.c_int
-    lib.kda_decode_step.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int,
+    lib.kda_decode_step.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                     ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P]
     lib.kda_tune.restype = ctypes.c_int
     lib.kda_tune.argtypes = [ctypes.POINTER(Problem), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P,
@@ -89,7 +89,7 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_prologue.restype = ctypes.c_int
     lib.kda_prologue.argtypes = [ctypes.POINTER(PrologueProblem)] + [_P] * 17
     lib.kda_norm_gate.restype = ctypes.c_int
-    lib.kda_norm_gate.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int, ctypes.c_float, _P, _P, _P, _P, _P]
+    lib.kda_norm_gate.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _P, _P, _P, _P, _P]
     lib.kda_dplr_chunk_fwd.restype = ctypes.c_int
     lib.kda_dplr_chunk_fwd.argtypes = [ctypes.POINTER(Problem)] + [_P] * 12
     lib.kda_chunk_bwd.restype = ctypes.c_int

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdint>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -48,6 +49,13 @@ namespace {
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 bool supported_head_dim(int d) { return d == 64 || d == 128; }
+
+// An element type that has passed validation (KDA_F32 or KDA_BF16), as the enum.
+kda_dtype_t dtype_of(int32_t io) { return io == KDA_BF16 ? KDA_BF16 : KDA_F32; }
+
+// a * b for a, b >= 0, saturating at INT64_MAX: size checks on caller-given dimensions never overflow
+int64_t sat_mul(int64_t a, int64_t b) { return (a != 0 && b > INT64_MAX / a) ? INT64_MAX : a * b; }
+int64_t sat_mul(int64_t a, int64_t b, int64_t c) { return sat_mul(sat_mul(a, b), c); }
 
 // Published MI355X peaks used for roofline fractions.
 constexpr double kPeakBf16Tflops = 2500.0;
@@ -120,32 +128,32 @@ kda_status_t resolve(const kda_problem_t *p, bool varlen, Resolved &r, bool chun
         r.num_seqs = p->batch;
         r.tokens = (int64_t)p->batch * p->seq_len;
     }
-    const int64_t blocks_max = (int64_t)r.num_seqs * p->num_heads * 4;
+    const int64_t blocks_max = sat_mul(r.num_seqs, p->num_heads, 4);
     if (blocks_max > 0x7fffffffLL) return fail(KDA_ERR_UNSUPPORTED, "too many (sequence, head) pairs");
-    if (r.tokens * p->num_heads * (int64_t)std::max(p->head_dim_k, p->head_dim_v) >= (1LL << 62))
+    if (sat_mul(r.tokens, p->num_heads, std::max(p->head_dim_k, p->head_dim_v)) >= (1LL << 62))
         return fail(KDA_ERR_UNSUPPORTED, "tensor too large");
     if (chunked) {
         const int64_t chains = (int64_t)r.num_seqs * p->num_heads;
         const int C = p->chunk_size ? p->chunk_size : default_chunk(*p, chains);
         r.cfg.chunk = C;
         r.cfg.dv_tile = p->dv_tile ? p->dv_tile : default_dv_tile((int64_t)r.num_seqs * p->num_heads, p->head_dim_v);
-        r.lds = kda::chunk_variant_lds_bytes(p->io_dtype, p->head_dim_k, r.cfg.dv_tile, r.cfg.chunk);
+        r.lds = kda::chunk_variant_lds_bytes(dtype_of(p->io_dtype), p->head_dim_k, r.cfg.dv_tile, r.cfg.chunk);
         // two-pass: scan workgroups of two compute waves, each owning 16 (32-column tiles) or 32
         // (64-column tiles) state columns.  By default 64-column tiles once they still give every CU
         // two workgroups: each record is then staged half as often (measured on 64 packed
         // sequences x 32 heads: 7.01 vs 8.71 ms); otherwise 32-column tiles, for parallelism.
         int scan_cols = p->dv_tile == 64 ? 64 : 32;
         if (p->dv_tile == 0 && p->head_dim_v >= 64 && chains * (p->head_dim_v / 64) >= 2 * kAssumedCUs &&
-            kda::split_variant_supported(p->io_dtype, p->head_dim_k, C, 2, 2))
+            kda::split_variant_supported(dtype_of(p->io_dtype), p->head_dim_k, C, 2, 2))
             scan_cols = 64;
         r.spw = scan_cols == 32 ? 1 : 2;
         r.nw = 2;
         r.two_pass_ok = p->dv_tile != 128 && scan_cols <= p->head_dim_v &&
-                        kda::split_variant_supported(p->io_dtype, p->head_dim_k, C, r.spw, r.nw);
+                        kda::split_variant_supported(dtype_of(p->io_dtype), p->head_dim_k, C, r.spw, r.nw);
         if (r.two_pass_ok) {
             const int64_t per = ((int64_t)p->seq_len + C - 1) / C;
             r.chunk_upper = varlen ? per + r.num_seqs : (int64_t)r.num_seqs * per;
-            r.ws_bytes = kda::split_workspace_bytes(p->io_dtype, p->head_dim_k, C, r.chunk_upper, p->num_heads,
+            r.ws_bytes = kda::split_workspace_bytes(dtype_of(p->io_dtype), p->head_dim_k, C, r.chunk_upper, p->num_heads,
                                                     r.num_seqs);
         }
         const bool fused_ok = r.lds > 0;
@@ -278,22 +286,22 @@ kda_status_t resolve_bwd(const kda_problem_t *p, bool varlen, BwdResolved &b) {
     } else {  // largest chunk with a compiled variant
         b.chunk = 0;
         for (int c : {64, 32, 16})
-            if (bwd_variant_supported(p->io_dtype, dk, dv, c) &&
-                kda::chunk_variant_lds_bytes(p->io_dtype, dk, 32, c) > 0) {
+            if (bwd_variant_supported(dtype_of(p->io_dtype), dk, dv, c) &&
+                kda::chunk_variant_lds_bytes(dtype_of(p->io_dtype), dk, 32, c) > 0) {
                 b.chunk = c;
                 break;
             }
         if (b.chunk == 0) return fail(KDA_ERR_UNSUPPORTED, "backward: no compiled variant for d_k=%d d_v=%d", dk, dv);
     }
-    if (!bwd_variant_supported(p->io_dtype, dk, dv, b.chunk))
+    if (!bwd_variant_supported(dtype_of(p->io_dtype), dk, dv, b.chunk))
         return fail(KDA_ERR_UNSUPPORTED, "backward: no compiled variant for io=%s d_k=%d d_v=%d chunk=%d (LDS)",
                     p->io_dtype == KDA_BF16 ? "bf16" : "fp32", dk, dv, b.chunk);
     // the forward again with the 32-column scan (twice the workgroups of the 64-column one)
-    b.two_pass = dv % 32 == 0 && kda::split_variant_supported(p->io_dtype, dk, b.chunk, 1, 2, true);
+    b.two_pass = dv % 32 == 0 && kda::split_variant_supported(dtype_of(p->io_dtype), dk, b.chunk, 1, 2, true);
     b.fwd_dv_tile = 0;
     if (!b.two_pass) {
         for (int t : {default_dv_tile((int64_t)b.r.num_seqs * p->num_heads, dv), 32})
-            if (t <= dv && kda::chunk_variant_lds_bytes(p->io_dtype, dk, t, b.chunk) > 0) {
+            if (t <= dv && kda::chunk_variant_lds_bytes(dtype_of(p->io_dtype), dk, t, b.chunk) > 0) {
                 b.fwd_dv_tile = t;
                 break;
             }
@@ -308,7 +316,7 @@ kda_status_t resolve_bwd(const kda_problem_t *p, bool varlen, BwdResolved &b) {
     const size_t states = align256((size_t)b.slots * p->num_heads * dk * dv * s_io);  // operand type
     const size_t tiles = align256((size_t)b.slots * p->num_heads * b.chunk * dv * s_io);
     // [chunk offsets][two-pass records (when two-pass)][states][state gradients][D][dU][records][flags]
-    b.off_hs = b.two_pass ? align256(kda::split_workspace_bytes(p->io_dtype, dk, b.chunk, b.slots, p->num_heads,
+    b.off_hs = b.two_pass ? align256(kda::split_workspace_bytes(dtype_of(p->io_dtype), dk, b.chunk, b.slots, p->num_heads,
                                                                 b.r.num_seqs))
                           : kda::split_plan_bytes(b.r.num_seqs);
     b.off_dhs = b.off_hs + states;
@@ -371,6 +379,28 @@ hipError_t launch_chunk_fwd(kda_dtype_t io, const FwdParams &p, const ChunkConfi
 
 }  // namespace kda
 
+namespace kda {
+
+kda_status_t check_chunk_fwd(const kda_problem_t *problem, const void *q, const void *k, const void *v,
+                             const float *g, const float *beta, const float *initial_state,
+                             const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, const void *out,
+                             const float *final_state, int64_t *num_seqs) {
+    try {
+        Resolved r;
+        kda_status_t st = resolve(problem, cu_seqlens != nullptr, r, true);
+        if (st != KDA_OK) return st;
+        st = check_tensors(problem, r, q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_host, out,
+                           final_state);
+        if (st != KDA_OK) return st;
+        if (num_seqs) *num_seqs = r.num_seqs;
+        return ok();
+    } catch (...) {
+        return fail(KDA_ERR_HIP, "unexpected exception in argument checks");
+    }
+}
+
+}  // namespace kda
+
 extern "C" {
 
 kda_status_t kda_chunk_fwd(const kda_problem_t *problem, const void *q, const void *k, const void *v,
@@ -391,11 +421,11 @@ kda_status_t kda_chunk_fwd(const kda_problem_t *problem, const void *q, const vo
         const kda::FwdParams fp =
             make_params(problem, r, q, k, v, g, beta, initial_state, cu_seqlens, out, final_state);
         if (algo == KDA_ALGO_TWO_PASS)
-            return hip_status(kda::launch_split_fwd(problem->io_dtype, fp, r.cfg.chunk, r.spw, r.nw,
+            return hip_status(kda::launch_split_fwd(dtype_of(problem->io_dtype), fp, r.cfg.chunk, r.spw, r.nw,
                                                     static_cast<char *>(workspace), r.chunk_upper,
                                                     static_cast<hipStream_t>(stream)),
                               "kda_chunk_fwd (two-pass) launch");
-        return hip_status(kda::launch_chunk_fwd(problem->io_dtype, fp, r.cfg, static_cast<hipStream_t>(stream)),
+        return hip_status(kda::launch_chunk_fwd(dtype_of(problem->io_dtype), fp, r.cfg, static_cast<hipStream_t>(stream)),
                           "kda_chunk_fwd (fused) launch");
     } catch (...) {
         return fail(KDA_ERR_HIP, "unexpected exception in kda_chunk_fwd");
@@ -464,7 +494,7 @@ kda_status_t kda_chunk_bwd(const kda_problem_t *problem, const void *q, const vo
         fp.chunk_off = varlen ? chunk_off : nullptr;
         fp.order = varlen ? kda::plan_order(ws, r.num_seqs) : nullptr;  // longest sequences first
         if (b.two_pass) {  // the two-pass forward builds the chunk-offset table itself
-            st = hip_status(kda::launch_split_fwd(problem->io_dtype, fp, b.chunk, 1, 2, ws, b.slots, s),
+            st = hip_status(kda::launch_split_fwd(dtype_of(problem->io_dtype), fp, b.chunk, 1, 2, ws, b.slots, s),
                             "kda_chunk_bwd forward launch");
         } else {
             if (varlen) {
@@ -472,7 +502,7 @@ kda_status_t kda_chunk_bwd(const kda_problem_t *problem, const void *q, const vo
                                 "kda_chunk_bwd plan launch");
                 if (st != KDA_OK) return st;
             }
-            st = hip_status(kda::launch_chunk_fwd(problem->io_dtype, fp, kda::ChunkConfig{b.chunk, b.fwd_dv_tile}, s),
+            st = hip_status(kda::launch_chunk_fwd(dtype_of(problem->io_dtype), fp, kda::ChunkConfig{b.chunk, b.fwd_dv_tile}, s),
                             "kda_chunk_bwd forward launch");
         }
         if (st != KDA_OK) return st;
@@ -513,7 +543,7 @@ kda_status_t kda_dplr_chunk_fwd(const kda_problem_t *problem, const void *q, con
         const int dvt = problem->dv_tile ? problem->dv_tile : 32;
         if (dvt > problem->head_dim_v)
             return fail(KDA_ERR_INVALID_ARGUMENT, "dv_tile %d exceeds d_v %d", dvt, problem->head_dim_v);
-        if (!kda::dplr_variant_supported(problem->io_dtype, problem->head_dim_k, dvt, C))
+        if (!kda::dplr_variant_supported(dtype_of(problem->io_dtype), problem->head_dim_k, dvt, C))
             return fail(KDA_ERR_UNSUPPORTED, "dplr: no compiled variant for io=%s d_k=%d dv_tile=%d chunk=%d",
                         problem->io_dtype == KDA_BF16 ? "bf16" : "fp32", problem->head_dim_k, dvt, C);
         // q, k, v, g, out checks as the forward (beta is not an input here: g stands in for it)
@@ -532,7 +562,7 @@ kda_status_t kda_dplr_chunk_fwd(const kda_problem_t *problem, const void *q, con
         dp.f = make_params(problem, r, q, k, v, g, nullptr, initial_state, cu_seqlens, out, final_state);
         dp.a = a;
         dp.b = b;
-        return hip_status(kda::launch_dplr_fwd(problem->io_dtype, dp, dvt, C, static_cast<hipStream_t>(stream)),
+        return hip_status(kda::launch_dplr_fwd(dtype_of(problem->io_dtype), dp, dvt, C, static_cast<hipStream_t>(stream)),
                           "kda_dplr_chunk_fwd launch");
     } catch (...) {
         return fail(KDA_ERR_HIP, "unexpected exception in kda_dplr_chunk_fwd");
@@ -630,7 +660,7 @@ kda_status_t kda_recurrent_fwd(const kda_problem_t *problem, const void *q, cons
         if (r.num_seqs == 0) return ok();
         const kda::FwdParams fp =
             make_params(problem, r, q, k, v, g, beta, initial_state, cu_seqlens, out, final_state);
-        return hip_status(kda::launch_recurrent_fwd(problem->io_dtype, fp, static_cast<hipStream_t>(stream)),
+        return hip_status(kda::launch_recurrent_fwd(dtype_of(problem->io_dtype), fp, static_cast<hipStream_t>(stream)),
                           "kda_recurrent_fwd launch");
     } catch (...) {
         return fail(KDA_ERR_HIP, "unexpected exception in kda_recurrent_fwd");
@@ -638,7 +668,7 @@ kda_status_t kda_recurrent_fwd(const kda_problem_t *problem, const void *q, cons
 }
 
 kda_status_t kda_decode_step(int32_t num_seqs, int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v,
-                             kda_dtype_t io_dtype, float scale, const void *q, const void *k, const void *v,
+                             int32_t io_dtype, float scale, const void *q, const void *k, const void *v,
                              const float *g, const float *beta, float *state, void *out, void *stream) {
     try {
         if (num_seqs < 0 || num_heads < 1)
@@ -649,7 +679,7 @@ kda_status_t kda_decode_step(int32_t num_seqs, int32_t num_heads, int32_t head_d
             return fail(KDA_ERR_UNSUPPORTED, "head dims d_k=%d d_v=%d: supported are 64 and 128", head_dim_k,
                         head_dim_v);
         if (!std::isfinite(scale)) return fail(KDA_ERR_INVALID_ARGUMENT, "scale is not finite");
-        if ((int64_t)num_seqs * num_heads * (head_dim_v / 32) > 0x7fffffffLL)
+        if (sat_mul(num_seqs, num_heads, head_dim_v / 32) > 0x7fffffffLL)
             return fail(KDA_ERR_UNSUPPORTED, "too many (sequence, head) pairs");
         if (num_seqs == 0) return ok();
         const void *req[] = {q, k, v, g, beta, state, out};
@@ -664,7 +694,7 @@ kda_status_t kda_decode_step(int32_t num_seqs, int32_t num_heads, int32_t head_d
         if (out == state || out == q || out == k || out == v || (const void *)state == (const void *)g ||
             (const void *)state == q || (const void *)state == k || (const void *)state == v)
             return fail(KDA_ERR_INVALID_ARGUMENT, "state or out aliases another tensor");
-        return hip_status(kda::launch_decode_step(io_dtype, num_seqs, num_heads, head_dim_k, head_dim_v, scale, q, k,
+        return hip_status(kda::launch_decode_step(dtype_of(io_dtype), num_seqs, num_heads, head_dim_k, head_dim_v, scale, q, k,
                                                   v, g, beta, state, out, static_cast<hipStream_t>(stream)),
                           "kda_decode_step launch");
     } catch (...) {
@@ -695,7 +725,7 @@ kda_status_t kda_prologue(const kda_prologue_t *p, const void *q_raw, const void
         if (varlen && !cu_seqlens) return fail(KDA_ERR_INVALID_ARGUMENT, "num_seqs > 0 needs cu_seqlens");
         const int64_t tokens = varlen ? (int64_t)p->seq_len : (int64_t)p->batch * p->seq_len;
         const int32_t nseq = varlen ? p->num_seqs : p->batch;
-        if (tokens * p->num_heads * (int64_t)std::max(p->head_dim_k, p->head_dim_v) >= (1LL << 40))
+        if (sat_mul(tokens, p->num_heads, std::max(p->head_dim_k, p->head_dim_v)) >= (1LL << 40))
             return fail(KDA_ERR_UNSUPPORTED, "tensor too large");
         if (tokens == 0 && !conv_state_out) return ok();
         const void *req[] = {q_raw, k_raw, v_raw, conv_q, conv_k, conv_v, g_raw, beta_raw, q, k, v, g, beta};
@@ -720,7 +750,7 @@ kda_status_t kda_prologue(const kda_prologue_t *p, const void *q_raw, const void
         const void *raw[3] = {q_raw, k_raw, v_raw};
         const float *w[3] = {conv_q, conv_k, conv_v};
         void *out[3] = {q, k, v};
-        return hip_status(kda::launch_prologue(p->io_dtype, tokens, nseq, varlen ? 0 : p->seq_len, p->num_heads,
+        return hip_status(kda::launch_prologue(dtype_of(p->io_dtype), tokens, nseq, varlen ? 0 : p->seq_len, p->num_heads,
                                                p->head_dim_k, p->head_dim_v, p->conv_width,
                                                varlen ? cu_seqlens : nullptr, p->norm_eps, raw, w, g_raw, beta_raw,
                                                conv_state, conv_state_out, out, g, beta,
@@ -731,7 +761,7 @@ kda_status_t kda_prologue(const kda_prologue_t *p, const void *q_raw, const void
     }
 }
 
-kda_status_t kda_norm_gate(int64_t rows, int32_t d, kda_dtype_t io_dtype, float eps, const void *o,
+kda_status_t kda_norm_gate(int64_t rows, int32_t d, int32_t io_dtype, float eps, const void *o,
                            const void *gate, const float *weight, void *out, void *stream) {
     try {
         if (rows < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "rows %lld < 0", (long long)rows);
@@ -739,7 +769,7 @@ kda_status_t kda_norm_gate(int64_t rows, int32_t d, kda_dtype_t io_dtype, float 
             return fail(KDA_ERR_INVALID_ARGUMENT, "io_dtype %d is not KDA_F32 or KDA_BF16", (int)io_dtype);
         if (!supported_head_dim(d)) return fail(KDA_ERR_UNSUPPORTED, "d=%d: supported are 64 and 128", d);
         if (!std::isfinite(eps) || eps < 0.f) return fail(KDA_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
-        if (kda::norm_gate_blocks(io_dtype, rows, d) > 0x7fffffffLL) return fail(KDA_ERR_UNSUPPORTED, "too many rows");
+        if (kda::norm_gate_blocks(dtype_of(io_dtype), rows, d) > 0x7fffffffLL) return fail(KDA_ERR_UNSUPPORTED, "too many rows");
         if (rows == 0) return ok();
         const void *req[] = {o, gate, weight, out};
         const char *names[] = {"o", "gate", "weight", "out"};
@@ -749,7 +779,7 @@ kda_status_t kda_norm_gate(int64_t rows, int32_t d, kda_dtype_t io_dtype, float 
         }
         if (out == gate || (const void *)weight == out || (const void *)weight == o || (const void *)weight == gate)
             return fail(KDA_ERR_INVALID_ARGUMENT, "out may alias o only");
-        return hip_status(kda::launch_norm_gate(io_dtype, rows, d, eps, o, gate, weight, out,
+        return hip_status(kda::launch_norm_gate(dtype_of(io_dtype), rows, d, eps, o, gate, weight, out,
                                                 static_cast<hipStream_t>(stream)),
                           "kda_norm_gate launch");
     } catch (...) {
@@ -777,7 +807,7 @@ kda_status_t kda_query(const kda_problem_t *problem, uint32_t flags, kda_query_r
             if (two) {  // the scan pass: one workgroup per (sequence, head, 16*spw*nw columns)
                 res->dv_tile = 16 * r.spw * r.nw;
                 int threads = 0, lds = 0;
-                kda::split_scan_shape(p.io_dtype, p.head_dim_k, r.cfg.chunk, r.spw, r.nw, threads, lds);
+                kda::split_scan_shape(dtype_of(p.io_dtype), p.head_dim_k, r.cfg.chunk, r.spw, r.nw, threads, lds);
                 res->threads_per_block = threads;
                 res->lds_bytes = lds;
                 res->grid_blocks = (int64_t)r.num_seqs * p.num_heads * (p.head_dim_v / res->dv_tile);

@@ -98,7 +98,7 @@ hipError_t launch_norm_gate_t(int64_t rows, float eps, const void *o, const void
 int64_t norm_gate_blocks(kda_dtype_t io, int64_t rows, int d) {
     const int n = io == KDA_BF16 ? 8 : 4;
     const int rpb = 256 / (d / n);
-    return (rows + rpb - 1) / rpb;
+    return rows / rpb + (rows % rpb != 0);  // no rows + rpb - 1: rows may be as large as INT64_MAX
 }
 
 hipError_t launch_norm_gate(kda_dtype_t io, int64_t rows, int d, float eps, const void *o, const void *z,

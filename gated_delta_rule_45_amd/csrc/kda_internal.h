@@ -8,6 +8,12 @@
 
 namespace kda {
 
+// The host-side argument checks of kda_chunk_fwd (problem, pointers, alignment, aliasing and
+// cu_seqlens_host), without the workspace; KDA_OK clears the error and reports the sequence count.
+kda_status_t check_chunk_fwd(const kda_problem_t *problem, const void *q, const void *k, const void *v,
+                             const float *g, const float *beta, const float *initial_state,
+                             const int32_t *cu_seqlens, const int32_t *cu_seqlens_host, const void *out,
+                             const float *final_state, int64_t *num_seqs);
 // Records a status message readable with kda_last_error() (this thread) and returns the status.
 kda_status_t set_error(kda_status_t st, const char *fmt, ...);
 

@@ -54,19 +54,22 @@ kda_status_t kda_chunk_fwd_noalloc(const kda_problem_t *problem, const void *q, 
         if (!problem) return kda::set_error(KDA_ERR_INVALID_ARGUMENT, "problem is NULL");
         kda_problem_t p = *problem;
         p.algo = KDA_ALGO_TWO_PASS;
-        if (cu_seqlens && p.num_seqs == 0)  // no sequence: nothing to compute, no scratch used
-            return kda_chunk_fwd(&p, q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_host, out, final_state,
-                                 nullptr, 0, stream);
-        if (!cu_seqlens) p.num_seqs = 0;  // kda_query: a plain batch
+        // every argument is checked on the host before the device is touched
+        int64_t num_seqs = 0;
+        kda_status_t st = kda::check_chunk_fwd(&p, q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_host,
+                                               out, final_state, &num_seqs);
+        if (st != KDA_OK) return st;
+        if (num_seqs == 0) return KDA_OK;  // no sequence: nothing to compute, no scratch used
+        kda_problem_t pq = p;
+        if (!cu_seqlens) pq.num_seqs = 0;  // kda_query: a plain batch
         kda_query_result_t r;
-        const kda_status_t st = kda_query(&p, 0, &r);  // validates the problem, host only
+        st = kda_query(&pq, 0, &r);
         if (st != KDA_OK) return st;
         if (r.workspace_bytes > kScratchBytes)
             return kda::set_error(KDA_ERR_WORKSPACE,
                                   "kda_chunk_fwd_noalloc: this problem needs %zu bytes of scratch, the library's "
                                   "fixed array holds %zu (call kda_chunk_fwd with a workspace)",
                                   r.workspace_bytes, kScratchBytes);
-        if (cu_seqlens) p.num_seqs = problem->num_seqs;
         void *ptr = nullptr;
         const hipError_t e = scratch_address(&ptr);
         if (e != hipSuccess)

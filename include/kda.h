@@ -58,6 +58,8 @@ typedef enum {
     KDA_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed */
 } kda_status_t;
 
+/* Element types.  Structs and parameters carry them as int32_t (any value can cross the ABI;
+ * values other than these are refused with KDA_ERR_INVALID_ARGUMENT). */
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
 
 /* How kda_chunk_fwd evaluates the chunks.
@@ -78,7 +80,7 @@ typedef struct {
     int32_t head_dim_k;  /* d_k in {64, 128} */
     int32_t head_dim_v;  /* d_v in {64, 128} */
     int32_t num_seqs;    /* with cu_seqlens: number of sequences (cu_seqlens has num_seqs+1 entries); else ignored */
-    kda_dtype_t io_dtype;/* dtype of q, k, v and out; g, beta and the state are always fp32 */
+    int32_t io_dtype;    /* kda_dtype_t: dtype of q, k, v and out; g, beta and the state are always fp32 */
     int32_t chunk_size;  /* 16, 32 or 64; 0 = library default (64, or 32 for fp32 with d_k = 128) */
     float scale;         /* multiplies the output (1.0 for o_t = S_t^T q_t) */
     int32_t dv_tile;     /* state columns per workgroup: 0 = library choice; fused: 32, 64 or 128;
@@ -205,7 +207,7 @@ kda_status_t kda_chunk_bwd_workspace(const kda_problem_t *problem, size_t *bytes
  *  state [num_seqs, H, d_k, d_v] fp32, read and overwritten; out [num_seqs, H, d_v].
  */
 kda_status_t kda_decode_step(int32_t num_seqs, int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v,
-                             kda_dtype_t io_dtype, float scale, const void *q, const void *k, const void *v,
+                             int32_t io_dtype, float scale, const void *q, const void *k, const void *v,
                              const float *g, const float *beta, float *state, void *out, void *stream);
 
 /* Shape of a kda_prologue call (same batch / packed conventions as kda_problem_t). */
@@ -217,7 +219,7 @@ typedef struct {
     int32_t head_dim_k;  /* 64 or 128 */
     int32_t head_dim_v;  /* 64 or 128 */
     int32_t conv_width;  /* W, taps of the short convolution: 1..4 */
-    kda_dtype_t io_dtype;/* raw q/k/v, outputs q/k/v and the convolution state */
+    int32_t io_dtype;    /* kda_dtype_t: raw q/k/v, outputs q/k/v and the convolution state */
     float norm_eps;      /* >= 0: q and k are divided by sqrt(sum x^2 + norm_eps) */
 } kda_prologue_t;
 
@@ -265,7 +267,7 @@ kda_status_t kda_prologue(const kda_prologue_t *problem, const void *q_raw, cons
  *  Errors: KDA_ERR_INVALID_ARGUMENT (sizes, eps, NULL or misaligned pointers, aliasing),
  *  KDA_ERR_UNSUPPORTED (d), KDA_ERR_HIP (launch).  rows == 0 launches nothing.
  */
-kda_status_t kda_norm_gate(int64_t rows, int32_t d, kda_dtype_t io_dtype, float eps, const void *o,
+kda_status_t kda_norm_gate(int64_t rows, int32_t d, int32_t io_dtype, float eps, const void *o,
                            const void *gate, const float *weight, void *out, void *stream);
 
 /* Result of kda_query. */

@@ -351,15 +351,22 @@ def test_noalloc_refuses_problems_beyond_its_array_on_the_host():
     and a workspace beyond its fixed 64 MiB array are refused with a message (no GPU needed)."""
     lib = kda.library()
     assert lib.kda_noalloc_scratch_bytes() == 64 << 20
-    P = ctypes.c_void_p(256)
-    assert lib.kda_chunk_fwd_noalloc(None, P, P, P, P, P, None, None, None, P, None, None) == \
+    P = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(6)]  # distinct aligned addresses, never read
+    assert lib.kda_chunk_fwd_noalloc(None, *P[:5], None, None, None, P[5], None, None) == \
         kda.KDA_ERR_INVALID_ARGUMENT
     p = kda.Problem(batch=4, seq_len=4096, num_heads=16, head_dim_k=128, head_dim_v=128, num_seqs=0,
                     io_dtype=kda.KDA_BF16, chunk_size=64, scale=1.0, dv_tile=0, algo=0)
-    assert lib.kda_chunk_fwd_noalloc(ctypes.byref(p), P, P, P, P, P, None, None, None, P, None, None) == \
+    # the arguments are checked first (here: out aliases q), then the size
+    assert lib.kda_chunk_fwd_noalloc(ctypes.byref(p), *P[:5], None, None, None, P[0], None, None) == \
+        kda.KDA_ERR_INVALID_ARGUMENT
+    assert lib.kda_chunk_fwd_noalloc(ctypes.byref(p), *P[:5], None, None, None, P[5], None, None) == \
         kda.KDA_ERR_WORKSPACE
     msg = lib.kda_last_error().decode()
     assert "247464448" in msg and str(64 << 20) in msg  # 512 B of plan + 4 x 64 x 16 records of 60,416 B
     p.chunk_size = 48
-    assert lib.kda_chunk_fwd_noalloc(ctypes.byref(p), P, P, P, P, P, None, None, None, P, None, None) == \
+    assert lib.kda_chunk_fwd_noalloc(ctypes.byref(p), *P[:5], None, None, None, P[5], None, None) == \
         kda.KDA_ERR_UNSUPPORTED
+    # an empty problem computes nothing and needs no device
+    p.chunk_size, p.batch = 64, 0
+    assert lib.kda_chunk_fwd_noalloc(ctypes.byref(p), None, None, None, None, None, None, None, None, None, None,
+                                     None) == kda.KDA_OK
