@@ -13,6 +13,8 @@ The prologue (kda_prologue: short convolution + Swish, q/k L2 norm, gate and bet
 and the output epilogue (kda_norm_gate: per-head RMSNorm and output gate) are timed on their
 own over the prefill shapes and reported next to the step, and so is the backward (kda_chunk_bwd:
 the gradients for a synthetic output gradient and final-state gradient on the prefill tensors).
+The decode step with the epilogue fused in (kda_decode_step_gated) is timed on the decode
+workload next to the two-kernel composition (kda_decode_step, then kda_norm_gate).
 `value` is prefill tokens/s (B*T tokens per chunk_fwd launch); the decode step is
 reported in GB/s next to it.  Inputs are resident in HBM before the timed region.
 Timing uses HIP events recorded on the stream the kernels are launched on.
@@ -290,6 +292,17 @@ def main():
     def decode():
         kda.decode_step(dq, dk_, dv_, dg, db, dstate, out=dout)
 
+    # decode step with the output epilogue: fused (one kernel) and composed (decode, then norm_gate)
+    _, dgate, dnw = (x.to(dev) for x in ki.epilogue_inputs((wd.B, wd.H, wd.dv), "bf16", seed=15))
+    dgout = torch.empty_like(dout)
+
+    def decode_gated():
+        kda.decode_step_gated(dq, dk_, dv_, dg, db, dstate, dgate, dnw, eps=1e-6, out=dgout)
+
+    def decode_then_norm_gate():
+        kda.decode_step(dq, dk_, dv_, dg, db, dstate, out=dout)
+        kda.norm_gate(dout, dgate, dnw, eps=1e-6, out=dgout)
+
     # ------------------------------------------- prologue (raw projections of the prefill shape)
     pin = ki.prologue_inputs(B, T, H, w.dk, w.dv, 4, "bf16", seed=6)
     pd = {k: (None if x is None else x.to(dev)) for k, x in pin.items()}
@@ -335,6 +348,8 @@ def main():
         backward()
         prefill()
         decode()
+        decode_gated()
+        decode_then_norm_gate()
         epilogue()
         prologue()
     torch.cuda.synchronize()
@@ -345,6 +360,8 @@ def main():
     t_epi = time_launches(epilogue, args.steps, stream)
     pre_med, pre_min = time_each(prefill, args.steps, stream)
     dec_med, dec_min = time_each(decode, args.steps, stream)
+    t_decg = time_launches(decode_gated, args.steps, stream)
+    t_decc = time_launches(decode_then_norm_gate, args.steps, stream)
     t_pro = time_launches(prologue, args.steps, stream)
     t_bwd = time_launches(backward, args.steps, stream)
     t_dplr = t_kfused = None
@@ -373,6 +390,8 @@ def main():
     pre_tflops = q["flops"] / (t_pre * 1e-3) / 1e12
     dec_bytes = (wd.B * wd.H * (2 * 4 * wd.dk * wd.dv + (2 * wd.dk + 2 * wd.dv) * 2 + 4 * wd.dk + 4))
     dec_gbps = dec_bytes / (t_dec * 1e-3) / 1e9
+    decg_bytes = dec_bytes + wd.B * wd.H * wd.dv * 2 + wd.dv * 4  # + gate (bf16) and the norm weight
+    decg_gbps = decg_bytes / (t_decg * 1e-3) / 1e9
     epi_rows = B * T * H
     epi_bytes = epi_rows * w.dv * 2 * 3 + w.dv * 4  # o and gate read, out written (bf16), weight
     epi_gbps = epi_bytes / (t_epi * 1e-3) / 1e9
@@ -419,6 +438,10 @@ def main():
         "decode": {"ms": round(t_dec, 4), "ms_median": round(dec_med, 4), "ms_min": round(dec_min, 4),
                    "gb_per_s": round(dec_gbps, 1), "hbm_frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
                    "bytes_per_launch": dec_bytes},
+        "decode_gated": {"kernel": "kda_decode_step_gated", "ms": round(t_decg, 4), "gb_per_s": round(decg_gbps, 1),
+                         "hbm_frac": round(decg_gbps / PEAK_HBM_GBPS, 4), "bytes_per_launch": decg_bytes,
+                         "composed_ms": round(t_decc, 4), "composed": "kda_decode_step + kda_norm_gate",
+                         "speedup_vs_composed": round(t_decc / t_decg, 3)},
         "tuned": None if tuned is None else {"chunk": tuned["chunk_size"], "dv_tile": tuned["dv_tile"],
                                              "algo": ["auto", "fused", "two_pass"][tuned["algo"]],
                                              "ms": round(tuned["tuned_ms"], 4)},

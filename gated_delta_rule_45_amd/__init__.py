@@ -22,7 +22,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "noalloc_scratch_bytes", "chunk_bwd", "dplr_chunk_fwd", "recurrent_fwd", "decode_step", "prologue", "norm_gate", "query", "tune", "KdaError",
+__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "noalloc_scratch_bytes", "chunk_bwd", "dplr_chunk_fwd", "recurrent_fwd", "decode_step", "decode_step_gated", "prologue", "norm_gate", "query", "tune", "KdaError",
            "LIB_PATH", "library"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
@@ -88,6 +88,10 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
                              ctypes.POINTER(QueryResult)]
     lib.kda_prologue.restype = ctypes.c_int
     lib.kda_prologue.argtypes = [ctypes.POINTER(PrologueProblem)] + [_P] * 17
+    lib.kda_decode_step_gated.restype = ctypes.c_int
+    lib.kda_decode_step_gated.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P,
+                                          ctypes.c_float, _P, _P]
     lib.kda_norm_gate.restype = ctypes.c_int
     lib.kda_norm_gate.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _P, _P, _P, _P, _P]
     lib.kda_dplr_chunk_fwd.restype = ctypes.c_int
@@ -439,8 +443,12 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
                 gate: Optional[torch.Tensor] = None, norm_weight: Optional[torch.Tensor] = None,
                 norm_eps: float = 1e-6):
     """One decode token per sequence.  q, k, g: [N, H, d_k]; v: [N, H, d_v]; beta: [N, H];
-    state: [N, H, d_k, d_v] fp32 (updated in place).  With gate and norm_weight the output
-    epilogue is applied to out in place.  Returns out [N, H, d_v]."""
+    state: [N, H, d_k, d_v] fp32 (updated in place).  With gate [N, H, d_v] and norm_weight
+    [d_v] the output epilogue (RMSNorm, gate) is fused into the same kernel
+    (kda_decode_step_gated) and out holds the gated output.  Returns out [N, H, d_v]."""
+    if gate is not None or norm_weight is not None:
+        return decode_step_gated(q, k, v, g, beta, state, gate, norm_weight, eps=norm_eps, scale=scale, out=out,
+                                 stream=stream)
     dev = q.device
     if q.dim() != 3:
         raise ValueError("q must be [N, H, d_k]")
@@ -458,8 +466,37 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
     st = library().kda_decode_step(N, H, dk, dv, _io_code(q.dtype), scale, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                    _ptr(beta), _ptr(state), _ptr(out), _stream_handle(dev, stream))
     _check(st)
-    if gate is not None or norm_weight is not None:
-        norm_gate(out, gate, norm_weight, eps=norm_eps, out=out, stream=stream)
+    return out
+
+
+def decode_step_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+                      state: torch.Tensor, gate: torch.Tensor, weight: torch.Tensor, *, eps: float = 1e-6,
+                      scale: float = 1.0, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Decode step with RMSNorm and the output gate in the same kernel: out = norm(o) * weight *
+    sigmoid(gate) for o = scale S^T q of each (sequence, head).  Shapes as decode_step, plus gate
+    [N, H, d_v] (io dtype) and weight [d_v] fp32.  Returns out [N, H, d_v]."""
+    dev = q.device
+    if q.dim() != 3:
+        raise ValueError("q must be [N, H, d_k]")
+    if gate is None or weight is None:
+        raise ValueError("decode_step_gated needs gate and weight")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    _need(q, "q", q.dtype, (N, H, dk), dev)
+    _need(k, "k", q.dtype, (N, H, dk), dev)
+    _need(v, "v", q.dtype, (N, H, dv), dev)
+    _need(g, "g", torch.float32, (N, H, dk), dev)
+    _need(beta, "beta", torch.float32, (N, H), dev)
+    _need(state, "state", torch.float32, (N, H, dk, dv), dev)
+    _need(gate, "gate", q.dtype, (N, H, dv), dev)
+    _need(weight, "weight", torch.float32, (dv,), dev)
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=q.dtype, device=dev)
+    _need(out, "out", q.dtype, (N, H, dv), dev)
+    st = library().kda_decode_step_gated(N, H, dk, dv, _io_code(q.dtype), scale, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                         _ptr(beta), _ptr(state), _ptr(gate), _ptr(weight), eps, _ptr(out),
+                                         _stream_handle(dev, stream))
+    _check(st)
     return out
 
 

@@ -702,6 +702,47 @@ kda_status_t kda_decode_step(int32_t num_seqs, int32_t num_heads, int32_t head_d
     }
 }
 
+kda_status_t kda_decode_step_gated(int32_t num_seqs, int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v,
+                                   int32_t io_dtype, float scale, const void *q, const void *k, const void *v,
+                                   const float *g, const float *beta, float *state, const void *gate,
+                                   const float *weight, float eps, void *out, void *stream) {
+    try {
+        if (num_seqs < 0 || num_heads < 1)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "bad sizes: num_seqs=%d num_heads=%d", num_seqs, num_heads);
+        if (io_dtype != KDA_F32 && io_dtype != KDA_BF16)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "io_dtype %d is not KDA_F32 or KDA_BF16", (int)io_dtype);
+        if (!supported_head_dim(head_dim_k) || !supported_head_dim(head_dim_v))
+            return fail(KDA_ERR_UNSUPPORTED, "head dims d_k=%d d_v=%d: supported are 64 and 128", head_dim_k,
+                        head_dim_v);
+        if (!std::isfinite(scale)) return fail(KDA_ERR_INVALID_ARGUMENT, "scale is not finite");
+        if (!std::isfinite(eps) || eps < 0.f) return fail(KDA_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+        if (sat_mul(num_seqs, num_heads) > 0x7fffffffLL)
+            return fail(KDA_ERR_UNSUPPORTED, "too many (sequence, head) pairs");
+        if (num_seqs == 0) return ok();
+        const void *req[] = {q, k, v, g, beta, state, gate, weight, out};
+        const char *names[] = {"q", "k", "v", "g", "beta", "state", "gate", "weight", "out"};
+        for (int i = 0; i < 9; ++i)
+            if (!req[i]) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
+        const void *al16[] = {q, k, v, g, state, gate, weight, out};
+        const char *n16[] = {"q", "k", "v", "g", "state", "gate", "weight", "out"};
+        for (int i = 0; i < 8; ++i)
+            if (!aligned(al16[i], 16)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", n16[i]);
+        if (!aligned(beta, 4)) return fail(KDA_ERR_INVALID_ARGUMENT, "beta is not 4-byte aligned");
+        // the written buffers (state, out) alias nothing
+        const void *ins[] = {q, k, v, g, beta, gate, weight};
+        for (const void *i : ins)
+            if (i == out || i == (const void *)state)
+                return fail(KDA_ERR_INVALID_ARGUMENT, "state or out aliases another tensor");
+        if (out == (const void *)state) return fail(KDA_ERR_INVALID_ARGUMENT, "out aliases state");
+        return hip_status(kda::launch_decode_gated(dtype_of(io_dtype), num_seqs, num_heads, head_dim_k, head_dim_v,
+                                                   scale, eps, q, k, v, g, beta, state, gate, weight, out,
+                                                   static_cast<hipStream_t>(stream)),
+                          "kda_decode_step_gated launch");
+    } catch (...) {
+        return fail(KDA_ERR_HIP, "unexpected exception in kda_decode_step_gated");
+    }
+}
+
 kda_status_t kda_prologue(const kda_prologue_t *p, const void *q_raw, const void *k_raw, const void *v_raw,
                           const float *conv_q, const float *conv_k, const float *conv_v, const float *g_raw,
                           const float *beta_raw, const int32_t *cu_seqlens, const void *conv_state,

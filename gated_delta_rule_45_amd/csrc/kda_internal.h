@@ -59,6 +59,11 @@ hipError_t launch_decode_step(kda_dtype_t io, int32_t N, int32_t H, int32_t dk, 
                               const void *q, const void *k, const void *v, const float *g, const float *beta,
                               float *state, void *out, hipStream_t stream);
 
+// Decode step with the output epilogue (RMSNorm and gate) fused in: one workgroup per (sequence, head).
+hipError_t launch_decode_gated(kda_dtype_t io, int32_t N, int32_t H, int32_t dk, int32_t dv, float scale, float eps,
+                               const void *q, const void *k, const void *v, const float *g, const float *beta,
+                               float *state, const void *gate, const float *weight, void *out, hipStream_t stream);
+
 constexpr int kChunkThreads = 256;
 
 // Plan of a packed batch at the start of the two-pass forward's and the backward's workspace:

@@ -200,6 +200,139 @@ __global__ void __launch_bounds__(256) kda_decode_kernel(int32_t H, float scale,
     }
 }
 
+// Decode step with the output epilogue fused in (Kimi Linear summary page: the per-token update
+// of "Kimi Delta Attention: fine-grained memory control", then the per-head RMSNorm and output
+// gate of "Kimi Linear model composition"; the page gives no formula for the latter, the reading is
+// out = o * rsqrt(mean(o^2) + eps) * w * sigmoid(z) over the d_v values of one head).
+//
+// The norm needs the whole d_v row of o, so one workgroup (NT threads) owns one (sequence, head): the
+// d_k x d_v fp32 state (64 KB at d = 128) is read and written once with 16-byte nontemporal
+// accesses, thread t holding columns 4 (t % CG) .. + 3 of rows t / CG + RG m.  The column sums
+// p = S'^T k and a = S'^T q cross the row groups of a wave with lane shuffles and the waves
+// through LDS; every thread then has o for its 4 columns, and the lanes of one row group (a
+// contiguous run of CG lanes) reduce sum(o^2) among themselves.  1024 threads (4 state rows of
+// 4 columns per thread at d = 128) measured at least as fast as 256 or 512 on the decode
+// workload; the kernel is bound by HBM like the plain decode step.
+#ifndef KDA_DECODE_GATED_THREADS
+#define KDA_DECODE_GATED_THREADS 1024
+#endif
+constexpr int kDecodeGatedThreads = KDA_DECODE_GATED_THREADS;
+
+template <typename IO, int DK, int DV, int NT>
+__global__ void __launch_bounds__(NT) kda_decode_gated_kernel(float scale, float eps, const IO *__restrict__ q,
+                                                               const IO *__restrict__ k, const IO *__restrict__ v,
+                                                               const float *__restrict__ g,
+                                                               const float *__restrict__ beta, float *state,
+                                                               const IO *__restrict__ gate,
+                                                               const float *__restrict__ weight, IO *__restrict__ out) {
+    constexpr int CG = DV / 4;      // 4-column groups (lanes of one row group)
+    constexpr int RG = NT / CG;     // row groups
+    constexpr int RPT = DK / RG;    // rows per thread
+    constexpr int WRG = 64 / CG;    // row groups per wave
+    constexpr int NWV = NT / 64;    // waves
+    static_assert(CG <= 64 && 64 % CG == 0 && DK % RG == 0 && RPT >= 1, "layout");
+    __shared__ float s_alpha[DK], s_k[DK], s_q[DK], s_v[DV];
+    __shared__ float s_beta, s_qk[(DK + 63) / 64];
+    __shared__ kda_v4f s_part[2][NWV][CG];  // per-wave partial p and S'^T q per column group
+
+    const int tid = threadIdx.x;
+    const int cg = tid % CG, rg = tid / CG, wv = tid >> 6;
+    const int64_t nh = blockIdx.x;
+    kda_v4f *Sg = reinterpret_cast<kda_v4f *>(state + nh * DK * DV) + cg;
+
+    kda_v4f S[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) S[m] = __builtin_nontemporal_load(Sg + (int64_t)(rg + RG * m) * (DV / 4));
+
+    using Tr = IoTraits<IO>;
+    if (tid < DK) {
+        const float kk = Tr::load1(k + nh * DK + tid), qq = Tr::load1(q + nh * DK + tid);
+        s_alpha[tid] = expf(g[nh * DK + tid]);
+        s_k[tid] = kk;
+        s_q[tid] = qq;
+        float kq = kk * qq;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) kq += __shfl_xor(kq, off, 64);
+        if ((tid & 63) == 0) s_qk[tid >> 6] = kq;
+    }
+    if (tid < DV) s_v[tid] = Tr::load1(v + nh * DV + tid);
+    if (tid == 0) s_beta = beta[nh];
+    // gate and weight of this thread's 4 columns, needed only at the end
+    float zc[4], wc[4];
+    {
+        const f32x4 ww = *reinterpret_cast<const f32x4 *>(weight + 4 * cg);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            zc[j] = Tr::load1(gate + nh * DV + 4 * cg + j);
+            wc[j] = ww[j];
+        }
+    }
+    __syncthreads();
+
+    // S' = Diag(alpha) S;  partial p = S'^T k and a = S'^T q over this thread's rows, summed over
+    // the row groups of the wave (lanes CG apart) and then, through LDS, over the 4 waves
+    kda_v4f pp = {0.f, 0.f, 0.f, 0.f}, aa = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const int i = rg + RG * m;
+        S[m] *= s_alpha[i];
+        pp += s_k[i] * S[m];
+        aa += s_q[i] * S[m];
+    }
+#pragma unroll
+    for (int off = CG; off < 64; off <<= 1) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            pp[j] += __shfl_xor(pp[j], off, 64);
+            aa[j] += __shfl_xor(aa[j], off, 64);
+        }
+    }
+    if ((tid & 63) < CG) {
+        s_part[0][wv][cg] = pp;
+        s_part[1][wv][cg] = aa;
+    }
+    __syncthreads();
+    kda_v4f ps = s_part[0][0][cg], as = s_part[1][0][cg];
+#pragma unroll
+    for (int w = 1; w < NWV; ++w) {
+        ps += s_part[0][w][cg];
+        as += s_part[1][w][cg];
+    }
+
+    // d = beta (v - p);  S = S' + k d^T;  o = scale (a + (k.q) d)
+    const float b = s_beta;
+    kda_v4f d;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) d[j] = b * (s_v[4 * cg + j] - ps[j]);
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        S[m] += s_k[rg + RG * m] * d;
+        __builtin_nontemporal_store(S[m], Sg + (int64_t)(rg + RG * m) * (DV / 4));
+    }
+    float qk = 0.f;
+#pragma unroll
+    for (int w = 0; w < (DK + 63) / 64; ++w) qk += s_qk[w];
+    float o[4], ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        o[j] = (as[j] + qk * d[j]) * scale;
+        ss = fmaf(o[j], o[j], ss);
+    }
+    // sum of o^2 over the CG lanes of this row group (xor offsets below CG stay inside it)
+#pragma unroll
+    for (int off = CG / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+    static_assert(WRG >= 1, "a row group lives inside one wave");
+    if (rg == 0) {
+        const float r = rsqrtf(ss * (1.0f / DV) + eps);
+        float4 y;
+        y.x = o[0] * r * wc[0] / (1.0f + __expf(-zc[0]));
+        y.y = o[1] * r * wc[1] / (1.0f + __expf(-zc[1]));
+        y.z = o[2] * r * wc[2] / (1.0f + __expf(-zc[2]));
+        y.w = o[3] * r * wc[3] / (1.0f + __expf(-zc[3]));
+        Tr::store4(out + nh * DV + 4 * cg, y);
+    }
+}
+
 template <typename IO, int DK, int DV>
 __global__ void __launch_bounds__(kSerialThreads) kda_recurrent_kernel(FwdParams p) {
     using L = SerialLayout<DK, DV>;
@@ -285,6 +418,37 @@ static hipError_t decode_dispatch(int32_t N, int32_t H, int32_t dk, int32_t dv, 
     KDA_SERIAL_DIMS(KDA_DEC_CASE)
 #undef KDA_DEC_CASE
     return hipErrorInvalidConfiguration;
+}
+
+template <typename IO>
+static hipError_t decode_gated_dispatch(int32_t N, int32_t H, int32_t dk, int32_t dv, float scale, float eps,
+                                        const void *q, const void *k, const void *v, const float *g,
+                                        const float *beta, float *state, const void *gate, const float *weight,
+                                        void *out, hipStream_t stream) {
+    const int64_t blocks = (int64_t)N * H;
+    if (blocks <= 0) return hipSuccess;
+#define KDA_DECG_CASE(DK_, DV_)                                                                                  \
+    if (dk == DK_ && dv == DV_) {                                                                                \
+        hipLaunchKernelGGL((kda_decode_gated_kernel<IO, DK_, DV_, kDecodeGatedThreads>), dim3((unsigned)blocks),      \
+                           dim3(kDecodeGatedThreads), 0, stream,                                                 \
+                           scale, eps, static_cast<const IO *>(q), static_cast<const IO *>(k),                   \
+                           static_cast<const IO *>(v), g, beta, state, static_cast<const IO *>(gate), weight,   \
+                           static_cast<IO *>(out));                                                              \
+        return hipGetLastError();                                                                                \
+    }
+    KDA_SERIAL_DIMS(KDA_DECG_CASE)
+#undef KDA_DECG_CASE
+    return hipErrorInvalidConfiguration;
+}
+
+hipError_t launch_decode_gated(kda_dtype_t io, int32_t N, int32_t H, int32_t dk, int32_t dv, float scale, float eps,
+                               const void *q, const void *k, const void *v, const float *g, const float *beta,
+                               float *state, const void *gate, const float *weight, void *out, hipStream_t stream) {
+    return io == KDA_BF16
+               ? decode_gated_dispatch<uint16_t>(N, H, dk, dv, scale, eps, q, k, v, g, beta, state, gate, weight, out,
+                                                 stream)
+               : decode_gated_dispatch<float>(N, H, dk, dv, scale, eps, q, k, v, g, beta, state, gate, weight, out,
+                                              stream);
 }
 
 hipError_t launch_recurrent_fwd(kda_dtype_t io, const FwdParams &p, hipStream_t stream) {

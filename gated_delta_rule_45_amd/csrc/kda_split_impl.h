@@ -539,10 +539,7 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
 // fragments are exactly the operand fragments of S^T, D's accumulator fragments those of
 // D^T, and the record's Q~ and P fragments serve unchanged as Q~^T and P^T.  Each lane then
 // holds 4 consecutive output columns of one token and stores them with one 8-byte write.
-// Copy waves per scan workgroup.  Each pair of copy waves holds one chunk's record and V tile
-// in registers on the way to LDS.  With 16-column compute waves two pairs take turns, so each
-// chunk's loads are issued two chunks ahead (a third pair measured no faster); the wider
-// compute waves need every register of their SIMD and keep a single pair, one chunk ahead.
+// Copy waves per scan workgroup with two record buffers (see ScanLayout).
 constexpr int scan_copy_waves(int spw) { return spw == 1 ? 4 : 2; }
 
 template <typename IO, int DK, int C, int SPW, int NW>
@@ -550,32 +547,41 @@ struct ScanLayout {
     using Rec = SplitRecord<IO, DK, C>;
     static constexpr int WCOLS = 16 * SPW;      // state columns per compute wave (SPW 16-column slices)
     static constexpr int DVT = WCOLS * NW;      // state columns per workgroup
-    static constexpr int NCW = scan_copy_waves(SPW);
-    static constexpr int NT = 64 * (NW + NCW);  // threads (compute waves + copy waves)
     static constexpr size_t kVBytes = (size_t)C * DVT * sizeof(IO);  // V tile [C][DVT]
     static constexpr int V_PIECES = (int)(kVBytes / 16);
-    static constexpr size_t oRec0 = 0;
-    static constexpr size_t oRec1 = Rec::kBytes;
-    static constexpr size_t oV0 = 2 * Rec::kBytes;
-    static constexpr size_t oV1 = oV0 + kVBytes;
-    static constexpr size_t kBytes = oV1 + kVBytes;
-    static constexpr bool kFits = kBytes <= 160 * 1024;
-    static_assert(Rec::kBytes % (64 * 16) == 0, "record is copied in whole wave units");
-    static_assert(V_PIECES % 64 == 0, "V tile is copied in whole wave units");
-    static_assert(!kFits || (Rec::kBytes / 1024 + V_PIECES / 64 + 1) / 2 <= 40, "copy wave register budget");
     // KEEP only: a per-compute-wave fp32 tile [16][LDK] through which the kept state and D leave
     // as 16-byte row segments (a few wide stores instead of one per accumulator element)
     static constexpr int LDK = WCOLS + 4;
     static constexpr size_t kKeepBytes = (size_t)NW * 16 * LDK * 4;
+    // Two record buffers (chunk c + 1 is written while chunk c is read) where they fit with the
+    // kept-state tile; otherwise one (fp32 records at d_k = 128, chunk 64: 117 KB each), and the
+    // next chunk is written after a second barrier per chunk, once every wave is done reading.
+    static constexpr bool SINGLE = 2 * (Rec::kBytes + kVBytes) + kKeepBytes > 160 * 1024;
+    // Copy waves: with two buffers, pairs that hold one chunk each in registers (two pairs take
+    // turns with 16-column compute waves, so each chunk's loads are issued two chunks ahead; a
+    // third pair measured no faster; the wider compute waves need every register of their SIMD and
+    // keep a single pair, one chunk ahead).  With one buffer, a group of four holds the next chunk.
+    static constexpr int NCW = SINGLE ? 4 : scan_copy_waves(SPW);
+    static constexpr int GROUP = SINGLE ? 4 : 2;  // copy waves that share one chunk
+    static constexpr int NT = 64 * (NW + NCW);  // threads (compute waves + copy waves)
+    static constexpr size_t oRec0 = 0;
+    static constexpr size_t oRec1 = SINGLE ? 0 : Rec::kBytes;
+    static constexpr size_t oV0 = (SINGLE ? 1 : 2) * Rec::kBytes;
+    static constexpr size_t oV1 = SINGLE ? oV0 : oV0 + kVBytes;
+    static constexpr size_t kBytes = oV1 + kVBytes;
+    static constexpr int UNITS_PER_WAVE = ((int)(Rec::kBytes / 1024) + V_PIECES / 64 + GROUP - 1) / GROUP;
+    static constexpr bool kFits = kBytes <= 160 * 1024 && UNITS_PER_WAVE <= 40 && (!SINGLE || SPW == 1);
+    static_assert(Rec::kBytes % (64 * 16) == 0, "record is copied in whole wave units");
+    static_assert(V_PIECES % 64 == 0, "V tile is copied in whole wave units");
     static constexpr bool kFitsKeep = kFits && kBytes + kKeepBytes <= 160 * 1024;
 };
 
-// One copy wave's half of a chunk's record and V tile (1 KB units dealt alternately to the two
-// waves of a pair).  The units are loaded into registers (16 bytes per lane, all in flight at
-// once) and later written to LDS; on gfx950 this moves about twice the bytes per cycle of the
-// direct global->LDS copy.  With SKIP_QP the Q~ and P sections, which only the output uses,
-// are not copied (their LDS stays stale and unread).
-template <typename IO, int DK, int C, int SPW, int NW, int HALF, bool SKIP_QP = false>
+// One copy wave's share of a chunk's record and V tile (1 KB units dealt in turn to the GROUP
+// waves that share a chunk; IDX is this wave's place in its group).  The units are loaded into
+// registers (16 bytes per lane, all in flight at once) and later written to LDS; on gfx950 this
+// moves about twice the bytes per cycle of the direct global->LDS copy.  With SKIP_QP the Q~ and
+// P sections, which only the output uses, are not copied (their LDS stays stale and unread).
+template <typename IO, int DK, int C, int SPW, int NW, int IDX, bool SKIP_QP = false>
 struct ChunkStager {
     using S = ScanLayout<IO, DK, C, SPW, NW>;
     using Rec = typename S::Rec;
@@ -594,7 +600,8 @@ struct ChunkStager {
         }
         return j;
     }
-    static constexpr int PER = (UNITS - HALF + 1) / 2;  // units of this wave
+    static constexpr int G = S::GROUP;
+    static constexpr int PER = (UNITS - IDX + G - 1) / G;  // units of this wave
     static constexpr int EP = 16 / (int)sizeof(IO);
     static constexpr int PPR = S::DVT / EP;  // 16-byte pieces per V row
     // A native vector type: HIP's uint4 is a union that the compiler leaves in scratch
@@ -604,7 +611,7 @@ struct ChunkStager {
     __device__ __forceinline__ void load(const char *rec, const IO *vrow0, int clen, int64_t vstride, int lane) {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int u = HALF + 2 * i;
+            const int u = IDX + G * i;
             if (u < USED) {
                 r[i] = *reinterpret_cast<const u32x4 *>(rec + (size_t)rec_unit(u) * 1024 + lane * 16);
             } else {
@@ -617,28 +624,42 @@ struct ChunkStager {
     __device__ __forceinline__ void store(char *lds_rec, char *lds_v, int lane) const {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int u = HALF + 2 * i;
+            const int u = IDX + G * i;
             char *dst = u < USED ? lds_rec + rec_unit(u) * 1024 : lds_v + (u - USED) * 1024;
             *reinterpret_cast<u32x4 *>(dst + lane * 16) = r[i];
         }
     }
 };
 
-// Copy wave CW.  Pair CW / 2 stages the chunks j with j % NPAIR == CW / 2.  Barrier c hands
-// chunk c to the compute waves; passing it also means every compute wave has finished chunk
-// c - 1, so that buffer may take chunk c + 1 (written from the registers of its pair, which
-// then load their next chunk).
+// Copy wave CW.  Group CW / GROUP stages the chunks j with j % NPAIR == CW / GROUP.  With two
+// buffers, barrier c hands chunk c to the compute waves; passing it also means every compute wave
+// has finished chunk c - 1, so that buffer may take chunk c + 1 (written from the registers of its
+// group, which then load their next chunk).  With one buffer every chunk has a second barrier,
+// after which every wave is done reading chunk c and chunk c + 1 (loaded while c was read) is
+// written.
 template <typename IO, int DK, int C, int SPW, int NW, int CW, bool SKIP_QP = false>
 __device__ __forceinline__ void copy_wave(char *smem, const char *rec0, size_t rec_stride, const IO *vbase,
                                           int64_t vstride, int len, int nchunks, int lane) {
     using S = ScanLayout<IO, DK, C, SPW, NW>;
-    constexpr int NPAIR = S::NCW / 2, PAIR = CW / 2;
-    ChunkStager<IO, DK, C, SPW, NW, CW % 2, SKIP_QP> st;
+    constexpr int NPAIR = S::NCW / S::GROUP, PAIR = CW / S::GROUP;
+    static_assert(!S::SINGLE || NPAIR == 1, "one buffer: one group of copy waves");
+    ChunkStager<IO, DK, C, SPW, NW, CW % S::GROUP, SKIP_QP> st;
 #define KDA_STAGE_LOAD(j) \
     st.load(rec0 + (size_t)(j) * rec_stride, vbase + (int64_t)(j) * C * vstride, min(C, len - (j) * C), vstride, lane)
 #define KDA_STAGE_STORE(j) \
     st.store(smem + (((j) & 1) ? S::oRec1 : S::oRec0), smem + (((j) & 1) ? S::oV1 : S::oV0), lane)
-    if constexpr (NPAIR == 1) {
+    if constexpr (S::SINGLE) {
+        if (nchunks > 0) {
+            KDA_STAGE_LOAD(0);
+            KDA_STAGE_STORE(0);
+        }
+        for (int c = 0; c < nchunks; ++c) {
+            __syncthreads();  // barrier c: chunk c is in LDS
+            if (c + 1 < nchunks) KDA_STAGE_LOAD(c + 1);
+            __syncthreads();  // every wave is done reading chunk c
+            if (c + 1 < nchunks) KDA_STAGE_STORE(c + 1);
+        }
+    } else if constexpr (NPAIR == 1) {
         if (nchunks > 0) {
             KDA_STAGE_LOAD(0);
             KDA_STAGE_STORE(0);
@@ -675,7 +696,7 @@ __device__ __forceinline__ void copy_wave(char *smem, const char *rec0, size_t r
 // no output (Q~ and P are neither staged nor used); a separate instantiation so the forward's
 // register allocation is not affected.
 template <typename IO, int DK, int C, int SPW, int NW, bool KEEP>
-__global__ void __launch_bounds__(64 * (NW + scan_copy_waves(SPW))) kda_scan_kernel(FwdParams p, const int32_t *__restrict__ chunk_off,
+__global__ void __launch_bounds__((ScanLayout<IO, DK, C, SPW, NW>::NT)) kda_scan_kernel(FwdParams p, const int32_t *__restrict__ chunk_off,
                                                                   const char *__restrict__ records) {
     using S = ScanLayout<IO, DK, C, SPW, NW>;
     using Rec = typename S::Rec;
@@ -903,6 +924,9 @@ __global__ void __launch_bounds__(64 * (NW + scan_copy_waves(SPW))) kda_scan_ker
 #pragma unroll
             for (int ct = 0; ct < KT; ++ct) gm[ct] = *reinterpret_cast<const float4 *>(gam + 16 * ct + 4 * q4);
         }
+        // one record buffer: the last read of this chunk's record is done; the copy waves may
+        // write the next chunk while the products below run
+        if constexpr (S::SINGLE) __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
         f32x4 M[SPW][KT];
 #pragma unroll
@@ -982,12 +1006,12 @@ struct ScanOwLayout {
     static constexpr size_t oSb = S::kBytes;                                     // [parity][wave][unit][lane]
     static constexpr size_t oDb = oSb + (size_t)2 * NW * SB_UNITS * 64 * 16;
     static constexpr size_t kBytes = oDb + (size_t)2 * NW * DB_UNITS * 64 * 16;
-    static constexpr bool kFits = S::kFits && kBytes <= 160 * 1024;
+    static constexpr bool kFits = S::kFits && !S::SINGLE && kBytes <= 160 * 1024;
     // KEEP: after the slots, one fp32 [KROWS][LDK] tile per writer wave (kept rows leave through
     // it): 64 rows where they fit, so a chunk's state and D leave in 3 read-backs, else 16
     static constexpr int KROWS = kBytes + (size_t)NW * 64 * S::LDK * 4 <= 160 * 1024 ? 64 : 16;
     static constexpr size_t kKeepBytes = (size_t)NW * KROWS * S::LDK * 4;
-    static constexpr bool kFitsKeep = S::kFits && kBytes + kKeepBytes <= 160 * 1024;
+    static constexpr bool kFitsKeep = S::kFits && !S::SINGLE && kBytes + kKeepBytes <= 160 * 1024;
     static_assert((Rec::KT * FB) % 16 == 0 && (2 * Rec::NPAIR * FB) % 16 == 0, "slot units");
 };
 
@@ -1020,7 +1044,7 @@ __device__ __forceinline__ void slot_get(const char *slot, int lane, Frag<BF> *f
 }
 
 template <typename IO, int DK, int C, int SPW, int NW, bool KEEP>
-__global__ void __launch_bounds__(64 * (2 * NW + scan_copy_waves(SPW))) kda_scan_ow_kernel(FwdParams p, const int32_t *__restrict__ chunk_off,
+__global__ void __launch_bounds__((ScanOwLayout<IO, DK, C, SPW, NW>::NT)) kda_scan_ow_kernel(FwdParams p, const int32_t *__restrict__ chunk_off,
                                                                      const char *__restrict__ records) {
     using S = ScanLayout<IO, DK, C, SPW, NW>;
     using SO = ScanOwLayout<IO, DK, C, SPW, NW>;

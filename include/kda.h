@@ -210,6 +210,28 @@ kda_status_t kda_decode_step(int32_t num_seqs, int32_t num_heads, int32_t head_d
                              int32_t io_dtype, float scale, const void *q, const void *k, const void *v,
                              const float *g, const float *beta, float *state, void *out, void *stream);
 
+/*
+ * kda_decode_step_gated -- kda_decode_step with the output epilogue applied in the same pass:
+ * the per-token update of the summary page's "Kimi Delta Attention" section, then the per-head
+ * RMSNorm and output gate of its "Kimi Linear model composition" section (no formula on the
+ * page; the reading, as for kda_norm_gate):
+ *
+ *     o   = scale S_t^T q_t                                   (one head, d_v values)
+ *     out = o / sqrt(mean_j o_j^2 + eps) * weight * sigmoid(gate)
+ *
+ *  q, k, g, v, beta, state as for kda_decode_step (state updated in place);
+ *  gate    [num_seqs, H, d_v] io dtype: the gate pre-activation of this token;
+ *  weight  [d_v] fp32, shared by the heads;  eps >= 0 and finite;
+ *  out     [num_seqs, H, d_v] io dtype: the gated, normalised output (o itself is not written).
+ *  Pointers are device memory, 16-byte aligned (beta 4-byte); state and out alias nothing.
+ *  One workgroup per (sequence, head) holds the whole state row block, so the norm needs no
+ *  second pass over o.  Errors as for kda_decode_step; num_seqs == 0 launches nothing.
+ */
+kda_status_t kda_decode_step_gated(int32_t num_seqs, int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v,
+                                   int32_t io_dtype, float scale, const void *q, const void *k, const void *v,
+                                   const float *g, const float *beta, float *state, const void *gate,
+                                   const float *weight, float eps, void *out, void *stream);
+
 /* Shape of a kda_prologue call (same batch / packed conventions as kda_problem_t). */
 typedef struct {
     int32_t batch;       /* B; must be 1 when num_seqs > 0 */

@@ -270,6 +270,21 @@ void decode_and_epilogue_validation() {
                            KDA_BF16, 1.f, q, k, v, g, beta, state, out, nullptr) == KDA_ERR_UNSUPPORTED);
     EXPECT(kda_decode_step(0, 32, 128, 128, KDA_BF16, 1.f, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                            nullptr, nullptr) == KDA_OK);
+    void *gate = dev(7);
+    float *w = devf(8);
+    EXPECT(kda_decode_step_gated(256, 32, 128, 128, 7, 1.f, q, k, v, g, beta, state, gate, w, 1e-6f, out, nullptr) ==
+           KDA_ERR_INVALID_ARGUMENT);
+    EXPECT(kda_decode_step_gated(256, 32, 128, 128, KDA_BF16, 1.f, q, k, v, g, beta, state, gate, w,
+                                 std::numeric_limits<float>::infinity(), out, nullptr) == KDA_ERR_INVALID_ARGUMENT);
+    EXPECT(kda_decode_step_gated(256, 32, 128, 128, KDA_BF16, 1.f, q, k, v, g, beta, state, nullptr, w, 1e-6f, out,
+                                 nullptr) == KDA_ERR_INVALID_ARGUMENT);
+    EXPECT(kda_decode_step_gated(256, 32, 128, 128, KDA_BF16, 1.f, q, k, v, g, beta, state, gate, w, 1e-6f, gate,
+                                 nullptr) == KDA_ERR_INVALID_ARGUMENT);
+    EXPECT(kda_decode_step_gated(std::numeric_limits<int32_t>::max(), std::numeric_limits<int32_t>::max(), 128, 128,
+                                 KDA_BF16, 1.f, q, k, v, g, beta, state, gate, w, 1e-6f, out, nullptr) ==
+           KDA_ERR_UNSUPPORTED);
+    EXPECT(kda_decode_step_gated(0, 32, 128, 128, KDA_BF16, 1.f, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                 nullptr, nullptr, 0.f, nullptr, nullptr) == KDA_OK);
     EXPECT(kda_norm_gate(-1, 128, KDA_BF16, 1e-6f, q, k, g, out, nullptr) == KDA_ERR_INVALID_ARGUMENT);
     EXPECT(kda_norm_gate(10, 96, KDA_BF16, 1e-6f, q, k, g, out, nullptr) == KDA_ERR_UNSUPPORTED);
     EXPECT(kda_norm_gate(10, 128, KDA_BF16, std::numeric_limits<float>::quiet_NaN(), q, k, g, out, nullptr) ==

@@ -72,7 +72,11 @@ def call_chunk(p, q=fake(0), k=fake(1), v=fake(2), g=fake(3), beta=fake(4), s0=N
     (dict(dv_tile=128), kda.KDA_ERR_INVALID_ARGUMENT),  # larger than d_v = 64
     (dict(io_dtype=7), kda.KDA_ERR_INVALID_ARGUMENT),
     (dict(scale=float("nan")), kda.KDA_ERR_INVALID_ARGUMENT),
-    (dict(io_dtype=kda.KDA_F32, head_dim_k=128, head_dim_v=128, chunk_size=64), kda.KDA_ERR_UNSUPPORTED),
+    # fp32 at d_k = 128, chunk 64 runs two-pass only (the fused kernel's LDS does not hold it):
+    # without a workspace the call is refused
+    (dict(io_dtype=kda.KDA_F32, head_dim_k=128, head_dim_v=128, chunk_size=64), kda.KDA_ERR_WORKSPACE),
+    (dict(io_dtype=kda.KDA_F32, head_dim_k=128, head_dim_v=128, chunk_size=64, algo=kda.KDA_ALGO_FUSED),
+     kda.KDA_ERR_UNSUPPORTED),
 ])
 def test_chunk_fwd_rejects_bad_problems(kw, status):
     assert call_chunk(problem(**kw)) == status
@@ -143,6 +147,30 @@ def test_decode_step_validation():
     assert f(*args(N=0)) == kda.KDA_OK
 
 
+def test_decode_step_gated_validation():
+    """Every refusal happens on the host, before any launch (no GPU needed)."""
+    lib = kda.library()
+    f = lambda *a: lib.kda_decode_step_gated(*a)
+    P = lambda i: ctypes.c_void_p(0x100000 * (i + 1))
+
+    def args(**kw):
+        return [kw.get("N", 4), kw.get("H", 2), kw.get("dk", 128), kw.get("dv", 128), kw.get("io", 1), 1.0,
+                P(0), P(1), P(2), P(3), P(4), kw.get("state", P(5)), kw.get("gate", P(6)), kw.get("weight", P(7)),
+                kw.get("eps", 1e-6), kw.get("out", P(8)), None]
+    assert f(*args(N=-1)) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert f(*args(dv=96)) == kda.KDA_ERR_UNSUPPORTED
+    assert f(*args(io=2)) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert f(*args(eps=-1.0)) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert f(*args(eps=float("nan"))) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert f(*args(gate=None)) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert "gate" in lib.kda_last_error().decode()
+    assert f(*args(weight=ctypes.c_void_p(0x800004))) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert f(*args(out=P(6))) == kda.KDA_ERR_INVALID_ARGUMENT   # out aliases gate
+    assert f(*args(state=P(7))) == kda.KDA_ERR_INVALID_ARGUMENT  # state aliases weight
+    assert f(*args(out=P(5))) == kda.KDA_ERR_INVALID_ARGUMENT   # out aliases state
+    assert f(*args(N=0)) == kda.KDA_OK
+
+
 def test_recurrent_validation():
     lib = kda.library()
     p = problem(head_dim_k=80)
@@ -178,8 +206,14 @@ def test_query_reports_config_and_work():
     assert r["lds_bytes"] == 2 * rec + 2 * 64 * 32 * 2 + 2 * 2 * 64 * (64 + 32)
     assert r["peak_hbm_gbps"] == 8000.0 and r["peak_bf16_tflops"] == 2500.0
     # unsupported variant is reported, not raised
-    r = kda.query(1, 64, 1, 128, 128, "f32", chunk_size=64)
+    r = kda.query(1, 64, 1, 128, 128, "f32", chunk_size=64, algo="fused")
     assert r["status"] == kda.KDA_ERR_UNSUPPORTED and r["supported"] == 0
+    # fp32, d_k = 128, chunk 64: two-pass with one record buffer (the 117 KB fp32 record does not
+    # fit twice): record + V tile [64][32] fp32, 2 compute + 4 copy waves
+    r = kda.query(1, 64, 1, 128, 128, "f32", chunk_size=64)
+    assert r["status"] == kda.KDA_OK and r["algo"] == kda.KDA_ALGO_TWO_PASS
+    rec32 = (3 * 32768 + 2 * 10240 + 512 + 1023) // 1024 * 1024
+    assert rec32 == 119808 and r["lds_bytes"] == rec32 + 64 * 32 * 4 and r["threads_per_block"] == 64 * 6
     # packed batch: num_seqs > 0, seq_len = total tokens
     r = kda.query(1, 1000, 32, 128, 128, "bf16", num_seqs=64)
     assert r["grid_blocks"] == 64 * 32 * (128 // r["dv_tile"])

@@ -189,7 +189,8 @@ def small(B, T, H, dk, dv, io, seed, **kw):
 
 @pytest.mark.parametrize("io,dk,dv,chunk", [("bf16", 128, 128, 64), ("bf16", 128, 128, 16), ("bf16", 128, 128, 32),
                                            ("bf16", 64, 128, 64), ("bf16", 128, 64, 32), ("f32", 64, 64, 64),
-                                           ("f32", 128, 128, 32), ("f32", 128, 64, 16)])
+                                           ("f32", 128, 128, 32), ("f32", 128, 64, 16), ("f32", 128, 128, 64),
+                                           ("f32", 128, 64, 64)])
 @pytest.mark.parametrize("algo", ALGOS)
 def test_ragged_lengths_and_dims(io, dk, dv, chunk, algo):
     # T = 203 is not a multiple of any chunk size: every sequence ends in a partial chunk
@@ -429,7 +430,7 @@ def test_side_stream_workspace():
 
 
 @pytest.mark.parametrize("io,dk,chunk", [("bf16", 128, 64), ("bf16", 128, 32), ("bf16", 128, 16), ("bf16", 64, 64),
-                                         ("f32", 64, 64), ("f32", 128, 32), ("f32", 64, 16)])
+                                         ("f32", 64, 64), ("f32", 128, 32), ("f32", 64, 16), ("f32", 128, 64)])
 @pytest.mark.parametrize("algo", ALGOS)
 def test_strong_decay_inside_a_chunk(io, dk, chunk, algo):
     """Channels that decay by e^-100 in one token, e^-20 per token over 40 tokens, e^-112 and
@@ -438,6 +439,14 @@ def test_strong_decay_inside_a_chunk(io, dk, chunk, algo):
     matrices switch to the split-level factors where a sub-chunk decays beyond 2^-96)."""
     inp = ki.plant_strong_decay(small(2, 203, 2, dk, 128, io, 51 + dk + chunk, s0_std=0.5))
     check_fwd(inp, chunk_size=chunk, label=f"strong-decay-{io}-d{dk}-c{chunk}", algo=algo)
+
+
+def test_fp32_dk128_chunk64_packed():
+    """fp32 at d_k = 128 with chunk 64: the two-pass scan with one record buffer (two barriers per
+    chunk), over a packed batch with an empty and a one-token sequence."""
+    inp = ki.make_inputs(1, 0, 3, 128, 128, "f32", 53, s0_std=0.5, lengths=[150, 1, 0, 64, 90, 200])
+    check_fwd(inp, chunk_size=64, label="f32-d128-c64 packed", algo="two_pass")
+    check_fwd(inp, chunk_size=64, dv_tile=32, label="f32-d128-c64 packed tile 32", algo="two_pass")
 
 
 def test_strong_decay_recurrent_and_packed():
