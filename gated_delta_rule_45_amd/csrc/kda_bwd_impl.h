@@ -201,22 +201,28 @@ __device__ __forceinline__ Frag<BF> bwd_turn(const Frag<BF> &a, const Frag<BF> &
     return frag_from_acc<BF>(t);
 }
 
+// One operand-type element as fp32.
+__device__ __forceinline__ float elem_f32(float x) { return x; }
+__device__ __forceinline__ float elem_f32(uint16_t x) { return bf16_to_f32(x); }
+
 // Diagonal-block terms of one sub-chunk for the gradient kernel, exact under any decay: the split
 // levels of kda_device.h (split_anchor), here in products that contract over the tokens.  The lane
 // holds token l16 of the sub-chunk and channels 4*q4 + j of its wave's 16: raw k and q (kk, qq) and
 // the in-sub-chunk cumulative log2 gate G.  P, A (rows r) and PT, LT (rows i) point at the
-// sub-chunk's diagonal 16 x 16 tiles of dP, dA, dP^T and dL^T (row stride LDC):
+// sub-chunk's diagonal 16 x 16 tiles of dP, dA, dP^T and dL^T (row stride LDC); without TRANS
+// there are no transposed tiles and the column side gathers dP^T and dL^T = (beta_r dA)^T from
+// the columns of P and A, with beta the sub-chunk's 16 betas:
 //   ROW: rowP[j] += sum_{i <= r} k_i dP_ri e^{G_r - G_i},  rowA[j] += sum_{i < r} k_i dA_ri e^{G_r - G_i}
 //        (r the lane's token)
 //   COL: col[j]  += sum_{r >= i} (q_r dP_ri + k_r dL_ri) e^{G_r - G_i}  (i the lane's token)
 // Per level, the tiles are masked to the pairs with both tokens in one block, the row-side token in
 // its second half and the column-side token in its first half, and the token operands carry
 // e^{-|G - a|} <= 1 (a the level's anchor); the diagonal pairs (factor 1) are added apart.
-template <bool BF, bool ROW, bool COL, typename OT>
+template <bool BF, bool ROW, bool COL, bool TRANS, typename OT>
 __device__ __forceinline__ void grad_diag_split(f32x4 &rowP, f32x4 &rowA, f32x4 &col, const float (&kk)[4],
                                                 const float (&qq)[4], const float (&G)[4], const OT *P, const OT *A,
-                                                const OT *PT, const OT *LT, int LDC, const Frag<BF> &eye, int l16,
-                                                int q4, int lane) {
+                                                const OT *PT, const OT *LT, const float *beta, int LDC,
+                                                const Frag<BF> &eye, int l16, int q4, int lane) {
     // the level loop stays rolled (anchors by lane shuffle): the common path of this kernel uses
     // every register, and an unrolled rare path would add code and temporaries to it
 #pragma unroll 1
@@ -228,9 +234,7 @@ __device__ __forceinline__ void grad_diag_split(f32x4 &rowP, f32x4 &rowA, f32x4 
         for (int j = 0; j < 4; ++j) f[j] = fast_exp2(-fabsf(G[j] - __shfl(G[j], src)));
         // B fragment of tokens x = 4*q4 + j (contracted) against the lane's token l16: keep x where
         // both lie in one block and the lane's token is in the half `lane_second`, x in the other
-        auto masked = [&](const OT *t, bool lane_second) {
-            const float4 v = unpack4<BF>(lds_frag(t + l16 * LDC + 4 * q4).v);
-            const float x[4] = {v.x, v.y, v.z, v.w};
+        auto masked_vals = [&](const float (&x)[4], bool lane_second) {
             float o[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -240,6 +244,32 @@ __device__ __forceinline__ void grad_diag_split(f32x4 &rowP, f32x4 &rowA, f32x4 
                 o[j] = (same && lane_sec == lane_second && x_sec != lane_second) ? x[j] : 0.f;
             }
             return make_frag<BF>(o[0], o[1], o[2], o[3]);
+        };
+        auto masked = [&](const OT *t, bool lane_second) {  // rows of t: tile element [l16][4 q4 + j]
+            const float4 v = unpack4<BF>(lds_frag(t + l16 * LDC + 4 * q4).v);
+            const float x[4] = {v.x, v.y, v.z, v.w};
+            return masked_vals(x, lane_second);
+        };
+        // the transposed tiles' element [l16][4 q4 + j] from the columns of P and A
+        auto masked_pt = [&](bool lane_second) {
+            if constexpr (TRANS) {
+                return masked(PT, lane_second);
+            } else {
+                float x[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) x[j] = elem_f32(P[(4 * q4 + j) * LDC + l16]);
+                return masked_vals(x, lane_second);
+            }
+        };
+        auto masked_lt = [&](bool lane_second) {
+            if constexpr (TRANS) {
+                return masked(LT, lane_second);
+            } else {
+                float x[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) x[j] = beta[4 * q4 + j] * elem_f32(A[(4 * q4 + j) * LDC + l16]);
+                return masked_vals(x, lane_second);
+            }
         };
         const Frag<BF> kT = bwd_turn<BF>(make_frag<BF>(kk[0] * f[0], kk[1] * f[1], kk[2] * f[2], kk[3] * f[3]), eye);
         if constexpr (ROW) {
@@ -257,8 +287,8 @@ __device__ __forceinline__ void grad_diag_split(f32x4 &rowP, f32x4 &rowA, f32x4 
             const Frag<BF> qT =
                 bwd_turn<BF>(make_frag<BF>(qq[0] * f[0], qq[1] * f[1], qq[2] * f[2], qq[3] * f[3]), eye);
             f32x4 tc = zero4();
-            mma16(tc, qT, masked(PT, false));
-            mma16(tc, kT, masked(LT, false));
+            mma16(tc, qT, masked_pt(false));
+            mma16(tc, kT, masked_lt(false));
             mfma_settle(tc);
 #pragma unroll
             for (int j = 0; j < 4; ++j) col[j] += f[j] * tc[j];
@@ -631,29 +661,37 @@ struct BwdScanLayout {
     static_assert(sizeof(IO) == sizeof(OT), "operand type follows the io type");
     static constexpr int LDH = 16 + 4;  // per-wave fp32 [DK][LDH] tile that turns dS around for its stores
     static constexpr size_t kVBytes = (size_t)C * LDV * S;
+    static constexpr size_t kHBytes = (size_t)NW * DK * LDH * 4;
+    // Two record buffers where they fit, else one (fp32 records at d_k = 128, chunk 64: 119 KB):
+    // then each chunk has a second barrier, after which the copy waves write the next one.
+    static constexpr bool SINGLE = 2 * (Rec::kBytes + kVBytes) + kHBytes > 160 * 1024;
+    static constexpr int GROUP = SINGLE ? NCW : 2;  // copy waves that share one chunk
     static constexpr size_t oRec0 = 0;
-    static constexpr size_t oRec1 = Rec::kBytes;
-    static constexpr size_t oV0 = 2 * Rec::kBytes;
-    static constexpr size_t oV1 = oV0 + kVBytes;
+    static constexpr size_t oRec1 = SINGLE ? 0 : Rec::kBytes;
+    static constexpr size_t oV0 = (SINGLE ? 1 : 2) * Rec::kBytes;
+    static constexpr size_t oV1 = SINGLE ? oV0 : oV0 + kVBytes;
     static constexpr size_t oH = oV1 + kVBytes;
-    static constexpr size_t kBytes = oH + (size_t)NW * DK * LDH * 4;
-    static constexpr bool kFits = kBytes <= 160 * 1024;
+    static constexpr size_t kBytes = oH + kHBytes;
+    static constexpr int UNITS_PER_WAVE = (REC_UNITS + V_UNITS + GROUP - 1) / GROUP;
+    static constexpr bool kFits = kBytes <= 160 * 1024 && UNITS_PER_WAVE <= 40;
 };
 
-// One copy wave's half of a chunk (record units and dO pieces dealt alternately to the two
-// waves of a pair), held in registers between its loads and its LDS writes.
-template <typename IO, int DK, int C, int HALF>
+// One copy wave's share of a chunk (record units and dO pieces dealt in turn to the GROUP waves
+// that share a chunk; IDX is this wave's place among them), held in registers between its loads
+// and its LDS writes.
+template <typename IO, int DK, int C, int IDX>
 struct BwdStager {
     using L = BwdScanLayout<IO, DK, C>;
     using OT = typename L::OT;
     static constexpr int UNITS = L::REC_UNITS + L::V_UNITS;
-    static constexpr int PER = (UNITS - HALF + 1) / 2;
+    static constexpr int G = L::GROUP;
+    static constexpr int PER = (UNITS - IDX + G - 1) / G;
     u32x4 r[PER];
 
     __device__ __forceinline__ void load(const char *rec, const IO *orow0, int clen, int64_t ostride, int lane) {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int u = HALF + 2 * i;
+            const int u = IDX + G * i;
             if (u < L::REC_UNITS) {
                 r[i] = *reinterpret_cast<const u32x4 *>(rec + (size_t)u * 1024 + lane * 16);
             } else {
@@ -666,7 +704,7 @@ struct BwdStager {
     __device__ __forceinline__ void store(char *lds_rec, OT *lds_o, int lane) const {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int u = HALF + 2 * i;
+            const int u = IDX + G * i;
             if (u < L::REC_UNITS) {
                 *reinterpret_cast<u32x4 *>(lds_rec + u * 1024 + lane * 16) = r[i];
             } else {
@@ -677,17 +715,19 @@ struct BwdStager {
     }
 };
 
-// Copy wave CW.  Stream element j is chunk nchunks - 1 - j.  Pair CW / 2 stages the elements
-// with j % 2 == CW / 2.  Barrier j hands element j to the compute waves; passing it also means
-// that both compute waves are done with element j - 1, whose buffer may take element j + 1.
+// Copy wave CW.  Stream element j is chunk nchunks - 1 - j.  With two buffers, pair CW / 2
+// stages the elements with j % 2 == CW / 2; barrier j hands element j to the compute waves, and
+// passing it also means that both compute waves are done with element j - 1, whose buffer may take
+// element j + 1.  With one buffer the four copy waves load element j + 1 after barrier j and
+// write it after the second barrier of element j, when the compute waves are done reading.
 template <typename IO, int DK, int C, int CW>
 __device__ __forceinline__ void bwd_copy_wave(char *smem, const char *records, int64_t slot0, int H, int h,
                                               const IO *obase, int64_t ostride, int len, int nchunks, int lane) {
     using L = BwdScanLayout<IO, DK, C>;
     using Rec = typename L::Rec;
     using OT = typename L::OT;
-    constexpr int NPAIR = L::NCW / 2, PAIR = CW / 2;
-    BwdStager<IO, DK, C, CW % 2> st;
+    constexpr int NPAIR = L::NCW / L::GROUP, PAIR = CW / L::GROUP;
+    BwdStager<IO, DK, C, CW % L::GROUP> st;
     auto load = [&](int j) {
         const int c = nchunks - 1 - j;
         st.load(records + (size_t)((slot0 + c) * H + h) * Rec::kBytes, obase + (int64_t)c * C * ostride,
@@ -697,18 +737,31 @@ __device__ __forceinline__ void bwd_copy_wave(char *smem, const char *records, i
         st.store(smem + ((j & 1) ? L::oRec1 : L::oRec0), reinterpret_cast<OT *>(smem + ((j & 1) ? L::oV1 : L::oV0)),
                  lane);
     };
-    if (PAIR < nchunks) {
-        load(PAIR);
-        if (PAIR == 0) {
+    if constexpr (L::SINGLE) {
+        if (nchunks > 0) {
+            load(0);
             store(0);
-            if (NPAIR < nchunks) load(NPAIR);
         }
-    }
-    for (int j = 0; j < nchunks; ++j) {
-        __syncthreads();  // barrier j: the buffer of element j + 1 is free
-        if ((j + 1) % NPAIR == PAIR && j + 1 < nchunks) {
-            store(j + 1);
-            if (j + 1 + NPAIR < nchunks) load(j + 1 + NPAIR);
+        for (int j = 0; j < nchunks; ++j) {
+            __syncthreads();  // barrier j: element j is in the buffer
+            if (j + 1 < nchunks) load(j + 1);
+            __syncthreads();  // the compute waves are done reading element j
+            if (j + 1 < nchunks) store(j + 1);
+        }
+    } else {
+        if (PAIR < nchunks) {
+            load(PAIR);
+            if (PAIR == 0) {
+                store(0);
+                if (NPAIR < nchunks) load(NPAIR);
+            }
+        }
+        for (int j = 0; j < nchunks; ++j) {
+            __syncthreads();  // barrier j: the buffer of element j + 1 is free
+            if ((j + 1) % NPAIR == PAIR && j + 1 < nchunks) {
+                store(j + 1);
+                if (j + 1 + NPAIR < nchunks) load(j + 1 + NPAIR);
+            }
         }
     }
 }
@@ -836,6 +889,9 @@ __global__ void __launch_bounds__(kBwdScanThreads) kda_bwd_scan_kernel(BwdParams
             for (int I = R & ~1; I + 1 < NSUB; I += 2)
                 mma32(z, dOf[I], dOf[I + 1], lds_frag(nr + 16 * I), lds_frag(nr + 16 * I + 16));
             if constexpr (NSUB % 2 == 1) mma16(z, dOf[NSUB - 1], lds_frag(nr + 16 * (NSUB - 1)));
+            // fp32: the dv store branches below put joins between these products and later writes
+            // of their registers, where the compiler leaves too few wait states
+            if constexpr (!BF) mfma_settle(z);
             dUt[R] = z;
         }
 
@@ -856,6 +912,9 @@ __global__ void __launch_bounds__(kBwdScanThreads) kda_bwd_scan_kernel(BwdParams
                 *reinterpret_cast<decltype(u.v) *>(du + (int64_t)r * DV) = u.v;
                 f32x4 t = zero4();
                 mma16(t, make_frag<BF>(-dUt[R][0], -dUt[R][1], -dUt[R][2], -dUt[R][3]), ident);
+                // fp32: the next tile's store branch puts a join between these products and a later
+                // write of their registers, where the compiler leaves too few wait states
+                if constexpr (!BF) mfma_settle(t);
                 nU[R] = frag_from_acc<BF>(t);
             }
         }
@@ -880,6 +939,7 @@ __global__ void __launch_bounds__(kBwdScanThreads) kda_bwd_scan_kernel(BwdParams
                 mma16(dS[ct], lds_frag(kt + 16 * (NSUB - 1)), nU[NSUB - 1]);
             }
         }
+        if constexpr (L::SINGLE) __syncthreads();  // one buffer: done reading this element
     }
 
     if (bp.ds0) {
@@ -912,14 +972,19 @@ struct BwdGradLayout {
 
     static constexpr size_t kTile = (size_t)C * LDV * sizeof(OT);
     static constexpr size_t kBlk = (size_t)C * LDC * sizeof(OT);
+    static constexpr size_t kSmall = (size_t)C * 4 * 2 + (size_t)DK * 4 + (size_t)NW * C * 4;
+    // The transposed blocks dP^T and dL^T are kept where they fit (one wide read per fragment);
+    // otherwise (fp32 at d_k = d_v = 128, chunk 64) their fragments are gathered from the
+    // columns of dP and dA (dL = beta_r dA).
+    static constexpr bool TRANS = 3 * kTile + 4 * kBlk + kSmall <= 160 * 1024;
     static constexpr size_t oO = 0;
     static constexpr size_t oU = oO + kTile;
     static constexpr size_t oD = oU + kTile;
-    static constexpr size_t oP = oD + kTile;    // dP   [r][i]
-    static constexpr size_t oPT = oP + kBlk;    // dP   [i][r]
-    static constexpr size_t oA = oPT + kBlk;    // dA   [r][i]
-    static constexpr size_t oLT = oA + kBlk;    // dL   [i][r]  (dL = beta_r dA)
-    static constexpr size_t oBeta = oLT + kBlk;
+    static constexpr size_t oP = oD + kTile;                     // dP   [r][i]
+    static constexpr size_t oPT = oP + kBlk;                     // dP   [i][r]  (TRANS)
+    static constexpr size_t oA = oPT + (TRANS ? kBlk : 0);       // dA   [r][i]
+    static constexpr size_t oLT = oA + kBlk;                     // dL   [i][r]  (TRANS; dL = beta_r dA)
+    static constexpr size_t oBeta = oLT + (TRANS ? kBlk : 0);
     static constexpr size_t oUV = oBeta + (size_t)C * 4;
     static constexpr size_t oGam = oUV + (size_t)C * 4;
     static constexpr size_t oDb = oGam + (size_t)DK * 4;
@@ -1092,10 +1157,14 @@ __global__ void __launch_bounds__(64 * (DK / 16)) kda_bwd_grad_kernel(BwdParams 
                 sA[r * LDC + 16 * I + l16] = va[j];
             }
         }
-        const Frag<BF> fp = make_frag<BF>(vp[0], vp[1], vp[2], vp[3]);
-        const Frag<BF> fl = make_frag<BF>(vl[0], vl[1], vl[2], vl[3]);
-        *reinterpret_cast<decltype(fp.v) *>(sPT + (16 * I + l16) * LDC + 16 * R + 4 * q4) = fp.v;
-        *reinterpret_cast<decltype(fl.v) *>(sLT + (16 * I + l16) * LDC + 16 * R + 4 * q4) = fl.v;
+        if constexpr (L::TRANS) {
+            const Frag<BF> fp = make_frag<BF>(vp[0], vp[1], vp[2], vp[3]);
+            const Frag<BF> fl = make_frag<BF>(vl[0], vl[1], vl[2], vl[3]);
+            *reinterpret_cast<decltype(fp.v) *>(sPT + (16 * I + l16) * LDC + 16 * R + 4 * q4) = fp.v;
+            *reinterpret_cast<decltype(fl.v) *>(sLT + (16 * I + l16) * LDC + 16 * R + 4 * q4) = fl.v;
+        } else {
+            (void)vl;
+        }
     }
 
     // ---- rows c = cw + l16 of S and dS (A operands straight from the chunk states), rowsum(dS .* S),
@@ -1179,6 +1248,25 @@ __global__ void __launch_bounds__(64 * (DK / 16)) kda_bwd_grad_kernel(BwdParams 
             if constexpr (SPLIT) mfma_settle(t);
             qrT[R] = frag_from_acc<BF>(t);
         }
+        // fragments of dP^T and dL^T (row i, the 4 columns r .. r + 3): read whole from their own
+        // blocks, or gathered from the columns of dP and dA (dL = beta_r dA)
+        auto pt_frag = [&](int i, int r) {
+            if constexpr (L::TRANS) {
+                return lds_frag(sPT + i * LDC + r);
+            } else {
+                return make_frag<BF>(elem_f32(sP[r * LDC + i]), elem_f32(sP[(r + 1) * LDC + i]),
+                                     elem_f32(sP[(r + 2) * LDC + i]), elem_f32(sP[(r + 3) * LDC + i]));
+            }
+        };
+        auto lt_frag = [&](int i, int r) {
+            if constexpr (L::TRANS) {
+                return lds_frag(sLT + i * LDC + r);
+            } else {
+                return make_frag<BF>(sBeta[r] * elem_f32(sA[r * LDC + i]), sBeta[r + 1] * elem_f32(sA[(r + 1) * LDC + i]),
+                                     sBeta[r + 2] * elem_f32(sA[(r + 2) * LDC + i]),
+                                     sBeta[r + 3] * elem_f32(sA[(r + 3) * LDC + i]));
+            }
+        };
         f32x4 Col[NSUB];
 #pragma unroll
         for (int I = 0; I < NSUB; ++I) Col[I] = zero4();
@@ -1188,8 +1276,8 @@ __global__ void __launch_bounds__(64 * (DK / 16)) kda_bwd_grad_kernel(BwdParams 
             for (int I = 0; I <= R; ++I) {
                 if (I == R && split[R]) continue;  // the diagonal block comes from the split levels below
                 f32x4 tc = zero4();
-                mma16(tc, qrT[R], lds_frag(sPT + (16 * I + l16) * LDC + 16 * R + 4 * q4));
-                mma16(tc, krT[R], lds_frag(sLT + (16 * I + l16) * LDC + 16 * R + 4 * q4));
+                mma16(tc, qrT[R], pt_frag(16 * I + l16, 16 * R + 4 * q4));
+                mma16(tc, krT[R], lt_frag(16 * I + l16, 16 * R + 4 * q4));
 #pragma unroll
                 for (int j = 0; j < 4; ++j) Col[I][j] += fast_exp2(bnd[R][j] - bnd[I + 1][j]) * tc[j];
             }
@@ -1203,9 +1291,10 @@ __global__ void __launch_bounds__(64 * (DK / 16)) kda_bwd_grad_kernel(BwdParams 
                 float qq[4];
                 unpk(qraw[R], qq);
                 f32x4 unused = zero4();
-                grad_diag_split<BF, false, true>(unused, unused, colD, kk, qq, G[R], sP + 16 * R * LDC + 16 * R,
-                                                 sA + 16 * R * LDC + 16 * R, sPT + 16 * R * LDC + 16 * R,
-                                                 sLT + 16 * R * LDC + 16 * R, LDC, eye, l16, q4, lane);
+                grad_diag_split<BF, false, true, L::TRANS>(unused, unused, colD, kk, qq, G[R],
+                                                           sP + 16 * R * LDC + 16 * R, sA + 16 * R * LDC + 16 * R,
+                                                           sPT + 16 * R * LDC + 16 * R, sLT + 16 * R * LDC + 16 * R,
+                                                           sBeta + 16 * R, LDC, eye, l16, q4, lane);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -1243,9 +1332,10 @@ __global__ void __launch_bounds__(64 * (DK / 16)) kda_bwd_grad_kernel(BwdParams 
             unpk(kraw[R], kk);
             unpk(qraw[R], qq);
             f32x4 unused = zero4();
-            grad_diag_split<BF, true, false>(RowPD, RowAD, unused, kk, qq, G[R], sP + 16 * R * LDC + 16 * R,
-                                             sA + 16 * R * LDC + 16 * R, sPT + 16 * R * LDC + 16 * R,
-                                             sLT + 16 * R * LDC + 16 * R, LDC, eye, l16, q4, lane);
+            grad_diag_split<BF, true, false, L::TRANS>(RowPD, RowAD, unused, kk, qq, G[R],
+                                                       sP + 16 * R * LDC + 16 * R, sA + 16 * R * LDC + 16 * R,
+                                                       sPT + 16 * R * LDC + 16 * R, sLT + 16 * R * LDC + 16 * R,
+                                                       sBeta + 16 * R, LDC, eye, l16, q4, lane);
         }
 #pragma unroll
         for (int I = 0; I <= R; ++I) {

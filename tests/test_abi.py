@@ -355,8 +355,13 @@ def test_bwd_validation():
     assert call(ptrs, ws=P(0x100010)) == kda.KDA_ERR_WORKSPACE  # misaligned
     assert call(ptrs, prob=_bwd_problem(head_dim_k=96)) == kda.KDA_ERR_UNSUPPORTED
     assert call(ptrs, prob=_bwd_problem(chunk_size=128)) == kda.KDA_ERR_UNSUPPORTED
-    # fp32 at chunk 64 with d = 128 does not fit the LDS budget
-    assert call(ptrs, prob=_bwd_problem(io_dtype=kda.KDA_F32)) == kda.KDA_ERR_UNSUPPORTED
+    # fp32 at chunk 64 with d = 128 is supported (one record buffer in the reverse scan, dP^T and
+    # dL^T gathered in the gradient kernel): its workspace is reported, and a call with a smaller
+    # one is refused before anything is launched
+    n = ctypes.c_size_t(0)
+    p32 = _bwd_problem(io_dtype=kda.KDA_F32)
+    assert lib.kda_chunk_bwd_workspace(ctypes.byref(p32), ctypes.byref(n)) == kda.KDA_OK and n.value > 0
+    assert call(ptrs, prob=p32, ws_bytes=n.value - 256) == kda.KDA_ERR_WORKSPACE
     # empty batch: nothing to do
     assert call(ptrs, prob=_bwd_problem(batch=0)) == kda.KDA_OK
 

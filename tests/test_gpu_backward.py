@@ -78,7 +78,7 @@ def skip_unsupported(inp, chunk):
         raise
 
 
-@pytest.mark.parametrize("chunk", [16, 32])
+@pytest.mark.parametrize("chunk", [16, 32, 64])
 def test_bwd_fp32_small(chunk):
     inp = ki.make_inputs(2, 50, 2, 64, 64, "f32", seed=21, s0_std=0.5)
     check_bwd(inp, chunk=chunk, scale=0.7, label=f"fp32 d64 c{chunk}")
@@ -142,11 +142,18 @@ def test_bwd_repeatable(dk, chunk):
         assert torch.equal(a[key], b[key]), key
 
 
-@pytest.mark.parametrize("chunk", [16, 32])
+@pytest.mark.parametrize("chunk", [16, 32, 64])
 def test_bwd_fp32_packed_sequences(chunk):
     """fp32 packed batch with an empty, a single-token and a ragged sequence."""
     inp = ki.make_inputs(1, 0, 2, 64, 64, "f32", seed=35, s0_std=0.1, lengths=[33, 1, 0, 47])
     check_bwd(inp, chunk=chunk, label=f"fp32 packed c{chunk}")
+
+
+def test_bwd_fp32_dk128_chunk64_packed():
+    """fp32 at d_k = d_v = 128, chunk 64 (one record buffer in the reverse scan, dP^T and dL^T
+    gathered from dP and dA in the gradient kernel) over a packed batch."""
+    inp = ki.make_inputs(1, 0, 2, 128, 128, "f32", seed=36, s0_std=0.3, lengths=[70, 1, 0, 129, 64])
+    check_bwd(inp, chunk=64, label="fp32 d128 packed c64")
 
 
 def test_bwd_side_stream_workspace():
@@ -173,7 +180,7 @@ def test_bwd_side_stream_workspace():
 
 
 @pytest.mark.parametrize("io,dk,chunk", [("bf16", 128, 64), ("bf16", 128, 16), ("bf16", 64, 32), ("f32", 64, 16),
-                                         ("f32", 64, 32)])
+                                         ("f32", 64, 32), ("f32", 128, 64), ("f32", 64, 64)])
 def test_bwd_strong_decay_inside_a_chunk(io, dk, chunk):
     """Gradients under the stress gates of kda_inputs.plant_strong_decay (decay of e^-100 in one
     token, e^-112 per sub-chunk, ...): finite and within the bars."""
