@@ -424,6 +424,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(pre_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(pre_gbps / PEAK_HBM_GBPS, 4),
                      "traffic": traffic.get("prefill_bytes") if q["algo"] == 2 else None,
+                     "frac_measured": None if q["algo"] != 2 or traffic.get("prefill_bytes") is None else
+                     round(traffic["prefill_bytes"] / (t_pre * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
                      "kernel": "kda_chunk_fwd (" + ["auto", "fused", "two_pass"][q["algo"]] + ")",
                      "launch_ms": round(t_pre, 4),
                      "bytes_per_launch": pre_bytes},

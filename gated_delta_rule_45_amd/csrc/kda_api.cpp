@@ -106,8 +106,8 @@ kda_status_t check_problem(const kda_problem_t *p, Resolved &r, bool chunked) {
     if (chunked) {
         if (p->chunk_size != 0 && p->chunk_size != 16 && p->chunk_size != 32 && p->chunk_size != 64)
             return fail(KDA_ERR_UNSUPPORTED, "chunk_size %d: supported are 16, 32, 64 (0 = default)", p->chunk_size);
-        if (p->dv_tile != 0 && p->dv_tile != 32 && p->dv_tile != 64 && p->dv_tile != 128)
-            return fail(KDA_ERR_UNSUPPORTED, "dv_tile %d: supported are 32, 64, 128 (0 = default)", p->dv_tile);
+        if (p->dv_tile != 0 && p->dv_tile != 16 && p->dv_tile != 32 && p->dv_tile != 64 && p->dv_tile != 128)
+            return fail(KDA_ERR_UNSUPPORTED, "dv_tile %d: supported are 16, 32, 64, 128 (0 = default)", p->dv_tile);
         if (p->dv_tile > p->head_dim_v)
             return fail(KDA_ERR_INVALID_ARGUMENT, "dv_tile %d exceeds d_v %d", p->dv_tile, p->head_dim_v);
         if (p->algo != KDA_ALGO_AUTO && p->algo != KDA_ALGO_FUSED && p->algo != KDA_ALGO_TWO_PASS)
@@ -139,15 +139,20 @@ kda_status_t resolve(const kda_problem_t *p, bool varlen, Resolved &r, bool chun
         r.cfg.dv_tile = p->dv_tile ? p->dv_tile : default_dv_tile((int64_t)r.num_seqs * p->num_heads, p->head_dim_v);
         r.lds = kda::chunk_variant_lds_bytes(dtype_of(p->io_dtype), p->head_dim_k, r.cfg.dv_tile, r.cfg.chunk);
         // two-pass: scan workgroups of two compute waves, each owning 16 (32-column tiles) or 32
-        // (64-column tiles) state columns.  By default 64-column tiles once they still give every CU
-        // two workgroups: each record is then staged half as often (measured on 64 packed
-        // sequences x 32 heads: 7.01 vs 8.71 ms); otherwise 32-column tiles, for parallelism.
-        int scan_cols = p->dv_tile == 64 ? 64 : 32;
+        // (64-column tiles) state columns, or of one 16-column wave.  By default 64-column tiles
+        // once they still give every CU two workgroups: each record is then staged half as often
+        // (measured on 64 packed sequences x 32 heads: 7.01 vs 8.71 ms, and 5.78 vs 6.62 ms with
+        // 16-column tiles at 9.1 ms); 16-column tiles where 32-column ones leave CUs idle (one
+        // 131,072-token sequence x 32 heads: 4.37 vs 4.52 ms); otherwise 32-column tiles.
+        int scan_cols = p->dv_tile == 64 ? 64 : p->dv_tile == 16 ? 16 : 32;
         if (p->dv_tile == 0 && p->head_dim_v >= 64 && chains * (p->head_dim_v / 64) >= 2 * kAssumedCUs &&
             kda::split_variant_supported(dtype_of(p->io_dtype), p->head_dim_k, C, 2, 2))
             scan_cols = 64;
-        r.spw = scan_cols == 32 ? 1 : 2;
-        r.nw = 2;
+        else if (p->dv_tile == 0 && chains * (p->head_dim_v / 32) < kAssumedCUs &&
+                 kda::split_variant_supported(dtype_of(p->io_dtype), p->head_dim_k, C, 1, 1))
+            scan_cols = 16;
+        r.spw = scan_cols == 64 ? 2 : 1;
+        r.nw = scan_cols == 16 ? 1 : 2;
         r.two_pass_ok = p->dv_tile != 128 && scan_cols <= p->head_dim_v &&
                         kda::split_variant_supported(dtype_of(p->io_dtype), p->head_dim_k, C, r.spw, r.nw);
         if (r.two_pass_ok) {
@@ -592,7 +597,7 @@ kda_status_t kda_tune(const kda_problem_t *problem, const void *q, const void *k
             if (e0) (void)hipEventDestroy(e0);
             return fail(KDA_ERR_HIP, "hipEventCreate failed");
         }
-        const int chunks[3] = {16, 32, 64}, tiles[3] = {32, 64, 128}, algos[2] = {KDA_ALGO_FUSED, KDA_ALGO_TWO_PASS};
+        const int chunks[3] = {16, 32, 64}, tiles[4] = {16, 32, 64, 128}, algos[2] = {KDA_ALGO_FUSED, KDA_ALGO_TWO_PASS};
         kda_problem_t winner{};
         float best_ms = -1.f;
         kda_status_t err = KDA_OK;
@@ -600,7 +605,7 @@ kda_status_t kda_tune(const kda_problem_t *problem, const void *q, const void *k
             if (problem->chunk_size && chunks[ci] != problem->chunk_size) continue;
             for (int ai = 0; ai < 2 && err == KDA_OK; ++ai) {
                 if (problem->algo != KDA_ALGO_AUTO && algos[ai] != problem->algo) continue;
-                for (int ti = 0; ti < 3 && err == KDA_OK; ++ti) {
+                for (int ti = 0; ti < 4 && err == KDA_OK; ++ti) {
                     if (problem->dv_tile && tiles[ti] != problem->dv_tile) continue;
                     kda_problem_t c = *problem;
                     c.chunk_size = chunks[ci];

@@ -570,9 +570,10 @@ struct ScanLayout {
     static constexpr size_t oV1 = SINGLE ? oV0 : oV0 + kVBytes;
     static constexpr size_t kBytes = oV1 + kVBytes;
     static constexpr int UNITS_PER_WAVE = ((int)(Rec::kBytes / 1024) + V_PIECES / 64 + GROUP - 1) / GROUP;
-    static constexpr bool kFits = kBytes <= 160 * 1024 && UNITS_PER_WAVE <= 40 && (!SINGLE || SPW == 1);
+    // (the V tile is copied in whole wave units: a 16-column bf16 tile needs C >= 32)
+    static constexpr bool kFits = kBytes <= 160 * 1024 && UNITS_PER_WAVE <= 40 && (!SINGLE || SPW == 1) &&
+                                  V_PIECES % 64 == 0;
     static_assert(Rec::kBytes % (64 * 16) == 0, "record is copied in whole wave units");
-    static_assert(V_PIECES % 64 == 0, "V tile is copied in whole wave units");
     static constexpr bool kFitsKeep = kFits && kBytes + kKeepBytes <= 160 * 1024;
 };
 
@@ -1434,7 +1435,7 @@ hipError_t launch_split_variant(const FwdParams &params, char *workspace, int64_
 }
 
 // F(DK, C, SPW, NW): NW compute waves of 16 * SPW state columns each (d_v tile 16 * SPW * NW)
-#define KDA_SPLIT_SHAPES(F, DK_, C_) F(DK_, C_, 1, 2) F(DK_, C_, 2, 2)
+#define KDA_SPLIT_SHAPES(F, DK_, C_) F(DK_, C_, 1, 1) F(DK_, C_, 1, 2) F(DK_, C_, 2, 2)
 #define KDA_SPLIT_VARIANTS(F)                                                                          \
     KDA_SPLIT_SHAPES(F, 64, 16) KDA_SPLIT_SHAPES(F, 64, 32) KDA_SPLIT_SHAPES(F, 64, 64)                \
     KDA_SPLIT_SHAPES(F, 128, 16) KDA_SPLIT_SHAPES(F, 128, 32) KDA_SPLIT_SHAPES(F, 128, 64)

@@ -210,10 +210,14 @@ def test_query_reports_config_and_work():
     assert r["status"] == kda.KDA_ERR_UNSUPPORTED and r["supported"] == 0
     # fp32, d_k = 128, chunk 64: two-pass with one record buffer (the 117 KB fp32 record does not
     # fit twice): record + V tile [64][32] fp32, 2 compute + 4 copy waves
-    r = kda.query(1, 64, 1, 128, 128, "f32", chunk_size=64)
+    r = kda.query(1, 64, 1, 128, 128, "f32", chunk_size=64, dv_tile=32)
     assert r["status"] == kda.KDA_OK and r["algo"] == kda.KDA_ALGO_TWO_PASS
     rec32 = (3 * 32768 + 2 * 10240 + 512 + 1023) // 1024 * 1024
     assert rec32 == 119808 and r["lds_bytes"] == rec32 + 64 * 32 * 4 and r["threads_per_block"] == 64 * 6
+    # one (sequence, head): too few 32-column workgroups to fill the GPU, so by default 16-column
+    # tiles (one compute wave and the four copy waves)
+    r = kda.query(1, 64, 1, 128, 128, "f32", chunk_size=64)
+    assert r["dv_tile"] == 16 and r["lds_bytes"] == rec32 + 64 * 16 * 4 and r["threads_per_block"] == 64 * 5
     # packed batch: num_seqs > 0, seq_len = total tokens
     r = kda.query(1, 1000, 32, 128, 128, "bf16", num_seqs=64)
     assert r["grid_blocks"] == 64 * 32 * (128 // r["dv_tile"])
