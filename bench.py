@@ -14,7 +14,9 @@ and the output epilogue (kda_norm_gate: per-head RMSNorm and output gate) are ti
 own over the prefill shapes and reported next to the step, and so is the backward (kda_chunk_bwd:
 the gradients for a synthetic output gradient and final-state gradient on the prefill tensors).
 The decode step with the epilogue fused in (kda_decode_step_gated) is timed on the decode
-workload next to the two-kernel composition (kda_decode_step, then kda_norm_gate).
+workload next to the two-kernel composition (kda_decode_step, then kda_norm_gate), and the
+forward on raw projections with the prologue fused in (kda_chunk_fwd_prologue) on the prefill
+shape next to kda_prologue followed by kda_chunk_fwd.
 `value` is prefill tokens/s (B*T tokens per chunk_fwd launch); the decode step is
 reported in GB/s next to it.  Inputs are resident in HBM before the timed region.
 Timing uses HIP events recorded on the stream the kernels are launched on.
@@ -311,6 +313,19 @@ def main():
         kda.prologue(pd["q_raw"], pd["k_raw"], pd["v_raw"], pd["conv_q"], pd["conv_k"], pd["conv_v"], pd["g_raw"],
                      pd["beta_raw"])
 
+    # the forward on raw projections: prologue fused into the two-pass kernels, and composed
+    # (kda_prologue, then kda_chunk_fwd)
+    def forward_raw_fused():
+        kda.chunk_fwd_prologue(pd["q_raw"], pd["k_raw"], pd["v_raw"], pd["conv_q"], pd["conv_k"], pd["conv_v"],
+                               pd["g_raw"], pd["beta_raw"], d["s0"], chunk_size=args.chunk, workspace=ws, out=out,
+                               final_state=fin)
+
+    def forward_raw_composed():
+        pq, pk, pv, pg, pb = kda.prologue(pd["q_raw"], pd["k_raw"], pd["v_raw"], pd["conv_q"], pd["conv_k"],
+                                          pd["conv_v"], pd["g_raw"], pd["beta_raw"])
+        kda.chunk_fwd(pq, pk, pv, pg, pb, d["s0"], chunk_size=args.chunk, algo="two_pass", workspace=ws, out=out,
+                      final_state=fin)
+
     # ------------------------------------------- output epilogue (prefill output shape)
     eo, ez, ew = (x.to(dev) for x in ki.epilogue_inputs((B, T, H, w.dv), "bf16", seed=5))
     eout = torch.empty_like(eo)
@@ -352,6 +367,8 @@ def main():
         decode_then_norm_gate()
         epilogue()
         prologue()
+        forward_raw_fused()
+        forward_raw_composed()
     torch.cuda.synchronize()
 
     # timed region: K steps, each = one prefill launch + one decode launch
@@ -363,6 +380,8 @@ def main():
     t_decg = time_launches(decode_gated, args.steps, stream)
     t_decc = time_launches(decode_then_norm_gate, args.steps, stream)
     t_pro = time_launches(prologue, args.steps, stream)
+    t_rawf = time_launches(forward_raw_fused, args.steps, stream)
+    t_rawc = time_launches(forward_raw_composed, args.steps, stream)
     t_bwd = time_launches(backward, args.steps, stream)
     t_dplr = t_kfused = None
     if not args.no_compare:
@@ -458,6 +477,10 @@ def main():
         "prologue": {"kernel": "kda_prologue", "conv_width": 4, "ms": round(t_pro, 4),
                      "gb_per_s": round(pro_gbps, 1), "hbm_frac": round(pro_gbps / PEAK_HBM_GBPS, 4),
                      "bytes_per_launch": pro_bytes, "traffic": traffic.get("prologue_bytes")},
+        "forward_raw": {"kernel": "kda_chunk_fwd_prologue", "conv_width": 4, "ms": round(t_rawf, 4),
+                        "tokens_per_s": round(tokens / (t_rawf * 1e-3), 1), "composed_ms": round(t_rawc, 4),
+                        "composed": "kda_prologue + kda_chunk_fwd (two-pass)",
+                        "speedup_vs_composed": round(t_rawc / t_rawf, 3)},
         "epilogue": {"kernel": "kda_norm_gate", "rows": epi_rows, "d": w.dv, "ms": round(t_epi, 4),
                      "gb_per_s": round(epi_gbps, 1), "hbm_frac": round(epi_gbps / PEAK_HBM_GBPS, 4),
                      "bytes_per_launch": epi_bytes, "traffic": traffic.get("epilogue_bytes")},

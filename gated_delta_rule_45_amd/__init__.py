@@ -22,7 +22,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "noalloc_scratch_bytes", "chunk_bwd", "dplr_chunk_fwd", "recurrent_fwd", "decode_step", "decode_step_gated", "prologue", "norm_gate", "query", "tune", "KdaError",
+__all__ = ["chunk_fwd", "chunk_fwd_prologue", "chunk_fwd_noalloc", "noalloc_scratch_bytes", "chunk_bwd", "dplr_chunk_fwd", "recurrent_fwd", "decode_step", "decode_step_gated", "prologue", "norm_gate", "query", "tune", "KdaError",
            "LIB_PATH", "library"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
@@ -88,6 +88,9 @@ def library(path: str = LIB_PATH) -> ctypes.CDLL:
                              ctypes.POINTER(QueryResult)]
     lib.kda_prologue.restype = ctypes.c_int
     lib.kda_prologue.argtypes = [ctypes.POINTER(PrologueProblem)] + [_P] * 17
+    lib.kda_chunk_fwd_prologue.restype = ctypes.c_int
+    lib.kda_chunk_fwd_prologue.argtypes = [ctypes.POINTER(Problem), ctypes.c_int32, ctypes.c_float] + [_P] * 14 + \
+        [ctypes.c_size_t, _P]
     lib.kda_decode_step_gated.restype = ctypes.c_int
     lib.kda_decode_step_gated.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                           ctypes.c_int32, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -273,6 +276,57 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     if gate is not None or norm_weight is not None:
         norm_gate(out, gate, norm_weight, eps=norm_eps, out=out, stream=stream)
     return out, fin
+
+
+def chunk_fwd_prologue(q_raw: torch.Tensor, k_raw: torch.Tensor, v_raw: torch.Tensor, conv_q: torch.Tensor,
+                       conv_k: torch.Tensor, conv_v: torch.Tensor, g_raw: torch.Tensor, beta_raw: torch.Tensor,
+                       initial_state: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None, *,
+                       cu_seqlens_host=None, norm_eps: float = 1e-6, chunk_size: int = 0, scale: float = 1.0,
+                       dv_tile: int = 0, workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                       final_state: Optional[torch.Tensor] = None, output_final_state: bool = True, stream=None):
+    """Chunkwise forward on the raw projections with the prologue fused into the two-pass kernels
+    (kda_chunk_fwd_prologue): the inputs are those of prologue() (zero convolution state), the
+    result that of chunk_fwd on prologue()'s outputs.  Returns (out, final_state)."""
+    dev = q_raw.device
+    p, n = _problem_from(q_raw, v_raw, cu_seqlens, chunk_size, scale, dv_tile, KDA_ALGO_TWO_PASS)
+    B, T, H, dk = q_raw.shape
+    dv = v_raw.shape[-1]
+    W = conv_q.shape[-1]
+    dt = q_raw.dtype
+    for t, name, tdt, shape in ((q_raw, "q_raw", dt, (B, T, H, dk)), (k_raw, "k_raw", dt, (B, T, H, dk)),
+                                (v_raw, "v_raw", dt, (B, T, H, dv)), (g_raw, "g_raw", torch.float32, (B, T, H, dk)),
+                                (beta_raw, "beta_raw", torch.float32, (B, T, H)),
+                                (conv_q, "conv_q", torch.float32, (H, dk, W)), (conv_k, "conv_k", torch.float32, (H, dk, W)),
+                                (conv_v, "conv_v", torch.float32, (H, dv, W))):
+        _need(t, name, tdt, shape, dev)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (n, H, dk, dv), dev)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, (n + 1,), dev)
+    host_cu = None
+    if cu_seqlens_host is not None:
+        host_cu = torch.as_tensor(cu_seqlens_host, dtype=torch.int32).contiguous().cpu()
+        if host_cu.numel() != n + 1:
+            raise ValueError("cu_seqlens_host has the wrong length")
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    _need(out, "out", dt, (B, T, H, dv), dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((n, H, dk, dv), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _need(final_state, "final_state", torch.float32, (n, H, dk, dv), dev)
+    own_ws = None
+    if workspace is None:
+        need = workspace_bytes(p)
+        workspace = own_ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = library().kda_chunk_fwd_prologue(
+        ctypes.byref(p), W, norm_eps, _ptr(q_raw), _ptr(k_raw), _ptr(v_raw), _ptr(conv_q), _ptr(conv_k), _ptr(conv_v),
+        _ptr(g_raw), _ptr(beta_raw), _ptr(initial_state), _ptr(cu_seqlens),
+        None if host_cu is None else ctypes.c_void_p(host_cu.data_ptr()), _ptr(out), _ptr(final_state),
+        ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(), _stream_handle(dev, stream))
+    _keep_for_stream(own_ws, dev, stream)
+    _check(st)
+    return out, final_state
 
 
 def chunk_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,

@@ -437,6 +437,59 @@ kda_status_t kda_chunk_fwd(const kda_problem_t *problem, const void *q, const vo
     }
 }
 
+kda_status_t kda_chunk_fwd_prologue(const kda_problem_t *problem, int32_t conv_width, float norm_eps,
+                                    const void *q_raw, const void *k_raw, const void *v_raw, const float *conv_q,
+                                    const float *conv_k, const float *conv_v, const float *g_raw,
+                                    const float *beta_raw, const float *initial_state, const int32_t *cu_seqlens,
+                                    const int32_t *cu_seqlens_host, void *out, float *final_state, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+    try {
+        Resolved r;
+        kda_status_t st = resolve(problem, cu_seqlens != nullptr, r, true);
+        if (st != KDA_OK) return st;
+        if (problem->algo == KDA_ALGO_FUSED || !r.two_pass_ok)
+            return fail(KDA_ERR_UNSUPPORTED, "fused prologue: runs in the two-pass algorithm, which has no variant for "
+                                             "io=%s d_k=%d chunk=%d dv_tile=%d",
+                        problem->io_dtype == KDA_BF16 ? "bf16" : "fp32", problem->head_dim_k, r.cfg.chunk,
+                        problem->dv_tile);
+        if (conv_width < 1 || conv_width > 4)
+            return fail(KDA_ERR_UNSUPPORTED, "conv_width %d: supported are 1..4", conv_width);
+        if (!std::isfinite(norm_eps) || norm_eps < 0.f)
+            return fail(KDA_ERR_INVALID_ARGUMENT, "norm_eps must be finite and >= 0");
+        // raw projections in the places of q, k, v, g and beta
+        st = check_tensors(problem, r, q_raw, k_raw, v_raw, g_raw, beta_raw, initial_state, cu_seqlens,
+                           cu_seqlens_host, out, final_state);
+        if (st != KDA_OK) return st;
+        if (r.tokens > 0) {
+            const float *taps[] = {conv_q, conv_k, conv_v};
+            const char *names[] = {"conv_q", "conv_k", "conv_v"};
+            for (int i = 0; i < 3; ++i) {
+                if (!taps[i]) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is NULL", names[i]);
+                if (!aligned(taps[i], 4)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s is not 4-byte aligned", names[i]);
+                if ((const void *)taps[i] == out || taps[i] == final_state)
+                    return fail(KDA_ERR_INVALID_ARGUMENT, "an output aliases %s", names[i]);
+            }
+        }
+        if (!workspace || workspace_bytes < r.ws_bytes || !aligned(workspace, 256))
+            return fail(KDA_ERR_WORKSPACE, "fused prologue: needs a 256-byte aligned workspace of %zu bytes (got %zu at %p)",
+                        r.ws_bytes, workspace_bytes, workspace);
+        if (r.num_seqs == 0) return ok();
+        kda::FwdParams fp = make_params(problem, r, q_raw, k_raw, v_raw, g_raw, beta_raw, initial_state, cu_seqlens,
+                                        out, final_state);
+        fp.conv[0] = conv_q;
+        fp.conv[1] = conv_k;
+        fp.conv[2] = conv_v;
+        fp.conv_w = conv_width;
+        fp.norm_eps = norm_eps;
+        return hip_status(kda::launch_split_fwd(dtype_of(problem->io_dtype), fp, r.cfg.chunk, r.spw, r.nw,
+                                                static_cast<char *>(workspace), r.chunk_upper,
+                                                static_cast<hipStream_t>(stream)),
+                          "kda_chunk_fwd_prologue launch");
+    } catch (...) {
+        return fail(KDA_ERR_HIP, "unexpected exception in kda_chunk_fwd_prologue");
+    }
+}
+
 kda_status_t kda_chunk_bwd_workspace(const kda_problem_t *problem, size_t *bytes) {
     try {
         if (!bytes) return fail(KDA_ERR_INVALID_ARGUMENT, "bytes is NULL");

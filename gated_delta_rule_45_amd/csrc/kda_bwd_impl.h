@@ -201,10 +201,6 @@ __device__ __forceinline__ Frag<BF> bwd_turn(const Frag<BF> &a, const Frag<BF> &
     return frag_from_acc<BF>(t);
 }
 
-// One operand-type element as fp32.
-__device__ __forceinline__ float elem_f32(float x) { return x; }
-__device__ __forceinline__ float elem_f32(uint16_t x) { return bf16_to_f32(x); }
-
 // Diagonal-block terms of one sub-chunk for the gradient kernel, exact under any decay: the split
 // levels of kda_device.h (split_anchor), here in products that contract over the tokens.  The lane
 // holds token l16 of the sub-chunk and channels 4*q4 + j of its wave's 16: raw k and q (kk, qq) and

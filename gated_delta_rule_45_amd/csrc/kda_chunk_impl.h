@@ -103,13 +103,6 @@ struct ChunkRaw {
     float beta;
 };
 
-// 4 packed io values (bf16 pair words or fp32) -> fp32
-template <bool BF, typename KQ>
-__device__ __forceinline__ float4 unpack4(const KQ &x) {
-    if constexpr (BF) return make_float4(bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y));
-    else return x;
-}
-
 template <typename IO, int DK, int DVT, int C>
 __device__ __forceinline__ void load_chunk(ChunkRaw<IO, DK, DVT, C> &raw, const FwdParams &p, int64_t tok0, int clen,
                                            int h, int col0, int tid) {

@@ -51,6 +51,14 @@ template <int N>
 __device__ __forceinline__ float row_shr(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xf, 0xf, true));
 }
+// Value from the lane n places higher in the same row of 16 lanes; 0 for the last n lanes.
+template <int N>
+__device__ __forceinline__ float row_shl(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x100 + N, 0xf, 0xf, true));
+}
+// One operand-type element as fp32.
+__device__ __forceinline__ float elem_f32(float x) { return x; }
+__device__ __forceinline__ float elem_f32(uint16_t x) { return bf16_to_f32(x); }
 // Inclusive prefix sum over each row of 16 lanes (Hillis-Steele, 4 DPP steps).
 __device__ __forceinline__ float scan16_add(float x) {
     x += row_shr<1>(x);
@@ -393,6 +401,82 @@ __device__ __forceinline__ void diag_block_split_rolled(f32x4 &accA, f32x4 &accP
         accPt[2] += jd == 2 ? dot : 0.f;
         accPt[3] += jd == 3 ? dot : 0.f;
     }
+}
+
+// diag_block_split_rolled with the lane's k, q (as the operator sees them; zero for tokens past the
+// chunk end) and its scanned log2 gate G already in registers: the fused prologue has no memory copy
+// of the transformed operands to reload.  The level loop stays rolled.
+template <typename IO, int KT>
+__device__ __forceinline__ void diag_block_split_regs(f32x4 &accA, f32x4 &accPt, const float (&kr)[KT][4],
+                                                      const float (&qr)[KT][4], const float (&G)[KT][4], int l16,
+                                                      int q4, int lane) {
+    constexpr bool BF = IoTraits<IO>::kBf16;
+    accA = zero4();
+    accPt = zero4();
+    float dot = 0.f;
+#pragma unroll
+    for (int ct = 0; ct < KT; ++ct)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dot += kr[ct][j] * qr[ct][j];
+#pragma unroll 1
+    for (int lvl = 0; lvl < 4; ++lvl) {
+        const int hs = 8 >> lvl;
+        const bool sec = (l16 & hs) != 0;
+        const int src = (lane & ~15) | ((l16 & ~(2 * hs - 1)) + hs - 1);  // the level's anchor token
+        f32x4 tA = zero4(), tPt = zero4();
+#pragma unroll
+        for (int ct = 0; ct < KT; ++ct) {
+            float a[4], b[4], c[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float f = __builtin_amdgcn_exp2f(-fabsf(G[ct][j] - __shfl(G[ct][j], src)));
+                a[j] = sec ? kr[ct][j] * f : 0.f;
+                b[j] = sec ? qr[ct][j] * f : 0.f;
+                c[j] = sec ? 0.f : kr[ct][j] * f;
+            }
+            const Frag<BF> ck = make_frag<BF>(c[0], c[1], c[2], c[3]);
+            mma16(tA, make_frag<BF>(a[0], a[1], a[2], a[3]), ck);
+            mma16(tPt, ck, make_frag<BF>(b[0], b[1], b[2], b[3]));
+        }
+        mfma_settle(tA, tPt);  // read after the loop's exit
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bool same = ((4 * q4 + j) >> (4 - lvl)) == (l16 >> (4 - lvl));
+            accA[j] += same ? tA[j] : 0.f;
+            accPt[j] += same ? tPt[j] : 0.f;
+        }
+    }
+    dot += __shfl_xor(dot, 16);
+    dot += __shfl_xor(dot, 32);
+    if (q4 == (l16 >> 2)) {
+        const int jd = l16 & 3;
+        accPt[0] += jd == 0 ? dot : 0.f;
+        accPt[1] += jd == 1 ? dot : 0.f;
+        accPt[2] += jd == 2 ? dot : 0.f;
+        accPt[3] += jd == 3 ? dot : 0.f;
+    }
+}
+
+// 4 packed io values (bf16 pair words or fp32) -> fp32
+template <bool BF, typename KQ>
+__device__ __forceinline__ float4 unpack4(const KQ &x) {
+    if constexpr (BF) return make_float4(bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y));
+    else return x;
+}
+
+// ---------------------------------------------------------- fused prologue ----
+// The activations of the prologue (Kimi Linear summary page, "Kimi Linear model composition";
+// the readings: Swish(c) = c sigmoid(c), g = -softplus(g_raw), beta = sigmoid(beta_raw)), in the
+// same fp32 forms as the standalone prologue kernels.
+__device__ __forceinline__ float swish_f(float c) { return c * __builtin_amdgcn_rcpf(1.0f + __expf(-c)); }
+__device__ __forceinline__ float neg_softplus_f(float x) { return -(fmaxf(x, 0.f) + __logf(1.0f + __expf(-fabsf(x)))); }
+__device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+// Filter taps of one channel as a 4-tap window over tokens t-3 .. t: tap i < W of the W-tap filter
+// (tap W-1 on the current token) lands at position 4 - W + i, the front is zero.
+__device__ __forceinline__ void conv_taps4(const float *w, int W, float (&w4)[4]) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) w4[d] = d >= 4 - W ? w[d - (4 - W)] : 0.f;
 }
 
 // Largest in-sub-chunk decay (log2 units) for which the single-anchor diagonal blocks stay exact:

@@ -36,6 +36,13 @@ struct FwdParams {
     void *hs = nullptr;
     void *dch = nullptr;
     const int32_t *chunk_off = nullptr;
+    // Fused prologue (two-pass forward only): q, k, v, g and beta hold the raw projections, and the
+    // kernels apply the short convolution (taps conv[0..2] for q, k, v: fp32 [H, d, conv_w]) with
+    // Swish, the L2 normalisation of q and k (norm_eps) and the gate and beta activations as they
+    // read them.  Null conv[0]: the inputs are the operator's own.
+    const float *conv[3] = {nullptr, nullptr, nullptr};
+    int32_t conv_w = 0;
+    float norm_eps = 0.f;
 };
 
 // Chunk-forward configuration chosen by the host.

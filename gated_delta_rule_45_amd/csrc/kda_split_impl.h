@@ -192,7 +192,12 @@ struct PrepLayout {
 
 // Three workgroups per CU (4 waves each): the kernel is bound by memory latency, and the waves of
 // the other workgroups hide it.
-template <typename IO, int DK, int C>
+// PRO: the inputs are the raw projections and phase 1 applies the prologue as it loads them (see
+// FwdParams::conv): each lane's raw k and q for its token and for the token three back (zero before
+// the sequence start), the two tokens between from its row neighbours by DPP row shifts, the
+// 4-tap causal convolution and Swish in fp32, then the L2 norm over the token's d_k channels
+// (the four lanes of a token); g = -softplus(g_raw) and beta = sigmoid(beta_raw) where read.
+template <typename IO, int DK, int C, bool PRO = false>
 __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_t *__restrict__ chunk_off,
                                                        char *__restrict__ records) {
     using L = PrepLayout<IO, DK, C>;
@@ -227,6 +232,19 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
     const int64_t tok0 = start + (int64_t)c * C;
     char *rec = records + (size_t)(gidx * H + h) * Rec::kBytes;
 
+    // fused prologue: the head's q and k filter taps as 4-tap windows, in the K_b rows (free until
+    // phase 3): [q | k][channel]
+    [[maybe_unused]] const float4 *sTap = reinterpret_cast<const float4 *>(smem + L::oKb);
+    if constexpr (PRO) {
+        static_assert(2 * DK * 16 <= (size_t)C * LDO * sizeof(OT), "the taps fit in the K_b rows");
+        if (tid < 2 * DK) {
+            float w4[4];
+            conv_taps4(p.conv[tid / DK] + ((int64_t)h * DK + tid % DK) * p.conv_w, p.conv_w, w4);
+            reinterpret_cast<float4 *>(smem + L::oKb)[tid] = make_float4(w4[0], w4[1], w4[2], w4[3]);
+        }
+        __syncthreads();
+    }
+
     // ================= 1: load sub-chunk, scan the gate (log2 domain)
     float G[KT][4], kr[KT][4], qr[KT][4];
     bool split = false;  // the sub-chunk decays too strongly for a single-anchor diagonal block
@@ -236,6 +254,72 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
         const int r = min(16 * R + l16, clen - 1);
         const int64_t row = ((tok0 + r) * H + h) * (int64_t)DK + 4 * q4;
         const float m = valid ? kLog2e : 0.f;
+        if constexpr (PRO) {
+            // token three back: inside the sequence (this or the previous chunk) or zero
+            const bool has3 = (int64_t)c * C + 16 * R + l16 - 3 >= 0;
+            const int64_t row3 = ((tok0 + min(16 * R + l16 - 3, clen - 1)) * H + h) * (int64_t)DK + 4 * q4;
+            // every load in flight first, packed as loaded
+            using KQ = typename std::conditional<BF, uint2, float4>::type;
+            KQ rk0[KT], rq0[KT], rk3[KT], rq3[KT];
+            float4 rg[KT];
+#pragma unroll
+            for (int ct = 0; ct < KT; ++ct) {
+                const IO *kp = static_cast<const IO *>(p.k), *qp = static_cast<const IO *>(p.q);
+                rg[ct] = *reinterpret_cast<const float4 *>(p.g + row + 16 * ct);
+                rk0[ct] = *reinterpret_cast<const KQ *>(kp + row + 16 * ct);
+                rq0[ct] = *reinterpret_cast<const KQ *>(qp + row + 16 * ct);
+                rk3[ct] = has3 ? *reinterpret_cast<const KQ *>(kp + row3 + 16 * ct) : KQ{};
+                rq3[ct] = has3 ? *reinterpret_cast<const KQ *>(qp + row3 + 16 * ct) : KQ{};
+            }
+            float sk = 0.f, sq = 0.f;
+#pragma unroll
+            for (int ct = 0; ct < KT; ++ct) {
+                // one channel tile at a time: only its taps and temporaries are live
+                __builtin_amdgcn_sched_barrier(0);
+                const float4 k0 = unpack4<BF>(rk0[ct]), q0 = unpack4<BF>(rq0[ct]);
+                const float4 k3 = unpack4<BF>(rk3[ct]), q3 = unpack4<BF>(rq3[ct]);
+                const float gx[4] = {rg[ct].x, rg[ct].y, rg[ct].z, rg[ct].w};
+                const float kx0[4] = {k0.x, k0.y, k0.z, k0.w}, kx3[4] = {k3.x, k3.y, k3.z, k3.w};
+                const float qx0[4] = {q0.x, q0.y, q0.z, q0.w}, qx3[4] = {q3.x, q3.y, q3.z, q3.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int ch = 16 * ct + 4 * q4 + j;
+                    G[ct][j] = neg_softplus_f(gx[j]) * m;
+                    const float4 tq = sTap[ch], tk = sTap[DK + ch];
+                    // raw inputs of tokens t-2 and t-1: row neighbours, or (first lanes of the row)
+                    // the token-three-back loads of lanes 1 and 2
+                    const float ka = row_shr<1>(kx0[j]), kb = row_shl<2>(kx3[j]);
+                    const float kc = row_shr<2>(kx0[j]), kd = row_shl<1>(kx3[j]);
+                    const float qa = row_shr<1>(qx0[j]), qb = row_shl<2>(qx3[j]);
+                    const float qc = row_shr<2>(qx0[j]), qd = row_shl<1>(qx3[j]);
+                    const float k1 = l16 >= 1 ? ka : kb, k2 = l16 >= 2 ? kc : kd;
+                    const float q1 = l16 >= 1 ? qa : qb, q2 = l16 >= 2 ? qc : qd;
+                    float ck = 0.f, cq = 0.f;
+                    ck = fmaf(tk.x, kx3[j], ck); ck = fmaf(tk.y, k2, ck);
+                    ck = fmaf(tk.z, k1, ck); ck = fmaf(tk.w, kx0[j], ck);
+                    cq = fmaf(tq.x, qx3[j], cq); cq = fmaf(tq.y, q2, cq);
+                    cq = fmaf(tq.z, q1, cq); cq = fmaf(tq.w, qx0[j], cq);
+                    kr[ct][j] = swish_f(ck);
+                    qr[ct][j] = swish_f(cq);
+                    sk = fmaf(kr[ct][j], kr[ct][j], sk);
+                    sq = fmaf(qr[ct][j], qr[ct][j], sq);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // L2 norm over the token's channels: the four lanes 16 apart hold a quarter each
+            sk += __shfl_xor(sk, 16);
+            sk += __shfl_xor(sk, 32);
+            sq += __shfl_xor(sq, 16);
+            sq += __shfl_xor(sq, 32);
+            const float rk = valid ? rsqrtf(sk + p.norm_eps) : 0.f, rq = valid ? rsqrtf(sq + p.norm_eps) : 0.f;
+#pragma unroll
+            for (int ct = 0; ct < KT; ++ct)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    kr[ct][j] *= rk;
+                    qr[ct][j] *= rq;
+                }
+        } else {
 #pragma unroll
         for (int ct = 0; ct < KT; ++ct) {
             const float4 gv = *reinterpret_cast<const float4 *>(p.g + row + 16 * ct);
@@ -246,6 +330,7 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
             kr[ct][2] = valid ? kv.z : 0.f; kr[ct][3] = valid ? kv.w : 0.f;
             qr[ct][0] = valid ? qv.x : 0.f; qr[ct][1] = valid ? qv.y : 0.f;
             qr[ct][2] = valid ? qv.z : 0.f; qr[ct][3] = valid ? qv.w : 0.f;
+        }
         }
 #pragma unroll
         for (int ct = 0; ct < KT; ++ct) {
@@ -261,13 +346,18 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
             // P come from the split levels (all factors <= 1, operands reloaded).  A_RR (times beta)
             // goes to its place in sX; P_RR to its fragment of the record (phase 4 skips both).
             f32x4 dA, dPt;
-            const int64_t row = ((tok0 + min(16 * R + l16, clen - 1)) * H + h) * (int64_t)DK + 4 * q4;
-            diag_block_split_rolled<IO>(dA, dPt, static_cast<const IO *>(p.k) + row, static_cast<const IO *>(p.q) + row,
-                                        p.g + row, valid, KT, l16, q4, lane);
+            if constexpr (PRO) {
+                diag_block_split_regs<IO, KT>(dA, dPt, kr, qr, G, l16, q4, lane);
+            } else {
+                const int64_t row = ((tok0 + min(16 * R + l16, clen - 1)) * H + h) * (int64_t)DK + 4 * q4;
+                diag_block_split_rolled<IO>(dA, dPt, static_cast<const IO *>(p.k) + row,
+                                            static_cast<const IO *>(p.q) + row, p.g + row, valid, KT, l16, q4, lane);
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int rr = 4 * q4 + j;
-                const float b = 16 * R + rr < clen ? p.beta[(tok0 + 16 * R + rr) * H + h] : 0.f;
+                float b = 16 * R + rr < clen ? p.beta[(tok0 + 16 * R + rr) * H + h] : 0.f;
+                if constexpr (PRO) b = 16 * R + rr < clen ? sigmoid_f(b) : 0.f;
                 sX[(16 * R + rr) * LDX + 16 * R + l16] = l16 < rr ? dA[j] * b : 0.f;
             }
             const Frag<BF> fp = make_frag<BF>(dPt[0], dPt[1], dPt[2], dPt[3]);
@@ -277,7 +367,11 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
             else *reinterpret_cast<decltype(fp.v) *>(tile + lane * Rec::PAIR_BYTES + Rec::FRAG_BYTES) = fp.v;
         }
     }
-    if (tid < C) sBeta[tid] = tid < clen ? p.beta[(tok0 + tid) * H + h] : 0.f;
+    if (tid < C) {
+        float b = tid < clen ? p.beta[(tok0 + tid) * H + h] : 0.f;
+        if constexpr (PRO) b = tid < clen ? sigmoid_f(b) : 0.f;
+        sBeta[tid] = b;
+    }
     __syncthreads();
 
     // ================= 2: per-channel boundary factors; Gamma = e^{G_C}
@@ -693,10 +787,35 @@ __device__ __forceinline__ void copy_wave(char *smem, const char *rec0, size_t r
 #undef KDA_STAGE_STORE
 }
 
+// Fused prologue (PRO) in the scans: V rows 16 r2 + 4 q4 + j (j < 4) of one column as the operator
+// sees them: Swish of the 4-tap causal convolution (taps w4, FwdParams::conv[2]) of the raw rows
+// staged in vb, the rows before the chunk from prev (that column's last three raw rows of the
+// previous chunk; zero at the sequence start).
+template <typename IO, int DVT>
+__device__ __forceinline__ void conv_v4(const IO *vb, int col, int base, const float (&w4)[4], const float (&prev)[3],
+                                        float (&out)[4]) {
+    float x[7];
+#pragma unroll
+    for (int i = 0; i < 7; ++i) {
+        const int row = base - 3 + i;
+        const float xv = elem_f32(vb[max(row, 0) * DVT + col]);
+        x[i] = row >= 0 ? xv : (row == -3 ? prev[0] : (row == -2 ? prev[1] : prev[2]));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float c = 0.f;
+        c = fmaf(w4[0], x[j], c);
+        c = fmaf(w4[1], x[j + 1], c);
+        c = fmaf(w4[2], x[j + 2], c);
+        c = fmaf(w4[3], x[j + 3], c);
+        out[j] = swish_f(c);
+    }
+}
+
 // KEEP: write each chunk's initial state and D (FwdParams::hs / dch) for the backward pass and
 // no output (Q~ and P are neither staged nor used); a separate instantiation so the forward's
 // register allocation is not affected.
-template <typename IO, int DK, int C, int SPW, int NW, bool KEEP>
+template <typename IO, int DK, int C, int SPW, int NW, bool KEEP, bool PRO = false>
 __global__ void __launch_bounds__((ScanLayout<IO, DK, C, SPW, NW>::NT)) kda_scan_kernel(FwdParams p, const int32_t *__restrict__ chunk_off,
                                                                   const char *__restrict__ records) {
     using S = ScanLayout<IO, DK, C, SPW, NW>;
@@ -784,6 +903,15 @@ __global__ void __launch_bounds__((ScanLayout<IO, DK, C, SPW, NW>::NT)) kda_scan
     // Gamma before the state products.  Scheduling fences keep the compiler from sinking the
     // reads next to their uses.
     constexpr int KP = KT / 2;                        // 32-wide k pairs of d_k
+    // fused prologue: V's filter taps for this lane's columns and the previous chunk's last raw rows
+    [[maybe_unused]] float vw4[SPW][4], vprev[SPW][3];
+    if constexpr (PRO) {
+#pragma unroll
+        for (int s = 0; s < SPW; ++s) {
+            conv_taps4(p.conv[2] + ((int64_t)h * DV + col0 + WC * wave + 16 * s + l16) * p.conv_w, p.conv_w, vw4[s]);
+            vprev[s][0] = vprev[s][1] = vprev[s][2] = 0.f;
+        }
+    }
     constexpr int GP = NSUB >= 2 ? NSUB - 2 : 0;      // row tile after which P and K-^T reads start
     constexpr int KT_H = (KT + 1) / 2;                // K-^T row tiles read at GP
 
@@ -808,7 +936,8 @@ __global__ void __launch_bounds__((ScanLayout<IO, DK, C, SPW, NW>::NT)) kda_scan
         const IO *vb = reinterpret_cast<const IO *>(smem + ((c & 1) ? S::oV1 : S::oV0));
 
         FragPair<BF> Kf[NSUB][KP], Qf[NSUB][KP], Tf[NSUB][NPAIR], Pf[NSUB][NPAIR], Bf[KT][NPAIR];
-        IO vv[SPW][NSUB][4];  // V as stored; converted where Y is formed
+        // V as stored (converted where Y is formed), or with the fused prologue already applied
+        typename std::conditional<PRO, float, IO>::type vv[SPW][NSUB][4];
         auto read_kq = [&](int rt) {
 #pragma unroll
             for (int kp = 0; kp < KP; ++kp) {
@@ -847,6 +976,16 @@ __global__ void __launch_bounds__((ScanLayout<IO, DK, C, SPW, NW>::NT)) kda_scan
             __builtin_amdgcn_sched_barrier(0);
             if (rt + 2 < NSUB) read_kq(rt + 2);
             if (rt == 0) {
+                if constexpr (PRO) {
+#pragma unroll
+                    for (int s = 0; s < SPW; ++s) {
+                        const int vc = WC * wave + 16 * s + l16;
+#pragma unroll
+                        for (int r2 = 0; r2 < NSUB; ++r2) conv_v4<IO, DVT>(vb, vc, 16 * r2 + 4 * q4, vw4[s], vprev[s], vv[s][r2]);
+#pragma unroll
+                        for (int i = 0; i < 3; ++i) vprev[s][i] = elem_f32(vb[(C - 3 + i) * DVT + vc]);
+                    }
+                } else {
 #pragma unroll
                 for (int s = 0; s < SPW; ++s)
 #pragma unroll
@@ -854,6 +993,7 @@ __global__ void __launch_bounds__((ScanLayout<IO, DK, C, SPW, NW>::NT)) kda_scan
 #pragma unroll
                         for (int j = 0; j < 4; ++j)
                             vv[s][r2][j] = vb[(16 * r2 + 4 * q4 + j) * DVT + WC * wave + 16 * s + l16];
+                }
 #pragma unroll
                 for (int R = 0; R < NSUB; ++R)
 #pragma unroll
@@ -884,10 +1024,10 @@ __global__ void __launch_bounds__((ScanLayout<IO, DK, C, SPW, NW>::NT)) kda_scan
             for (int s = 0; s < SPW; ++s)
 #pragma unroll
                 for (int rt = 0; rt < 2 * NPAIR; ++rt)
-                    Yb[s][rt] = rt < NSUB ? make_frag<BF>(Tr::to_float(vv[s][rt][0]) - AK[s][rt][0],
-                                                          Tr::to_float(vv[s][rt][1]) - AK[s][rt][1],
-                                                          Tr::to_float(vv[s][rt][2]) - AK[s][rt][2],
-                                                          Tr::to_float(vv[s][rt][3]) - AK[s][rt][3])
+                    Yb[s][rt] = rt < NSUB ? make_frag<BF>(elem_f32(vv[s][rt][0]) - AK[s][rt][0],
+                                                          elem_f32(vv[s][rt][1]) - AK[s][rt][1],
+                                                          elem_f32(vv[s][rt][2]) - AK[s][rt][2],
+                                                          elem_f32(vv[s][rt][3]) - AK[s][rt][3])
                                           : make_frag<BF>(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
             for (int R = 0; R < NSUB; ++R) {
@@ -1044,7 +1184,7 @@ __device__ __forceinline__ void slot_get(const char *slot, int lane, Frag<BF> *f
     }
 }
 
-template <typename IO, int DK, int C, int SPW, int NW, bool KEEP>
+template <typename IO, int DK, int C, int SPW, int NW, bool KEEP, bool PRO = false>
 __global__ void __launch_bounds__((ScanOwLayout<IO, DK, C, SPW, NW>::NT)) kda_scan_ow_kernel(FwdParams p, const int32_t *__restrict__ chunk_off,
                                                                      const char *__restrict__ records) {
     using S = ScanLayout<IO, DK, C, SPW, NW>;
@@ -1242,6 +1382,15 @@ __global__ void __launch_bounds__((ScanOwLayout<IO, DK, C, SPW, NW>::NT)) kda_sc
     slot_put<BF, SBN>(smem + SO::oSb + (size_t)(wave * SO::SB_UNITS) * 64 * 16, lane, Sb);
 
     constexpr int GP = NSUB >= 2 ? NSUB - 2 : 0;  // row tile after which the K-^T reads start
+    // fused prologue: V's filter taps for this lane's columns and the previous chunk's last raw rows
+    [[maybe_unused]] float vw4[SPW][4], vprev[SPW][3];
+    if constexpr (PRO) {
+#pragma unroll
+        for (int s = 0; s < SPW; ++s) {
+            conv_taps4(p.conv[2] + ((int64_t)h * DV + col0 + WC * wave + 16 * s + l16) * p.conv_w, p.conv_w, vw4[s]);
+            vprev[s][0] = vprev[s][1] = vprev[s][2] = 0.f;
+        }
+    }
     constexpr int KT_H = (KT + 1) / 2;
     for (int c = 0; c < nchunks; ++c) {
         __syncthreads();  // chunk c is in LDS
@@ -1249,7 +1398,7 @@ __global__ void __launch_bounds__((ScanOwLayout<IO, DK, C, SPW, NW>::NT)) kda_sc
         const IO *vb = reinterpret_cast<const IO *>(smem + ((c & 1) ? S::oV1 : S::oV0));
 
         FragPair<BF> Kf[NSUB][KP], Tf[NSUB][NPAIR], Bf[KT][NPAIR];
-        IO vv[SPW][NSUB][4];
+        typename std::conditional<PRO, float, IO>::type vv[SPW][NSUB][4];  // see kda_scan_kernel
         auto read_k = [&](int rt) {
 #pragma unroll
             for (int kp = 0; kp < KP; ++kp)
@@ -1280,6 +1429,16 @@ __global__ void __launch_bounds__((ScanOwLayout<IO, DK, C, SPW, NW>::NT)) kda_sc
             __builtin_amdgcn_sched_barrier(0);
             if (rt + 2 < NSUB) read_k(rt + 2);
             if (rt == 0) {
+                if constexpr (PRO) {
+#pragma unroll
+                    for (int s = 0; s < SPW; ++s) {
+                        const int vc = WC * wave + 16 * s + l16;
+#pragma unroll
+                        for (int r2 = 0; r2 < NSUB; ++r2) conv_v4<IO, DVT>(vb, vc, 16 * r2 + 4 * q4, vw4[s], vprev[s], vv[s][r2]);
+#pragma unroll
+                        for (int i = 0; i < 3; ++i) vprev[s][i] = elem_f32(vb[(C - 3 + i) * DVT + vc]);
+                    }
+                } else {
 #pragma unroll
                 for (int s = 0; s < SPW; ++s)
 #pragma unroll
@@ -1287,6 +1446,7 @@ __global__ void __launch_bounds__((ScanOwLayout<IO, DK, C, SPW, NW>::NT)) kda_sc
 #pragma unroll
                         for (int j = 0; j < 4; ++j)
                             vv[s][r2][j] = vb[(16 * r2 + 4 * q4 + j) * DVT + WC * wave + 16 * s + l16];
+                }
 #pragma unroll
                 for (int R = 0; R < NSUB; ++R)
 #pragma unroll
@@ -1308,10 +1468,10 @@ __global__ void __launch_bounds__((ScanOwLayout<IO, DK, C, SPW, NW>::NT)) kda_sc
             for (int s = 0; s < SPW; ++s)
 #pragma unroll
                 for (int rt = 0; rt < 2 * NPAIR; ++rt)
-                    Yb[s][rt] = rt < NSUB ? make_frag<BF>(Tr::to_float(vv[s][rt][0]) - AK[s][rt][0],
-                                                          Tr::to_float(vv[s][rt][1]) - AK[s][rt][1],
-                                                          Tr::to_float(vv[s][rt][2]) - AK[s][rt][2],
-                                                          Tr::to_float(vv[s][rt][3]) - AK[s][rt][3])
+                    Yb[s][rt] = rt < NSUB ? make_frag<BF>(elem_f32(vv[s][rt][0]) - AK[s][rt][0],
+                                                          elem_f32(vv[s][rt][1]) - AK[s][rt][1],
+                                                          elem_f32(vv[s][rt][2]) - AK[s][rt][2],
+                                                          elem_f32(vv[s][rt][3]) - AK[s][rt][3])
                                           : make_frag<BF>(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
             for (int R = 0; R < NSUB; ++R) {
@@ -1394,10 +1554,11 @@ hipError_t launch_split_variant(const FwdParams &params, char *workspace, int64_
     FwdParams p = params;
     if (p.cu) p.order = plan_order(workspace, p.num_seqs);  // the scan runs the longest sequences first
     const bool keep = p.hs != nullptr;
+    const bool pro = p.conv[0] != nullptr;  // fused prologue: the inputs are raw projections
     if constexpr (!split_fits<IO, DK, C, SPW, NW>()) {
         return hipErrorInvalidConfiguration;
     } else {
-        if (keep && (!ScanLayout<IO, DK, C, SPW, NW>::kFitsKeep || p.out != nullptr))
+        if (keep && (!ScanLayout<IO, DK, C, SPW, NW>::kFitsKeep || p.out != nullptr || pro))
             return hipErrorInvalidConfiguration;  // the kept forward writes S and D, never O
         int32_t *chunk_off = reinterpret_cast<int32_t *>(workspace);
         char *records = workspace + split_plan_bytes(p.num_seqs);
@@ -1407,8 +1568,12 @@ hipError_t launch_split_variant(const FwdParams &params, char *workspace, int64_
         }
         const int64_t prep_blocks = chunk_upper * p.H;
         if (prep_blocks > 0) {
-            hipLaunchKernelGGL((kda_prep_kernel<IO, DK, C>), dim3((unsigned)prep_blocks), dim3(256), 0, stream, p,
-                               chunk_off, records);
+            if (pro)
+                hipLaunchKernelGGL((kda_prep_kernel<IO, DK, C, true>), dim3((unsigned)prep_blocks), dim3(256), 0, stream,
+                                   p, chunk_off, records);
+            else
+                hipLaunchKernelGGL((kda_prep_kernel<IO, DK, C>), dim3((unsigned)prep_blocks), dim3(256), 0, stream, p,
+                                   chunk_off, records);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
@@ -1422,11 +1587,19 @@ hipError_t launch_split_variant(const FwdParams &params, char *workspace, int64_
                     hipLaunchKernelGGL((kda_scan_kernel<IO, DK, C, SPW, NW, true>), dim3((unsigned)scan_blocks),
                                        dim3(ScanLayout<IO, DK, C, SPW, NW>::NT), 0, stream, p, chunk_off, records);
             } else if constexpr (ScanOwLayout<IO, DK, C, SPW, NW>::kFits) {
-                hipLaunchKernelGGL((kda_scan_ow_kernel<IO, DK, C, SPW, NW, false>), dim3((unsigned)scan_blocks),
-                                   dim3(ScanOwLayout<IO, DK, C, SPW, NW>::NT), 0, stream, p, chunk_off, records);
+                if (pro)
+                    hipLaunchKernelGGL((kda_scan_ow_kernel<IO, DK, C, SPW, NW, false, true>), dim3((unsigned)scan_blocks),
+                                       dim3(ScanOwLayout<IO, DK, C, SPW, NW>::NT), 0, stream, p, chunk_off, records);
+                else
+                    hipLaunchKernelGGL((kda_scan_ow_kernel<IO, DK, C, SPW, NW, false>), dim3((unsigned)scan_blocks),
+                                       dim3(ScanOwLayout<IO, DK, C, SPW, NW>::NT), 0, stream, p, chunk_off, records);
             } else {
-                hipLaunchKernelGGL((kda_scan_kernel<IO, DK, C, SPW, NW, false>), dim3((unsigned)scan_blocks),
-                                   dim3(ScanLayout<IO, DK, C, SPW, NW>::NT), 0, stream, p, chunk_off, records);
+                if (pro)
+                    hipLaunchKernelGGL((kda_scan_kernel<IO, DK, C, SPW, NW, false, true>), dim3((unsigned)scan_blocks),
+                                       dim3(ScanLayout<IO, DK, C, SPW, NW>::NT), 0, stream, p, chunk_off, records);
+                else
+                    hipLaunchKernelGGL((kda_scan_kernel<IO, DK, C, SPW, NW, false>), dim3((unsigned)scan_blocks),
+                                       dim3(ScanLayout<IO, DK, C, SPW, NW>::NT), 0, stream, p, chunk_off, records);
             }
             return hipGetLastError();
         }

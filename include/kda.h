@@ -136,6 +136,33 @@ kda_status_t kda_recurrent_fwd(const kda_problem_t *problem, const void *q, cons
                                float *final_state, void *stream);
 
 /*
+ * kda_chunk_fwd_prologue -- kda_chunk_fwd (two-pass algorithm) on the raw projections, with the
+ * prologue of kda_prologue applied inside the kernels as they read their inputs (summary page,
+ * "Kimi Linear model composition"; readings as for kda_prologue): q, k and v pass the causal
+ * depthwise convolution of conv_width taps and Swish, q and k the L2 normalisation with
+ * norm_eps, g = -softplus(g_raw), beta = sigmoid(beta_raw).  The convolution sees zeros before
+ * every sequence's first token (use kda_prologue, then kda_chunk_fwd, to carry a convolution
+ * state across calls).  The normalised q, k, v, g and beta are not written anywhere.
+ *
+ *  problem, initial_state, cu_seqlens, cu_seqlens_host, out, final_state, workspace, stream:
+ *                  as for kda_chunk_fwd; problem->algo must not be KDA_ALGO_FUSED, and the
+ *                  workspace is required (kda_query with KDA_ALGO_TWO_PASS reports its size).
+ *  q_raw, k_raw    [tokens, H, d_k] io dtype;  v_raw [tokens, H, d_v] io dtype
+ *  conv_q, conv_k  [H, d_k, conv_width] fp32;  conv_v [H, d_v, conv_width] fp32 (tap
+ *                  conv_width - 1 on the current token), 4-byte aligned
+ *  g_raw           [tokens, H, d_k] fp32;  beta_raw [tokens, H] fp32
+ *  conv_width      1..4 (KDA_ERR_UNSUPPORTED otherwise);  norm_eps >= 0 and finite.
+ * Errors as for kda_chunk_fwd; KDA_ERR_UNSUPPORTED also where the two-pass algorithm has no
+ * variant for the problem.
+ */
+kda_status_t kda_chunk_fwd_prologue(const kda_problem_t *problem, int32_t conv_width, float norm_eps,
+                                    const void *q_raw, const void *k_raw, const void *v_raw, const float *conv_q,
+                                    const float *conv_k, const float *conv_v, const float *g_raw,
+                                    const float *beta_raw, const float *initial_state, const int32_t *cu_seqlens,
+                                    const int32_t *cu_seqlens_host, void *out, float *final_state, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+
+/*
  * kda_chunk_bwd -- gradients of the chunkwise forward (training).
  * Kimi Linear summary page, "Chunkwise parallel algorithm" section: the WY/UT chunk form
  * is what makes the operator trainable at matrix-core speed; the gradients are the

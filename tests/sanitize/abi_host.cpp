@@ -212,6 +212,29 @@ void forward_validation() {
     auto cu0 = host_cu({0});
     EXPECT(kda_chunk_fwd(&p, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, cu_dev, cu0.get(), nullptr, nullptr,
                          nullptr, 0, nullptr) == KDA_OK);
+    // fused prologue: one defect per call
+    {
+        const float *tq = devf(10), *tk = devf(11), *tv = devf(12);
+        kda_problem_t pp = prefill();
+        EXPECT(kda_chunk_fwd_prologue(&pp, 5, 1e-6f, q, k, v, tq, tk, tv, g, beta, s0, nullptr, nullptr, out, sf, ws,
+                                      ws_bytes, nullptr) == KDA_ERR_UNSUPPORTED);
+        EXPECT(kda_chunk_fwd_prologue(&pp, 4, std::numeric_limits<float>::quiet_NaN(), q, k, v, tq, tk, tv, g, beta, s0,
+                                      nullptr, nullptr, out, sf, ws, ws_bytes, nullptr) == KDA_ERR_INVALID_ARGUMENT);
+        EXPECT(kda_chunk_fwd_prologue(&pp, 4, 1e-6f, q, k, v, nullptr, tk, tv, g, beta, s0, nullptr, nullptr, out, sf,
+                                      ws, ws_bytes, nullptr) == KDA_ERR_INVALID_ARGUMENT);
+        EXPECT(kda_chunk_fwd_prologue(&pp, 4, 1e-6f, q, k, v, tq, tk, tv, g, beta, s0, nullptr, nullptr, out, sf, ws,
+                                      1024, nullptr) == KDA_ERR_WORKSPACE);
+        pp.algo = KDA_ALGO_FUSED;
+        EXPECT(kda_chunk_fwd_prologue(&pp, 4, 1e-6f, q, k, v, tq, tk, tv, g, beta, s0, nullptr, nullptr, out, sf, ws,
+                                      ws_bytes, nullptr) == KDA_ERR_UNSUPPORTED);
+        pp = prefill();
+        pp.batch = 1;
+        pp.seq_len = 12;
+        pp.num_seqs = 3;
+        auto badp = host_cu({0, 5, 13, 12});
+        EXPECT(kda_chunk_fwd_prologue(&pp, 4, 1e-6f, q, k, v, tq, tk, tv, g, beta, s0, cu_dev, badp.get(), out, sf, ws,
+                                      ws_bytes, nullptr) == KDA_ERR_INVALID_ARGUMENT);
+    }
     // tune: refused before any timing
     kda_query_result_t best;
     p = prefill();

@@ -147,6 +147,33 @@ def test_decode_step_validation():
     assert f(*args(N=0)) == kda.KDA_OK
 
 
+def test_chunk_fwd_prologue_validation():
+    """Every refusal happens on the host, before any launch (no GPU needed): each call below has
+    exactly one defect."""
+    lib = kda.library()
+    P = lambda i: ctypes.c_void_p(0x100000 * (i + 1))
+    WS = ctypes.c_void_p(0x10000000)
+
+    def call(prob=None, W=4, eps=1e-6, taps=(P(3), P(4), P(5)), out=P(9), ws=WS, ws_bytes=1 << 30):
+        prob = prob or problem(seq_len=100)
+        return lib.kda_chunk_fwd_prologue(ctypes.byref(prob), W, eps, P(0), P(1), P(2), *taps, P(6), P(7), None, None,
+                                          None, out, None, ws, ws_bytes, None)
+    assert call(prob=problem(seq_len=100, algo=kda.KDA_ALGO_FUSED)) == kda.KDA_ERR_UNSUPPORTED
+    assert call(W=0) == kda.KDA_ERR_UNSUPPORTED
+    assert call(W=5) == kda.KDA_ERR_UNSUPPORTED
+    assert call(eps=-1.0) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert call(eps=float("inf")) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert call(taps=(P(3), None, P(5))) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert "conv_k" in lib.kda_last_error().decode()
+    assert call(taps=(P(3), P(4), ctypes.c_void_p(0x600002))) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert call(out=P(4)) == kda.KDA_ERR_INVALID_ARGUMENT  # out aliases conv_k
+    assert call(out=P(0)) == kda.KDA_ERR_INVALID_ARGUMENT  # out aliases q_raw
+    assert call(ws=None) == kda.KDA_ERR_WORKSPACE
+    assert call(ws_bytes=1024) == kda.KDA_ERR_WORKSPACE
+    assert call(prob=problem(seq_len=100, chunk_size=48)) == kda.KDA_ERR_UNSUPPORTED
+    assert call(prob=problem(batch=0)) == kda.KDA_OK  # nothing to compute, nothing launched
+
+
 def test_decode_step_gated_validation():
     """Every refusal happens on the host, before any launch (no GPU needed)."""
     lib = kda.library()

@@ -132,3 +132,107 @@ def test_prologue_then_chunk_fwd(algo):
     srel = np.abs(fin.double().cpu().numpy() - s_ref).max() / np.abs(s_ref).max()
     say(f"  out max_rel={rel:.3e} state max_rel={srel:.3e}")
     assert rel <= 2e-2 and srel <= 2e-2
+
+
+# ------------------------------------------------ prologue fused into the forward ----
+TOL_F32_ABS = 1e-4
+TOL_BF16_REL = 2e-2
+
+
+def fused_reference(inp, bounds, B, T, eps=EPS, s0=None, cu=None):
+    """Composed oracles: the prologue oracle (fp64), then the forward oracle on its outputs."""
+    q, k, v, g, b, _ = reference(inp, bounds, eps)
+    H, dk, dv = q.shape[1], q.shape[2], v.shape[2]
+    f32 = lambda x, d: np.ascontiguousarray(x.reshape(B, T, H, d), dtype=np.float32)
+    return oracle.fwd(f32(q, dk), f32(k, dk), f32(v, dv), f32(g, dk), np.ascontiguousarray(b.reshape(B, T, H), np.float32),
+                      initial_state=None if s0 is None else s0.numpy(), cu_seqlens=None if cu is None else cu.numpy())
+
+
+def compare_fused(name, got, ref, io):
+    g = got.detach().double().cpu().numpy()
+    assert g.shape == ref.shape and np.all(np.isfinite(g)), name
+    err = float(np.abs(g - ref).max()) if g.size else 0.0
+    scale = float(np.abs(ref).max()) if ref.size else 0.0
+    say(f"  {name}: max_abs={err:.3e} max_rel={err / scale if scale else err:.3e}")
+    if io == "f32":
+        assert err <= TOL_F32_ABS, name
+    else:
+        assert err <= TOL_BF16_REL * scale, name
+
+
+def run_fused(inp, s0=None, chunk=0, dv_tile=0, eps=EPS):
+    d = {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
+    return kda.chunk_fwd_prologue(d["q_raw"], d["k_raw"], d["v_raw"], d["conv_q"], d["conv_k"], d["conv_v"], d["g_raw"],
+                                  d["beta_raw"], None if s0 is None else s0.to(DEV), d["cu_seqlens"], norm_eps=eps,
+                                  chunk_size=chunk, dv_tile=dv_tile)
+
+
+@pytest.mark.parametrize("io,dk,dv", [("bf16", 128, 128), ("bf16", 64, 128), ("f32", 128, 64), ("f32", 64, 64)])
+@pytest.mark.parametrize("W", [1, 3, 4])
+@pytest.mark.parametrize("chunk", [0, 16, 64])
+def test_chunk_fwd_prologue_batch(io, dk, dv, W, chunk):
+    """kda_chunk_fwd_prologue (convolution, Swish, L2 norm, gate and beta activations inside the
+    two-pass kernels) against the prologue oracle followed by the forward oracle; T = 203 ends in a
+    partial chunk at every chunk size and crosses sub-chunk and chunk boundaries with the
+    convolution window."""
+    B, T, H = 2, 203, 3
+    say(f"fused prologue io={io} d_k={dk} d_v={dv} W={W} chunk={chunk}")
+    inp = ki.prologue_inputs(B, T, H, dk, dv, W, io, seed=100 + W + dk + chunk)
+    s0 = 0.1 * torch.randn((B, H, dk, dv), generator=torch.Generator().manual_seed(7))
+    r = kda.query(B, T, H, dk, dv, io, chunk_size=chunk, algo="two_pass")
+    if not r["supported"]:
+        pytest.skip(f"two-pass has no variant for {io} d_k={dk} chunk={chunk}")
+    out, fin = run_fused(inp, s0=s0, chunk=chunk)
+    torch.cuda.synchronize()
+    o_ref, f_ref = fused_reference(inp, [(0, T), (T, T)], B, T, s0=s0)
+    compare_fused("out", out, o_ref, io)
+    compare_fused("final_state", fin, f_ref, io)
+
+
+@pytest.mark.parametrize("chunk,dv_tile", [(0, 0), (32, 32), (64, 16), (64, 64)])
+def test_chunk_fwd_prologue_packed(chunk, dv_tile):
+    """Packed batch with empty, one- and two-token sequences (the convolution window restarts at
+    every sequence start, also inside a chunk slot's first rows) and the scan tilings."""
+    lengths = [0, 1, 2, 5, 70, 3, 0, 133, 64]
+    inp = ki.prologue_inputs(1, 0, 2, 128, 128, 4, "bf16", seed=31 + chunk + dv_tile, lengths=lengths)
+    T = sum(lengths)
+    bounds = [(int(inp["cu_seqlens"][n]), lengths[n]) for n in range(len(lengths))]
+    say(f"fused prologue packed lengths={lengths} chunk={chunk} dv_tile={dv_tile}")
+    out, fin = run_fused(inp, chunk=chunk, dv_tile=dv_tile)
+    torch.cuda.synchronize()
+    o_ref, f_ref = fused_reference(inp, bounds, 1, T, cu=inp["cu_seqlens"])
+    compare_fused("out", out, o_ref, "bf16")
+    compare_fused("final_state", fin, f_ref, "bf16")
+
+
+def test_chunk_fwd_prologue_matches_the_composition_on_the_gpu():
+    """The fused path against kda_prologue followed by kda_chunk_fwd (two-pass) on the same raw
+    inputs (the composition rounds q, k, v to bf16 between the calls; both within the bar of the
+    composed oracles), at 2 x 1,024 tokens x 8 heads, d = 128."""
+    B, T, H = 2, 1024, 8
+    inp = ki.prologue_inputs(B, T, H, 128, 128, 4, "bf16", seed=55)
+    d = {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
+    out_f, fin_f = run_fused(inp)
+    q, k, v, g, b = kda.prologue(d["q_raw"], d["k_raw"], d["v_raw"], d["conv_q"], d["conv_k"], d["conv_v"], d["g_raw"],
+                                 d["beta_raw"], norm_eps=EPS)
+    out_c, fin_c = kda.chunk_fwd(q, k, v, g, b, algo="two_pass")
+    torch.cuda.synchronize()
+    o_ref, f_ref = fused_reference(inp, [(n * T, T) for n in range(B)], B, T)
+    compare_fused("fused out", out_f, o_ref, "bf16")
+    compare_fused("fused final_state", fin_f, f_ref, "bf16")
+    compare_fused("composed out", out_c, o_ref, "bf16")
+    compare_fused("composed final_state", fin_c, f_ref, "bf16")
+
+
+def test_chunk_fwd_prologue_strong_decay():
+    """g_raw of 100 on one token and 20 over 40 tokens (g ~ -100 and -20 per token): the fused
+    prep's diagonal blocks switch to the split levels from registers; finite and within the bar."""
+    B, T, H = 1, 203, 2
+    inp = ki.prologue_inputs(B, T, H, 128, 128, 4, "bf16", seed=61)
+    inp["g_raw"][0, 37, :, 5] = 100.0
+    inp["g_raw"][0, 70:110, :, 9] = 20.0
+    out, fin = run_fused(inp, chunk=64)
+    torch.cuda.synchronize()
+    o_ref, f_ref = fused_reference(inp, [(0, T)], B, T)
+    compare_fused("out", out, o_ref, "bf16")
+    compare_fused("final_state", fin, f_ref, "bf16")
