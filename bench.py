@@ -462,7 +462,8 @@ def main():
         "decode_gated": {"kernel": "kda_decode_step_gated", "ms": round(t_decg, 4), "gb_per_s": round(decg_gbps, 1),
                          "hbm_frac": round(decg_gbps / PEAK_HBM_GBPS, 4), "bytes_per_launch": decg_bytes,
                          "composed_ms": round(t_decc, 4), "composed": "kda_decode_step + kda_norm_gate",
-                         "speedup_vs_composed": round(t_decc / t_decg, 3)},
+                         "speedup_vs_composed": round(t_decc / t_decg, 3),
+                         "traffic": traffic.get("decode_gated_bytes")},
         "tuned": None if tuned is None else {"chunk": tuned["chunk_size"], "dv_tile": tuned["dv_tile"],
                                              "algo": ["auto", "fused", "two_pass"][tuned["algo"]],
                                              "ms": round(tuned["tuned_ms"], 4)},
@@ -480,7 +481,8 @@ def main():
         "forward_raw": {"kernel": "kda_chunk_fwd_prologue", "conv_width": 4, "ms": round(t_rawf, 4),
                         "tokens_per_s": round(tokens / (t_rawf * 1e-3), 1), "composed_ms": round(t_rawc, 4),
                         "composed": "kda_prologue + kda_chunk_fwd (two-pass)",
-                        "speedup_vs_composed": round(t_rawc / t_rawf, 3)},
+                        "speedup_vs_composed": round(t_rawc / t_rawf, 3),
+                        "traffic": traffic.get("forward_raw_bytes")},
         "epilogue": {"kernel": "kda_norm_gate", "rows": epi_rows, "d": w.dv, "ms": round(t_epi, 4),
                      "gb_per_s": round(epi_gbps, 1), "hbm_frac": round(epi_gbps / PEAK_HBM_GBPS, 4),
                      "bytes_per_launch": epi_bytes, "traffic": traffic.get("epilogue_bytes")},
