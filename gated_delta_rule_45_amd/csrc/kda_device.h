@@ -46,6 +46,20 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float a) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Wait until at most N of this wave's vector memory loads are outstanding (they complete in
+// issue order); the other counters are left alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt holds 0..63");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land at
+// lds + 16 l (lds is the same for every lane of the wave).  The write is complete once this
+// wave's vmcnt has counted the load; other waves may read it after a barrier that follows.
+__device__ __forceinline__ void load_lds16(const void *src, void *lds) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+
 // Value from the lane n places lower in the same row of 16 lanes; 0 for the first n lanes.
 template <int N>
 __device__ __forceinline__ float row_shr(float x) {

@@ -633,7 +633,7 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
 // fragments are exactly the operand fragments of S^T, D's accumulator fragments those of
 // D^T, and the record's Q~ and P fragments serve unchanged as Q~^T and P^T.  Each lane then
 // holds 4 consecutive output columns of one token and stores them with one 8-byte write.
-// Copy waves per scan workgroup with two record buffers (see ScanLayout).
+// Copy waves per scan workgroup with two or more record buffers (see ScanLayout).
 constexpr int scan_copy_waves(int spw) { return spw == 1 ? 4 : 2; }
 
 template <typename IO, int DK, int C, int SPW, int NW>
@@ -647,35 +647,54 @@ struct ScanLayout {
     // as 16-byte row segments (a few wide stores instead of one per accumulator element)
     static constexpr int LDK = WCOLS + 4;
     static constexpr size_t kKeepBytes = (size_t)NW * 16 * LDK * 4;
-    // Two record buffers (chunk c + 1 is written while chunk c is read) where they fit with the
-    // kept-state tile; otherwise one (fp32 records at d_k = 128, chunk 64: 117 KB each), and the
-    // next chunk is written after a second barrier per chunk, once every wave is done reading.
-    static constexpr bool SINGLE = 2 * (Rec::kBytes + kVBytes) + kKeepBytes > 160 * 1024;
-    // Copy waves: with two buffers, pairs that hold one chunk each in registers (two pairs take
-    // turns with 16-column compute waves, so each chunk's loads are issued two chunks ahead; a
-    // third pair measured no faster; the wider compute waves need every register of their SIMD and
-    // keep a single pair, one chunk ahead).  With one buffer, a group of four holds the next chunk.
+    // One record buffer holds a chunk's record and its V tile.  At least two (chunk c + 1 is
+    // written while chunk c is read) where they fit with the kept-state tile; otherwise one (fp32
+    // records at d_k = 128, chunk 64: 117 KB each), and the next chunk is written after a second
+    // barrier per chunk, once every wave is done reading.
+    static constexpr size_t kBufBytes = Rec::kBytes + kVBytes;
+    static constexpr bool SINGLE = 2 * kBufBytes + kKeepBytes > 160 * 1024;
+    // LDS that the output-wave scan places after the buffers: its S and D slots, two per compute
+    // wave (SPW 16-column slices of the state in KT k tiles, and of D in 2 NPAIR row tiles).
+    static constexpr size_t kOwSlotBytes =
+        (size_t)2 * NW * SPW * (Rec::KT + 2 * Rec::NPAIR) * Rec::FRAG_BYTES * 64;
+    static constexpr bool buffers_fit(int n) { return n * kBufBytes + kOwSlotBytes + kKeepBytes <= 160 * 1024; }
+    // Buffers: as many as fit up to four, so that small records are loaded up to three chunks ahead.
+    static constexpr int NBUF = SINGLE ? 1 : buffers_fit(4) ? 4 : buffers_fit(3) ? 3 : 2;
+    // DIRECT (three or four buffers): the copy waves load each chunk from global memory straight
+    // into its LDS buffer (16 bytes per lane), NBUF - 1 chunks ahead.  Otherwise they load into
+    // registers and write LDS at the barrier that frees the buffer, which lets two buffers run two
+    // chunks ahead.  Measured on bf16, d_k = 128: one 131,072-token sequence x 32 heads at chunk 32
+    // (four buffers) 4.18 instead of 4.38 ms per forward call, 4 x 4,096 tokens x 16 heads at chunk
+    // 32 with 64-column tiles (three) 0.234 instead of 0.299 ms; with two buffers the direct copy
+    // (one chunk ahead) was slower, 0.246 instead of 0.219 ms at chunk 64.
+    static constexpr bool DIRECT = !SINGLE && NBUF >= 3;
+    // Copy waves.  Direct: every copy wave takes a share of every chunk.  Registers, two buffers:
+    // pairs that hold one chunk each (two pairs take turns with 16-column compute waves, so each
+    // chunk's loads are issued two chunks ahead; the wider compute waves need every register of
+    // their SIMD and keep a single pair, one chunk ahead).  One buffer: a group of four holds the
+    // next chunk.
     static constexpr int NCW = SINGLE ? 4 : scan_copy_waves(SPW);
-    static constexpr int GROUP = SINGLE ? 4 : 2;  // copy waves that share one chunk
+    static constexpr int GROUP = SINGLE ? 4 : DIRECT ? NCW : 2;  // copy waves that share one chunk
     static constexpr int NT = 64 * (NW + NCW);  // threads (compute waves + copy waves)
-    static constexpr size_t oRec0 = 0;
-    static constexpr size_t oRec1 = SINGLE ? 0 : Rec::kBytes;
-    static constexpr size_t oV0 = (SINGLE ? 1 : 2) * Rec::kBytes;
-    static constexpr size_t oV1 = SINGLE ? oV0 : oV0 + kVBytes;
-    static constexpr size_t kBytes = oV1 + kVBytes;
+    // [record 0 .. record NBUF-1][V 0 .. V NBUF-1]
+    static constexpr size_t oV = (size_t)NBUF * Rec::kBytes;
+    __host__ __device__ static constexpr size_t rec_off(int c) { return (size_t)(NBUF == 1 ? 0 : c % NBUF) * Rec::kBytes; }
+    __host__ __device__ static constexpr size_t v_off(int c) { return oV + (size_t)(NBUF == 1 ? 0 : c % NBUF) * kVBytes; }
+    static constexpr size_t kBytes = (size_t)NBUF * kBufBytes;
     static constexpr int UNITS_PER_WAVE = ((int)(Rec::kBytes / 1024) + V_PIECES / 64 + GROUP - 1) / GROUP;
-    // (the V tile is copied in whole wave units: a 16-column bf16 tile needs C >= 32)
-    static constexpr bool kFits = kBytes <= 160 * 1024 && UNITS_PER_WAVE <= 40 && (!SINGLE || SPW == 1) &&
-                                  V_PIECES % 64 == 0;
+    // (the V tile is copied in whole wave units: a 16-column bf16 tile needs C >= 32; register
+    // copies hold at most 40 units per lane, direct ones at most 63 loads in flight per wave)
+    static constexpr bool kFits = kBytes <= 160 * 1024 && (!SINGLE || SPW == 1) && V_PIECES % 64 == 0 &&
+                                  (DIRECT ? (NBUF - 1) * UNITS_PER_WAVE <= 63 : UNITS_PER_WAVE <= 40);
     static_assert(Rec::kBytes % (64 * 16) == 0, "record is copied in whole wave units");
     static constexpr bool kFitsKeep = kFits && kBytes + kKeepBytes <= 160 * 1024;
 };
 
 // One copy wave's share of a chunk's record and V tile (1 KB units dealt in turn to the GROUP
-// waves that share a chunk; IDX is this wave's place in its group).  The units are loaded into
-// registers (16 bytes per lane, all in flight at once) and later written to LDS; on gfx950 this
-// moves about twice the bytes per cycle of the direct global->LDS copy.  With SKIP_QP the Q~ and
-// P sections, which only the output uses, are not copied (their LDS stays stale and unread).
+// waves that share a chunk; IDX is this wave's place in its group), 16 bytes per lane, either
+// loaded into registers and later written to LDS (load, store) or loaded straight into LDS
+// (issue; the layouts with ScanLayout::DIRECT).  With SKIP_QP the Q~ and P sections, which only
+// the output uses, are not copied (their LDS stays stale and unread).
 template <typename IO, int DK, int C, int SPW, int NW, int IDX, bool SKIP_QP = false>
 struct ChunkStager {
     using S = ScanLayout<IO, DK, C, SPW, NW>;
@@ -716,6 +735,20 @@ struct ChunkStager {
             }
         }
     }
+    __device__ __forceinline__ void issue(const char *rec, const IO *vrow0, int clen, int64_t vstride, char *lds_rec,
+                                          char *lds_v, int lane) const {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int u = IDX + G * i;
+            if (u < USED) {
+                load_lds16(rec + (size_t)rec_unit(u) * 1024 + lane * 16, lds_rec + rec_unit(u) * 1024);
+            } else {
+                const int piece = (u - USED) * 64 + lane;
+                const int row = min(piece / PPR, clen - 1);  // rows past the end re-read the last row
+                load_lds16(vrow0 + row * vstride + (piece % PPR) * EP, lds_v + (u - USED) * 1024);
+            }
+        }
+    }
     __device__ __forceinline__ void store(char *lds_rec, char *lds_v, int lane) const {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
@@ -726,12 +759,14 @@ struct ChunkStager {
     }
 };
 
-// Copy wave CW.  Group CW / GROUP stages the chunks j with j % NPAIR == CW / GROUP.  With two
-// buffers, barrier c hands chunk c to the compute waves; passing it also means every compute wave
-// has finished chunk c - 1, so that buffer may take chunk c + 1 (written from the registers of its
-// group, which then load their next chunk).  With one buffer every chunk has a second barrier,
-// after which every wave is done reading chunk c and chunk c + 1 (loaded while c was read) is
-// written.
+// Copy wave CW.  Barrier c hands chunk c to the compute waves; passing it also means every
+// compute wave has finished chunk c - 1, so that buffer may take the next chunk.  DIRECT: the
+// loads of chunk c + NBUF - 1 go into that buffer, and before barrier c + 1 each copy wave waits
+// until its share of chunk c + 1 has landed (the newer chunks may still be in flight).  Registers,
+// two buffers: group CW / GROUP stages the chunks j with j % NPAIR == CW / GROUP; the freed buffer
+// takes chunk c + 1 from the registers of its group, which then load their next chunk.  One
+// buffer: every chunk has a second barrier, after which every wave is done reading chunk c and
+// chunk c + 1 (loaded while c was read) is written.
 template <typename IO, int DK, int C, int SPW, int NW, int CW, bool SKIP_QP = false>
 __device__ __forceinline__ void copy_wave(char *smem, const char *rec0, size_t rec_stride, const IO *vbase,
                                           int64_t vstride, int len, int nchunks, int lane) {
@@ -741,9 +776,24 @@ __device__ __forceinline__ void copy_wave(char *smem, const char *rec0, size_t r
     ChunkStager<IO, DK, C, SPW, NW, CW % S::GROUP, SKIP_QP> st;
 #define KDA_STAGE_LOAD(j) \
     st.load(rec0 + (size_t)(j) * rec_stride, vbase + (int64_t)(j) * C * vstride, min(C, len - (j) * C), vstride, lane)
-#define KDA_STAGE_STORE(j) \
-    st.store(smem + (((j) & 1) ? S::oRec1 : S::oRec0), smem + (((j) & 1) ? S::oV1 : S::oV0), lane)
-    if constexpr (S::SINGLE) {
+#define KDA_STAGE_STORE(j) st.store(smem + S::rec_off(j), smem + S::v_off(j), lane)
+#define KDA_STAGE_ISSUE(j)                                                                                \
+    st.issue(rec0 + (size_t)(j) * rec_stride, vbase + (int64_t)(j) * C * vstride, min(C, len - (j) * C), \
+             vstride, smem + S::rec_off(j), smem + S::v_off(j), lane)
+    if constexpr (S::DIRECT) {
+        constexpr int NB = S::NBUF;
+        for (int j = 0; j < NB - 1 && j < nchunks; ++j) KDA_STAGE_ISSUE(j);
+        wait_vmcnt<0>();
+        for (int c = 0; c < nchunks; ++c) {
+            __syncthreads();  // barrier c: chunk c is in LDS, the buffer of chunk c - 1 is free
+            if (c + NB - 1 < nchunks) {
+                KDA_STAGE_ISSUE(c + NB - 1);
+                wait_vmcnt<(NB - 2) * decltype(st)::PER>();  // this wave's share of chunk c + 1 has landed
+            } else {
+                wait_vmcnt<0>();
+            }
+        }
+    } else if constexpr (S::SINGLE) {
         if (nchunks > 0) {
             KDA_STAGE_LOAD(0);
             KDA_STAGE_STORE(0);
@@ -785,6 +835,7 @@ __device__ __forceinline__ void copy_wave(char *smem, const char *rec0, size_t r
     }
 #undef KDA_STAGE_LOAD
 #undef KDA_STAGE_STORE
+#undef KDA_STAGE_ISSUE
 }
 
 // Fused prologue (PRO) in the scans: V rows 16 r2 + 4 q4 + j (j < 4) of one column as the operator
@@ -932,8 +983,8 @@ __global__ void __launch_bounds__((ScanLayout<IO, DK, C, SPW, NW>::NT)) kda_scan
                 keep_rows<OT, WC, S::LDK>(hs + (int64_t)16 * ct * DV, DV, keep_tile, lane);
             }
         }
-        const char *rb = smem + ((c & 1) ? S::oRec1 : S::oRec0);
-        const IO *vb = reinterpret_cast<const IO *>(smem + ((c & 1) ? S::oV1 : S::oV0));
+        const char *rb = smem + S::rec_off(c);
+        const IO *vb = reinterpret_cast<const IO *>(smem + S::v_off(c));
 
         FragPair<BF> Kf[NSUB][KP], Qf[NSUB][KP], Tf[NSUB][NPAIR], Pf[NSUB][NPAIR], Bf[KT][NPAIR];
         // V as stored (converted where Y is formed), or with the fused prologue already applied
@@ -1147,6 +1198,7 @@ struct ScanOwLayout {
     static constexpr size_t oSb = S::kBytes;                                     // [parity][wave][unit][lane]
     static constexpr size_t oDb = oSb + (size_t)2 * NW * SB_UNITS * 64 * 16;
     static constexpr size_t kBytes = oDb + (size_t)2 * NW * DB_UNITS * 64 * 16;
+    static_assert(kBytes - S::kBytes == S::kOwSlotBytes, "slot bytes counted when choosing the buffers");
     static constexpr bool kFits = S::kFits && !S::SINGLE && kBytes <= 160 * 1024;
     // KEEP: after the slots, one fp32 [KROWS][LDK] tile per writer wave (kept rows leave through
     // it): 64 rows where they fit, so a chunk's state and D leave in 3 read-backs, else 16
@@ -1330,7 +1382,7 @@ __global__ void __launch_bounds__((ScanOwLayout<IO, DK, C, SPW, NW>::NT)) kda_sc
         for (int c = 0; c < nchunks; ++c) {
             __syncthreads();  // chunk c is in LDS; S of chunk c and D of chunk c - 1 are in their slots
             if (c > 0) finish(c - 1);
-            const char *rb = smem + ((c & 1) ? S::oRec1 : S::oRec0);
+            const char *rb = smem + S::rec_off(c);
             Frag<BF> Sb[SPW * KT];
             slot_get<BF, SBN>(smem + SO::oSb + (size_t)(((c & 1) * NW + ow) * SO::SB_UNITS) * 64 * 16, lane, Sb);
             FragPair<BF> Qf[NSUB][KP];
@@ -1394,8 +1446,8 @@ __global__ void __launch_bounds__((ScanOwLayout<IO, DK, C, SPW, NW>::NT)) kda_sc
     constexpr int KT_H = (KT + 1) / 2;
     for (int c = 0; c < nchunks; ++c) {
         __syncthreads();  // chunk c is in LDS
-        const char *rb = smem + ((c & 1) ? S::oRec1 : S::oRec0);
-        const IO *vb = reinterpret_cast<const IO *>(smem + ((c & 1) ? S::oV1 : S::oV0));
+        const char *rb = smem + S::rec_off(c);
+        const IO *vb = reinterpret_cast<const IO *>(smem + S::v_off(c));
 
         FragPair<BF> Kf[NSUB][KP], Tf[NSUB][NPAIR], Bf[KT][NPAIR];
         typename std::conditional<PRO, float, IO>::type vv[SPW][NSUB][4];  // see kda_scan_kernel
