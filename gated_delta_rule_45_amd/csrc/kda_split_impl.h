@@ -193,10 +193,11 @@ struct PrepLayout {
 // Three workgroups per CU (4 waves each): the kernel is bound by memory latency, and the waves of
 // the other workgroups hide it.
 // PRO: the inputs are the raw projections and phase 1 applies the prologue as it loads them (see
-// FwdParams::conv): each lane's raw k and q for its token and for the token three back (zero before
-// the sequence start), the two tokens between from its row neighbours by DPP row shifts, the
-// 4-tap causal convolution and Swish in fp32, then the L2 norm over the token's d_k channels
-// (the four lanes of a token); g = -softplus(g_raw) and beta = sigmoid(beta_raw) where read.
+// FwdParams::conv): each lane's raw k and q for its token, the three tokens before it from its row
+// neighbours by DPP row shifts (the first three lanes of a row of 16 tokens also load the three
+// tokens before the row, zero before the sequence start), the 4-tap causal convolution and Swish
+// in fp32, then the L2 norm over the token's d_k channels (the four lanes of a token);
+// g = -softplus(g_raw) and beta = sigmoid(beta_raw) where read.
 template <typename IO, int DK, int C, bool PRO = false>
 __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_t *__restrict__ chunk_off,
                                                        char *__restrict__ records) {
@@ -255,8 +256,9 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
         const int64_t row = ((tok0 + r) * H + h) * (int64_t)DK + 4 * q4;
         const float m = valid ? kLog2e : 0.f;
         if constexpr (PRO) {
-            // token three back: inside the sequence (this or the previous chunk) or zero
-            const bool has3 = (int64_t)c * C + 16 * R + l16 - 3 >= 0;
+            // token three back: inside the sequence (this or the previous chunk) or zero; loaded by
+            // the first three lanes of each row only, the others take it from the lane three below
+            const bool has3 = (int64_t)c * C + 16 * R + l16 - 3 >= 0 && l16 < 3;
             const int64_t row3 = ((tok0 + min(16 * R + l16 - 3, clen - 1)) * H + h) * (int64_t)DK + 4 * q4;
             // every load in flight first, packed as loaded
             using KQ = typename std::conditional<BF, uint2, float4>::type;
@@ -286,18 +288,20 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
                     const int ch = 16 * ct + 4 * q4 + j;
                     G[ct][j] = neg_softplus_f(gx[j]) * m;
                     const float4 tq = sTap[ch], tk = sTap[DK + ch];
-                    // raw inputs of tokens t-2 and t-1: row neighbours, or (first lanes of the row)
-                    // the token-three-back loads of lanes 1 and 2
+                    // raw inputs of tokens t-3, t-2 and t-1: row neighbours, or (first lanes of the
+                    // row) the token-three-back loads of lanes 0, 1 and 2
                     const float ka = row_shr<1>(kx0[j]), kb = row_shl<2>(kx3[j]);
                     const float kc = row_shr<2>(kx0[j]), kd = row_shl<1>(kx3[j]);
+                    const float ke = row_shr<3>(kx0[j]);
                     const float qa = row_shr<1>(qx0[j]), qb = row_shl<2>(qx3[j]);
                     const float qc = row_shr<2>(qx0[j]), qd = row_shl<1>(qx3[j]);
-                    const float k1 = l16 >= 1 ? ka : kb, k2 = l16 >= 2 ? kc : kd;
-                    const float q1 = l16 >= 1 ? qa : qb, q2 = l16 >= 2 ? qc : qd;
+                    const float qe = row_shr<3>(qx0[j]);
+                    const float k1 = l16 >= 1 ? ka : kb, k2 = l16 >= 2 ? kc : kd, k3 = l16 >= 3 ? ke : kx3[j];
+                    const float q1 = l16 >= 1 ? qa : qb, q2 = l16 >= 2 ? qc : qd, q3 = l16 >= 3 ? qe : qx3[j];
                     float ck = 0.f, cq = 0.f;
-                    ck = fmaf(tk.x, kx3[j], ck); ck = fmaf(tk.y, k2, ck);
+                    ck = fmaf(tk.x, k3, ck); ck = fmaf(tk.y, k2, ck);
                     ck = fmaf(tk.z, k1, ck); ck = fmaf(tk.w, kx0[j], ck);
-                    cq = fmaf(tq.x, qx3[j], cq); cq = fmaf(tq.y, q2, cq);
+                    cq = fmaf(tq.x, q3, cq); cq = fmaf(tq.y, q2, cq);
                     cq = fmaf(tq.z, q1, cq); cq = fmaf(tq.w, qx0[j], cq);
                     kr[ct][j] = swish_f(ck);
                     qr[ct][j] = swish_f(cq);
