@@ -1117,6 +1117,19 @@ __global__ void __launch_bounds__(64 * (DK / 16)) kda_bwd_grad_kernel(BwdParams 
     }
     __syncthreads();
 
+    // rows c = cw + l16 of S and dS (A operands straight from the chunk states, operand type: 4
+    // consecutive columns are an A fragment), loaded here so that they arrive during the dP / dA products
+    Frag<BF> sf[DV / 16], dsf[DV / 16];
+    {
+        const OT *Sr = static_cast<const OT *>(bp.hs) + base * DK * DV + (int64_t)(cw + l16) * DV + 4 * q4;
+        const OT *dSr = static_cast<const OT *>(bp.dhs) + base * DK * DV + (int64_t)(cw + l16) * DV + 4 * q4;
+#pragma unroll
+        for (int kt = 0; kt < DV / 16; ++kt) {
+            sf[kt] = lds_frag(Sr + 16 * kt);
+            dsf[kt] = lds_frag(dSr + 16 * kt);
+        }
+    }
+
     // ---- dP = scale lower_incl(dO D^T), dA = -strictly_lower(dU D^T), block pairs R >= I
 #pragma unroll
     for (int pi0 = 0; pi0 < L::NPAIR; pi0 += NW) {
@@ -1163,20 +1176,13 @@ __global__ void __launch_bounds__(64 * (DK / 16)) kda_bwd_grad_kernel(BwdParams 
         }
     }
 
-    // ---- rows c = cw + l16 of S and dS (A operands straight from the chunk states), rowsum(dS .* S),
-    //      and dS D^T; S dO^T and S dU^T are formed later, just before the row side needs them
-    Frag<BF> sf[DV / 16];
+    // ---- rowsum(dS .* S) over the rows c = cw + l16 of S and dS, and dS D^T; S dO^T and S dU^T are
+    //      formed later, just before the row side needs them
     f32x4 Zs[NSUB];
     {
-        // the states are stored in the operand type: 4 consecutive columns are an A fragment
-        const OT *Sr = static_cast<const OT *>(bp.hs) + base * DK * DV + (int64_t)(cw + l16) * DV + 4 * q4;
-        const OT *dSr = static_cast<const OT *>(bp.dhs) + base * DK * DV + (int64_t)(cw + l16) * DV + 4 * q4;
-        Frag<BF> dsf[DV / 16];
         float gam = 0.f;
 #pragma unroll
         for (int kt = 0; kt < DV / 16; ++kt) {
-            sf[kt] = lds_frag(Sr + 16 * kt);
-            dsf[kt] = lds_frag(dSr + 16 * kt);
             const float4 a = unpack4<BF>(sf[kt].v), b = unpack4<BF>(dsf[kt].v);
             gam += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
         }
