@@ -551,19 +551,6 @@ kda_status_t kda_chunk_bwd(const kda_problem_t *problem, const void *q, const vo
         fp.dch = ws + b.off_dch;
         fp.chunk_off = varlen ? chunk_off : nullptr;
         fp.order = varlen ? kda::plan_order(ws, r.num_seqs) : nullptr;  // longest sequences first
-        if (b.two_pass) {  // the two-pass forward builds the chunk-offset table itself
-            st = hip_status(kda::launch_split_fwd(dtype_of(problem->io_dtype), fp, b.chunk, 1, 2, ws, b.slots, s),
-                            "kda_chunk_bwd forward launch");
-        } else {
-            if (varlen) {
-                st = hip_status(kda::launch_chunk_plan(cu_seqlens, r.num_seqs, b.chunk, ws, s),
-                                "kda_chunk_bwd plan launch");
-                if (st != KDA_OK) return st;
-            }
-            st = hip_status(kda::launch_chunk_fwd(dtype_of(problem->io_dtype), fp, kda::ChunkConfig{b.chunk, b.fwd_dv_tile}, s),
-                            "kda_chunk_bwd forward launch");
-        }
-        if (st != KDA_OK) return st;
         kda::BwdParams bp;
         bp.f = fp;
         bp.d_out = d_out;
@@ -581,9 +568,31 @@ kda_status_t kda_chunk_bwd(const kda_problem_t *problem, const void *q, const vo
         bp.brec = ws + b.off_brec;
         bp.split_flag = reinterpret_cast<int32_t *>(ws + b.off_flag);
         bp.slots = b.slots;
-        const hipError_t e = problem->io_dtype == KDA_BF16 ? kda::launch_bwd_bf16(bp, b.chunk, s)
-                                                           : kda::launch_bwd_f32(bp, b.chunk, s);
-        return hip_status(e, "kda_chunk_bwd launch");
+        auto launch_bwd = [&](int phases) {
+            bp.phases = phases;
+            return problem->io_dtype == KDA_BF16 ? kda::launch_bwd_bf16(bp, b.chunk, s) : kda::launch_bwd_f32(bp, b.chunk, s);
+        };
+        if (varlen) {
+            st = hip_status(kda::launch_chunk_plan(cu_seqlens, r.num_seqs, b.chunk, ws, s), "kda_chunk_bwd plan launch");
+            if (st != KDA_OK) return st;
+        }
+        if (b.two_pass) {
+            // the backward's prep kernel also writes the two-pass forward's records (one pass over
+            // q, k, g and beta serves both); the forward then launches its scan only
+            bp.frec = ws + kda::split_plan_bytes(r.num_seqs);
+            st = hip_status(launch_bwd(1), "kda_chunk_bwd prep launch");
+            if (st != KDA_OK) return st;
+            kda::FwdParams fk = fp;
+            fk.skip_prep = true;
+            st = hip_status(kda::launch_split_fwd(dtype_of(problem->io_dtype), fk, b.chunk, 1, 2, ws, b.slots, s),
+                            "kda_chunk_bwd forward launch");
+            if (st != KDA_OK) return st;
+            return hip_status(launch_bwd(2), "kda_chunk_bwd launch");
+        }
+        st = hip_status(kda::launch_chunk_fwd(dtype_of(problem->io_dtype), fp, kda::ChunkConfig{b.chunk, b.fwd_dv_tile}, s),
+                        "kda_chunk_bwd forward launch");
+        if (st != KDA_OK) return st;
+        return hip_status(launch_bwd(3), "kda_chunk_bwd launch");
     } catch (...) {
         return fail(KDA_ERR_HIP, "unexpected exception in kda_chunk_bwd");
     }

@@ -23,10 +23,12 @@
 //          W_rc = sum_i dA_ri k_ic e^{G_rc - G_ic}
 //
 // Four launches:
-//   1. the forward again (two-pass, or the fused kernel where no two-pass variant exists)
-//      keeps each chunk's initial state S and D;
-//   2. kda_bwd_prep_kernel: one workgroup per (chunk, head), all chunks in parallel; builds
-//      the chunk's gated operands, A^T, P^T and the diagonal blocks of X^T as one record;
+//   1. kda_bwd_prep_kernel: one workgroup per (chunk, head), all chunks in parallel; builds
+//      the chunk's gated operands, A^T, P^T and the diagonal blocks of X^T as one record, and
+//      (two-pass forward) the forward's record of the chunk from the same operands: K~, K-^T,
+//      T = X Diag(beta) and e^{G_C}, the same values the forward's prep kernel writes;
+//   2. the forward again (its scan only on those records, or the fused kernel where no two-pass
+//      variant exists, launched before the prep kernel) keeps each chunk's initial state S and D;
 //   3. kda_bwd_scan_kernel: one workgroup per (sequence, head, d_v tile), chunks in
 //      reverse order; streams the records, keeps dS in registers, writes dv, dU and the
 //      chunk-end dS of every chunk, and d(initial state);
@@ -46,6 +48,7 @@
 #include "kda_chunk_impl.h"
 #include "kda_device.h"
 #include "kda_internal.h"
+#include "kda_split_record.h"
 
 namespace kda {
 
@@ -341,6 +344,9 @@ __global__ void __launch_bounds__(kChunkThreads) kda_bwd_prep_kernel(BwdParams b
     const int len = p.cu ? p.cu[n + 1] - p.cu[n] : p.T;
     const int clen = min(C, len - ci * C);
     char *rec = records + (size_t)(slot * H + h) * Rec::kBytes;
+    // the forward's record of this chunk (BwdParams::frec): written alongside, from the same operands
+    using FRec = SplitRecord<IO, DK, C>;
+    char *frec = bp.frec ? bp.frec + (size_t)(slot * H + h) * FRec::kBytes : nullptr;
 
     BwdRaw<IO, DK> raw;
     bwd_load_keys<IO, DK, C>(raw, p, start + (int64_t)ci * C, clen, h, tid);
@@ -393,7 +399,9 @@ __global__ void __launch_bounds__(kChunkThreads) kda_bwd_prep_kernel(BwdParams b
 #pragma unroll
             for (int I = 0; I + 2 <= R; ++I) sSH[L::shift_slot(R, I) * DK + c] = fast_exp2(bnd[R] - bnd[I + 1]);
         }
-        sGam[c] = fast_exp2(gc);
+        const float gam = fast_exp2(gc);
+        sGam[c] = gam;
+        if (frec) reinterpret_cast<float *>(frec + FRec::oGam)[c] = gam;
     }
     __syncthreads();
 
@@ -406,6 +414,7 @@ __global__ void __launch_bounds__(kChunkThreads) kda_bwd_prep_kernel(BwdParams b
         const float br = sBeta[16 * R + l16];
         OT *rq = reinterpret_cast<OT *>(rec + Rec::oQtT);
         OT *rk = reinterpret_cast<OT *>(rec + Rec::oBKtT);
+        Frag<BF> fk_even;  // forward record: the even channel tile's K~ fragment, stored with the odd one's
 #pragma unroll
         for (int ct = 0; ct < KT; ++ct) {
             const int c = 16 * ct + 4 * q4;
@@ -419,14 +428,15 @@ __global__ void __launch_bounds__(kChunkThreads) kda_bwd_prep_kernel(BwdParams b
             const float ecv[4] = {ec.x, ec.y, ec.z, ec.w};
             const float4 kv = unpack4<BF>(raw.k[ct]), qv = unpack4<BF>(raw.q[ct]);
             const float kx[4] = {kv.x, kv.y, kv.z, kv.w}, qx[4] = {qv.x, qv.y, qv.z, qv.w};
-            float kb[4], kt[4], qt[4], kbar[4], kd[4];
+            float kb[4], kt[4], qt[4], kbar[4], kd[4], kf[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const float fr = valid ? fast_exp2(G[ct][j]) : 0.f;
                 const float fb = valid ? fast_exp2(tv[j] - G[ct][j]) : 0.f;
                 kb[j] = kx[j] * fb;
                 kd[j] = kb[j] * edv[j];
-                kt[j] = kx[j] * fr * ebv[j] * br;
+                kf[j] = kx[j] * fr * ebv[j];  // the forward's K~
+                kt[j] = kf[j] * br;
                 qt[j] = qx[j] * fr * ebv[j];
                 kbar[j] = kb[j] * ecv[j];
             }
@@ -441,6 +451,22 @@ __global__ void __launch_bounds__(kChunkThreads) kda_bwd_prep_kernel(BwdParams b
             *reinterpret_cast<decltype(tq.v) *>(rq + toff) = tq.v;
             const Frag<BF> tk = bwd_turn<BF>(make_frag<BF>(kt[0], kt[1], kt[2], kt[3]), eye);
             *reinterpret_cast<decltype(tk.v) *>(rk + toff) = tk.v;
+            if (frec) {
+                // K~ in 16 x 32 operand tiles (row tile R, channel tile pair ct / 2); K-^T: the turned
+                // fragment is this sub-chunk's half of operand tile (ct, R / 2)
+                const Frag<BF> fk = make_frag<BF>(kf[0], kf[1], kf[2], kf[3]);
+                if (ct % 2 == 0) fk_even = fk;
+                else store_pair<BF>(frec + FRec::oKt + (size_t)(R * (KT / 2) + ct / 2) * FRec::TILE_BYTES, lane, fk_even, fk);
+                *reinterpret_cast<decltype(tb.v) *>(frec + FRec::oKbT + ((size_t)ct * FRec::NPAIR + R / 2) * FRec::TILE_BYTES +
+                                                    lane * FRec::PAIR_BYTES + (R % 2) * FRec::FRAG_BYTES) = tb.v;
+            }
+        }
+        if (frec && NSUB % 2 == 1 && R == NSUB - 1) {  // odd sub-chunk count: the unused half of the last pair
+            const Frag<BF> z = make_frag<BF>(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int ct = 0; ct < KT; ++ct)
+                *reinterpret_cast<decltype(z.v) *>(frec + FRec::oKbT + ((size_t)ct * FRec::NPAIR + R / 2) * FRec::TILE_BYTES +
+                                                   lane * FRec::PAIR_BYTES + FRec::FRAG_BYTES) = z.v;
         }
     }
     __syncthreads();
@@ -579,6 +605,32 @@ __global__ void __launch_bounds__(kChunkThreads) kda_bwd_prep_kernel(BwdParams b
             *reinterpret_cast<float4 *>(sX + (16 * I + l16) * LDX + 16 * R + 4 * q4) = make_float4(xo[0], xo[1], xo[2], xo[3]);
         }
         __syncthreads();
+    }
+    // forward record: T = X Diag(beta) in its half tiles (X_RR in place, X_RI stored transposed in
+    // block (I, R); rows l16, columns 4 q4 + j of each 16 x 16 block)
+    if (frec && wave < NSUB) {
+        const int R = wave;
+#pragma unroll
+        for (int pp = 0; pp < FRec::NPAIR; ++pp) {
+            if (2 * pp > R) break;
+            Frag<BF> f[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int I = 2 * pp + u;
+                float4 xv = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (I == R) {
+                    xv = *reinterpret_cast<const float4 *>(sX + (16 * R + l16) * LDX + 16 * R + 4 * q4);
+                } else if (I < R) {
+                    const float *xt = sX + (16 * I + 4 * q4) * LDX + 16 * R + l16;
+                    xv = make_float4(xt[0], xt[LDX], xt[2 * LDX], xt[3 * LDX]);
+                }
+                const float4 bv = I < NSUB ? *reinterpret_cast<const float4 *>(sBeta + 16 * I + 4 * q4)
+                                           : make_float4(0.f, 0.f, 0.f, 0.f);
+                f[u] = make_frag<BF>(xv.x * bv.x, xv.y * bv.y, xv.z * bv.z, xv.w * bv.w);
+            }
+            if (FRec::tp_half(R, pp)) store_frag<BF>(frec + FRec::oT + FRec::tp_off(R, pp), lane, f[0]);
+            else store_pair<BF>(frec + FRec::oT + FRec::tp_off(R, pp), lane, f[0], f[1]);
+        }
     }
 
     // ================= 6: M^T = K-^T X in tiles (16 channels x 16 tokens), each accumulator
@@ -1439,12 +1491,13 @@ hipError_t launch_bwd_variant(const BwdParams &bp, hipStream_t stream) {
     } else {
         const FwdParams &p = bp.f;
         const int64_t prep_blocks = bp.slots * p.H;
-        if (prep_blocks > 0) {
+        if (prep_blocks > 0 && (bp.phases & 1)) {
             hipLaunchKernelGGL((kda_bwd_prep_kernel<IO, DK, C>), dim3((unsigned)prep_blocks), dim3(kChunkThreads), 0,
                                stream, bp, bp.brec);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
+        if (!(bp.phases & 2)) return hipSuccess;
         const int64_t scan_blocks = (int64_t)p.num_seqs * p.H * (DV / kBwdScanTile);
         if (scan_blocks > 0) {
             hipLaunchKernelGGL((kda_bwd_scan_kernel<IO, DK, C>), dim3((unsigned)scan_blocks),

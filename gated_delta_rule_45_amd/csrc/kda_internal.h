@@ -43,6 +43,9 @@ struct FwdParams {
     const float *conv[3] = {nullptr, nullptr, nullptr};
     int32_t conv_w = 0;
     float norm_eps = 0.f;
+    // two-pass forward without its plan and prep launches: the chunk offsets and the records are
+    // already in the workspace (the backward's prep kernel writes them)
+    bool skip_prep = false;
 };
 
 // Chunk-forward configuration chosen by the host.
@@ -119,6 +122,10 @@ struct BwdParams {
     int32_t *split_flag;  // [slot, H] 1 where a sub-chunk of the chunk decays beyond the single-anchor
                           // limit of the diagonal blocks (kda_bwd_prep_kernel writes every entry)
     int64_t slots;        // upper bound on the number of chunk slots
+    // [slot, H] two-pass forward records for the forward pass that keeps S and D (K~, K-^T, T and
+    // e^{G_C}; the output's Q~ and P are left out), written by kda_bwd_prep_kernel; null: not written
+    char *frec = nullptr;
+    int phases = 3;  // launches: 1 = the prep kernel, 2 = the reverse scan and the gradients
 };
 bool bwd_supported_bf16(int dk, int dv, int chunk);
 size_t bwd_record_bytes_bf16(int dk, int chunk);
