@@ -3,7 +3,8 @@
 
 One step = one pass of the hot path over one batch of synthetic input:
   * kda_chunk_fwd over the prefill workload (B=4, T=4096, H=16, d_k=d_v=128, bf16 q/k/v,
-    fp32 gate/beta/state, chunk 64, initial state given, final state written), and
+    fp32 gate/beta/state, the library-default chunk (32), initial state given, final state
+    written), and
   * kda_decode_step over the decode workload (256 sequences x 32 heads, fp32 state
     128x128 updated in place).
 The long-prefill (1 x 131,072 tokens x 32 heads) and packed-varlen (64 sequences, lengths
@@ -240,7 +241,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--dv-tile", type=int, default=0)
-    ap.add_argument("--chunk", type=int, default=64)
+    ap.add_argument("--chunk", type=int, default=0, help="forward chunk (0: the library's default)")
+    ap.add_argument("--bwd-chunk", type=int, default=64, help="backward chunk")
     ap.add_argument("--algo", default="auto", choices=["auto", "fused", "two_pass"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-workloads", action="store_true",
@@ -335,14 +337,14 @@ def main():
 
     # ------------------------------------------- backward (training) on the prefill tensors
     d_out_b, dsf_b = (None if x is None else x.to(dev) for x in ki.grad_inputs(inp, 8))
-    bp, _ = kda._problem_from(d["q"], d["v"], None, args.chunk, 1.0, 0, 0)
+    bp, _ = kda._problem_from(d["q"], d["v"], None, args.bwd_chunk, 1.0, 0, 0)
     bws = torch.empty(kda.bwd_workspace_bytes(bp), dtype=torch.uint8, device=dev)
     bout = kda.chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d_out_b, initial_state=d["s0"],
-                         d_final_state=dsf_b, chunk_size=args.chunk, workspace=bws)
+                         d_final_state=dsf_b, chunk_size=args.bwd_chunk, workspace=bws)
 
     def backward():
         kda.chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d_out_b, initial_state=d["s0"], d_final_state=dsf_b,
-                      chunk_size=args.chunk, workspace=bws, out=bout)
+                      chunk_size=args.bwd_chunk, workspace=bws, out=bout)
 
     # ------------------------------------------- general-DPLR comparator on the prefill tensors
     a_d, b_d, kw_d = (x.to(dev) for x in ki.dplr_inputs(inp, 9))
@@ -467,7 +469,7 @@ def main():
         "tuned": None if tuned is None else {"chunk": tuned["chunk_size"], "dv_tile": tuned["dv_tile"],
                                              "algo": ["auto", "fused", "two_pass"][tuned["algo"]],
                                              "ms": round(tuned["tuned_ms"], 4)},
-        "backward": {"kernel": "kda_chunk_bwd", "chunk": args.chunk, "ms": round(t_bwd, 4),
+        "backward": {"kernel": "kda_chunk_bwd", "chunk": args.bwd_chunk, "ms": round(t_bwd, 4),
                      "tokens_per_s": round(tokens / (t_bwd * 1e-3), 1), "gb_per_s": round(bwd_gbps, 1),
                      "hbm_frac": round(bwd_gbps / PEAK_HBM_GBPS, 4), "bytes_per_launch": bwd_bytes,
                      "traffic": traffic.get("backward_bytes")},

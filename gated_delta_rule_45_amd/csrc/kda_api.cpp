@@ -60,7 +60,20 @@ int64_t sat_mul(int64_t a, int64_t b, int64_t c) { return sat_mul(sat_mul(a, b),
 // Published MI355X peaks used for roofline fractions.
 constexpr double kPeakBf16Tflops = 2500.0;
 constexpr double kPeakHbmGBps = 8000.0;
-constexpr int kAssumedCUs = 256;
+
+// Compute units of the current device, read once per device (256 on MI355X; also the value used
+// when no device is visible, as for the host-only queries).
+int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
 
 struct Resolved {
     int64_t tokens = 0;     // flattened token count
@@ -73,21 +86,19 @@ struct Resolved {
     size_t ws_bytes = 0;            // two-pass: workspace bytes
 };
 
-// Default chunk: 64, or 32 where the sequential chunk chain is the critical path (too few
-// (sequence, head) chains to give every CU a 32-column scan workgroup), which halves each step
-// of the chain (measured on one 131,072-token sequence x 32 heads: 4.72 vs 5.14 ms).
-int default_chunk(const kda_problem_t &p, int64_t chains) {
-    if (p.io_dtype == KDA_F32 && p.head_dim_k == 128) return 32;
-    if (chains * (p.head_dim_v / 32) < kAssumedCUs) return 32;
-    return 64;
-}
+// Default chunk: 32.  Measured with d_k = d_v = 128 in bf16, against chunk 64: 4 x 4,096 tokens x
+// 16 heads 0.208 vs 0.220 ms, 64 packed sequences x 32 heads 5.60 vs 5.77 ms, one 131,072-token
+// sequence x 32 heads 4.14 vs 4.47 ms.  The prep kernel does less block work per token (three
+// 16 x 16 blocks of A and P per 32 tokens instead of ten per 64) with four workgroups of two
+// waves per SIMD pair, and the scan's records are small enough for direct staging.
+int default_chunk(const kda_problem_t &, int64_t) { return 32; }
 
 // d_v tile: whole rows of the state per workgroup when there are enough (sequence, head)
 // chains to fill the GPU, otherwise narrower tiles so more workgroups run side by side
 // (each tile redoes the key-side work of its chunk).
 int default_dv_tile(int64_t chains, int dv) {
     int t = dv;
-    while (t > 32 && chains * (dv / t) < kAssumedCUs) t /= 2;
+    while (t > 32 && chains * (dv / t) < device_cus()) t /= 2;
     return t;
 }
 
@@ -145,10 +156,11 @@ kda_status_t resolve(const kda_problem_t *p, bool varlen, Resolved &r, bool chun
         // 16-column tiles at 9.1 ms); 16-column tiles where 32-column ones leave CUs idle (one
         // 131,072-token sequence x 32 heads: 4.37 vs 4.52 ms); otherwise 32-column tiles.
         int scan_cols = p->dv_tile == 64 ? 64 : p->dv_tile == 16 ? 16 : 32;
-        if (p->dv_tile == 0 && p->head_dim_v >= 64 && chains * (p->head_dim_v / 64) >= 2 * kAssumedCUs &&
+        const int cus = device_cus();
+        if (p->dv_tile == 0 && p->head_dim_v >= 64 && chains * (p->head_dim_v / 64) >= 2 * cus &&
             kda::split_variant_supported(dtype_of(p->io_dtype), p->head_dim_k, C, 2, 2))
             scan_cols = 64;
-        else if (p->dv_tile == 0 && chains * (p->head_dim_v / 32) < kAssumedCUs &&
+        else if (p->dv_tile == 0 && chains * (p->head_dim_v / 32) < cus &&
                  kda::split_variant_supported(dtype_of(p->io_dtype), p->head_dim_k, C, 1, 1))
             scan_cols = 16;
         r.spw = scan_cols == 64 ? 2 : 1;

@@ -59,6 +59,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void load_lds16(const void *src, void *lds) {
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
 }
+// 4 bytes per lane likewise: lane l's bytes land at lds + 4 l
+__device__ __forceinline__ void load_lds4(const void *src, void *lds) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 4, 0, 0);
+}
 
 // Value from the lane n places lower in the same row of 16 lanes; 0 for the first n lanes.
 template <int N>

@@ -117,40 +117,48 @@ __device__ __forceinline__ int64_t first_chunk(const FwdParams &p, const int32_t
 }
 
 // ------------------------------------------------------------------- prep ----
-template <typename IO, int DK, int C>
+template <typename IO, int DK, int C, bool PRO = false>
 struct PrepLayout {
     using Rec = SplitRecord<IO, DK, C>;
     static constexpr bool BF = Rec::BF;
     using OT = typename std::conditional<BF, uint16_t, float>::type;
     static constexpr int NSUB = C / 16, KT = DK / 16;
+    // one wave per sub-chunk, and at least d_k threads for the per-channel factors
+    static constexpr int NT = 64 * (NSUB > DK / 64 ? NSUB : DK / 64);
     static constexpr int PADO = 16 / (int)sizeof(OT);
     static constexpr int LDO = DK + PADO;
     static constexpr int LDX = C + 4;
     static constexpr int NSHIFT = NSUB >= 3 ? (NSUB - 1) * (NSUB - 2) / 2 : 0;
+    // K_b rows of every sub-chunk but the last, whose K_b is never a column operand
+    static constexpr int KB_ROWS = C - 16;
     static constexpr size_t oKb = 0;
-    static constexpr size_t oX = oKb + (size_t)C * LDO * sizeof(OT);
+    static constexpr size_t oX = oKb + (size_t)KB_ROWS * LDO * sizeof(OT);
     static constexpr size_t oTot = oX + (size_t)C * LDX * 4;
     static constexpr size_t oEB = oTot + (size_t)NSUB * DK * 4;
-    static constexpr size_t oED = oEB + (size_t)NSUB * DK * 4;
-    static constexpr size_t oEC = oED + (size_t)NSUB * DK * 4;
+    static constexpr size_t oEC = oEB + (size_t)NSUB * DK * 4;
     static constexpr size_t oSH = oEC + (size_t)NSUB * DK * 4;
     static constexpr size_t oBeta = oSH + (size_t)(NSHIFT > 0 ? NSHIFT : 1) * DK * 4;
-    static constexpr size_t kBytes = oBeta + (size_t)C * 4;
+    static constexpr size_t oTap = oBeta + (size_t)C * 4;  // the fused prologue's q and k filter taps
+    static constexpr size_t kBytes = oTap + (PRO ? (size_t)2 * DK * 16 : 0);
     __host__ __device__ static constexpr int shift_slot(int R, int I) { return (R - 2) * (R - 1) / 2 + I; }
 };
 
-// Three workgroups per CU (4 waves each): the kernel is bound by memory latency, and the waves of
-// the other workgroups hide it.
+// Several workgroups per CU (4 waves each; see kPrepWaves): each spends much of its time waiting
+// for its loads, and the waves of the other workgroups hide it.
 // PRO: the inputs are the raw projections and phase 1 applies the prologue as it loads them (see
 // FwdParams::conv): each lane's raw k and q for its token, the three tokens before it from its row
 // neighbours by DPP row shifts (the first three lanes of a row of 16 tokens also load the three
 // tokens before the row, zero before the sequence start), the 4-tap causal convolution and Swish
 // in fp32, then the L2 norm over the token's d_k channels (the four lanes of a token);
 // g = -softplus(g_raw) and beta = sigmoid(beta_raw) where read.
+// Waves per SIMD the prep kernel is compiled for: four workgroups per CU for bf16 io (128
+// registers, 38 KB of LDS at d_k = 128, chunk 64), three with the fused prologue, two for fp32 io.
+template <typename IO, bool PRO>
+constexpr int kPrepWaves = std::is_same<IO, float>::value ? 2 : PRO ? 3 : 4;
 template <typename IO, int DK, int C, bool PRO = false>
-__global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_t *__restrict__ chunk_off,
+__global__ void __launch_bounds__((PrepLayout<IO, DK, C, PRO>::NT), (kPrepWaves<IO, PRO>)) kda_prep_kernel(FwdParams p, const int32_t *__restrict__ chunk_off,
                                                        char *__restrict__ records) {
-    using L = PrepLayout<IO, DK, C>;
+    using L = PrepLayout<IO, DK, C, PRO>;
     using Rec = typename L::Rec;
     using OT = typename L::OT;
     constexpr bool BF = L::BF;
@@ -163,7 +171,6 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
     float *sX = reinterpret_cast<float *>(smem + L::oX);
     float *sTot = reinterpret_cast<float *>(smem + L::oTot);
     float *sEB = reinterpret_cast<float *>(smem + L::oEB);
-    float *sED = reinterpret_cast<float *>(smem + L::oED);
     float *sEC = reinterpret_cast<float *>(smem + L::oEC);
     float *sSH = reinterpret_cast<float *>(smem + L::oSH);
     float *sBeta = reinterpret_cast<float *>(smem + L::oBeta);
@@ -182,21 +189,34 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
     const int64_t tok0 = start + (int64_t)c * C;
     char *rec = records + (size_t)(gidx * H + h) * Rec::kBytes;
 
-    // fused prologue: the head's q and k filter taps as 4-tap windows, in the K_b rows (free until
-    // phase 3): [q | k][channel]
-    [[maybe_unused]] const float4 *sTap = reinterpret_cast<const float4 *>(smem + L::oKb);
+    // fused prologue: the head's q and k filter taps as 4-tap windows: [q | k][channel]
+    [[maybe_unused]] const float4 *sTap = reinterpret_cast<const float4 *>(smem + L::oTap);
     if constexpr (PRO) {
-        static_assert(2 * DK * 16 <= (size_t)C * LDO * sizeof(OT), "the taps fit in the K_b rows");
-        if (tid < 2 * DK) {
+        for (int i = tid; i < 2 * DK; i += L::NT) {
             float w4[4];
-            conv_taps4(p.conv[tid / DK] + ((int64_t)h * DK + tid % DK) * p.conv_w, p.conv_w, w4);
-            reinterpret_cast<float4 *>(smem + L::oKb)[tid] = make_float4(w4[0], w4[1], w4[2], w4[3]);
+            conv_taps4(p.conv[i / DK] + ((int64_t)h * DK + i % DK) * p.conv_w, p.conv_w, w4);
+            reinterpret_cast<float4 *>(smem + L::oTap)[i] = make_float4(w4[0], w4[1], w4[2], w4[3]);
         }
         __syncthreads();
     }
 
+    // beta of the chunk's tokens to sBeta, issued before the sub-chunk loads: straight into LDS
+    // (tokens past the chunk end are zeroed in phase 2), or, for the fused prologue, through a
+    // register that phase 1 passes through the sigmoid
+    [[maybe_unused]] float bta = 0.f;
+    if (tid < C) {
+        const float *bp = p.beta + (tok0 + min(tid, clen - 1)) * H + h;
+        if constexpr (PRO) bta = *bp;
+        else load_lds4(bp, sBeta);
+    }
+
     // ================= 1: load sub-chunk, scan the gate (log2 domain)
-    float G[KT][4], kr[KT][4], qr[KT][4];
+    // The lane's k and q stay packed as loaded until phase 3 (bf16 pairs: exact, and half the
+    // registers); fp32 io and the fused prologue, which forms them in fp32, keep fp32.
+    constexpr bool PACKED = BF && !PRO;
+    using KQ = typename std::conditional<PACKED, uint2, float4>::type;
+    float G[KT][4];
+    KQ kin[KT], qin[KT];
     bool split = false;  // the sub-chunk decays too strongly for a single-anchor diagonal block
     if (wave < NSUB) {
         const int R = wave;
@@ -210,18 +230,19 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
             const bool has3 = (int64_t)c * C + 16 * R + l16 - 3 >= 0 && l16 < 3;
             const int64_t row3 = ((tok0 + min(16 * R + l16 - 3, clen - 1)) * H + h) * (int64_t)DK + 4 * q4;
             // every load in flight first, packed as loaded
-            using KQ = typename std::conditional<BF, uint2, float4>::type;
-            KQ rk0[KT], rq0[KT], rk3[KT], rq3[KT];
+            using RKQ = typename std::conditional<BF, uint2, float4>::type;
+            RKQ rk0[KT], rq0[KT], rk3[KT], rq3[KT];
             float4 rg[KT];
 #pragma unroll
             for (int ct = 0; ct < KT; ++ct) {
                 const IO *kp = static_cast<const IO *>(p.k), *qp = static_cast<const IO *>(p.q);
                 rg[ct] = *reinterpret_cast<const float4 *>(p.g + row + 16 * ct);
-                rk0[ct] = *reinterpret_cast<const KQ *>(kp + row + 16 * ct);
-                rq0[ct] = *reinterpret_cast<const KQ *>(qp + row + 16 * ct);
-                rk3[ct] = has3 ? *reinterpret_cast<const KQ *>(kp + row3 + 16 * ct) : KQ{};
-                rq3[ct] = has3 ? *reinterpret_cast<const KQ *>(qp + row3 + 16 * ct) : KQ{};
+                rk0[ct] = *reinterpret_cast<const RKQ *>(kp + row + 16 * ct);
+                rq0[ct] = *reinterpret_cast<const RKQ *>(qp + row + 16 * ct);
+                rk3[ct] = has3 ? *reinterpret_cast<const RKQ *>(kp + row3 + 16 * ct) : RKQ{};
+                rq3[ct] = has3 ? *reinterpret_cast<const RKQ *>(qp + row3 + 16 * ct) : RKQ{};
             }
+            float kr[KT][4], qr[KT][4];
             float sk = 0.f, sq = 0.f;
 #pragma unroll
             for (int ct = 0; ct < KT; ++ct) {
@@ -266,23 +287,19 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
             sq += __shfl_xor(sq, 32);
             const float rk = valid ? rsqrtf(sk + p.norm_eps) : 0.f, rq = valid ? rsqrtf(sq + p.norm_eps) : 0.f;
 #pragma unroll
-            for (int ct = 0; ct < KT; ++ct)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    kr[ct][j] *= rk;
-                    qr[ct][j] *= rq;
-                }
+            for (int ct = 0; ct < KT; ++ct) {
+                kin[ct] = make_float4(kr[ct][0] * rk, kr[ct][1] * rk, kr[ct][2] * rk, kr[ct][3] * rk);
+                qin[ct] = make_float4(qr[ct][0] * rq, qr[ct][1] * rq, qr[ct][2] * rq, qr[ct][3] * rq);
+            }
         } else {
 #pragma unroll
         for (int ct = 0; ct < KT; ++ct) {
             const float4 gv = *reinterpret_cast<const float4 *>(p.g + row + 16 * ct);
-            const float4 kv = Tr::load4(static_cast<const IO *>(p.k) + row + 16 * ct);
-            const float4 qv = Tr::load4(static_cast<const IO *>(p.q) + row + 16 * ct);
+            const KQ kv = *reinterpret_cast<const KQ *>(static_cast<const IO *>(p.k) + row + 16 * ct);
+            const KQ qv = *reinterpret_cast<const KQ *>(static_cast<const IO *>(p.q) + row + 16 * ct);
             G[ct][0] = gv.x * m; G[ct][1] = gv.y * m; G[ct][2] = gv.z * m; G[ct][3] = gv.w * m;
-            kr[ct][0] = valid ? kv.x : 0.f; kr[ct][1] = valid ? kv.y : 0.f;
-            kr[ct][2] = valid ? kv.z : 0.f; kr[ct][3] = valid ? kv.w : 0.f;
-            qr[ct][0] = valid ? qv.x : 0.f; qr[ct][1] = valid ? qv.y : 0.f;
-            qr[ct][2] = valid ? qv.z : 0.f; qr[ct][3] = valid ? qv.w : 0.f;
+            kin[ct] = valid ? kv : KQ{};
+            qin[ct] = valid ? qv : KQ{};
         }
         }
 #pragma unroll
@@ -294,40 +311,97 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
                     make_float4(G[ct][0], G[ct][1], G[ct][2], G[ct][3]);
         }
         split = diag_needs_split<KT>(G);
+        f32x4 dA = zero4(), dPt = zero4();
         if (split) {
             // This sub-chunk decays by more than 2^-96 in some channel: its diagonal blocks of A and
-            // P come from the split levels (all factors <= 1, operands reloaded).  A_RR (times beta)
-            // goes to its place in sX; P_RR to its fragment of the record (phase 4 skips both).
-            f32x4 dA, dPt;
+            // P come from the split levels (all factors <= 1, operands reloaded).
             if constexpr (PRO) {
+                float kr[KT][4], qr[KT][4];
+#pragma unroll
+                for (int ct = 0; ct < KT; ++ct) {
+                    kr[ct][0] = kin[ct].x; kr[ct][1] = kin[ct].y; kr[ct][2] = kin[ct].z; kr[ct][3] = kin[ct].w;
+                    qr[ct][0] = qin[ct].x; qr[ct][1] = qin[ct].y; qr[ct][2] = qin[ct].z; qr[ct][3] = qin[ct].w;
+                }
                 diag_block_split_regs<IO, KT>(dA, dPt, kr, qr, G, l16, q4, lane);
             } else {
-                const int64_t row = ((tok0 + min(16 * R + l16, clen - 1)) * H + h) * (int64_t)DK + 4 * q4;
                 diag_block_split_rolled<IO>(dA, dPt, static_cast<const IO *>(p.k) + row,
                                             static_cast<const IO *>(p.q) + row, p.g + row, valid, KT, l16, q4, lane);
             }
+        }
+        // Per channel-tile pair: K_b = k e^{b_{R+1} - G} (the column operand of the later sub-chunks'
+        // off-diagonal blocks) to LDS, and the diagonal blocks, which pair the row operands
+        // k_r e^{G_r - b_R} (and the same for q) with the column operand k_i e^{b_R - G_i} (at most
+        // 2^96 unless `split`, when the blocks above replace them).  The sub-chunk total of each
+        // channel is in sTot (lane 15 of each row wrote it above).
+        wave_lds_sync();
+        f32x4 accA = zero4(), accPt = zero4();
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int rr = 4 * q4 + j;
-                float b = 16 * R + rr < clen ? p.beta[(tok0 + 16 * R + rr) * H + h] : 0.f;
-                if constexpr (PRO) b = 16 * R + rr < clen ? sigmoid_f(b) : 0.f;
-                sX[(16 * R + rr) * LDX + 16 * R + l16] = l16 < rr ? dA[j] * b : 0.f;
+        for (int kp = 0; kp < KT / 2; ++kp) {
+            Frag<BF> fk[2], fq[2], fd[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int ct = 2 * kp + u;
+                const int ch = 16 * ct + 4 * q4;
+                const float4 tot = *reinterpret_cast<const float4 *>(sTot + R * DK + ch);
+                const float tv[4] = {tot.x, tot.y, tot.z, tot.w};
+                const float4 kf = unpack4<PACKED>(kin[ct]), qf = unpack4<PACKED>(qin[ct]);
+                const float kx[4] = {kf.x, kf.y, kf.z, kf.w}, qx[4] = {qf.x, qf.y, qf.z, qf.w};
+                float kb[4], kd[4], kr[4], qr[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float fr = fast_exp2(G[ct][j]);          // e^{G_r - b_R}     <= 1
+                    const float fb = fast_exp2(tv[j] - G[ct][j]);  // e^{b_{R+1} - G_r} <= 1
+                    kr[j] = kx[j] * fr;
+                    qr[j] = qx[j] * fr;
+                    kb[j] = kx[j] * fb;
+                    kd[j] = kb[j] * fast_exp2(-tv[j]);
+                }
+                fk[u] = make_frag<BF>(kr[0], kr[1], kr[2], kr[3]);
+                fq[u] = make_frag<BF>(qr[0], qr[1], qr[2], qr[3]);
+                fd[u] = make_frag<BF>(kd[0], kd[1], kd[2], kd[3]);
+                if (R < NSUB - 1) {
+                    const Frag<BF> fkb = make_frag<BF>(kb[0], kb[1], kb[2], kb[3]);
+                    *reinterpret_cast<decltype(fkb.v) *>(sKb + (16 * R + l16) * LDO + ch) = fkb.v;
+                }
             }
-            const Frag<BF> fp = make_frag<BF>(dPt[0], dPt[1], dPt[2], dPt[3]);
+            mma32(accA, fk[0], fk[1], fd[0], fd[1]);   // A_RR:  rows r, columns i
+            mma32(accPt, fd[0], fd[1], fq[0], fq[1]);  // P_RR^T: rows i, columns r
+        }
+        mfma_settle(accA, accPt);
+        if (split) {
+            accA = dA;
+            accPt = dPt;
+        }
+        // A_RR (strictly lower, beta not yet applied) to its place in sX (lane: rows rr = 4*q4 + j,
+        // column l16); P_RR to its fragment of the record (the P_RR^T accumulator is the P_RR
+        // operand fragment: row l16, columns 4*q4 + j)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int rr = 4 * q4 + j;
+            sX[(16 * R + rr) * LDX + 16 * R + l16] = l16 < rr ? accA[j] : 0.f;
+        }
+        {
+            float pv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pv[j] = 4 * q4 + j > l16 ? 0.f : accPt[j];
+            const Frag<BF> fp = make_frag<BF>(pv[0], pv[1], pv[2], pv[3]);
             char *tile = rec + Rec::oP + Rec::tp_off(R, R / 2);
             // even R: the half tile is this fragment alone; odd R: the right fragment of the pair
             if (Rec::tp_half(R, R / 2)) store_frag<BF>(tile, lane, fp);
             else *reinterpret_cast<decltype(fp.v) *>(tile + lane * Rec::PAIR_BYTES + Rec::FRAG_BYTES) = fp.v;
         }
     }
-    if (tid < C) {
-        float b = tid < clen ? p.beta[(tok0 + tid) * H + h] : 0.f;
-        if constexpr (PRO) b = tid < clen ? sigmoid_f(b) : 0.f;
-        sBeta[tid] = b;
+    if constexpr (PRO) {
+        if (tid < C) sBeta[tid] = tid < clen ? sigmoid_f(bta) : 0.f;
+    } else if (wave == 0) {
+        wait_vmcnt<0>();  // the beta loads into LDS are complete
     }
     __syncthreads();
 
     // ================= 2: per-channel boundary factors; Gamma = e^{G_C}
+    if constexpr (!PRO) {
+        if (tid < C && tid >= clen) sBeta[tid] = 0.f;
+    }
     if (tid < DK) {
         const int ch = tid;
         float tot[NSUB], bnd[NSUB + 1];
@@ -341,7 +415,6 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
 #pragma unroll
         for (int R = 0; R < NSUB; ++R) {
             sEB[R * DK + ch] = fast_exp2(bnd[R]);
-            sED[R * DK + ch] = fast_exp2(-tot[R]);
             sEC[R * DK + ch] = fast_exp2(gc - bnd[R + 1]);
 #pragma unroll
             for (int I = 0; I + 2 <= R; ++I) sSH[L::shift_slot(R, I) * DK + ch] = fast_exp2(bnd[R] - bnd[I + 1]);
@@ -350,15 +423,16 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
     }
     __syncthreads();
 
-    // ================= 3: gated operands.  K~ and Q~ go straight to the record; K- is
-    // transposed in registers by a product with the identity (exact: every term is the
-    // operand times 1 or 0), which leaves this sub-chunk's half of each K-^T operand tile in
-    // fragment layout; K_b = k e^{b_{R+1} - G} goes to LDS as the column operand of the
-    // later rows' off-diagonal blocks.
-    Frag<BF> kdiag[KT];
+    // ================= 3: gated operands and the off-diagonal blocks of A and P.
+    // K~ and Q~ go straight to the record; K- is transposed in registers by a product with the
+    // identity (exact: every term is the operand times 1 or 0), which leaves this sub-chunk's half
+    // of each K-^T operand tile in fragment layout.  Block (R, I), I < R, pairs the row operands
+    // k_r e^{G_r - b_{I+1}} (and the same for q) with the column operand K_b of sub-chunk I (in
+    // LDS since phase 1); for I <= R - 2 the row operands take the extra factor
+    // e^{b_R - b_{I+1}} <= 1.  Each channel-tile pair adds its part to every block as soon as its
+    // row operands exist, so no row operand outlives its pair.
     if (wave < NSUB) {
         const int R = wave;
-        const int r = 16 * R + l16;
         Frag<BF> eye;  // identity as a B operand: rows 4*q4 + j, column l16
         {
             float e[4];
@@ -368,41 +442,43 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
         }
         char *kbt_half = rec + Rec::oKbT + (size_t)(R / 2) * Rec::TILE_BYTES + lane * Rec::PAIR_BYTES +
                          (R % 2) * Rec::FRAG_BYTES;
+        constexpr int NOFF = NSUB > 1 ? NSUB - 1 : 1;
+        f32x4 accA[NOFF], accPt[NOFF];
+#pragma unroll
+        for (int I = 0; I < NOFF; ++I) {
+            accA[I] = zero4();
+            accPt[I] = zero4();
+        }
 #pragma unroll
         for (int kp = 0; kp < KT / 2; ++kp) {
             Frag<BF> fkt[2], fqt[2];
+            float kr[2][4], qr[2][4];  // k and q times e^{G_r - b_R}
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int ct = 2 * kp + u;
                 const int ch = 16 * ct + 4 * q4;
                 const float4 tot = *reinterpret_cast<const float4 *>(sTot + R * DK + ch);
                 const float4 eb = *reinterpret_cast<const float4 *>(sEB + R * DK + ch);
-                const float4 ed = *reinterpret_cast<const float4 *>(sED + R * DK + ch);
                 const float4 ec = *reinterpret_cast<const float4 *>(sEC + R * DK + ch);
                 const float tv[4] = {tot.x, tot.y, tot.z, tot.w};
                 const float ebv[4] = {eb.x, eb.y, eb.z, eb.w};
-                const float edv[4] = {ed.x, ed.y, ed.z, ed.w};
                 const float ecv[4] = {ec.x, ec.y, ec.z, ec.w};
-                float kb[4], kt[4], qt[4], kbar[4], kd[4];
+                const float4 kf = unpack4<PACKED>(kin[ct]), qf = unpack4<PACKED>(qin[ct]);
+                const float kx[4] = {kf.x, kf.y, kf.z, kf.w}, qx[4] = {qf.x, qf.y, qf.z, qf.w};
+                float kt[4], qt[4], kbar[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const float fr = fast_exp2(G[ct][j]);          // e^{G_r - b_R}     <= 1
                     const float fb = fast_exp2(tv[j] - G[ct][j]);  // e^{b_{R+1} - G_r} <= 1
-                    const float krow = kr[ct][j] * fr;
-                    const float qrow = qr[ct][j] * fr;
-                    kb[j] = kr[ct][j] * fb;
-                    kd[j] = kb[j] * edv[j];
-                    kt[j] = krow * ebv[j];
-                    qt[j] = qrow * ebv[j];
-                    kbar[j] = kb[j] * ecv[j];
-                    kr[ct][j] = krow;
-                    qr[ct][j] = qrow;
+                    kr[u][j] = kx[j] * fr;
+                    qr[u][j] = qx[j] * fr;
+                    const float kb = kx[j] * fb;
+                    kt[j] = kr[u][j] * ebv[j];
+                    qt[j] = qr[u][j] * ebv[j];
+                    kbar[j] = kb * ecv[j];
                 }
-                kdiag[ct] = make_frag<BF>(kd[0], kd[1], kd[2], kd[3]);
                 fkt[u] = make_frag<BF>(kt[0], kt[1], kt[2], kt[3]);
                 fqt[u] = make_frag<BF>(qt[0], qt[1], qt[2], qt[3]);
-                const Frag<BF> fkb = make_frag<BF>(kb[0], kb[1], kb[2], kb[3]);
-                *reinterpret_cast<decltype(fkb.v) *>(sKb + r * LDO + ch) = fkb.v;
                 f32x4 kbt = zero4();
                 mma16(kbt, make_frag<BF>(kbar[0], kbar[1], kbar[2], kbar[3]), eye);
                 const Frag<BF> fkbt = frag_from_acc<BF>(kbt);
@@ -410,6 +486,31 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
             }
             store_pair<BF>(rec + Rec::oKt + (size_t)(R * (KT / 2) + kp) * Rec::TILE_BYTES, lane, fkt[0], fkt[1]);
             store_pair<BF>(rec + Rec::oQt + (size_t)(R * (KT / 2) + kp) * Rec::TILE_BYTES, lane, fqt[0], fqt[1]);
+            const int ct = 2 * kp;
+#pragma unroll
+            for (int I = 0; I < NSUB - 1; ++I) {
+                if (I >= R) break;
+                const OT *colp = sKb + (16 * I + l16) * LDO;
+                const Frag<BF> b0 = lds_frag(colp + 16 * ct + 4 * q4);
+                const Frag<BF> b1 = lds_frag(colp + 16 * (ct + 1) + 4 * q4);
+                Frag<BF> ka0, ka1, qa0, qa1;
+                if (I + 2 <= R) {
+                    const float *shp = sSH + L::shift_slot(R, I) * DK + 4 * q4;
+                    const float4 s0 = *reinterpret_cast<const float4 *>(shp + 16 * ct);
+                    const float4 s1 = *reinterpret_cast<const float4 *>(shp + 16 * (ct + 1));
+                    ka0 = make_frag<BF>(kr[0][0] * s0.x, kr[0][1] * s0.y, kr[0][2] * s0.z, kr[0][3] * s0.w);
+                    ka1 = make_frag<BF>(kr[1][0] * s1.x, kr[1][1] * s1.y, kr[1][2] * s1.z, kr[1][3] * s1.w);
+                    qa0 = make_frag<BF>(qr[0][0] * s0.x, qr[0][1] * s0.y, qr[0][2] * s0.z, qr[0][3] * s0.w);
+                    qa1 = make_frag<BF>(qr[1][0] * s1.x, qr[1][1] * s1.y, qr[1][2] * s1.z, qr[1][3] * s1.w);
+                } else {
+                    ka0 = make_frag<BF>(kr[0][0], kr[0][1], kr[0][2], kr[0][3]);
+                    ka1 = make_frag<BF>(kr[1][0], kr[1][1], kr[1][2], kr[1][3]);
+                    qa0 = make_frag<BF>(qr[0][0], qr[0][1], qr[0][2], qr[0][3]);
+                    qa1 = make_frag<BF>(qr[1][0], qr[1][1], qr[1][2], qr[1][3]);
+                }
+                mma32(accA[I], ka0, ka1, b0, b1);   // A_RI:  rows r, columns i
+                mma32(accPt[I], b0, b1, qa0, qa1);  // P_RI^T: rows i, columns r
+            }
         }
         if (NSUB % 2 == 1 && R == NSUB - 1) {  // odd sub-chunk count: zero the unused half of the last pair
             const Frag<BF> z = make_frag<BF>(0.f, 0.f, 0.f, 0.f);
@@ -417,96 +518,43 @@ __global__ void __launch_bounds__(256) kda_prep_kernel(FwdParams p, const int32_
             for (int ct = 0; ct < KT; ++ct)
                 *reinterpret_cast<decltype(z.v) *>(kbt_half + Rec::FRAG_BYTES + (size_t)ct * NPAIR * Rec::TILE_BYTES) = z.v;
         }
-    }
-    __syncthreads();
-
-    // ================= 4: row-R blocks of A (to LDS) and P (to the record); X_RR
-    // Block (R, I) pairs the row operands k_r e^{G_r - b_{I+1}} (and the same for q) with the
-    // column operand K_b of sub-chunk I; both factors are at most 1.  For I = R the column
-    // operand is k_i e^{b_R - G_i} (at most 2^96 unless `split`, when the block comes from the
-    // split levels instead), and for I <= R - 2 the row operands take the extra factor
-    // e^{b_R - b_{I+1}} <= 1.
-    if (wave < NSUB) {
-        const int R = wave;
+        // A_RI (times beta) to sX: lane holds rows rr = 4*q4 + j, column l16; P_RI^T accumulator =
+        // P_RI operand fragment: row l16, columns 4*q4 + j
         Frag<BF> pf[2 * NPAIR];
 #pragma unroll
-        for (int I = 0; I < 2 * NPAIR; ++I) pf[I] = make_frag<BF>(0.f, 0.f, 0.f, 0.f);
+        for (int I = 0; I < NSUB - 1; ++I) {
+            if (I >= R) break;
+            mfma_settle(accA[I], accPt[I]);
 #pragma unroll
-        for (int I = 0; I < NSUB; ++I) {
-            if (I > R) break;
-            const OT *colp = sKb + (16 * I + l16) * LDO;
-            const float *shp = sSH + (I + 2 <= R ? L::shift_slot(R, I) : 0) * DK + 4 * q4;
-            f32x4 accA = zero4(), accPt = zero4();
-            // (with `split` the diagonal block was formed in phase 1: this product is discarded)
-#pragma unroll
-            for (int ct = 0; ct < KT; ct += 2) {
-                Frag<BF> b0, b1, ka0, ka1, qa0, qa1;
-                if (I == R) {
-                    b0 = kdiag[ct];
-                    b1 = kdiag[ct + 1];
-                } else {
-                    b0 = lds_frag(colp + 16 * ct + 4 * q4);
-                    b1 = lds_frag(colp + 16 * (ct + 1) + 4 * q4);
-                }
-                if (I + 2 <= R) {
-                    const float4 s0 = *reinterpret_cast<const float4 *>(shp + 16 * ct);
-                    const float4 s1 = *reinterpret_cast<const float4 *>(shp + 16 * (ct + 1));
-                    ka0 = make_frag<BF>(kr[ct][0] * s0.x, kr[ct][1] * s0.y, kr[ct][2] * s0.z, kr[ct][3] * s0.w);
-                    ka1 = make_frag<BF>(kr[ct + 1][0] * s1.x, kr[ct + 1][1] * s1.y, kr[ct + 1][2] * s1.z,
-                                        kr[ct + 1][3] * s1.w);
-                    qa0 = make_frag<BF>(qr[ct][0] * s0.x, qr[ct][1] * s0.y, qr[ct][2] * s0.z, qr[ct][3] * s0.w);
-                    qa1 = make_frag<BF>(qr[ct + 1][0] * s1.x, qr[ct + 1][1] * s1.y, qr[ct + 1][2] * s1.z,
-                                        qr[ct + 1][3] * s1.w);
-                } else {
-                    ka0 = make_frag<BF>(kr[ct][0], kr[ct][1], kr[ct][2], kr[ct][3]);
-                    ka1 = make_frag<BF>(kr[ct + 1][0], kr[ct + 1][1], kr[ct + 1][2], kr[ct + 1][3]);
-                    qa0 = make_frag<BF>(qr[ct][0], qr[ct][1], qr[ct][2], qr[ct][3]);
-                    qa1 = make_frag<BF>(qr[ct + 1][0], qr[ct + 1][1], qr[ct + 1][2], qr[ct + 1][3]);
-                }
-                mma32(accA, ka0, ka1, b0, b1);   // A_RI:  rows r, columns i
-                mma32(accPt, b0, b1, qa0, qa1);  // P_RI^T: rows i, columns r
+            for (int j = 0; j < 4; ++j) {
+                const int rr = 4 * q4 + j;
+                sX[(16 * R + rr) * LDX + 16 * I + l16] = accA[I][j] * sBeta[16 * R + rr];
             }
-            mfma_settle(accA, accPt);  // read below, partly behind the `split` branches
-            // A_RI: lane holds rows rr = 4*q4 + j, column l16
-            if (!(I == R && split)) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int rr = 4 * q4 + j;
-                    float a = accA[j] * sBeta[16 * R + rr];
-                    if (I == R && l16 >= rr) a = 0.f;
-                    sX[(16 * R + rr) * LDX + 16 * I + l16] = a;
-                }
-            }
-            // P_RI^T accumulator = P_RI operand fragment: row l16, columns 4*q4 + j
-            float pv[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) pv[j] = (I == R && 4 * q4 + j > l16) ? 0.f : accPt[j];
-            pf[I] = make_frag<BF>(pv[0], pv[1], pv[2], pv[3]);
+            pf[I] = make_frag<BF>(accPt[I][0], accPt[I][1], accPt[I][2], accPt[I][3]);
         }
+        // P tiles of row R; the fragment P_RR came from phase 1
 #pragma unroll
         for (int pp = 0; pp < NPAIR; ++pp)
-            if (2 * pp <= R)
-            {
-                char *tile = rec + Rec::oP + Rec::tp_off(R, pp);
-                if (split && 2 * pp + 1 >= R) {  // the tile holding P_RR, whose fragment phase 1 wrote
-                    if (!Rec::tp_half(R, pp))     // odd R: the left fragment, P_R,R-1
-                        *reinterpret_cast<decltype(pf[0].v) *>(tile + lane * Rec::PAIR_BYTES) = pf[2 * pp].v;
-                } else if (Rec::tp_half(R, pp)) {
-                    store_frag<BF>(tile, lane, pf[2 * pp]);
-                } else {
-                    store_pair<BF>(tile, lane, pf[2 * pp], pf[2 * pp + 1]);
-                }
+            if (2 * pp + 1 < R) {
+                store_pair<BF>(rec + Rec::oP + Rec::tp_off(R, pp), lane, pf[2 * pp], pf[2 * pp + 1]);
+            } else if (2 * pp + 1 == R) {  // odd R: the left fragment P_R,R-1 of the tile holding P_RR
+                *reinterpret_cast<decltype(pf[0].v) *>(rec + Rec::oP + Rec::tp_off(R, pp) + lane * Rec::PAIR_BYTES) =
+                    pf[2 * pp].v;
             }
 
-        // X_RR = (I + A_RR)^{-1}, row by row; lane l16 owns column l16 (this wave wrote A_RR)
-        wave_lds_sync();
+        // X_RR = (I + Diag(beta) A_RR)^{-1}, row by row (phase 1 left A_RR without beta); lane l16
+        // owns column l16
         float *Ab = sX + (16 * R) * LDX + 16 * R;
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
+            const float br = sBeta[16 * R + r];
             float s = (r == l16) ? 1.f : 0.f;
 #pragma unroll
-            for (int m = 0; m < r; ++m) s -= Ab[r * LDX + m] * x[m];
+            for (int m = 0; m < r; ++m) {
+                const float a = Ab[r * LDX + m] * br;
+                s -= a * x[m];
+            }
             x[r] = s;
         }
         if (q4 == 0) {
@@ -1550,7 +1598,7 @@ constexpr size_t split_record_bytes() {
 
 template <typename IO, int DK, int C, int SPW, int NW>
 constexpr bool split_fits() {
-    return ScanLayout<IO, DK, C, SPW, NW>::kFits && PrepLayout<IO, DK, C>::kBytes <= 160 * 1024;
+    return ScanLayout<IO, DK, C, SPW, NW>::kFits && PrepLayout<IO, DK, C, true>::kBytes <= 160 * 1024;
 }
 
 // Workspace: [plan: chunk offsets and longest-first order, split_plan_bytes][records]
@@ -1574,10 +1622,12 @@ hipError_t launch_split_variant(const FwdParams &params, char *workspace, int64_
         const int64_t prep_blocks = chunk_upper * p.H;
         if (prep_blocks > 0 && !p.skip_prep) {
             if (pro)
-                hipLaunchKernelGGL((kda_prep_kernel<IO, DK, C, true>), dim3((unsigned)prep_blocks), dim3(256), 0, stream,
+                hipLaunchKernelGGL((kda_prep_kernel<IO, DK, C, true>), dim3((unsigned)prep_blocks),
+                                   dim3(PrepLayout<IO, DK, C, true>::NT), 0, stream,
                                    p, chunk_off, records);
             else
-                hipLaunchKernelGGL((kda_prep_kernel<IO, DK, C>), dim3((unsigned)prep_blocks), dim3(256), 0, stream, p,
+                hipLaunchKernelGGL((kda_prep_kernel<IO, DK, C>), dim3((unsigned)prep_blocks),
+                                   dim3(PrepLayout<IO, DK, C>::NT), 0, stream, p,
                                    chunk_off, records);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;

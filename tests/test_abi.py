@@ -207,8 +207,9 @@ def test_recurrent_validation():
 
 
 def test_query_reports_config_and_work():
-    # prefill workload: B=4, T=4096, H=16, d=128, chunk 64, bf16
-    r = kda.query(4, 4096, 16, 128, 128, "bf16")
+    # prefill workload: B=4, T=4096, H=16, d=128, bf16; chunk 32 by default
+    assert kda.query(4, 4096, 16, 128, 128, "bf16")["chunk_size"] == 32
+    r = kda.query(4, 4096, 16, 128, 128, "bf16", chunk_size=64)
     assert r["status"] == kda.KDA_OK and r["supported"] == 1
     assert r["algo"] == kda.KDA_ALGO_TWO_PASS and r["chunk_size"] == 64
     # plan (chunk-offset table and longest-first order, 256 B each) + one record per chunk-head:
@@ -219,7 +220,7 @@ def test_query_reports_config_and_work():
     rec = (rec + 1023) // 1024 * 1024
     assert r["workspace_bytes"] == 2 * 256 + 4 * 64 * 16 * rec
     assert r["grid_blocks"] == 4 * 16 * (128 // r["dv_tile"])
-    rf = kda.query(4, 4096, 16, 128, 128, "bf16", algo="fused")
+    rf = kda.query(4, 4096, 16, 128, 128, "bf16", chunk_size=64, algo="fused")
     assert rf["algo"] == kda.KDA_ALGO_FUSED and rf["workspace_bytes"] == 0
     assert rf["grid_blocks"] == 4 * 16 * (128 // rf["dv_tile"])
     ht = 4 * 4096 * 16
