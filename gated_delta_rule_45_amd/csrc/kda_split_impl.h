@@ -18,14 +18,14 @@
 //
 // Pass 2 (kda_scan_kernel): one workgroup per (sequence, head, d_v tile); each compute wave
 // owns 16 or 32 columns of the fp32 state, kept in registers.  Per chunk, with the record
-// staged in LDS by copy waves that load it one or two chunks ahead:
+// staged in LDS by copy waves that load it one to three chunks ahead:
 //
 //   Y = V - K~ S        D = T Y         O = scale (Q~ S + P D)        S <- Gamma S + K-^T D
 //
 // (D = T (V - K~ S) equals the WY form U - W S with W = T K~ and U = T V.)  Where LDS allows,
 // kda_scan_ow_kernel runs the same algebra with the state chain and the output on separate
-// waves; the KEEP instantiation (chunk states for the backward pass) and shapes whose extra
-// LDS slots do not fit use kda_scan_kernel.
+// waves (its KEEP instantiation, for the backward pass, writes each chunk's initial state and
+// D instead of the output); shapes whose extra LDS slots do not fit use kda_scan_kernel.
 #pragma once
 
 #include <type_traits>

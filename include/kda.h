@@ -81,10 +81,11 @@ typedef struct {
     int32_t head_dim_v;  /* d_v in {64, 128} */
     int32_t num_seqs;    /* with cu_seqlens: number of sequences (cu_seqlens has num_seqs+1 entries); else ignored */
     int32_t io_dtype;    /* kda_dtype_t: dtype of q, k, v and out; g, beta and the state are always fp32 */
-    int32_t chunk_size;  /* 16, 32 or 64; 0 = library default (64, or 32 for fp32 with d_k = 128) */
+    int32_t chunk_size;  /* 16, 32 or 64; 0 = library default (32 for the forward, the largest
+                            compiled chunk, 64, for kda_chunk_bwd) */
     float scale;         /* multiplies the output (1.0 for o_t = S_t^T q_t) */
     int32_t dv_tile;     /* state columns per workgroup: 0 = library choice; fused: 32, 64 or 128;
-                            two-pass: 32 or 64 (tuning) */
+                            two-pass: 16, 32 or 64 */
     int32_t algo;        /* kda_algo_t */
 } kda_problem_t;
 
@@ -189,8 +190,8 @@ kda_status_t kda_chunk_fwd_prologue(const kda_problem_t *problem, int32_t conv_w
  *                  one record of per-chunk operands for the reverse scan);
  *                  contents on entry ignored, on return unspecified.  Required.
  * No output may alias an input or another output.  Status and error behaviour as for
- * kda_chunk_fwd; KDA_ERR_UNSUPPORTED when no compiled variant fits (fp32 io with
- * chunk 64 at d_v = 128, for instance).
+ * kda_chunk_fwd; KDA_ERR_UNSUPPORTED for a head dimension or chunk size without a compiled
+ * variant.
  */
 kda_status_t kda_chunk_bwd(const kda_problem_t *problem, const void *q, const void *k, const void *v,
                            const float *g, const float *beta, const float *initial_state,
