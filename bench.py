@@ -3,8 +3,8 @@
 
 One step = one pass of the hot path over one batch of synthetic input:
   * kda_chunk_fwd over the prefill workload (B=4, T=4096, H=16, d_k=d_v=128, bf16 q/k/v,
-    fp32 gate/beta/state, the library-default chunk (32), initial state given, final state
-    written), and
+    fp32 gate/beta/state, chunk 64 as the workload names it, initial state given, final state
+    written; the library's default chunk, 32, is timed beside it), and
   * kda_decode_step over the decode workload (256 sequences x 32 heads, fp32 state
     128x128 updated in place).
 The long-prefill (1 x 131,072 tokens x 32 heads) and packed-varlen (64 sequences, lengths
@@ -147,8 +147,9 @@ def cpu_baseline(inp):
 def workload_leg(name, kda, ki, torch, dev, stream, steps, cpu_heads, want_cpu):
     """kda_chunk_fwd over one of the other full-size chunked workloads (long prefill, packed varlen),
     inputs drawn on the GPU with the workload's recipe and seed (kda_inputs.workload_inputs_on),
-    library-default configuration, initial state given and final state written.  The CPU oracle is
-    timed on `cpu_heads` of its heads (all sequences, all tokens of those heads)."""
+    at the workload's chunk with the library's other defaults, and again with the library's
+    default chunk (`default_chunk`); initial state given and final state written.  The CPU oracle
+    is timed on `cpu_heads` of its heads (all sequences, all tokens of those heads)."""
     w = ki.WORKLOADS[name]
     inp = ki.workload_inputs_on(name, dev)
     B, T, H = inp.q.shape[0], inp.q.shape[1], inp.q.shape[2]
@@ -157,19 +158,26 @@ def workload_leg(name, kda, ki, torch, dev, stream, steps, cpu_heads, want_cpu):
     out = torch.empty_like(inp.v)
     fin = torch.empty((n, H, w.dk, w.dv), dtype=torch.float32, device=dev)
     cu_host = inp.cu_seqlens.cpu() if varlen else None
-    q = kda.query(B, T, H, w.dk, w.dv, w.io, num_seqs=n if varlen else 0, device=True)
-    ws = torch.empty(max(q["workspace_bytes"], 1), dtype=torch.uint8, device=dev)
-
-    def call():
-        kda.chunk_fwd(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.s0, inp.cu_seqlens, cu_seqlens_host=cu_host,
-                      workspace=ws, out=out, final_state=fin)
-
-    for _ in range(2):
-        call()
-    torch.cuda.synchronize()
     reps = max(3, steps // 4)
-    ms = time_launches(call, reps, stream)
+
+    def timed(chunk):
+        q = kda.query(B, T, H, w.dk, w.dv, w.io, num_seqs=n if varlen else 0, chunk_size=chunk, device=True)
+        ws = torch.empty(max(q["workspace_bytes"], 1), dtype=torch.uint8, device=dev)
+
+        def call():
+            kda.chunk_fwd(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.s0, inp.cu_seqlens, cu_seqlens_host=cu_host,
+                          chunk_size=chunk, workspace=ws, out=out, final_state=fin)
+
+        for _ in range(2):
+            call()
+        torch.cuda.synchronize()
+        ms = time_launches(call, reps, stream)
+        del ws
+        return q, ms
+
     tokens = B * T
+    qd, msd = timed(0)
+    q, ms = timed(w.chunk)
     gbps = q["hbm_bytes"] / (ms * 1e-3) / 1e9
     leg = {"workload": f"{name}: " + (f"{n} packed sequences, {T} tokens" if varlen else f"B={B} T={T}") +
                        f", H={H}, d_k=d_v={w.dk}, {w.io} q/k/v, fp32 gate/beta/state",
@@ -177,6 +185,9 @@ def workload_leg(name, kda, ki, torch, dev, stream, steps, cpu_heads, want_cpu):
            "calls_timed": reps, "ms": round(ms, 4), "tokens_per_s": round(tokens / (ms * 1e-3), 1),
            "bytes_per_launch": q["hbm_bytes"], "gb_per_s": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
            "tflops": round(q["flops"] / (ms * 1e-3) / 1e12, 2),
+           "default_chunk": {"chunk": qd["chunk_size"], "dv_tile": qd["dv_tile"], "ms": round(msd, 4),
+                             "tokens_per_s": round(tokens / (msd * 1e-3), 1),
+                             "hbm_frac": round(qd["hbm_bytes"] / (msd * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
            "data": "synthetic, drawn on the GPU with the workload's recipe and seed"}
     log(f"{name}: {leg['ms']} ms per call, {leg['tokens_per_s'] / 1e6:.1f} M tokens/s, hbm_frac {leg['hbm_frac']}")
     if want_cpu:
@@ -197,7 +208,7 @@ def workload_leg(name, kda, ki, torch, dev, stream, steps, cpu_heads, want_cpu):
                                "sample": f"{len(sel)} of {H} heads, every sequence and token, fp64 token recurrence, "
                                          f"{dt:.2f} s wall, scaled to the whole workload"}
         log(f"{name}: CPU oracle on {len(sel)} heads took {dt:.1f} s")
-    del inp, out, fin, ws
+    del inp, out, fin
     torch.cuda.empty_cache()
     return leg
 
@@ -241,7 +252,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--dv-tile", type=int, default=0)
-    ap.add_argument("--chunk", type=int, default=0, help="forward chunk (0: the library's default)")
+    ap.add_argument("--chunk", type=int, default=64,
+                    help="forward chunk of the prefill step (the workload's 64; 0: the library's default)")
     ap.add_argument("--bwd-chunk", type=int, default=64, help="backward chunk")
     ap.add_argument("--algo", default="auto", choices=["auto", "fused", "two_pass"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -284,6 +296,14 @@ def main():
     def prefill():
         kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], chunk_size=args.chunk,
                       dv_tile=args.dv_tile, algo=args.algo, workspace=ws, out=out, final_state=fin)
+
+    # the same call with the library's default chunk, reported beside the step
+    qdef = kda.query(B, T, H, w.dk, w.dv, "bf16", device=True)
+    ws_def = torch.empty(max(qdef["workspace_bytes"], 1), dtype=torch.uint8, device=dev)
+
+    def prefill_default():
+        kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], workspace=ws_def, out=out,
+                      final_state=fin)
 
     # ----------------------------------------------------------------- decode
     wd = ki.WORKLOADS["decode"]
@@ -371,6 +391,7 @@ def main():
         prologue()
         forward_raw_fused()
         forward_raw_composed()
+        prefill_default()
     torch.cuda.synchronize()
 
     # timed region: K steps, each = one prefill launch + one decode launch
@@ -378,6 +399,7 @@ def main():
     t_dec = time_launches(decode, args.steps, stream)
     t_epi = time_launches(epilogue, args.steps, stream)
     pre_med, pre_min = time_each(prefill, args.steps, stream)
+    t_pre_def = time_launches(prefill_default, args.steps, stream)
     dec_med, dec_min = time_each(decode, args.steps, stream)
     t_decg = time_launches(decode_gated, args.steps, stream)
     t_decc = time_launches(decode_then_norm_gate, args.steps, stream)
@@ -458,6 +480,11 @@ def main():
                     "tokens_per_s": round(pre_tps, 1), "gb_per_s": round(pre_gbps, 1),
                     "hbm_frac": round(pre_gbps / PEAK_HBM_GBPS, 4), "tflops": round(pre_tflops, 2),
                     "mfma_frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4), "flops_per_launch": q["flops"]},
+        "prefill_default_chunk": {"chunk": qdef["chunk_size"], "dv_tile": qdef["dv_tile"], "ms": round(t_pre_def, 4),
+                                  "tokens_per_s": round(tokens / (t_pre_def * 1e-3), 1),
+                                  "hbm_frac": round(pre_bytes / (t_pre_def * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                                  "tflops": round(qdef["flops"] / (t_pre_def * 1e-3) / 1e12, 2),
+                                  "traffic": traffic.get("prefill_default_chunk_bytes")},
         "decode": {"ms": round(t_dec, 4), "ms_median": round(dec_med, 4), "ms_min": round(dec_min, 4),
                    "gb_per_s": round(dec_gbps, 1), "hbm_frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
                    "bytes_per_launch": dec_bytes},

@@ -151,12 +151,13 @@ struct PrepLayout {
 // tokens before the row, zero before the sequence start), the 4-tap causal convolution and Swish
 // in fp32, then the L2 norm over the token's d_k channels (the four lanes of a token);
 // g = -softplus(g_raw) and beta = sigmoid(beta_raw) where read.
-// Waves per SIMD the prep kernel is compiled for: four workgroups per CU for bf16 io (128
-// registers, 38 KB of LDS at d_k = 128, chunk 64), three with the fused prologue, two for fp32 io.
-template <typename IO, bool PRO>
-constexpr int kPrepWaves = std::is_same<IO, float>::value ? 2 : PRO ? 3 : 4;
+// Waves per SIMD the prep kernel is compiled for: four for bf16 io up to chunk 32 (128 registers;
+// eight two-wave workgroups per CU at d_k = 128, chunk 32), three at chunk 64 (the row operands of
+// phase 1 are kept for phase 3 instead of recomputed) and with the fused prologue, two for fp32 io.
+template <typename IO, int C, bool PRO>
+constexpr int kPrepWaves = std::is_same<IO, float>::value ? 2 : (PRO || C >= 64) ? 3 : 4;
 template <typename IO, int DK, int C, bool PRO = false>
-__global__ void __launch_bounds__((PrepLayout<IO, DK, C, PRO>::NT), (kPrepWaves<IO, PRO>)) kda_prep_kernel(FwdParams p, const int32_t *__restrict__ chunk_off,
+__global__ void __launch_bounds__((PrepLayout<IO, DK, C, PRO>::NT), (kPrepWaves<IO, C, PRO>)) kda_prep_kernel(FwdParams p, const int32_t *__restrict__ chunk_off,
                                                        char *__restrict__ records) {
     using L = PrepLayout<IO, DK, C, PRO>;
     using Rec = typename L::Rec;
@@ -217,6 +218,10 @@ __global__ void __launch_bounds__((PrepLayout<IO, DK, C, PRO>::NT), (kPrepWaves<
     using KQ = typename std::conditional<PACKED, uint2, float4>::type;
     float G[KT][4];
     KQ kin[KT], qin[KT];
+    // chunk 64: phase 1's k e^{G_r - b_R}, q e^{G_r - b_R} and k e^{b_{R+1} - G_r} stay in registers
+    // for phase 3 (at three waves per SIMD); smaller chunks recompute them there (four waves)
+    constexpr bool KEEPROW = NSUB >= 4;
+    [[maybe_unused]] float krs[KEEPROW ? KT : 1][4], qrs[KEEPROW ? KT : 1][4], kbs[KEEPROW ? KT : 1][4];
     bool split = false;  // the sub-chunk decays too strongly for a single-anchor diagonal block
     if (wave < NSUB) {
         const int R = wave;
@@ -355,6 +360,11 @@ __global__ void __launch_bounds__((PrepLayout<IO, DK, C, PRO>::NT), (kPrepWaves<
                     qr[j] = qx[j] * fr;
                     kb[j] = kx[j] * fb;
                     kd[j] = kb[j] * fast_exp2(-tv[j]);
+                    if constexpr (KEEPROW) {
+                        krs[ct][j] = kr[j];
+                        qrs[ct][j] = qr[j];
+                        kbs[ct][j] = kb[j];
+                    }
                 }
                 fk[u] = make_frag<BF>(kr[0], kr[1], kr[2], kr[3]);
                 fq[u] = make_frag<BF>(qr[0], qr[1], qr[2], qr[3]);
@@ -457,25 +467,38 @@ __global__ void __launch_bounds__((PrepLayout<IO, DK, C, PRO>::NT), (kPrepWaves<
             for (int u = 0; u < 2; ++u) {
                 const int ct = 2 * kp + u;
                 const int ch = 16 * ct + 4 * q4;
-                const float4 tot = *reinterpret_cast<const float4 *>(sTot + R * DK + ch);
                 const float4 eb = *reinterpret_cast<const float4 *>(sEB + R * DK + ch);
                 const float4 ec = *reinterpret_cast<const float4 *>(sEC + R * DK + ch);
-                const float tv[4] = {tot.x, tot.y, tot.z, tot.w};
                 const float ebv[4] = {eb.x, eb.y, eb.z, eb.w};
                 const float ecv[4] = {ec.x, ec.y, ec.z, ec.w};
-                const float4 kf = unpack4<PACKED>(kin[ct]), qf = unpack4<PACKED>(qin[ct]);
-                const float kx[4] = {kf.x, kf.y, kf.z, kf.w}, qx[4] = {qf.x, qf.y, qf.z, qf.w};
+                float kb[4];
+                if constexpr (KEEPROW) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        kr[u][j] = krs[ct][j];
+                        qr[u][j] = qrs[ct][j];
+                        kb[j] = kbs[ct][j];
+                    }
+                } else {  // the same values as phase 1's
+                    const float4 tot = *reinterpret_cast<const float4 *>(sTot + R * DK + ch);
+                    const float tv[4] = {tot.x, tot.y, tot.z, tot.w};
+                    const float4 kf = unpack4<PACKED>(kin[ct]), qf = unpack4<PACKED>(qin[ct]);
+                    const float kx[4] = {kf.x, kf.y, kf.z, kf.w}, qx[4] = {qf.x, qf.y, qf.z, qf.w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float fr = fast_exp2(G[ct][j]);          // e^{G_r - b_R}     <= 1
+                        const float fb = fast_exp2(tv[j] - G[ct][j]);  // e^{b_{R+1} - G_r} <= 1
+                        kr[u][j] = kx[j] * fr;
+                        qr[u][j] = qx[j] * fr;
+                        kb[j] = kx[j] * fb;
+                    }
+                }
                 float kt[4], qt[4], kbar[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float fr = fast_exp2(G[ct][j]);          // e^{G_r - b_R}     <= 1
-                    const float fb = fast_exp2(tv[j] - G[ct][j]);  // e^{b_{R+1} - G_r} <= 1
-                    kr[u][j] = kx[j] * fr;
-                    qr[u][j] = qx[j] * fr;
-                    const float kb = kx[j] * fb;
                     kt[j] = kr[u][j] * ebv[j];
                     qt[j] = qr[u][j] * ebv[j];
-                    kbar[j] = kb * ecv[j];
+                    kbar[j] = kb[j] * ecv[j];
                 }
                 fkt[u] = make_frag<BF>(kt[0], kt[1], kt[2], kt[3]);
                 fqt[u] = make_frag<BF>(qt[0], qt[1], qt[2], qt[3]);
