@@ -212,8 +212,8 @@ __global__ void __launch_bounds__((PrepLayout<IO, DK, C, PRO>::NT), (kPrepWaves<
     }
 
     // ================= 1: load sub-chunk, scan the gate (log2 domain)
-    // The lane's k and q stay packed as loaded until phase 3 (bf16 pairs: exact, and half the
-    // registers); fp32 io and the fused prologue, which forms them in fp32, keep fp32.
+    // The lane's k and q stay packed as loaded until they are used (bf16 pairs: exact, and half
+    // the registers); fp32 io and the fused prologue, which forms them in fp32, keep fp32.
     constexpr bool PACKED = BF && !PRO;
     using KQ = typename std::conditional<PACKED, uint2, float4>::type;
     float G[KT][4];
