@@ -587,7 +587,7 @@ __global__ void __launch_bounds__((PrepLayout<IO, DK, C, PRO>::NT), (kPrepWaves<
     }
     __syncthreads();
 
-    // ================= 5: off-diagonal blocks of X, one block diagonal at a time:
+    // ================= 4: off-diagonal blocks of X, one block diagonal at a time:
     // X_RI = -X_RR sum_{J=I}^{R-1} A_RJ X_JI  (fp32 matrix-core products).
     // sX holds A_RI below the diagonal (kept), X_RR on the diagonal, and X_RI transposed in
     // the otherwise unused upper block (I, R): X_RI[a][b] at sX[(16I + b) * LDX + 16R + a].
@@ -621,7 +621,7 @@ __global__ void __launch_bounds__((PrepLayout<IO, DK, C, PRO>::NT), (kPrepWaves<
         __syncthreads();
     }
 
-    // ================= 6: T = X Diag(beta) to the record
+    // ================= 5: T = X Diag(beta) to the record
     if (wave < NSUB) {
         const int R = wave;
 #pragma unroll
