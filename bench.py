@@ -479,7 +479,12 @@ def main():
         "prefill": {"ms": round(t_pre, 4), "ms_median": round(pre_med, 4), "ms_min": round(pre_min, 4),
                     "tokens_per_s": round(pre_tps, 1), "gb_per_s": round(pre_gbps, 1),
                     "hbm_frac": round(pre_gbps / PEAK_HBM_GBPS, 4), "tflops": round(pre_tflops, 2),
-                    "mfma_frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4), "flops_per_launch": q["flops"]},
+                    "mfma_frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4), "flops_per_launch": q["flops"],
+                    "flops_count": "per head-token 2C(d_k+d_v) + C^2/3 + 6 d_k d_v: the products this algorithm "
+                                   "runs (A, P, T(V - K~S), PD, K~S, Q~S, K-^T D); forming W = T K~ as well, which "
+                                   "it never does, would add C d_k",
+                    "mfma_frac_with_w": round(pre_tflops * (1 + tokens * H * q["chunk_size"] * w.dk / q["flops"])
+                                              / PEAK_BF16_TFLOPS, 4)},
         "prefill_default_chunk": {"chunk": qdef["chunk_size"], "dv_tile": qdef["dv_tile"], "ms": round(t_pre_def, 4),
                                   "tokens_per_s": round(tokens / (t_pre_def * 1e-3), 1),
                                   "hbm_frac": round(pre_bytes / (t_pre_def * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),

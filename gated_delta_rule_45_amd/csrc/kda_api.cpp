@@ -580,6 +580,7 @@ kda_status_t kda_chunk_bwd(const kda_problem_t *problem, const void *q, const vo
         bp.brec = ws + b.off_brec;
         bp.split_flag = reinterpret_cast<int32_t *>(ws + b.off_flag);
         bp.slots = b.slots;
+        bp.cus = device_cus();
         auto launch_bwd = [&](int phases) {
             bp.phases = phases;
             return problem->io_dtype == KDA_BF16 ? kda::launch_bwd_bf16(bp, b.chunk, s) : kda::launch_bwd_f32(bp, b.chunk, s);

@@ -43,6 +43,7 @@
 // factors are <= 1 and the middle one is a per-channel constant of the block pair.
 #pragma once
 
+#include <algorithm>
 #include <type_traits>
 
 #include "kda_chunk_impl.h"
@@ -1050,7 +1051,10 @@ struct BwdGradLayout {
 
 // SPLIT: this instantiation takes the chunks kda_bwd_prep_kernel flagged (some sub-chunk decays beyond
 // the single-anchor limit of the diagonal blocks) and forms their diagonal-block terms from the split
-// levels; the other instantiation takes every other chunk with no trace of that path in its code.
+// levels; the other instantiation takes every other chunk with no trace of that path in its code.  Such
+// chunks are rare, so the SPLIT grid has about one workgroup per CU, and each walks the (slot, head)
+// pairs blockIdx.x, + gridDim.x, ... and takes the flagged ones: in the common case the launch costs a
+// few flag reads instead of one empty 92 KB workgroup per pair.
 template <typename IO, int DK, int DV, int C, bool SPLIT>
 __global__ void __launch_bounds__(64 * (DK / 16)) kda_bwd_grad_kernel(BwdParams bp) {
     using L = BwdGradLayout<IO, DK, DV, C>;
@@ -1078,8 +1082,32 @@ __global__ void __launch_bounds__(64 * (DK / 16)) kda_bwd_grad_kernel(BwdParams 
     const int lane = tid & 63, l16 = lane & 15, q4 = lane >> 4;
     const int H = p.H;
 
-    const int64_t slot = blockIdx.x / H;
-    const int h = (int)(blockIdx.x % H);
+    [[maybe_unused]] int64_t item = blockIdx.x;  // SPLIT: the (slot, head) pair this pass takes
+next_item:
+    if constexpr (SPLIT) {
+        // the next flagged pair among item, item + gridDim.x, ...: thread t checks the t-th of them,
+        // and the first flagged one wins
+        __shared__ int s_first;
+        for (;;) {
+            if (item >= bp.slots * H) return;
+            if (tid == 0) s_first = NT;
+            __syncthreads();
+            const int64_t cand = item + (int64_t)gridDim.x * tid;
+            int n0, c0;
+            if (cand < bp.slots * H && bwd_slot_chunk(p, C, cand / H, n0, c0) && bp.split_flag[cand] != 0)
+                atomicMin(&s_first, tid);
+            __syncthreads();
+            const int first = s_first;
+            __syncthreads();  // every thread has read s_first before it is reset
+            if (first < NT) {
+                item += (int64_t)gridDim.x * first;
+                break;
+            }
+            item += (int64_t)gridDim.x * NT;
+        }
+    }
+    const int64_t slot = SPLIT ? item / H : blockIdx.x / H;
+    const int h = SPLIT ? (int)(item % H) : (int)(blockIdx.x % H);
     int n, ci;
     if (!bwd_slot_chunk(p, C, slot, n, ci)) return;
     if ((bp.split_flag[slot * H + h] != 0) != SPLIT) return;  // the other instantiation's chunk
@@ -1475,6 +1503,11 @@ __global__ void __launch_bounds__(64 * (DK / 16)) kda_bwd_grad_kernel(BwdParams 
         for (int w = 0; w < NW; ++w) x += sDb[w * C + tid];
         bp.dbeta[(tok0 + tid) * H + h] = x;
     }
+    if constexpr (SPLIT) {
+        __syncthreads();  // the next pair restages the LDS this one still reads
+        item += gridDim.x;
+        goto next_item;
+    }
 }
 
 // ================================================================== launch ====
@@ -1511,8 +1544,9 @@ hipError_t launch_bwd_variant(const BwdParams &bp, hipStream_t stream) {
                                dim3(BwdGradLayout<IO, DK, DV, C>::NT), 0, stream, bp);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
-            // chunks with strong decay (flagged by the prep kernel); the other workgroups exit at once
-            hipLaunchKernelGGL((kda_bwd_grad_kernel<IO, DK, DV, C, true>), dim3((unsigned)grad_blocks),
+            // chunks with strong decay (flagged by the prep kernel), walked by about one workgroup per CU
+            const int64_t split_blocks = std::min<int64_t>(grad_blocks, std::max(1, bp.cus));
+            hipLaunchKernelGGL((kda_bwd_grad_kernel<IO, DK, DV, C, true>), dim3((unsigned)split_blocks),
                                dim3(BwdGradLayout<IO, DK, DV, C>::NT), 0, stream, bp);
             return hipGetLastError();
         }

@@ -126,6 +126,7 @@ struct BwdParams {
     // e^{G_C}; the output's Q~ and P are left out), written by kda_bwd_prep_kernel; null: not written
     char *frec = nullptr;
     int phases = 3;  // launches: 1 = the prep kernel, 2 = the reverse scan and the gradients
+    int cus = 256;   // compute units of the device (grid of the strong-decay gradient pass)
 };
 bool bwd_supported_bf16(int dk, int dv, int chunk);
 size_t bwd_record_bytes_bf16(int dk, int chunk);

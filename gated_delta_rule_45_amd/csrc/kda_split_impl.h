@@ -165,7 +165,6 @@ __global__ void __launch_bounds__((PrepLayout<IO, DK, C, PRO>::NT), (kPrepWaves<
     constexpr bool BF = L::BF;
     constexpr int NSUB = L::NSUB, KT = L::KT, NPAIR = Rec::NPAIR;
     constexpr int LDO = L::LDO, LDX = L::LDX;
-    using Tr = IoTraits<IO>;
 
     __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
     OT *sKb = reinterpret_cast<OT *>(smem + L::oKb);
