@@ -1049,6 +1049,32 @@ struct BwdGradLayout {
 };
 
 
+// Advances `item` to the first (slot, head) pair among item, item + gridDim.x, ... that
+// kda_bwd_prep_kernel flagged (thread t checks the t-th candidate, the first flagged one wins); false
+// when there is none.  Every thread of the workgroup calls it and gets the same answer.
+template <int C, int NT>
+__device__ __forceinline__ bool next_flagged_pair(const BwdParams &bp, int64_t &item) {
+    __shared__ int s_first;
+    const int64_t items = bp.slots * bp.f.H;
+    const int tid = threadIdx.x;
+    for (; item < items; item += (int64_t)gridDim.x * NT) {
+        if (tid == 0) s_first = NT;
+        __syncthreads();
+        const int64_t cand = item + (int64_t)gridDim.x * tid;
+        int n, ci;
+        if (cand < items && bwd_slot_chunk(bp.f, C, cand / bp.f.H, n, ci) && bp.split_flag[cand] != 0)
+            atomicMin(&s_first, tid);
+        __syncthreads();
+        const int first = s_first;
+        __syncthreads();  // every thread has read s_first before the next round resets it
+        if (first < NT) {
+            item += (int64_t)gridDim.x * first;
+            return true;
+        }
+    }
+    return false;
+}
+
 // SPLIT: this instantiation takes the chunks kda_bwd_prep_kernel flagged (some sub-chunk decays beyond
 // the single-anchor limit of the diagonal blocks) and forms their diagonal-block terms from the split
 // levels; the other instantiation takes every other chunk with no trace of that path in its code.  Such
@@ -1082,30 +1108,13 @@ __global__ void __launch_bounds__(64 * (DK / 16)) kda_bwd_grad_kernel(BwdParams 
     const int lane = tid & 63, l16 = lane & 15, q4 = lane >> 4;
     const int H = p.H;
 
-    [[maybe_unused]] int64_t item = blockIdx.x;  // SPLIT: the (slot, head) pair this pass takes
-next_item:
+    // SPLIT: the (slot, head) pair this pass takes; a workgroup with no flagged pair leaves here,
+    // before anything the pass keeps across pairs is formed
+    [[maybe_unused]] int64_t item = blockIdx.x;
     if constexpr (SPLIT) {
-        // the next flagged pair among item, item + gridDim.x, ...: thread t checks the t-th of them,
-        // and the first flagged one wins
-        __shared__ int s_first;
-        for (;;) {
-            if (item >= bp.slots * H) return;
-            if (tid == 0) s_first = NT;
-            __syncthreads();
-            const int64_t cand = item + (int64_t)gridDim.x * tid;
-            int n0, c0;
-            if (cand < bp.slots * H && bwd_slot_chunk(p, C, cand / H, n0, c0) && bp.split_flag[cand] != 0)
-                atomicMin(&s_first, tid);
-            __syncthreads();
-            const int first = s_first;
-            __syncthreads();  // every thread has read s_first before it is reset
-            if (first < NT) {
-                item += (int64_t)gridDim.x * first;
-                break;
-            }
-            item += (int64_t)gridDim.x * NT;
-        }
+        if (!next_flagged_pair<C, NT>(bp, item)) return;
     }
+next_item:
     const int64_t slot = SPLIT ? item / H : blockIdx.x / H;
     const int h = SPLIT ? (int)(item % H) : (int)(blockIdx.x % H);
     int n, ci;
@@ -1506,7 +1515,7 @@ next_item:
     if constexpr (SPLIT) {
         __syncthreads();  // the next pair restages the LDS this one still reads
         item += gridDim.x;
-        goto next_item;
+        if (next_flagged_pair<C, NT>(bp, item)) goto next_item;
     }
 }
 
