@@ -188,3 +188,13 @@ def test_bwd_strong_decay_inside_a_chunk(io, dk, chunk):
                                                s0_std=0.5))
     skip_unsupported(inp, chunk)
     check_bwd(inp, chunk=chunk, label=f"strong decay {io} d{dk} c{chunk}")
+
+
+@pytest.mark.parametrize("chunk", [16, 64])
+def test_bwd_strong_decay_every_chunk_many_per_workgroup(chunk):
+    """Every chunk flagged for the split-level gradient pass (kda_inputs.plant_strong_decay decays one
+    channel by e^-112 per sub-chunk throughout) and more flagged chunk-heads than the pass has
+    workgroups (one per CU), so each workgroup takes several in turn (2,048 at chunk 16, 512 at 64)."""
+    inp = ki.plant_strong_decay(ki.make_inputs(2, 4096, 4, 128, 128, "bf16", seed=71 + chunk, s0_std=0.5))
+    skip_unsupported(inp, chunk)
+    check_bwd(inp, chunk=chunk, label=f"strong decay every chunk c{chunk}")
